@@ -1,0 +1,142 @@
+"""FP8 (OCP e4m3fn) payload oracle. Test infrastructure only.
+
+The pages name BF16/FP8 payloads for the token copy kernels (torchtitan PR 5541, "AI-Generated
+Details" and "Verification") and say nothing more. Readings:
+  * encoding: OCP e4m3fn (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no infinity,
+    0x7F/0xFF NaN, largest finite 448, subnormals m * 2^-9), round to nearest even, saturating
+    at +-448;
+  * per-row absmax scaling: amax = max |a| over the row; the quantiser multiplies by the FP32
+    value 448 / amax (FP32 division), rounds the FP32 product to e4m3, and stores the FP32
+    dequantisation scale amax / 448; an all-zero row stores code 0 and scale 1. Both sides take
+    these FP32 steps, so the codes are compared bit for bit;
+  * activations are scaled per token (row of x), weights per output channel (row of W1[e] over
+    H, row of W2[e] over I), h per dispatched row (over I) before the down projection;
+  * products accumulate in FP32 (exactly, here in FP64) and are dequantised by s_row * s_col.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .ffn import combine, silu
+from .routing import dispatch, layout, route
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode_table() -> np.ndarray:
+    """Value of each of the 256 codes (NaN for 0x7F and 0xFF)."""
+    vals = np.zeros(256)
+    for code in range(256):
+        s = -1.0 if code & 0x80 else 1.0
+        ex = (code >> 3) & 0xF
+        m = code & 0x7
+        if ex == 0xF and m == 0x7:
+            vals[code] = np.nan
+        elif ex == 0:
+            vals[code] = s * m * 2.0 ** -9
+        else:
+            vals[code] = s * (1.0 + m / 8.0) * 2.0 ** (ex - 7)
+    return vals
+
+
+_TABLE = e4m3_decode_table()
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    return _TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+def e4m3_encode(v: np.ndarray) -> np.ndarray:
+    """Round FP32 values to e4m3fn codes: nearest, ties to even mantissa, saturating at 448."""
+    v = np.asarray(v, dtype=np.float32)
+    a = np.abs(v).astype(np.float64)
+    nan = np.isnan(a)
+    a = np.where(nan, 0.0, a)
+    # binade of a: a = f * 2^ex with f in [0.5, 1), so floor(log2 a) = ex - 1; subnormals share
+    # the 2^-6 binade's quantum 2^-9
+    ex = np.frexp(a)[1].astype(np.int64) - 1
+    ex = np.maximum(ex, -6)
+    quantum = np.ldexp(1.0, ex - 3)
+    mag = np.round(a / quantum) * quantum                 # numpy rounds half to even
+    mag = np.minimum(mag, E4M3_MAX)
+    # encode the rounded magnitude
+    ex2 = np.frexp(np.where(mag > 0, mag, 1.0))[1].astype(np.int64) - 1
+    normal = mag >= 2.0 ** -6
+    efield = np.where(normal, ex2 + 7, 0)
+    mfield = np.where(normal, np.round(mag / np.ldexp(1.0, ex2) * 8.0) - 8.0,
+                      np.round(mag / 2.0 ** -9)).astype(np.int64)
+    code = (efield << 3) | mfield
+    code = np.where(np.signbit(v), code | 0x80, code)
+    code = np.where(nan, 0x7F, code)
+    return code.astype(np.uint8)
+
+
+def quantize_rows(a: np.ndarray):
+    """Per-row absmax quantisation (FP32 steps as stated in the module header).
+    Returns (codes uint8 [R, K], scale float32 [R])."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    amax = np.max(np.abs(a), axis=-1) if a.shape[-1] else np.zeros(a.shape[:-1], np.float32)
+    amax = amax.astype(np.float32)
+    zero = amax == 0
+    safe = np.where(zero, np.float32(1.0), amax).astype(np.float32)
+    inv = (np.float32(E4M3_MAX) / safe).astype(np.float32)
+    v = (a * inv[..., None]).astype(np.float32)
+    codes = e4m3_encode(v)
+    codes[zero] = 0
+    scale = np.where(zero, np.float32(1.0), (safe / np.float32(E4M3_MAX)).astype(np.float32))
+    return codes, scale.astype(np.float32)
+
+
+def dequantize_rows(codes, scale):
+    return e4m3_decode(codes) * np.asarray(scale, dtype=np.float64)[..., None]
+
+
+def forward(x, logits, w1, w2, *, k, e0, E_local, n_chunks, P_c=None, wq=None):
+    """FP8 forward: quantise x per token and weights per output channel, grouped GEMMs with
+    FP64 accumulation and s_row * s_col dequantisation, h quantised per row before the down
+    projection; yd and combine unrounded (FP64).
+
+    wq: optional precomputed (w1_codes, w1_scale, w2_codes, w2_scale)."""
+    T, H = x.shape
+    E = logits.shape[1]
+    if P_c is None:
+        tc = -(-T // n_chunks)
+        P_c = ((tc * min(k, E_local) + 3) // 4) * 4
+    idx, gates = route(logits, k)
+    counts, offsets, row_of, src_token = layout(idx, E, e0, E_local, n_chunks, P_c)
+    xq, xs = quantize_rows(x)                   # per token
+    if wq is None:
+        w1q, w1s = quantize_rows(w1)            # [E_l, 2I, H] codes, [E_l, 2I] scales
+        w2q, w2s = quantize_rows(w2)            # [E_l, H, I] codes, [E_l, H] scales
+    else:
+        w1q, w1s, w2q, w2s = wq
+    xdq = dispatch(xq.astype(np.int64), src_token).astype(np.uint8)
+    xds = np.ones(src_token.size, dtype=np.float32)
+    v = src_token >= 0
+    xds[v] = xs[src_token[v]]
+    I = w1.shape[1] // 2
+    P = src_token.size
+    h = np.zeros((P, I))
+    yd = np.zeros((P, H))
+    hq_all = np.zeros((P, I), dtype=np.uint8)
+    hs_all = np.ones(P, dtype=np.float32)
+    for c in range(n_chunks):
+        for e in range(E_local):
+            r0 = c * P_c + int(offsets[c, e])
+            r1 = c * P_c + int(offsets[c, e + 1])
+            if r1 == r0:
+                continue
+            a = e4m3_decode(xdq[r0:r1])
+            acc = a @ e4m3_decode(w1q[e]).T
+            gu = acc * xds[r0:r1, None].astype(np.float64) * w1s[e][None, :].astype(np.float64)
+            hh = silu(gu[:, :I]) * gu[:, I:]
+            h[r0:r1] = hh
+            hq, hs = quantize_rows(hh.astype(np.float32))
+            hq_all[r0:r1] = hq
+            hs_all[r0:r1] = hs
+            acc2 = e4m3_decode(hq) @ e4m3_decode(w2q[e]).T
+            yd[r0:r1] = acc2 * hs[:, None].astype(np.float64) * w2s[e][None, :].astype(np.float64)
+    out = combine(yd, gates, row_of)
+    return dict(idx=idx, gates=gates, counts=counts, offsets=offsets, row_of=row_of,
+                src_token=src_token, xq=xq, xs=xs, xdq=xdq, xds=xds, w1q=w1q, w1s=w1s,
+                w2q=w2q, w2s=w2s, h=h, hq=hq_all, hs=hs_all, yd=yd, out=out, P_c=P_c)

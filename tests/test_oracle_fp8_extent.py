@@ -1,0 +1,153 @@
+"""Pins for the FP8 encoder (torch's float8_e4m3fn, the OCP table, error bounds) and for the
+extent bookkeeping (the numbers printed in ART PR 971's native validation)."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import extent, fp8
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_e4m3_table_closed_forms():
+    t = fp8.e4m3_decode_table()
+    assert t[0x7E] == 448.0 and t[0xFE] == -448.0
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF])
+    assert t[0x01] == 2.0 ** -9 and t[0x08] == 2.0 ** -6 and t[0x38] == 1.0
+    finite = t[np.isfinite(t)]
+    assert finite.size == 254
+
+
+def test_e4m3_encode_round_trips_every_code():
+    t = fp8.e4m3_decode_table()
+    codes = np.array([c for c in range(256) if np.isfinite(t[c])], dtype=np.uint8)
+    back = fp8.e4m3_encode(t[codes].astype(np.float32))
+    # +0 and -0 keep their sign bit; every other code maps to itself
+    np.testing.assert_array_equal(back, codes)
+
+
+def test_e4m3_encode_matches_torch_in_range():
+    rng = np.random.default_rng(0)
+    v = np.concatenate([
+        rng.standard_normal(200000).astype(np.float32) * 50,
+        (rng.uniform(-1, 1, 50000) * 2.0 ** -6).astype(np.float32),            # subnormal range
+        (rng.uniform(-448, 448, 50000)).astype(np.float32),
+    ])
+    t = fp8.e4m3_decode_table()
+    mids = [(t[c] + t[c + 1]) / 2 for c in range(0, 0x7E)]                       # exact ties
+    v = np.concatenate([v, np.array(mids, np.float32), -np.array(mids, np.float32)])
+    v = v[np.abs(v) <= 448]
+    ours = fp8.e4m3_encode(v)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(ours, ref)
+
+
+def test_e4m3_saturates():
+    v = np.array([449.0, 464.0, 1e6, -500.0, 480.0], np.float32)
+    np.testing.assert_array_equal(fp8.e4m3_encode(v), [0x7E, 0x7E, 0x7E, 0xFE, 0x7E])
+
+
+def test_quantize_rows_error_bound_and_zero_row():
+    rng = np.random.default_rng(4)
+    a = rng.standard_normal((64, 300)).astype(np.float32) * rng.uniform(0.01, 10, (64, 1)).astype(np.float32)
+    a[5] = 0
+    codes, scale = fp8.quantize_rows(a)
+    assert np.all(codes[5] == 0) and scale[5] == 1.0
+    deq = fp8.dequantize_rows(codes, scale)
+    bound = 2.0 ** -4 * np.abs(a) + 2.0 ** -9 * scale[:, None] * (1 + 1e-6)
+    assert np.all(np.abs(deq - a) <= bound)
+    # the row maximum maps onto +-448 (up to one FP32 rounding of amax * (448 / amax))
+    top = np.abs(fp8.e4m3_decode(codes)).max(1)
+    assert np.all(top[np.arange(64) != 5] == 448.0)
+
+
+def test_extent_tracker_reproduces_art971_fixture():
+    g = json.load(open(os.path.join(GOLDEN, "extent_art971.json")))
+    tr = extent.ExtentTracker()
+    H, es, rows = g["H"], g["elem_size_bf16"], g["logical_rows"]
+    floor0 = g["workspace_floor_sequence"][0]
+    assert extent.workspace_floor(floor0, tr.current(rows), H, es) == g["workspace_floor_sequence"][0]
+    hnd = tr.acquire(g["live_extent_rows"])
+    P = tr.current(rows)
+    assert P == g["live_extent_rows"]
+    assert extent.output_bytes(P, H, es) == g["bytes_with_live_extent"]
+    assert extent.workspace_floor(floor0, P, H, es) == g["workspace_floor_sequence"][1]
+    tr.release(hnd)
+    P = tr.current(rows)
+    assert extent.output_bytes(P, H, es) == g["bytes_after_release"] == g["retained_bytes"]
+    assert extent.workspace_floor(floor0, P, H, es) == g["workspace_floor_sequence"][2]
+    # the live extent needs zero growth of the native buffer, yet the output is a fresh allocation
+    assert g["live_extent_rows"] <= g["native_buffer_rows"]
+    assert g["output_floor_bytes_review"] == 2 ** 19 * 1709
+
+
+def test_extent_tracker_semantics():
+    tr = extent.ExtentTracker()
+    assert tr.current(0) == 0 and tr.current(5) == 8
+    a = tr.acquire(101)
+    b = tr.acquire(37)
+    assert tr.current(10) == 104          # max with the live high-water, rounded up to 4
+    assert tr.current(200) == 200         # a larger own extent wins (maximum, not sum)
+    tr.release(a)
+    assert tr.current(10) == 40
+    tr.release(b)
+    assert tr.current(10) == 12
+    with pytest.raises(KeyError):
+        tr.release(b)
+
+
+def test_router_accum_golden_is_fp32_epsilon():
+    g = json.load(open(os.path.join(GOLDEN, "router_fp32_accum_megatron7342.json")))
+    assert abs(g["max_abs_error"] - 2.0 ** -23) < 1e-11
+
+
+def _exact_e4m3_rows(rng, shape):
+    """Random e4m3-representable values whose every row has absmax exactly 448 (scale 1)."""
+    t = fp8.e4m3_decode_table()
+    finite = t[np.isfinite(t)]
+    a = rng.choice(finite, size=shape).astype(np.float32)
+    a[..., 0] = 448.0
+    return a
+
+
+def test_fp8_forward_exact_when_quantisation_is_identity():
+    import oracle
+    rng = np.random.default_rng(21)
+    T, H, I, E, k = 40, 32, 16, 4, 2
+    x = _exact_e4m3_rows(rng, (T, H)) * np.float32(2.0 ** -6)        # per-row scale 2^-6 exactly
+    w1 = _exact_e4m3_rows(rng, (E, 2 * I, H)) * np.float32(2.0 ** -12)
+    w2 = _exact_e4m3_rows(rng, (E, H, I)) * np.float32(2.0 ** -12)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    f8 = fp8.forward(x, logits, w1, w2, k=k, e0=0, E_local=E, n_chunks=2)
+    f64 = oracle.forward(x, logits, w1, w2, k=k, e0=0, E_local=E, n_chunks=2)
+    np.testing.assert_array_equal(f8["xs"], np.float32(2.0 ** -6))
+    np.testing.assert_array_equal(fp8.dequantize_rows(f8["xq"], f8["xs"]), x)
+    used = f64["src_token"] >= 0
+    np.testing.assert_allclose(f8["h"][used], f64["h"][used], rtol=1e-12, atol=1e-30)
+    # the down projection sees h through one per-row quantisation: bounded relative error
+    err = np.linalg.norm(f8["out"] - f64["out"]) / np.linalg.norm(f64["out"])
+    assert err < 2.0 ** -4
+
+
+def test_fp8_forward_close_to_exact_forward():
+    import oracle
+    rng = np.random.default_rng(22)
+    T, H, I, E, El, k = 96, 64, 48, 8, 4, 3
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    w1 = (rng.standard_normal((El, 2 * I, H)) * 0.05).astype(np.float32)
+    w2 = (rng.standard_normal((El, H, I)) * 0.05).astype(np.float32)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    f8 = fp8.forward(x, logits, w1, w2, k=k, e0=2, E_local=El, n_chunks=2)
+    f64 = oracle.forward(x, logits, w1, w2, k=k, e0=2, E_local=El, n_chunks=2)
+    for key in ("idx", "counts", "offsets", "row_of", "src_token"):
+        np.testing.assert_array_equal(f8[key], f64[key])
+    err = np.linalg.norm(f8["out"] - f64["out"]) / np.linalg.norm(f64["out"])
+    # four independent e4m3 roundings (x, W1, h, W2), each about 3.6% RMS relative (3 mantissa
+    # bits): sqrt(4) * 3.6% = 7.2% expected; a misplaced scale is off by orders of magnitude
+    assert 1e-3 < err < 0.1
+    # codes of dispatched rows are the token's codes
+    v = f8["src_token"] >= 0
+    np.testing.assert_array_equal(f8["xdq"][v], f8["xq"][f8["src_token"][v]])
