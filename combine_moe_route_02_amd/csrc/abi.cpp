@@ -1,0 +1,514 @@
+// C ABI of the MoE layer share (include/moe.h): argument validation, extent bookkeeping,
+// workspace sizing, the stage calls and the two-stream chunk schedule of the layer primitives.
+#include "../../include/moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdarg>
+#include <cstdio>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+moe_status hip_check(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MOE_OK;
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define MOE_TRY(expr)                      \
+  do {                                     \
+    moe_status _st = (expr);               \
+    if (_st != MOE_OK) return _st;         \
+  } while (0)
+#define MOE_HIP(expr, what) MOE_TRY(hip_check((expr), (what)))
+#define MOE_NEED(p) \
+  do { if (!(p)) return fail(MOE_ERR_ARG, "%s: argument '%s' is NULL", __func__, #p); } while (0)
+
+int64_t round4(int64_t x) { return (x + 3) / 4 * 4; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t tokens_per_chunk(const moe_desc* d) { return cdiv(d->T, d->n_chunks); }
+int64_t min_pc(const moe_desc* d) {
+  int64_t kk = d->k < d->E_local ? d->k : d->E_local;
+  return tokens_per_chunk(d) * kk;
+}
+int elem_size(int dtype) { return dtype == MOE_F32 ? 4 : 2; }  // payload rows (FP8: BF16 x/yd)
+
+moe_status validate(const moe_desc* d) {
+  if (!d) return fail(MOE_ERR_ARG, "descriptor is NULL");
+  if (d->reserved != 0) return fail(MOE_ERR_ARG, "descriptor field 'reserved' must be 0");
+  if (d->dtype != MOE_F32 && d->dtype != MOE_BF16 && d->dtype != MOE_FP8_E4M3)
+    return fail(MOE_ERR_ARG, "unknown dtype %d", d->dtype);
+  if (d->T < 0) return fail(MOE_ERR_ARG, "T = %lld is negative", (long long)d->T);
+  if (d->n_chunks < 1) return fail(MOE_ERR_ARG, "n_chunks = %d must be >= 1", d->n_chunks);
+  if (d->E < 1 || d->E > 1024) return fail(MOE_ERR_UNSUPPORTED, "E = %d outside 1..1024", d->E);
+  if (d->k < 1 || d->k > d->E) return fail(MOE_ERR_ARG, "k = %d outside 1..E", d->k);
+  if (d->k > 8) return fail(MOE_ERR_UNSUPPORTED, "k = %d above 8", d->k);
+  if (d->e0 < 0 || d->E_local < 0 || (int64_t)d->e0 + d->E_local > d->E)
+    return fail(MOE_ERR_ARG, "local experts [%d, %d) not inside [0, %d)", d->e0, d->e0 + d->E_local, d->E);
+  if ((int64_t)d->n_chunks * d->E_local > 1024)
+    return fail(MOE_ERR_UNSUPPORTED, "n_chunks * E_local = %lld above 1024",
+                (long long)d->n_chunks * d->E_local);
+  if (d->H <= 0 || d->H % 64) return fail(MOE_ERR_UNSUPPORTED, "H = %d must be a positive multiple of 64", d->H);
+  if (d->I <= 0 || d->I % 64) return fail(MOE_ERR_UNSUPPORTED, "I = %d must be a positive multiple of 64", d->I);
+  if (d->dtype == MOE_BF16 && d->E % 4) return fail(MOE_ERR_UNSUPPORTED, "BF16 path needs E %% 4 == 0 (E = %d)", d->E);
+  if (d->dtype == MOE_FP8_E4M3 && d->H > 8192)
+    return fail(MOE_ERR_UNSUPPORTED, "FP8 dispatch keeps a row in registers: H = %d above 8192", d->H);
+  if (d->P_c % 4) return fail(MOE_ERR_CAPACITY, "P_c = %lld is not a multiple of 4", (long long)d->P_c);
+  if (d->P_c < min_pc(d))
+    return fail(MOE_ERR_CAPACITY, "P_c = %lld below ceil(T/n)*min(k,E_local) = %lld", (long long)d->P_c,
+                (long long)min_pc(d));
+  if (d->P_out % 4) return fail(MOE_ERR_CAPACITY, "P_out = %lld is not a multiple of 4", (long long)d->P_out);
+  if (d->P_out < d->T) return fail(MOE_ERR_CAPACITY, "P_out = %lld below T = %lld", (long long)d->P_out, (long long)d->T);
+  if ((int64_t)d->n_chunks * d->P_c > INT32_MAX || d->T * d->k > INT32_MAX)
+    return fail(MOE_ERR_UNSUPPORTED, "row indices exceed int32");
+  return MOE_OK;
+}
+
+moe_status check_chunk(const moe_desc* d, int chunk) {
+  if (chunk < -1 || chunk >= d->n_chunks)
+    return fail(MOE_ERR_ARG, "chunk = %d outside -1..%d", chunk, d->n_chunks - 1);
+  return MOE_OK;
+}
+
+struct Range { int64_t t0, t1; int c0, nc; };
+Range range_of(const moe_desc* d, int chunk) {
+  if (chunk < 0) return {0, d->T, 0, d->n_chunks};
+  int64_t tc = tokens_per_chunk(d);
+  int64_t a = chunk * tc, b = a + tc;
+  if (a > d->T) a = d->T;
+  if (b > d->T) b = d->T;
+  return {a, b, chunk, 1};
+}
+
+bool is_bf16_rows(const moe_desc* d) { return d->dtype != MOE_F32; }
+// dispatch rows of the descriptor (0 when no expert is local)
+int64_t rows_of(const moe_desc* d) { return d->E_local > 0 ? (int64_t)d->n_chunks * d->P_c : 0; }
+
+// Events for the two-stream schedule, created once per device and reused.
+struct EventPool {
+  std::vector<hipEvent_t> ev;
+};
+std::mutex g_pool_mu;
+std::map<int, EventPool> g_pools;
+
+moe_status events(int count, hipEvent_t** out) {
+  int dev = 0;
+  MOE_HIP(hipGetDevice(&dev), "hipGetDevice");
+  std::lock_guard<std::mutex> lk(g_pool_mu);
+  EventPool& p = g_pools[dev];
+  while ((int)p.ev.size() < count) {
+    hipEvent_t e;
+    MOE_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming), "hipEventCreateWithFlags");
+    p.ev.push_back(e);
+  }
+  *out = p.ev.data();
+  return MOE_OK;
+}
+
+int64_t router_scratch(const moe_desc* d) {
+  return moe::router_partials_bytes(tokens_per_chunk(d), d->E, d->H);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+int32_t moe_abi_version(void) { return 1; }
+
+moe_status moe_required_extent(int64_t T, int32_t k, int32_t E_local, int32_t n_chunks, int64_t* P_c,
+                               int64_t* P_out) {
+  if (!P_c || !P_out) return fail(MOE_ERR_ARG, "output pointer is NULL");
+  if (T < 0 || k < 1 || E_local < 0 || n_chunks < 1) return fail(MOE_ERR_ARG, "invalid extent arguments");
+  int64_t kk = k < E_local ? k : E_local;
+  *P_c = round4(cdiv(T, n_chunks) * kk);
+  int64_t po = round4(T * k);
+  *P_out = po > round4(T) ? po : round4(T);
+  return MOE_OK;
+}
+
+moe_status moe_workspace_bytes(const moe_desc* d, moe_workspace_sizes* o) {
+  MOE_TRY(validate(d));
+  if (!o) return fail(MOE_ERR_ARG, "output pointer is NULL");
+  const int64_t T = d->T, H = d->H, I = d->I, E = d->E, El = d->E_local, K = d->k, n = d->n_chunks;
+  const int64_t P = n * d->P_c;
+  const int64_t es = elem_size(d->dtype);
+  const bool fp8 = d->dtype == MOE_FP8_E4M3;
+  *o = moe_workspace_sizes{};
+  o->topk_idx = T * K * 4;
+  o->gates = T * K * 4;
+  o->counts = n * E * 4;
+  o->offsets = n * (El + 1) * 4;
+  o->row_of = T * K * 4;
+  o->src_token = P * 4;
+  o->xd = P * H * (fp8 ? 1 : es);
+  o->xd_scale = fp8 ? P * 4 : 0;
+  o->gu = fp8 ? 0 : P * 2 * I * es;
+  o->h = P * I * es;
+  o->h_scale = fp8 ? P * 4 : 0;
+  o->yd = P * H * es;
+  o->out = d->P_out * H * es;
+  if (!fp8) {
+    o->dyd = P * H * es;
+    o->dgates = T * K * 4;
+    o->dlogits = T * E * 4;
+    o->dwr_acc = E * H * 4;
+    o->dgu = P * 2 * I * es;
+    o->dxd = P * H * es;
+    o->dx = T * H * es;
+    o->dw1 = El * 2 * I * H * es;
+    o->dw2 = El * H * I * es;
+    o->dwr = E * H * es;
+  }
+  o->route_scratch = moe::route_scratch_bytes(T, (int)n, (int)E);
+  o->route_bwd_scratch = fp8 ? 0 : router_scratch(d);
+  o->workspace = o->route_scratch > o->route_bwd_scratch ? o->route_scratch : o->route_bwd_scratch;
+  return MOE_OK;
+}
+
+// ----------------------------------------------------------------------------- stage calls
+
+moe_status moe_route(const moe_desc* d, int chunk, const float* logits, int32_t* topk_idx, float* gates,
+                     int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* src_token,
+                     void* workspace, void* stream) {
+  MOE_TRY(validate(d));
+  MOE_TRY(check_chunk(d, chunk));
+  if (d->T > 0) { MOE_NEED(logits); MOE_NEED(topk_idx); MOE_NEED(gates); MOE_NEED(row_of); }
+  if (rows_of(d) > 0) MOE_NEED(src_token);
+  MOE_NEED(counts); MOE_NEED(offsets); MOE_NEED(workspace);
+  Range r = range_of(d, chunk);
+  MOE_HIP(moe::launch_route(logits, topk_idx, gates, counts, offsets, row_of, src_token,
+                            (int32_t*)workspace, d->T, d->E, d->e0, d->E_local, d->k, d->n_chunks,
+                            r.c0, r.nc, d->P_c, (hipStream_t)stream),
+          "route");
+  return MOE_OK;
+}
+
+moe_status moe_dispatch(const moe_desc* d, int chunk, const void* x, const int32_t* row_of, void* xd,
+                        float* xd_scale, float* h_scale, void* stream) {
+  MOE_TRY(validate(d));
+  MOE_TRY(check_chunk(d, chunk));
+  Range r = range_of(d, chunk);
+  if (r.t1 <= r.t0) return MOE_OK;
+  MOE_NEED(x); MOE_NEED(row_of);
+  if (rows_of(d) == 0) return MOE_OK;  // no local expert: nothing to write
+  MOE_NEED(xd);
+  if (d->dtype == MOE_FP8_E4M3) {
+    MOE_NEED(xd_scale); MOE_NEED(h_scale);
+    MOE_HIP(moe::launch_dispatch_fp8(x, row_of, xd, xd_scale, h_scale, r.t0, r.t1, d->k, d->H,
+                                     (hipStream_t)stream), "dispatch_fp8");
+  } else {
+    MOE_HIP(moe::launch_dispatch(x, row_of, xd, r.t0, r.t1, d->k, (int64_t)d->H * elem_size(d->dtype),
+                                 (hipStream_t)stream), "dispatch");
+  }
+  return MOE_OK;
+}
+
+moe_status moe_expert_ffn(const moe_desc* d, int chunk, const void* xd, const float* xd_scale,
+                          const void* w1, const float* w1_scale, const void* w2, const float* w2_scale,
+                          const int32_t* offsets, void* gu, void* h, float* h_scale, void* yd,
+                          void* stream) {
+  MOE_TRY(validate(d));
+  MOE_TRY(check_chunk(d, chunk));
+  Range r = range_of(d, chunk);
+  if (rows_of(d) == 0) return MOE_OK;
+  MOE_NEED(xd); MOE_NEED(w1); MOE_NEED(w2); MOE_NEED(offsets); MOE_NEED(h); MOE_NEED(yd);
+  if (d->dtype == MOE_FP8_E4M3) {
+    MOE_NEED(xd_scale); MOE_NEED(w1_scale); MOE_NEED(w2_scale); MOE_NEED(h_scale);
+    MOE_HIP(moe::launch_expert_fwd_fp8(xd, xd_scale, w1, w1_scale, w2, w2_scale, offsets, h, h_scale,
+                                       yd, d->H, d->I, d->E_local, r.c0, r.nc, d->P_c,
+                                       (hipStream_t)stream), "expert_ffn_fp8");
+    return MOE_OK;
+  }
+  MOE_HIP(moe::launch_expert_fwd(is_bf16_rows(d), xd, w1, w2, offsets, gu, h, yd, d->H, d->I,
+                                 d->E_local, r.c0, r.nc, d->P_c, (hipStream_t)stream), "expert_ffn");
+  return MOE_OK;
+}
+
+moe_status moe_combine(const moe_desc* d, int chunk, const void* yd, const float* gates,
+                       const int32_t* row_of, void* out, void* stream) {
+  MOE_TRY(validate(d));
+  MOE_TRY(check_chunk(d, chunk));
+  Range r = range_of(d, chunk);
+  if (r.t1 <= r.t0) return MOE_OK;
+  MOE_NEED(gates); MOE_NEED(row_of); MOE_NEED(out);
+  if (rows_of(d) > 0) MOE_NEED(yd);
+  MOE_HIP(moe::launch_combine(is_bf16_rows(d), yd, gates, row_of, out, r.t0, r.t1, d->k,
+                              (int64_t)d->H * elem_size(d->dtype), (hipStream_t)stream), "combine");
+  return MOE_OK;
+}
+
+static moe_status no_fp8_bwd(const moe_desc* d) {
+  if (d->dtype == MOE_FP8_E4M3) return fail(MOE_ERR_UNSUPPORTED, "the FP8 payload path is forward only");
+  return MOE_OK;
+}
+
+moe_status moe_combine_bwd(const moe_desc* d, int chunk, const void* dy, const void* yd, const float* gates,
+                           const int32_t* row_of, void* dyd, float* dgates, void* stream) {
+  MOE_TRY(validate(d));
+  MOE_TRY(no_fp8_bwd(d));
+  MOE_TRY(check_chunk(d, chunk));
+  Range r = range_of(d, chunk);
+  if (r.t1 <= r.t0) return MOE_OK;
+  MOE_NEED(dy); MOE_NEED(gates); MOE_NEED(row_of); MOE_NEED(dgates);
+  if (rows_of(d) > 0) { MOE_NEED(yd); MOE_NEED(dyd); }
+  MOE_HIP(moe::launch_combine_bwd(is_bf16_rows(d), dy, yd, gates, row_of, dyd, dgates, r.t0, r.t1, d->k,
+                                  (int64_t)d->H * elem_size(d->dtype), (hipStream_t)stream), "combine_bwd");
+  return MOE_OK;
+}
+
+moe_status moe_route_bwd(const moe_desc* d, int chunk, const float* dgates, const float* gates,
+                         const int32_t* topk_idx, const void* x, float* dlogits, float* dwr_acc, void* dwr,
+                         void* workspace, void* stream) {
+  MOE_TRY(validate(d));
+  MOE_TRY(no_fp8_bwd(d));
+  MOE_TRY(check_chunk(d, chunk));
+  MOE_NEED(dwr_acc); MOE_NEED(workspace);
+  if (d->T > 0) { MOE_NEED(dgates); MOE_NEED(gates); MOE_NEED(topk_idx); MOE_NEED(x); MOE_NEED(dlogits); }
+  const int cfirst = chunk < 0 ? 0 : chunk, clast = chunk < 0 ? d->n_chunks - 1 : chunk;
+  if (clast == d->n_chunks - 1) MOE_NEED(dwr);
+  for (int c = cfirst; c <= clast; ++c) {
+    Range r = range_of(d, c);
+    MOE_HIP(moe::launch_route_bwd_dlogits(dgates, gates, topk_idx, dlogits, r.t0, r.t1, d->k, d->E,
+                                          (hipStream_t)stream), "route_bwd_dlogits");
+    MOE_HIP(moe::launch_router_wgrad(is_bf16_rows(d), dlogits, x, (float*)workspace, dwr_acc, c == 0,
+                                     c == d->n_chunks - 1 ? dwr : nullptr, r.t0, r.t1, d->E, d->H,
+                                     (hipStream_t)stream), "router_wgrad");
+  }
+  return MOE_OK;
+}
+
+moe_status moe_expert_wgrad(const moe_desc* d, const void* dyd, const void* dgu, const void* xd, const void* h,
+                            const int32_t* offsets, void* dw1, void* dw2, void* stream) {
+  MOE_TRY(validate(d));
+  MOE_TRY(no_fp8_bwd(d));
+  if (d->E_local == 0) return MOE_OK;
+  MOE_NEED(offsets); MOE_NEED(dw1); MOE_NEED(dw2);
+  if (rows_of(d) > 0) { MOE_NEED(dyd); MOE_NEED(dgu); MOE_NEED(xd); MOE_NEED(h); }
+  MOE_HIP(moe::launch_expert_wgrad(is_bf16_rows(d), dyd, dgu, xd, h, offsets, dw1, dw2, d->H, d->I,
+                                   d->E_local, d->n_chunks, d->P_c, (hipStream_t)stream), "expert_wgrad");
+  return MOE_OK;
+}
+
+moe_status moe_expert_ffn_bwd(const moe_desc* d, int chunk, const void* dyd, const void* xd, const void* gu,
+                              const void* h, const void* w1, const void* w2, const int32_t* offsets,
+                              void* dgu, void* dxd, void* dw1, void* dw2, void* stream) {
+  MOE_TRY(validate(d));
+  MOE_TRY(no_fp8_bwd(d));
+  MOE_TRY(check_chunk(d, chunk));
+  if (d->E_local == 0) return MOE_OK;
+  Range r = range_of(d, chunk);
+  if (rows_of(d) == 0) return chunk < 0 ? moe_expert_wgrad(d, dyd, dgu, xd, h, offsets, dw1, dw2, stream) : MOE_OK;
+  MOE_NEED(dyd); MOE_NEED(gu); MOE_NEED(w1); MOE_NEED(w2); MOE_NEED(offsets); MOE_NEED(dgu); MOE_NEED(dxd);
+  MOE_HIP(moe::launch_expert_dgrad(is_bf16_rows(d), dyd, gu, w1, w2, offsets, dgu, dxd, d->H, d->I,
+                                   d->E_local, r.c0, r.nc, d->P_c, (hipStream_t)stream), "expert_dgrad");
+  if (chunk < 0) return moe_expert_wgrad(d, dyd, dgu, xd, h, offsets, dw1, dw2, stream);
+  return MOE_OK;
+}
+
+moe_status moe_dispatch_bwd(const moe_desc* d, int chunk, const void* dxd, const int32_t* row_of,
+                            const int32_t* topk_idx, const float* dlogits, const void* w_r, void* dx,
+                            void* stream) {
+  MOE_TRY(validate(d));
+  MOE_TRY(no_fp8_bwd(d));
+  MOE_TRY(check_chunk(d, chunk));
+  Range r = range_of(d, chunk);
+  if (r.t1 <= r.t0) return MOE_OK;
+  MOE_NEED(row_of); MOE_NEED(topk_idx); MOE_NEED(dlogits); MOE_NEED(w_r); MOE_NEED(dx);
+  if (rows_of(d) > 0) MOE_NEED(dxd);
+  MOE_HIP(moe::launch_dispatch_bwd(is_bf16_rows(d), dxd, row_of, topk_idx, dlogits, w_r, dx, r.t0, r.t1,
+                                   d->k, d->E, (int64_t)d->H * elem_size(d->dtype), (hipStream_t)stream),
+          "dispatch_bwd");
+  return MOE_OK;
+}
+
+moe_status moe_quantize_rows_fp8(int64_t rows, int32_t cols, const void* src_bf16, void* codes, float* scale,
+                                 void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 8) return fail(MOE_ERR_ARG, "rows/cols invalid (cols %% 8 == 0 required)");
+  if (rows == 0) return MOE_OK;
+  MOE_NEED(src_bf16); MOE_NEED(codes); MOE_NEED(scale);
+  MOE_HIP(moe::launch_quantize_rows_fp8(src_bf16, codes, scale, rows, cols, (hipStream_t)stream),
+          "quantize_rows_fp8");
+  return MOE_OK;
+}
+
+// ----------------------------------------------------------------------------- layer primitives
+
+static moe_status check_fwd_tensors(const moe_desc* d, const moe_tensors* t) {
+  if (!t) return fail(MOE_ERR_ARG, "tensors is NULL");
+  MOE_NEED(t->counts); MOE_NEED(t->offsets); MOE_NEED(t->workspace);
+  if (d->T > 0) {
+    MOE_NEED(t->x); MOE_NEED(t->logits); MOE_NEED(t->topk_idx); MOE_NEED(t->gates); MOE_NEED(t->row_of);
+    MOE_NEED(t->out);
+  }
+  if (rows_of(d) > 0) {
+    MOE_NEED(t->w1); MOE_NEED(t->w2); MOE_NEED(t->src_token); MOE_NEED(t->xd); MOE_NEED(t->h); MOE_NEED(t->yd);
+    if (d->dtype == MOE_FP8_E4M3) { MOE_NEED(t->xd_scale); MOE_NEED(t->h_scale); MOE_NEED(t->w1_scale); MOE_NEED(t->w2_scale); }
+  }
+  return MOE_OK;
+}
+
+static moe_status check_bwd_tensors(const moe_desc* d, const moe_tensors* t) {
+  MOE_TRY(no_fp8_bwd(d));
+  MOE_NEED(t->w_r); MOE_NEED(t->dwr_acc); MOE_NEED(t->dwr);
+  if (d->T > 0) { MOE_NEED(t->dy); MOE_NEED(t->dgates); MOE_NEED(t->dlogits); MOE_NEED(t->dx); }
+  if (rows_of(d) > 0) {
+    MOE_NEED(t->gu); MOE_NEED(t->dyd); MOE_NEED(t->dgu); MOE_NEED(t->dxd); MOE_NEED(t->dw1); MOE_NEED(t->dw2);
+  }
+  return MOE_OK;
+}
+
+// Forward schedule. aux: R0 D0 | R1 D1 C0 | R2 D2 C1 | ... ; compute: F0 | F1 | ...
+// (routing+dispatch of chunk c+1 overlap the expert GEMMs of chunk c; combine c after F c).
+static moe_status forward_sched(const moe_desc* d, const moe_tensors* t, hipStream_t cs, hipStream_t as) {
+  const int n = d->n_chunks;
+  const bool two = cs != as;
+  hipEvent_t* ev = nullptr;
+  MOE_TRY(events(2 * n + 2, &ev));
+  hipEvent_t ev_start = ev[0], ev_done = ev[1];
+  hipEvent_t* ev_disp = ev + 2;
+  hipEvent_t* ev_ffn = ev + 2 + n;
+  if (two) {
+    MOE_HIP(hipEventRecord(ev_start, cs), "hipEventRecord");
+    MOE_HIP(hipStreamWaitEvent(as, ev_start, 0), "hipStreamWaitEvent");
+  }
+  for (int c = 0; c < n; ++c) {
+    MOE_TRY(moe_route(d, c, t->logits, t->topk_idx, t->gates, t->counts, t->offsets, t->row_of, t->src_token,
+                      t->workspace, as));
+    MOE_TRY(moe_dispatch(d, c, t->x, t->row_of, t->xd, t->xd_scale, t->h_scale, as));
+    if (two) {
+      MOE_HIP(hipEventRecord(ev_disp[c], as), "hipEventRecord");
+      MOE_HIP(hipStreamWaitEvent(cs, ev_disp[c], 0), "hipStreamWaitEvent");
+    }
+    MOE_TRY(moe_expert_ffn(d, c, t->xd, t->xd_scale, t->w1, t->w1_scale, t->w2, t->w2_scale, t->offsets,
+                           t->gu, t->h, t->h_scale, t->yd, cs));
+    if (two) MOE_HIP(hipEventRecord(ev_ffn[c], cs), "hipEventRecord");
+    if (c >= 1) {
+      if (two) MOE_HIP(hipStreamWaitEvent(as, ev_ffn[c - 1], 0), "hipStreamWaitEvent");
+      MOE_TRY(moe_combine(d, c - 1, t->yd, t->gates, t->row_of, t->out, as));
+    }
+  }
+  if (two) MOE_HIP(hipStreamWaitEvent(as, ev_ffn[n - 1], 0), "hipStreamWaitEvent");
+  MOE_TRY(moe_combine(d, n - 1, t->yd, t->gates, t->row_of, t->out, as));
+  if (two) {
+    MOE_HIP(hipEventRecord(ev_done, as), "hipEventRecord");
+    MOE_HIP(hipStreamWaitEvent(cs, ev_done, 0), "hipStreamWaitEvent");
+  }
+  return MOE_OK;
+}
+
+// Backward schedule. aux: CB0 RB0 | CB1 RB1 DB0 | ... ; compute: DG0 | DG1 | ... | wgrad.
+// Every chunk's input-gradient work is issued before the expert weight gradients.
+static moe_status backward_sched(const moe_desc* d, const moe_tensors* t, hipStream_t cs, hipStream_t as) {
+  const int n = d->n_chunks;
+  const bool two = cs != as;
+  hipEvent_t* ev = nullptr;
+  MOE_TRY(events(4 * n + 4, &ev));
+  // events [2n+2, 4n+4): distinct from the forward schedule's [0, 2n+2)
+  hipEvent_t ev_start = ev[2 * n + 2], ev_done = ev[2 * n + 3];
+  hipEvent_t* cb = ev + 2 * n + 4;  // n events: combine/route backward of chunk c done
+  hipEvent_t* dg = ev + 3 * n + 4;  // n events: expert dgrad of chunk c done
+  if (two) {
+    MOE_HIP(hipEventRecord(ev_start, cs), "hipEventRecord");
+    MOE_HIP(hipStreamWaitEvent(as, ev_start, 0), "hipStreamWaitEvent");
+  }
+  for (int c = 0; c < n; ++c) {
+    MOE_TRY(moe_combine_bwd(d, c, t->dy, t->yd, t->gates, t->row_of, t->dyd, t->dgates, as));
+    MOE_TRY(moe_route_bwd(d, c, t->dgates, t->gates, t->topk_idx, t->x, t->dlogits, t->dwr_acc, t->dwr,
+                          t->workspace, as));
+    if (two) {
+      MOE_HIP(hipEventRecord(cb[c], as), "hipEventRecord");
+      MOE_HIP(hipStreamWaitEvent(cs, cb[c], 0), "hipStreamWaitEvent");
+    }
+    MOE_TRY(moe_expert_ffn_bwd(d, c, t->dyd, t->xd, t->gu, t->h, t->w1, t->w2, t->offsets, t->dgu, t->dxd,
+                               nullptr, nullptr, cs));
+    if (two) MOE_HIP(hipEventRecord(dg[c], cs), "hipEventRecord");
+    if (c >= 1) {
+      if (two) MOE_HIP(hipStreamWaitEvent(as, dg[c - 1], 0), "hipStreamWaitEvent");
+      MOE_TRY(moe_dispatch_bwd(d, c - 1, t->dxd, t->row_of, t->topk_idx, t->dlogits, t->w_r, t->dx, as));
+    }
+  }
+  if (two) MOE_HIP(hipStreamWaitEvent(as, dg[n - 1], 0), "hipStreamWaitEvent");
+  MOE_TRY(moe_dispatch_bwd(d, n - 1, t->dxd, t->row_of, t->topk_idx, t->dlogits, t->w_r, t->dx, as));
+  MOE_TRY(moe_expert_wgrad(d, t->dyd, t->dgu, t->xd, t->h, t->offsets, t->dw1, t->dw2, cs));
+  if (two) {
+    MOE_HIP(hipEventRecord(ev_done, as), "hipEventRecord");
+    MOE_HIP(hipStreamWaitEvent(cs, ev_done, 0), "hipStreamWaitEvent");
+  }
+  return MOE_OK;
+}
+
+moe_status moe_layer_forward(const moe_desc* d, const moe_tensors* t, void* compute_stream, void* aux_stream) {
+  MOE_TRY(validate(d));
+  MOE_TRY(check_fwd_tensors(d, t));
+  return forward_sched(d, t, (hipStream_t)compute_stream, (hipStream_t)aux_stream);
+}
+
+moe_status moe_layer_backward(const moe_desc* d, const moe_tensors* t, void* compute_stream, void* aux_stream) {
+  MOE_TRY(validate(d));
+  MOE_TRY(check_fwd_tensors(d, t));
+  MOE_TRY(check_bwd_tensors(d, t));
+  return backward_sched(d, t, (hipStream_t)compute_stream, (hipStream_t)aux_stream);
+}
+
+moe_status moe_layer_forward_backward(const moe_desc* d, const moe_tensors* t, void* compute_stream,
+                                      void* aux_stream) {
+  MOE_TRY(validate(d));
+  MOE_TRY(check_fwd_tensors(d, t));
+  MOE_TRY(check_bwd_tensors(d, t));
+  MOE_TRY(forward_sched(d, t, (hipStream_t)compute_stream, (hipStream_t)aux_stream));
+  return backward_sched(d, t, (hipStream_t)compute_stream, (hipStream_t)aux_stream);
+}
+
+// ----------------------------------------------------------------------------- extent tracker
+
+struct moe_extent_tracker {
+  std::map<int64_t, int64_t> live;  // handle -> rows
+  int64_t next = 1;
+};
+
+moe_extent_tracker* moe_extent_tracker_create(void) { return new (std::nothrow) moe_extent_tracker(); }
+void moe_extent_tracker_destroy(moe_extent_tracker* tr) { delete tr; }
+
+moe_status moe_extent_acquire(moe_extent_tracker* tr, int64_t rows, int64_t* handle) {
+  if (!tr || !handle) return fail(MOE_ERR_ARG, "tracker or handle pointer is NULL");
+  if (rows < 0) return fail(MOE_ERR_ARG, "rows = %lld is negative", (long long)rows);
+  *handle = tr->next++;
+  tr->live[*handle] = rows;
+  return MOE_OK;
+}
+
+moe_status moe_extent_release(moe_extent_tracker* tr, int64_t handle) {
+  if (!tr) return fail(MOE_ERR_ARG, "tracker is NULL");
+  auto it = tr->live.find(handle);
+  if (it == tr->live.end()) return fail(MOE_ERR_ARG, "handle %lld is not live", (long long)handle);
+  tr->live.erase(it);
+  return MOE_OK;
+}
+
+int64_t moe_extent_current(const moe_extent_tracker* tr, int64_t required_rows) {
+  int64_t m = required_rows < 0 ? 0 : required_rows;
+  if (tr)
+    for (const auto& kv : tr->live) m = kv.second > m ? kv.second : m;
+  return round4(m);
+}
+
+}  // extern "C"

@@ -1,0 +1,66 @@
+// Shared device helpers for the MoE layer-share kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define MOE_DEV __device__ __forceinline__
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+typedef __attribute__((ext_vector_type(4))) int i32x4_t;
+
+struct alignas(16) u32x4 { uint32_t x, y, z, w; };
+
+MOE_DEV float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// FP32 -> BF16, round to nearest even (NaN stays NaN).
+MOE_DEV uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+MOE_DEV uint32_t pack_bf2(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+// Element load/store helpers for payload types (float or uint16_t BF16 bits).
+template <typename T> MOE_DEV float ld_elem(const T* p);
+template <> MOE_DEV float ld_elem<float>(const float* p) { return *p; }
+template <> MOE_DEV float ld_elem<uint16_t>(const uint16_t* p) { return bf2f(*p); }
+template <typename T> MOE_DEV void st_elem(T* p, float v);
+template <> MOE_DEV void st_elem<float>(float* p, float v) { *p = v; }
+template <> MOE_DEV void st_elem<uint16_t>(uint16_t* p, float v) { *p = f2bf(v); }
+
+MOE_DEV float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
+
+MOE_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+MOE_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Token range of chunk c (chunks of ceil(T/n) tokens, the last takes the remainder).
+struct ChunkRange { int64_t t0, t1; };
+MOE_DEV ChunkRange chunk_range(int64_t T, int n, int c) {
+  int64_t tc = (T + n - 1) / n;
+  int64_t a = c * tc, b = a + tc;
+  if (a > T) a = T;
+  if (b > T) b = T;
+  return {a, b};
+}
+
+}  // namespace moe

@@ -1,0 +1,57 @@
+// Internal kernel launchers (host side). Every launcher enqueues on `s` and returns the HIP
+// launch status; none allocates memory or synchronises.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// routing
+int route_blocks_per_chunk(int64_t T, int n);
+int64_t route_scratch_bytes(int64_t T, int n, int E);
+hipError_t launch_route(const float* logits, int32_t* topk_idx, float* gates, int32_t* counts,
+                        int32_t* offsets, int32_t* row_of, int32_t* src_token, int32_t* scratch,
+                        int64_t T, int E, int e0, int El, int K, int n, int chunk0, int nchunks,
+                        int64_t P_c, hipStream_t s);
+
+// row copies
+hipError_t launch_dispatch(const void* x, const int32_t* row_of, void* xd, int64_t t0, int64_t t1,
+                           int K, int64_t row_bytes, hipStream_t s);
+hipError_t launch_dispatch_fp8(const void* x, const int32_t* row_of, void* xd, float* xd_scale,
+                               float* h_scale, int64_t t0, int64_t t1, int K, int H, hipStream_t s);
+hipError_t launch_quantize_rows_fp8(const void* src, void* codes, float* scale, int64_t rows,
+                                    int cols, hipStream_t s);
+hipError_t launch_combine(bool bf16, const void* yd, const float* gates, const int32_t* row_of,
+                          void* out, int64_t t0, int64_t t1, int K, int64_t row_bytes, hipStream_t s);
+hipError_t launch_combine_bwd(bool bf16, const void* dy, const void* yd, const float* gates,
+                              const int32_t* row_of, void* dyd, float* dgates, int64_t t0,
+                              int64_t t1, int K, int64_t row_bytes, hipStream_t s);
+hipError_t launch_route_bwd_dlogits(const float* dgates, const float* gates, const int32_t* idx,
+                                    float* dlogits, int64_t t0, int64_t t1, int K, int E,
+                                    hipStream_t s);
+hipError_t launch_dispatch_bwd(bool bf16, const void* dxd, const int32_t* row_of, const int32_t* idx,
+                               const float* dlogits, const void* w_r, void* dx, int64_t t0,
+                               int64_t t1, int K, int E, int64_t row_bytes, hipStream_t s);
+
+// grouped GEMMs
+hipError_t launch_expert_fwd(bool bf16, const void* xd, const void* w1, const void* w2,
+                             const int32_t* offsets, void* gu, void* h, void* yd, int H, int I,
+                             int El, int c0, int nc, int64_t P_c, hipStream_t s);
+hipError_t launch_expert_fwd_fp8(const void* xd, const float* xd_scale, const void* w1,
+                                 const float* w1_scale, const void* w2, const float* w2_scale,
+                                 const int32_t* offsets, void* h, float* h_scale, void* yd, int H,
+                                 int I, int El, int c0, int nc, int64_t P_c, hipStream_t s);
+hipError_t launch_expert_dgrad(bool bf16, const void* dyd, const void* gu, const void* w1,
+                               const void* w2, const int32_t* offsets, void* dgu, void* dxd, int H,
+                               int I, int El, int c0, int nc, int64_t P_c, hipStream_t s);
+hipError_t launch_expert_wgrad(bool bf16, const void* dyd, const void* dgu, const void* xd,
+                               const void* h, const int32_t* offsets, void* dw1, void* dw2, int H,
+                               int I, int El, int n, int64_t P_c, hipStream_t s);
+int router_ksplit(int64_t tokens);
+int64_t router_partials_bytes(int64_t Tc, int E, int H);
+hipError_t launch_router_wgrad(bool bf16, const float* dlogits, const void* x, float* partials,
+                               float* dwr_acc, bool first, void* dwr, int64_t t0, int64_t t1, int E,
+                               int H, hipStream_t s);
+
+}  // namespace moe

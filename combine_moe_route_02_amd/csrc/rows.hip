@@ -1,0 +1,419 @@
+// Row-copy kernels of the layer share: dispatch, combine and their transposes, plus the
+// per-token part of the routing backward. All are HBM-bound: one wave owns one token, its
+// lanes cover the hidden dimension with 16-byte vectors (coalesced 1 KiB per wave access),
+// every index is 64-bit, and each token row is read once.
+//
+// torchtitan PR 5541 ("AI-Generated Details") describes its BF16/FP8 row-copy kernels with
+// multi-row tiles, tail masks and 64-bit addressing; these kernels keep those properties for the
+// gather/scatter between token order and expert-contiguous order. ART PR 971 (description)
+// gives combine's fresh [P, H] output cropped to the logical rows: only rows t < T are written.
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+constexpr int kTokPerBlock = 4;   // one wave per token
+constexpr int kBatch = 4;         // 16-byte vectors per lane kept in flight
+
+// ---------------------------------------------------------------------------------------------
+// Dispatch (F32 / BF16): scatter x[t] to xd[row_of[t][j]] for every local slot; bitwise copy.
+__global__ __launch_bounds__(256) void dispatch_copy_kernel(
+    const u32x4* __restrict__ x, const int32_t* __restrict__ row_of, u32x4* __restrict__ xd,
+    int64_t t0, int64_t t1, int K, int64_t nvec) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = t0 + (int64_t)blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
+  if (t >= t1) return;
+  const int32_t myrow = lane < K ? row_of[t * K + lane] : -1;
+  if (__ballot(myrow >= 0) == 0) return;  // token has no local expert: not read at all
+  const u32x4* src = x + t * nvec;
+  for (int64_t v0 = 0; v0 < nvec; v0 += 64 * kBatch) {
+    u32x4 v[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      int64_t i = v0 + b * 64 + lane;
+      if (i < nvec) v[b] = src[i];
+    }
+    for (int j = 0; j < K; ++j) {
+      int32_t r = __shfl(myrow, j, 64);
+      if (r < 0) continue;
+      u32x4* dst = xd + (int64_t)r * nvec;
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        int64_t i = v0 + b * 64 + lane;
+        if (i < nvec) dst[i] = v[b];
+      }
+    }
+  }
+}
+
+// FP8 conversion: OCP e4m3fn, round to nearest even; inputs are already within +-448.
+MOE_DEV uint32_t pack_fp8x4(float a, float b, float c, float d) {
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+  return (uint32_t)r;
+}
+
+MOE_DEV float clamp448(float v) { return fminf(fmaxf(v, -448.f), 448.f); }
+
+// Quantise one 16-byte BF16 vector (8 values) with multiplier inv -> 8 e4m3 codes.
+MOE_DEV uint2 quant8(const u32x4& v, float inv) {
+  float f[8] = {bf2f(v.x & 0xffff), bf2f(v.x >> 16), bf2f(v.y & 0xffff), bf2f(v.y >> 16),
+                bf2f(v.z & 0xffff), bf2f(v.z >> 16), bf2f(v.w & 0xffff), bf2f(v.w >> 16)};
+  uint2 q;
+  q.x = pack_fp8x4(clamp448(f[0] * inv), clamp448(f[1] * inv), clamp448(f[2] * inv), clamp448(f[3] * inv));
+  q.y = pack_fp8x4(clamp448(f[4] * inv), clamp448(f[5] * inv), clamp448(f[6] * inv), clamp448(f[7] * inv));
+  return q;
+}
+
+MOE_DEV float absmax8(const u32x4& v) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m = fmaxf(m, fabsf(bf2f(w[i] & 0xffff)));
+    m = fmaxf(m, fabsf(bf2f(w[i] >> 16)));
+  }
+  return m;
+}
+
+// Dispatch (FP8): per token absmax over the BF16 row, codes = e4m3(x * (448/amax)),
+// xd_scale[row] = amax/448 (1 for a zero row); h_scale[row] cleared. Row of <= 16 vectors/lane.
+constexpr int kFp8MaxVec = 16;
+__global__ __launch_bounds__(256) void dispatch_fp8_kernel(
+    const u32x4* __restrict__ x, const int32_t* __restrict__ row_of, uint2* __restrict__ xd,
+    float* __restrict__ xd_scale, float* __restrict__ h_scale, int64_t t0, int64_t t1, int K,
+    int64_t nvec) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = t0 + (int64_t)blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
+  if (t >= t1) return;
+  const int32_t myrow = lane < K ? row_of[t * K + lane] : -1;
+  if (__ballot(myrow >= 0) == 0) return;
+  const u32x4* src = x + t * nvec;
+  u32x4 v[kFp8MaxVec];
+  float m = 0.f;
+#pragma unroll
+  for (int b = 0; b < kFp8MaxVec; ++b) {
+    int64_t i = b * 64 + lane;
+    if (i < nvec) { v[b] = src[i]; m = fmaxf(m, absmax8(v[b])); }
+  }
+  const float amax = wave_max(m);
+  const float inv = amax > 0.f ? 448.0f / amax : 0.f;
+  const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+  uint2 q[kFp8MaxVec];
+#pragma unroll
+  for (int b = 0; b < kFp8MaxVec; ++b) {
+    int64_t i = b * 64 + lane;
+    if (i < nvec) q[b] = quant8(v[b], inv);
+  }
+  for (int j = 0; j < K; ++j) {
+    int32_t r = __shfl(myrow, j, 64);
+    if (r < 0) continue;
+    uint2* dst = xd + (int64_t)r * nvec;
+#pragma unroll
+    for (int b = 0; b < kFp8MaxVec; ++b) {
+      int64_t i = b * 64 + lane;
+      if (i < nvec) dst[i] = q[b];
+    }
+    if (lane == 0) { xd_scale[r] = scale; h_scale[r] = 0.f; }
+  }
+}
+
+// Row quantisation of a [rows, cols] BF16 matrix (weights), same FP32 steps as dispatch.
+__global__ __launch_bounds__(256) void quantize_rows_fp8_kernel(
+    const u32x4* __restrict__ src, uint2* __restrict__ codes, float* __restrict__ scale,
+    int64_t rows, int64_t nvec) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const u32x4* s = src + r * nvec;
+  float m = 0.f;
+  for (int64_t i = lane; i < nvec; i += 64) m = fmaxf(m, absmax8(s[i]));
+  const float amax = wave_max(m);
+  const float inv = amax > 0.f ? 448.0f / amax : 0.f;
+  for (int64_t i = lane; i < nvec; i += 64) codes[r * nvec + i] = quant8(s[i], inv);
+  if (lane == 0) scale[r] = amax > 0.f ? amax / 448.0f : 1.0f;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Vector helpers over a 16-byte payload vector: 4 FP32 or 8 BF16 values.
+template <typename T> struct Vec;
+template <> struct Vec<float> {
+  static constexpr int N = 4;
+  MOE_DEV static void to_f(const u32x4& v, float* f) {
+    f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+  }
+  MOE_DEV static u32x4 from_f(const float* f) {
+    return {__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])};
+  }
+};
+template <> struct Vec<uint16_t> {
+  static constexpr int N = 8;
+  MOE_DEV static void to_f(const u32x4& v, float* f) {
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { f[2 * i] = bf2f(w[i] & 0xffff); f[2 * i + 1] = bf2f(w[i] >> 16); }
+  }
+  MOE_DEV static u32x4 from_f(const float* f) {
+    return {pack_bf2(f[0], f[1]), pack_bf2(f[2], f[3]), pack_bf2(f[4], f[5]), pack_bf2(f[6], f[7])};
+  }
+};
+
+// Combine: out[t] = RNE(sum_j g_tj * yd[row_of[t][j]]), FP32 accumulation, j ascending.
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(
+    const u32x4* __restrict__ yd, const float* __restrict__ gates, const int32_t* __restrict__ row_of,
+    u32x4* __restrict__ out, int64_t t0, int64_t t1, int K, int64_t nvec) {
+  using V = Vec<T>;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = t0 + (int64_t)blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
+  if (t >= t1) return;
+  const int32_t myrow = lane < K ? row_of[t * K + lane] : -1;
+  const float mygate = lane < K ? gates[t * K + lane] : 0.f;
+  for (int64_t v0 = 0; v0 < nvec; v0 += 64 * kBatch) {
+    float acc[kBatch][V::N];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b)
+#pragma unroll
+      for (int q = 0; q < V::N; ++q) acc[b][q] = 0.f;
+    for (int j = 0; j < K; ++j) {
+      int32_t r = __shfl(myrow, j, 64);
+      if (r < 0) continue;
+      float g = __shfl(mygate, j, 64);
+      const u32x4* src = yd + (int64_t)r * nvec;
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        int64_t i = v0 + b * 64 + lane;
+        if (i < nvec) {
+          float f[V::N];
+          V::to_f(src[i], f);
+#pragma unroll
+          for (int q = 0; q < V::N; ++q) acc[b][q] = fmaf(g, f[q], acc[b][q]);
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      int64_t i = v0 + b * 64 + lane;
+      if (i < nvec) out[t * nvec + i] = V::from_f(acc[b]);
+    }
+  }
+}
+
+// Combine backward: dyd[row_of[t][j]] = g_tj * dy[t]; dgates[t][j] = <dy[t], yd[row]> (FP32).
+template <typename T>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(
+    const u32x4* __restrict__ dy, const u32x4* __restrict__ yd, const float* __restrict__ gates,
+    const int32_t* __restrict__ row_of, u32x4* __restrict__ dyd, float* __restrict__ dgates,
+    int64_t t0, int64_t t1, int K, int64_t nvec) {
+  using V = Vec<T>;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = t0 + (int64_t)blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
+  if (t >= t1) return;
+  const int32_t myrow = lane < K ? row_of[t * K + lane] : -1;
+  const float mygate = lane < K ? gates[t * K + lane] : 0.f;
+  const bool any = __ballot(myrow >= 0) != 0;
+  float dg[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) dg[j] = 0.f;
+  if (any) {
+    for (int64_t v0 = 0; v0 < nvec; v0 += 64 * kBatch) {
+      float d[kBatch][V::N];
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        int64_t i = v0 + b * 64 + lane;
+        if (i < nvec) V::to_f(dy[t * nvec + i], d[b]);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j >= K) break;
+        int32_t r = __shfl(myrow, j, 64);
+        if (r < 0) continue;
+        float g = __shfl(mygate, j, 64);
+        const u32x4* src = yd + (int64_t)r * nvec;
+        u32x4* dst = dyd + (int64_t)r * nvec;
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+          int64_t i = v0 + b * 64 + lane;
+          if (i < nvec) {
+            float f[V::N], o[V::N];
+            V::to_f(src[i], f);
+#pragma unroll
+            for (int q = 0; q < V::N; ++q) { dg[j] = fmaf(d[b][q], f[q], dg[j]); o[q] = g * d[b][q]; }
+            dst[i] = V::from_f(o);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= K) break;
+    float s = wave_sum(dg[j]);
+    int32_t r = __shfl(myrow, j, 64);
+    if (lane == 0) dgates[t * K + j] = (r >= 0) ? s : 0.f;
+  }
+}
+
+// Route backward, per token: dlogits[t][e] = g_j (dg_j - sum_i g_i dg_i) where e = idx[t][j],
+// zero for every other expert (the full row of E columns is written).
+__global__ __launch_bounds__(256) void route_bwd_dlogits_kernel(
+    const float* __restrict__ dgates, const float* __restrict__ gates, const int32_t* __restrict__ idx,
+    float* __restrict__ dlogits, int64_t t0, int64_t t1, int K, int E) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = t0 + (int64_t)blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
+  if (t >= t1) return;
+  const float g = lane < K ? gates[t * K + lane] : 0.f;
+  const float d = lane < K ? dgates[t * K + lane] : 0.f;
+  const int id = lane < K ? idx[t * K + lane] : -1;
+  float s = 0.f;  // sum_i g_i dg_i, slots in ascending order
+  for (int j = 0; j < K; ++j) s = fmaf(__shfl(g, j, 64), __shfl(d, j, 64), s);
+  const float dl = g * (d - s);
+  for (int e = lane; e < E; e += 64) {
+    float v = 0.f;
+    for (int j = 0; j < K; ++j) {
+      int ej = __shfl(id, j, 64);
+      float dj = __shfl(dl, j, 64);
+      v = (ej == e) ? dj : v;
+    }
+    dlogits[t * E + e] = v;
+  }
+}
+
+// Dispatch backward: dx[t] = RNE(sum_j local dxd[row_of[t][j]] + sum_j dlogits[t][e_j] W_r[e_j]).
+template <typename T>
+__global__ __launch_bounds__(256) void dispatch_bwd_kernel(
+    const u32x4* __restrict__ dxd, const int32_t* __restrict__ row_of, const int32_t* __restrict__ idx,
+    const float* __restrict__ dlogits, const u32x4* __restrict__ w_r, u32x4* __restrict__ dx,
+    int64_t t0, int64_t t1, int K, int E, int64_t nvec) {
+  using V = Vec<T>;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = t0 + (int64_t)blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
+  if (t >= t1) return;
+  const int32_t myrow = lane < K ? row_of[t * K + lane] : -1;
+  const int myid = lane < K ? idx[t * K + lane] : 0;
+  const float mydl = lane < K ? dlogits[t * E + myid] : 0.f;
+  for (int64_t v0 = 0; v0 < nvec; v0 += 64 * kBatch) {
+    float acc[kBatch][V::N];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b)
+#pragma unroll
+      for (int q = 0; q < V::N; ++q) acc[b][q] = 0.f;
+    for (int j = 0; j < K; ++j) {
+      int32_t r = __shfl(myrow, j, 64);
+      if (r < 0) continue;
+      const u32x4* src = dxd + (int64_t)r * nvec;
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        int64_t i = v0 + b * 64 + lane;
+        if (i < nvec) {
+          float f[V::N];
+          V::to_f(src[i], f);
+#pragma unroll
+          for (int q = 0; q < V::N; ++q) acc[b][q] += f[q];
+        }
+      }
+    }
+    for (int j = 0; j < K; ++j) {
+      int e = __shfl(myid, j, 64);
+      float dl = __shfl(mydl, j, 64);
+      const u32x4* wr = w_r + (int64_t)e * nvec;
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        int64_t i = v0 + b * 64 + lane;
+        if (i < nvec) {
+          float f[V::N];
+          V::to_f(wr[i], f);
+#pragma unroll
+          for (int q = 0; q < V::N; ++q) acc[b][q] = fmaf(dl, f[q], acc[b][q]);
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      int64_t i = v0 + b * 64 + lane;
+      if (i < nvec) dx[t * nvec + i] = V::from_f(acc[b]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Launchers. Token range [t0, t1); nvec = 16-byte vectors per row.
+static inline dim3 tok_grid(int64_t ntok) { return dim3((unsigned)((ntok + kTokPerBlock - 1) / kTokPerBlock)); }
+
+hipError_t launch_dispatch(const void* x, const int32_t* row_of, void* xd, int64_t t0, int64_t t1,
+                           int K, int64_t row_bytes, hipStream_t s) {
+  if (t1 <= t0) return hipSuccess;
+  hipLaunchKernelGGL(dispatch_copy_kernel, tok_grid(t1 - t0), dim3(256), 0, s, (const u32x4*)x,
+                     row_of, (u32x4*)xd, t0, t1, K, row_bytes / 16);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_fp8(const void* x, const int32_t* row_of, void* xd, float* xd_scale,
+                               float* h_scale, int64_t t0, int64_t t1, int K, int H, hipStream_t s) {
+  if (t1 <= t0) return hipSuccess;
+  hipLaunchKernelGGL(dispatch_fp8_kernel, tok_grid(t1 - t0), dim3(256), 0, s, (const u32x4*)x,
+                     row_of, (uint2*)xd, xd_scale, h_scale, t0, t1, K, (int64_t)H / 8);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_rows_fp8(const void* src, void* codes, float* scale, int64_t rows,
+                                    int cols, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_rows_fp8_kernel, tok_grid(rows), dim3(256), 0, s, (const u32x4*)src,
+                     (uint2*)codes, scale, rows, (int64_t)cols / 8);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(bool bf16, const void* yd, const float* gates, const int32_t* row_of,
+                          void* out, int64_t t0, int64_t t1, int K, int64_t row_bytes, hipStream_t s) {
+  if (t1 <= t0) return hipSuccess;
+  if (bf16)
+    hipLaunchKernelGGL(combine_kernel<uint16_t>, tok_grid(t1 - t0), dim3(256), 0, s,
+                       (const u32x4*)yd, gates, row_of, (u32x4*)out, t0, t1, K, row_bytes / 16);
+  else
+    hipLaunchKernelGGL(combine_kernel<float>, tok_grid(t1 - t0), dim3(256), 0, s,
+                       (const u32x4*)yd, gates, row_of, (u32x4*)out, t0, t1, K, row_bytes / 16);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_bwd(bool bf16, const void* dy, const void* yd, const float* gates,
+                              const int32_t* row_of, void* dyd, float* dgates, int64_t t0,
+                              int64_t t1, int K, int64_t row_bytes, hipStream_t s) {
+  if (t1 <= t0) return hipSuccess;
+  if (bf16)
+    hipLaunchKernelGGL(combine_bwd_kernel<uint16_t>, tok_grid(t1 - t0), dim3(256), 0, s,
+                       (const u32x4*)dy, (const u32x4*)yd, gates, row_of, (u32x4*)dyd, dgates,
+                       t0, t1, K, row_bytes / 16);
+  else
+    hipLaunchKernelGGL(combine_bwd_kernel<float>, tok_grid(t1 - t0), dim3(256), 0, s,
+                       (const u32x4*)dy, (const u32x4*)yd, gates, row_of, (u32x4*)dyd, dgates,
+                       t0, t1, K, row_bytes / 16);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_bwd_dlogits(const float* dgates, const float* gates, const int32_t* idx,
+                                    float* dlogits, int64_t t0, int64_t t1, int K, int E,
+                                    hipStream_t s) {
+  if (t1 <= t0) return hipSuccess;
+  hipLaunchKernelGGL(route_bwd_dlogits_kernel, tok_grid(t1 - t0), dim3(256), 0, s, dgates, gates,
+                     idx, dlogits, t0, t1, K, E);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_bwd(bool bf16, const void* dxd, const int32_t* row_of, const int32_t* idx,
+                               const float* dlogits, const void* w_r, void* dx, int64_t t0,
+                               int64_t t1, int K, int E, int64_t row_bytes, hipStream_t s) {
+  if (t1 <= t0) return hipSuccess;
+  if (bf16)
+    hipLaunchKernelGGL(dispatch_bwd_kernel<uint16_t>, tok_grid(t1 - t0), dim3(256), 0, s,
+                       (const u32x4*)dxd, row_of, idx, dlogits, (const u32x4*)w_r, (u32x4*)dx,
+                       t0, t1, K, E, row_bytes / 16);
+  else
+    hipLaunchKernelGGL(dispatch_bwd_kernel<float>, tok_grid(t1 - t0), dim3(256), 0, s,
+                       (const u32x4*)dxd, row_of, idx, dlogits, (const u32x4*)w_r, (u32x4*)dx,
+                       t0, t1, K, E, row_bytes / 16);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,238 @@
+/*
+ * moe.h -- C ABI of one GPU's share of a Mixture-of-Experts layer on MI355X (gfx950).
+ *
+ * The layer share is: top-k routing over FP32 router logits, dispatch of token rows into
+ * expert-contiguous rows, a grouped SwiGLU expert FFN, and combine (gate-weighted
+ * gather-reduce back to token order into a fresh [P_out, H] output cropped to the logical
+ * rows), forward and backward, processed in token-wise chunks.
+ *
+ * Sources (the pages the operation comes from; they print no formula, so each call states the
+ * reading it implements):
+ *   - token-wise ChunkedEP, Megatron-LM PR 7342, "Summary": three primitives (forward,
+ *     backward, fused forward/backward), caller-owned output and dgrad buffers, tokens split
+ *     into chunks so one chunk's dispatch overlaps another chunk's expert compute;
+ *     "Numerical status -- unresolved": router weight gradients accumulate across chunks in
+ *     FP32 before a single dtype conversion; "Tests and limitations": no router auxiliary loss.
+ *   - "Price HybridEP recompute outputs at the live communication extent", OpenPipe/ART PR 971
+ *     (description and review comments): combine writes a fresh [P, H] output at the live
+ *     communication extent, rounded up to four rows, cropped to the logical rows by the caller;
+ *     while an earlier larger graph is live its extent is kept as a high-water mark.
+ *   - torchtitan PR 5541 (paged stash for HybridEP), "AI-Generated Details": multi-row tiles,
+ *     tail masks and 64-bit addressing for BF16/FP8 row payloads.
+ *   - "[graph_trainer] Overlap HybridEP and paging across combined PP graphs" (torchtitan
+ *     PR 5542), "Verification": input-gradient work is issued before expert weight gradients.
+ *
+ * Conventions for every call below
+ *   - Pointers named as device buffers are device (HBM) addresses, caller-owned; the library
+ *     never allocates device memory and never synchronises the host. `stream` is a hipStream_t
+ *     passed as void* (NULL = the null stream).
+ *   - Host-side validation happens before any launch; on a non-OK status nothing was launched
+ *     and moe_last_error() returns a thread-local message. MOE_ERR_HIP reports a launch error.
+ *   - `chunk` selects one token chunk c in [0, n_chunks), or -1 for every chunk in order.
+ *     Chunk c holds tokens [c*Tc, min(T, (c+1)*Tc)) with Tc = ceil(T / n_chunks), and owns the
+ *     dispatch rows [c*P_c, (c+1)*P_c).
+ *   - All arrays are row-major and dense. Element types depend on desc.dtype:
+ *        tensor                         MOE_F32   MOE_BF16   MOE_FP8_E4M3 (forward only)
+ *        x, dy, dx, W_r, dwr            f32       bf16       bf16 (x), -
+ *        xd                             f32       bf16       e4m3 codes + xd_scale f32 [P]
+ *        W1, W2                         f32       bf16       e4m3 codes + w1_scale [E_l,2I],
+ *                                                            w2_scale [E_l,H] (f32)
+ *        gu, h, yd, dyd, dgu, dxd       f32       bf16       h: bf16 and h_scale f32 [P]; yd bf16
+ *        out                            f32       bf16       bf16
+ *        dw1, dw2                       f32       bf16       -
+ *     logits, gates, dgates, dlogits, dwr_acc are always f32; every index array is int32.
+ *   - Shapes: logits [T,E]; topk_idx, gates, row_of, dgates [T,k]; counts [n,E];
+ *     offsets [n,E_l+1]; src_token [P]; xd, yd, dyd, dxd [P,H]; gu, dgu [P,2I]; h [P,I];
+ *     out [P_out,H]; W1, dw1 [E_l,2I,H] (rows 0..I-1 gate, I..2I-1 up); W2, dw2 [E_l,H,I];
+ *     W_r, dwr, dwr_acc [E,H]; dlogits [T,E]; with P = n_chunks * P_c.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_ARG = -1,         /* null pointer, bad chunk index, inconsistent shape */
+  MOE_ERR_CAPACITY = -2,    /* P_c / P_out not a multiple of 4 or below the static minimum */
+  MOE_ERR_UNSUPPORTED = -3, /* shape or dtype outside what the kernels handle */
+  MOE_ERR_HIP = -4          /* a HIP launch/runtime error; message in moe_last_error() */
+} moe_status;
+
+/* Layer-share descriptor.
+ *   T         logical tokens on this GPU (>= 0)
+ *   H, I      hidden and expert intermediate size (multiples of 64)
+ *   E         router width (all experts, 1..1024); e0, E_local: local experts [e0, e0+E_local)
+ *   k         top-k (1..8, <= E)
+ *   n_chunks  token-wise chunks (>= 1)
+ *   P_c       dispatch rows per chunk region: multiple of 4, >= ceil(T/n)*min(k, E_local)
+ *             (the static worst case, so no count ever returns to the host)
+ *   P_out     combine output rows: multiple of 4, >= T (rows T..P_out-1 are never written)
+ *   dtype     moe_dtype of the payloads (table above) */
+typedef struct moe_desc {
+  int64_t T;
+  int32_t H, I, E, e0, E_local, k, n_chunks;
+  int64_t P_c;
+  int64_t P_out;
+  int32_t dtype;
+  int32_t reserved; /* must be 0 */
+} moe_desc;
+
+/* ---------------------------------------------------------------------------------------
+ * Stage calls
+ * ------------------------------------------------------------------------------------- */
+
+/* Routing (ChunkedEP "Summary": top-k routing per token chunk; no auxiliary loss).
+ * Per token: the k largest logits (ties to the lower expert index, NaN ranks lowest), slot 0
+ * the largest; gates = softmax over the k selected logits (= full softmax, top-k,
+ * renormalise). counts[c][e] = slots of chunk c choosing expert e (all E experts);
+ * offsets[c] = exclusive prefix sum over the local experts' counts, offsets[c][E_l] = N_c;
+ * row_of[t][j] = c*P_c + offsets[c][e-e0] + (number of earlier tokens of chunk c choosing e),
+ * -1 for a non-local expert; src_token[row] = the row's token, -1 for rows N_c..P_c-1.
+ * workspace: device scratch of moe_workspace_bytes().route_scratch bytes (contents undefined
+ * on return). Bit-exact and deterministic (no order-dependent atomics). */
+moe_status moe_route(const moe_desc* d, int chunk, const float* logits, int32_t* topk_idx,
+                     float* gates, int32_t* counts, int32_t* offsets, int32_t* row_of,
+                     int32_t* src_token, void* workspace, void* stream);
+
+/* Dispatch: xd[row_of[t][j]] = x[t] for every local slot (a bitwise row copy for F32/BF16;
+ * each touched token row is read once). FP8: per token amax over the BF16 row,
+ * xd = e4m3(x * (448/amax)) with FP32 steps, RNE, saturating; xd_scale[row] = amax/448 (1 for
+ * an all-zero row); h_scale[row] is cleared for the FFN's row maxima. Rows N_c..P_c-1 are not
+ * written. xd_scale/h_scale may be NULL unless dtype is FP8. */
+moe_status moe_dispatch(const moe_desc* d, int chunk, const void* x, const int32_t* row_of,
+                        void* xd, float* xd_scale, float* h_scale, void* stream);
+
+/* Grouped SwiGLU expert FFN over every local expert's rows [c*P_c + offsets[c][e],
+ * c*P_c + offsets[c][e+1]): G = xd W1g^T, U = xd W1u^T (FP32 accumulation),
+ * h = silu(G) * U with silu(z) = z/(1+exp(-z)), yd = h W2^T. gu (may be NULL) saves G and U
+ * for the backward ([P,2I], G in columns 0..I-1). h is required ([P,I]). FP8: GEMMs on FP8
+ * MFMA with dequantisation s_row*s_col; h is kept in BF16 with its row absmax in h_scale and
+ * is quantised per row to e4m3 on the way into the down projection. */
+moe_status moe_expert_ffn(const moe_desc* d, int chunk, const void* xd, const float* xd_scale,
+                          const void* w1, const float* w1_scale, const void* w2,
+                          const float* w2_scale, const int32_t* offsets, void* gu, void* h,
+                          float* h_scale, void* yd, void* stream);
+
+/* Combine (ART PR 971: fresh [P, H] output cropped to the logical rows):
+ * out[t] = RNE( sum over local slots j, ascending, of gates[t][j] * yd[row_of[t][j]] ) with
+ * FP32 accumulation; a token without a local expert gets a zero row. Writes rows of the chunk
+ * only; rows T..P_out-1 are left untouched. */
+moe_status moe_combine(const moe_desc* d, int chunk, const void* yd, const float* gates,
+                       const int32_t* row_of, void* out, void* stream);
+
+/* Combine backward: dyd[row_of[t][j]] = gates[t][j] * dy[t] (rounded once to the payload
+ * type); dgates[t][j] = <dy[t], yd[row_of[t][j]]> in FP32, 0 for non-local slots. */
+moe_status moe_combine_bwd(const moe_desc* d, int chunk, const void* dy, const void* yd,
+                           const float* gates, const int32_t* row_of, void* dyd, float* dgates,
+                           void* stream);
+
+/* Route backward (ChunkedEP "Numerical status": FP32 accumulation across chunks, then one
+ * conversion). dlogits[t][idx[t][j]] = g_j * (dg_j - sum_i g_i dg_i), zero for unselected
+ * experts (all E columns written for the chunk's rows). Router weight gradient of the
+ * caller's projection logits = x W_r^T: the chunk's dlogits^T x is computed in FP32 (dlogits
+ * split into a BF16 high and low part, x exact) and stored into dwr_acc for the first chunk,
+ * added to it for later chunks; after the last chunk (or chunk = -1) dwr = dwr_acc converted
+ * once (RNE) to the payload type. workspace: moe_workspace_bytes().route_bwd_scratch bytes. */
+moe_status moe_route_bwd(const moe_desc* d, int chunk, const float* dgates, const float* gates,
+                         const int32_t* topk_idx, const void* x, float* dlogits, float* dwr_acc,
+                         void* dwr, void* workspace, void* stream);
+
+/* Expert FFN backward, input-gradient part, per chunk: dh = dyd W2; with s = sigmoid(G):
+ * dG = dh * U * s * (1 + G (1 - s)), dU = dh * silu(G) (G, U read from gu);
+ * dxd = [dG dU] W1. With chunk = -1 it then runs moe_expert_wgrad over every chunk. */
+moe_status moe_expert_ffn_bwd(const moe_desc* d, int chunk, const void* dyd, const void* xd,
+                              const void* gu, const void* h, const void* w1, const void* w2,
+                              const int32_t* offsets, void* dgu, void* dxd, void* dw1, void* dw2,
+                              void* stream);
+
+/* Expert weight gradients over the rows of every chunk in one FP32 reduction, converted once:
+ * dW2[e] = sum_rows dyd^T h, dW1[e] = sum_rows dgu^T xd; an expert with no rows gets zeros. */
+moe_status moe_expert_wgrad(const moe_desc* d, const void* dyd, const void* dgu, const void* xd,
+                            const void* h, const int32_t* offsets, void* dw1, void* dw2,
+                            void* stream);
+
+/* Dispatch backward: dx[t] = RNE( sum over local slots of dxd[row_of[t][j]]
+ * + sum_j dlogits[t][idx[t][j]] * W_r[idx[t][j]] ) with FP32 accumulation (the second sum is
+ * the router projection's input gradient; dlogits is zero off the selected experts). */
+moe_status moe_dispatch_bwd(const moe_desc* d, int chunk, const void* dxd, const int32_t* row_of,
+                            const int32_t* topk_idx, const float* dlogits, const void* w_r,
+                            void* dx, void* stream);
+
+/* FP8 weight quantisation (outside the timed path): per row of a [rows, cols] BF16 matrix,
+ * codes = e4m3(w * (448/amax)) and scale = amax/448 with the FP32 steps of moe_dispatch. */
+moe_status moe_quantize_rows_fp8(int64_t rows, int32_t cols, const void* src_bf16, void* codes,
+                                 float* scale, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Layer primitives (ChunkedEP "Summary": forward, backward, fused forward/backward). They
+ * own the two-stream chunk schedule: routing and dispatch of chunk c+1 on `aux` overlap the
+ * expert GEMMs of chunk c on `compute`; combine of chunk c runs on `aux` after them. On return
+ * all work is ordered before later work on `compute`. Both streams must be distinct, at the
+ * default priority.
+ * ------------------------------------------------------------------------------------- */
+typedef struct moe_tensors {
+  /* inputs */
+  const void* x; const float* logits; const void* w1; const float* w1_scale;
+  const void* w2; const float* w2_scale; const void* w_r; const void* dy;
+  /* routing state and saved context (caller-owned; kept between forward and backward) */
+  int32_t* topk_idx; float* gates; int32_t* counts; int32_t* offsets; int32_t* row_of;
+  int32_t* src_token; void* xd; float* xd_scale; void* gu; void* h; float* h_scale; void* yd;
+  /* forward output: [P_out, H] */
+  void* out;
+  /* backward buffers and outputs */
+  void* dyd; float* dgates; float* dlogits; float* dwr_acc; void* dgu; void* dxd;
+  void* dx; void* dw1; void* dw2; void* dwr;
+  /* scratch of moe_workspace_bytes().workspace bytes */
+  void* workspace;
+} moe_tensors;
+
+moe_status moe_layer_forward(const moe_desc* d, const moe_tensors* t, void* compute_stream,
+                             void* aux_stream);
+moe_status moe_layer_backward(const moe_desc* d, const moe_tensors* t, void* compute_stream,
+                              void* aux_stream);
+moe_status moe_layer_forward_backward(const moe_desc* d, const moe_tensors* t,
+                                      void* compute_stream, void* aux_stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Host-only helpers: they never initialise HIP.
+ * ------------------------------------------------------------------------------------- */
+
+/* Default extents: *P_c = round4(ceil(T/n) * min(k, E_local)), *P_out = round4(T * k). */
+moe_status moe_required_extent(int64_t T, int32_t k, int32_t E_local, int32_t n_chunks,
+                               int64_t* P_c, int64_t* P_out);
+
+/* Bytes of every caller buffer for a descriptor (0 where the dtype does not use it). */
+typedef struct moe_workspace_sizes {
+  int64_t topk_idx, gates, counts, offsets, row_of, src_token;
+  int64_t xd, xd_scale, gu, h, h_scale, yd, out;
+  int64_t dyd, dgates, dlogits, dwr_acc, dgu, dxd, dx, dw1, dw2, dwr;
+  int64_t route_scratch, route_bwd_scratch, workspace; /* workspace = max of the scratches */
+} moe_workspace_sizes;
+moe_status moe_workspace_bytes(const moe_desc* d, moe_workspace_sizes* out);
+
+/* Live-extent tracker (ART PR 971): acquire() records a live graph's extent and returns a
+ * handle; release() ends it; current(required) = round4(max(required, largest live extent)).
+ * Not thread-safe per tracker. */
+typedef struct moe_extent_tracker moe_extent_tracker;
+moe_extent_tracker* moe_extent_tracker_create(void);
+void moe_extent_tracker_destroy(moe_extent_tracker* tr);
+moe_status moe_extent_acquire(moe_extent_tracker* tr, int64_t rows, int64_t* handle);
+moe_status moe_extent_release(moe_extent_tracker* tr, int64_t handle);
+int64_t moe_extent_current(const moe_extent_tracker* tr, int64_t required_rows);
+
+/* Message for the last non-OK status on this thread ("" if none). */
+const char* moe_last_error(void);
+/* ABI version (incremented on any incompatible change). */
+int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,221 @@
+"""GPU-vs-oracle harness shared by the GPU parity tests, smoke() and the benchmark's checks.
+
+Runs the HIP library through its C ABI (via the ctypes binding) on seeded inputs from
+``moe_inputs`` and the CPU oracle on the same inputs, and compares:
+  * integers (top-k indices, counts, offsets, row_of, src_token) and dispatched payload bytes:
+    bit for bit;
+  * FP32 gates: absolute error <= 1e-6;
+  * values on the FP32 path: rel-L2 <= 1e-5 and max|d| / max(1, max|ref|) <= 1e-5;
+  * values on the BF16 path: rel-L2 <= 5e-3 and max|d| / max(1, max|ref|) <= 2e-2 (the stated BF16
+    bounds, with the absolute bound scaled by the tensor's magnitude because a BF16 half-ulp
+    alone exceeds 2e-2 once |v| >= 8);
+  * FP8 forward output: rel-L2 <= 2e-2 against the FP8 oracle.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, Optional
+
+import numpy as np
+
+import moe_inputs
+import oracle
+from oracle import fp8 as ofp8
+
+TOL = {"f32": (1e-5, 1e-5), "bf16": (5e-3, 2e-2), "fp8": (2e-2, 1.0)}
+
+
+def rel_l2(got, want):
+    want = np.asarray(want, dtype=np.float64)
+    got = np.asarray(got, dtype=np.float64)
+    den = np.linalg.norm(want)
+    return float(np.linalg.norm(got - want) / (den if den > 0 else 1.0))
+
+
+def scaled_max(got, want):
+    want = np.asarray(want, dtype=np.float64)
+    got = np.asarray(got, dtype=np.float64)
+    if want.size == 0:
+        return 0.0
+    return float(np.max(np.abs(got - want)) / max(1.0, float(np.max(np.abs(want)))))
+
+
+def assert_close(name, got, want, dtype):
+    rl, sm = TOL[dtype]
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    e1, e2 = rel_l2(got, want), scaled_max(got, want)
+    assert e1 <= rl and e2 <= sm, f"{name}: rel-L2 {e1:.3e} (<= {rl}), scaled max {e2:.3e} (<= {sm})"
+    return e1, e2
+
+
+# ----------------------------------------------------------------------------- device plumbing
+
+def _torch():
+    import torch
+    return torch
+
+
+def to_dev(inp: Dict[str, np.ndarray], name: str, dtype: str):
+    torch = _torch()
+    if name == "logits" or dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(inp[name], dtype=np.float32)).cuda()
+    bits = np.ascontiguousarray(inp[name + "_bits"]).view(np.int16)
+    return torch.from_numpy(bits).cuda().view(torch.bfloat16)
+
+
+def to_np(t) -> np.ndarray:
+    """Device tensor -> numpy FP64/int (BF16 decoded from its bits on the host)."""
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        bits = t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        return moe_inputs.bf16_bits_to_f32(bits).astype(np.float64)
+    a = t.cpu().numpy()
+    return a.astype(np.float64) if a.dtype.kind == "f" else a
+
+
+def bits_np(t) -> np.ndarray:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    if t.dtype == torch.float32:
+        return t.contiguous().view(torch.int32).cpu().numpy().view(np.uint32)
+    return t.cpu().numpy()
+
+
+@dataclasses.dataclass
+class Run:
+    cfg: moe_inputs.MoeConfig
+    desc: object
+    bufs: Dict[str, object]
+    inp: Dict[str, np.ndarray]
+
+
+def run_gpu(cfg: moe_inputs.MoeConfig, inp=None, backward: Optional[bool] = None, P_out=None,
+            layer: bool = True, sentinel: Optional[float] = None, two_streams: bool = True) -> Run:
+    """Run the layer share on cuda:0 through the C ABI (layer primitives, or stage calls)."""
+    import combine_moe_route_02_amd as mh
+    torch = _torch()
+    if backward is None:
+        backward = cfg.backward
+    if inp is None:
+        inp = moe_inputs.make_inputs(cfg, with_backward=backward)
+    d = mh.make_desc(T=cfg.T, H=cfg.H, I=cfg.I, E=cfg.E, E_local=cfg.E_local, k=cfg.k,
+                     n_chunks=cfg.n_chunks, dtype=cfg.dtype, e0=cfg.e0, P_out=P_out)
+    bufs = mh.allocate(d, backward=backward)
+    if sentinel is not None:
+        bufs["out"].fill_(sentinel)
+    wdt = "bf16" if cfg.dtype == "fp8" else cfg.dtype
+    for name in ("x", "logits", "w1", "w2", "w_r") + (("dy",) if backward else ()):
+        bufs[name] = to_dev(inp, name, wdt)
+    if cfg.dtype == "fp8":
+        w1b, w2b = bufs["w1"], bufs["w2"]
+        bufs["w1"] = torch.empty(w1b.shape, dtype=torch.uint8, device="cuda")
+        bufs["w2"] = torch.empty(w2b.shape, dtype=torch.uint8, device="cuda")
+        bufs["w1_scale"] = torch.empty(w1b.shape[:-1], dtype=torch.float32, device="cuda")
+        bufs["w2_scale"] = torch.empty(w2b.shape[:-1], dtype=torch.float32, device="cuda")
+        mh.moe_quantize_rows_fp8(cfg.E_local * 2 * cfg.I, cfg.H, w1b, bufs["w1"], bufs["w1_scale"])
+        mh.moe_quantize_rows_fp8(cfg.E_local * cfg.H, cfg.I, w2b, bufs["w2"], bufs["w2_scale"])
+    cs = torch.cuda.current_stream()
+    aux = torch.cuda.Stream() if two_streams else cs
+    if layer:
+        if backward:
+            mh.moe_layer_forward_backward(d, bufs, cs, aux)
+        else:
+            mh.moe_layer_forward(d, bufs, cs, aux)
+    else:
+        run_stages(mh, d, bufs, backward, cs)
+    torch.cuda.synchronize()
+    return Run(cfg, d, bufs, inp)
+
+
+def run_stages(mh, d, b, backward, s):
+    """The same computation through the stage calls, chunk = -1 (all chunks in order)."""
+    mh.moe_route(d, -1, b["logits"], b["topk_idx"], b["gates"], b["counts"], b["offsets"], b["row_of"],
+                 b["src_token"], b["workspace"], s)
+    mh.moe_dispatch(d, -1, b["x"], b["row_of"], b["xd"], b.get("xd_scale"), b.get("h_scale"), s)
+    mh.moe_expert_ffn(d, -1, b["xd"], b.get("xd_scale"), b["w1"], b.get("w1_scale"), b["w2"], b.get("w2_scale"),
+                      b["offsets"], b.get("gu"), b["h"], b.get("h_scale"), b["yd"], s)
+    mh.moe_combine(d, -1, b["yd"], b["gates"], b["row_of"], b["out"], s)
+    if backward:
+        mh.moe_combine_bwd(d, -1, b["dy"], b["yd"], b["gates"], b["row_of"], b["dyd"], b["dgates"], s)
+        mh.moe_route_bwd(d, -1, b["dgates"], b["gates"], b["topk_idx"], b["x"], b["dlogits"], b["dwr_acc"],
+                         b["dwr"], b["workspace"], s)
+        mh.moe_expert_ffn_bwd(d, -1, b["dyd"], b["xd"], b["gu"], b["h"], b["w1"], b["w2"], b["offsets"],
+                              b["dgu"], b["dxd"], b["dw1"], b["dw2"], s)
+        mh.moe_dispatch_bwd(d, -1, b["dxd"], b["row_of"], b["topk_idx"], b["dlogits"], b["w_r"], b["dx"], s)
+
+
+# ----------------------------------------------------------------------------- oracle + checks
+
+def run_oracle(run: Run, backward: Optional[bool] = None):
+    cfg, inp = run.cfg, run.inp
+    if backward is None:
+        backward = cfg.backward
+    if cfg.dtype == "fp8":
+        return ofp8.forward(inp["x"], inp["logits"], inp["w1"], inp["w2"], k=cfg.k, e0=cfg.e0,
+                            E_local=cfg.E_local, n_chunks=cfg.n_chunks, P_c=run.desc.P_c)
+    f = oracle.forward(inp["x"], inp["logits"], inp["w1"], inp["w2"], k=cfg.k, e0=cfg.e0,
+                       E_local=cfg.E_local, n_chunks=cfg.n_chunks, P_c=run.desc.P_c)
+    if backward:
+        f["bwd"] = oracle.backward(f, inp["x"], inp["dy"], inp["w1"], inp["w2"], inp["w_r"])
+    return f
+
+
+def check_routing(run: Run, ref) -> None:
+    b = run.bufs
+    for name in ("topk_idx", "counts", "offsets", "row_of", "src_token"):
+        got = b[name].cpu().numpy()
+        want = ref["idx" if name == "topk_idx" else name]
+        assert got.shape == want.shape, name
+        bad = np.count_nonzero(got != want)
+        assert bad == 0, f"{name}: {bad} of {got.size} entries differ"
+    g = b["gates"].cpu().numpy().astype(np.float64)
+    err = float(np.max(np.abs(g - ref["gates"]))) if g.size else 0.0
+    assert err <= 1e-6, f"gates: max abs {err:.3e}"
+
+
+def check_dispatch_bytes(run: Run, ref) -> None:
+    """Every used row of xd holds its token's payload bytes exactly."""
+    src = ref["src_token"]
+    used = np.nonzero(src >= 0)[0]
+    if run.cfg.dtype == "fp8":
+        got = run.bufs["xd"].cpu().numpy()[used]
+        want = ref["xq"][src[used]]
+        bad = np.count_nonzero(got != want)
+        assert bad == 0, f"xd fp8 codes: {bad} bytes differ"
+        s = run.bufs["xd_scale"].cpu().numpy()[used]
+        np.testing.assert_array_equal(s.view(np.uint32), ref["xs"][src[used]].view(np.uint32))
+        return
+    got = bits_np(run.bufs["xd"])[used]
+    x_bits = run.inp["x_bits"] if run.cfg.dtype == "bf16" else run.inp["x"].view(np.uint32)
+    want = x_bits[src[used]]
+    bad = np.count_nonzero(got != want)
+    assert bad == 0, f"xd: {bad} payload elements differ"
+
+
+def check_forward(run: Run, ref, sentinel=None) -> Dict[str, float]:
+    check_routing(run, ref)
+    check_dispatch_bytes(run, ref)
+    T = run.cfg.T
+    out = run.bufs["out"]
+    got = to_np(out[:T])
+    errs = {}
+    errs["out"] = assert_close("out", got, ref["out"], run.cfg.dtype)
+    if sentinel is not None and out.shape[0] > T:
+        tail = to_np(out[T:])
+        assert np.all(tail == sentinel), "combine wrote rows beyond the logical tokens"
+    return errs
+
+
+def check_backward(run: Run, ref) -> Dict[str, float]:
+    bw = ref["bwd"]
+    b = run.bufs
+    dt = run.cfg.dtype
+    errs = {}
+    errs["dgates"] = assert_close("dgates", to_np(b["dgates"]), bw["dgates"], dt)
+    errs["dlogits"] = assert_close("dlogits", to_np(b["dlogits"]), bw["dlogits"], dt)
+    errs["dx"] = assert_close("dx", to_np(b["dx"]), bw["dx"], dt)
+    errs["dw1"] = assert_close("dw1", to_np(b["dw1"]), bw["dw1"], dt)
+    errs["dw2"] = assert_close("dw2", to_np(b["dw2"]), bw["dw2"], dt)
+    errs["dwr"] = assert_close("dwr", to_np(b["dwr"]), bw["dwr"], dt)
+    return errs

@@ -1,0 +1,127 @@
+"""Host-only checks of the C ABI (no GPU): the library loads, exports every function declared in
+include/moe.h, validates descriptors before any launch, and its host helpers (extents, workspace
+sizes, live-extent tracker) agree with the oracle and with ART PR 971's printed byte counts."""
+import json
+import os
+import re
+
+import pytest
+
+import oracle
+from oracle import extent as oextent
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+mh = pytest.importorskip("combine_moe_route_02_amd")
+
+
+def _lib_or_skip():
+    if not os.path.exists(mh.LIB_PATH):
+        pytest.skip("libmoe.so not built (run __graft_entry__.build())")
+    return mh.lib()
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    L = _lib_or_skip()
+    names = _declared_functions()
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(mh.exported_symbols())
+    assert L.moe_abi_version() == 1
+
+
+@pytest.mark.parametrize("T,k,El,n", [(256, 2, 8, 1), (16384, 8, 16, 2), (32768, 8, 16, 2), (10, 3, 2, 3),
+                                      (0, 2, 4, 2), (7, 8, 3, 4)])
+def test_required_extent_matches_oracle(T, k, El, n):
+    _lib_or_skip()
+    assert mh.required_extent(T, k, El, n) == oracle.required_extent(T, k, El, n)
+
+
+def _desc(**kw):
+    base = dict(T=1000, H=256, I=192, E=32, e0=0, E_local=8, k=4, n_chunks=2, dtype="bf16")
+    base.update(kw)
+    if "P_c" not in base or "P_out" not in base:
+        pc, po = oracle.required_extent(base["T"], max(1, base["k"]), base["E_local"], max(1, base["n_chunks"]))
+        base.setdefault("P_c", pc)
+        base.setdefault("P_out", po)
+    dt = base.pop("dtype")
+    return mh.MoeDesc(dtype=mh.DTYPES.get(dt, dt) if isinstance(dt, str) else dt, reserved=0, **base)
+
+
+def _status_of(fn, *a):
+    try:
+        fn(*a)
+    except mh.MoeError as e:
+        return e.status, str(e)
+    return 0, ""
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=9, E=32), -3), (dict(k=0), -1), (dict(E_local=40), -1), (dict(H=100), -3), (dict(I=32), -3),
+    (dict(n_chunks=0, P_c=4, P_out=1000), -1), (dict(P_c=2002), -2), (dict(P_c=1996), -2), (dict(P_out=998), -2),
+    (dict(P_out=1002), -2), (dict(dtype=7), -1), (dict(E=30, E_local=8), -3), (dict(E=2000, E_local=8), -3),
+])
+def test_descriptor_validation(kw, status):
+    _lib_or_skip()
+    d = _desc(**kw)
+    st, msg = _status_of(mh.moe_route, d, 0, None, None, None, None, None, None, None, None, 0)
+    assert st == status, msg
+    assert mh.last_error()
+
+
+def test_null_pointers_and_bad_chunk_are_rejected_before_launch():
+    _lib_or_skip()
+    d = _desc()
+    assert _status_of(mh.moe_route, d, 0, None, None, None, None, None, None, None, None, 0)[0] == -1
+    assert _status_of(mh.moe_route, d, 2, 1, 1, 1, 1, 1, 1, 1, 1, 0)[0] == -1      # chunk out of range
+    assert _status_of(mh.moe_dispatch, d, -2, 1, 1, 1, None, None, 0)[0] == -1
+    assert _status_of(mh.moe_combine, d, 0, None, 1, 1, 1, 0)[0] == -1
+    assert _status_of(mh.moe_expert_ffn, d, 0, 1, None, 1, None, None, None, 1, None, 1, None, 1, 0)[0] == -1
+    fp8 = _desc(dtype="fp8")
+    assert _status_of(mh.moe_combine_bwd, fp8, 0, 1, 1, 1, 1, 1, 1, 0)[0] == -3    # FP8 is forward only
+    assert _status_of(mh.moe_quantize_rows_fp8, 4, 12, 1, 1, 1, 0)[0] == -1
+
+
+def test_workspace_bytes():
+    _lib_or_skip()
+    d = mh.make_desc(T=16384, H=2048, I=768, E=128, E_local=16, k=8, n_chunks=2, dtype="bf16")
+    ws = mh.workspace_bytes(d)
+    P = 2 * 65536
+    assert ws["xd"] == P * 2048 * 2 and ws["yd"] == P * 2048 * 2 and ws["gu"] == P * 1536 * 2
+    assert ws["out"] == 131072 * 2048 * 2                     # fresh [P_out, H] BF16 output
+    assert ws["dw1"] == 16 * 1536 * 2048 * 2 and ws["dwr_acc"] == 128 * 2048 * 4
+    assert ws["workspace"] == max(ws["route_scratch"], ws["route_bwd_scratch"]) > 0
+    f8 = mh.make_desc(T=16384, H=2048, I=768, E=128, E_local=16, k=8, n_chunks=2, dtype="fp8")
+    ws8 = mh.workspace_bytes(f8)
+    assert ws8["xd"] == P * 2048 and ws8["xd_scale"] == P * 4 and ws8["dw1"] == 0
+
+
+def test_extent_tracker_matches_art971_fixture_and_oracle():
+    _lib_or_skip()
+    g = json.load(open(os.path.join(GOLDEN, "extent_art971.json")))
+    tr = mh.ExtentTracker()
+    ot = oextent.ExtentTracker()
+    H, es, rows = g["H"], g["elem_size_bf16"], g["logical_rows"]
+    h = tr.acquire(g["live_extent_rows"])
+    oh = ot.acquire(g["live_extent_rows"])
+    assert tr.current(rows) == ot.current(rows) == g["live_extent_rows"]
+    assert tr.current(rows) * H * es == g["bytes_with_live_extent"]
+    tr.release(h)
+    ot.release(oh)
+    assert tr.current(rows) * H * es == g["bytes_after_release"]
+    with pytest.raises(mh.MoeError):
+        tr.release(h)
+    for req, live in [(0, []), (5, []), (10, [101, 37]), (200, [101]), (3, [7, 9, 13])]:
+        a, b = mh.ExtentTracker(), oextent.ExtentTracker()
+        for r in live:
+            a.acquire(r)
+            b.acquire(r)
+        assert a.current(req) == b.current(req)

@@ -1,0 +1,146 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the same seeded inputs.
+
+Small cases span several tiles, ragged tails (T not divisible by n_chunks, partial M/N tiles),
+local subsets, empty experts and every chunk count 1..4; the full-size cases run the one-rank
+shapes (16K tokens, H 2048, 16 of 128 experts, top-8, I 768) in the layer primitive's
+two-stream launch configuration."""
+import numpy as np
+import pytest
+
+import moe_inputs
+from moe_inputs import MoeConfig
+
+pytestmark = pytest.mark.gpu
+
+harness = pytest.importorskip("harness")
+
+
+def _require_gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import combine_moe_route_02_amd as mh
+    mh.lib()  # raises if the HIP library is missing: the GPU tests never fall back
+
+
+SMALL = [
+    MoeConfig("tiny", T=256, H=128, I=256, E=8, E_local=8, k=2, n_chunks=1, dtype="f32", seed_base=0,
+              x_std=0.02, backward=True),
+    MoeConfig("f32_sub", T=301, H=128, I=192, E=16, E_local=5, e0=3, k=4, n_chunks=3, dtype="f32",
+              seed_base=10, backward=True),
+    MoeConfig("bf16_rag", T=1000, H=256, I=192, E=32, E_local=8, e0=4, k=4, n_chunks=2, dtype="bf16",
+              seed_base=20, backward=True),
+    MoeConfig("bf16_full_local", T=2048, H=512, I=256, E=16, E_local=16, k=8, n_chunks=2, dtype="bf16",
+              seed_base=30, backward=True),
+    MoeConfig("bf16_n3", T=777, H=384, I=320, E=64, E_local=16, e0=48, k=6, n_chunks=3, dtype="bf16",
+              seed_base=40, backward=True),
+    MoeConfig("bf16_n4_zipf", T=1500, H=256, I=128, E=32, E_local=8, k=8, n_chunks=4, dtype="bf16",
+              seed_base=50, zipf_s=1.2, n_empty=2, backward=True),
+    MoeConfig("bf16_n1", T=640, H=128, I=64, E=8, E_local=4, e0=2, k=2, n_chunks=1, dtype="bf16",
+              seed_base=60, backward=True),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=[c.name for c in SMALL])
+def test_small_forward_backward(cfg):
+    _require_gpu()
+    print(f"[parity] {cfg}", flush=True)
+    run = harness.run_gpu(cfg, sentinel=-7.0)
+    ref = harness.run_oracle(run)
+    harness.check_forward(run, ref, sentinel=-7.0)
+    harness.check_backward(run, ref)
+
+
+@pytest.mark.parametrize("cfg", SMALL[1:4], ids=[c.name for c in SMALL[1:4]])
+def test_stage_calls_match_layer_primitive(cfg):
+    """chunk = -1 stage calls on one stream produce bitwise the layer primitive's results."""
+    _require_gpu()
+    a = harness.run_gpu(cfg, layer=True)
+    b = harness.run_gpu(cfg, layer=False, two_streams=False)
+    for name in ("topk_idx", "row_of", "src_token", "counts", "offsets"):
+        np.testing.assert_array_equal(a.bufs[name].cpu().numpy(), b.bufs[name].cpu().numpy())
+    for name in ("out", "dx", "dw1", "dw2", "dwr", "dlogits"):
+        ga, gb = harness.bits_np(a.bufs[name]), harness.bits_np(b.bufs[name])
+        if name == "out":
+            ga, gb = ga[:cfg.T], gb[:cfg.T]
+        np.testing.assert_array_equal(ga, gb, err_msg=name)
+
+
+def test_forward_is_chunk_invariant_and_deterministic():
+    """Forward results do not depend on the chunk count (no split reduction in the forward) and
+    repeat bit for bit."""
+    _require_gpu()
+    base = SMALL[3]
+    outs = []
+    for n in (1, 2, 3, 4):
+        r = harness.run_gpu(base.replace(n_chunks=n), backward=False)
+        outs.append(harness.bits_np(r.bufs["out"])[:base.T])
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o, outs[0])
+    r = harness.run_gpu(base, backward=True)
+    r2 = harness.run_gpu(base, backward=True)
+    for name in ("out", "dx", "dw1", "dw2", "dwr"):
+        a, b = harness.bits_np(r.bufs[name]), harness.bits_np(r2.bufs[name])
+        if name == "out":                     # rows T..P_out-1 are never written
+            a, b = a[:base.T], b[:base.T]
+        np.testing.assert_array_equal(a, b, err_msg=name)
+
+
+def test_no_local_expert():
+    _require_gpu()
+    cfg = MoeConfig("none_local", T=200, H=128, I=64, E=8, E_local=0, e0=8, k=2, n_chunks=2, dtype="bf16",
+                    seed_base=70, backward=True)
+    run = harness.run_gpu(cfg, sentinel=3.0)
+    ref = harness.run_oracle(run)
+    harness.check_forward(run, ref, sentinel=3.0)
+    assert np.all(harness.to_np(run.bufs["out"][:cfg.T]) == 0)
+    harness.check_backward(run, ref)
+
+
+def test_all_tokens_to_one_local_expert_and_neg_inf_logits():
+    _require_gpu()
+    cfg = MoeConfig("one_expert", T=700, H=256, I=128, E=16, E_local=4, k=3, n_chunks=2, dtype="bf16",
+                    seed_base=80, backward=True)
+    inp = moe_inputs.make_inputs(cfg)
+    lg = inp["logits"]
+    lg[:, 1] += 50.0                       # every token picks local expert 1 first
+    lg[:, 5:9] = -np.inf                   # several experts can never be chosen
+    run = harness.run_gpu(cfg, inp=inp)
+    ref = harness.run_oracle(run)
+    assert np.all(ref["idx"][:, 0] == 1)
+    harness.check_forward(run, ref)
+    harness.check_backward(run, ref)
+
+
+# ----------------------------------------------------------------------------- full sizes
+
+@pytest.fixture(scope="module")
+def fwd16k():
+    _require_gpu()
+    cfg = moe_inputs.CONFIGS["fwd16k"]
+    run = harness.run_gpu(cfg, sentinel=-3.0)
+    ref = harness.run_oracle(run)
+    return run, ref
+
+
+def test_full_forward_16k_routing_bitwise(fwd16k):
+    run, ref = fwd16k
+    harness.check_routing(run, ref)
+    harness.check_dispatch_bytes(run, ref)
+    assert int(ref["counts"].sum()) == run.cfg.T * run.cfg.k
+
+
+def test_full_forward_16k_values(fwd16k):
+    run, ref = fwd16k
+    errs = harness.check_forward(run, ref, sentinel=-3.0)
+    print("[fwd16k]", errs)
+
+
+def test_full_fused_16k_forward_backward():
+    _require_gpu()
+    cfg = moe_inputs.CONFIGS["fb16k"]
+    print(f"[parity] {cfg}", flush=True)
+    run = harness.run_gpu(cfg)
+    ref = harness.run_oracle(run)
+    print("[fb16k fwd]", harness.check_forward(run, ref), flush=True)
+    print("[fb16k bwd]", harness.check_backward(run, ref), flush=True)
