@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Benchmark of one GPU's share of the MoE layer: fused forward+backward tokens/s at 16K tokens.
+
+Workload: one EP8 rank's share, BF16, T=16384 tokens in two token-wise chunks of 8192, H=2048,
+16 local of 128 experts, top-8, SwiGLU I=768, forward and backward (route, dispatch, grouped expert
+GEMMs, combine, and their backward with grouped wgrad and the FP32-accumulated router gradient).
+Inputs are seeded synthetic tensors already resident in HBM when timing starts.
+
+Prints one JSON line. `value` is fused forward+backward tokens/s; the forward-only rate, every
+kernel's measured duration and algorithmic throughput, the dominant kernel's roofline, and the CPU
+oracle's rate on a bounded token sample ride along.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/s (fwd, fwd+bwd) @16K tok top-k8; %HBM BW, %MFMA peak"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense BF16 MFMA, TFLOP/s
+PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X vector FP32
+
+GEMM_KERNELS = {"gemm_gateup_swiglu", "gemm_down", "gemm_down_dgrad_swiglu", "gemm_gateup_dgrad",
+                "gemm_wgrad_down", "gemm_wgrad_gateup", "gemm_router_wgrad"}
+
+
+def algorithmic_work(cfg, counts, offsets, k_sel_local_tokens):
+    """Per fused step: name -> (work, unit). FLOPs for GEMMs (useful multiply-adds x 2), bytes that
+    the step must move for the row kernels (each tensor element read or written once)."""
+    T, H, I, E, k, El = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.E_local
+    N = int(offsets[:, El].sum())              # local rows over all chunks
+    Tt = int(k_sel_local_tokens)               # tokens with at least one local expert
+    s = 2                                      # BF16 payload bytes
+    S = min(16, max(1, math.ceil(math.ceil(T / cfg.n_chunks) / 64)))
+    w = {
+        "gemm_gateup_swiglu": (2.0 * N * H * 2 * I, "flop"),
+        "gemm_down": (2.0 * N * I * H, "flop"),
+        "gemm_down_dgrad_swiglu": (2.0 * N * H * I, "flop"),
+        "gemm_gateup_dgrad": (2.0 * N * 2 * I * H, "flop"),
+        "gemm_wgrad_down": (2.0 * N * H * I, "flop"),
+        "gemm_wgrad_gateup": (2.0 * N * 2 * I * H, "flop"),
+        "gemm_router_wgrad": (2.0 * T * E * H, "flop"),
+        "route_topk": (T * E * 4 + T * k * 8, "byte"),
+        "route_layout": (T * k * 8 + cfg.n_chunks * 0 + N * 4, "byte"),
+        "dispatch": (Tt * H * s + N * H * s + T * k * 4, "byte"),
+        "combine": (N * H * s + T * H * s + T * k * 8, "byte"),
+        "combine_bwd": (Tt * H * s + 2 * N * H * s + T * k * 12, "byte"),
+        "route_bwd_dlogits": (T * k * 12 + T * E * 4, "byte"),
+        "dispatch_bwd": (N * H * s + T * H * s + T * k * 12 + E * H * s, "byte"),
+        "router_reduce": (cfg.n_chunks * (S * E * H * 4 + 2 * E * H * 4) + E * H * s, "byte"),
+    }
+    return w, N, Tt
+
+
+def cpu_baseline(cfg, inp, budget_s: float):
+    """Time the CPU oracle (as it stands) on a bounded prefix of the workload's tokens."""
+    import numpy as np
+    import oracle
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    Ts = 1024
+    while True:
+        x = inp["x"][:Ts]
+        lg = inp["logits"][:Ts]
+        dy = inp["dy"][:Ts]
+        t0 = time.perf_counter()
+        f = oracle.forward(x, lg, inp["w1"], inp["w2"], k=cfg.k, e0=cfg.e0, E_local=cfg.E_local,
+                           n_chunks=cfg.n_chunks)
+        oracle.backward(f, x, dy, inp["w1"], inp["w2"], inp["w_r"])
+        dt = time.perf_counter() - t0
+        if dt * 2 > budget_s or Ts * 2 > cfg.T:
+            break
+        Ts *= 2
+    return {"value": Ts / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"FP64 NumPy oracle, fused forward+backward on the first {Ts} of {cfg.T} tokens "
+                      f"(same H/I/E/k/chunks), {dt:.2f} s, scaled to tokens/s",
+            "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="fb16k")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share of the layer; --gpus {args.gpus} is not supported "
+              f"(this build has no multi-GPU path: run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import moe_inputs
+    import combine_moe_route_02_amd as mh
+
+    mh.lib()  # the HIP library must be present: there is no other path
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    cfg = moe_inputs.CONFIGS[args.workload]
+    inp = moe_inputs.make_inputs(cfg, with_backward=True)
+
+    d = mh.make_desc(T=cfg.T, H=cfg.H, I=cfg.I, E=cfg.E, E_local=cfg.E_local, k=cfg.k, n_chunks=cfg.n_chunks,
+                     dtype=cfg.dtype, e0=cfg.e0)
+    bufs = mh.allocate(d, backward=True)
+
+    def dev(name):
+        if name == "logits":
+            return torch.from_numpy(inp["logits"]).cuda()
+        return torch.from_numpy(inp[name + "_bits"].view(np.int16)).cuda().view(torch.bfloat16)
+
+    for name in ("x", "logits", "w1", "w2", "w_r", "dy"):
+        bufs[name] = dev(name)
+    cs = torch.cuda.Stream()
+    aux = torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    def fb():
+        mh.moe_layer_forward_backward(d, bufs, cs, aux)
+
+    def fwd():
+        mh.moe_layer_forward(d, bufs, cs, aux)
+
+    for _ in range(args.warmup):
+        fb()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` fused steps, every kernel launch bracketed by HIP events on
+    # the stream it runs on
+    mh.moe_trace_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        fb()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    mh.moe_trace_disable()
+    entries = mh.moe_trace_entries()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # the same loop without the launch log, for the tracing overhead
+    torch.cuda.synchronize()
+    u0 = time.perf_counter()
+    for _ in range(args.steps):
+        fb()
+    torch.cuda.synchronize()
+    ms_untraced = (time.perf_counter() - u0) * 1e3 / args.steps
+
+    # forward only
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize()
+    f0 = time.perf_counter()
+    for _ in range(args.steps):
+        fwd()
+    torch.cuda.synchronize()
+    ms_fwd = (time.perf_counter() - f0) * 1e3 / args.steps
+
+    counts = bufs["counts"].cpu().numpy()
+    offsets = bufs["offsets"].cpu().numpy()
+    row_of = bufs["row_of"].cpu().numpy()
+    touched = int(np.count_nonzero((row_of >= 0).any(axis=1)))
+    work, N, Tt = algorithmic_work(cfg, counts, offsets, touched)
+
+    per = {}
+    for name, _stream, ms in entries:
+        p = per.setdefault(name, [0, 0.0])
+        p[0] += 1
+        p[1] += ms
+    kernels = {}
+    for name, (cnt, tot) in per.items():
+        launches = cnt / args.steps
+        avg_us = tot / cnt * 1e3
+        entry = {"launches_per_step": launches, "avg_us": round(avg_us, 3), "ms_per_step": round(tot / args.steps, 4)}
+        if name in work:
+            wk, unit = work[name]
+            rate = wk / (tot / args.steps * 1e-3)
+            if unit == "flop":
+                entry.update(achieved_tflops=round(rate / 1e12, 2), frac_mfma=round(rate / 1e12 / PEAK_BF16_TFLOPS, 4))
+            else:
+                entry.update(achieved_gbs=round(rate / 1e9, 1), frac_hbm=round(rate / 1e9 / PEAK_HBM_GBS, 4))
+        kernels[name] = entry
+    dom = max(per, key=lambda n: per[n][1])
+    dcnt, dtot = per[dom]
+    wk, unit = work.get(dom, (None, None))
+    if unit == "flop":
+        ach = wk / (dtot / args.steps * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": dom,
+                "avg_launch_us": round(dtot / dcnt * 1e3, 3), "work_per_launch": wk / (dcnt / args.steps)}
+    else:
+        ach = wk / (dtot / args.steps * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "kernel": dom,
+                "avg_launch_us": round(dtot / dcnt * 1e3, 3), "work_per_launch": wk / (dcnt / args.steps)}
+
+    gemm_flops = sum(work[n][0] for n in GEMM_KERNELS)
+    gemm_ms = sum(per[n][1] for n in GEMM_KERNELS if n in per) / args.steps
+    value = cfg.T / (ms_per_step * 1e-3)
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "one EP8 rank's MoE layer share, BF16 fused forward+backward",
+                   "tokens": cfg.T, "n_chunks": cfg.n_chunks, "hidden": cfg.H, "intermediate": cfg.I,
+                   "experts": cfg.E, "local_experts": cfg.E_local, "top_k": cfg.k,
+                   "local_rows": N, "tokens_with_local_expert": Tt},
+        "fwd_tokens_per_s": round(cfg.T / (ms_fwd * 1e-3), 1), "fwd_ms": round(ms_fwd, 4),
+        "ms_per_step_untraced": round(ms_untraced, 4),
+        "gemm_tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 2) if gemm_ms > 0 else None,
+        "roofline": roof, "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -78,10 +78,14 @@ _SIGS = {
     "moe_extent_acquire": [c_void_p, c_int64, POINTER(c_int64)],
     "moe_extent_release": [c_void_p, c_int64],
     "moe_extent_current": [c_void_p, c_int64],
+    "moe_trace_enable": [c_int32],
+    "moe_trace_disable": [],
+    "moe_trace_count": [],
+    "moe_trace_entry": [c_int64, POINTER(c_char_p), POINTER(c_void_p), POINTER(ctypes.c_float)],
     "moe_last_error": [],
     "moe_abi_version": [],
 }
-_RESTYPE = {"moe_extent_tracker_create": c_void_p, "moe_extent_tracker_destroy": None,
+_RESTYPE = {"moe_extent_tracker_create": c_void_p, "moe_extent_tracker_destroy": None, "moe_trace_count": c_int64,
             "moe_extent_current": c_int64, "moe_last_error": c_char_p, "moe_abi_version": c_int32}
 
 
@@ -256,6 +260,26 @@ class ExtentTracker:
         if getattr(self, "_h", None) and _LIB is not None:
             _LIB.moe_extent_tracker_destroy(self._h)
             self._h = None
+
+
+def moe_trace_enable(timing: bool = False) -> None:
+    _check(lib().moe_trace_enable(1 if timing else 0), "moe_trace_enable")
+
+
+def moe_trace_disable() -> None:
+    _check(lib().moe_trace_disable(), "moe_trace_disable")
+
+
+def moe_trace_entries():
+    """The launch log of this thread: list of (kernel name, stream handle, device ms or -1)."""
+    L = lib()
+    out = []
+    for i in range(L.moe_trace_count()):
+        name, stream, ms = c_char_p(), c_void_p(), ctypes.c_float()
+        _check(L.moe_trace_entry(i, ctypes.byref(name), ctypes.byref(stream), ctypes.byref(ms)),
+               "moe_trace_entry")
+        out.append((name.value.decode(), stream.value or 0, ms.value))
+    return out
 
 
 # ------------------------------------------------------------------ device buffers (torch plumbing)

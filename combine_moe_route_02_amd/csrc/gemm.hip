@@ -17,6 +17,7 @@
 // transposed in registers while staging (8 K-rows x V columns per thread).
 #include "common.h"
 #include "launch.h"
+#include "trace.h"
 
 namespace moe {
 namespace gemm {
@@ -674,12 +675,15 @@ namespace {
 constexpr int kPersistentGrid = 512;  // 256 CUs x 2 resident workgroups
 
 template <int BM, int BN, int WM, int WN, int MODE>
-hipError_t run_rows(const RowsArgs& a, hipStream_t s) {
+hipError_t run_rows(const char* name, const RowsArgs& a, hipStream_t s) {
   size_t lds = (size_t)2 * (BM + BN) * BK * sizeof(uint16_t);
   auto k = rows_gemm_kernel<BM, BN, WM, WN, MODE>;
   hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k, dim3(kPersistentGrid), dim3(kThreads), lds, s, a);
+  {
+    MOE_TRACE(name, s);
+    hipLaunchKernelGGL(k, dim3(kPersistentGrid), dim3(kThreads), lds, s, a);
+  }
   return hipGetLastError();
 }
 }  // namespace
@@ -693,26 +697,32 @@ hipError_t launch_expert_fwd(bool bf16, const void* xd, const void* w1, const vo
     a.A = (const uint16_t*)xd; a.B = (const uint16_t*)w1; a.C = (uint16_t*)h; a.C2 = (uint16_t*)gu;
     a.lda = H; a.ldc = I; a.strideB = (int64_t)2 * I * H; a.K = H; a.N = I; a.I = I;
     a.offsets = offsets; a.El = El; a.c0 = c0; a.nc = nc; a.P_c = P_c;
-    hipError_t e = run_rows<128, 128, 2, 2, kGateUp>(a, s);
+    hipError_t e = run_rows<128, 128, 2, 2, kGateUp>("gemm_gateup_swiglu", a, s);
     if (e != hipSuccess) return e;
     RowsArgs b{};
     b.A = (const uint16_t*)h; b.B = (const uint16_t*)w2; b.C = (uint16_t*)yd;
     b.lda = I; b.ldc = H; b.strideB = (int64_t)H * I; b.K = I; b.N = H; b.I = I;
     b.offsets = offsets; b.El = El; b.c0 = c0; b.nc = nc; b.P_c = P_c;
-    return run_rows<128, 128, 2, 2, kDown>(b, s);
+    return run_rows<128, 128, 2, 2, kDown>("gemm_down", b, s);
   }
   SimtRowsArgs a{};
   a.A = (const float*)xd; a.B = (const float*)w1; a.C = (float*)h; a.C2 = (float*)gu;
   a.lda = H; a.ldc = I; a.strideB = (int64_t)2 * I * H; a.K = H; a.N = I; a.I = I;
   a.offsets = offsets; a.El = El; a.c0 = c0; a.nc = nc; a.P_c = P_c;
-  hipLaunchKernelGGL(simt_rows_kernel<kGateUp>, dim3(kPersistentGrid), dim3(256), 0, s, a);
+  {
+    MOE_TRACE("gemm_gateup_swiglu_f32", s);
+    hipLaunchKernelGGL(simt_rows_kernel<kGateUp>, dim3(kPersistentGrid), dim3(256), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   SimtRowsArgs b{};
   b.A = (const float*)h; b.B = (const float*)w2; b.C = (float*)yd;
   b.lda = I; b.ldc = H; b.strideB = (int64_t)H * I; b.K = I; b.N = H; b.I = I;
   b.offsets = offsets; b.El = El; b.c0 = c0; b.nc = nc; b.P_c = P_c;
-  hipLaunchKernelGGL(simt_rows_kernel<kDown>, dim3(kPersistentGrid), dim3(256), 0, s, b);
+  {
+    MOE_TRACE("gemm_down_f32", s);
+    hipLaunchKernelGGL(simt_rows_kernel<kDown>, dim3(kPersistentGrid), dim3(256), 0, s, b);
+  }
   return hipGetLastError();
 }
 
@@ -725,26 +735,32 @@ hipError_t launch_expert_dgrad(bool bf16, const void* dyd, const void* gu, const
     a.A = (const uint16_t*)dyd; a.B = (const uint16_t*)w2; a.C = (uint16_t*)dgu; a.aux = (const uint16_t*)gu;
     a.lda = H; a.ldc = 2 * I; a.strideB = (int64_t)H * I; a.K = H; a.N = I; a.I = I;
     a.offsets = offsets; a.El = El; a.c0 = c0; a.nc = nc; a.P_c = P_c;
-    hipError_t e = run_rows<128, 128, 2, 2, kDownBwd>(a, s);
+    hipError_t e = run_rows<128, 128, 2, 2, kDownBwd>("gemm_down_dgrad_swiglu", a, s);
     if (e != hipSuccess) return e;
     RowsArgs b{};
     b.A = (const uint16_t*)dgu; b.B = (const uint16_t*)w1; b.C = (uint16_t*)dxd;
     b.lda = 2 * I; b.ldc = H; b.strideB = (int64_t)2 * I * H; b.K = 2 * I; b.N = H; b.I = I;
     b.offsets = offsets; b.El = El; b.c0 = c0; b.nc = nc; b.P_c = P_c;
-    return run_rows<128, 128, 2, 2, kGateUpBwd>(b, s);
+    return run_rows<128, 128, 2, 2, kGateUpBwd>("gemm_gateup_dgrad", b, s);
   }
   SimtRowsArgs a{};
   a.A = (const float*)dyd; a.B = (const float*)w2; a.C = (float*)dgu; a.aux = (const float*)gu;
   a.lda = H; a.ldc = 2 * I; a.strideB = (int64_t)H * I; a.K = H; a.N = I; a.I = I;
   a.offsets = offsets; a.El = El; a.c0 = c0; a.nc = nc; a.P_c = P_c;
-  hipLaunchKernelGGL(simt_rows_kernel<kDownBwd>, dim3(kPersistentGrid), dim3(256), 0, s, a);
+  {
+    MOE_TRACE("gemm_down_dgrad_swiglu_f32", s);
+    hipLaunchKernelGGL(simt_rows_kernel<kDownBwd>, dim3(kPersistentGrid), dim3(256), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   SimtRowsArgs b{};
   b.A = (const float*)dgu; b.B = (const float*)w1; b.C = (float*)dxd;
   b.lda = 2 * I; b.ldc = H; b.strideB = (int64_t)2 * I * H; b.K = 2 * I; b.N = H; b.I = I;
   b.offsets = offsets; b.El = El; b.c0 = c0; b.nc = nc; b.P_c = P_c;
-  hipLaunchKernelGGL(simt_rows_kernel<kGateUpBwd>, dim3(kPersistentGrid), dim3(256), 0, s, b);
+  {
+    MOE_TRACE("gemm_gateup_dgrad_f32", s);
+    hipLaunchKernelGGL(simt_rows_kernel<kGateUpBwd>, dim3(kPersistentGrid), dim3(256), 0, s, b);
+  }
   return hipGetLastError();
 }
 
@@ -762,26 +778,38 @@ hipError_t launch_expert_wgrad(bool bf16, const void* dyd, const void* dgu, cons
     KGroupArgs a{};
     a.A = dyd; a.B = (const uint16_t*)h; a.C = dw2; a.lda = H; a.ldb = I; a.strideC = (int64_t)H * I;
     a.M = H; a.N = I; a.offsets = offsets; a.El = El; a.n_chunks = n; a.P_c = P_c;
-    hipLaunchKernelGGL(k, dim3(El * ((H + BM - 1) / BM) * ((I + BN - 1) / BN)), dim3(kThreads), lds, s, a);
+    {
+      MOE_TRACE("gemm_wgrad_down", s);
+      hipLaunchKernelGGL(k, dim3(El * ((H + BM - 1) / BM) * ((I + BN - 1) / BN)), dim3(kThreads), lds, s, a);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     // dW1[e] [2I, H] = sum dgu^T xd
     KGroupArgs b{};
     b.A = dgu; b.B = (const uint16_t*)xd; b.C = dw1; b.lda = 2 * I; b.ldb = H; b.strideC = (int64_t)2 * I * H;
     b.M = 2 * I; b.N = H; b.offsets = offsets; b.El = El; b.n_chunks = n; b.P_c = P_c;
-    hipLaunchKernelGGL(k, dim3(El * ((2 * I + BM - 1) / BM) * ((H + BN - 1) / BN)), dim3(kThreads), lds, s, b);
+    {
+      MOE_TRACE("gemm_wgrad_gateup", s);
+      hipLaunchKernelGGL(k, dim3(El * ((2 * I + BM - 1) / BM) * ((H + BN - 1) / BN)), dim3(kThreads), lds, s, b);
+    }
     return hipGetLastError();
   }
   SimtKArgs a{};
   a.A = (const float*)dyd; a.B = (const float*)h; a.C = (float*)dw2; a.lda = H; a.ldb = I;
   a.strideC = (int64_t)H * I; a.M = H; a.N = I; a.offsets = offsets; a.El = El; a.n_chunks = n; a.P_c = P_c;
-  hipLaunchKernelGGL(simt_kgroup_kernel, dim3(El * ((H + 63) / 64) * ((I + 63) / 64)), dim3(256), 0, s, a);
+  {
+    MOE_TRACE("gemm_wgrad_down_f32", s);
+    hipLaunchKernelGGL(simt_kgroup_kernel, dim3(El * ((H + 63) / 64) * ((I + 63) / 64)), dim3(256), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   SimtKArgs b{};
   b.A = (const float*)dgu; b.B = (const float*)xd; b.C = (float*)dw1; b.lda = 2 * I; b.ldb = H;
   b.strideC = (int64_t)2 * I * H; b.M = 2 * I; b.N = H; b.offsets = offsets; b.El = El; b.n_chunks = n; b.P_c = P_c;
-  hipLaunchKernelGGL(simt_kgroup_kernel, dim3(El * ((2 * I + 63) / 64) * ((H + 63) / 64)), dim3(256), 0, s, b);
+  {
+    MOE_TRACE("gemm_wgrad_gateup_f32", s);
+    hipLaunchKernelGGL(simt_kgroup_kernel, dim3(El * ((2 * I + 63) / 64) * ((H + 63) / 64)), dim3(256), 0, s, b);
+  }
   return hipGetLastError();
 }
 
@@ -818,12 +846,18 @@ hipError_t launch_router_wgrad(bool bf16, const float* dlogits, const void* x, f
       KGroupArgs a{};
       a.A = dlogits; a.B = (const uint16_t*)x; a.C = partials; a.lda = E; a.ldb = H;
       a.strideC = (int64_t)E * H; a.M = E; a.N = H; a.k0 = t0; a.klen = len; a.ksplit = ks;
-      hipLaunchKernelGGL(k, dim3(S * ((E + BM - 1) / BM) * ((H + BN - 1) / BN)), dim3(kThreads), lds, s, a);
+      {
+        MOE_TRACE("gemm_router_wgrad", s);
+        hipLaunchKernelGGL(k, dim3(S * ((E + BM - 1) / BM) * ((H + BN - 1) / BN)), dim3(kThreads), lds, s, a);
+      }
     } else {
       SimtKArgs a{};
       a.A = dlogits; a.B = (const float*)x; a.C = partials; a.lda = E; a.ldb = H;
       a.strideC = (int64_t)E * H; a.M = E; a.N = H; a.k0 = t0; a.klen = len; a.ksplit = ks; a.router = true;
-      hipLaunchKernelGGL(simt_kgroup_kernel, dim3(S * ((E + 63) / 64) * ((H + 63) / 64)), dim3(256), 0, s, a);
+      {
+        MOE_TRACE("gemm_router_wgrad_f32", s);
+        hipLaunchKernelGGL(simt_kgroup_kernel, dim3(S * ((E + 63) / 64) * ((H + 63) / 64)), dim3(256), 0, s, a);
+      }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -833,11 +867,17 @@ hipError_t launch_router_wgrad(bool bf16, const float* dlogits, const void* x, f
   const int64_t MN = (int64_t)E * H;
   dim3 g((unsigned)((MN + 255) / 256));
   if (bf16)
-    hipLaunchKernelGGL(reduce_partials_kernel<uint16_t>, g, dim3(256), 0, s, partials, S, MN, dwr_acc,
-                       first, (uint16_t*)dwr);
+    {
+      MOE_TRACE("router_reduce", s);
+      hipLaunchKernelGGL(reduce_partials_kernel<uint16_t>, g, dim3(256), 0, s, partials, S, MN, dwr_acc,
+                         first, (uint16_t*)dwr);
+    }
   else
-    hipLaunchKernelGGL(reduce_partials_kernel<float>, g, dim3(256), 0, s, partials, S, MN, dwr_acc,
-                       first, (float*)dwr);
+    {
+      MOE_TRACE("router_reduce", s);
+      hipLaunchKernelGGL(reduce_partials_kernel<float>, g, dim3(256), 0, s, partials, S, MN, dwr_acc,
+                         first, (float*)dwr);
+    }
   return hipGetLastError();
 }
 

@@ -15,6 +15,7 @@
 //                same expert from per-wave 64-bit ballot masks (popcount below the lane).
 #include "common.h"
 #include "launch.h"
+#include "trace.h"
 
 namespace moe {
 
@@ -174,10 +175,12 @@ hipError_t launch_route(const float* logits, int32_t* topk_idx, float* gates, in
   size_t sm1 = (size_t)E * sizeof(int);
   switch (K) {
 #define MOE_ROUTE_K(KK)                                                                      \
-  case KK:                                                                                   \
+  case KK: {                                                                                 \
+    MOE_TRACE("route_topk", s);                                                              \
     hipLaunchKernelGGL(route_topk_kernel<KK>, grid, block, sm1, s, logits, topk_idx, gates, \
                        scratch, T, E, n, chunk0, nbpc);                                      \
-    break;
+    break;                                                                                   \
+  }
     MOE_ROUTE_K(1) MOE_ROUTE_K(2) MOE_ROUTE_K(3) MOE_ROUTE_K(4)
     MOE_ROUTE_K(5) MOE_ROUTE_K(6) MOE_ROUTE_K(7) MOE_ROUTE_K(8)
 #undef MOE_ROUTE_K
@@ -186,8 +189,11 @@ hipError_t launch_route(const float* logits, int32_t* topk_idx, float* gates, in
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   size_t sm2 = (size_t)El * 4 + (size_t)(El + 1) * 4 + 8 + (size_t)4 * El * 8 + (size_t)4 * El * 4;
-  hipLaunchKernelGGL(route_layout_kernel, grid, block, sm2, s, topk_idx, scratch, counts, offsets,
-                     row_of, src_token, T, E, e0, El, K, n, chunk0, nbpc, P_c);
+  {
+    MOE_TRACE("route_layout", s);
+    hipLaunchKernelGGL(route_layout_kernel, grid, block, sm2, s, topk_idx, scratch, counts, offsets,
+                       row_of, src_token, T, E, e0, El, K, n, chunk0, nbpc, P_c);
+  }
   return hipGetLastError();
 }
 

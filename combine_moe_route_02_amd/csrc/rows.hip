@@ -9,6 +9,7 @@
 // gives combine's fresh [P, H] output cropped to the logical rows: only rows t < T are written.
 #include "common.h"
 #include "launch.h"
+#include "trace.h"
 
 namespace moe {
 
@@ -344,24 +345,33 @@ static inline dim3 tok_grid(int64_t ntok) { return dim3((unsigned)((ntok + kTokP
 hipError_t launch_dispatch(const void* x, const int32_t* row_of, void* xd, int64_t t0, int64_t t1,
                            int K, int64_t row_bytes, hipStream_t s) {
   if (t1 <= t0) return hipSuccess;
-  hipLaunchKernelGGL(dispatch_copy_kernel, tok_grid(t1 - t0), dim3(256), 0, s, (const u32x4*)x,
-                     row_of, (u32x4*)xd, t0, t1, K, row_bytes / 16);
+  {
+    MOE_TRACE("dispatch", s);
+    hipLaunchKernelGGL(dispatch_copy_kernel, tok_grid(t1 - t0), dim3(256), 0, s, (const u32x4*)x,
+                       row_of, (u32x4*)xd, t0, t1, K, row_bytes / 16);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_dispatch_fp8(const void* x, const int32_t* row_of, void* xd, float* xd_scale,
                                float* h_scale, int64_t t0, int64_t t1, int K, int H, hipStream_t s) {
   if (t1 <= t0) return hipSuccess;
-  hipLaunchKernelGGL(dispatch_fp8_kernel, tok_grid(t1 - t0), dim3(256), 0, s, (const u32x4*)x,
-                     row_of, (uint2*)xd, xd_scale, h_scale, t0, t1, K, (int64_t)H / 8);
+  {
+    MOE_TRACE("dispatch_fp8", s);
+    hipLaunchKernelGGL(dispatch_fp8_kernel, tok_grid(t1 - t0), dim3(256), 0, s, (const u32x4*)x,
+                       row_of, (uint2*)xd, xd_scale, h_scale, t0, t1, K, (int64_t)H / 8);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_quantize_rows_fp8(const void* src, void* codes, float* scale, int64_t rows,
                                     int cols, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(quantize_rows_fp8_kernel, tok_grid(rows), dim3(256), 0, s, (const u32x4*)src,
-                     (uint2*)codes, scale, rows, (int64_t)cols / 8);
+  {
+    MOE_TRACE("quantize_rows_fp8", s);
+    hipLaunchKernelGGL(quantize_rows_fp8_kernel, tok_grid(rows), dim3(256), 0, s, (const u32x4*)src,
+                       (uint2*)codes, scale, rows, (int64_t)cols / 8);
+  }
   return hipGetLastError();
 }
 
@@ -369,11 +379,17 @@ hipError_t launch_combine(bool bf16, const void* yd, const float* gates, const i
                           void* out, int64_t t0, int64_t t1, int K, int64_t row_bytes, hipStream_t s) {
   if (t1 <= t0) return hipSuccess;
   if (bf16)
-    hipLaunchKernelGGL(combine_kernel<uint16_t>, tok_grid(t1 - t0), dim3(256), 0, s,
-                       (const u32x4*)yd, gates, row_of, (u32x4*)out, t0, t1, K, row_bytes / 16);
+    {
+      MOE_TRACE("combine", s);
+      hipLaunchKernelGGL(combine_kernel<uint16_t>, tok_grid(t1 - t0), dim3(256), 0, s,
+                         (const u32x4*)yd, gates, row_of, (u32x4*)out, t0, t1, K, row_bytes / 16);
+    }
   else
-    hipLaunchKernelGGL(combine_kernel<float>, tok_grid(t1 - t0), dim3(256), 0, s,
-                       (const u32x4*)yd, gates, row_of, (u32x4*)out, t0, t1, K, row_bytes / 16);
+    {
+      MOE_TRACE("combine", s);
+      hipLaunchKernelGGL(combine_kernel<float>, tok_grid(t1 - t0), dim3(256), 0, s,
+                         (const u32x4*)yd, gates, row_of, (u32x4*)out, t0, t1, K, row_bytes / 16);
+    }
   return hipGetLastError();
 }
 
@@ -382,13 +398,19 @@ hipError_t launch_combine_bwd(bool bf16, const void* dy, const void* yd, const f
                               int64_t t1, int K, int64_t row_bytes, hipStream_t s) {
   if (t1 <= t0) return hipSuccess;
   if (bf16)
-    hipLaunchKernelGGL(combine_bwd_kernel<uint16_t>, tok_grid(t1 - t0), dim3(256), 0, s,
-                       (const u32x4*)dy, (const u32x4*)yd, gates, row_of, (u32x4*)dyd, dgates,
-                       t0, t1, K, row_bytes / 16);
+    {
+      MOE_TRACE("combine_bwd", s);
+      hipLaunchKernelGGL(combine_bwd_kernel<uint16_t>, tok_grid(t1 - t0), dim3(256), 0, s,
+                         (const u32x4*)dy, (const u32x4*)yd, gates, row_of, (u32x4*)dyd, dgates,
+                         t0, t1, K, row_bytes / 16);
+    }
   else
-    hipLaunchKernelGGL(combine_bwd_kernel<float>, tok_grid(t1 - t0), dim3(256), 0, s,
-                       (const u32x4*)dy, (const u32x4*)yd, gates, row_of, (u32x4*)dyd, dgates,
-                       t0, t1, K, row_bytes / 16);
+    {
+      MOE_TRACE("combine_bwd", s);
+      hipLaunchKernelGGL(combine_bwd_kernel<float>, tok_grid(t1 - t0), dim3(256), 0, s,
+                         (const u32x4*)dy, (const u32x4*)yd, gates, row_of, (u32x4*)dyd, dgates,
+                         t0, t1, K, row_bytes / 16);
+    }
   return hipGetLastError();
 }
 
@@ -396,8 +418,11 @@ hipError_t launch_route_bwd_dlogits(const float* dgates, const float* gates, con
                                     float* dlogits, int64_t t0, int64_t t1, int K, int E,
                                     hipStream_t s) {
   if (t1 <= t0) return hipSuccess;
-  hipLaunchKernelGGL(route_bwd_dlogits_kernel, tok_grid(t1 - t0), dim3(256), 0, s, dgates, gates,
-                     idx, dlogits, t0, t1, K, E);
+  {
+    MOE_TRACE("route_bwd_dlogits", s);
+    hipLaunchKernelGGL(route_bwd_dlogits_kernel, tok_grid(t1 - t0), dim3(256), 0, s, dgates, gates,
+                       idx, dlogits, t0, t1, K, E);
+  }
   return hipGetLastError();
 }
 
@@ -406,13 +431,19 @@ hipError_t launch_dispatch_bwd(bool bf16, const void* dxd, const int32_t* row_of
                                int64_t t1, int K, int E, int64_t row_bytes, hipStream_t s) {
   if (t1 <= t0) return hipSuccess;
   if (bf16)
-    hipLaunchKernelGGL(dispatch_bwd_kernel<uint16_t>, tok_grid(t1 - t0), dim3(256), 0, s,
-                       (const u32x4*)dxd, row_of, idx, dlogits, (const u32x4*)w_r, (u32x4*)dx,
-                       t0, t1, K, E, row_bytes / 16);
+    {
+      MOE_TRACE("dispatch_bwd", s);
+      hipLaunchKernelGGL(dispatch_bwd_kernel<uint16_t>, tok_grid(t1 - t0), dim3(256), 0, s,
+                         (const u32x4*)dxd, row_of, idx, dlogits, (const u32x4*)w_r, (u32x4*)dx,
+                         t0, t1, K, E, row_bytes / 16);
+    }
   else
-    hipLaunchKernelGGL(dispatch_bwd_kernel<float>, tok_grid(t1 - t0), dim3(256), 0, s,
-                       (const u32x4*)dxd, row_of, idx, dlogits, (const u32x4*)w_r, (u32x4*)dx,
-                       t0, t1, K, E, row_bytes / 16);
+    {
+      MOE_TRACE("dispatch_bwd", s);
+      hipLaunchKernelGGL(dispatch_bwd_kernel<float>, tok_grid(t1 - t0), dim3(256), 0, s,
+                         (const u32x4*)dxd, row_of, idx, dlogits, (const u32x4*)w_r, (u32x4*)dx,
+                         t0, t1, K, E, row_bytes / 16);
+    }
   return hipGetLastError();
 }
 

@@ -227,6 +227,18 @@ moe_status moe_extent_acquire(moe_extent_tracker* tr, int64_t rows, int64_t* han
 moe_status moe_extent_release(moe_extent_tracker* tr, int64_t handle);
 int64_t moe_extent_current(const moe_extent_tracker* tr, int64_t required_rows);
 
+/* Launch log and per-kernel timing (tracing; torchtitan PR 5542 "Verification" checks the issue
+ * order of input-gradient work against weight-gradient GEMMs from a launch trace). After
+ * moe_trace_enable(timing), every kernel the library launches from this thread is appended to
+ * a thread-local log with its name and stream; with timing != 0 it is bracketed by two HIP
+ * events on that stream. moe_trace_enable clears the log. moe_trace_entry returns entry i
+ * (name: static string; ms: device duration, -1 without timing; waits for that entry's end
+ * event). Tracing adds host work per launch; it is off by default. */
+moe_status moe_trace_enable(int32_t timing);
+moe_status moe_trace_disable(void);
+int64_t moe_trace_count(void);
+moe_status moe_trace_entry(int64_t i, const char** name, void** stream, float* ms);
+
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* moe_last_error(void);
 /* ABI version (incremented on any incompatible change). */

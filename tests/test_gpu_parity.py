@@ -144,3 +144,29 @@ def test_full_fused_16k_forward_backward():
     ref = harness.run_oracle(run)
     print("[fb16k fwd]", harness.check_forward(run, ref), flush=True)
     print("[fb16k bwd]", harness.check_backward(run, ref), flush=True)
+
+
+def test_backward_launch_order_input_grad_before_wgrad():
+    """Every chunk's input-gradient work (combine backward, expert dgrad, dispatch backward) is
+    issued before the expert weight-gradient GEMMs, and chunk c+1's routing/dispatch is issued on
+    the auxiliary stream before chunk c's combine."""
+    _require_gpu()
+    import combine_moe_route_02_amd as mh
+    cfg = SMALL[3]
+    mh.moe_trace_enable(False)
+    try:
+        run = harness.run_gpu(cfg)
+    finally:
+        mh.moe_trace_disable()
+    log = mh.moe_trace_entries()
+    names = [n for n, _, _ in log]
+    first_wgrad = min(i for i, n in enumerate(names) if n.startswith("gemm_wgrad"))
+    for kind in ("combine_bwd", "gemm_down_dgrad_swiglu", "gemm_gateup_dgrad", "dispatch_bwd"):
+        idx = [i for i, n in enumerate(names) if n == kind]
+        assert len(idx) == cfg.n_chunks, (kind, idx)
+        assert max(idx) < first_wgrad, kind
+    # forward overlap order: route of chunk 1 precedes combine of chunk 0
+    assert names.index("route_topk", names.index("route_topk") + 1) < names.index("combine")
+    streams = {n: s for n, s, _ in log}
+    assert streams["dispatch"] == streams["combine"] != streams["gemm_gateup_swiglu"]
+    assert streams["gemm_wgrad_gateup"] == streams["gemm_gateup_swiglu"]
