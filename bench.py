@@ -171,6 +171,39 @@ def main():
     torch.cuda.synchronize()
     ms_fwd = (time.perf_counter() - f0) * 1e3 / args.steps
 
+    # isolated: the same stage calls chunk by chunk on one stream (no two-stream overlap), for
+    # each kernel's own cost
+    def stages():
+        b = bufs
+        for c in range(cfg.n_chunks):
+            mh.moe_route(d, c, b["logits"], b["topk_idx"], b["gates"], b["counts"], b["offsets"], b["row_of"],
+                         b["src_token"], b["workspace"], cs)
+            mh.moe_dispatch(d, c, b["x"], b["row_of"], b["xd"], None, None, cs)
+            mh.moe_expert_ffn(d, c, b["xd"], None, b["w1"], None, b["w2"], None, b["offsets"], b["gu"], b["h"],
+                              None, b["yd"], cs)
+            mh.moe_combine(d, c, b["yd"], b["gates"], b["row_of"], b["out"], cs)
+        for c in range(cfg.n_chunks):
+            mh.moe_combine_bwd(d, c, b["dy"], b["yd"], b["gates"], b["row_of"], b["dyd"], b["dgates"], cs)
+            mh.moe_route_bwd(d, c, b["dgates"], b["gates"], b["topk_idx"], b["x"], b["dlogits"], b["dwr_acc"],
+                             b["dwr"], b["workspace"], cs)
+            mh.moe_expert_ffn_bwd(d, c, b["dyd"], b["xd"], b["gu"], b["h"], b["w1"], b["w2"], b["offsets"],
+                                  b["dgu"], b["dxd"], None, None, cs)
+            mh.moe_dispatch_bwd(d, c, b["dxd"], b["row_of"], b["topk_idx"], b["dlogits"], b["w_r"], b["dx"], cs)
+        mh.moe_expert_wgrad(d, b["dyd"], b["dgu"], b["xd"], b["h"], b["offsets"], b["dw1"], b["dw2"], cs)
+
+    stages()
+    torch.cuda.synchronize()
+    mh.moe_trace_enable(True)
+    for _ in range(args.steps):
+        stages()
+    torch.cuda.synchronize()
+    mh.moe_trace_disable()
+    iso = {}
+    for name, _stream, ms in mh.moe_trace_entries():
+        p = iso.setdefault(name, [0, 0.0])
+        p[0] += 1
+        p[1] += ms
+
     counts = bufs["counts"].cpu().numpy()
     offsets = bufs["offsets"].cpu().numpy()
     row_of = bufs["row_of"].cpu().numpy()
@@ -194,6 +227,13 @@ def main():
                 entry.update(achieved_tflops=round(rate / 1e12, 2), frac_mfma=round(rate / 1e12 / PEAK_BF16_TFLOPS, 4))
             else:
                 entry.update(achieved_gbs=round(rate / 1e9, 1), frac_hbm=round(rate / 1e9 / PEAK_HBM_GBS, 4))
+        if name in iso:
+            ic, it = iso[name]
+            entry["isolated_avg_us"] = round(it / ic * 1e3, 3)
+            if name in work:
+                wk, unit = work[name]
+                r = wk / (it / args.steps * 1e-3)
+                entry["isolated_frac"] = round(r / 1e12 / PEAK_BF16_TFLOPS if unit == "flop" else r / 1e9 / PEAK_HBM_GBS, 4)
         kernels[name] = entry
     dom = max(per, key=lambda n: per[n][1])
     dcnt, dtot = per[dom]
@@ -209,6 +249,7 @@ def main():
                 "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "kernel": dom,
                 "avg_launch_us": round(dtot / dcnt * 1e3, 3), "work_per_launch": wk / (dcnt / args.steps)}
 
+    iso_ms = sum(v[1] for v in iso.values()) / args.steps
     gemm_flops = sum(work[n][0] for n in GEMM_KERNELS)
     gemm_ms = sum(per[n][1] for n in GEMM_KERNELS if n in per) / args.steps
     value = cfg.T / (ms_per_step * 1e-3)
@@ -223,6 +264,7 @@ def main():
                    "local_rows": N, "tokens_with_local_expert": Tt},
         "fwd_tokens_per_s": round(cfg.T / (ms_fwd * 1e-3), 1), "fwd_ms": round(ms_fwd, 4),
         "ms_per_step_untraced": round(ms_untraced, 4),
+        "isolated_kernel_ms_sum": round(iso_ms, 4),
         "gemm_tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 2) if gemm_ms > 0 else None,
         "roofline": roof, "kernels": kernels,
     }

@@ -26,80 +26,143 @@ constexpr int BK = 64;
 constexpr int kThreads = 256;
 constexpr int kMaxGroups = 1024;
 
-MOE_DEV int sw(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 3); }
+// LDS tile address (in BF16 elements) of 16-byte chunk `chunk` of tile row `row`: rows of 128 bytes
+// with the chunk XOR-swizzled by row % 8, so that 8 consecutive rows read at one chunk (MFMA
+// fragments) and the 8 chunks of one row (staging writes) each cover all banks; row % 8 does
+// not change between 32-row MFMA blocks, so their addresses differ by constants.
+#ifndef MOE_SWZ
+#define MOE_SWZ 0
+#endif
+MOE_DEV int swz(int row) {
+#if MOE_SWZ == 0
+  return row & 7;
+#elif MOE_SWZ == 1
+  return (row ^ (row >> 3) ^ (row >> 4)) & 7;
+#else
+  return (row ^ (row >> 3)) & 7;
+#endif
+}
+MOE_DEV int sw(int row, int chunk) { return row * BK + ((chunk ^ swz(row)) << 3); }
 
 MOE_DEV u32x4 zero4() { return {0u, 0u, 0u, 0u}; }
 
 // ---------------------------------------------------------------------------------------------
 // Operand staging (global -> registers -> LDS)
 
-// K-contiguous rows: tile row r at rowptr(r) + k. R rows x 64 BF16; R/32 vectors per thread.
-template <int R>
+// Operands are staged with raw buffer loads: the tile's base address and its valid extent
+// live in a scalar buffer descriptor (reads past num_records return zero, which masks rows
+// beyond an expert's segment or a matrix edge), each lane keeps one 32-bit byte offset, and
+// the per-row / per-stage offsets are wave-uniform scalar offsets.
+typedef __attribute__((ext_vector_type(4))) int i32x4_t;
+typedef __attribute__((ext_vector_type(2))) int i32x2_t;
+constexpr int kBufferWord3 = 0x00020000;  // gfx9-family raw buffer descriptor word 3
+
+MOE_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int64_t lim = 0x7fffffff;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)(bytes < 0 ? 0 : (bytes > lim ? lim : bytes)),
+                                           kBufferWord3);
+}
+
+// K-contiguous rows, R rows x 64 BF16 per stage; thread tid stages rows tid/8 + 32*i (i < R/32),
+// 16-byte chunk tid%8 of each. SWIGLU_WTN > 0 maps tile rows to interleaved gate/up weight rows
+// (per wave column block of SWIGLU_WTN rows: first half gate rows j, second half up rows I + j).
+template <int R, int SWIGLU_WTN = 0>
 struct KMajor {
   static constexpr int NV = R / 32;
-  const uint16_t* p[NV];
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t voff;  // this lane's byte offset (row tid/8, chunk tid%8)
+  uint32_t ldb;   // bytes between consecutive rows
+  uint32_t upb;   // SwiGLU: bytes from a gate row to its up row
   u32x4 v[NV];
-  MOE_DEV void fetch(int k0) {
-#pragma unroll
-    for (int i = 0; i < NV; ++i) v[i] = p[i] ? *(const u32x4*)(p[i] + k0) : zero4();
+  // base: row 0 of the tile; valid_rows: rows readable from base (beyond them loads return 0)
+  MOE_DEV void init(const uint16_t* base, int64_t ld, int64_t valid_rows, int tid, int64_t up_rows = 0,
+                   uint32_t run_time_zero = 0) {
+    zero = run_time_zero;
+    ldb = (uint32_t)(ld * 2);
+    upb = (uint32_t)(up_rows * ld * 2);
+    rsrc = make_rsrc(base, valid_rows * ld * 2);
+    voff = (uint32_t)(tid >> 3) * ldb + (uint32_t)(tid & 7) * 16u;
   }
+  MOE_DEV uint32_t offset(int i) const {
+    if constexpr (SWIGLU_WTN == 0) {
+      return (uint32_t)(32 * i) * ldb;
+    } else {
+      const int r0 = 32 * i;  // tid/8 < 32 never crosses a 32-row boundary
+      const int wb = r0 / SWIGLU_WTN, q0 = r0 % SWIGLU_WTN, hw = SWIGLU_WTN / 2;
+      const int j0 = wb * hw + (q0 < hw ? q0 : q0 - hw);
+      return (uint32_t)j0 * ldb + (q0 < hw ? 0u : upb);
+    }
+  }
+  MOE_DEV void fetch(int k0, int /*tid*/) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      i32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)voff, (int)(offset(i) + (uint32_t)k0 * 2u), 0);
+      v[i] = u32x4{(uint32_t)t.x, (uint32_t)t.y, (uint32_t)t.z, (uint32_t)t.w};
+    }
+  }
+  uint32_t zero;  // 0 at run time; XOR-ing it keeps the staging data in VGPRs (see commit)
+  // The XOR with a run-time zero is a VALU use of the staged data: without it the register
+  // allocator may keep the staging registers in AGPRs, where they compete with the MFMA
+  // accumulators and spill inside the K loop.
   MOE_DEV void commit(uint16_t* lds, int tid) const {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       int id = tid + i * kThreads;
-      *(u32x4*)(lds + sw(id >> 3, id & 7)) = v[i];
+      *(u32x4*)(lds + sw(id >> 3, id & 7)) = u32x4{v[i].x ^ zero, v[i].y ^ zero, v[i].z ^ zero, v[i].w ^ zero};
     }
   }
-  // row r of thread's i-th vector
-  MOE_DEV static int row_of(int tid, int i) { return (tid + i * kThreads) >> 3; }
-  MOE_DEV static int chunk_of(int tid) { return tid & 7; }
+  MOE_DEV static int row_of(int tid, int i) { return (tid >> 3) + 32 * i; }
 };
 
 // K along HBM rows: element (mn, k) at base[k * ld + mn]. One block of 8 K-rows x V columns per
-// thread (V = R/32), transposed in registers into V K-contiguous 16-byte chunks.
-template <int R>
+// thread (V = R/32; K block tid%8, mn block tid/8), transposed in registers into V K-contiguous
+// 16-byte chunks. Each group of 8 lanes then writes the 8 chunks of the same LDS rows
+// (conflict-free), and each global load instruction reads whole 128-byte lines.
+template <int R, bool MASK_K = true>
 struct KSlow {
   static constexpr int V = R / 32;
-  static constexpr int W = V / 2;           // dwords per loaded K-row (V BF16 values)
-  const uint16_t* base;                     // points at (k = 0, mn = this thread's first column)
-  int64_t ld;
-  int kvalid;                               // K rows valid in the current segment
-  bool mnok;
+  static constexpr int W = V / 2;  // dwords per loaded K-row (V BF16 values)
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t voff;                   // (8 * kblk) K-rows + this lane's mn block, in bytes
+  uint32_t ldb;                    // bytes between K-rows
   uint32_t v[8][W];
-  MOE_DEV int mnblk(int tid) const { return tid & 31; }
-  MOE_DEV int kblk(int tid) const { return tid >> 5; }
-  MOE_DEV void fetch(int k0, int tid) {
-    const int kb = k0 + 8 * kblk(tid);
+  MOE_DEV int mnblk(int tid) const { return tid >> 3; }
+  MOE_DEV int kblk(int tid) const { return tid & 7; }
+  // base: element (k = 0, mn = 0) of the tile; valid_k: K-rows readable (later rows load 0)
+  MOE_DEV void init(const uint16_t* base, int64_t ld, int64_t valid_k, int tid) {
+    ldb = (uint32_t)(ld * 2);
+    rsrc = make_rsrc(base, valid_k * ld * 2);
+    voff = (uint32_t)(8 * kblk(tid)) * ldb + (uint32_t)(mnblk(tid) * V * 2);
+  }
+  MOE_DEV void fetch(int k0, int /*tid*/) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      bool ok = mnok && (kb + i) < kvalid;
-      const uint16_t* q = base + (int64_t)(kb + i) * ld;
+      const int so = (int)((uint32_t)(k0 + i) * ldb);
       if constexpr (W == 4) {
-        u32x4 t = ok ? *(const u32x4*)q : zero4();
+        i32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)voff, so, 0);
         v[i][0] = t.x; v[i][1] = t.y; v[i][2] = t.z; v[i][3] = t.w;
       } else if constexpr (W == 2) {
-        uint2 t = ok ? *(const uint2*)q : make_uint2(0u, 0u);
+        i32x2_t t = __builtin_amdgcn_raw_buffer_load_b64(rsrc, (int)voff, so, 0);
         v[i][0] = t.x; v[i][1] = t.y;
       } else {
-        v[i][0] = ok ? *(const uint32_t*)q : 0u;
+        v[i][0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, (int)voff, so, 0);
       }
     }
   }
+  // Column pair (2p, 2p+1) comes from dword p of every loaded K-row.
   MOE_DEV void commit(uint16_t* lds, int tid) const {
     const int mb = mnblk(tid), kb = kblk(tid);
 #pragma unroll
-    for (int c = 0; c < V; ++c) {
-      const int half = c & 1, wd = c >> 1;
-      u32x4 o;
-      uint32_t w[4];
+    for (int p = 0; p < V / 2; ++p) {
+      uint32_t e[4], o[4];  // even column 2p and odd column 2p+1, 8 K values each
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        uint32_t lo = half ? (v[2 * q][wd] >> 16) : (v[2 * q][wd] & 0xffffu);
-        uint32_t hi = half ? (v[2 * q + 1][wd] & 0xffff0000u) : (v[2 * q + 1][wd] << 16);
-        w[q] = lo | hi;
+        e[q] = (v[2 * q][p] & 0xffffu) | (v[2 * q + 1][p] << 16);
+        o[q] = (v[2 * q][p] >> 16) | (v[2 * q + 1][p] & 0xffff0000u);
       }
-      o.x = w[0]; o.y = w[1]; o.z = w[2]; o.w = w[3];
-      *(u32x4*)(lds + sw(mb * V + c, kb)) = o;
+      const int r0 = mb * V + 2 * p;
+      *(u32x4*)(lds + sw(r0, kb)) = u32x4{e[0], e[1], e[2], e[3]};
+      *(u32x4*)(lds + sw(r0 + 1, kb)) = u32x4{o[0], o[1], o[2], o[3]};
     }
   }
 };
@@ -107,26 +170,27 @@ struct KSlow {
 // FP32 operand with K along HBM rows, split into BF16 high and low parts (x = hi + lo + O(2^-17 x)).
 template <int R>
 struct KSlowSplit {
-  static constexpr int V = R / 32;
-  const float* base;
-  int64_t ld;
-  int kvalid;
+  static constexpr int V = R / 32;  // floats per K-row (V/4 16-byte loads)
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t voff, ldb;
   float v[8][V];
-  MOE_DEV void fetch(int k0, int tid) {
-    const int kb = k0 + 8 * (tid >> 5);
+  MOE_DEV void init(const float* base, int64_t ld, int64_t valid_k, int tid) {
+    ldb = (uint32_t)(ld * 4);
+    rsrc = make_rsrc(base, valid_k * ld * 4);
+    voff = (uint32_t)(8 * (tid & 7)) * ldb + (uint32_t)((tid >> 3) * V * 4);
+  }
+  MOE_DEV void fetch(int k0, int /*tid*/) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      bool ok = (kb + i) < kvalid;
-      const float* q = base + (int64_t)(kb + i) * ld;
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int c = 0; c < V; c += 4) {
-        float4 t = ok ? *(const float4*)(q + c) : make_float4(0.f, 0.f, 0.f, 0.f);
-        v[i][c] = t.x; v[i][c + 1] = t.y; v[i][c + 2] = t.z; v[i][c + 3] = t.w;
+        i32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)voff + 4 * c, (int)((uint32_t)(k0 + i) * ldb), 0);
+        v[i][c] = __int_as_float(t.x); v[i][c + 1] = __int_as_float(t.y);
+        v[i][c + 2] = __int_as_float(t.z); v[i][c + 3] = __int_as_float(t.w);
       }
-    }
   }
   MOE_DEV void commit(uint16_t* lds_hi, uint16_t* lds_lo, int tid) const {
-    const int mb = tid & 31, kb = tid >> 5;
+    const int mb = tid >> 3, kb = tid & 7;
 #pragma unroll
     for (int c = 0; c < V; ++c) {
       uint32_t wh[4], wl[4];
@@ -146,6 +210,10 @@ struct KSlowSplit {
 
 // ---------------------------------------------------------------------------------------------
 // MFMA inner product over one LDS stage: acc[tm][tn] += A[rows] * B[rows]^T over 64 K.
+// The MFMA is issued with the B fragment as its first operand, so the 32x32 result block is
+// transposed: lane l holds output row (l & 31) and, for accumulator element i, output column
+// 8*(i/4) + 4*(l/32) + i%4 -- four consecutive columns per group of four elements, which the
+// epilogues store as one 8-byte BF16 vector.
 template <int TM, int TN>
 MOE_DEV void mma_stage(const uint16_t* la, const uint16_t* lb, int arow0, int brow0, int lane,
                        f32x16_t (&acc)[TM][TN]) {
@@ -161,13 +229,46 @@ MOE_DEV void mma_stage(const uint16_t* la, const uint16_t* lb, int arow0, int br
     for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn)
-        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[tm], b[tn], acc[tm][tn], 0, 0, 0);
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[tn], a[tm], acc[tm][tn], 0, 0, 0);
   }
 }
 
-// Output coordinates of accumulator element i of a 32x32 MFMA tile held by `lane`.
-MOE_DEV int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
-MOE_DEV int acc_col(int lane) { return lane & 31; }
+// Output coordinates inside a 32x32 block for lane `lane`: row, and first column of group g.
+MOE_DEV int out_row(int lane) { return lane & 31; }
+MOE_DEV int out_col(int g, int lane) { return 8 * g + 4 * (lane >> 5); }
+
+// K loop over nks LDS stages with a global-read prefetch depth of two: two register staging
+// sets per operand alternate, so the loads of stage s+2 are in flight while stage s is
+// multiplied and stage s+1 is committed to the other LDS buffer. Unrolled by two so that each
+// staging set is addressed statically.
+template <int TM, int TN, class LdA, class LdB>
+MOE_DEV void kloop_pgr2(LdA& a0, LdA& a1, LdB& b0, LdB& b1, int nks, uint16_t* A0, uint16_t* A1,
+                        uint16_t* B0, uint16_t* B1, int tid, int arow0, int brow0, int lane,
+                        f32x16_t (&acc)[TM][TN]) {
+  if (nks <= 0) return;
+  a0.fetch(0, tid);
+  b0.fetch(0, tid);
+  if (nks > 1) { a1.fetch(BK, tid); b1.fetch(BK, tid); }
+  a0.commit(A0, tid);
+  b0.commit(B0, tid);
+  __syncthreads();
+  for (int ks = 0; ks < nks; ks += 2) {
+    if (ks + 2 < nks) { a0.fetch((ks + 2) * BK, tid); b0.fetch((ks + 2) * BK, tid); }
+    mma_stage<TM, TN>(A0, B0, arow0, brow0, lane, acc);
+    if (ks + 1 < nks) { a1.commit(A1, tid); b1.commit(B1, tid); }
+    __syncthreads();
+    if (ks + 1 >= nks) break;
+    if (ks + 3 < nks) { a1.fetch((ks + 3) * BK, tid); b1.fetch((ks + 3) * BK, tid); }
+    mma_stage<TM, TN>(A1, B1, arow0, brow0, lane, acc);
+    if (ks + 2 < nks) { a0.commit(A0, tid); b0.commit(B0, tid); }
+    __syncthreads();
+  }
+}
+
+MOE_DEV uint2 pack4(float a, float b, float c, float d) { return make_uint2(pack_bf2(a, b), pack_bf2(c, d)); }
+MOE_DEV void unpack4(uint2 v, float* f) {
+  f[0] = bf2f(v.x & 0xffff); f[1] = bf2f(v.x >> 16); f[2] = bf2f(v.y & 0xffff); f[3] = bf2f(v.y >> 16);
+}
 
 // ---------------------------------------------------------------------------------------------
 // Row-grouped GEMMs (forward and input-gradient), persistent over device-side groups.
@@ -187,6 +288,8 @@ struct RowsArgs {
   const int32_t* offsets;
   int El, c0, nc;
   int64_t P_c;
+  uint32_t zero;         // always 0 (a value the compiler cannot fold)
+  int one;               // always 1 (trip count of the loop around the K loop)
 };
 
 template <int BM, int BN, int WM, int WN, int MODE>
@@ -224,50 +327,44 @@ __global__ __launch_bounds__(kThreads) void rows_gemm_kernel(RowsArgs a) {
   }
   __syncthreads();
   const int total = s_pre[G];
-
-  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+  // One tile per workgroup; the grid is a static upper bound and surplus workgroups exit.
+  // Workgroups are dealt round-robin to the 8 XCDs (block b runs on XCD b % 8); tile indices
+  // are assigned so that each XCD gets a contiguous range of ceil(total/8) tiles, and the tiles
+  // of one expert (same weights, same rows) share that XCD's L2.
+  const int per_xcd = (total + 7) / 8;
+  const int slot = blockIdx.x / 8;
+  {
+    const int tile = (blockIdx.x % 8) * per_xcd + slot;
+    if (slot >= per_xcd || tile >= total) return;
     int lo = 0, hi = G;  // find g with s_pre[g] <= tile < s_pre[g+1]
     while (hi - lo > 1) { int mid = (lo + hi) >> 1; if (s_pre[mid] <= tile) lo = mid; else hi = mid; }
-    const int g = lo;
+    // tile parameters are wave-uniform: keep them in scalar registers
+    const int g = __builtin_amdgcn_readfirstlane(lo);
     const int e = g % a.El;
-    const int t_in = tile - s_pre[g];
+    const int t_in = tile - __builtin_amdgcn_readfirstlane(s_pre[g]);
     const int mt = t_in / ntiles, nt = t_in % ntiles;
-    const int64_t r0 = s_r0[g] + (int64_t)mt * BM;
-    const int mvalid = min(BM, s_len[g] - mt * BM);
+    const int64_t rg = s_r0[g];
+    const int64_t r0 = (((int64_t)__builtin_amdgcn_readfirstlane((int)(rg >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((int)(rg & 0xffffffff))) + (int64_t)mt * BM;
+    const int mvalid = min(BM, __builtin_amdgcn_readfirstlane(s_len[g]) - mt * BM);
     const int n0 = nt * OUTN;
     const uint16_t* Be = a.B + (int64_t)e * a.strideB;
 
     KMajor<BM> ldA;
-#pragma unroll
-    for (int i = 0; i < KMajor<BM>::NV; ++i) {
-      int r = KMajor<BM>::row_of(tid, i);
-      ldA.p[i] = r < mvalid ? a.A + (r0 + r) * a.lda + KMajor<BM>::chunk_of(tid) * 8 : nullptr;
-    }
-    KMajor<BN> ldB;
-    KSlow<BN> ldBs;
+    ldA.init(a.A + r0 * a.lda, a.lda, mvalid, tid, 0, a.zero);
+    KMajor<BN, kSwiGLU ? WTN : 0> ldB;
+    KSlow<BN, false> ldBs;
     if constexpr (!kBSlow) {
-#pragma unroll
-      for (int i = 0; i < KMajor<BN>::NV; ++i) {
-        int r = KMajor<BN>::row_of(tid, i);
-        int grow;
-        if constexpr (kSwiGLU) {
-          // tile row r -> wave column block r / WTN; first half gate rows, second half up rows
-          int wb = r / WTN, q = r % WTN;
-          int j = n0 + wb * (WTN / 2) + (q < WTN / 2 ? q : q - WTN / 2);
-          grow = (q < WTN / 2) ? j : a.I + j;
-          ldB.p[i] = j < a.N ? Be + (int64_t)grow * a.K + KMajor<BN>::chunk_of(tid) * 8 : nullptr;
-        } else {
-          grow = n0 + r;
-          ldB.p[i] = grow < a.N ? Be + (int64_t)grow * a.K + KMajor<BN>::chunk_of(tid) * 8 : nullptr;
-        }
+      if constexpr (kSwiGLU) {
+        // tile row r -> wave column block r / WTN; first half gate rows, second half up rows;
+        // readable rows run to the end of this expert's W1 (gate rows past N are discarded)
+        ldB.init(Be + (int64_t)n0 * a.K, a.K, 2 * (int64_t)a.I - n0, tid, a.I, a.zero);
+      } else {
+        ldB.init(Be + (int64_t)n0 * a.K, a.K, (int64_t)a.N - n0, tid, 0, a.zero);
       }
     } else {
-      // B(n, k) = W_e[k * N + n]
-      ldBs.ld = a.N;
-      ldBs.kvalid = a.K;
-      int col = n0 + ldBs.mnblk(tid) * KSlow<BN>::V;
-      ldBs.mnok = col < a.N;
-      ldBs.base = Be + col;
+      // B(n, k) = W_e[k * N + n]: K-rows of N elements starting at column n0
+      ldBs.init(Be + n0, a.N, a.K, tid);
     }
 
     f32x16_t acc[TM][TN];
@@ -279,78 +376,94 @@ __global__ __launch_bounds__(kThreads) void rows_gemm_kernel(RowsArgs a) {
         for (int q = 0; q < 16; ++q) acc[tm][tn][q] = 0.f;
 
     const int nks = a.K / BK;
-    ldA.fetch(0);
-    if constexpr (kBSlow) ldBs.fetch(0, tid); else ldB.fetch(0);
-    ldA.commit(LA(0), tid);
-    if constexpr (kBSlow) ldBs.commit(LB(0), tid); else ldB.commit(LB(0), tid);
-    __syncthreads();
-    for (int ks = 0; ks < nks; ++ks) {
-      const int cur = ks & 1;
-      if (ks + 1 < nks) {
-        ldA.fetch((ks + 1) * BK);
-        if constexpr (kBSlow) ldBs.fetch((ks + 1) * BK, tid); else ldB.fetch((ks + 1) * BK);
+    KMajor<BM> ldA1 = ldA;
+    // a.one == 1: an enclosing loop the compiler cannot remove; with it the register allocator
+    // keeps the two staging sets and the accumulators in registers through the K loop
+    for (int rep = 0; rep < a.one; ++rep) {
+      if constexpr (kBSlow) {
+        KSlow<BN, false> ldBs1 = ldBs;
+        kloop_pgr2<TM, TN>(ldA, ldA1, ldBs, ldBs1, nks, LA(0), LA(1), LB(0), LB(1), tid, wm * WTM, wn * WTN,
+                           lane, acc);
+      } else {
+        auto ldB1 = ldB;
+        kloop_pgr2<TM, TN>(ldA, ldA1, ldB, ldB1, nks, LA(0), LA(1), LB(0), LB(1), tid, wm * WTM, wn * WTN,
+                           lane, acc);
       }
-      mma_stage<TM, TN>(LA(cur), LB(cur), wm * WTM, wn * WTN, lane, acc);
-      if (ks + 1 < nks) {
-        ldA.commit(LA(cur ^ 1), tid);
-        if constexpr (kBSlow) ldBs.commit(LB(cur ^ 1), tid); else ldB.commit(LB(cur ^ 1), tid);
-      }
-      __syncthreads();
     }
 
-    // epilogue
+    // epilogue: rows past the expert's segment and columns past N are not written
+    const int mrow = wm * WTM + out_row(lane);
     if constexpr (kSwiGLU) {
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
+      const int64_t I2 = 2 * (int64_t)a.I;
+#pragma clang loop unroll(full)
+      for (int tm = 0; tm < TM; ++tm) {
+        const int m = mrow + tm * 32;
+        if (m >= mvalid) continue;
+        const int64_t row = r0 + m;
+#pragma clang loop unroll(full)
         for (int tn = 0; tn < TN / 2; ++tn)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int m = wm * WTM + tm * 32 + acc_row(i, lane);
-            const int j = n0 + wn * (WTN / 2) + tn * 32 + acc_col(lane);
-            if (m < mvalid && j < a.N) {
-              const float gv = acc[tm][tn][i], uv = acc[tm][tn + TN / 2][i];
-              const float hv = gv * sigmoidf_(gv) * uv;
-              const int64_t row = r0 + m;
-              a.C[row * a.ldc + j] = f2bf(hv);
-              if (a.C2) {
-                a.C2[row * (2 * (int64_t)a.I) + j] = f2bf(gv);
-                a.C2[row * (2 * (int64_t)a.I) + a.I + j] = f2bf(uv);
-              }
+#pragma clang loop unroll(full)
+          for (int g = 0; g < 4; ++g) {
+            const int j = n0 + wn * (WTN / 2) + tn * 32 + out_col(g, lane);
+            if (j >= a.N) continue;
+            float gv[4], uv[4], hv[4];
+#pragma clang loop unroll(full)
+            for (int q = 0; q < 4; ++q) {
+              gv[q] = acc[tm][tn][4 * g + q];
+              uv[q] = acc[tm][tn + TN / 2][4 * g + q];
+              hv[q] = gv[q] * sigmoidf_(gv[q]) * uv[q];
+            }
+            *(uint2*)(a.C + row * a.ldc + j) = pack4(hv[0], hv[1], hv[2], hv[3]);
+            if (a.C2) {
+              *(uint2*)(a.C2 + row * I2 + j) = pack4(gv[0], gv[1], gv[2], gv[3]);
+              *(uint2*)(a.C2 + row * I2 + a.I + j) = pack4(uv[0], uv[1], uv[2], uv[3]);
             }
           }
+      }
     } else if constexpr (MODE == kDownBwd) {
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
+      const int64_t I2 = 2 * (int64_t)a.I;
+#pragma clang loop unroll(full)
+      for (int tm = 0; tm < TM; ++tm) {
+        const int m = mrow + tm * 32;
+        if (m >= mvalid) continue;
+        const int64_t row = r0 + m;
+#pragma clang loop unroll(full)
         for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int m = wm * WTM + tm * 32 + acc_row(i, lane);
-            const int j = n0 + wn * WTN + tn * 32 + acc_col(lane);
-            if (m < mvalid && j < a.N) {
-              const int64_t row = r0 + m;
-              const int64_t I2 = 2 * (int64_t)a.I;
-              const float gv = bf2f(a.aux[row * I2 + j]), uv = bf2f(a.aux[row * I2 + a.I + j]);
-              const float dh = acc[tm][tn][i];
-              const float s = sigmoidf_(gv);
-              a.C[row * I2 + j] = f2bf(dh * uv * s * (1.f + gv * (1.f - s)));
-              a.C[row * I2 + a.I + j] = f2bf(dh * gv * s);
+#pragma clang loop unroll(full)
+          for (int g = 0; g < 4; ++g) {
+            const int j = n0 + wn * WTN + tn * 32 + out_col(g, lane);
+            if (j >= a.N) continue;
+            float gv[4], uv[4], dg[4], du[4];
+            unpack4(*(const uint2*)(a.aux + row * I2 + j), gv);
+            unpack4(*(const uint2*)(a.aux + row * I2 + a.I + j), uv);
+#pragma clang loop unroll(full)
+            for (int q = 0; q < 4; ++q) {
+              const float dh = acc[tm][tn][4 * g + q];
+              const float sg = sigmoidf_(gv[q]);
+              dg[q] = dh * uv[q] * sg * (1.f + gv[q] * (1.f - sg));
+              du[q] = dh * gv[q] * sg;
             }
+            *(uint2*)(a.C + row * I2 + j) = pack4(dg[0], dg[1], dg[2], dg[3]);
+            *(uint2*)(a.C + row * I2 + a.I + j) = pack4(du[0], du[1], du[2], du[3]);
           }
+      }
     } else {
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
+#pragma clang loop unroll(full)
+      for (int tm = 0; tm < TM; ++tm) {
+        const int m = mrow + tm * 32;
+        if (m >= mvalid) continue;
+        const int64_t row = r0 + m;
+#pragma clang loop unroll(full)
         for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int m = wm * WTM + tm * 32 + acc_row(i, lane);
-            const int n = n0 + wn * WTN + tn * 32 + acc_col(lane);
-            if (m < mvalid && n < a.N) a.C[(r0 + m) * a.ldc + n] = f2bf(acc[tm][tn][i]);
+#pragma clang loop unroll(full)
+          for (int g = 0; g < 4; ++g) {
+            const int n = n0 + wn * WTN + tn * 32 + out_col(g, lane);
+            if (n >= a.N) continue;
+            const f32x16_t& v = acc[tm][tn];
+            *(uint2*)(a.C + row * a.ldc + n) = pack4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
           }
+      }
     }
-    __syncthreads();
   }
 }
 
@@ -413,23 +526,23 @@ __global__ __launch_bounds__(kThreads) void kgroup_gemm_kernel(KGroupArgs a) {
     }
     if (len <= 0) continue;
     KSlow<BN> ldB;
-    ldB.ld = a.ldb;
-    ldB.kvalid = len;
-    ldB.mnok = n0 + ldB.mnblk(tid) * KSlow<BN>::V < a.N;
-    ldB.base = a.B + row0 * a.ldb + n0 + ldB.mnblk(tid) * KSlow<BN>::V;
+    ldB.init(a.B + row0 * a.ldb + n0, a.ldb, len, tid);
     KSlow<BM> ldA;
     KSlowSplit<BM> ldAs;
     if constexpr (ROUTER) {
-      ldAs.ld = a.lda;
-      ldAs.kvalid = (m0 + (tid & 31) * KSlowSplit<BM>::V < a.M) ? len : 0;
-      ldAs.base = (const float*)a.A + row0 * a.lda + m0 + (tid & 31) * KSlowSplit<BM>::V;
+      ldAs.init((const float*)a.A + row0 * a.lda + m0, a.lda, len, tid);
     } else {
-      ldA.ld = a.lda;
-      ldA.kvalid = len;
-      ldA.mnok = m0 + ldA.mnblk(tid) * KSlow<BM>::V < a.M;
-      ldA.base = (const uint16_t*)a.A + row0 * a.lda + m0 + ldA.mnblk(tid) * KSlow<BM>::V;
+      ldA.init((const uint16_t*)a.A + row0 * a.lda + m0, a.lda, len, tid);
     }
     const int nks = (len + BK - 1) / BK;
+    if constexpr (!ROUTER) {
+      KSlow<BM> ldA1 = ldA;
+      KSlow<BN> ldB1 = ldB;
+      kloop_pgr2<TM, TN>(ldA, ldA1, ldB, ldB1, nks, LA(0), LA(1), LB(0), LB(1), tid, wm * WTM, wn * WTN,
+                         lane, acc);
+      __syncthreads();  // the next segment restages both LDS buffers
+      continue;
+    }
     if constexpr (ROUTER) { ldAs.fetch(0, tid); ldAs.commit(LA(0), LA(0) + BM * BK, tid); }
     else { ldA.fetch(0, tid); ldA.commit(LA(0), tid); }
     ldB.fetch(0, tid);
@@ -453,20 +566,24 @@ __global__ __launch_bounds__(kThreads) void kgroup_gemm_kernel(KGroupArgs a) {
   }
 
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm)
+  for (int tm = 0; tm < TM; ++tm) {
+    const int m = m0 + wm * WTM + tm * 32 + out_row(lane);
+    if (m >= a.M) continue;
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int m = m0 + wm * WTM + tm * 32 + acc_row(i, lane);
-        const int n = n0 + wn * WTN + tn * 32 + acc_col(lane);
-        if (m >= a.M || n >= a.N) continue;
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * WTN + tn * 32 + out_col(g, lane);
+        if (n >= a.N) continue;
+        const f32x16_t& v = acc[tm][tn];
+        const int64_t o = (int64_t)grp * a.strideC + (int64_t)m * a.N + n;
         if constexpr (ROUTER) {
-          ((float*)a.C)[(int64_t)grp * a.strideC + (int64_t)m * a.N + n] = acc[tm][tn][i];
+          *(float4*)((float*)a.C + o) = make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
         } else {
-          ((uint16_t*)a.C)[(int64_t)grp * a.strideC + (int64_t)m * a.N + n] = f2bf(acc[tm][tn][i]);
+          *(uint2*)((uint16_t*)a.C + o) = pack4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
         }
       }
+  }
 }
 
 #undef LA
@@ -495,6 +612,8 @@ struct SimtRowsArgs {
   const int32_t* offsets;
   int El, c0, nc;
   int64_t P_c;
+  uint32_t zero;  // unused by the SIMT kernels (shared launcher code sets it)
+  int one;
 };
 
 template <int MODE>
@@ -672,17 +791,26 @@ __global__ __launch_bounds__(256) void simt_kgroup_kernel(SimtKArgs a) {
 using namespace gemm;
 
 namespace {
-constexpr int kPersistentGrid = 512;  // 256 CUs x 2 resident workgroups
+constexpr int kSimtGrid = 512;  // persistent grid of the FP32 SIMT kernels
 
+// Grid: the static upper bound of tiles -- per chunk at most floor(P_c / BM) + E_local row
+// tiles (every expert adds at most one partial tile) times the column tiles -- rounded up to
+// the 8 XCDs. The device-side count decides which workgroups work.
 template <int BM, int BN, int WM, int WN, int MODE>
 hipError_t run_rows(const char* name, const RowsArgs& a, hipStream_t s) {
   size_t lds = (size_t)2 * (BM + BN) * BK * sizeof(uint16_t);
   auto k = rows_gemm_kernel<BM, BN, WM, WN, MODE>;
   hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
+  const int outn = (MODE == kGateUp) ? BN / 2 : BN;
+  const int64_t ntiles = (a.N + outn - 1) / outn;
+  const int64_t mtiles = (int64_t)a.nc * (a.P_c / BM + a.El);
+  const int64_t per_xcd = (mtiles * ntiles + 7) / 8;
+  const int64_t grid = per_xcd * 8;
+  if (grid <= 0) return hipSuccess;
   {
     MOE_TRACE(name, s);
-    hipLaunchKernelGGL(k, dim3(kPersistentGrid), dim3(kThreads), lds, s, a);
+    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kThreads), lds, s, a);
   }
   return hipGetLastError();
 }
@@ -696,32 +824,32 @@ hipError_t launch_expert_fwd(bool bf16, const void* xd, const void* w1, const vo
     RowsArgs a{};
     a.A = (const uint16_t*)xd; a.B = (const uint16_t*)w1; a.C = (uint16_t*)h; a.C2 = (uint16_t*)gu;
     a.lda = H; a.ldc = I; a.strideB = (int64_t)2 * I * H; a.K = H; a.N = I; a.I = I;
-    a.offsets = offsets; a.El = El; a.c0 = c0; a.nc = nc; a.P_c = P_c;
-    hipError_t e = run_rows<128, 128, 2, 2, kGateUp>("gemm_gateup_swiglu", a, s);
+    a.offsets = offsets; a.El = El; a.c0 = c0; a.nc = nc; a.P_c = P_c; a.one = 1; a.zero = 0;
+    hipError_t e = run_rows<256, 256, 2, 2, kGateUp>("gemm_gateup_swiglu", a, s);
     if (e != hipSuccess) return e;
     RowsArgs b{};
     b.A = (const uint16_t*)h; b.B = (const uint16_t*)w2; b.C = (uint16_t*)yd;
     b.lda = I; b.ldc = H; b.strideB = (int64_t)H * I; b.K = I; b.N = H; b.I = I;
-    b.offsets = offsets; b.El = El; b.c0 = c0; b.nc = nc; b.P_c = P_c;
-    return run_rows<128, 128, 2, 2, kDown>("gemm_down", b, s);
+    b.offsets = offsets; b.El = El; b.c0 = c0; b.nc = nc; b.P_c = P_c; b.one = 1; b.zero = 0;
+    return run_rows<256, 256, 2, 2, kDown>("gemm_down", b, s);
   }
   SimtRowsArgs a{};
   a.A = (const float*)xd; a.B = (const float*)w1; a.C = (float*)h; a.C2 = (float*)gu;
   a.lda = H; a.ldc = I; a.strideB = (int64_t)2 * I * H; a.K = H; a.N = I; a.I = I;
-  a.offsets = offsets; a.El = El; a.c0 = c0; a.nc = nc; a.P_c = P_c;
+  a.offsets = offsets; a.El = El; a.c0 = c0; a.nc = nc; a.P_c = P_c; a.one = 1; a.zero = 0;
   {
     MOE_TRACE("gemm_gateup_swiglu_f32", s);
-    hipLaunchKernelGGL(simt_rows_kernel<kGateUp>, dim3(kPersistentGrid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(simt_rows_kernel<kGateUp>, dim3(kSimtGrid), dim3(256), 0, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   SimtRowsArgs b{};
   b.A = (const float*)h; b.B = (const float*)w2; b.C = (float*)yd;
   b.lda = I; b.ldc = H; b.strideB = (int64_t)H * I; b.K = I; b.N = H; b.I = I;
-  b.offsets = offsets; b.El = El; b.c0 = c0; b.nc = nc; b.P_c = P_c;
+  b.offsets = offsets; b.El = El; b.c0 = c0; b.nc = nc; b.P_c = P_c; b.one = 1; b.zero = 0;
   {
     MOE_TRACE("gemm_down_f32", s);
-    hipLaunchKernelGGL(simt_rows_kernel<kDown>, dim3(kPersistentGrid), dim3(256), 0, s, b);
+    hipLaunchKernelGGL(simt_rows_kernel<kDown>, dim3(kSimtGrid), dim3(256), 0, s, b);
   }
   return hipGetLastError();
 }
@@ -734,32 +862,32 @@ hipError_t launch_expert_dgrad(bool bf16, const void* dyd, const void* gu, const
     RowsArgs a{};
     a.A = (const uint16_t*)dyd; a.B = (const uint16_t*)w2; a.C = (uint16_t*)dgu; a.aux = (const uint16_t*)gu;
     a.lda = H; a.ldc = 2 * I; a.strideB = (int64_t)H * I; a.K = H; a.N = I; a.I = I;
-    a.offsets = offsets; a.El = El; a.c0 = c0; a.nc = nc; a.P_c = P_c;
-    hipError_t e = run_rows<128, 128, 2, 2, kDownBwd>("gemm_down_dgrad_swiglu", a, s);
+    a.offsets = offsets; a.El = El; a.c0 = c0; a.nc = nc; a.P_c = P_c; a.one = 1; a.zero = 0;
+    hipError_t e = run_rows<256, 256, 2, 2, kDownBwd>("gemm_down_dgrad_swiglu", a, s);
     if (e != hipSuccess) return e;
     RowsArgs b{};
     b.A = (const uint16_t*)dgu; b.B = (const uint16_t*)w1; b.C = (uint16_t*)dxd;
     b.lda = 2 * I; b.ldc = H; b.strideB = (int64_t)2 * I * H; b.K = 2 * I; b.N = H; b.I = I;
-    b.offsets = offsets; b.El = El; b.c0 = c0; b.nc = nc; b.P_c = P_c;
-    return run_rows<128, 128, 2, 2, kGateUpBwd>("gemm_gateup_dgrad", b, s);
+    b.offsets = offsets; b.El = El; b.c0 = c0; b.nc = nc; b.P_c = P_c; b.one = 1; b.zero = 0;
+    return run_rows<256, 256, 2, 2, kGateUpBwd>("gemm_gateup_dgrad", b, s);
   }
   SimtRowsArgs a{};
   a.A = (const float*)dyd; a.B = (const float*)w2; a.C = (float*)dgu; a.aux = (const float*)gu;
   a.lda = H; a.ldc = 2 * I; a.strideB = (int64_t)H * I; a.K = H; a.N = I; a.I = I;
-  a.offsets = offsets; a.El = El; a.c0 = c0; a.nc = nc; a.P_c = P_c;
+  a.offsets = offsets; a.El = El; a.c0 = c0; a.nc = nc; a.P_c = P_c; a.one = 1; a.zero = 0;
   {
     MOE_TRACE("gemm_down_dgrad_swiglu_f32", s);
-    hipLaunchKernelGGL(simt_rows_kernel<kDownBwd>, dim3(kPersistentGrid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(simt_rows_kernel<kDownBwd>, dim3(kSimtGrid), dim3(256), 0, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   SimtRowsArgs b{};
   b.A = (const float*)dgu; b.B = (const float*)w1; b.C = (float*)dxd;
   b.lda = 2 * I; b.ldc = H; b.strideB = (int64_t)2 * I * H; b.K = 2 * I; b.N = H; b.I = I;
-  b.offsets = offsets; b.El = El; b.c0 = c0; b.nc = nc; b.P_c = P_c;
+  b.offsets = offsets; b.El = El; b.c0 = c0; b.nc = nc; b.P_c = P_c; b.one = 1; b.zero = 0;
   {
     MOE_TRACE("gemm_gateup_dgrad_f32", s);
-    hipLaunchKernelGGL(simt_rows_kernel<kGateUpBwd>, dim3(kPersistentGrid), dim3(256), 0, s, b);
+    hipLaunchKernelGGL(simt_rows_kernel<kGateUpBwd>, dim3(kSimtGrid), dim3(256), 0, s, b);
   }
   return hipGetLastError();
 }
@@ -769,7 +897,7 @@ hipError_t launch_expert_wgrad(bool bf16, const void* dyd, const void* dgu, cons
                                int I, int El, int n, int64_t P_c, hipStream_t s) {
   if (El <= 0) return hipSuccess;
   if (bf16) {
-    constexpr int BM = 128, BN = 128;
+    constexpr int BM = 256, BN = 256;
     size_t lds = (size_t)2 * (BM + BN) * BK * sizeof(uint16_t);
     auto k = kgroup_gemm_kernel<BM, BN, 2, 2, false>;
     hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -18,9 +18,10 @@ constexpr int kBatch = 4;         // 16-byte vectors per lane kept in flight
 
 // ---------------------------------------------------------------------------------------------
 // Dispatch (F32 / BF16): scatter x[t] to xd[row_of[t][j]] for every local slot; bitwise copy.
+template <int K>
 __global__ __launch_bounds__(256) void dispatch_copy_kernel(
     const u32x4* __restrict__ x, const int32_t* __restrict__ row_of, u32x4* __restrict__ xd,
-    int64_t t0, int64_t t1, int K, int64_t nvec) {
+    int64_t t0, int64_t t1, int64_t nvec) {
   const int lane = threadIdx.x & 63;
   const int64_t t = t0 + (int64_t)blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
   if (t >= t1) return;
@@ -34,6 +35,7 @@ __global__ __launch_bounds__(256) void dispatch_copy_kernel(
       int64_t i = v0 + b * 64 + lane;
       if (i < nvec) v[b] = src[i];
     }
+#pragma unroll
     for (int j = 0; j < K; ++j) {
       int32_t r = __shfl(myrow, j, 64);
       if (r < 0) continue;
@@ -161,10 +163,10 @@ template <> struct Vec<uint16_t> {
 };
 
 // Combine: out[t] = RNE(sum_j g_tj * yd[row_of[t][j]]), FP32 accumulation, j ascending.
-template <typename T>
+template <typename T, int K>
 __global__ __launch_bounds__(256) void combine_kernel(
     const u32x4* __restrict__ yd, const float* __restrict__ gates, const int32_t* __restrict__ row_of,
-    u32x4* __restrict__ out, int64_t t0, int64_t t1, int K, int64_t nvec) {
+    u32x4* __restrict__ out, int64_t t0, int64_t t1, int64_t nvec) {
   using V = Vec<T>;
   const int lane = threadIdx.x & 63;
   const int64_t t = t0 + (int64_t)blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
@@ -177,6 +179,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
     for (int b = 0; b < kBatch; ++b)
 #pragma unroll
       for (int q = 0; q < V::N; ++q) acc[b][q] = 0.f;
+#pragma unroll
     for (int j = 0; j < K; ++j) {
       int32_t r = __shfl(myrow, j, 64);
       if (r < 0) continue;
@@ -202,11 +205,11 @@ __global__ __launch_bounds__(256) void combine_kernel(
 }
 
 // Combine backward: dyd[row_of[t][j]] = g_tj * dy[t]; dgates[t][j] = <dy[t], yd[row]> (FP32).
-template <typename T>
+template <typename T, int K>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(
     const u32x4* __restrict__ dy, const u32x4* __restrict__ yd, const float* __restrict__ gates,
     const int32_t* __restrict__ row_of, u32x4* __restrict__ dyd, float* __restrict__ dgates,
-    int64_t t0, int64_t t1, int K, int64_t nvec) {
+    int64_t t0, int64_t t1, int64_t nvec) {
   using V = Vec<T>;
   const int lane = threadIdx.x & 63;
   const int64_t t = t0 + (int64_t)blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
@@ -214,9 +217,9 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
   const int32_t myrow = lane < K ? row_of[t * K + lane] : -1;
   const float mygate = lane < K ? gates[t * K + lane] : 0.f;
   const bool any = __ballot(myrow >= 0) != 0;
-  float dg[8];
+  float dg[K];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) dg[j] = 0.f;
+  for (int j = 0; j < K; ++j) dg[j] = 0.f;
   if (any) {
     for (int64_t v0 = 0; v0 < nvec; v0 += 64 * kBatch) {
       float d[kBatch][V::N];
@@ -226,8 +229,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
         if (i < nvec) V::to_f(dy[t * nvec + i], d[b]);
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (j >= K) break;
+      for (int j = 0; j < K; ++j) {
         int32_t r = __shfl(myrow, j, 64);
         if (r < 0) continue;
         float g = __shfl(mygate, j, 64);
@@ -248,8 +250,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
     }
   }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j >= K) break;
+  for (int j = 0; j < K; ++j) {
     float s = wave_sum(dg[j]);
     int32_t r = __shfl(myrow, j, 64);
     if (lane == 0) dgates[t * K + j] = (r >= 0) ? s : 0.f;
@@ -282,11 +283,11 @@ __global__ __launch_bounds__(256) void route_bwd_dlogits_kernel(
 }
 
 // Dispatch backward: dx[t] = RNE(sum_j local dxd[row_of[t][j]] + sum_j dlogits[t][e_j] W_r[e_j]).
-template <typename T>
+template <typename T, int K>
 __global__ __launch_bounds__(256) void dispatch_bwd_kernel(
     const u32x4* __restrict__ dxd, const int32_t* __restrict__ row_of, const int32_t* __restrict__ idx,
     const float* __restrict__ dlogits, const u32x4* __restrict__ w_r, u32x4* __restrict__ dx,
-    int64_t t0, int64_t t1, int K, int E, int64_t nvec) {
+    int64_t t0, int64_t t1, int E, int64_t nvec) {
   using V = Vec<T>;
   const int lane = threadIdx.x & 63;
   const int64_t t = t0 + (int64_t)blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
@@ -300,6 +301,7 @@ __global__ __launch_bounds__(256) void dispatch_bwd_kernel(
     for (int b = 0; b < kBatch; ++b)
 #pragma unroll
       for (int q = 0; q < V::N; ++q) acc[b][q] = 0.f;
+#pragma unroll
     for (int j = 0; j < K; ++j) {
       int32_t r = __shfl(myrow, j, 64);
       if (r < 0) continue;
@@ -315,6 +317,7 @@ __global__ __launch_bounds__(256) void dispatch_bwd_kernel(
         }
       }
     }
+#pragma unroll
     for (int j = 0; j < K; ++j) {
       int e = __shfl(myid, j, 64);
       float dl = __shfl(mydl, j, 64);
@@ -342,13 +345,27 @@ __global__ __launch_bounds__(256) void dispatch_bwd_kernel(
 // Launchers. Token range [t0, t1); nvec = 16-byte vectors per row.
 static inline dim3 tok_grid(int64_t ntok) { return dim3((unsigned)((ntok + kTokPerBlock - 1) / kTokPerBlock)); }
 
+// K (top-k, 1..8) is a template parameter of the row kernels so that the slot loops unroll.
+#define MOE_SWITCH_K(K, ...)                     \
+  switch (K) {                                   \
+    case 1: { constexpr int KK = 1; __VA_ARGS__; } break; \
+    case 2: { constexpr int KK = 2; __VA_ARGS__; } break; \
+    case 3: { constexpr int KK = 3; __VA_ARGS__; } break; \
+    case 4: { constexpr int KK = 4; __VA_ARGS__; } break; \
+    case 5: { constexpr int KK = 5; __VA_ARGS__; } break; \
+    case 6: { constexpr int KK = 6; __VA_ARGS__; } break; \
+    case 7: { constexpr int KK = 7; __VA_ARGS__; } break; \
+    case 8: { constexpr int KK = 8; __VA_ARGS__; } break; \
+    default: return hipErrorInvalidValue;      \
+  }
+
 hipError_t launch_dispatch(const void* x, const int32_t* row_of, void* xd, int64_t t0, int64_t t1,
                            int K, int64_t row_bytes, hipStream_t s) {
   if (t1 <= t0) return hipSuccess;
   {
     MOE_TRACE("dispatch", s);
-    hipLaunchKernelGGL(dispatch_copy_kernel, tok_grid(t1 - t0), dim3(256), 0, s, (const u32x4*)x,
-                       row_of, (u32x4*)xd, t0, t1, K, row_bytes / 16);
+    MOE_SWITCH_K(K, hipLaunchKernelGGL(dispatch_copy_kernel<KK>, tok_grid(t1 - t0), dim3(256), 0, s,
+                                       (const u32x4*)x, row_of, (u32x4*)xd, t0, t1, row_bytes / 16));
   }
   return hipGetLastError();
 }
@@ -381,14 +398,14 @@ hipError_t launch_combine(bool bf16, const void* yd, const float* gates, const i
   if (bf16)
     {
       MOE_TRACE("combine", s);
-      hipLaunchKernelGGL(combine_kernel<uint16_t>, tok_grid(t1 - t0), dim3(256), 0, s,
-                         (const u32x4*)yd, gates, row_of, (u32x4*)out, t0, t1, K, row_bytes / 16);
+      MOE_SWITCH_K(K, hipLaunchKernelGGL((combine_kernel<uint16_t, KK>), tok_grid(t1 - t0), dim3(256), 0, s,
+                         (const u32x4*)yd, gates, row_of, (u32x4*)out, t0, t1, row_bytes / 16));
     }
   else
     {
       MOE_TRACE("combine", s);
-      hipLaunchKernelGGL(combine_kernel<float>, tok_grid(t1 - t0), dim3(256), 0, s,
-                         (const u32x4*)yd, gates, row_of, (u32x4*)out, t0, t1, K, row_bytes / 16);
+      MOE_SWITCH_K(K, hipLaunchKernelGGL((combine_kernel<float, KK>), tok_grid(t1 - t0), dim3(256), 0, s,
+                         (const u32x4*)yd, gates, row_of, (u32x4*)out, t0, t1, row_bytes / 16));
     }
   return hipGetLastError();
 }
@@ -400,16 +417,16 @@ hipError_t launch_combine_bwd(bool bf16, const void* dy, const void* yd, const f
   if (bf16)
     {
       MOE_TRACE("combine_bwd", s);
-      hipLaunchKernelGGL(combine_bwd_kernel<uint16_t>, tok_grid(t1 - t0), dim3(256), 0, s,
+      MOE_SWITCH_K(K, hipLaunchKernelGGL((combine_bwd_kernel<uint16_t, KK>), tok_grid(t1 - t0), dim3(256), 0, s,
                          (const u32x4*)dy, (const u32x4*)yd, gates, row_of, (u32x4*)dyd, dgates,
-                         t0, t1, K, row_bytes / 16);
+                         t0, t1, row_bytes / 16));
     }
   else
     {
       MOE_TRACE("combine_bwd", s);
-      hipLaunchKernelGGL(combine_bwd_kernel<float>, tok_grid(t1 - t0), dim3(256), 0, s,
+      MOE_SWITCH_K(K, hipLaunchKernelGGL((combine_bwd_kernel<float, KK>), tok_grid(t1 - t0), dim3(256), 0, s,
                          (const u32x4*)dy, (const u32x4*)yd, gates, row_of, (u32x4*)dyd, dgates,
-                         t0, t1, K, row_bytes / 16);
+                         t0, t1, row_bytes / 16));
     }
   return hipGetLastError();
 }
@@ -433,16 +450,16 @@ hipError_t launch_dispatch_bwd(bool bf16, const void* dxd, const int32_t* row_of
   if (bf16)
     {
       MOE_TRACE("dispatch_bwd", s);
-      hipLaunchKernelGGL(dispatch_bwd_kernel<uint16_t>, tok_grid(t1 - t0), dim3(256), 0, s,
+      MOE_SWITCH_K(K, hipLaunchKernelGGL((dispatch_bwd_kernel<uint16_t, KK>), tok_grid(t1 - t0), dim3(256), 0, s,
                          (const u32x4*)dxd, row_of, idx, dlogits, (const u32x4*)w_r, (u32x4*)dx,
-                         t0, t1, K, E, row_bytes / 16);
+                         t0, t1, E, row_bytes / 16));
     }
   else
     {
       MOE_TRACE("dispatch_bwd", s);
-      hipLaunchKernelGGL(dispatch_bwd_kernel<float>, tok_grid(t1 - t0), dim3(256), 0, s,
+      MOE_SWITCH_K(K, hipLaunchKernelGGL((dispatch_bwd_kernel<float, KK>), tok_grid(t1 - t0), dim3(256), 0, s,
                          (const u32x4*)dxd, row_of, idx, dlogits, (const u32x4*)w_r, (u32x4*)dx,
-                         t0, t1, K, E, row_bytes / 16);
+                         t0, t1, E, row_bytes / 16));
     }
   return hipGetLastError();
 }
