@@ -214,22 +214,32 @@ struct KSlowSplit {
 // transposed: lane l holds output row (l & 31) and, for accumulator element i, output column
 // 8*(i/4) + 4*(l/32) + i%4 -- four consecutive columns per group of four elements, which the
 // epilogues store as one 8-byte BF16 vector.
-template <int TM, int TN>
+template <int TM, int TN, int TMA = TM>
 MOE_DEV void mma_stage(const uint16_t* la, const uint16_t* lb, int arow0, int brow0, int lane,
-                       f32x16_t (&acc)[TM][TN]) {
+                       f32x16_t (&acc)[TM][TN], int tma = TM) {
   const int r = lane & 31, hk = lane >> 5;
+  bf16x8_t fa[2][TM], fb[2][TN];
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) fa[0][tm] = *(const bf16x8_t*)(la + sw(arow0 + tm * 32 + r, hk));
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) fb[0][tn] = *(const bf16x8_t*)(lb + sw(brow0 + tn * 32 + r, hk));
 #pragma unroll
   for (int kk = 0; kk < BK / 16; ++kk) {
-    bf16x8_t a[TM], b[TN];
+    const int cb = kk & 1, nb = cb ^ 1;
+    if (kk + 1 < BK / 16) {
 #pragma unroll
-    for (int tm = 0; tm < TM; ++tm) a[tm] = *(const bf16x8_t*)(la + sw(arow0 + tm * 32 + r, 2 * kk + hk));
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn) b[tn] = *(const bf16x8_t*)(lb + sw(brow0 + tn * 32 + r, 2 * kk + hk));
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
+      for (int tm = 0; tm < TM; ++tm)
+        fa[nb][tm] = *(const bf16x8_t*)(la + sw(arow0 + tm * 32 + r, 2 * (kk + 1) + hk));
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn)
-        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[tn], a[tm], acc[tm][tn], 0, 0, 0);
+        fb[nb][tn] = *(const bf16x8_t*)(lb + sw(brow0 + tn * 32 + r, 2 * (kk + 1) + hk));
+    }
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+      if (tm < tma)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cb][tn], fa[cb][tm], acc[tm][tn], 0, 0, 0);
   }
 }
 
@@ -241,10 +251,10 @@ MOE_DEV int out_col(int g, int lane) { return 8 * g + 4 * (lane >> 5); }
 // sets per operand alternate, so the loads of stage s+2 are in flight while stage s is
 // multiplied and stage s+1 is committed to the other LDS buffer. Unrolled by two so that each
 // staging set is addressed statically.
-template <int TM, int TN, class LdA, class LdB>
+template <int TM, int TN, int TMA, class LdA, class LdB>
 MOE_DEV void kloop_pgr2(LdA& a0, LdA& a1, LdB& b0, LdB& b1, int nks, uint16_t* A0, uint16_t* A1,
                         uint16_t* B0, uint16_t* B1, int tid, int arow0, int brow0, int lane,
-                        f32x16_t (&acc)[TM][TN]) {
+                        f32x16_t (&acc)[TM][TN], int tma = TM) {
   if (nks <= 0) return;
   a0.fetch(0, tid);
   b0.fetch(0, tid);
@@ -254,12 +264,12 @@ MOE_DEV void kloop_pgr2(LdA& a0, LdA& a1, LdB& b0, LdB& b1, int nks, uint16_t* A
   __syncthreads();
   for (int ks = 0; ks < nks; ks += 2) {
     if (ks + 2 < nks) { a0.fetch((ks + 2) * BK, tid); b0.fetch((ks + 2) * BK, tid); }
-    mma_stage<TM, TN>(A0, B0, arow0, brow0, lane, acc);
+    mma_stage<TM, TN, TMA>(A0, B0, arow0, brow0, lane, acc, tma);
     if (ks + 1 < nks) { a1.commit(A1, tid); b1.commit(B1, tid); }
     __syncthreads();
     if (ks + 1 >= nks) break;
     if (ks + 3 < nks) { a1.fetch((ks + 3) * BK, tid); b1.fetch((ks + 3) * BK, tid); }
-    mma_stage<TM, TN>(A1, B1, arow0, brow0, lane, acc);
+    mma_stage<TM, TN, TMA>(A1, B1, arow0, brow0, lane, acc, tma);
     if (ks + 2 < nks) { a0.commit(A0, tid); b0.commit(B0, tid); }
     __syncthreads();
   }
@@ -379,15 +389,22 @@ __global__ __launch_bounds__(kThreads) void rows_gemm_kernel(RowsArgs a) {
     KMajor<BM> ldA1 = ldA;
     // a.one == 1: an enclosing loop the compiler cannot remove; with it the register allocator
     // keeps the two staging sets and the accumulators in registers through the K loop
+    // 32-row blocks of this wave that hold rows of the segment (the last tile of an expert is
+    // usually partial): the K loop is specialised on it, so empty blocks cost no MFMA
+    const int tma = __builtin_amdgcn_readfirstlane(max(0, min(TM, (mvalid - wm * WTM + 31) / 32)));
     for (int rep = 0; rep < a.one; ++rep) {
       if constexpr (kBSlow) {
         KSlow<BN, false> ldBs1 = ldBs;
-        kloop_pgr2<TM, TN>(ldA, ldA1, ldBs, ldBs1, nks, LA(0), LA(1), LB(0), LB(1), tid, wm * WTM, wn * WTN,
-                           lane, acc);
+#define MOE_KLOOP(TMA_) kloop_pgr2<TM, TN, TMA_>(ldA, ldA1, ldBs, ldBs1, nks, LA(0), LA(1), LB(0), LB(1), tid, \
+                                                 wm * WTM, wn * WTN, lane, acc, tma)
+        MOE_KLOOP(TM);
+#undef MOE_KLOOP
       } else {
         auto ldB1 = ldB;
-        kloop_pgr2<TM, TN>(ldA, ldA1, ldB, ldB1, nks, LA(0), LA(1), LB(0), LB(1), tid, wm * WTM, wn * WTN,
-                           lane, acc);
+#define MOE_KLOOP(TMA_) kloop_pgr2<TM, TN, TMA_>(ldA, ldA1, ldB, ldB1, nks, LA(0), LA(1), LB(0), LB(1), tid, \
+                                                 wm * WTM, wn * WTN, lane, acc, tma)
+        MOE_KLOOP(TM);
+#undef MOE_KLOOP
       }
     }
 
@@ -538,8 +555,8 @@ __global__ __launch_bounds__(kThreads) void kgroup_gemm_kernel(KGroupArgs a) {
     if constexpr (!ROUTER) {
       KSlow<BM> ldA1 = ldA;
       KSlow<BN> ldB1 = ldB;
-      kloop_pgr2<TM, TN>(ldA, ldA1, ldB, ldB1, nks, LA(0), LA(1), LB(0), LB(1), tid, wm * WTM, wn * WTN,
-                         lane, acc);
+      kloop_pgr2<TM, TN, TM>(ldA, ldA1, ldB, ldB1, nks, LA(0), LA(1), LB(0), LB(1), tid, wm * WTM, wn * WTN,
+                             lane, acc);
       __syncthreads();  // the next segment restages both LDS buffers
       continue;
     }
