@@ -305,7 +305,8 @@ def allocate(d: MoeDesc, device="cuda", backward: bool = True, fill=None):
         "out": ((d.P_out, H), pay), "workspace": ((max(1, ws["workspace"]),), u8),
     }
     if fp8:
-        spec.update({"xd_scale": ((P,), f32), "h_scale": ((P,), f32)})
+        # h: [P, I] BF16 values followed by their [P, I] e4m3 codes
+        spec.update({"xd_scale": ((P,), f32), "h_scale": ((P,), f32), "h": ((3 * P * I,), u8)})
     else:
         spec["gu"] = ((P, 2 * I), pay)
     if backward and not fp8:

@@ -162,7 +162,7 @@ moe_status moe_workspace_bytes(const moe_desc* d, moe_workspace_sizes* o) {
   o->xd = P * H * (fp8 ? 1 : es);
   o->xd_scale = fp8 ? P * 4 : 0;
   o->gu = fp8 ? 0 : P * 2 * I * es;
-  o->h = P * I * es;
+  o->h = P * I * (fp8 ? 3 : es);  // FP8: BF16 values, then e4m3 codes
   o->h_scale = fp8 ? P * 4 : 0;
   o->yd = P * H * es;
   o->out = d->P_out * H * es;
@@ -235,7 +235,7 @@ moe_status moe_expert_ffn(const moe_desc* d, int chunk, const void* xd, const fl
     MOE_NEED(xd_scale); MOE_NEED(w1_scale); MOE_NEED(w2_scale); MOE_NEED(h_scale);
     MOE_HIP(moe::launch_expert_fwd_fp8(xd, xd_scale, w1, w1_scale, w2, w2_scale, offsets, h, h_scale,
                                        yd, d->H, d->I, d->E_local, r.c0, r.nc, d->P_c,
-                                       (hipStream_t)stream), "expert_ffn_fp8");
+                                       rows_of(d), (hipStream_t)stream), "expert_ffn_fp8");
     return MOE_OK;
   }
   MOE_HIP(moe::launch_expert_fwd(is_bf16_rows(d), xd, w1, w2, offsets, gu, h, yd, d->H, d->I,

@@ -1,20 +1,16 @@
-// Grouped expert GEMMs on CDNA4 matrix cores (BF16 MFMA 32x32x16, FP32 accumulation) and an
-// FP32 SIMT variant for FP32 payloads.
+// Router weight gradient on BF16 matrix cores (FP32 dlogits split into BF16 high and low parts,
+// FP32 accumulation, split-K partials reduced in order) and FP32 SIMT grouped GEMMs for FP32
+// payloads; the BF16/FP8 expert GEMMs live in grouped_gemm.hip.
 //
-// The expert FFN is a grouped GEMM whose groups are the local experts' row segments in the
-// expert-contiguous dispatch buffer (token-wise ChunkedEP, Megatron-LM PR 7342, "Summary":
-// expert compute per token chunk). Group sizes are only known on the device (the offset table
-// written by routing), so the row-grouped kernels are persistent: every workgroup rebuilds the
-// group -> tile prefix from the offset table and strides over the tiles; nothing returns to the
-// host. Weight-gradient kernels iterate K over the rows of every chunk of one expert in one
-// FP32 reduction and convert once (the FP32-accumulate-then-convert rule that ChunkedEP's
-// "Numerical status -- unresolved" states for the router weights).
+// Token-wise ChunkedEP (Megatron-LM PR 7342, "Numerical status -- unresolved") accumulates the
+// router weight gradient across chunks in FP32 and converts it once: each chunk's dlogits^T x is
+// computed in FP32 (dlogits = hi + lo with hi, lo BF16, x exactly BF16), its split-K partials are
+// summed in a fixed order into the FP32 accumulator, and the last chunk converts it once.
 //
-// Tile engine: workgroup of 256 threads (4 waves, wave grid WM x WN), LDS stages of BK = 64,
-// double-buffered; both operands live in LDS K-contiguous with the eight 16-byte chunks of a row
-// XOR-swizzled by the row index (conflict-free ds_read_b128 for the MFMA operand layout).
-// Operands whose K runs along rows in HBM (NN dgrad weights, TN wgrad activations) are
-// transposed in registers while staging (8 K-rows x V columns per thread).
+// Router tile engine: 256 threads (4 waves, 2 x 2), LDS stages of BK = 64, double-buffered,
+// K-contiguous 128-byte rows with 16-byte chunks XOR-swizzled by the row index; operands whose K
+// runs along HBM rows are transposed in registers while staging (8 K-rows x V columns per
+// thread).
 #include "common.h"
 #include "launch.h"
 #include "trace.h"
@@ -66,58 +62,6 @@ MOE_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
 // K-contiguous rows, R rows x 64 BF16 per stage; thread tid stages rows tid/8 + 32*i (i < R/32),
 // 16-byte chunk tid%8 of each. SWIGLU_WTN > 0 maps tile rows to interleaved gate/up weight rows
 // (per wave column block of SWIGLU_WTN rows: first half gate rows j, second half up rows I + j).
-template <int R, int SWIGLU_WTN = 0>
-struct KMajor {
-  static constexpr int NV = R / 32;
-  __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t voff;  // this lane's byte offset (row tid/8, chunk tid%8)
-  uint32_t ldb;   // bytes between consecutive rows
-  uint32_t upb;   // SwiGLU: bytes from a gate row to its up row
-  u32x4 v[NV];
-  // base: row 0 of the tile; valid_rows: rows readable from base (beyond them loads return 0)
-  MOE_DEV void init(const uint16_t* base, int64_t ld, int64_t valid_rows, int tid, int64_t up_rows = 0,
-                   uint32_t run_time_zero = 0) {
-    zero = run_time_zero;
-    ldb = (uint32_t)(ld * 2);
-    upb = (uint32_t)(up_rows * ld * 2);
-    rsrc = make_rsrc(base, valid_rows * ld * 2);
-    voff = (uint32_t)(tid >> 3) * ldb + (uint32_t)(tid & 7) * 16u;
-  }
-  MOE_DEV uint32_t offset(int i) const {
-    if constexpr (SWIGLU_WTN == 0) {
-      return (uint32_t)(32 * i) * ldb;
-    } else {
-      const int r0 = 32 * i;  // tid/8 < 32 never crosses a 32-row boundary
-      const int wb = r0 / SWIGLU_WTN, q0 = r0 % SWIGLU_WTN, hw = SWIGLU_WTN / 2;
-      const int j0 = wb * hw + (q0 < hw ? q0 : q0 - hw);
-      return (uint32_t)j0 * ldb + (q0 < hw ? 0u : upb);
-    }
-  }
-  MOE_DEV void fetch(int k0, int /*tid*/) {
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      i32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)voff, (int)(offset(i) + (uint32_t)k0 * 2u), 0);
-      v[i] = u32x4{(uint32_t)t.x, (uint32_t)t.y, (uint32_t)t.z, (uint32_t)t.w};
-    }
-  }
-  uint32_t zero;  // 0 at run time; XOR-ing it keeps the staging data in VGPRs (see commit)
-  // The XOR with a run-time zero is a VALU use of the staged data: without it the register
-  // allocator may keep the staging registers in AGPRs, where they compete with the MFMA
-  // accumulators and spill inside the K loop.
-  MOE_DEV void commit(uint16_t* lds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      int id = tid + i * kThreads;
-      *(u32x4*)(lds + sw(id >> 3, id & 7)) = u32x4{v[i].x ^ zero, v[i].y ^ zero, v[i].z ^ zero, v[i].w ^ zero};
-    }
-  }
-  MOE_DEV static int row_of(int tid, int i) { return (tid >> 3) + 32 * i; }
-};
-
-// K along HBM rows: element (mn, k) at base[k * ld + mn]. One block of 8 K-rows x V columns per
-// thread (V = R/32; K block tid%8, mn block tid/8), transposed in registers into V K-contiguous
-// 16-byte chunks. Each group of 8 lanes then writes the 8 chunks of the same LDS rows
-// (conflict-free), and each global load instruction reads whole 128-byte lines.
 template <int R, bool MASK_K = true>
 struct KSlow {
   static constexpr int V = R / 32;
@@ -246,246 +190,10 @@ MOE_DEV void mma_stage(const uint16_t* la, const uint16_t* lb, int arow0, int br
 // Output coordinates inside a 32x32 block for lane `lane`: row, and first column of group g.
 MOE_DEV int out_row(int lane) { return lane & 31; }
 MOE_DEV int out_col(int g, int lane) { return 8 * g + 4 * (lane >> 5); }
-
-// K loop over nks LDS stages with a global-read prefetch depth of two: two register staging
-// sets per operand alternate, so the loads of stage s+2 are in flight while stage s is
-// multiplied and stage s+1 is committed to the other LDS buffer. Unrolled by two so that each
-// staging set is addressed statically.
-template <int TM, int TN, int TMA, class LdA, class LdB>
-MOE_DEV void kloop_pgr2(LdA& a0, LdA& a1, LdB& b0, LdB& b1, int nks, uint16_t* A0, uint16_t* A1,
-                        uint16_t* B0, uint16_t* B1, int tid, int arow0, int brow0, int lane,
-                        f32x16_t (&acc)[TM][TN], int tma = TM) {
-  if (nks <= 0) return;
-  a0.fetch(0, tid);
-  b0.fetch(0, tid);
-  if (nks > 1) { a1.fetch(BK, tid); b1.fetch(BK, tid); }
-  a0.commit(A0, tid);
-  b0.commit(B0, tid);
-  __syncthreads();
-  for (int ks = 0; ks < nks; ks += 2) {
-    if (ks + 2 < nks) { a0.fetch((ks + 2) * BK, tid); b0.fetch((ks + 2) * BK, tid); }
-    mma_stage<TM, TN, TMA>(A0, B0, arow0, brow0, lane, acc, tma);
-    if (ks + 1 < nks) { a1.commit(A1, tid); b1.commit(B1, tid); }
-    __syncthreads();
-    if (ks + 1 >= nks) break;
-    if (ks + 3 < nks) { a1.fetch((ks + 3) * BK, tid); b1.fetch((ks + 3) * BK, tid); }
-    mma_stage<TM, TN, TMA>(A1, B1, arow0, brow0, lane, acc, tma);
-    if (ks + 2 < nks) { a0.commit(A0, tid); b0.commit(B0, tid); }
-    __syncthreads();
-  }
-}
-
 MOE_DEV uint2 pack4(float a, float b, float c, float d) { return make_uint2(pack_bf2(a, b), pack_bf2(c, d)); }
 MOE_DEV void unpack4(uint2 v, float* f) {
   f[0] = bf2f(v.x & 0xffff); f[1] = bf2f(v.x >> 16); f[2] = bf2f(v.y & 0xffff); f[3] = bf2f(v.y >> 16);
 }
-
-// ---------------------------------------------------------------------------------------------
-// Row-grouped GEMMs (forward and input-gradient), persistent over device-side groups.
-//   C[r0 + m][n] = sum_k A[r0 + m][k] * B_e(n, k) for the rows of local expert e in a chunk.
-enum RowsMode { kGateUp = 0, kDown = 1, kDownBwd = 2, kGateUpBwd = 3 };
-
-struct RowsArgs {
-  const uint16_t* A;     // [P, K] dispatch-ordered rows
-  const uint16_t* B;     // expert weights, stride strideB per expert
-  uint16_t* C;           // [P, ldc] output rows
-  uint16_t* C2;          // second output (kGateUp: gu save, nullable)
-  const uint16_t* aux;   // kDownBwd: gu [P, 2I]
-  int64_t lda, ldc, strideB;
-  int K;                 // reduction length
-  int N;                 // output columns (kGateUp/kDownBwd: I)
-  int I;
-  const int32_t* offsets;
-  int El, c0, nc;
-  int64_t P_c;
-  uint32_t zero;         // always 0 (a value the compiler cannot fold)
-  int one;               // always 1 (trip count of the loop around the K loop)
-};
-
-template <int BM, int BN, int WM, int WN, int MODE>
-__global__ __launch_bounds__(kThreads) void rows_gemm_kernel(RowsArgs a) {
-  constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
-  static_assert(WM * WN == 4, "4 waves");
-  constexpr bool kSwiGLU = (MODE == kGateUp);
-  constexpr bool kBSlow = (MODE == kDownBwd || MODE == kGateUpBwd);
-  // output columns per tile: the gate/up GEMM holds a gate and an up half per wave
-  constexpr int OUTN = kSwiGLU ? BN / 2 : BN;
-  __shared__ int s_pre[kMaxGroups + 1];
-  __shared__ int64_t s_r0[kMaxGroups];
-  __shared__ int s_len[kMaxGroups];
-  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-  // stage s: A tile at lds + s*BM*BK, B tile at lds + 2*BM*BK + s*BN*BK
-#define LA(s) (lds + (s) * (BM * BK))
-#define LB(s) (lds + 2 * BM * BK + (s) * (BN * BK))
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-  const int G = a.nc * a.El;
-  const int ntiles = (a.N + OUTN - 1) / OUTN;
-  for (int g = tid; g < G; g += kThreads) {
-    const int c = a.c0 + g / a.El, e = g % a.El;
-    const int32_t* off = a.offsets + (int64_t)c * (a.El + 1);
-    const int len = off[e + 1] - off[e];
-    s_r0[g] = (int64_t)c * a.P_c + off[e];
-    s_len[g] = len;
-    s_pre[g + 1] = ((len + BM - 1) / BM) * ntiles;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    s_pre[0] = 0;
-    for (int g = 0; g < G; ++g) s_pre[g + 1] += s_pre[g];
-  }
-  __syncthreads();
-  const int total = s_pre[G];
-  // One tile per workgroup; the grid is a static upper bound and surplus workgroups exit.
-  // Workgroups are dealt round-robin to the 8 XCDs (block b runs on XCD b % 8); tile indices
-  // are assigned so that each XCD gets a contiguous range of ceil(total/8) tiles, and the tiles
-  // of one expert (same weights, same rows) share that XCD's L2.
-  const int per_xcd = (total + 7) / 8;
-  const int slot = blockIdx.x / 8;
-  {
-    const int tile = (blockIdx.x % 8) * per_xcd + slot;
-    if (slot >= per_xcd || tile >= total) return;
-    int lo = 0, hi = G;  // find g with s_pre[g] <= tile < s_pre[g+1]
-    while (hi - lo > 1) { int mid = (lo + hi) >> 1; if (s_pre[mid] <= tile) lo = mid; else hi = mid; }
-    // tile parameters are wave-uniform: keep them in scalar registers
-    const int g = __builtin_amdgcn_readfirstlane(lo);
-    const int e = g % a.El;
-    const int t_in = tile - __builtin_amdgcn_readfirstlane(s_pre[g]);
-    const int mt = t_in / ntiles, nt = t_in % ntiles;
-    const int64_t rg = s_r0[g];
-    const int64_t r0 = (((int64_t)__builtin_amdgcn_readfirstlane((int)(rg >> 32)) << 32) |
-                        (uint32_t)__builtin_amdgcn_readfirstlane((int)(rg & 0xffffffff))) + (int64_t)mt * BM;
-    const int mvalid = min(BM, __builtin_amdgcn_readfirstlane(s_len[g]) - mt * BM);
-    const int n0 = nt * OUTN;
-    const uint16_t* Be = a.B + (int64_t)e * a.strideB;
-
-    KMajor<BM> ldA;
-    ldA.init(a.A + r0 * a.lda, a.lda, mvalid, tid, 0, a.zero);
-    KMajor<BN, kSwiGLU ? WTN : 0> ldB;
-    KSlow<BN, false> ldBs;
-    if constexpr (!kBSlow) {
-      if constexpr (kSwiGLU) {
-        // tile row r -> wave column block r / WTN; first half gate rows, second half up rows;
-        // readable rows run to the end of this expert's W1 (gate rows past N are discarded)
-        ldB.init(Be + (int64_t)n0 * a.K, a.K, 2 * (int64_t)a.I - n0, tid, a.I, a.zero);
-      } else {
-        ldB.init(Be + (int64_t)n0 * a.K, a.K, (int64_t)a.N - n0, tid, 0, a.zero);
-      }
-    } else {
-      // B(n, k) = W_e[k * N + n]: K-rows of N elements starting at column n0
-      ldBs.init(Be + n0, a.N, a.K, tid);
-    }
-
-    f32x16_t acc[TM][TN];
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) acc[tm][tn][q] = 0.f;
-
-    const int nks = a.K / BK;
-    KMajor<BM> ldA1 = ldA;
-    // a.one == 1: an enclosing loop the compiler cannot remove; with it the register allocator
-    // keeps the two staging sets and the accumulators in registers through the K loop
-    // 32-row blocks of this wave that hold rows of the segment (the last tile of an expert is
-    // usually partial): the K loop is specialised on it, so empty blocks cost no MFMA
-    const int tma = __builtin_amdgcn_readfirstlane(max(0, min(TM, (mvalid - wm * WTM + 31) / 32)));
-    for (int rep = 0; rep < a.one; ++rep) {
-      if constexpr (kBSlow) {
-        KSlow<BN, false> ldBs1 = ldBs;
-#define MOE_KLOOP(TMA_) kloop_pgr2<TM, TN, TMA_>(ldA, ldA1, ldBs, ldBs1, nks, LA(0), LA(1), LB(0), LB(1), tid, \
-                                                 wm * WTM, wn * WTN, lane, acc, tma)
-        MOE_KLOOP(TM);
-#undef MOE_KLOOP
-      } else {
-        auto ldB1 = ldB;
-#define MOE_KLOOP(TMA_) kloop_pgr2<TM, TN, TMA_>(ldA, ldA1, ldB, ldB1, nks, LA(0), LA(1), LB(0), LB(1), tid, \
-                                                 wm * WTM, wn * WTN, lane, acc, tma)
-        MOE_KLOOP(TM);
-#undef MOE_KLOOP
-      }
-    }
-
-    // epilogue: rows past the expert's segment and columns past N are not written
-    const int mrow = wm * WTM + out_row(lane);
-    if constexpr (kSwiGLU) {
-      const int64_t I2 = 2 * (int64_t)a.I;
-#pragma clang loop unroll(full)
-      for (int tm = 0; tm < TM; ++tm) {
-        const int m = mrow + tm * 32;
-        if (m >= mvalid) continue;
-        const int64_t row = r0 + m;
-#pragma clang loop unroll(full)
-        for (int tn = 0; tn < TN / 2; ++tn)
-#pragma clang loop unroll(full)
-          for (int g = 0; g < 4; ++g) {
-            const int j = n0 + wn * (WTN / 2) + tn * 32 + out_col(g, lane);
-            if (j >= a.N) continue;
-            float gv[4], uv[4], hv[4];
-#pragma clang loop unroll(full)
-            for (int q = 0; q < 4; ++q) {
-              gv[q] = acc[tm][tn][4 * g + q];
-              uv[q] = acc[tm][tn + TN / 2][4 * g + q];
-              hv[q] = gv[q] * sigmoidf_(gv[q]) * uv[q];
-            }
-            *(uint2*)(a.C + row * a.ldc + j) = pack4(hv[0], hv[1], hv[2], hv[3]);
-            if (a.C2) {
-              *(uint2*)(a.C2 + row * I2 + j) = pack4(gv[0], gv[1], gv[2], gv[3]);
-              *(uint2*)(a.C2 + row * I2 + a.I + j) = pack4(uv[0], uv[1], uv[2], uv[3]);
-            }
-          }
-      }
-    } else if constexpr (MODE == kDownBwd) {
-      const int64_t I2 = 2 * (int64_t)a.I;
-#pragma clang loop unroll(full)
-      for (int tm = 0; tm < TM; ++tm) {
-        const int m = mrow + tm * 32;
-        if (m >= mvalid) continue;
-        const int64_t row = r0 + m;
-#pragma clang loop unroll(full)
-        for (int tn = 0; tn < TN; ++tn)
-#pragma clang loop unroll(full)
-          for (int g = 0; g < 4; ++g) {
-            const int j = n0 + wn * WTN + tn * 32 + out_col(g, lane);
-            if (j >= a.N) continue;
-            float gv[4], uv[4], dg[4], du[4];
-            unpack4(*(const uint2*)(a.aux + row * I2 + j), gv);
-            unpack4(*(const uint2*)(a.aux + row * I2 + a.I + j), uv);
-#pragma clang loop unroll(full)
-            for (int q = 0; q < 4; ++q) {
-              const float dh = acc[tm][tn][4 * g + q];
-              const float sg = sigmoidf_(gv[q]);
-              dg[q] = dh * uv[q] * sg * (1.f + gv[q] * (1.f - sg));
-              du[q] = dh * gv[q] * sg;
-            }
-            *(uint2*)(a.C + row * I2 + j) = pack4(dg[0], dg[1], dg[2], dg[3]);
-            *(uint2*)(a.C + row * I2 + a.I + j) = pack4(du[0], du[1], du[2], du[3]);
-          }
-      }
-    } else {
-#pragma clang loop unroll(full)
-      for (int tm = 0; tm < TM; ++tm) {
-        const int m = mrow + tm * 32;
-        if (m >= mvalid) continue;
-        const int64_t row = r0 + m;
-#pragma clang loop unroll(full)
-        for (int tn = 0; tn < TN; ++tn)
-#pragma clang loop unroll(full)
-          for (int g = 0; g < 4; ++g) {
-            const int n = n0 + wn * WTN + tn * 32 + out_col(g, lane);
-            if (n >= a.N) continue;
-            const f32x16_t& v = acc[tm][tn];
-            *(uint2*)(a.C + row * a.ldc + n) = pack4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
-          }
-      }
-    }
-  }
-}
-
-#undef LA
-#undef LB
 
 // ---------------------------------------------------------------------------------------------
 // K-grouped GEMMs: weight gradients C_e[m][n] = sum over the rows of every chunk of expert e of
@@ -504,19 +212,19 @@ struct KGroupArgs {
   int ksplit;
 };
 
-template <int BM, int BN, int WM, int WN, bool ROUTER>
-__global__ __launch_bounds__(kThreads) void kgroup_gemm_kernel(KGroupArgs a) {
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(kThreads) void router_wgrad_kernel(KGroupArgs a) {
   constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-  constexpr int AS = ROUTER ? 2 : 1;  // A planes (hi, lo)
-#define LA(s) (lds + (s) * (AS * BM * BK))
-#define LB(s) (lds + 2 * AS * BM * BK + (s) * (BN * BK))
+  // stage s: A high/low planes at lds + s*2*BM*BK, B tile after both stages of A
+#define LA(s) (lds + (s) * (2 * BM * BK))
+#define LB(s) (lds + 4 * BM * BK + (s) * (BN * BK))
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int mtiles = (a.M + BM - 1) / BM, ntiles = (a.N + BN - 1) / BN;
   const int tile = blockIdx.x;
-  const int grp = tile / (mtiles * ntiles);       // expert (or K split)
+  const int grp = tile / (mtiles * ntiles);       // K split
   const int t_in = tile % (mtiles * ntiles);
   const int m0 = (t_in / ntiles) * BM, n0 = (t_in % ntiles) * BN;
 
@@ -528,54 +236,30 @@ __global__ __launch_bounds__(kThreads) void kgroup_gemm_kernel(KGroupArgs a) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[tm][tn][q] = 0.f;
 
-  const int nseg = ROUTER ? 1 : a.n_chunks;
-  for (int sgi = 0; sgi < nseg; ++sgi) {
-    int64_t row0;
-    int len;
-    if constexpr (ROUTER) {
-      row0 = a.k0 + (int64_t)grp * a.ksplit;
-      int64_t rem = a.k0 + a.klen - row0;
-      len = (int)(rem < a.ksplit ? (rem < 0 ? 0 : rem) : a.ksplit);
-    } else {
-      const int32_t* off = a.offsets + (int64_t)sgi * (a.El + 1);
-      row0 = (int64_t)sgi * a.P_c + off[grp];
-      len = off[grp + 1] - off[grp];
-    }
-    if (len <= 0) continue;
+  const int64_t row0 = a.k0 + (int64_t)grp * a.ksplit;
+  const int64_t rem = a.k0 + a.klen - row0;
+  const int len = (int)(rem < a.ksplit ? (rem < 0 ? 0 : rem) : a.ksplit);
+  if (len > 0) {
     KSlow<BN> ldB;
     ldB.init(a.B + row0 * a.ldb + n0, a.ldb, len, tid);
-    KSlow<BM> ldA;
     KSlowSplit<BM> ldAs;
-    if constexpr (ROUTER) {
-      ldAs.init((const float*)a.A + row0 * a.lda + m0, a.lda, len, tid);
-    } else {
-      ldA.init((const uint16_t*)a.A + row0 * a.lda + m0, a.lda, len, tid);
-    }
+    ldAs.init((const float*)a.A + row0 * a.lda + m0, a.lda, len, tid);
     const int nks = (len + BK - 1) / BK;
-    if constexpr (!ROUTER) {
-      KSlow<BM> ldA1 = ldA;
-      KSlow<BN> ldB1 = ldB;
-      kloop_pgr2<TM, TN, TM>(ldA, ldA1, ldB, ldB1, nks, LA(0), LA(1), LB(0), LB(1), tid, wm * WTM, wn * WTN,
-                             lane, acc);
-      __syncthreads();  // the next segment restages both LDS buffers
-      continue;
-    }
-    if constexpr (ROUTER) { ldAs.fetch(0, tid); ldAs.commit(LA(0), LA(0) + BM * BK, tid); }
-    else { ldA.fetch(0, tid); ldA.commit(LA(0), tid); }
+    ldAs.fetch(0, tid);
+    ldAs.commit(LA(0), LA(0) + BM * BK, tid);
     ldB.fetch(0, tid);
     ldB.commit(LB(0), tid);
     __syncthreads();
     for (int ks = 0; ks < nks; ++ks) {
       const int cur = ks & 1;
       if (ks + 1 < nks) {
-        if constexpr (ROUTER) ldAs.fetch((ks + 1) * BK, tid); else ldA.fetch((ks + 1) * BK, tid);
+        ldAs.fetch((ks + 1) * BK, tid);
         ldB.fetch((ks + 1) * BK, tid);
       }
       mma_stage<TM, TN>(LA(cur), LB(cur), wm * WTM, wn * WTN, lane, acc);
-      if constexpr (ROUTER) mma_stage<TM, TN>(LA(cur) + BM * BK, LB(cur), wm * WTM, wn * WTN, lane, acc);
+      mma_stage<TM, TN>(LA(cur) + BM * BK, LB(cur), wm * WTM, wn * WTN, lane, acc);
       if (ks + 1 < nks) {
-        if constexpr (ROUTER) ldAs.commit(LA(cur ^ 1), LA(cur ^ 1) + BM * BK, tid);
-        else ldA.commit(LA(cur ^ 1), tid);
+        ldAs.commit(LA(cur ^ 1), LA(cur ^ 1) + BM * BK, tid);
         ldB.commit(LB(cur ^ 1), tid);
       }
       __syncthreads();
@@ -594,11 +278,7 @@ __global__ __launch_bounds__(kThreads) void kgroup_gemm_kernel(KGroupArgs a) {
         if (n >= a.N) continue;
         const f32x16_t& v = acc[tm][tn];
         const int64_t o = (int64_t)grp * a.strideC + (int64_t)m * a.N + n;
-        if constexpr (ROUTER) {
-          *(float4*)((float*)a.C + o) = make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
-        } else {
-          *(uint2*)((uint16_t*)a.C + o) = pack4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
-        }
+        *(float4*)((float*)a.C + o) = make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
       }
   }
 }
@@ -622,6 +302,8 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(const float* __res
 
 // ---------------------------------------------------------------------------------------------
 // FP32 SIMT path (FP32 payloads): same grouping, 64x64 tiles, 4x4 outputs per thread.
+enum SimtMode { kGateUp = 0, kDown = 1, kDownBwd = 2, kGateUpBwd = 3 };
+
 struct SimtRowsArgs {
   const float* A; const float* B; float* C; float* C2; const float* aux;
   int64_t lda, ldc, strideB;
@@ -809,47 +491,13 @@ using namespace gemm;
 
 namespace {
 constexpr int kSimtGrid = 512;  // persistent grid of the FP32 SIMT kernels
-
-// Grid: the static upper bound of tiles -- per chunk at most floor(P_c / BM) + E_local row
-// tiles (every expert adds at most one partial tile) times the column tiles -- rounded up to
-// the 8 XCDs. The device-side count decides which workgroups work.
-template <int BM, int BN, int WM, int WN, int MODE>
-hipError_t run_rows(const char* name, const RowsArgs& a, hipStream_t s) {
-  size_t lds = (size_t)2 * (BM + BN) * BK * sizeof(uint16_t);
-  auto k = rows_gemm_kernel<BM, BN, WM, WN, MODE>;
-  hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  const int outn = (MODE == kGateUp) ? BN / 2 : BN;
-  const int64_t ntiles = (a.N + outn - 1) / outn;
-  const int64_t mtiles = (int64_t)a.nc * (a.P_c / BM + a.El);
-  const int64_t per_xcd = (mtiles * ntiles + 7) / 8;
-  const int64_t grid = per_xcd * 8;
-  if (grid <= 0) return hipSuccess;
-  {
-    MOE_TRACE(name, s);
-    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kThreads), lds, s, a);
-  }
-  return hipGetLastError();
-}
 }  // namespace
 
 hipError_t launch_expert_fwd(bool bf16, const void* xd, const void* w1, const void* w2,
                              const int32_t* offsets, void* gu, void* h, void* yd, int H, int I,
                              int El, int c0, int nc, int64_t P_c, hipStream_t s) {
   if (nc <= 0 || El <= 0) return hipSuccess;
-  if (bf16) {
-    RowsArgs a{};
-    a.A = (const uint16_t*)xd; a.B = (const uint16_t*)w1; a.C = (uint16_t*)h; a.C2 = (uint16_t*)gu;
-    a.lda = H; a.ldc = I; a.strideB = (int64_t)2 * I * H; a.K = H; a.N = I; a.I = I;
-    a.offsets = offsets; a.El = El; a.c0 = c0; a.nc = nc; a.P_c = P_c; a.one = 1; a.zero = 0;
-    hipError_t e = run_rows<256, 256, 2, 2, kGateUp>("gemm_gateup_swiglu", a, s);
-    if (e != hipSuccess) return e;
-    RowsArgs b{};
-    b.A = (const uint16_t*)h; b.B = (const uint16_t*)w2; b.C = (uint16_t*)yd;
-    b.lda = I; b.ldc = H; b.strideB = (int64_t)H * I; b.K = I; b.N = H; b.I = I;
-    b.offsets = offsets; b.El = El; b.c0 = c0; b.nc = nc; b.P_c = P_c; b.one = 1; b.zero = 0;
-    return run_rows<256, 256, 2, 2, kDown>("gemm_down", b, s);
-  }
+  if (bf16) return gg_expert_fwd_bf16(xd, w1, w2, offsets, gu, h, yd, H, I, El, c0, nc, P_c, s);
   SimtRowsArgs a{};
   a.A = (const float*)xd; a.B = (const float*)w1; a.C = (float*)h; a.C2 = (float*)gu;
   a.lda = H; a.ldc = I; a.strideB = (int64_t)2 * I * H; a.K = H; a.N = I; a.I = I;
@@ -875,19 +523,7 @@ hipError_t launch_expert_dgrad(bool bf16, const void* dyd, const void* gu, const
                                const void* w2, const int32_t* offsets, void* dgu, void* dxd, int H,
                                int I, int El, int c0, int nc, int64_t P_c, hipStream_t s) {
   if (nc <= 0 || El <= 0) return hipSuccess;
-  if (bf16) {
-    RowsArgs a{};
-    a.A = (const uint16_t*)dyd; a.B = (const uint16_t*)w2; a.C = (uint16_t*)dgu; a.aux = (const uint16_t*)gu;
-    a.lda = H; a.ldc = 2 * I; a.strideB = (int64_t)H * I; a.K = H; a.N = I; a.I = I;
-    a.offsets = offsets; a.El = El; a.c0 = c0; a.nc = nc; a.P_c = P_c; a.one = 1; a.zero = 0;
-    hipError_t e = run_rows<256, 256, 2, 2, kDownBwd>("gemm_down_dgrad_swiglu", a, s);
-    if (e != hipSuccess) return e;
-    RowsArgs b{};
-    b.A = (const uint16_t*)dgu; b.B = (const uint16_t*)w1; b.C = (uint16_t*)dxd;
-    b.lda = 2 * I; b.ldc = H; b.strideB = (int64_t)2 * I * H; b.K = 2 * I; b.N = H; b.I = I;
-    b.offsets = offsets; b.El = El; b.c0 = c0; b.nc = nc; b.P_c = P_c; b.one = 1; b.zero = 0;
-    return run_rows<256, 256, 2, 2, kGateUpBwd>("gemm_gateup_dgrad", b, s);
-  }
+  if (bf16) return gg_expert_dgrad_bf16(dyd, gu, w1, w2, offsets, dgu, dxd, H, I, El, c0, nc, P_c, s);
   SimtRowsArgs a{};
   a.A = (const float*)dyd; a.B = (const float*)w2; a.C = (float*)dgu; a.aux = (const float*)gu;
   a.lda = H; a.ldc = 2 * I; a.strideB = (int64_t)H * I; a.K = H; a.N = I; a.I = I;
@@ -913,32 +549,7 @@ hipError_t launch_expert_wgrad(bool bf16, const void* dyd, const void* dgu, cons
                                const void* h, const int32_t* offsets, void* dw1, void* dw2, int H,
                                int I, int El, int n, int64_t P_c, hipStream_t s) {
   if (El <= 0) return hipSuccess;
-  if (bf16) {
-    constexpr int BM = 256, BN = 256;
-    size_t lds = (size_t)2 * (BM + BN) * BK * sizeof(uint16_t);
-    auto k = kgroup_gemm_kernel<BM, BN, 2, 2, false>;
-    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    // dW2[e] [H, I] = sum dyd^T h
-    KGroupArgs a{};
-    a.A = dyd; a.B = (const uint16_t*)h; a.C = dw2; a.lda = H; a.ldb = I; a.strideC = (int64_t)H * I;
-    a.M = H; a.N = I; a.offsets = offsets; a.El = El; a.n_chunks = n; a.P_c = P_c;
-    {
-      MOE_TRACE("gemm_wgrad_down", s);
-      hipLaunchKernelGGL(k, dim3(El * ((H + BM - 1) / BM) * ((I + BN - 1) / BN)), dim3(kThreads), lds, s, a);
-    }
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    // dW1[e] [2I, H] = sum dgu^T xd
-    KGroupArgs b{};
-    b.A = dgu; b.B = (const uint16_t*)xd; b.C = dw1; b.lda = 2 * I; b.ldb = H; b.strideC = (int64_t)2 * I * H;
-    b.M = 2 * I; b.N = H; b.offsets = offsets; b.El = El; b.n_chunks = n; b.P_c = P_c;
-    {
-      MOE_TRACE("gemm_wgrad_gateup", s);
-      hipLaunchKernelGGL(k, dim3(El * ((2 * I + BM - 1) / BM) * ((H + BN - 1) / BN)), dim3(kThreads), lds, s, b);
-    }
-    return hipGetLastError();
-  }
+  if (bf16) return gg_expert_wgrad_bf16(dyd, dgu, xd, h, offsets, dw1, dw2, H, I, El, n, P_c, s);
   SimtKArgs a{};
   a.A = (const float*)dyd; a.B = (const float*)h; a.C = (float*)dw2; a.lda = H; a.ldb = I;
   a.strideC = (int64_t)H * I; a.M = H; a.N = I; a.offsets = offsets; a.El = El; a.n_chunks = n; a.P_c = P_c;
@@ -985,7 +596,7 @@ hipError_t launch_router_wgrad(bool bf16, const float* dlogits, const void* x, f
     if (bf16) {
       constexpr int BM = 128, BN = 128;
       size_t lds = (size_t)2 * (2 * BM + BN) * BK * sizeof(uint16_t);
-      auto k = kgroup_gemm_kernel<BM, BN, 2, 2, true>;
+      auto k = router_wgrad_kernel<BM, BN, 2, 2>;
       hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
       KGroupArgs a{};

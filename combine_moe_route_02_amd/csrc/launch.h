@@ -38,16 +38,31 @@ hipError_t launch_dispatch_bwd(bool bf16, const void* dxd, const int32_t* row_of
 hipError_t launch_expert_fwd(bool bf16, const void* xd, const void* w1, const void* w2,
                              const int32_t* offsets, void* gu, void* h, void* yd, int H, int I,
                              int El, int c0, int nc, int64_t P_c, hipStream_t s);
+// FP8: h holds [P, I] BF16 values followed by [P, I] e4m3 codes (P = n_chunks * P_c)
 hipError_t launch_expert_fwd_fp8(const void* xd, const float* xd_scale, const void* w1,
                                  const float* w1_scale, const void* w2, const float* w2_scale,
                                  const int32_t* offsets, void* h, float* h_scale, void* yd, int H,
-                                 int I, int El, int c0, int nc, int64_t P_c, hipStream_t s);
+                                 int I, int El, int c0, int nc, int64_t P_c, int64_t P, hipStream_t s);
+// per-row e4m3 quantisation of the BF16 rows [c*P_c, c*P_c + N_c) of chunks c0..c0+nc-1
+hipError_t launch_quantize_segments_fp8(const void* src, void* codes, float* scale,
+                                        const int32_t* offsets, int El, int c0, int nc, int64_t P_c,
+                                        int cols, hipStream_t s);
 hipError_t launch_expert_dgrad(bool bf16, const void* dyd, const void* gu, const void* w1,
                                const void* w2, const int32_t* offsets, void* dgu, void* dxd, int H,
                                int I, int El, int c0, int nc, int64_t P_c, hipStream_t s);
 hipError_t launch_expert_wgrad(bool bf16, const void* dyd, const void* dgu, const void* xd,
                                const void* h, const int32_t* offsets, void* dw1, void* dw2, int H,
                                int I, int El, int n, int64_t P_c, hipStream_t s);
+// BF16 grouped GEMMs on the direct-to-LDS MFMA engine (grouped_gemm.hip)
+hipError_t gg_expert_fwd_bf16(const void* xd, const void* w1, const void* w2, const int32_t* offsets,
+                              void* gu, void* h, void* yd, int H, int I, int El, int c0, int nc,
+                              int64_t P_c, hipStream_t s);
+hipError_t gg_expert_dgrad_bf16(const void* dyd, const void* gu, const void* w1, const void* w2,
+                                const int32_t* offsets, void* dgu, void* dxd, int H, int I, int El,
+                                int c0, int nc, int64_t P_c, hipStream_t s);
+hipError_t gg_expert_wgrad_bf16(const void* dyd, const void* dgu, const void* xd, const void* h,
+                                const int32_t* offsets, void* dw1, void* dw2, int H, int I, int El,
+                                int n, int64_t P_c, hipStream_t s);
 int router_ksplit(int64_t tokens);
 int64_t router_partials_bytes(int64_t Tc, int E, int H);
 hipError_t launch_router_wgrad(bool bf16, const float* dlogits, const void* x, float* partials,

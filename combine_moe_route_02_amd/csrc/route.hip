@@ -7,113 +7,134 @@
 // the selected logits. The permutation is the stable sort of (token, slot) pairs by expert inside
 // each chunk: within an expert, rows follow ascending token index.
 //
-// Two launches, both deterministic:
-//   route_topk   one lane per token: top-k, gates, and a per-64-token-block histogram of all
-//                E experts (LDS integer adds: the sum does not depend on their order).
-//   route_layout per block: prefix of the earlier blocks' histograms (exclusive scan), local
-//                offsets, then each token's rank among the block's earlier tokens choosing the
-//                same expert from a 64-bit ballot mask (popcount below the lane).
+// Two launches per chunk range, both deterministic:
+//   route_topk   16 lanes per token (4 tokens per wave, 64 tokens per 1024-thread block). Each
+//                lane keeps a sorted top-K list of its share of the experts as 64-bit keys
+//                (order-preserving logit bits above the complemented expert index, so ties go to
+//                the lower index), then K rounds of a 16-lane max merge the lists. A per-block
+//                histogram over all E experts is summed in LDS with integer atomics (the sum
+//                does not depend on their order).
+//   route_layout per block: rows that earlier blocks of the chunk give each local expert (one
+//                wave per expert, lanes over blocks), local offsets, then each token's rank among
+//                the block's earlier tokens choosing the same expert from a 64-bit ballot mask
+//                (popcount below the lane); one wave per top-k slot.
 #include "common.h"
 #include "launch.h"
 #include "trace.h"
 
 namespace moe {
 
-constexpr int kRouteBlock = 64;   // tokens per block: one wave
-constexpr int kLogitTile = 128;   // logits per token staged in LDS at a time
+constexpr int kRouteBlock = 64;     // tokens per block (one histogram per block)
+constexpr int kRouteThreads = 1024; // 16 waves
+constexpr int kGroup = 16;          // lanes per token in route_topk
 
-// One wave per 64 tokens. The wave stages a [64, 128] tile of logits through LDS with coalesced
-// 16-byte loads (rows padded to 129 floats so that each lane reading its own row is
-// conflict-free), then every lane runs an unrolled top-K insertion over its token's logits.
+// Order-preserving map of a logit to 32 bits: larger logit -> larger key; NaN ranks as -inf and
+// -0 equals +0.
+MOE_DEV uint32_t logit_key(float x) {
+  if (x != x) x = -__builtin_huge_valf();
+  if (x == 0.f) x = 0.f;
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+MOE_DEV float key_logit(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+// Full key: logit key above the complemented expert index, so equal logits rank the lower index
+// higher. Every real key is > 0; 0 marks an empty list slot.
+MOE_DEV uint64_t full_key(float x, int e) {
+  return ((uint64_t)logit_key(x) << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
+}
+
 template <int K>
-__global__ __launch_bounds__(kRouteBlock) void route_topk_kernel(
+MOE_DEV void insert_key(uint64_t (&l)[K], uint64_t key) {
+#pragma unroll
+  for (int s = 0; s < K; ++s) {
+    const uint64_t cur = l[s];
+    const bool take = key > cur;
+    l[s] = take ? key : cur;
+    key = take ? cur : key;
+  }
+}
+
+MOE_DEV uint64_t shfl_xor_u64(uint64_t v, int o) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, o, kWave);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), o, kWave);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+template <int K>
+__global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
     const float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ gates,
     int32_t* __restrict__ block_hist, int64_t T, int E, int n, int chunk0, int nbpc) {
-  __shared__ float tile[kRouteBlock][kLogitTile + 1];
   extern __shared__ int hist[];  // [E]
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
   const int c = chunk0 + blockIdx.x / nbpc;
   const int bl = blockIdx.x % nbpc;
   const ChunkRange cr = chunk_range(T, n, c);
-  for (int e = lane; e < E; e += kRouteBlock) hist[e] = 0;
-  const int64_t tb = cr.t0 + (int64_t)bl * kRouteBlock;
-  const int ntok = (int)max((int64_t)0, min((int64_t)kRouteBlock, cr.t1 - tb));
-  const int64_t t = tb + lane;
-  const bool valid = lane < ntok;
+  for (int e = tid; e < E; e += kRouteThreads) hist[e] = 0;
+  __syncthreads();
+  const int q = tid & (kGroup - 1);                 // lane within the token's group
+  const int64_t t = cr.t0 + (int64_t)bl * kRouteBlock + (tid / kGroup);
+  const bool valid = t < cr.t1;
 
-  float v[K];
-  int id[K];
+  uint64_t l[K];
 #pragma unroll
-  for (int s = 0; s < K; ++s) { v[s] = -__builtin_huge_valf(); id[s] = 0x7fffffff; }
-  for (int e0 = 0; e0 < E; e0 += kLogitTile) {
-    const int w = min(kLogitTile, E - e0);
-    __syncthreads();
-    if ((E & 3) == 0 && w == kLogitTile) {
-      // full tile: 32 float4 per token row; two rows per wave instruction, all loads in flight
-      constexpr int kQ = kLogitTile / 4;
-#pragma unroll 8
-      for (int i = lane; i < kRouteBlock * kQ; i += kRouteBlock) {
-        const int r = i / kQ, q = i % kQ;
-        if (r < ntok) {
-          const float4 f = *(const float4*)(logits + (tb + r) * (int64_t)E + e0 + 4 * q);
-          tile[r][4 * q] = f.x; tile[r][4 * q + 1] = f.y; tile[r][4 * q + 2] = f.z; tile[r][4 * q + 3] = f.w;
+  for (int s = 0; s < K; ++s) l[s] = 0;
+  if (valid) {
+    const float* row = logits + t * (int64_t)E;
+    if ((E & 3) == 0) {
+      // lane q reads experts [base + 4q, base + 4q + 4): 256 contiguous bytes per group
+      for (int base = 0; base < E; base += 4 * kGroup) {
+        const int e = base + 4 * q;
+        if (e < E) {
+          const float4 f = *(const float4*)(row + e);
+          insert_key<K>(l, full_key(f.x, e));
+          insert_key<K>(l, full_key(f.y, e + 1));
+          insert_key<K>(l, full_key(f.z, e + 2));
+          insert_key<K>(l, full_key(f.w, e + 3));
         }
-      }
-    } else if ((E & 3) == 0) {
-      const int w4 = w >> 2;
-      for (int i = lane; i < ntok * w4; i += kRouteBlock) {
-        const int r = i / w4, q = i % w4;
-        const float4 f = *(const float4*)(logits + (tb + r) * (int64_t)E + e0 + 4 * q);
-        tile[r][4 * q] = f.x; tile[r][4 * q + 1] = f.y; tile[r][4 * q + 2] = f.z; tile[r][4 * q + 3] = f.w;
       }
     } else {
-      for (int i = lane; i < ntok * w; i += kRouteBlock) {
-        const int r = i / w, q = i % w;
-        tile[r][q] = logits[(tb + r) * (int64_t)E + e0 + q];
-      }
-    }
-    __syncthreads();
-    if (valid) {
-      for (int q = 0; q < w; ++q) {
-        float x = tile[lane][q];
-        if (x != x) x = -__builtin_huge_valf();  // NaN ranks lowest
-        int xi = e0 + q;
-        // candidate beats slot s if larger, or equal with a lower index (only sentinels)
-        if (x > v[K - 1] || (x == v[K - 1] && xi < id[K - 1])) {
-#pragma unroll
-          for (int s = 0; s < K; ++s) {
-            bool take = x > v[s] || (x == v[s] && xi < id[s]);
-            float tv = v[s];
-            int ti = id[s];
-            v[s] = take ? x : v[s];
-            id[s] = take ? xi : id[s];
-            x = take ? tv : x;
-            xi = take ? ti : xi;
-          }
-        }
-      }
+      for (int e = q; e < E; e += kGroup) insert_key<K>(l, full_key(row[e], e));
     }
   }
-  if (valid) {
-    float p[K];
-    float sum = 0.f;
+  // K rounds: the group's largest head wins and its lane pops it (keys are distinct)
+  uint64_t sel[K];
 #pragma unroll
-    for (int s = 0; s < K; ++s) { p[s] = expf(v[s] - v[0]); sum += p[s]; }
+  for (int s = 0; s < K; ++s) {
+    uint64_t m = l[0];
+#pragma unroll
+    for (int o = kGroup / 2; o > 0; o >>= 1) {
+      const uint64_t other = shfl_xor_u64(m, o);
+      m = other > m ? other : m;
+    }
+    sel[s] = m;
+    if (l[0] == m) {
+#pragma unroll
+      for (int r = 0; r + 1 < K; ++r) l[r] = l[r + 1];
+      l[K - 1] = 0;
+    }
+  }
+  if (valid && q < K) {
+    const float v0 = key_logit((uint32_t)(sel[0] >> 32));
+    float sum = 0.f, mine = 0.f;
+    int myid = 0;
 #pragma unroll
     for (int s = 0; s < K; ++s) {
-      topk_idx[t * K + s] = id[s];
-      gates[t * K + s] = p[s] / sum;
-      atomicAdd(&hist[id[s]], 1);
+      const float p = expf(key_logit((uint32_t)(sel[s] >> 32)) - v0);
+      sum += p;
+      if (s == q) { mine = p; myid = (int)(0xffffffffu - (uint32_t)sel[s]); }
     }
+    topk_idx[t * K + q] = myid;
+    gates[t * K + q] = mine / sum;
+    atomicAdd(&hist[myid], 1);
   }
   __syncthreads();
   int32_t* out = block_hist + ((int64_t)c * nbpc + bl) * E;
-  for (int e = lane; e < E; e += kRouteBlock) out[e] = hist[e];
+  for (int e = tid; e < E; e += kRouteThreads) out[e] = hist[e];
 }
 
-// One wave per 64 tokens: local offsets from the chunk's block histograms, then each token's
-// rank among the block's earlier tokens choosing the same expert from a 64-bit ballot mask.
-__global__ __launch_bounds__(kRouteBlock) void route_layout_kernel(
+__global__ __launch_bounds__(kRouteThreads) void route_layout_kernel(
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ block_hist,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ row_of,
     int32_t* __restrict__ src_token, int64_t T, int E, int e0, int El, int K, int n, int chunk0,
@@ -124,17 +145,17 @@ __global__ __launch_bounds__(kRouteBlock) void route_layout_kernel(
   int* off = base + El;
   uint64_t* mask = (uint64_t*)(((uintptr_t)(off + El + 1) + 7) & ~(uintptr_t)7);
 
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int kWaves = kRouteThreads / 64;
   const int c = chunk0 + blockIdx.x / nbpc;
   const int bl = blockIdx.x % nbpc;
   const ChunkRange cr = chunk_range(T, n, c);
   const int32_t* bh = block_hist + (int64_t)c * nbpc * E;
 
-  // per local expert: rows owned by earlier blocks of this chunk, and the chunk total; lanes
-  // stride over the blocks and a wave reduction sums them
-  for (int el = 0; el < El; ++el) {
+  // one wave per local expert: rows owned by earlier blocks of this chunk, and the chunk total
+  for (int el = wave; el < El; el += kWaves) {
     int before = 0, total = 0;
-    for (int b = lane; b < nbpc; b += kRouteBlock) {
+    for (int b = lane; b < nbpc; b += 64) {
       const int h = bh[(int64_t)b * E + e0 + el];
       before += (b < bl) ? h : 0;
       total += h;
@@ -143,9 +164,9 @@ __global__ __launch_bounds__(kRouteBlock) void route_layout_kernel(
     total = wave_sum_int(total);
     if (lane == 0) { base[el] = before; off[el + 1] = total; }
   }
-  for (int el = lane; el < El; el += kRouteBlock) mask[el] = 0;
+  for (int el = tid; el < El; el += kRouteThreads) mask[el] = 0;
   __syncthreads();
-  if (lane == 0) {  // exclusive scan over local experts (El is small)
+  if (tid == 0) {  // exclusive scan over the local experts
     int run = 0;
     for (int el = 0; el < El; ++el) { int cnt = off[el + 1]; off[el] = run; run += cnt; }
     off[El] = run;
@@ -153,40 +174,39 @@ __global__ __launch_bounds__(kRouteBlock) void route_layout_kernel(
   __syncthreads();
   const int N_c = off[El];
   if (bl == 0) {
-    for (int e = lane; e < E; e += kRouteBlock) {
+    for (int e = tid; e < E; e += kRouteThreads) {
       int total = 0;
 #pragma unroll 16
       for (int b = 0; b < nbpc; ++b) total += bh[(int64_t)b * E + e];
       counts[(int64_t)c * E + e] = total;
     }
-    for (int el = lane; el <= El; el += kRouteBlock) offsets[(int64_t)c * (El + 1) + el] = off[el];
+    for (int el = tid; el <= El; el += kRouteThreads) offsets[(int64_t)c * (El + 1) + el] = off[el];
   }
 
+  // wave j < K owns slot j of the block's 64 tokens (lane = token)
   const int64_t t = cr.t0 + (int64_t)bl * kRouteBlock + lane;
   const bool valid = t < cr.t1;
-  if (valid) {
-    for (int j = 0; j < K; ++j) {
-      int el = topk_idx[t * K + j] - e0;
-      if (el >= 0 && el < El) atomicOr((unsigned long long*)&mask[el], 1ull << lane);
-    }
+  const int j = wave;
+  int el = -1;
+  if (valid && j < K) {
+    el = topk_idx[t * K + j] - e0;
+    if (el >= 0 && el < El) atomicOr((unsigned long long*)&mask[el], 1ull << lane);
+    else el = -1;
   }
   __syncthreads();
-  if (valid) {
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int j = 0; j < K; ++j) {
-      int el = topk_idx[t * K + j] - e0;
-      int32_t row = -1;
-      if (el >= 0 && el < El) {
-        int rank = __popcll(mask[el] & below);
-        int64_t r = (int64_t)c * P_c + off[el] + base[el] + rank;
-        src_token[r] = (int32_t)t;
-        row = (int32_t)r;
-      }
-      row_of[t * K + j] = row;
+  if (valid && j < K) {
+    int32_t row = -1;
+    if (el >= 0) {
+      const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+      const int rank = __popcll(mask[el] & below);
+      const int64_t r = (int64_t)c * P_c + off[el] + base[el] + rank;
+      src_token[r] = (int32_t)t;
+      row = (int32_t)r;
     }
+    row_of[t * K + j] = row;
   }
   // rows N_c..P_c-1 of this chunk's region hold no token
-  for (int64_t r = N_c + (int64_t)bl * kRouteBlock + lane; r < P_c; r += (int64_t)nbpc * kRouteBlock)
+  for (int64_t r = N_c + (int64_t)bl * kRouteThreads + tid; r < P_c; r += (int64_t)nbpc * kRouteThreads)
     src_token[(int64_t)c * P_c + r] = -1;
 }
 
@@ -205,7 +225,7 @@ hipError_t launch_route(const float* logits, int32_t* topk_idx, float* gates, in
                         int64_t T, int E, int e0, int El, int K, int n, int chunk0, int nchunks,
                         int64_t P_c, hipStream_t s) {
   const int nbpc = route_blocks_per_chunk(T, n);
-  dim3 grid(nbpc * nchunks), block(kRouteBlock);
+  dim3 grid(nbpc * nchunks), block(kRouteThreads);
   size_t sm1 = (size_t)E * sizeof(int);
   switch (K) {
 #define MOE_ROUTE_K(KK)                                                                      \

@@ -137,6 +137,28 @@ __global__ __launch_bounds__(256) void quantize_rows_fp8_kernel(
   if (lane == 0) scale[r] = amax > 0.f ? amax / 448.0f : 1.0f;
 }
 
+// Per-row quantisation of the dispatch rows [c*P_c, c*P_c + N_c) of chunk c (N_c from the offset
+// table, so the row count stays on the device): one wave per row, grid-stride over the rows, the
+// FP32 steps of dispatch.
+__global__ __launch_bounds__(256) void quantize_segments_fp8_kernel(
+    const u32x4* __restrict__ src, uint2* __restrict__ codes, float* __restrict__ scale,
+    const int32_t* __restrict__ offsets, int El, int c0, int64_t P_c, int64_t nvec) {
+  const int lane = threadIdx.x & 63;
+  const int c = c0 + (int)blockIdx.y;
+  const int64_t n = offsets[(int64_t)c * (El + 1) + El];
+  for (int64_t r = (int64_t)blockIdx.x * kTokPerBlock + (threadIdx.x >> 6); r < n;
+       r += (int64_t)gridDim.x * kTokPerBlock) {
+    const int64_t row = (int64_t)c * P_c + r;
+    const u32x4* s = src + row * nvec;
+    float m = 0.f;
+    for (int64_t i = lane; i < nvec; i += 64) m = fmaxf(m, absmax8(s[i]));
+    const float amax = wave_max(m);
+    const float inv = amax > 0.f ? 448.0f / amax : 0.f;
+    for (int64_t i = lane; i < nvec; i += 64) codes[row * nvec + i] = quant8(s[i], inv);
+    if (lane == 0) scale[row] = amax > 0.f ? amax / 448.0f : 1.0f;
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // Vector helpers over a 16-byte payload vector: 4 FP32 or 8 BF16 values.
 template <typename T> struct Vec;
@@ -388,6 +410,18 @@ hipError_t launch_quantize_rows_fp8(const void* src, void* codes, float* scale, 
     MOE_TRACE("quantize_rows_fp8", s);
     hipLaunchKernelGGL(quantize_rows_fp8_kernel, tok_grid(rows), dim3(256), 0, s, (const u32x4*)src,
                        (uint2*)codes, scale, rows, (int64_t)cols / 8);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_segments_fp8(const void* src, void* codes, float* scale,
+                                        const int32_t* offsets, int El, int c0, int nc, int64_t P_c,
+                                        int cols, hipStream_t s) {
+  if (nc <= 0 || El <= 0) return hipSuccess;
+  {
+    MOE_TRACE("quantize_h_fp8", s);
+    hipLaunchKernelGGL(quantize_segments_fp8_kernel, dim3(256, (unsigned)nc), dim3(256), 0, s,
+                       (const u32x4*)src, (uint2*)codes, scale, offsets, El, c0, P_c, (int64_t)cols / 8);
   }
   return hipGetLastError();
 }

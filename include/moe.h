@@ -37,7 +37,8 @@
  *        xd                             f32       bf16       e4m3 codes + xd_scale f32 [P]
  *        W1, W2                         f32       bf16       e4m3 codes + w1_scale [E_l,2I],
  *                                                            w2_scale [E_l,H] (f32)
- *        gu, h, yd, dyd, dgu, dxd       f32       bf16       h: bf16 and h_scale f32 [P]; yd bf16
+ *        gu, h, yd, dyd, dgu, dxd       f32       bf16       h: [P,I] bf16 then [P,I] e4m3 codes
+ *                                                            (3*P*I bytes), h_scale f32 [P]; yd bf16
  *        out                            f32       bf16       bf16
  *        dw1, dw2                       f32       bf16       -
  *     logits, gates, dgates, dlogits, dwr_acc are always f32; every index array is int32.
@@ -104,7 +105,7 @@ moe_status moe_route(const moe_desc* d, int chunk, const float* logits, int32_t*
 /* Dispatch: xd[row_of[t][j]] = x[t] for every local slot (a bitwise row copy for F32/BF16;
  * each touched token row is read once). FP8: per token amax over the BF16 row,
  * xd = e4m3(x * (448/amax)) with FP32 steps, RNE, saturating; xd_scale[row] = amax/448 (1 for
- * an all-zero row); h_scale[row] is cleared for the FFN's row maxima. Rows N_c..P_c-1 are not
+ * an all-zero row); h_scale[row] is cleared (moe_expert_ffn writes it). Rows N_c..P_c-1 are not
  * written. xd_scale/h_scale may be NULL unless dtype is FP8. */
 moe_status moe_dispatch(const moe_desc* d, int chunk, const void* x, const int32_t* row_of,
                         void* xd, float* xd_scale, float* h_scale, void* stream);
@@ -112,9 +113,11 @@ moe_status moe_dispatch(const moe_desc* d, int chunk, const void* x, const int32
 /* Grouped SwiGLU expert FFN over every local expert's rows [c*P_c + offsets[c][e],
  * c*P_c + offsets[c][e+1]): G = xd W1g^T, U = xd W1u^T (FP32 accumulation),
  * h = silu(G) * U with silu(z) = z/(1+exp(-z)), yd = h W2^T. gu (may be NULL) saves G and U
- * for the backward ([P,2I], G in columns 0..I-1). h is required ([P,I]). FP8: GEMMs on FP8
- * MFMA with dequantisation s_row*s_col; h is kept in BF16 with its row absmax in h_scale and
- * is quantised per row to e4m3 on the way into the down projection. */
+ * for the backward ([P,2I], G in columns 0..I-1). h is required ([P,I]). FP8: both GEMMs run on
+ * FP8 MFMA with FP32 accumulation dequantised by s_row*s_col; h is written in BF16, then each
+ * dispatch row of h is quantised to e4m3 (per-row absmax, the FP32 steps of moe_dispatch) into
+ * the codes half of the h buffer with its scale in h_scale, and the down projection reads the
+ * codes. gu is unused for FP8. */
 moe_status moe_expert_ffn(const moe_desc* d, int chunk, const void* xd, const float* xd_scale,
                           const void* w1, const float* w1_scale, const void* w2,
                           const float* w2_scale, const int32_t* offsets, void* gu, void* h,

@@ -170,3 +170,42 @@ def test_backward_launch_order_input_grad_before_wgrad():
     streams = {n: s for n, s, _ in log}
     assert streams["dispatch"] == streams["combine"] != streams["gemm_gateup_swiglu"]
     assert streams["gemm_wgrad_gateup"] == streams["gemm_gateup_swiglu"]
+
+
+# ----------------------------------------------------------------------------- FP8 payload path
+
+FP8_SMALL = [
+    MoeConfig("fp8_rag", T=1000, H=256, I=192, E=32, E_local=8, e0=4, k=4, n_chunks=2, dtype="fp8",
+              seed_base=90),
+    MoeConfig("fp8_n3_tail", T=777, H=384, I=320, E=64, E_local=16, e0=48, k=6, n_chunks=3, dtype="fp8",
+              seed_base=95),
+]
+
+
+def _check_fp8_weight_codes(run, ref):
+    """The GPU's per-row weight quantisation gives the oracle's codes and scales bit for bit."""
+    np.testing.assert_array_equal(run.bufs["w1"].cpu().numpy(), ref["w1q"])
+    np.testing.assert_array_equal(run.bufs["w2"].cpu().numpy(), ref["w2q"])
+    np.testing.assert_array_equal(run.bufs["w1_scale"].cpu().numpy().view(np.uint32), ref["w1s"].view(np.uint32))
+    np.testing.assert_array_equal(run.bufs["w2_scale"].cpu().numpy().view(np.uint32), ref["w2s"].view(np.uint32))
+
+
+@pytest.mark.parametrize("cfg", FP8_SMALL, ids=[c.name for c in FP8_SMALL])
+def test_fp8_forward_small(cfg):
+    _require_gpu()
+    print(f"[parity] {cfg}", flush=True)
+    run = harness.run_gpu(cfg, sentinel=-5.0)
+    ref = harness.run_oracle(run)
+    _check_fp8_weight_codes(run, ref)
+    print("[fp8]", harness.check_forward(run, ref, sentinel=-5.0))
+
+
+@pytest.mark.parametrize("name", ["fp8_16k", "fp8_16k_h7168"])
+def test_fp8_forward_full(name):
+    _require_gpu()
+    cfg = moe_inputs.CONFIGS[name]
+    print(f"[parity] {cfg}", flush=True)
+    run = harness.run_gpu(cfg, sentinel=-5.0)
+    ref = harness.run_oracle(run)
+    _check_fp8_weight_codes(run, ref)
+    print(f"[{name}]", harness.check_forward(run, ref, sentinel=-5.0), flush=True)
