@@ -10,7 +10,9 @@
 // one FP32 reduction and convert once (the FP32-accumulate-then-convert rule that ChunkedEP's
 // "Numerical status -- unresolved" states for the router weights).
 //
-// Engine (one 256-thread workgroup = 4 waves in a 2 x 2 grid over a BM x BN output tile):
+// Engine (one 512-thread workgroup = 8 waves in a 2 x 4 grid over a BM x BN output tile, two
+// waves per SIMD: on gfx950 one wave issues global -> LDS loads at only ~5 B/clk, so eight waves
+// share the ~32 B/clk per CU that a 256 x 256 tile needs; LDS reads stay below the port's rate):
 //   * Operands reach LDS by direct-to-LDS 16-byte buffer loads (buffer_load_dwordx4 ... lds):
 //     no staging registers, no VALU on the load path. The scalar buffer descriptor's extent
 //     masks rows past an expert's segment or a matrix edge (such loads return zero).
@@ -37,7 +39,9 @@
 namespace moe {
 namespace gg {
 
-constexpr int kThreads = 256;
+constexpr int kWM = 2, kWN = 4;       // waves per workgroup along M and N
+constexpr int kWaves = kWM * kWN;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kNst = 4;             // LDS ring stages
 constexpr int kRowB = 64;           // K bytes per MN row per stage
 constexpr int kKRows = 32;          // K rows per stage for 16-bit K-slow operands
@@ -70,10 +74,11 @@ MOE_DEV int ks_off(int k, int c) { return k * (2 * R) + ((c ^ ((k & 3) << 2)) <<
 
 // ---------------------------------------------------------------------------------------------
 // Operand tile loader: R MN rows, one stage = R * 64 bytes = R / 16 wave instructions of 1 KiB,
-// R / 64 per wave.
+// spread over the workgroup's waves.
 template <int R, bool KSLOW>
 struct Loader {
-  static constexpr int NI = R / 64;
+  static constexpr int NI = R / (16 * kWaves);
+  static_assert(NI >= 1 && R % (16 * kWaves) == 0, "tile rows must cover every wave");
   __amdgpu_buffer_rsrc_t rs;
   uint32_t voff[NI];
   uint32_t step;  // HBM bytes between consecutive stages
@@ -313,7 +318,7 @@ constexpr size_t rows_lds_bytes() {
 
 template <int BM, int BN, int MODE, bool FP8>
 __global__ __launch_bounds__(kThreads) void rows_kernel(RowsArgs a) {
-  constexpr int WTM = BM / 2, WTN = BN / 2, TM = WTM / 32, TN = WTN / 32;
+  constexpr int WTM = BM / kWM, WTN = BN / kWN, TM = WTM / 32, TN = WTN / 32;
   constexpr bool kSwiGLU = (MODE == kGateUp);
   constexpr bool kBKS = (MODE == kDownBwd || MODE == kGateUpBwd);
   constexpr int ES = FP8 ? 1 : 2;      // element bytes
@@ -326,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(RowsArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / kWN, wn = wave % kWN;
   const int G = a.nc * a.El;
   const int ntiles = (a.N + OUTN - 1) / OUTN;
   for (int g = tid; g < G; g += kThreads) {
@@ -560,11 +565,11 @@ constexpr size_t wgrad_lds_bytes() {
 
 template <int BM, int BN>
 __global__ __launch_bounds__(kThreads) void wgrad_kernel(WgradArgs a) {
-  constexpr int WTM = BM / 2, WTN = BN / 2, TM = WTM / 32, TN = WTN / 32;
+  constexpr int WTM = BM / kWM, WTN = BN / kWN, TM = WTM / 32, TN = WTN / 32;
   extern __shared__ __attribute__((aligned(1024))) char ring[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / kWN, wn = wave % kWN;
   const int mtiles = (a.M + BM - 1) / BM, ntiles = (a.N + BN - 1) / BN;
   const int total = a.El * mtiles * ntiles;
   const int per_xcd = (total + 7) / 8;
