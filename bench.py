@@ -29,6 +29,107 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense BF16 MFMA, TFLOP/s
 PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X vector FP32
 
+# launch-log name -> (source file under the package's csrc/, substring of the kernel symbol that
+# rocprofv3 reports for it)
+KERNEL_SYMBOLS = {
+    "route_topk": ("route.hip", "route_topk_kernel"),
+    "route_layout": ("route.hip", "route_layout_kernel"),
+    "dispatch": ("rows.hip", "dispatch_copy_kernel"),
+    "combine": ("rows.hip", "combine_kernel"),
+    "combine_bwd": ("rows.hip", "combine_bwd_kernel"),
+    "route_bwd_dlogits": ("rows.hip", "route_bwd_dlogits_kernel"),
+    "dispatch_bwd": ("rows.hip", "dispatch_bwd_kernel"),
+    "gemm_gateup_swiglu": ("grouped_gemm.hip", "rows_kernel<256, 256, 0, false>"),
+    "gemm_down": ("grouped_gemm.hip", "rows_kernel<256, 256, 1, false>"),
+    "gemm_down_dgrad_swiglu": ("grouped_gemm.hip", "rows_kernel<256, 128, 2, false>"),
+    "gemm_gateup_dgrad": ("grouped_gemm.hip", "rows_kernel<256, 256, 3, false>"),
+    "gemm_wgrad_down": ("grouped_gemm.hip", "wgrad_kernel<256, 128>"),
+    "gemm_wgrad_gateup": ("grouped_gemm.hip", "wgrad_kernel<256, 256>"),
+    "gemm_router_wgrad": ("gemm.hip", "router_wgrad_kernel"),
+    "router_reduce": ("gemm.hip", "reduce_partials_kernel"),
+}
+CALIBRATION_BYTES = 64 << 20   # a plain elementwise copy of this many bytes (read and written once,
+CALIBRATION_SYMBOL = "MulFunctor"  # one dispatch: y = 2 * x in FP32) runs before the timed region
+
+
+def source_sha(name: str) -> str:
+    """Short hash of a kernel's source file (and the shared headers): counters taken on other
+    source are not reported for this build."""
+    import hashlib
+    csrc = os.path.join(ROOT, "combine_moe_route_02_amd", "csrc")
+    h = hashlib.sha256()
+    for f in (KERNEL_SYMBOLS[name][0], "common.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _counter_rows(d):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def pmc_summary(fetch_dir: str, write_dir: str, cmd: str) -> str:
+    """Markdown summary of two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch):
+    per kernel the median per dispatch, each scaled by what the counter reads for the calibration
+    copy of known size, plus one machine-readable `traffic:` line per kernel for the roofline."""
+    import statistics
+    med = {}
+    for tag, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        per = {}
+        for r in _counter_rows(d):
+            if r["Counter_Name"] != tag:
+                continue
+            per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+        med[tag] = {k: statistics.median(v) for k, v in per.items()}
+
+    def find(tag, sym):
+        hits = [v for k, v in med[tag].items() if sym in k]
+        return hits[0] if hits else None
+    cal_f = find("FETCH_SIZE", CALIBRATION_SYMBOL)
+    cal_w = find("WRITE_SIZE", CALIBRATION_SYMBOL)
+    if not cal_f or not cal_w:
+        raise SystemExit("calibration copy kernel not found in the counter runs")
+    f_fetch, f_write = CALIBRATION_BYTES / cal_f, CALIBRATION_BYTES / cal_w
+    out = ["# HBM traffic per launch from rocprofv3 counters", "",
+           "Commands (from the repository root, MI355X):", "", "```", cmd, "```", "",
+           f"Calibration: a {CALIBRATION_BYTES >> 20} MiB elementwise copy (`y = 2x`, kernel `{CALIBRATION_SYMBOL}`) reads "
+           f"FETCH_SIZE {cal_f / 1024:.0f} KiB and WRITE_SIZE {cal_w / 1024:.0f} KiB, so FETCH_SIZE is scaled by "
+           f"{f_fetch:.3f} and WRITE_SIZE by {f_write:.3f}.", "",
+           "| kernel | fetch MB/launch (scaled) | write MB/launch (scaled) |", "|---|---:|---:|"]
+    lines = []
+    for name, (src, sym) in KERNEL_SYMBOLS.items():
+        fv, wv = find("FETCH_SIZE", sym), find("WRITE_SIZE", sym)
+        if fv is None or wv is None:
+            continue
+        fb, wb = fv * f_fetch, wv * f_write
+        out.append(f"| `{name}` | {fb / 1e6:.2f} | {wb / 1e6:.2f} |")
+        lines.append(f"traffic: kernel={name} source_sha={source_sha(name)} fetch_bytes={fb:.0f} write_bytes={wb:.0f}")
+    out += ["", "Machine-readable lines (bench.py reads them when the source hash matches):", "", "```"] + lines + ["```", ""]
+    return "\n".join(out)
+
+
+def committed_traffic(name: str):
+    """Calibrated HBM bytes per launch for a kernel from profiles/*traffic*.md, or None when no
+    summary was taken on this kernel's current source."""
+    import glob
+    want = source_sha(name) if name in KERNEL_SYMBOLS else None
+    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*traffic*.md"))):
+        with open(f) as fh:
+            for line in fh:
+                if not line.startswith("traffic:"):
+                    continue
+                kv = dict(x.split("=", 1) for x in line.split()[1:])
+                if kv.get("kernel") == name and kv.get("source_sha") == want:
+                    return float(kv["fetch_bytes"]) + float(kv["write_bytes"])
+    return None
+
+
 GEMM_KERNELS = {"gemm_gateup_swiglu", "gemm_down", "gemm_down_dgrad_swiglu", "gemm_gateup_dgrad",
                 "gemm_wgrad_down", "gemm_wgrad_gateup", "gemm_router_wgrad"}
 
@@ -98,7 +199,12 @@ def main():
     ap.add_argument("--workload", default="fb16k")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COMMANDS"),
+                    help="write the markdown traffic summary of two rocprofv3 --pmc runs and exit (no GPU)")
     args = ap.parse_args()
+    if args.pmc_summary:
+        print(pmc_summary(*args.pmc_summary))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the layer; --gpus {args.gpus} is not supported "
               f"(this build has no multi-GPU path: run with --gpus 1)", file=sys.stderr)
@@ -129,6 +235,15 @@ def main():
     cs = torch.cuda.Stream()
     aux = torch.cuda.Stream()
     torch.cuda.synchronize()
+
+    # calibration for the HBM byte counters: one elementwise kernel that reads and writes a known
+    # number of bytes once
+    cal_src = torch.ones(CALIBRATION_BYTES // 4, dtype=torch.float32, device="cuda")
+    cal_dst = torch.empty_like(cal_src)
+    for _ in range(2):
+        torch.mul(cal_src, 2.0, out=cal_dst)
+    torch.cuda.synchronize()
+    del cal_src, cal_dst
 
     def fb():
         mh.moe_layer_forward_backward(d, bufs, cs, aux)
@@ -241,12 +356,12 @@ def main():
     if unit == "flop":
         ach = wk / (dtot / args.steps * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": dom,
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": committed_traffic(dom), "kernel": dom,
                 "avg_launch_us": round(dtot / dcnt * 1e3, 3), "work_per_launch": wk / (dcnt / args.steps)}
     else:
         ach = wk / (dtot / args.steps * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "kernel": dom,
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": committed_traffic(dom), "kernel": dom,
                 "avg_launch_us": round(dtot / dcnt * 1e3, 3), "work_per_launch": wk / (dcnt / args.steps)}
 
     iso_ms = sum(v[1] for v in iso.values()) / args.steps

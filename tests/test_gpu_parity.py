@@ -209,3 +209,51 @@ def test_fp8_forward_full(name):
     ref = harness.run_oracle(run)
     _check_fp8_weight_codes(run, ref)
     print(f"[{name}]", harness.check_forward(run, ref, sentinel=-5.0), flush=True)
+
+
+# ----------------------------------------------------------------------------- 32K fused, imbalanced + live extent
+
+def test_full_fused_32k_forward_backward():
+    """Fused forward+backward at 32768 tokens in two chunks (router gradient accumulated in FP32
+    across the chunks, converted once)."""
+    _require_gpu()
+    cfg = moe_inputs.CONFIGS["fb32k"]
+    print(f"[parity] {cfg}", flush=True)
+    run = harness.run_gpu(cfg)
+    ref = harness.run_oracle(run)
+    print("[fb32k fwd]", harness.check_forward(run, ref), flush=True)
+    print("[fb32k bwd]", harness.check_backward(run, ref), flush=True)
+
+
+def test_full_imbalanced_routing_at_live_extent():
+    """Zipf(1.2)-biased routing with empty local experts; combine writes a fresh output at the
+    extent a live 32K-token graph holds (262144 rows), crops to the logical rows, and gives the
+    same logical rows once that graph is released and the call's own extent (131072) applies."""
+    _require_gpu()
+    import combine_moe_route_02_amd as mh
+    cfg = moe_inputs.CONFIGS["zipf16k"]
+    big = moe_inputs.CONFIGS["fb32k"]
+    tr = mh.ExtentTracker()
+    own = mh.required_extent(cfg.T, cfg.k, cfg.E_local, cfg.n_chunks)[1]
+    live = tr.acquire(mh.required_extent(big.T, big.k, big.E_local, big.n_chunks)[1])
+    P_live = tr.current(own)
+    assert (own, P_live) == (131072, 262144)
+    print(f"[parity] {cfg} P_out={P_live}", flush=True)
+    run = harness.run_gpu(cfg, P_out=P_live, sentinel=-9.0)
+    out = run.bufs["out"]
+    assert tuple(out.shape) == (P_live, cfg.H)
+    assert out.untyped_storage().nbytes() == P_live * cfg.H * 2
+    ref = harness.run_oracle(run)
+    counts = ref["counts"][:, cfg.e0:cfg.e0 + cfg.E_local].sum(axis=0)
+    print("[zipf16k] local rows per expert", counts.tolist(), flush=True)
+    assert np.count_nonzero(counts == 0) >= cfg.n_empty
+    print("[zipf16k fwd]", harness.check_forward(run, ref, sentinel=-9.0), flush=True)
+    print("[zipf16k bwd]", harness.check_backward(run, ref), flush=True)
+    tr.release(live)
+    P_own = tr.current(own)
+    assert P_own == own
+    run2 = harness.run_gpu(cfg, inp=run.inp, P_out=P_own)
+    assert tuple(run2.bufs["out"].shape) == (P_own, cfg.H)
+    np.testing.assert_array_equal(harness.bits_np(run2.bufs["out"])[:cfg.T], harness.bits_np(out)[:cfg.T])
+    for name in ("dx", "dw1", "dw2", "dwr"):
+        np.testing.assert_array_equal(harness.bits_np(run2.bufs[name]), harness.bits_np(run.bufs[name]), err_msg=name)
