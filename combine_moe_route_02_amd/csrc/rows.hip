@@ -1,7 +1,11 @@
 // Row-copy kernels of the layer share: dispatch, combine and their transposes, plus the
-// per-token part of the routing backward. All are HBM-bound: one wave owns one token, its
-// lanes cover the hidden dimension with 16-byte vectors (coalesced 1 KiB per wave access),
-// every index is 64-bit, and each token row is read once.
+// per-token part of the routing backward. All are HBM-bound, with 64-bit indexing throughout.
+//
+// Dispatch, combine and combine backward run one 256-thread block per token: thread i moves the
+// 16-byte vectors i, i + 256, ... of the token's row (one vector per thread at H = 2048 BF16), and
+// the token's slot rows and gates are broadcast from lanes 0..k-1 with v_readlane (scalar), so
+// every wave issues few memory instructions and many waves keep HBM busy. Dispatch backward and
+// the FP8 dispatch keep one wave per token (the FP8 quantiser needs the row's absmax in one wave).
 //
 // torchtitan PR 5541 ("AI-Generated Details") describes its BF16/FP8 row-copy kernels with
 // multi-row tiles, tail masks and 64-bit addressing; these kernels keep those properties for the
@@ -13,38 +17,31 @@
 
 namespace moe {
 
-constexpr int kTokPerBlock = 4;   // one wave per token
+constexpr int kTokPerBlock = 4;   // one wave per token (wave-per-token kernels)
 constexpr int kBatch = 4;         // 16-byte vectors per lane kept in flight
+constexpr int kBlockThreads = 256;  // block-per-token kernels
+
+// Broadcast lane j's value to the wave (scalar register).
+MOE_DEV int bcast_i(int v, int j) { return __builtin_amdgcn_readlane(v, j); }
+MOE_DEV float bcast_f(float v, int j) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j)); }
 
 // ---------------------------------------------------------------------------------------------
-// Dispatch (F32 / BF16): scatter x[t] to xd[row_of[t][j]] for every local slot; bitwise copy.
+// Dispatch (F32 / BF16): scatter x[t] to xd[row_of[t][j]] for every local slot; bitwise copy. A
+// token without a local expert is not read at all.
 template <int K>
-__global__ __launch_bounds__(256) void dispatch_copy_kernel(
+__global__ __launch_bounds__(kBlockThreads) void dispatch_copy_kernel(
     const u32x4* __restrict__ x, const int32_t* __restrict__ row_of, u32x4* __restrict__ xd,
     int64_t t0, int64_t t1, int64_t nvec) {
   const int lane = threadIdx.x & 63;
-  const int64_t t = t0 + (int64_t)blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
-  if (t >= t1) return;
+  const int64_t t = t0 + blockIdx.x;
   const int32_t myrow = lane < K ? row_of[t * K + lane] : -1;
-  if (__ballot(myrow >= 0) == 0) return;  // token has no local expert: not read at all
-  const u32x4* src = x + t * nvec;
-  for (int64_t v0 = 0; v0 < nvec; v0 += 64 * kBatch) {
-    u32x4 v[kBatch];
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      int64_t i = v0 + b * 64 + lane;
-      if (i < nvec) v[b] = src[i];
-    }
+  if (__ballot(myrow >= 0) == 0) return;
+  for (int64_t i = threadIdx.x; i < nvec; i += kBlockThreads) {
+    const u32x4 v = x[t * nvec + i];
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-      int32_t r = __shfl(myrow, j, 64);
-      if (r < 0) continue;
-      u32x4* dst = xd + (int64_t)r * nvec;
-#pragma unroll
-      for (int b = 0; b < kBatch; ++b) {
-        int64_t i = v0 + b * 64 + lane;
-        if (i < nvec) dst[i] = v[b];
-      }
+      const int32_t r = bcast_i(myrow, j);
+      if (r >= 0) xd[(int64_t)r * nvec + i] = v;
     }
   }
 }
@@ -184,98 +181,96 @@ template <> struct Vec<uint16_t> {
   }
 };
 
-// Combine: out[t] = RNE(sum_j g_tj * yd[row_of[t][j]]), FP32 accumulation, j ascending.
+// Combine: out[t] = RNE(sum_j g_tj * yd[row_of[t][j]]), FP32 accumulation, j ascending; a token
+// without a local expert gets a zero row.
 template <typename T, int K>
-__global__ __launch_bounds__(256) void combine_kernel(
+__global__ __launch_bounds__(kBlockThreads) void combine_kernel(
     const u32x4* __restrict__ yd, const float* __restrict__ gates, const int32_t* __restrict__ row_of,
     u32x4* __restrict__ out, int64_t t0, int64_t t1, int64_t nvec) {
   using V = Vec<T>;
   const int lane = threadIdx.x & 63;
-  const int64_t t = t0 + (int64_t)blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
-  if (t >= t1) return;
+  const int64_t t = t0 + blockIdx.x;
   const int32_t myrow = lane < K ? row_of[t * K + lane] : -1;
   const float mygate = lane < K ? gates[t * K + lane] : 0.f;
-  for (int64_t v0 = 0; v0 < nvec; v0 += 64 * kBatch) {
-    float acc[kBatch][V::N];
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b)
-#pragma unroll
-      for (int q = 0; q < V::N; ++q) acc[b][q] = 0.f;
+  for (int64_t i = threadIdx.x; i < nvec; i += kBlockThreads) {
+    u32x4 v[K];
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-      int32_t r = __shfl(myrow, j, 64);
-      if (r < 0) continue;
-      float g = __shfl(mygate, j, 64);
-      const u32x4* src = yd + (int64_t)r * nvec;
-#pragma unroll
-      for (int b = 0; b < kBatch; ++b) {
-        int64_t i = v0 + b * 64 + lane;
-        if (i < nvec) {
-          float f[V::N];
-          V::to_f(src[i], f);
-#pragma unroll
-          for (int q = 0; q < V::N; ++q) acc[b][q] = fmaf(g, f[q], acc[b][q]);
-        }
-      }
+      const int32_t r = bcast_i(myrow, j);
+      if (r >= 0) v[j] = yd[(int64_t)r * nvec + i];
     }
+    float acc[V::N];
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      int64_t i = v0 + b * 64 + lane;
-      if (i < nvec) out[t * nvec + i] = V::from_f(acc[b]);
+    for (int q = 0; q < V::N; ++q) acc[q] = 0.f;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      if (bcast_i(myrow, j) < 0) continue;
+      const float g = bcast_f(mygate, j);
+      float f[V::N];
+      V::to_f(v[j], f);
+#pragma unroll
+      for (int q = 0; q < V::N; ++q) acc[q] = fmaf(g, f[q], acc[q]);
     }
+    out[t * nvec + i] = V::from_f(acc);
   }
 }
 
-// Combine backward: dyd[row_of[t][j]] = g_tj * dy[t]; dgates[t][j] = <dy[t], yd[row]> (FP32).
+// Combine backward: dyd[row_of[t][j]] = g_tj * dy[t]; dgates[t][j] = <dy[t], yd[row]> (FP32): each
+// thread's partial over its vectors, a wave sum, then the four waves' sums in order (no atomics).
 template <typename T, int K>
-__global__ __launch_bounds__(256) void combine_bwd_kernel(
+__global__ __launch_bounds__(kBlockThreads) void combine_bwd_kernel(
     const u32x4* __restrict__ dy, const u32x4* __restrict__ yd, const float* __restrict__ gates,
     const int32_t* __restrict__ row_of, u32x4* __restrict__ dyd, float* __restrict__ dgates,
     int64_t t0, int64_t t1, int64_t nvec) {
   using V = Vec<T>;
-  const int lane = threadIdx.x & 63;
-  const int64_t t = t0 + (int64_t)blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
-  if (t >= t1) return;
+  constexpr int NW = kBlockThreads / 64;
+  __shared__ float part[NW][K];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t = t0 + blockIdx.x;
   const int32_t myrow = lane < K ? row_of[t * K + lane] : -1;
   const float mygate = lane < K ? gates[t * K + lane] : 0.f;
-  const bool any = __ballot(myrow >= 0) != 0;
+  const uint64_t local = __ballot(myrow >= 0);
   float dg[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) dg[j] = 0.f;
-  if (any) {
-    for (int64_t v0 = 0; v0 < nvec; v0 += 64 * kBatch) {
-      float d[kBatch][V::N];
+  if (local) {
+    for (int64_t i = threadIdx.x; i < nvec; i += kBlockThreads) {
+      float d[V::N];
+      V::to_f(dy[t * nvec + i], d);
+      u32x4 v[K];
 #pragma unroll
-      for (int b = 0; b < kBatch; ++b) {
-        int64_t i = v0 + b * 64 + lane;
-        if (i < nvec) V::to_f(dy[t * nvec + i], d[b]);
+      for (int j = 0; j < K; ++j) {
+        const int32_t r = bcast_i(myrow, j);
+        if (r >= 0) v[j] = yd[(int64_t)r * nvec + i];
       }
 #pragma unroll
       for (int j = 0; j < K; ++j) {
-        int32_t r = __shfl(myrow, j, 64);
+        const int32_t r = bcast_i(myrow, j);
         if (r < 0) continue;
-        float g = __shfl(mygate, j, 64);
-        const u32x4* src = yd + (int64_t)r * nvec;
-        u32x4* dst = dyd + (int64_t)r * nvec;
+        const float g = bcast_f(mygate, j);
+        float f[V::N], o[V::N];
+        V::to_f(v[j], f);
 #pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
-          int64_t i = v0 + b * 64 + lane;
-          if (i < nvec) {
-            float f[V::N], o[V::N];
-            V::to_f(src[i], f);
-#pragma unroll
-            for (int q = 0; q < V::N; ++q) { dg[j] = fmaf(d[b][q], f[q], dg[j]); o[q] = g * d[b][q]; }
-            dst[i] = V::from_f(o);
-          }
-        }
+        for (int q = 0; q < V::N; ++q) { dg[j] = fmaf(d[q], f[q], dg[j]); o[q] = g * d[q]; }
+        dyd[(int64_t)r * nvec + i] = V::from_f(o);
       }
     }
   }
 #pragma unroll
   for (int j = 0; j < K; ++j) {
-    float s = wave_sum(dg[j]);
-    int32_t r = __shfl(myrow, j, 64);
-    if (lane == 0) dgates[t * K + j] = (r >= 0) ? s : 0.f;
+    if (!((local >> j) & 1)) continue;
+    const float w = wave_sum(dg[j]);
+    if (lane == 0) part[wave][j] = w;
+  }
+  __syncthreads();
+  if (threadIdx.x < K) {
+    const int j = threadIdx.x;
+    float sum = 0.f;
+    if ((local >> j) & 1) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) sum += part[w][j];
+    }
+    dgates[t * K + j] = sum;
   }
 }
 
@@ -386,7 +381,7 @@ hipError_t launch_dispatch(const void* x, const int32_t* row_of, void* xd, int64
   if (t1 <= t0) return hipSuccess;
   {
     MOE_TRACE("dispatch", s);
-    MOE_SWITCH_K(K, hipLaunchKernelGGL(dispatch_copy_kernel<KK>, tok_grid(t1 - t0), dim3(256), 0, s,
+    MOE_SWITCH_K(K, hipLaunchKernelGGL(dispatch_copy_kernel<KK>, dim3((unsigned)(t1 - t0)), dim3(kBlockThreads), 0, s,
                                        (const u32x4*)x, row_of, (u32x4*)xd, t0, t1, row_bytes / 16));
   }
   return hipGetLastError();
@@ -432,13 +427,13 @@ hipError_t launch_combine(bool bf16, const void* yd, const float* gates, const i
   if (bf16)
     {
       MOE_TRACE("combine", s);
-      MOE_SWITCH_K(K, hipLaunchKernelGGL((combine_kernel<uint16_t, KK>), tok_grid(t1 - t0), dim3(256), 0, s,
+      MOE_SWITCH_K(K, hipLaunchKernelGGL((combine_kernel<uint16_t, KK>), dim3((unsigned)(t1 - t0)), dim3(kBlockThreads), 0, s,
                          (const u32x4*)yd, gates, row_of, (u32x4*)out, t0, t1, row_bytes / 16));
     }
   else
     {
       MOE_TRACE("combine", s);
-      MOE_SWITCH_K(K, hipLaunchKernelGGL((combine_kernel<float, KK>), tok_grid(t1 - t0), dim3(256), 0, s,
+      MOE_SWITCH_K(K, hipLaunchKernelGGL((combine_kernel<float, KK>), dim3((unsigned)(t1 - t0)), dim3(kBlockThreads), 0, s,
                          (const u32x4*)yd, gates, row_of, (u32x4*)out, t0, t1, row_bytes / 16));
     }
   return hipGetLastError();
@@ -451,14 +446,14 @@ hipError_t launch_combine_bwd(bool bf16, const void* dy, const void* yd, const f
   if (bf16)
     {
       MOE_TRACE("combine_bwd", s);
-      MOE_SWITCH_K(K, hipLaunchKernelGGL((combine_bwd_kernel<uint16_t, KK>), tok_grid(t1 - t0), dim3(256), 0, s,
+      MOE_SWITCH_K(K, hipLaunchKernelGGL((combine_bwd_kernel<uint16_t, KK>), dim3((unsigned)(t1 - t0)), dim3(kBlockThreads), 0, s,
                          (const u32x4*)dy, (const u32x4*)yd, gates, row_of, (u32x4*)dyd, dgates,
                          t0, t1, row_bytes / 16));
     }
   else
     {
       MOE_TRACE("combine_bwd", s);
-      MOE_SWITCH_K(K, hipLaunchKernelGGL((combine_bwd_kernel<float, KK>), tok_grid(t1 - t0), dim3(256), 0, s,
+      MOE_SWITCH_K(K, hipLaunchKernelGGL((combine_bwd_kernel<float, KK>), dim3((unsigned)(t1 - t0)), dim3(kBlockThreads), 0, s,
                          (const u32x4*)dy, (const u32x4*)yd, gates, row_of, (u32x4*)dyd, dgates,
                          t0, t1, row_bytes / 16));
     }
