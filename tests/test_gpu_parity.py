@@ -257,3 +257,56 @@ def test_full_imbalanced_routing_at_live_extent():
     np.testing.assert_array_equal(harness.bits_np(run2.bufs["out"])[:cfg.T], harness.bits_np(out)[:cfg.T])
     for name in ("dx", "dw1", "dw2", "dwr"):
         np.testing.assert_array_equal(harness.bits_np(run2.bufs[name]), harness.bits_np(run.bufs[name]), err_msg=name)
+
+
+# ----------------------------------------------------------------------------- edge cases
+
+EDGE = [
+    # an empty last chunk: ceil(5/4) = 2 tokens per chunk -> [0,2) [2,4) [4,5) [5,5)
+    MoeConfig("t5_n4", T=5, H=128, I=64, E=8, E_local=4, e0=2, k=2, n_chunks=4, dtype="bf16",
+              seed_base=110, backward=True),
+    # the widest router the ABI accepts, 64 local experts, top-8
+    MoeConfig("e1024", T=700, H=128, I=64, E=1024, E_local=64, e0=512, k=8, n_chunks=2, dtype="bf16",
+              seed_base=120, backward=True),
+    # top-1: every gate is 1
+    MoeConfig("k1", T=900, H=256, I=128, E=16, E_local=8, k=1, n_chunks=2, dtype="bf16", seed_base=130,
+              backward=True),
+    # H and I not powers of two (partial column tiles in every GEMM)
+    MoeConfig("h192", T=600, H=192, I=320, E=16, E_local=16, k=4, n_chunks=2, dtype="bf16", seed_base=140,
+              backward=True),
+]
+
+
+@pytest.mark.parametrize("cfg", EDGE, ids=[c.name for c in EDGE])
+def test_edge_shapes(cfg):
+    _require_gpu()
+    print(f"[parity] {cfg}", flush=True)
+    run = harness.run_gpu(cfg, sentinel=-11.0)
+    ref = harness.run_oracle(run)
+    harness.check_forward(run, ref, sentinel=-11.0)
+    harness.check_backward(run, ref)
+    if cfg.k == 1:
+        assert np.all(run.bufs["gates"].cpu().numpy() == 1.0)
+
+
+def test_zero_tokens_launches_nothing():
+    """T = 0: every stage call and layer primitive returns OK and writes nothing."""
+    _require_gpu()
+    import torch
+    import combine_moe_route_02_amd as mh
+    d = mh.make_desc(T=0, H=128, I=64, E=8, E_local=4, k=2, n_chunks=2, dtype="bf16")
+    b = mh.allocate(d, backward=True, fill=7)
+    for name, shape in (("x", (0, 128)), ("dy", (0, 128))):
+        b[name] = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    b["logits"] = torch.empty((0, 8), dtype=torch.float32, device="cuda")
+    b["w1"] = torch.zeros((4, 128, 128), dtype=torch.bfloat16, device="cuda")
+    b["w2"] = torch.zeros((4, 128, 64), dtype=torch.bfloat16, device="cuda")
+    b["w_r"] = torch.zeros((8, 128), dtype=torch.bfloat16, device="cuda")
+    b["out"] = torch.full((max(4, int(d.P_out)), 128), 5.0, dtype=torch.bfloat16, device="cuda")
+    s = torch.cuda.current_stream()
+    mh.moe_layer_forward_backward(d, b, s, torch.cuda.Stream())
+    torch.cuda.synchronize()
+    assert torch.all(b["out"] == 5.0)
+    assert torch.all(b["counts"] == 0) and torch.all(b["offsets"] == 0)
+    # weight gradients of an empty batch are zero
+    assert torch.all(b["dw1"] == 0) and torch.all(b["dw2"] == 0) and torch.all(b["dwr"] == 0)
