@@ -27,6 +27,7 @@ if ROOT not in sys.path:
 METRIC = "MoE layer tokens/s (fwd, fwd+bwd) @16K tok top-k8; %HBM BW, %MFMA peak"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense BF16 MFMA, TFLOP/s
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
 PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X vector FP32
 
 # launch-log name -> (source file under the package's csrc/, substring of the kernel symbol that
@@ -191,6 +192,56 @@ def cpu_baseline(cfg, inp, budget_s: float):
             "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
+def fp8_forward(args, cfg, inp, mh, torch, np):
+    """Forward-only FP8 rate at the same shapes: tokens/s and the FP8 GEMMs' TFLOP/s."""
+    d8 = mh.make_desc(T=cfg.T, H=cfg.H, I=cfg.I, E=cfg.E, E_local=cfg.E_local, k=cfg.k, n_chunks=cfg.n_chunks,
+                      dtype="fp8", e0=cfg.e0)
+    b8 = mh.allocate(d8, backward=False)
+    b8["x"] = torch.from_numpy(inp["x_bits"].view(np.int16)).cuda().view(torch.bfloat16)
+    b8["logits"] = torch.from_numpy(inp["logits"]).cuda()
+    w1 = torch.from_numpy(inp["w1_bits"].view(np.int16)).cuda().view(torch.bfloat16)
+    w2 = torch.from_numpy(inp["w2_bits"].view(np.int16)).cuda().view(torch.bfloat16)
+    b8["w1"] = torch.empty(w1.shape, dtype=torch.uint8, device="cuda")
+    b8["w2"] = torch.empty(w2.shape, dtype=torch.uint8, device="cuda")
+    b8["w1_scale"] = torch.empty(w1.shape[:-1], dtype=torch.float32, device="cuda")
+    b8["w2_scale"] = torch.empty(w2.shape[:-1], dtype=torch.float32, device="cuda")
+    mh.moe_quantize_rows_fp8(cfg.E_local * 2 * cfg.I, cfg.H, w1, b8["w1"], b8["w1_scale"])
+    mh.moe_quantize_rows_fp8(cfg.E_local * cfg.H, cfg.I, w2, b8["w2"], b8["w2_scale"])
+    del w1, w2
+    cs, aux = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(args.warmup):
+        mh.moe_layer_forward(d8, b8, cs, aux)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        mh.moe_layer_forward(d8, b8, cs, aux)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    mh.moe_trace_enable(True)
+    for _ in range(args.steps):
+        mh.moe_layer_forward(d8, b8, cs, aux)
+    torch.cuda.synchronize()
+    mh.moe_trace_disable()
+    per = {}
+    for name, _s, t in mh.moe_trace_entries():
+        p = per.setdefault(name, [0, 0.0])
+        p[0] += 1
+        p[1] += t
+    N = int(b8["offsets"].cpu().numpy()[:, cfg.E_local].sum())
+    flops = {"gemm_gateup_swiglu_fp8": 2.0 * N * cfg.H * 2 * cfg.I, "gemm_down_fp8": 2.0 * N * cfg.I * cfg.H}
+    out = {"tokens_per_s": round(cfg.T / (ms * 1e-3), 1), "ms": round(ms, 4), "peak_fp8_tflops": PEAK_FP8_TFLOPS,
+           "kernels": {}}
+    for name, (cnt, tot) in per.items():
+        e = {"avg_us": round(tot / cnt * 1e3, 3), "ms_per_step": round(tot / args.steps, 4)}
+        if name in flops:
+            r = flops[name] / (tot / args.steps * 1e-3) / 1e12
+            e.update(achieved_tflops=round(r, 2), frac_mfma=round(r / PEAK_FP8_TFLOPS, 4))
+        out["kernels"][name] = e
+    del b8
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -319,6 +370,10 @@ def main():
         p[0] += 1
         p[1] += ms
 
+    # FP8 payload path, forward only (the same shapes; weights quantised per output row outside the
+    # timed region): expert GEMMs on FP8 MFMA, dispatch quantises per token, combine in BF16
+    fp8 = fp8_forward(args, cfg, inp, mh, torch, np)
+
     counts = bufs["counts"].cpu().numpy()
     offsets = bufs["offsets"].cpu().numpy()
     row_of = bufs["row_of"].cpu().numpy()
@@ -383,6 +438,7 @@ def main():
         "gemm_tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 2) if gemm_ms > 0 else None,
         "roofline": roof, "kernels": kernels,
     }
+    line["fp8_fwd"] = fp8
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_budget)
     print(json.dumps(line), flush=True)
