@@ -20,17 +20,16 @@ struct alignas(16) u32x4 { uint32_t x, y, z, w; };
 
 MOE_DEV float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// FP32 -> BF16, round to nearest even (NaN stays NaN).
-MOE_DEV uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
+// FP32 -> BF16, round to nearest even (NaN stays NaN): gfx950's v_cvt_pk_bf16_f32, two values per
+// instruction.
 MOE_DEV uint32_t pack_bf2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  const bf16x2_t v = __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, v);
 }
+MOE_DEV uint16_t f2bf(float f) { return (uint16_t)(pack_bf2(f, 0.f) & 0xffffu); }
 
 // Element load/store helpers for payload types (float or uint16_t BF16 bits).
 template <typename T> MOE_DEV float ld_elem(const T* p);
@@ -40,7 +39,9 @@ template <typename T> MOE_DEV void st_elem(T* p, float v);
 template <> MOE_DEV void st_elem<float>(float* p, float v) { *p = v; }
 template <> MOE_DEV void st_elem<uint16_t>(uint16_t* p, float v) { *p = f2bf(v); }
 
-MOE_DEV float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
+// Logistic sigmoid with the hardware exponential and reciprocal (about 1 ulp each): the SwiGLU
+// epilogues evaluate it for every element of h, where an IEEE division would dominate the VALU time.
+MOE_DEV float sigmoidf_(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 MOE_DEV float wave_sum(float v) {
 #pragma unroll

@@ -258,6 +258,13 @@ MOE_DEV void unpack4(uint2 v, float* f) {
 MOE_DEV int out_row(int lane) { return lane & 31; }
 MOE_DEV int out_col(int g, int lane) { return 8 * g + 4 * (lane >> 5); }
 
+// Workgroup barrier for the LDS staging area only: every wave's LDS accesses are complete, but its
+// global stores may still be in flight (a __syncthreads fence would wait for them as well).
+MOE_DEV void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xf | (7 << 4) | (3 << 14));  // lgkmcnt(0), other counters untouched
+  __builtin_amdgcn_s_barrier();
+}
+
 // Output staging: a [BM, W] BF16 tile in LDS with a row pitch of W * 2 + 16 bytes (16-byte aligned
 // rows; the pad spreads the MFMA-layout writes of 32 rows over the banks).
 template <int W> constexpr int pitch() { return W * 2 + 16; }
@@ -448,12 +455,12 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(RowsArgs a) {
             *(uint2*)(sg + m * pitch<W>() + 2 * jl) = pack4(gv[0], gv[1], gv[2], gv[3]);
             *(uint2*)(su + m * pitch<W>() + 2 * jl) = pack4(uv[0], uv[1], uv[2], uv[3]);
           }
-      __syncthreads();
+      lds_barrier();
       if (a.C2) {
         store_staged<BM, W>(sg, a.C2 + r0 * 2 * (int64_t)a.I + n0, 2 * (int64_t)a.I, mvalid, nvalid, tid);
         store_staged<BM, W>(su, a.C2 + r0 * 2 * (int64_t)a.I + a.I + n0, 2 * (int64_t)a.I, mvalid, nvalid, tid);
       }
-      __syncthreads();
+      lds_barrier();
       // h = silu(G) * U from the FP32 accumulators
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
@@ -476,9 +483,9 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(RowsArgs a) {
             const int m = mrow + tm * 32;
             *(uint2*)(sg + m * pitch<W>() + 2 * jl) = pack4(hv[0], hv[1], hv[2], hv[3]);
           }
-      __syncthreads();
+      lds_barrier();
       store_staged<BM, W>(sg, a.C + r0 * a.ldc + n0, a.ldc, mvalid, nvalid, tid);
-      __syncthreads();
+      lds_barrier();
     } else if constexpr (MODE == kDownBwd) {
       // G and U of the tile's rows and columns, staged coalesced; dG and dU overwrite them in place
       constexpr int W = BN;
@@ -487,7 +494,7 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(RowsArgs a) {
       const int64_t I2 = 2 * (int64_t)a.I;
       load_staged<BM, W>(sg, a.aux + r0 * I2 + n0, I2, mvalid, nvalid, tid);
       load_staged<BM, W>(su, a.aux + r0 * I2 + a.I + n0, I2, mvalid, nvalid, tid);
-      __syncthreads();
+      lds_barrier();
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
@@ -511,10 +518,10 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(RowsArgs a) {
             *(uint2*)pg = pack4(dg[0], dg[1], dg[2], dg[3]);
             *(uint2*)pu = pack4(du[0], du[1], du[2], du[3]);
           }
-      __syncthreads();
+      lds_barrier();
       store_staged<BM, W>(sg, a.C + r0 * I2 + n0, I2, mvalid, nvalid, tid);
       store_staged<BM, W>(su, a.C + r0 * I2 + a.I + n0, I2, mvalid, nvalid, tid);
-      __syncthreads();
+      lds_barrier();
     } else {
       constexpr int W = BN;
       float sr[TM];
@@ -535,9 +542,9 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(RowsArgs a) {
             }
             *(uint2*)(ring + (mrow + tm * 32) * pitch<W>() + 2 * nl) = pack4(v[0], v[1], v[2], v[3]);
           }
-      __syncthreads();
+      lds_barrier();
       store_staged<BM, W>(ring, a.C + r0 * a.ldc + n0, a.ldc, mvalid, nvalid, tid);
-      __syncthreads();
+      lds_barrier();
     }
   }
 }
@@ -614,10 +621,10 @@ __global__ __launch_bounds__(kThreads) void wgrad_kernel(WgradArgs a) {
           *(uint2*)(ring + (mrow + tm * 32) * pitch<BN>() + 2 * nl) =
               pack4(v[4 * gq], v[4 * gq + 1], v[4 * gq + 2], v[4 * gq + 3]);
         }
-    __syncthreads();
+    lds_barrier();
     store_staged<BM, BN>(ring, a.C + (int64_t)grp * a.strideC + (int64_t)m0 * a.N + n0, a.N,
                          min(BM, a.M - m0), min(BN, a.N - n0), tid);
-    __syncthreads();
+    lds_barrier();
   }
 }
 
