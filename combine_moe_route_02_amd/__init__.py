@@ -82,6 +82,7 @@ _SIGS = {
     "moe_trace_disable": [],
     "moe_trace_count": [],
     "moe_trace_entry": [c_int64, POINTER(c_char_p), POINTER(c_void_p), POINTER(ctypes.c_float)],
+    "moe_trace_span": [c_int64, POINTER(ctypes.c_float), POINTER(ctypes.c_float)],
     "moe_last_error": [],
     "moe_abi_version": [],
 }
@@ -279,6 +280,17 @@ def moe_trace_entries():
         _check(L.moe_trace_entry(i, ctypes.byref(name), ctypes.byref(stream), ctypes.byref(ms)),
                "moe_trace_entry")
         out.append((name.value.decode(), stream.value or 0, ms.value))
+    return out
+
+
+def moe_trace_timeline():
+    """Timed launch log as (kernel name, stream handle, start ms, end ms), times after entry 0."""
+    L = lib()
+    out = []
+    for i, (name, stream, _ms) in enumerate(moe_trace_entries()):
+        t0, t1 = ctypes.c_float(), ctypes.c_float()
+        _check(L.moe_trace_span(i, ctypes.byref(t0), ctypes.byref(t1)), "moe_trace_span")
+        out.append((name, stream, t0.value, t1.value))
     return out
 
 

@@ -116,7 +116,7 @@ moe_status events(int count, hipEvent_t** out) {
   EventPool& p = g_pools[dev];
   while ((int)p.ev.size() < count) {
     hipEvent_t e;
-    MOE_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming), "hipEventCreateWithFlags");
+    MOE_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming | hipEventDisableSystemFence), "hipEventCreateWithFlags");
     p.ev.push_back(e);
   }
   *out = p.ev.data();
@@ -376,82 +376,103 @@ static moe_status check_bwd_tensors(const moe_desc* d, const moe_tensors* t) {
   return MOE_OK;
 }
 
-// Forward schedule. aux: R0 D0 | R1 D1 C0 | R2 D2 C1 | ... ; compute: F0 | F1 | ...
-// (routing+dispatch of chunk c+1 overlap the expert GEMMs of chunk c; combine c after F c).
-static moe_status forward_sched(const moe_desc* d, const moe_tensors* t, hipStream_t cs, hipStream_t as) {
+// Two-stream schedules. A wait of one stream on the other's event costs the waiting stream
+// about as much as a kernel launch even when the event has already completed, so the compute
+// stream waits only where it needs work of the auxiliary stream, and the work that nothing can
+// overlap (the first chunk's routing and dispatch, the last chunk's combine, the first chunk's
+// combine backward) runs on the compute stream itself. With one stream (cs == as) the issue order
+// alone is a valid sequential order.
+//
+// Forward, n chunks:
+//   compute: R0 D0 F0 | wait(disp1) F1 | ... | wait(disp n-1) F n-1, C n-1
+//   aux:     wait(disp0) R1 D1 | wait(ffn0) C0, R2 D2 | wait(ffn1) C1, R3 D3 | ...
+// Routing/dispatch of chunk c+1 overlaps the expert GEMMs of chunk c; combine c-1 overlaps F c.
+// With `join` the compute stream finally waits for the auxiliary stream.
+static moe_status forward_sched(const moe_desc* d, const moe_tensors* t, hipStream_t cs, hipStream_t as,
+                                bool join) {
   const int n = d->n_chunks;
-  const bool two = cs != as;
+  const bool two = cs != as && n > 1;
   hipEvent_t* ev = nullptr;
-  MOE_TRY(events(2 * n + 2, &ev));
-  hipEvent_t ev_start = ev[0], ev_done = ev[1];
-  hipEvent_t* ev_disp = ev + 2;
-  hipEvent_t* ev_ffn = ev + 2 + n;
+  MOE_TRY(events(2 * n + 1, &ev));
+  hipEvent_t* disp = ev;       // n events: dispatch of chunk c done
+  hipEvent_t* ffn = ev + n;    // n events: expert FFN of chunk c done
+  hipEvent_t done = ev[2 * n];
+  MOE_TRY(moe_route(d, 0, t->logits, t->topk_idx, t->gates, t->counts, t->offsets, t->row_of, t->src_token,
+                    t->workspace, cs));
+  MOE_TRY(moe_dispatch(d, 0, t->x, t->row_of, t->xd, t->xd_scale, t->h_scale, cs));
   if (two) {
-    MOE_HIP(hipEventRecord(ev_start, cs), "hipEventRecord");
-    MOE_HIP(hipStreamWaitEvent(as, ev_start, 0), "hipStreamWaitEvent");
+    MOE_HIP(hipEventRecord(disp[0], cs), "hipEventRecord");
+    MOE_HIP(hipStreamWaitEvent(as, disp[0], 0), "hipStreamWaitEvent");
   }
   for (int c = 0; c < n; ++c) {
-    MOE_TRY(moe_route(d, c, t->logits, t->topk_idx, t->gates, t->counts, t->offsets, t->row_of, t->src_token,
-                      t->workspace, as));
-    MOE_TRY(moe_dispatch(d, c, t->x, t->row_of, t->xd, t->xd_scale, t->h_scale, as));
-    if (two) {
-      MOE_HIP(hipEventRecord(ev_disp[c], as), "hipEventRecord");
-      MOE_HIP(hipStreamWaitEvent(cs, ev_disp[c], 0), "hipStreamWaitEvent");
+    const hipStream_t side = two ? as : cs;
+    if (c + 1 < n) {
+      MOE_TRY(moe_route(d, c + 1, t->logits, t->topk_idx, t->gates, t->counts, t->offsets, t->row_of,
+                        t->src_token, t->workspace, side));
+      MOE_TRY(moe_dispatch(d, c + 1, t->x, t->row_of, t->xd, t->xd_scale, t->h_scale, side));
+      if (two) MOE_HIP(hipEventRecord(disp[c + 1], as), "hipEventRecord");
     }
+    if (two && c >= 1) MOE_HIP(hipStreamWaitEvent(cs, disp[c], 0), "hipStreamWaitEvent");
     MOE_TRY(moe_expert_ffn(d, c, t->xd, t->xd_scale, t->w1, t->w1_scale, t->w2, t->w2_scale, t->offsets,
                            t->gu, t->h, t->h_scale, t->yd, cs));
-    if (two) MOE_HIP(hipEventRecord(ev_ffn[c], cs), "hipEventRecord");
-    if (c >= 1) {
-      if (two) MOE_HIP(hipStreamWaitEvent(as, ev_ffn[c - 1], 0), "hipStreamWaitEvent");
-      MOE_TRY(moe_combine(d, c - 1, t->yd, t->gates, t->row_of, t->out, as));
+    if (c + 1 < n) {
+      if (two) {
+        MOE_HIP(hipEventRecord(ffn[c], cs), "hipEventRecord");
+        MOE_HIP(hipStreamWaitEvent(as, ffn[c], 0), "hipStreamWaitEvent");
+      }
+      MOE_TRY(moe_combine(d, c, t->yd, t->gates, t->row_of, t->out, side));
+    } else {
+      MOE_TRY(moe_combine(d, c, t->yd, t->gates, t->row_of, t->out, cs));
     }
   }
-  if (two) MOE_HIP(hipStreamWaitEvent(as, ev_ffn[n - 1], 0), "hipStreamWaitEvent");
-  MOE_TRY(moe_combine(d, n - 1, t->yd, t->gates, t->row_of, t->out, as));
-  if (two) {
-    MOE_HIP(hipEventRecord(ev_done, as), "hipEventRecord");
-    MOE_HIP(hipStreamWaitEvent(cs, ev_done, 0), "hipStreamWaitEvent");
+  if (two && join) {
+    MOE_HIP(hipEventRecord(done, as), "hipEventRecord");
+    MOE_HIP(hipStreamWaitEvent(cs, done, 0), "hipStreamWaitEvent");
   }
   return MOE_OK;
 }
 
-// Backward schedule. aux: CB0 RB0 | CB1 RB1 DB0 | ... ; compute: DG0 | DG1 | ... | wgrad.
-// Every chunk's input-gradient work is issued before the expert weight gradients.
+// Backward, n chunks (CB combine backward, RB route backward, DG expert dgrad, DB dispatch
+// backward, W expert weight gradients):
+//   compute: CB0 DG0 | wait(cb1) DG1 | ... | DG n-1, W, wait(done)
+//   aux:     wait(cb0) CB1 RB0 wait(dg0) DB0 | CB2 RB1 wait(dg1) DB1 | ... | RB n-1 wait(dg n-1) DB n-1
+// Route backward of chunk c runs in chunk order (the FP32 router-gradient sum is ordered), and
+// every chunk's input-gradient work is issued before the weight-gradient GEMMs.
 static moe_status backward_sched(const moe_desc* d, const moe_tensors* t, hipStream_t cs, hipStream_t as) {
   const int n = d->n_chunks;
   const bool two = cs != as;
+  const hipStream_t side = two ? as : cs;
   hipEvent_t* ev = nullptr;
-  MOE_TRY(events(4 * n + 4, &ev));
-  // events [2n+2, 4n+4): distinct from the forward schedule's [0, 2n+2)
-  hipEvent_t ev_start = ev[2 * n + 2], ev_done = ev[2 * n + 3];
-  hipEvent_t* cb = ev + 2 * n + 4;  // n events: combine/route backward of chunk c done
-  hipEvent_t* dg = ev + 3 * n + 4;  // n events: expert dgrad of chunk c done
+  MOE_TRY(events(4 * n + 2, &ev));
+  // events [2n+1, 4n+2): distinct from the forward schedule's [0, 2n+1)
+  hipEvent_t* cb = ev + 2 * n + 1;  // n events: combine backward of chunk c done
+  hipEvent_t* dg = ev + 3 * n + 1;  // n events: expert dgrad of chunk c done
+  hipEvent_t done = ev[4 * n + 1];
+  MOE_TRY(moe_combine_bwd(d, 0, t->dy, t->yd, t->gates, t->row_of, t->dyd, t->dgates, cs));
   if (two) {
-    MOE_HIP(hipEventRecord(ev_start, cs), "hipEventRecord");
-    MOE_HIP(hipStreamWaitEvent(as, ev_start, 0), "hipStreamWaitEvent");
+    MOE_HIP(hipEventRecord(cb[0], cs), "hipEventRecord");
+    MOE_HIP(hipStreamWaitEvent(as, cb[0], 0), "hipStreamWaitEvent");
   }
   for (int c = 0; c < n; ++c) {
-    MOE_TRY(moe_combine_bwd(d, c, t->dy, t->yd, t->gates, t->row_of, t->dyd, t->dgates, as));
-    MOE_TRY(moe_route_bwd(d, c, t->dgates, t->gates, t->topk_idx, t->x, t->dlogits, t->dwr_acc, t->dwr,
-                          t->workspace, as));
-    if (two) {
-      MOE_HIP(hipEventRecord(cb[c], as), "hipEventRecord");
-      MOE_HIP(hipStreamWaitEvent(cs, cb[c], 0), "hipStreamWaitEvent");
+    if (c + 1 < n) {
+      MOE_TRY(moe_combine_bwd(d, c + 1, t->dy, t->yd, t->gates, t->row_of, t->dyd, t->dgates, side));
+      if (two) MOE_HIP(hipEventRecord(cb[c + 1], as), "hipEventRecord");
     }
+    MOE_TRY(moe_route_bwd(d, c, t->dgates, t->gates, t->topk_idx, t->x, t->dlogits, t->dwr_acc, t->dwr,
+                          t->workspace, side));
+    if (two && c >= 1) MOE_HIP(hipStreamWaitEvent(cs, cb[c], 0), "hipStreamWaitEvent");
     MOE_TRY(moe_expert_ffn_bwd(d, c, t->dyd, t->xd, t->gu, t->h, t->w1, t->w2, t->offsets, t->dgu, t->dxd,
                                nullptr, nullptr, cs));
-    if (two) MOE_HIP(hipEventRecord(dg[c], cs), "hipEventRecord");
-    if (c >= 1) {
-      if (two) MOE_HIP(hipStreamWaitEvent(as, dg[c - 1], 0), "hipStreamWaitEvent");
-      MOE_TRY(moe_dispatch_bwd(d, c - 1, t->dxd, t->row_of, t->topk_idx, t->dlogits, t->w_r, t->dx, as));
+    if (two) {
+      MOE_HIP(hipEventRecord(dg[c], cs), "hipEventRecord");
+      MOE_HIP(hipStreamWaitEvent(as, dg[c], 0), "hipStreamWaitEvent");
     }
+    MOE_TRY(moe_dispatch_bwd(d, c, t->dxd, t->row_of, t->topk_idx, t->dlogits, t->w_r, t->dx, side));
   }
-  if (two) MOE_HIP(hipStreamWaitEvent(as, dg[n - 1], 0), "hipStreamWaitEvent");
-  MOE_TRY(moe_dispatch_bwd(d, n - 1, t->dxd, t->row_of, t->topk_idx, t->dlogits, t->w_r, t->dx, as));
   MOE_TRY(moe_expert_wgrad(d, t->dyd, t->dgu, t->xd, t->h, t->offsets, t->dw1, t->dw2, cs));
   if (two) {
-    MOE_HIP(hipEventRecord(ev_done, as), "hipEventRecord");
-    MOE_HIP(hipStreamWaitEvent(cs, ev_done, 0), "hipStreamWaitEvent");
+    MOE_HIP(hipEventRecord(done, as), "hipEventRecord");
+    MOE_HIP(hipStreamWaitEvent(cs, done, 0), "hipStreamWaitEvent");
   }
   return MOE_OK;
 }
@@ -459,7 +480,7 @@ static moe_status backward_sched(const moe_desc* d, const moe_tensors* t, hipStr
 moe_status moe_layer_forward(const moe_desc* d, const moe_tensors* t, void* compute_stream, void* aux_stream) {
   MOE_TRY(validate(d));
   MOE_TRY(check_fwd_tensors(d, t));
-  return forward_sched(d, t, (hipStream_t)compute_stream, (hipStream_t)aux_stream);
+  return forward_sched(d, t, (hipStream_t)compute_stream, (hipStream_t)aux_stream, true);
 }
 
 moe_status moe_layer_backward(const moe_desc* d, const moe_tensors* t, void* compute_stream, void* aux_stream) {
@@ -474,7 +495,9 @@ moe_status moe_layer_forward_backward(const moe_desc* d, const moe_tensors* t, v
   MOE_TRY(validate(d));
   MOE_TRY(check_fwd_tensors(d, t));
   MOE_TRY(check_bwd_tensors(d, t));
-  MOE_TRY(forward_sched(d, t, (hipStream_t)compute_stream, (hipStream_t)aux_stream));
+  // no join between the two: the backward's first wait of the auxiliary stream follows the
+  // whole forward on the compute stream, and its final join covers the forward's aux work
+  MOE_TRY(forward_sched(d, t, (hipStream_t)compute_stream, (hipStream_t)aux_stream, false));
   return backward_sched(d, t, (hipStream_t)compute_stream, (hipStream_t)aux_stream);
 }
 

@@ -8,14 +8,15 @@
 // each chunk: within an expert, rows follow ascending token index.
 //
 // Two launches per chunk range, both deterministic:
-//   route_topk   16 lanes per token (4 tokens per wave, 64 tokens per 1024-thread block). Each
+//   route_topk   16 lanes per token (4 tokens per wave, 16 tokens per 256-thread block). Each
 //                lane keeps a sorted top-K list of its share of the experts as 64-bit keys
 //                (order-preserving logit bits above the complemented expert index, so ties go to
-//                the lower index), then K rounds of a 16-lane max merge the lists. A per-block
-//                histogram over all E experts is summed in LDS with integer atomics (the sum
+//                the lower index), then K rounds of a 16-lane max merge the lists. A histogram
+//                over all E experts per 16 tokens is summed in LDS with integer atomics (the sum
 //                does not depend on their order).
-//   route_layout per block: rows that earlier blocks of the chunk give each local expert (one
-//                wave per expert, lanes over blocks), local offsets, then each token's rank among
+//   route_layout per 64-token block: rows that earlier tokens of the chunk give each local expert
+//                (one wave per expert, lanes over the 16-token histograms), local offsets, then
+//                each token's rank among
 //                the block's earlier tokens choosing the same expert from a 64-bit ballot mask
 //                (popcount below the lane); one wave per top-k slot.
 #include "common.h"
@@ -24,9 +25,12 @@
 
 namespace moe {
 
-constexpr int kRouteBlock = 64;     // tokens per block (one histogram per block)
-constexpr int kRouteThreads = 1024; // 16 waves
+constexpr int kRouteBlock = 64;     // tokens per route_layout block (one ballot wave)
+constexpr int kRouteThreads = 1024; // route_layout: 16 waves
 constexpr int kGroup = 16;          // lanes per token in route_topk
+constexpr int kTopkThreads = 256;   // route_topk block
+constexpr int kHistTok = kTopkThreads / kGroup;  // tokens per histogram (16)
+constexpr int kSub = kRouteBlock / kHistTok;     // histograms per route_layout block (4)
 
 // Order-preserving map of a logit to 32 bits: larger logit -> larger key; NaN ranks as -inf and
 // -0 equals +0.
@@ -63,7 +67,7 @@ MOE_DEV uint64_t shfl_xor_u64(uint64_t v, int o) {
 }
 
 template <int K>
-__global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
+__global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
     const float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ gates,
     int32_t* __restrict__ block_hist, int64_t T, int E, int n, int chunk0, int nbpc) {
   extern __shared__ int hist[];  // [E]
@@ -71,10 +75,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
   const int c = chunk0 + blockIdx.x / nbpc;
   const int bl = blockIdx.x % nbpc;
   const ChunkRange cr = chunk_range(T, n, c);
-  for (int e = tid; e < E; e += kRouteThreads) hist[e] = 0;
+  for (int e = tid; e < E; e += kTopkThreads) hist[e] = 0;
   __syncthreads();
   const int q = tid & (kGroup - 1);                 // lane within the token's group
-  const int64_t t = cr.t0 + (int64_t)bl * kRouteBlock + (tid / kGroup);
+  const int64_t t = cr.t0 + (int64_t)bl * kHistTok + (tid / kGroup);
   const bool valid = t < cr.t1;
 
   uint64_t l[K];
@@ -130,8 +134,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
     atomicAdd(&hist[myid], 1);
   }
   __syncthreads();
-  int32_t* out = block_hist + ((int64_t)c * nbpc + bl) * E;
-  for (int e = tid; e < E; e += kRouteThreads) out[e] = hist[e];
+  // expert-major: the counts of expert e over the chunk's histograms are contiguous
+  int32_t* out = block_hist + (int64_t)c * E * nbpc + bl;
+  for (int e = tid; e < E; e += kTopkThreads) out[(int64_t)e * nbpc] = hist[e];
 }
 
 __global__ __launch_bounds__(kRouteThreads) void route_layout_kernel(
@@ -150,15 +155,22 @@ __global__ __launch_bounds__(kRouteThreads) void route_layout_kernel(
   const int c = chunk0 + blockIdx.x / nbpc;
   const int bl = blockIdx.x % nbpc;
   const ChunkRange cr = chunk_range(T, n, c);
-  const int32_t* bh = block_hist + (int64_t)c * nbpc * E;
+  const int nh = nbpc * kSub;  // 16-token histograms of the chunk
+  const int32_t* bh = block_hist + (int64_t)c * E * nh;  // [E][nh]
 
-  // one wave per local expert: rows owned by earlier blocks of this chunk, and the chunk total
+  // one wave per local expert: rows owned by earlier tokens of this chunk, and the chunk total
   for (int el = wave; el < El; el += kWaves) {
     int before = 0, total = 0;
-    for (int b = lane; b < nbpc; b += 64) {
-      const int h = bh[(int64_t)b * E + e0 + el];
-      before += (b < bl) ? h : 0;
-      total += h;
+    const int32_t* he = bh + (int64_t)(e0 + el) * nh;
+    for (int b0 = 0; b0 < nh; b0 += 256) {  // four loads in flight per lane
+      int h[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) h[u] = (b0 + 64 * u + lane < nh) ? he[b0 + 64 * u + lane] : 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        before += (b0 + 64 * u + lane < bl * kSub) ? h[u] : 0;
+        total += h[u];
+      }
     }
     before = wave_sum_int(before);
     total = wave_sum_int(total);
@@ -173,15 +185,23 @@ __global__ __launch_bounds__(kRouteThreads) void route_layout_kernel(
   }
   __syncthreads();
   const int N_c = off[El];
-  if (bl == 0) {
-    for (int e = tid; e < E; e += kRouteThreads) {
-      int total = 0;
-#pragma unroll 16
-      for (int b = 0; b < nbpc; ++b) total += bh[(int64_t)b * E + e];
-      counts[(int64_t)c * E + e] = total;
+  // per-expert counts over all E experts, spread over the chunk's blocks, one wave per expert
+  // (integer sums: the order does not matter)
+  for (int e = bl + nbpc * wave; e < E; e += nbpc * kWaves) {
+    const int32_t* he = bh + (int64_t)e * nh;
+    int total = 0;
+    for (int b0 = 0; b0 < nh; b0 += 256) {
+      int h[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) h[u] = (b0 + 64 * u + lane < nh) ? he[b0 + 64 * u + lane] : 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) total += h[u];
     }
-    for (int el = tid; el <= El; el += kRouteThreads) offsets[(int64_t)c * (El + 1) + el] = off[el];
+    total = wave_sum_int(total);
+    if (lane == 0) counts[(int64_t)c * E + e] = total;
   }
+  if (bl == 0)
+    for (int el = tid; el <= El; el += kRouteThreads) offsets[(int64_t)c * (El + 1) + el] = off[el];
 
   // wave j < K owns slot j of the block's 64 tokens (lane = token)
   const int64_t t = cr.t0 + (int64_t)bl * kRouteBlock + lane;
@@ -217,7 +237,7 @@ int route_blocks_per_chunk(int64_t T, int n) {
 }
 
 int64_t route_scratch_bytes(int64_t T, int n, int E) {
-  return (int64_t)n * route_blocks_per_chunk(T, n) * E * (int64_t)sizeof(int32_t);
+  return (int64_t)n * route_blocks_per_chunk(T, n) * kSub * E * (int64_t)sizeof(int32_t);
 }
 
 hipError_t launch_route(const float* logits, int32_t* topk_idx, float* gates, int32_t* counts,
@@ -226,13 +246,14 @@ hipError_t launch_route(const float* logits, int32_t* topk_idx, float* gates, in
                         int64_t P_c, hipStream_t s) {
   const int nbpc = route_blocks_per_chunk(T, n);
   dim3 grid(nbpc * nchunks), block(kRouteThreads);
+  dim3 grid1(nbpc * kSub * nchunks), block1(kTopkThreads);
   size_t sm1 = (size_t)E * sizeof(int);
   switch (K) {
 #define MOE_ROUTE_K(KK)                                                                      \
   case KK: {                                                                                 \
     MOE_TRACE("route_topk", s);                                                              \
-    hipLaunchKernelGGL(route_topk_kernel<KK>, grid, block, sm1, s, logits, topk_idx, gates, \
-                       scratch, T, E, n, chunk0, nbpc);                                      \
+    hipLaunchKernelGGL(route_topk_kernel<KK>, grid1, block1, sm1, s, logits, topk_idx, gates, \
+                       scratch, T, E, n, chunk0, nbpc * kSub);                               \
     break;                                                                                   \
   }
     MOE_ROUTE_K(1) MOE_ROUTE_K(2) MOE_ROUTE_K(3) MOE_ROUTE_K(4)

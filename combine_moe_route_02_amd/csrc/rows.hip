@@ -275,7 +275,8 @@ __global__ __launch_bounds__(kBlockThreads) void combine_bwd_kernel(
 }
 
 // Route backward, per token: dlogits[t][e] = g_j (dg_j - sum_i g_i dg_i) where e = idx[t][j],
-// zero for every other expert (the full row of E columns is written).
+// zero for every other expert (the full row of E columns is written): the row is cleared with
+// coalesced stores, then lanes 0..K-1 store their slot's value (same wave, program order).
 __global__ __launch_bounds__(256) void route_bwd_dlogits_kernel(
     const float* __restrict__ dgates, const float* __restrict__ gates, const int32_t* __restrict__ idx,
     float* __restrict__ dlogits, int64_t t0, int64_t t1, int K, int E) {
@@ -286,17 +287,11 @@ __global__ __launch_bounds__(256) void route_bwd_dlogits_kernel(
   const float d = lane < K ? dgates[t * K + lane] : 0.f;
   const int id = lane < K ? idx[t * K + lane] : -1;
   float s = 0.f;  // sum_i g_i dg_i, slots in ascending order
-  for (int j = 0; j < K; ++j) s = fmaf(__shfl(g, j, 64), __shfl(d, j, 64), s);
-  const float dl = g * (d - s);
-  for (int e = lane; e < E; e += 64) {
-    float v = 0.f;
-    for (int j = 0; j < K; ++j) {
-      int ej = __shfl(id, j, 64);
-      float dj = __shfl(dl, j, 64);
-      v = (ej == e) ? dj : v;
-    }
-    dlogits[t * E + e] = v;
-  }
+  for (int j = 0; j < K; ++j)
+    s = fmaf(bcast_f(g, j), bcast_f(d, j), s);
+  float* row = dlogits + t * (int64_t)E;
+  for (int e = lane; e < E; e += 64) row[e] = 0.f;
+  if (lane < K) row[id] = g * (d - s);
 }
 
 // Dispatch backward: dx[t] = RNE(sum_j local dxd[row_of[t][j]] + sum_j dlogits[t][e_j] W_r[e_j]).

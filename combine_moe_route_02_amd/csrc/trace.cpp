@@ -31,7 +31,7 @@ thread_local State g;
 int take_event() {
   if (g.used == g.pool.size()) {
     hipEvent_t e;
-    hipError_t r = hipEventCreate(&e);
+    hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableSystemFence);  // timing only
     if (r != hipSuccess) { g.err = r; return -1; }
     g.pool.push_back(e);
   }
@@ -104,6 +104,18 @@ moe_status moe_trace_entry(int64_t i, const char** name, void** stream, float* m
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   return g.err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_trace_span(int64_t i, float* start_ms, float* end_ms) {
+  if (i < 0 || i >= (int64_t)g.recs.size() || !start_ms || !end_ms) return MOE_ERR_ARG;
+  const auto& r0 = g.recs[0];
+  const auto& r = g.recs[(size_t)i];
+  if (r0.ev0 < 0 || r.ev0 < 0 || r.ev1 < 0) return MOE_ERR_HIP;
+  hipError_t e = hipEventSynchronize(g.pool[r.ev1]);
+  if (e == hipSuccess) e = hipEventSynchronize(g.pool[r0.ev0]);
+  if (e == hipSuccess) e = hipEventElapsedTime(start_ms, g.pool[r0.ev0], g.pool[r.ev0]);
+  if (e == hipSuccess) e = hipEventElapsedTime(end_ms, g.pool[r0.ev0], g.pool[r.ev1]);
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 }  // extern "C"

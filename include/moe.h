@@ -241,6 +241,10 @@ moe_status moe_trace_enable(int32_t timing);
 moe_status moe_trace_disable(void);
 int64_t moe_trace_count(void);
 moe_status moe_trace_entry(int64_t i, const char** name, void** stream, float* ms);
+/* Timeline of a timed log: start and end of entry i in ms after the start of entry 0 (both
+ * events are waited for). MOE_ERR_ARG for a bad index or NULL outputs, MOE_ERR_HIP without
+ * timing. Entries on different streams give the overlap of their kernels. */
+moe_status moe_trace_span(int64_t i, float* start_ms, float* end_ms);
 
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* moe_last_error(void);

@@ -148,8 +148,8 @@ def test_full_fused_16k_forward_backward():
 
 def test_backward_launch_order_input_grad_before_wgrad():
     """Every chunk's input-gradient work (combine backward, expert dgrad, dispatch backward) is
-    issued before the expert weight-gradient GEMMs, and chunk c+1's routing/dispatch is issued on
-    the auxiliary stream before chunk c's combine."""
+    issued before the expert weight-gradient GEMMs, chunk c+1's routing/dispatch is issued before
+    chunk c's combine, and each kernel runs on the stream the two-stream schedule gives it."""
     _require_gpu()
     import combine_moe_route_02_amd as mh
     cfg = SMALL[3]
@@ -167,9 +167,20 @@ def test_backward_launch_order_input_grad_before_wgrad():
         assert max(idx) < first_wgrad, kind
     # forward overlap order: route of chunk 1 precedes combine of chunk 0
     assert names.index("route_topk", names.index("route_topk") + 1) < names.index("combine")
-    streams = {n: s for n, s, _ in log}
-    assert streams["dispatch"] == streams["combine"] != streams["gemm_gateup_swiglu"]
-    assert streams["gemm_wgrad_gateup"] == streams["gemm_gateup_swiglu"]
+    # stream placement: the first chunk's routing/dispatch and the last chunk's combine (nothing
+    # to overlap them with) run on the compute stream; later chunks' routing/dispatch and the
+    # earlier chunks' combines run on the auxiliary stream
+    def streams_of(kind):
+        return [s for n, s, _ in log if n == kind]
+    compute = streams_of("gemm_gateup_swiglu")[0]
+    assert set(streams_of("gemm_gateup_swiglu") + streams_of("gemm_wgrad_gateup")) == {compute}
+    disp, comb = streams_of("dispatch"), streams_of("combine")
+    assert disp[0] == compute and comb[-1] == compute
+    aux = disp[1]
+    assert aux != compute and set(disp[1:]) == {aux} and set(comb[:-1]) == {aux}
+    cbw, dbw = streams_of("combine_bwd"), streams_of("dispatch_bwd")
+    assert cbw[0] == compute and set(cbw[1:]) == {aux} and set(dbw) == {aux}
+    assert set(streams_of("route_bwd_dlogits")) == {aux}
 
 
 # ----------------------------------------------------------------------------- FP8 payload path
