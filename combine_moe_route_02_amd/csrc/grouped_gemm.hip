@@ -207,16 +207,22 @@ MOE_DEV void stage_mma(const char* sa, const char* sb, int arow0, int brow0, int
           acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk][tn], fa[kk][tm], acc[tm][tn], 0, 0, 0);
     constexpr int RD = ((AKS ? 2 : 1) * TMA + (BKS ? 2 : 1) * TN);  // LDS reads per k16 step
     constexpr int MF = TMA * TN;                                     // MFMAs per k16 step
+    // With a K-slow weight operand (input gradients, weight gradients) the loads go out first,
+    // right after the stage barrier (measured faster there); otherwise they follow the first
+    // MFMAs.
+    if constexpr (BKS) __builtin_amdgcn_sched_group_barrier(0x020, VM, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
 #pragma unroll
     for (int i = 0; i < RD; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    if constexpr (!BKS) {
 #pragma unroll
-    for (int i = 0; i < VM; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      for (int i = 0; i < VM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2 * MF, 0);
   }
@@ -334,6 +340,7 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(RowsArgs a) {
   __shared__ int s_pre[kMaxGroups + 1];
   __shared__ int64_t s_r0[kMaxGroups];
   __shared__ int s_len[kMaxGroups];
+  __shared__ int s_preb[kMaxGroups + 1];
   extern __shared__ __attribute__((aligned(1024))) char ring[];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -341,34 +348,45 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(RowsArgs a) {
   const int wm = wave / kWN, wn = wave % kWN;
   const int G = a.nc * a.El;
   const int ntiles = (a.N + OUTN - 1) / OUTN;
+  // Two tile classes, each in group order: "large" row tiles (full, or a last tile of more than
+  // BM / 2 rows) and "small" last tiles (at most BM / 2 rows, cheaper: half the waves issue no
+  // MFMA). Large tiles are dealt first, so the small ones fill a second round where one is needed.
   for (int g = tid; g < G; g += kThreads) {
     const int c = a.c0 + g / a.El, e = g % a.El;
     const int32_t* off = a.offsets + (int64_t)c * (a.El + 1);
     const int len = off[e + 1] - off[e];
+    const int rem = len % BM;
     s_r0[g] = (int64_t)c * a.P_c + off[e];
     s_len[g] = len;
-    s_pre[g + 1] = ((len + BM - 1) / BM) * ntiles;
+    s_pre[g + 1] = (len / BM + (rem > BM / 2 ? 1 : 0)) * ntiles;
+    s_preb[g + 1] = (rem > 0 && rem <= BM / 2 ? 1 : 0) * ntiles;
   }
   __syncthreads();
   if (tid == 0) {
     s_pre[0] = 0;
     for (int g = 0; g < G; ++g) s_pre[g + 1] += s_pre[g];
+  } else if (tid == 64) {
+    s_preb[0] = 0;
+    for (int g = 0; g < G; ++g) s_preb[g + 1] += s_preb[g];
   }
   __syncthreads();
-  const int total = s_pre[G];
+  const int total_l = s_pre[G], total_s = s_preb[G];
   // Workgroups are dealt round-robin to the 8 XCDs (block b runs on XCD b % 8); each XCD owns a
-  // contiguous range of tiles, so the tiles of one expert share that XCD's L2.
-  const int per_xcd = (total + 7) / 8;
+  // contiguous range of the large tiles and one of the small tiles, so the tiles of one expert
+  // share that XCD's L2. An XCD's workgroups walk its large range, then its small range.
+  const int pxl = (total_l + 7) / 8, pxs = (total_s + 7) / 8;
   const int xcd = blockIdx.x % 8, wg_per_xcd = gridDim.x / 8;
-  for (int slot = blockIdx.x / 8; slot < per_xcd; slot += wg_per_xcd) {
-    const int tile = xcd * per_xcd + slot;
-    if (tile >= total) break;
+  for (int slot = blockIdx.x / 8; slot < pxl + pxs; slot += wg_per_xcd) {
+    const bool large = slot < pxl;
+    const int tile = large ? xcd * pxl + slot : xcd * pxs + (slot - pxl);
+    if (tile >= (large ? total_l : total_s)) continue;
+    const int* pre = large ? s_pre : s_preb;
     int lo = 0, hi = G;
-    while (hi - lo > 1) { const int mid = (lo + hi) >> 1; if (s_pre[mid] <= tile) lo = mid; else hi = mid; }
+    while (hi - lo > 1) { const int mid = (lo + hi) >> 1; if (pre[mid] <= tile) lo = mid; else hi = mid; }
     const int g = __builtin_amdgcn_readfirstlane(lo);
     const int e = g % a.El;
-    const int t_in = tile - __builtin_amdgcn_readfirstlane(s_pre[g]);
-    const int mt = t_in / ntiles, nt = t_in % ntiles;
+    const int t_in = tile - __builtin_amdgcn_readfirstlane(pre[g]);
+    const int mt = large ? t_in / ntiles : s_len[g] / BM, nt = t_in % ntiles;
     const int64_t rg = s_r0[g];
     const int64_t r0 = (((int64_t)__builtin_amdgcn_readfirstlane((int)(rg >> 32)) << 32) |
                         (uint32_t)__builtin_amdgcn_readfirstlane((int)(rg & 0xffffffff))) + (int64_t)mt * BM;
