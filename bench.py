@@ -163,6 +163,23 @@ def algorithmic_work(cfg, counts, offsets, k_sel_local_tokens):
     return w, N, Tt
 
 
+def gemm_bytes(cfg, N):
+    """HBM bytes each grouped GEMM must move per fused step, every tensor read or written once: the
+    row operands, the weights once per launch (per chunk for the row-grouped GEMMs), the outputs.
+    With the flops this gives the GEMM's arithmetic intensity and its attainable rate
+    min(MFMA peak, intensity x HBM peak)."""
+    H, I, El, n, s = cfg.H, cfg.I, cfg.E_local, cfg.n_chunks, 2
+    w1, w2 = El * 2 * I * H * s, El * H * I * s
+    return {
+        "gemm_gateup_swiglu": N * H * s + n * w1 + N * I * s + N * 2 * I * s,
+        "gemm_down": N * I * s + n * w2 + N * H * s,
+        "gemm_down_dgrad_swiglu": N * H * s + n * w2 + 2 * N * 2 * I * s,
+        "gemm_gateup_dgrad": N * 2 * I * s + n * w1 + N * H * s,
+        "gemm_wgrad_down": N * H * s + N * I * s + w2,
+        "gemm_wgrad_gateup": N * 2 * I * s + N * H * s + w1,
+    }
+
+
 def cpu_baseline(cfg, inp, budget_s: float):
     """Time the CPU oracle (as it stands) on a bounded prefix of the workload's tokens."""
     import numpy as np
@@ -370,6 +387,50 @@ def main():
         p[0] += 1
         p[1] += ms
 
+    # the row kernels once more, each stage called back to back `reps` times between two events
+    # on its stream: per-launch event overhead (a few us) amortised away
+    def amortized_us(fn, reps=20):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(cs)
+        for _ in range(reps):
+            fn()
+        e1.record(cs)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    b = bufs
+    row_stages = {
+        "dispatch": lambda c: mh.moe_dispatch(d, c, b["x"], b["row_of"], b["xd"], None, None, cs),
+        "combine": lambda c: mh.moe_combine(d, c, b["yd"], b["gates"], b["row_of"], b["out"], cs),
+        "combine_bwd": lambda c: mh.moe_combine_bwd(d, c, b["dy"], b["yd"], b["gates"], b["row_of"], b["dyd"],
+                                                    b["dgates"], cs),
+        "dispatch_bwd": lambda c: mh.moe_dispatch_bwd(d, c, b["dxd"], b["row_of"], b["topk_idx"], b["dlogits"],
+                                                      b["w_r"], b["dx"], cs),
+    }
+    amort = {name: amortized_us(lambda f=f: [f(c) for c in range(cfg.n_chunks)]) for name, f in row_stages.items()}
+
+    # the same layer with one chunk (no overlap, larger per-expert GEMMs), untraced
+    n1 = None
+    if cfg.n_chunks > 1:
+        d1 = mh.make_desc(T=cfg.T, H=cfg.H, I=cfg.I, E=cfg.E, E_local=cfg.E_local, k=cfg.k, n_chunks=1,
+                          dtype=cfg.dtype, e0=cfg.e0)
+        b1 = mh.allocate(d1, backward=True)
+        for name in ("x", "logits", "w1", "w2", "w_r", "dy"):
+            b1[name] = bufs[name]
+        for _ in range(args.warmup):
+            mh.moe_layer_forward_backward(d1, b1, cs, aux)
+        torch.cuda.synchronize()
+        n0 = time.perf_counter()
+        for _ in range(args.steps):
+            mh.moe_layer_forward_backward(d1, b1, cs, aux)
+        torch.cuda.synchronize()
+        ms1 = (time.perf_counter() - n0) * 1e3 / args.steps
+        n1 = {"n_chunks": 1, "ms_per_step_untraced": round(ms1, 4), "tokens_per_s": round(cfg.T / (ms1 * 1e-3), 1)}
+        del b1
+        torch.cuda.empty_cache()
+
     # FP8 payload path, forward only (the same shapes; weights quantised per output row outside the
     # timed region): expert GEMMs on FP8 MFMA, dispatch quantises per token, combine in BF16
     fp8 = fp8_forward(args, cfg, inp, mh, torch, np)
@@ -386,6 +447,7 @@ def main():
         p[0] += 1
         p[1] += ms
     kernels = {}
+    gbytes = gemm_bytes(cfg, N)
     for name, (cnt, tot) in per.items():
         launches = cnt / args.steps
         avg_us = tot / cnt * 1e3
@@ -395,8 +457,18 @@ def main():
             rate = wk / (tot / args.steps * 1e-3)
             if unit == "flop":
                 entry.update(achieved_tflops=round(rate / 1e12, 2), frac_mfma=round(rate / 1e12 / PEAK_BF16_TFLOPS, 4))
+                if name in gbytes:
+                    ai = wk / gbytes[name]
+                    attain = min(PEAK_BF16_TFLOPS, ai * PEAK_HBM_GBS / 1e3)
+                    entry.update(intensity_flop_per_byte=round(ai, 1), attainable_tflops=round(attain, 1),
+                                 frac_attainable=round(rate / 1e12 / attain, 4))
             else:
                 entry.update(achieved_gbs=round(rate / 1e9, 1), frac_hbm=round(rate / 1e9 / PEAK_HBM_GBS, 4))
+        if name in amort:
+            us = amort[name]  # both chunks
+            entry["isolated_amortized_us"] = round(us / cfg.n_chunks, 3)
+            if name in work:
+                entry["isolated_amortized_frac"] = round(work[name][0] / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
         if name in iso:
             ic, it = iso[name]
             entry["isolated_avg_us"] = round(it / ic * 1e3, 3)
@@ -438,6 +510,7 @@ def main():
         "gemm_tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 2) if gemm_ms > 0 else None,
         "roofline": roof, "kernels": kernels,
     }
+    line["one_chunk"] = n1
     line["fp8_fwd"] = fp8
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_budget)
