@@ -22,11 +22,13 @@ Modules:
   brute     per-token loops for tiny inputs (pins the vectorised forms).
   fp8       OCP e4m3fn encode/decode and per-row absmax quantisation; FP8 forward.
   extent    live-extent tracker and combine-output workspace floor.
+  stash     paged activation stash: page-aligned store/load of saved rows with live-prefix and
+            page-tail masks.
 
 Every function here is pinned by a ``-m "not gpu"`` test (brute force, closed forms, library
 special cases, finite differences, autograd, printed numbers); none is "parity unpinned".
 """
-from . import routing, ffn, brute, fp8, extent  # noqa: F401
+from . import routing, ffn, brute, fp8, extent, stash  # noqa: F401
 from .routing import (round4, chunk_bounds, required_extent, route, layout,  # noqa: F401
                       dispatch, unpermute)
 from .ffn import expert_ffn, combine, forward, backward  # noqa: F401
