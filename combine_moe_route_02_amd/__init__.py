@@ -68,6 +68,10 @@ _SIGS = {
     "moe_expert_wgrad": [POINTER(MoeDesc)] + [c_void_p] * 8,
     "moe_dispatch_bwd": [POINTER(MoeDesc), c_int] + [c_void_p] * 7,
     "moe_quantize_rows_fp8": [c_int64, c_int32] + [c_void_p] * 4,
+    "moe_stash_store": [c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_int64, c_int64, c_void_p,
+                        c_void_p, c_int32, c_int32, c_void_p],
+    "moe_stash_load": [c_void_p, c_void_p, c_int64, c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p,
+                       c_void_p, c_int32, c_void_p],
     "moe_layer_forward": [POINTER(MoeDesc), POINTER(MoeTensors), c_void_p, c_void_p],
     "moe_layer_backward": [POINTER(MoeDesc), POINTER(MoeTensors), c_void_p, c_void_p],
     "moe_layer_forward_backward": [POINTER(MoeDesc), POINTER(MoeTensors), c_void_p, c_void_p],
@@ -196,6 +200,20 @@ def moe_dispatch_bwd(d, chunk, dxd, row_of, topk_idx, dlogits, w_r, dx, stream=N
 def moe_quantize_rows_fp8(rows, cols, src_bf16, codes, scale, stream=None):
     _check(lib().moe_quantize_rows_fp8(rows, cols, _ptr(src_bf16), _ptr(codes), _ptr(scale), _stream(stream)),
            "moe_quantize_rows_fp8")
+
+
+def moe_stash_store(src, src_scale, live_rows, row_bytes, pool, pool_scale, num_pages, page_rows, pages,
+                    page_meta=None, owner=0, max_ctas=0, stream=None):
+    _check(lib().moe_stash_store(_ptr(src), _ptr(src_scale), live_rows, row_bytes, _ptr(pool), _ptr(pool_scale),
+                                 num_pages, page_rows, _ptr(pages), _ptr(page_meta), owner, max_ctas,
+                                 _stream(stream)), "moe_stash_store")
+
+
+def moe_stash_load(pool, pool_scale, live_rows, row_bytes, num_pages, page_rows, pages, dst, dst_scale=None,
+                   recycled=None, max_ctas=0, stream=None):
+    _check(lib().moe_stash_load(_ptr(pool), _ptr(pool_scale), live_rows, row_bytes, num_pages, page_rows,
+                                _ptr(pages), _ptr(dst), _ptr(dst_scale), _ptr(recycled), max_ctas,
+                                _stream(stream)), "moe_stash_load")
 
 
 def _tensors(bufs: Dict[str, object]) -> MoeTensors:

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <cstdint>
 #include <cstdarg>
 #include <cstdio>
 #include <map>
@@ -347,6 +348,53 @@ moe_status moe_quantize_rows_fp8(int64_t rows, int32_t cols, const void* src_bf1
   MOE_NEED(src_bf16); MOE_NEED(codes); MOE_NEED(scale);
   MOE_HIP(moe::launch_quantize_rows_fp8(src_bf16, codes, scale, rows, cols, (hipStream_t)stream),
           "quantize_rows_fp8");
+  return MOE_OK;
+}
+
+// ----------------------------------------------------------------------------- paged stash
+
+static moe_status check_stash(const char* fn, const void* rows, const void* pool, const void* scale_a,
+                              const void* scale_b, int64_t live_rows, int64_t row_bytes, int64_t num_pages,
+                              int64_t page_rows, const int32_t* pages, int32_t max_ctas) {
+  if (live_rows < 0 || num_pages < 0) return fail(MOE_ERR_ARG, "%s: negative live_rows or num_pages", fn);
+  if (row_bytes <= 0 || row_bytes % 16) return fail(MOE_ERR_ARG, "%s: row_bytes = %lld is not a positive multiple of 16", fn, (long long)row_bytes);
+  if (page_rows < 1) return fail(MOE_ERR_ARG, "%s: page_rows = %lld below 1", fn, (long long)page_rows);
+  if (max_ctas < 0) return fail(MOE_ERR_ARG, "%s: max_ctas = %d is negative", fn, max_ctas);
+  if ((scale_a == nullptr) != (scale_b == nullptr))
+    return fail(MOE_ERR_ARG, "%s: the two scale pointers must both be NULL or both be set", fn);
+  if (live_rows == 0) return MOE_OK;
+  if (!rows || !pool || !pages) return fail(MOE_ERR_ARG, "%s: a tensor, pool or page-table pointer is NULL", fn);
+  if (((uintptr_t)rows | (uintptr_t)pool) & 15) return fail(MOE_ERR_ARG, "%s: tensor and pool must be 16-byte aligned", fn);
+  if (num_pages > (INT64_MAX / 2) / page_rows / row_bytes || live_rows > (INT64_MAX / 2) / row_bytes)
+    return fail(MOE_ERR_ARG, "%s: pool or tensor size overflows 64-bit offsets", fn);
+  if ((live_rows + page_rows - 1) / page_rows > INT32_MAX) return fail(MOE_ERR_ARG, "%s: too many pages", fn);
+  return MOE_OK;
+}
+
+moe_status moe_stash_store(const void* src, const float* src_scale, int64_t live_rows, int64_t row_bytes,
+                           void* pool, float* pool_scale, int64_t num_pages, int64_t page_rows,
+                           const int32_t* pages, int32_t* page_meta, int32_t owner, int32_t max_ctas,
+                           void* stream) {
+  MOE_TRY(check_stash(__func__, src, pool, src_scale, pool_scale, live_rows, row_bytes, num_pages, page_rows,
+                      pages, max_ctas));
+  if (live_rows == 0) return MOE_OK;
+  MOE_HIP(moe::launch_stash_copy(true, src, src_scale, pool, pool_scale, live_rows, row_bytes, num_pages,
+                                 page_rows, pages, page_meta, owner, max_ctas ? max_ctas : 2048,
+                                 (hipStream_t)stream),
+          "stash_store");
+  return MOE_OK;
+}
+
+moe_status moe_stash_load(const void* pool, const float* pool_scale, int64_t live_rows, int64_t row_bytes,
+                          int64_t num_pages, int64_t page_rows, const int32_t* pages, void* dst,
+                          float* dst_scale, int32_t* recycled, int32_t max_ctas, void* stream) {
+  MOE_TRY(check_stash(__func__, dst, pool, pool_scale, dst_scale, live_rows, row_bytes, num_pages, page_rows,
+                      pages, max_ctas));
+  if (live_rows == 0) return MOE_OK;
+  MOE_HIP(moe::launch_stash_copy(false, pool, pool_scale, dst, dst_scale, live_rows, row_bytes, num_pages,
+                                 page_rows, pages, recycled, 0, max_ctas ? max_ctas : 2048,
+                                 (hipStream_t)stream),
+          "stash_load");
   return MOE_OK;
 }
 

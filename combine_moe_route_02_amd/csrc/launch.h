@@ -63,6 +63,11 @@ hipError_t gg_expert_dgrad_bf16(const void* dyd, const void* gu, const void* w1,
 hipError_t gg_expert_wgrad_bf16(const void* dyd, const void* dgu, const void* xd, const void* h,
                                 const int32_t* offsets, void* dw1, void* dw2, int H, int I, int El,
                                 int n, int64_t P_c, hipStream_t s);
+// paged activation stash (stash.hip): store = rows -> pool pages, else pool pages -> rows
+hipError_t launch_stash_copy(bool store, const void* from, const float* from_scale, void* to,
+                             float* to_scale, int64_t live_rows, int64_t row_bytes, int64_t num_pages,
+                             int64_t page_rows, const int32_t* pages, int32_t* record, int32_t owner,
+                             int32_t max_ctas, hipStream_t s);
 int router_ksplit(int64_t tokens);
 int64_t router_partials_bytes(int64_t Tc, int E, int H);
 hipError_t launch_router_wgrad(bool bf16, const float* dlogits, const void* x, float* partials,

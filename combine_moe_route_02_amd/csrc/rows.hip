@@ -11,6 +11,8 @@
 // multi-row tiles, tail masks and 64-bit addressing; these kernels keep those properties for the
 // gather/scatter between token order and expert-contiguous order. ART PR 971 (description)
 // gives combine's fresh [P, H] output cropped to the logical rows: only rows t < T are written.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 #include "trace.h"
@@ -307,50 +309,54 @@ __global__ __launch_bounds__(256) void dispatch_bwd_kernel(
   const int32_t myrow = lane < K ? row_of[t * K + lane] : -1;
   const int myid = lane < K ? idx[t * K + lane] : 0;
   const float mydl = lane < K ? dlogits[t * E + myid] : 0.f;
-  for (int64_t v0 = 0; v0 < nvec; v0 += 64 * kBatch) {
-    float acc[kBatch][V::N];
+  const uint64_t local = __ballot(myrow >= 0);
+  u32x4* dst = dx + t * nvec;
+  // NB vectors i0, i0 + 64, ... per lane; each slot's loads are issued together before use
+  auto pass = [&](int64_t i0, auto nb) {
+    constexpr int NB = decltype(nb)::value;
+    float acc[NB][V::N];
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int q = 0; q < V::N; ++q) acc[b][q] = 0.f;
+    // expert path: the local slots' dxd rows, j ascending
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-      int32_t r = __shfl(myrow, j, 64);
-      if (r < 0) continue;
-      const u32x4* src = dxd + (int64_t)r * nvec;
+      if (!((local >> j) & 1)) continue;
+      const u32x4* src = dxd + (int64_t)bcast_i(myrow, j) * nvec;
+      u32x4 v[NB];
 #pragma unroll
-      for (int b = 0; b < kBatch; ++b) {
-        int64_t i = v0 + b * 64 + lane;
-        if (i < nvec) {
-          float f[V::N];
-          V::to_f(src[i], f);
+      for (int b = 0; b < NB; ++b) v[b] = src[i0 + 64 * b];
 #pragma unroll
-          for (int q = 0; q < V::N; ++q) acc[b][q] += f[q];
-        }
+      for (int b = 0; b < NB; ++b) {
+        float f[V::N];
+        V::to_f(v[b], f);
+#pragma unroll
+        for (int q = 0; q < V::N; ++q) acc[b][q] += f[q];
+      }
+    }
+    // router path: dlogits[t][e_j] * W_r[e_j] for every slot, j ascending (W_r stays in L2)
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const u32x4* wr = w_r + (int64_t)bcast_i(myid, j) * nvec;
+      const float dl = bcast_f(mydl, j);
+      u32x4 w[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) w[b] = wr[i0 + 64 * b];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        float f[V::N];
+        V::to_f(w[b], f);
+#pragma unroll
+        for (int q = 0; q < V::N; ++q) acc[b][q] = fmaf(dl, f[q], acc[b][q]);
       }
     }
 #pragma unroll
-    for (int j = 0; j < K; ++j) {
-      int e = __shfl(myid, j, 64);
-      float dl = __shfl(mydl, j, 64);
-      const u32x4* wr = w_r + (int64_t)e * nvec;
-#pragma unroll
-      for (int b = 0; b < kBatch; ++b) {
-        int64_t i = v0 + b * 64 + lane;
-        if (i < nvec) {
-          float f[V::N];
-          V::to_f(wr[i], f);
-#pragma unroll
-          for (int q = 0; q < V::N; ++q) acc[b][q] = fmaf(dl, f[q], acc[b][q]);
-        }
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      int64_t i = v0 + b * 64 + lane;
-      if (i < nvec) dx[t * nvec + i] = V::from_f(acc[b]);
-    }
-  }
+    for (int b = 0; b < NB; ++b) dst[i0 + 64 * b] = V::from_f(acc[b]);
+  };
+  int64_t i0 = lane;
+  for (; i0 + 64 * (kBatch - 1) < nvec; i0 += 64 * kBatch) pass(i0, std::integral_constant<int, kBatch>());
+  for (; i0 < nvec; i0 += 64) pass(i0, std::integral_constant<int, 1>());
 }
 
 // ---------------------------------------------------------------------------------------------

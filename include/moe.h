@@ -174,6 +174,37 @@ moe_status moe_quantize_rows_fp8(int64_t rows, int32_t cols, const void* src_bf1
                                  float* scale, void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Paged activation stash (torchtitan PR 5541, "AI-Generated Details": page-aligned multi-token
+ * copy tiles, one page resolved per tile, the first tile of a page records or recycles it,
+ * live-prefix and page-tail masks, 64-bit addressing, a bounded copy grid).
+ *
+ * A saved tensor is `live_rows` rows of `row_bytes` bytes (any payload: BF16, FP8 codes, FP32;
+ * row_bytes a positive multiple of 16). The pool is `num_pages` pages of `page_rows` rows of
+ * the same row_bytes, contiguous: page p starts at pool + p*page_rows*row_bytes. Logical page i
+ * (tensor rows i*page_rows .. (i+1)*page_rows - 1) lives in physical page pages[i], for
+ * i < ceil(live_rows / page_rows); the entries must be distinct. An entry outside
+ * [0, num_pages) names no page: its rows are not copied (and nothing is written for it).
+ * Only live rows move; rows of the last page past the live prefix keep their contents.
+ * Optional FP32 per-row scales (FP8 payloads) are paged alongside: `*_scale` pointers are both
+ * NULL or both set, pool scales [num_pages * page_rows].
+ * The pool may be device memory or pinned host memory; src, dst and pool must be 16-byte
+ * aligned. `max_ctas` caps the copy grid (0: 2048). Nothing is launched when live_rows is 0.
+ * Errors: MOE_ERR_ARG for a NULL required pointer, misalignment, a negative size, row_bytes not
+ * a positive multiple of 16, page_rows < 1, a scale pointer set without its pair. */
+
+/* Store: pool rows <- tensor rows. page_meta (nullable, int32 [2 * num_pages]) receives, for every
+ * logical page with a valid entry p: page_meta[2p] = owner, page_meta[2p+1] = its live rows. */
+moe_status moe_stash_store(const void* src, const float* src_scale, int64_t live_rows, int64_t row_bytes,
+                           void* pool, float* pool_scale, int64_t num_pages, int64_t page_rows,
+                           const int32_t* pages, int32_t* page_meta, int32_t owner, int32_t max_ctas,
+                           void* stream);
+/* Load: tensor rows <- pool rows. recycled (nullable, int32 [ceil(live_rows / page_rows)])
+ * receives the physical page of each logical page in order (-1 for an invalid entry). */
+moe_status moe_stash_load(const void* pool, const float* pool_scale, int64_t live_rows, int64_t row_bytes,
+                          int64_t num_pages, int64_t page_rows, const int32_t* pages, void* dst,
+                          float* dst_scale, int32_t* recycled, int32_t max_ctas, void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * Layer primitives (ChunkedEP "Summary": forward, backward, fused forward/backward). They
  * own the two-stream chunk schedule: routing and dispatch of chunk c+1 on `aux` overlap the
  * expert GEMMs of chunk c on `compute`; combine of chunk c runs on `aux` after them. On return

@@ -125,3 +125,28 @@ def test_extent_tracker_matches_art971_fixture_and_oracle():
             a.acquire(r)
             b.acquire(r)
         assert a.current(req) == b.current(req)
+
+
+def test_stash_argument_errors_before_any_launch():
+    L = _lib_or_skip()
+    import ctypes
+    buf = (ctypes.c_uint8 * 64)()
+    a = ctypes.addressof(buf)
+    a16 = (a + 15) // 16 * 16
+    pg = (ctypes.c_int32 * 4)()
+    pa = ctypes.addressof(pg)
+    # row_bytes not a multiple of 16, page_rows < 1, a scale pointer without its pair, a negative
+    # size, a NULL tensor, a misaligned tensor: MOE_ERR_ARG (-1), nothing launched
+    for args in [(a16, None, 4, 24, a16, None, 2, 2, pa, None, 0, 0, None),
+                 (a16, None, 4, 16, a16, None, 2, 0, pa, None, 0, 0, None),
+                 (a16, a16, 4, 16, a16, None, 2, 2, pa, None, 0, 0, None),
+                 (a16, None, -1, 16, a16, None, 2, 2, pa, None, 0, 0, None),
+                 (None, None, 4, 16, a16, None, 2, 2, pa, None, 0, 0, None),
+                 (a16 + 4, None, 4, 16, a16, None, 2, 2, pa, None, 0, 0, None)]:
+        assert L.moe_stash_store(*args) == -1, args
+    for args in [(a16, None, 4, 16, 2, 2, pa, None, None, None, -1, None),
+                 (a16, None, 4, 16, 2, 2, None, a16, None, None, 0, None)]:
+        assert L.moe_stash_load(*args) == -1, args
+    # an empty live prefix is valid and launches nothing (no GPU needed)
+    assert L.moe_stash_store(None, None, 0, 16, None, None, 0, 1, None, None, 0, 0, None) == 0
+    assert L.moe_stash_load(None, None, 0, 16, 0, 1, None, None, None, None, 0, None) == 0
