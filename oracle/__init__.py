@@ -30,5 +30,5 @@ special cases, finite differences, autograd, printed numbers); none is "parity u
 """
 from . import routing, ffn, brute, fp8, extent, stash  # noqa: F401
 from .routing import (round4, chunk_bounds, required_extent, route, layout,  # noqa: F401
-                      dispatch, unpermute)
+                      dispatch, unpermute, router_logits)
 from .ffn import expert_ffn, combine, forward, backward  # noqa: F401

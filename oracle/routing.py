@@ -38,6 +38,16 @@ def required_extent(T: int, k: int, E_local: int, n: int):
     return round4(tc * min(k, E_local)), max(round4(T * k), round4(T))
 
 
+def router_logits(x: np.ndarray, w_r: np.ndarray) -> np.ndarray:
+    """Router projection before the top-k: logits[t, e] = sum_h x[t, h] * W_r[e, h] (FP64).
+
+    The pages give the router weight only through its gradient (ChunkedEP "Numerical status --
+    unresolved": FP32 accumulation of the router-weight gradient across chunks); the projection is
+    its plain forward counterpart, the linear map whose weight-gradient is dlogits^T x.
+    """
+    return np.asarray(x, dtype=np.float64) @ np.asarray(w_r, dtype=np.float64).T
+
+
 def route(logits: np.ndarray, k: int):
     """Top-k selection and renormalised softmax gates for every token.
 

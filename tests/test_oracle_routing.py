@@ -138,3 +138,25 @@ def test_extent_rules():
     assert oracle.required_extent(10, 3, 2, 3) == (8, 32)              # min(k, E_local) per token
     assert oracle.chunk_bounds(10, 3) == [(0, 4), (4, 8), (8, 10)]
     assert oracle.chunk_bounds(2, 4) == [(0, 1), (1, 2), (2, 2), (2, 2)]
+
+
+def test_router_logits_brute_force_and_one_hot_rows():
+    """logits = x . W_r^T: per-element loops on a tiny case; one-hot router rows pick columns."""
+    from oracle import routing
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((5, 7))
+    w = rng.standard_normal((3, 7))
+    got = routing.router_logits(x, w)
+    for t in range(5):
+        for e in range(3):
+            acc = 0.0
+            for h in range(7):
+                acc += x[t, h] * w[e, h]
+            assert abs(got[t, e] - acc) <= 1e-12 * (1 + abs(acc))
+    onehot = np.zeros((4, 7))
+    cols = [6, 0, 3, 3]
+    for e, c in enumerate(cols):
+        onehot[e, c] = 1.0
+    np.testing.assert_array_equal(routing.router_logits(x, onehot), x[:, cols])
+    # a transposed operand would fail this shape check (T, E) = (5, 3)
+    assert got.shape == (5, 3)
