@@ -411,6 +411,39 @@ def main():
     }
     amort = {name: amortized_us(lambda f=f: [f(c) for c in range(cfg.n_chunks)]) for name, f in row_stages.items()}
 
+    # routing from x (router projection fused into the top-k) against routing from given logits,
+    # all chunks per call; the second call restores the timed step's routing in the buffers
+    chunks = range(cfg.n_chunks)
+    rx_us = amortized_us(lambda: [mh.moe_route_x(d, c, b["x"], b["w_r"], None, b["topk_idx"], b["gates"],
+                                                 b["counts"], b["offsets"], b["row_of"], b["src_token"],
+                                                 b["workspace"], cs) for c in chunks])
+    rl_us = amortized_us(lambda: [mh.moe_route(d, c, b["logits"], b["topk_idx"], b["gates"], b["counts"],
+                                               b["offsets"], b["row_of"], b["src_token"], b["workspace"], cs)
+                                  for c in chunks])
+    proj_flops = 2.0 * cfg.T * cfg.E * cfg.H
+    route_x_line = {"from_x_us_per_step": round(rx_us, 3), "from_logits_us_per_step": round(rl_us, 3),
+                    "projection_tflops_est": round(proj_flops / ((rx_us - rl_us) * 1e-6) / 1e12, 1)
+                    if rx_us > rl_us else None}
+
+    # paged activation stash: one chunk's expert-output rows (yd) stored into a page pool under a
+    # shuffled page table and loaded back, each called back to back between one event pair
+    live = int(bufs["offsets"][0, cfg.E_local].item())
+    rb, page_rows = cfg.H * 2, 256
+    npg = -(-live // page_rows)
+    g = torch.Generator().manual_seed(7)
+    pages = torch.randperm(npg, generator=g).to(torch.int32).cuda()
+    pool = torch.empty((npg * page_rows, rb), dtype=torch.uint8, device="cuda")
+    back = torch.empty((live, rb), dtype=torch.uint8, device="cuda")
+    yd0 = bufs["yd"].view(torch.uint8)
+    st_us = amortized_us(lambda: mh.moe_stash_store(yd0, None, live, rb, pool, None, npg, page_rows, pages,
+                                                    stream=cs))
+    ld_us = amortized_us(lambda: mh.moe_stash_load(pool, None, live, rb, npg, page_rows, pages, back, stream=cs))
+    moved = 2.0 * live * rb
+    stash_line = {"rows": live, "row_bytes": rb, "page_rows": page_rows, "store_us": round(st_us, 3),
+                  "load_us": round(ld_us, 3), "store_frac_hbm": round(moved / (st_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                  "load_frac_hbm": round(moved / (ld_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    del pool, back
+
     # the same layer with one chunk (no overlap, larger per-expert GEMMs), untraced
     n1 = None
     if cfg.n_chunks > 1:
@@ -511,6 +544,8 @@ def main():
         "roofline": roof, "kernels": kernels,
     }
     line["one_chunk"] = n1
+    line["stash"] = stash_line
+    line["route_from_x"] = route_x_line
     line["fp8_fwd"] = fp8
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_budget)

@@ -59,6 +59,7 @@ _LIB = None
 
 _SIGS = {
     "moe_route": [POINTER(MoeDesc), c_int] + [c_void_p] * 9,
+    "moe_route_x": [POINTER(MoeDesc), c_int] + [c_void_p] * 11,
     "moe_dispatch": [POINTER(MoeDesc), c_int] + [c_void_p] * 6,
     "moe_expert_ffn": [POINTER(MoeDesc), c_int] + [c_void_p] * 12,
     "moe_combine": [POINTER(MoeDesc), c_int] + [c_void_p] * 5,
@@ -152,6 +153,13 @@ def moe_route(d, chunk, logits, topk_idx, gates, counts, offsets, row_of, src_to
     _check(lib().moe_route(ctypes.byref(d), chunk, _ptr(logits), _ptr(topk_idx), _ptr(gates), _ptr(counts),
                            _ptr(offsets), _ptr(row_of), _ptr(src_token), _ptr(workspace), _stream(stream)),
            "moe_route")
+
+
+def moe_route_x(d, chunk, x, w_r, logits, topk_idx, gates, counts, offsets, row_of, src_token, workspace,
+                stream=None):
+    _check(lib().moe_route_x(ctypes.byref(d), chunk, _ptr(x), _ptr(w_r), _ptr(logits), _ptr(topk_idx), _ptr(gates),
+                             _ptr(counts), _ptr(offsets), _ptr(row_of), _ptr(src_token), _ptr(workspace),
+                             _stream(stream)), "moe_route_x")
 
 
 def moe_dispatch(d, chunk, x, row_of, xd, xd_scale=None, h_scale=None, stream=None):

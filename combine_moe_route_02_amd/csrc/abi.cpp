@@ -203,6 +203,25 @@ moe_status moe_route(const moe_desc* d, int chunk, const float* logits, int32_t*
   return MOE_OK;
 }
 
+moe_status moe_route_x(const moe_desc* d, int chunk, const void* x, const void* w_r, float* logits,
+                       int32_t* topk_idx, float* gates, int32_t* counts, int32_t* offsets, int32_t* row_of,
+                       int32_t* src_token, void* workspace, void* stream) {
+  MOE_TRY(validate(d));
+  MOE_TRY(check_chunk(d, chunk));
+  if (d->dtype == MOE_F32) return fail(MOE_ERR_UNSUPPORTED, "moe_route_x: x and W_r must be BF16 (dtype BF16 or FP8)");
+  if (d->E % 32 || d->E > 512)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_route_x: E = %d must be a multiple of 32, at most 512", d->E);
+  if (d->T > 0) { MOE_NEED(x); MOE_NEED(w_r); MOE_NEED(topk_idx); MOE_NEED(gates); MOE_NEED(row_of); }
+  if (rows_of(d) > 0) MOE_NEED(src_token);
+  MOE_NEED(counts); MOE_NEED(offsets); MOE_NEED(workspace);
+  Range r = range_of(d, chunk);
+  MOE_HIP(moe::launch_route_x(x, w_r, logits, topk_idx, gates, counts, offsets, row_of, src_token,
+                              (int32_t*)workspace, d->T, d->E, d->H, d->e0, d->E_local, d->k, d->n_chunks,
+                              r.c0, r.nc, d->P_c, (hipStream_t)stream),
+          "route_x");
+  return MOE_OK;
+}
+
 moe_status moe_dispatch(const moe_desc* d, int chunk, const void* x, const int32_t* row_of, void* xd,
                         float* xd_scale, float* h_scale, void* stream) {
   MOE_TRY(validate(d));

@@ -10,6 +10,12 @@ namespace moe {
 // routing
 int route_blocks_per_chunk(int64_t T, int n);
 int64_t route_scratch_bytes(int64_t T, int n, int E);
+// routing from x: logits = x . W_r^T (BF16 MFMA, FP32 accumulation) fused with the top-k, then
+// the layout kernel; logits may be NULL. Needs E % 32 == 0, E <= 512.
+hipError_t launch_route_x(const void* x, const void* w_r, float* logits, int32_t* topk_idx, float* gates,
+                          int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* src_token,
+                          int32_t* scratch, int64_t T, int E, int H, int e0, int El, int K, int n, int chunk0,
+                          int nchunks, int64_t P_c, hipStream_t s);
 hipError_t launch_route(const float* logits, int32_t* topk_idx, float* gates, int32_t* counts,
                         int32_t* offsets, int32_t* row_of, int32_t* src_token, int32_t* scratch,
                         int64_t T, int E, int e0, int El, int K, int n, int chunk0, int nchunks,

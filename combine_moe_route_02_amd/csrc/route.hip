@@ -7,7 +7,8 @@
 // the selected logits. The permutation is the stable sort of (token, slot) pairs by expert inside
 // each chunk: within an expert, rows follow ascending token index.
 //
-// Two launches per chunk range, both deterministic:
+// Two launches per chunk range, both deterministic (route_topk, or route_proj_topk when routing
+// starts from x and the router weight):
 //   route_topk   16 lanes per token (4 tokens per wave, 16 tokens per 256-thread block). Each
 //                lane keeps a sorted top-K list of its share of the experts as 64-bit keys
 //                (order-preserving logit bits above the complemented expert index, so ties go to
@@ -19,6 +20,8 @@
 //                each token's rank among
 //                the block's earlier tokens choosing the same expert from a 64-bit ballot mask
 //                (popcount below the lane); one wave per top-k slot.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 #include "trace.h"
@@ -66,26 +69,15 @@ MOE_DEV uint64_t shfl_xor_u64(uint64_t v, int o) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// Top-K of one token's logits row (nullptr: no token) for the 16-lane group of lane q: each lane
+// keeps a sorted list of its share of the experts, then K rounds of a 16-lane max merge the
+// lists (keys are distinct). Every lane of the group must call it (it shuffles).
 template <int K>
-__global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
-    const float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ gates,
-    int32_t* __restrict__ block_hist, int64_t T, int E, int n, int chunk0, int nbpc) {
-  extern __shared__ int hist[];  // [E]
-  const int tid = threadIdx.x;
-  const int c = chunk0 + blockIdx.x / nbpc;
-  const int bl = blockIdx.x % nbpc;
-  const ChunkRange cr = chunk_range(T, n, c);
-  for (int e = tid; e < E; e += kTopkThreads) hist[e] = 0;
-  __syncthreads();
-  const int q = tid & (kGroup - 1);                 // lane within the token's group
-  const int64_t t = cr.t0 + (int64_t)bl * kHistTok + (tid / kGroup);
-  const bool valid = t < cr.t1;
-
+MOE_DEV void select_topk(const float* row, int E, int q, uint64_t (&sel)[K]) {
   uint64_t l[K];
 #pragma unroll
   for (int s = 0; s < K; ++s) l[s] = 0;
-  if (valid) {
-    const float* row = logits + t * (int64_t)E;
+  if (row) {
     if ((E & 3) == 0) {
       // lane q reads experts [base + 4q, base + 4q + 4): 256 contiguous bytes per group
       for (int base = 0; base < E; base += 4 * kGroup) {
@@ -102,8 +94,6 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
       for (int e = q; e < E; e += kGroup) insert_key<K>(l, full_key(row[e], e));
     }
   }
-  // K rounds: the group's largest head wins and its lane pops it (keys are distinct)
-  uint64_t sel[K];
 #pragma unroll
   for (int s = 0; s < K; ++s) {
     uint64_t m = l[0];
@@ -119,24 +109,141 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
       l[K - 1] = 0;
     }
   }
-  if (valid && q < K) {
-    const float v0 = key_logit((uint32_t)(sel[0] >> 32));
-    float sum = 0.f, mine = 0.f;
-    int myid = 0;
+}
+
+// Lane q < K of a token's group writes slot q (descending logit): the expert, its gate
+// exp(l_q - l_0) / sum_s exp(l_s - l_0) over the K selected logits, and one histogram count.
+template <int K>
+MOE_DEV void emit_topk(const uint64_t (&sel)[K], int q, int64_t t, int32_t* topk_idx, float* gates, int* hist) {
+  const float v0 = key_logit((uint32_t)(sel[0] >> 32));
+  float sum = 0.f, mine = 0.f;
+  int myid = 0;
 #pragma unroll
-    for (int s = 0; s < K; ++s) {
-      const float p = expf(key_logit((uint32_t)(sel[s] >> 32)) - v0);
-      sum += p;
-      if (s == q) { mine = p; myid = (int)(0xffffffffu - (uint32_t)sel[s]); }
-    }
-    topk_idx[t * K + q] = myid;
-    gates[t * K + q] = mine / sum;
-    atomicAdd(&hist[myid], 1);
+  for (int s = 0; s < K; ++s) {
+    const float p = expf(key_logit((uint32_t)(sel[s] >> 32)) - v0);
+    sum += p;
+    if (s == q) { mine = p; myid = (int)(0xffffffffu - (uint32_t)sel[s]); }
   }
+  topk_idx[t * K + q] = myid;
+  gates[t * K + q] = mine / sum;
+  atomicAdd(&hist[myid], 1);
+}
+
+template <int K>
+__global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
+    const float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ gates,
+    int32_t* __restrict__ block_hist, int64_t T, int E, int n, int chunk0, int nbpc) {
+  extern __shared__ int hist[];  // [E]
+  const int tid = threadIdx.x;
+  const int c = chunk0 + blockIdx.x / nbpc;
+  const int bl = blockIdx.x % nbpc;
+  const ChunkRange cr = chunk_range(T, n, c);
+  for (int e = tid; e < E; e += kTopkThreads) hist[e] = 0;
+  __syncthreads();
+  const int q = tid & (kGroup - 1);                 // lane within the token's group
+  const int64_t t = cr.t0 + (int64_t)bl * kHistTok + (tid / kGroup);
+  const bool valid = t < cr.t1;
+  uint64_t sel[K];
+  select_topk<K>(valid ? logits + t * (int64_t)E : nullptr, E, q, sel);
+  if (valid && q < K) emit_topk<K>(sel, q, t, topk_idx, gates, hist);
   __syncthreads();
   // expert-major: the counts of expert e over the chunk's histograms are contiguous
   int32_t* out = block_hist + (int64_t)c * E * nbpc + bl;
   for (int e = tid; e < E; e += kTopkThreads) out[(int64_t)e * nbpc] = hist[e];
+}
+
+// Router projection fused with the top-K: logits = x . W_r^T for 32 tokens and all E experts on
+// BF16 MFMA with FP32 accumulation, then the same selection as route_topk from LDS. Eight waves:
+// wave w takes the 32-expert blocks w % 4, w % 4 + 4, ... over K half w / 4 (so 2 x E/32 MFMA
+// streams per block); the two K halves are added in LDS in a fixed order (half 0 + half 1).
+// Operands come straight from global memory (x rows once per block, W_r from L2), eight 16-wide
+// K steps per batch with all loads issued first.
+constexpr int kProjTok = 32;
+constexpr int kProjThreads = 512;
+
+template <int K, int NB>
+__global__ __launch_bounds__(kProjThreads) void route_proj_topk_kernel(
+    const __bf16* __restrict__ x, const __bf16* __restrict__ w_r, float* __restrict__ logits,
+    int32_t* __restrict__ topk_idx, float* __restrict__ gates, int32_t* __restrict__ block_hist, int64_t T,
+    int E, int H, int n, int chunk0, int nb32) {
+  extern __shared__ __attribute__((aligned(16))) float lg[];  // [kProjTok][E + 4], then int [2][E]
+  const int ldl = E + 4;
+  int* hist = (int*)(lg + kProjTok * ldl);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = chunk0 + blockIdx.x / nb32, bl = blockIdx.x % nb32;
+  const ChunkRange cr = chunk_range(T, n, c);
+  const int64_t tb = cr.t0 + (int64_t)bl * kProjTok;  // first token of the block
+  const int ntok = (int)max((int64_t)0, min((int64_t)kProjTok, cr.t1 - tb));
+  for (int e = tid; e < 2 * E; e += kProjThreads) hist[e] = 0;
+  const int neb = E / 32, kh = wave / 4;
+  if (ntok > 0) {
+    // MFMA fragments: lane l holds rows l & 31 and K values 8 (l >> 5) .. +7 of each 16-wide step
+    const int r = lane & 31, h8 = 8 * (lane >> 5), Hh = H / 2;
+    const __bf16* xa = x + (tb + min(r, ntok - 1)) * (int64_t)H + kh * Hh + h8;  // tail rows repeat
+    const __bf16* wb[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+      wb[i] = w_r + (int64_t)(min(wave % 4 + 4 * i, neb - 1) * 32 + r) * H + kh * Hh + h8;
+    f32x16_t acc[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
+    // NS 16-wide K steps per batch, every load of the batch issued before its MFMAs
+    auto batch = [&](int k0, auto ns) {
+      constexpr int NS = decltype(ns)::value;
+      bf16x8_t fa[NS], fb[NB][NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) fa[s] = *(const bf16x8_t*)(xa + k0 + 16 * s);
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) fb[i][s] = *(const bf16x8_t*)(wb[i] + k0 + 16 * s);
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[i][s], fa[s], acc[i], 0, 0, 0);
+    };
+    int k0 = 0;
+    for (; k0 + 128 <= Hh; k0 += 128) batch(k0, std::integral_constant<int, 8>());
+    for (; k0 < Hh; k0 += 16) batch(k0, std::integral_constant<int, 1>());
+    // acc[i][4g + q] is (token r, expert 32 eb + 8g + 4 (lane >> 5) + q); half 1 stores, half 0 adds
+    for (int pass = 1; pass >= 0; --pass) {
+      if (kh == pass) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          const int eb = wave % 4 + 4 * i;
+          if (eb >= neb) continue;
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              float* d = lg + r * ldl + eb * 32 + 8 * g + 4 * (lane >> 5) + q;
+              *d = pass ? acc[i][4 * g + q] : acc[i][4 * g + q] + *d;
+            }
+        }
+      }
+      __syncthreads();
+    }
+  } else {
+    __syncthreads();
+    __syncthreads();
+  }
+  // top-K: 32 tokens x 16 lanes
+  const int q = tid & (kGroup - 1), tl = tid / kGroup;
+  const bool valid = tl < ntok;
+  uint64_t sel[K];
+  select_topk<K>(valid ? lg + tl * ldl : nullptr, E, q, sel);
+  if (valid && q < K) emit_topk<K>(sel, q, tb + tl, topk_idx, gates, hist + (tl / kHistTok) * E);
+  if (logits)
+    for (int i = tid; i < ntok * E; i += kProjThreads)
+      logits[(tb + i / E) * (int64_t)E + i % E] = lg[(i / E) * ldl + i % E];
+  __syncthreads();
+  // this block's two 16-token histograms, expert-major
+  const int nh = 2 * nb32;
+  for (int i = tid; i < 2 * E; i += kProjThreads)
+    block_hist[((int64_t)c * E + i % E) * nh + 2 * bl + i / E] = hist[i];
 }
 
 __global__ __launch_bounds__(kRouteThreads) void route_layout_kernel(
@@ -240,12 +347,58 @@ int64_t route_scratch_bytes(int64_t T, int n, int E) {
   return (int64_t)n * route_blocks_per_chunk(T, n) * kSub * E * (int64_t)sizeof(int32_t);
 }
 
+static hipError_t launch_layout(const int32_t* topk_idx, const int32_t* scratch, int32_t* counts,
+                               int32_t* offsets, int32_t* row_of, int32_t* src_token, int64_t T, int E,
+                               int e0, int El, int K, int n, int chunk0, int nchunks, int64_t P_c,
+                               hipStream_t s) {
+  const int nbpc = route_blocks_per_chunk(T, n);
+  size_t sm2 = (size_t)El * 4 + (size_t)(El + 1) * 4 + 8 + (size_t)El * 8;
+  MOE_TRACE("route_layout", s);
+  hipLaunchKernelGGL(route_layout_kernel, dim3(nbpc * nchunks), dim3(kRouteThreads), sm2, s, topk_idx, scratch,
+                     counts, offsets, row_of, src_token, T, E, e0, El, K, n, chunk0, nbpc, P_c);
+  return hipGetLastError();
+}
+
+size_t route_x_lds_bytes(int E) { return (size_t)kProjTok * (E + 4) * 4 + (size_t)2 * E * 4; }
+
+hipError_t launch_route_x(const void* x, const void* w_r, float* logits, int32_t* topk_idx, float* gates,
+                          int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* src_token,
+                          int32_t* scratch, int64_t T, int E, int H, int e0, int El, int K, int n, int chunk0,
+                          int nchunks, int64_t P_c, hipStream_t s) {
+  const int nb32 = route_blocks_per_chunk(T, n) * (kRouteBlock / kProjTok);
+  const int NB = (E + 127) / 128;
+  const size_t lds = route_x_lds_bytes(E);
+  dim3 grid(nb32 * nchunks), block(kProjThreads);
+  {
+    MOE_TRACE("route_proj_topk", s);
+    switch (K * 8 + NB) {
+#define MOE_RX(KK, NN)                                                                                 \
+  case KK * 8 + NN: {                                                                                 \
+    auto k = route_proj_topk_kernel<KK, NN>;                                                          \
+    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+    if (e != hipSuccess) return e;                                                                    \
+    hipLaunchKernelGGL(k, grid, block, lds, s, (const __bf16*)x, (const __bf16*)w_r, logits, topk_idx,   \
+                       gates, scratch, T, E, H, n, chunk0, nb32);                                      \
+    break;                                                                                            \
+  }
+#define MOE_RX_K(KK) MOE_RX(KK, 1) MOE_RX(KK, 2) MOE_RX(KK, 3) MOE_RX(KK, 4)
+      MOE_RX_K(1) MOE_RX_K(2) MOE_RX_K(3) MOE_RX_K(4) MOE_RX_K(5) MOE_RX_K(6) MOE_RX_K(7) MOE_RX_K(8)
+#undef MOE_RX_K
+#undef MOE_RX
+      default: return hipErrorInvalidValue;
+    }
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return launch_layout(topk_idx, scratch, counts, offsets, row_of, src_token, T, E, e0, El, K, n, chunk0, nchunks,
+                       P_c, s);
+}
+
 hipError_t launch_route(const float* logits, int32_t* topk_idx, float* gates, int32_t* counts,
                         int32_t* offsets, int32_t* row_of, int32_t* src_token, int32_t* scratch,
                         int64_t T, int E, int e0, int El, int K, int n, int chunk0, int nchunks,
                         int64_t P_c, hipStream_t s) {
   const int nbpc = route_blocks_per_chunk(T, n);
-  dim3 grid(nbpc * nchunks), block(kRouteThreads);
   dim3 grid1(nbpc * kSub * nchunks), block1(kTopkThreads);
   size_t sm1 = (size_t)E * sizeof(int);
   switch (K) {
@@ -263,13 +416,8 @@ hipError_t launch_route(const float* logits, int32_t* topk_idx, float* gates, in
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  size_t sm2 = (size_t)El * 4 + (size_t)(El + 1) * 4 + 8 + (size_t)El * 8;
-  {
-    MOE_TRACE("route_layout", s);
-    hipLaunchKernelGGL(route_layout_kernel, grid, block, sm2, s, topk_idx, scratch, counts, offsets,
-                       row_of, src_token, T, E, e0, El, K, n, chunk0, nbpc, P_c);
-  }
-  return hipGetLastError();
+  return launch_layout(topk_idx, scratch, counts, offsets, row_of, src_token, T, E, e0, El, K, n, chunk0, nchunks,
+                       P_c, s);
 }
 
 }  // namespace moe

@@ -102,6 +102,15 @@ moe_status moe_route(const moe_desc* d, int chunk, const float* logits, int32_t*
                      float* gates, int32_t* counts, int32_t* offsets, int32_t* row_of,
                      int32_t* src_token, void* workspace, void* stream);
 
+/* Routing from the token activations (the router projection fused into routing): logits =
+ * x . W_r^T with BF16 x [T,H] and W_r [E,H], FP32 accumulation on MFMA, then the top-k of
+ * moe_route on those logits, which stay in registers and LDS; `logits` (nullable, FP32 [T,E])
+ * receives them. Every other argument and output is moe_route's. Needs a BF16 or FP8 descriptor
+ * (x is BF16 in both) and E a multiple of 32, at most 512 (MOE_ERR_UNSUPPORTED otherwise). */
+moe_status moe_route_x(const moe_desc* d, int chunk, const void* x, const void* w_r, float* logits,
+                       int32_t* topk_idx, float* gates, int32_t* counts, int32_t* offsets, int32_t* row_of,
+                       int32_t* src_token, void* workspace, void* stream);
+
 /* Dispatch: xd[row_of[t][j]] = x[t] for every local slot (a bitwise row copy for F32/BF16;
  * each touched token row is read once). FP8: per token amax over the BF16 row,
  * xd = e4m3(x * (448/amax)) with FP32 steps, RNE, saturating; xd_scale[row] = amax/448 (1 for
