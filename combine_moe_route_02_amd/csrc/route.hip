@@ -153,19 +153,20 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
 }
 
 // Router projection fused with the top-K: logits = x . W_r^T for 32 tokens and all E experts on
-// BF16 MFMA with FP32 accumulation, then the same selection as route_topk from LDS. Eight waves:
-// wave w takes the 32-expert blocks w % 4, w % 4 + 4, ... over K half w / 4 (so 2 x E/32 MFMA
-// streams per block); the two K halves are added in LDS in a fixed order (half 0 + half 1).
-// Operands come straight from global memory (x rows once per block, W_r from L2), eight 16-wide
-// K steps per batch with all loads issued first.
+// BF16 MFMA with FP32 accumulation, then the same selection as route_topk from LDS. 4 * KS waves:
+// wave w takes the 32-expert blocks w % 4, w % 4 + 4, ... (NB of them) over K part w / 4 of KS;
+// the KS partial tiles are added in LDS in a fixed order (part KS-1 first, part 0 last). Operands
+// come straight from global memory (x rows once per block, W_r from L2) in batches of four
+// 16-wide K steps, double-buffered: the next batch's loads are in flight while this one's MFMAs
+// run.
 constexpr int kProjTok = 32;
-constexpr int kProjThreads = 512;
 
-template <int K, int NB>
-__global__ __launch_bounds__(kProjThreads) void route_proj_topk_kernel(
+template <int K, int NB, int KS>
+__global__ __launch_bounds__(256 * KS) void route_proj_topk_kernel(
     const __bf16* __restrict__ x, const __bf16* __restrict__ w_r, float* __restrict__ logits,
     int32_t* __restrict__ topk_idx, float* __restrict__ gates, int32_t* __restrict__ block_hist, int64_t T,
     int E, int H, int n, int chunk0, int nb32) {
+  constexpr int kThreads = 256 * KS, NS = 4;
   extern __shared__ __attribute__((aligned(16))) float lg[];  // [kProjTok][E + 4], then int [2][E]
   const int ldl = E + 4;
   int* hist = (int*)(lg + kProjTok * ldl);
@@ -174,43 +175,61 @@ __global__ __launch_bounds__(kProjThreads) void route_proj_topk_kernel(
   const ChunkRange cr = chunk_range(T, n, c);
   const int64_t tb = cr.t0 + (int64_t)bl * kProjTok;  // first token of the block
   const int ntok = (int)max((int64_t)0, min((int64_t)kProjTok, cr.t1 - tb));
-  for (int e = tid; e < 2 * E; e += kProjThreads) hist[e] = 0;
-  const int neb = E / 32, kh = wave / 4;
+  for (int e = tid; e < 2 * E; e += kThreads) hist[e] = 0;
+  const int neb = E / 32, kp = wave / 4, Hq = H / KS;
   if (ntok > 0) {
     // MFMA fragments: lane l holds rows l & 31 and K values 8 (l >> 5) .. +7 of each 16-wide step
-    const int r = lane & 31, h8 = 8 * (lane >> 5), Hh = H / 2;
-    const __bf16* xa = x + (tb + min(r, ntok - 1)) * (int64_t)H + kh * Hh + h8;  // tail rows repeat
+    const int r = lane & 31, h8 = 8 * (lane >> 5);
+    const __bf16* xa = x + (tb + min(r, ntok - 1)) * (int64_t)H + kp * Hq + h8;  // tail rows repeat
     const __bf16* wb[NB];
 #pragma unroll
     for (int i = 0; i < NB; ++i)
-      wb[i] = w_r + (int64_t)(min(wave % 4 + 4 * i, neb - 1) * 32 + r) * H + kh * Hh + h8;
+      wb[i] = w_r + (int64_t)(min(wave % 4 + 4 * i, neb - 1) * 32 + r) * H + kp * Hq + h8;
     f32x16_t acc[NB];
 #pragma unroll
     for (int i = 0; i < NB; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
-    // NS 16-wide K steps per batch, every load of the batch issued before its MFMAs
-    auto batch = [&](int k0, auto ns) {
-      constexpr int NS = decltype(ns)::value;
-      bf16x8_t fa[NS], fb[NB][NS];
+    auto load = [&](int k0, bf16x8_t (&fa)[NS], bf16x8_t (&fb)[NB][NS]) {
 #pragma unroll
       for (int s = 0; s < NS; ++s) fa[s] = *(const bf16x8_t*)(xa + k0 + 16 * s);
 #pragma unroll
       for (int i = 0; i < NB; ++i)
 #pragma unroll
         for (int s = 0; s < NS; ++s) fb[i][s] = *(const bf16x8_t*)(wb[i] + k0 + 16 * s);
+    };
+    auto mma = [&](const bf16x8_t (&fa)[NS], const bf16x8_t (&fb)[NB][NS]) {
 #pragma unroll
       for (int s = 0; s < NS; ++s)
 #pragma unroll
         for (int i = 0; i < NB; ++i)
           acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[i][s], fa[s], acc[i], 0, 0, 0);
     };
-    int k0 = 0;
-    for (; k0 + 128 <= Hh; k0 += 128) batch(k0, std::integral_constant<int, 8>());
-    for (; k0 < Hh; k0 += 16) batch(k0, std::integral_constant<int, 1>());
-    // acc[i][4g + q] is (token r, expert 32 eb + 8g + 4 (lane >> 5) + q); half 1 stores, half 0 adds
-    for (int pass = 1; pass >= 0; --pass) {
-      if (kh == pass) {
+    constexpr int kStep = 16 * NS;
+    if (Hq % (2 * kStep) == 0) {
+      bf16x8_t fa0[NS], fb0[NB][NS], fa1[NS], fb1[NB][NS];
+      load(0, fa0, fb0);
+      for (int k0 = 0; k0 < Hq; k0 += 2 * kStep) {
+        load(k0 + kStep, fa1, fb1);
+        mma(fa0, fb0);
+        if (k0 + 2 * kStep < Hq) load(k0 + 2 * kStep, fa0, fb0);
+        mma(fa1, fb1);
+      }
+    } else {
+      for (int k0 = 0; k0 < Hq; k0 += 16) {  // H / KS is a multiple of 16
+        bf16x8_t fa[1], fb[NB][1];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) fb[i][0] = *(const bf16x8_t*)(wb[i] + k0);
+        fa[0] = *(const bf16x8_t*)(xa + k0);
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[i][0], fa[0], acc[i], 0, 0, 0);
+      }
+    }
+    // acc[i][4g + q] is (token r, expert 32 eb + 8g + 4 (lane >> 5) + q): part KS-1 stores, the
+    // others add in descending part order
+    for (int pass = KS - 1; pass >= 0; --pass) {
+      if (kp == pass) {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
           const int eb = wave % 4 + 4 * i;
@@ -220,7 +239,7 @@ __global__ __launch_bounds__(kProjThreads) void route_proj_topk_kernel(
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               float* d = lg + r * ldl + eb * 32 + 8 * g + 4 * (lane >> 5) + q;
-              *d = pass ? acc[i][4 * g + q] : acc[i][4 * g + q] + *d;
+              *d = pass == KS - 1 ? acc[i][4 * g + q] : acc[i][4 * g + q] + *d;
             }
         }
       }
@@ -228,21 +247,23 @@ __global__ __launch_bounds__(kProjThreads) void route_proj_topk_kernel(
     }
   } else {
     __syncthreads();
-    __syncthreads();
   }
-  // top-K: 32 tokens x 16 lanes
-  const int q = tid & (kGroup - 1), tl = tid / kGroup;
-  const bool valid = tl < ntok;
-  uint64_t sel[K];
-  select_topk<K>(valid ? lg + tl * ldl : nullptr, E, q, sel);
-  if (valid && q < K) emit_topk<K>(sel, q, tb + tl, topk_idx, gates, hist + (tl / kHistTok) * E);
+  // top-K: 16 lanes per token, kThreads / 16 tokens per round
+  const int q = tid & (kGroup - 1);
+  for (int tl0 = 0; tl0 < kProjTok; tl0 += kThreads / kGroup) {
+    const int tl = tl0 + tid / kGroup;
+    const bool valid = tl < ntok;
+    uint64_t sel[K];
+    select_topk<K>(valid ? lg + tl * ldl : nullptr, E, q, sel);
+    if (valid && q < K) emit_topk<K>(sel, q, tb + tl, topk_idx, gates, hist + (tl / kHistTok) * E);
+  }
   if (logits)
-    for (int i = tid; i < ntok * E; i += kProjThreads)
+    for (int i = tid; i < ntok * E; i += kThreads)
       logits[(tb + i / E) * (int64_t)E + i % E] = lg[(i / E) * ldl + i % E];
   __syncthreads();
   // this block's two 16-token histograms, expert-major
   const int nh = 2 * nb32;
-  for (int i = tid; i < 2 * E; i += kProjThreads)
+  for (int i = tid; i < 2 * E; i += kThreads)
     block_hist[((int64_t)c * E + i % E) * nh + 2 * bl + i / E] = hist[i];
 }
 
@@ -368,20 +389,20 @@ hipError_t launch_route_x(const void* x, const void* w_r, float* logits, int32_t
   const int nb32 = route_blocks_per_chunk(T, n) * (kRouteBlock / kProjTok);
   const int NB = (E + 127) / 128;
   const size_t lds = route_x_lds_bytes(E);
-  dim3 grid(nb32 * nchunks), block(kProjThreads);
+  dim3 grid(nb32 * nchunks);
   {
     MOE_TRACE("route_proj_topk", s);
     switch (K * 8 + NB) {
-#define MOE_RX(KK, NN)                                                                                 \
+#define MOE_RX(KK, NN, KS)                                                                             \
   case KK * 8 + NN: {                                                                                 \
-    auto k = route_proj_topk_kernel<KK, NN>;                                                          \
+    auto k = route_proj_topk_kernel<KK, NN, KS>;                                                      \
     hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
     if (e != hipSuccess) return e;                                                                    \
-    hipLaunchKernelGGL(k, grid, block, lds, s, (const __bf16*)x, (const __bf16*)w_r, logits, topk_idx,   \
-                       gates, scratch, T, E, H, n, chunk0, nb32);                                      \
+    hipLaunchKernelGGL(k, grid, dim3(256 * KS), lds, s, (const __bf16*)x, (const __bf16*)w_r, logits,  \
+                       topk_idx, gates, scratch, T, E, H, n, chunk0, nb32);                            \
     break;                                                                                            \
   }
-#define MOE_RX_K(KK) MOE_RX(KK, 1) MOE_RX(KK, 2) MOE_RX(KK, 3) MOE_RX(KK, 4)
+#define MOE_RX_K(KK) MOE_RX(KK, 1, 4) MOE_RX(KK, 2, 2) MOE_RX(KK, 3, 1) MOE_RX(KK, 4, 1)
       MOE_RX_K(1) MOE_RX_K(2) MOE_RX_K(3) MOE_RX_K(4) MOE_RX_K(5) MOE_RX_K(6) MOE_RX_K(7) MOE_RX_K(8)
 #undef MOE_RX_K
 #undef MOE_RX
