@@ -216,9 +216,11 @@ moe_status moe_stash_load(const void* pool, const float* pool_scale, int64_t liv
 /* ---------------------------------------------------------------------------------------
  * Layer primitives (ChunkedEP "Summary": forward, backward, fused forward/backward). They
  * own the two-stream chunk schedule: routing and dispatch of chunk c+1 on `aux` overlap the
- * expert GEMMs of chunk c on `compute`; combine of chunk c runs on `aux` after them. On return
- * all work is ordered before later work on `compute`. Both streams must be distinct, at the
- * default priority.
+ * expert GEMMs of chunk c on `compute`, and combine of chunk c runs on `aux` after them. The
+ * first chunk's routing and dispatch, the last chunk's combine and the first chunk's combine
+ * backward run on `compute`, which waits on `aux` only where it consumes aux work. On return
+ * all work is ordered before later work on `compute`. Both streams at the default priority;
+ * with compute == aux everything runs in issue order on that one stream.
  * ------------------------------------------------------------------------------------- */
 typedef struct moe_tensors {
   /* inputs */
