@@ -423,7 +423,9 @@ static moe_status check_fwd_tensors(const moe_desc* d, const moe_tensors* t) {
   if (!t) return fail(MOE_ERR_ARG, "tensors is NULL");
   MOE_NEED(t->counts); MOE_NEED(t->offsets); MOE_NEED(t->workspace);
   if (d->T > 0) {
-    MOE_NEED(t->x); MOE_NEED(t->logits); MOE_NEED(t->topk_idx); MOE_NEED(t->gates); MOE_NEED(t->row_of);
+    MOE_NEED(t->x); MOE_NEED(t->topk_idx); MOE_NEED(t->gates); MOE_NEED(t->row_of);
+    if (!t->logits && !t->w_r)
+      return fail(MOE_ERR_ARG, "layer: logits and w_r are both NULL (one of them routes the tokens)");
     MOE_NEED(t->out);
   }
   if (rows_of(d) > 0) {
@@ -441,6 +443,16 @@ static moe_status check_bwd_tensors(const moe_desc* d, const moe_tensors* t) {
     MOE_NEED(t->gu); MOE_NEED(t->dyd); MOE_NEED(t->dgu); MOE_NEED(t->dxd); MOE_NEED(t->dw1); MOE_NEED(t->dw2);
   }
   return MOE_OK;
+}
+
+// Routing of one chunk in a layer primitive: from the given logits, or (logits NULL) from x and
+// the router weight with the projection fused into the top-k.
+static moe_status route_any(const moe_desc* d, int c, const moe_tensors* t, hipStream_t s) {
+  if (t->logits)
+    return moe_route(d, c, t->logits, t->topk_idx, t->gates, t->counts, t->offsets, t->row_of, t->src_token,
+                     t->workspace, s);
+  return moe_route_x(d, c, t->x, t->w_r, nullptr, t->topk_idx, t->gates, t->counts, t->offsets, t->row_of,
+                     t->src_token, t->workspace, s);
 }
 
 // Two-stream schedules. A wait of one stream on the other's event costs the waiting stream
@@ -464,8 +476,7 @@ static moe_status forward_sched(const moe_desc* d, const moe_tensors* t, hipStre
   hipEvent_t* disp = ev;       // n events: dispatch of chunk c done
   hipEvent_t* ffn = ev + n;    // n events: expert FFN of chunk c done
   hipEvent_t done = ev[2 * n];
-  MOE_TRY(moe_route(d, 0, t->logits, t->topk_idx, t->gates, t->counts, t->offsets, t->row_of, t->src_token,
-                    t->workspace, cs));
+  MOE_TRY(route_any(d, 0, t, cs));
   MOE_TRY(moe_dispatch(d, 0, t->x, t->row_of, t->xd, t->xd_scale, t->h_scale, cs));
   if (two) {
     MOE_HIP(hipEventRecord(disp[0], cs), "hipEventRecord");
@@ -474,8 +485,7 @@ static moe_status forward_sched(const moe_desc* d, const moe_tensors* t, hipStre
   for (int c = 0; c < n; ++c) {
     const hipStream_t side = two ? as : cs;
     if (c + 1 < n) {
-      MOE_TRY(moe_route(d, c + 1, t->logits, t->topk_idx, t->gates, t->counts, t->offsets, t->row_of,
-                        t->src_token, t->workspace, side));
+      MOE_TRY(route_any(d, c + 1, t, side));
       MOE_TRY(moe_dispatch(d, c + 1, t->x, t->row_of, t->xd, t->xd_scale, t->h_scale, side));
       if (two) MOE_HIP(hipEventRecord(disp[c + 1], as), "hipEventRecord");
     }

@@ -6,8 +6,8 @@
 // A tile is up to kTileRows rows of one logical page, so each tile reads its page-table entry
 // once (a scalar load) and all its addresses are one 64-bit base plus row/column offsets. Each
 // 256-thread block walks tiles grid-stride; the grid is capped (max_ctas) so the copy can share the
-// GPU with compute. Rows move as 16-byte vectors, four rows' loads in flight per thread before
-// their stores. The pool may be device memory or pinned host memory.
+// GPU with compute. Rows move as 16-byte vectors, a full tile's loads (eight rows) in flight per
+// thread before their stores. The pool may be device memory or pinned host memory.
 #include <type_traits>
 
 #include "common.h"
@@ -18,19 +18,19 @@ namespace moe {
 namespace {
 
 constexpr int kStashThreads = 256;
-constexpr int kTileRows = 16;
+constexpr int kTileRows = 8;
 
 // Copy `rows` rows of nvec 16-byte vectors: src row i -> dst row i (row strides in vectors).
 MOE_DEV void copy_rows(const u32x4* __restrict__ src, u32x4* __restrict__ dst, int rows, int64_t nvec) {
   const int tid = threadIdx.x;
   int r = 0;
-  for (; r + 4 <= rows; r += 4) {
+  for (; r + kTileRows <= rows; r += kTileRows) {
     for (int64_t v = tid; v < nvec; v += kStashThreads) {
-      u32x4 a[4];
+      u32x4 a[kTileRows];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) a[u] = src[(int64_t)(r + u) * nvec + v];
+      for (int u = 0; u < kTileRows; ++u) a[u] = src[(int64_t)(r + u) * nvec + v];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) dst[(int64_t)(r + u) * nvec + v] = a[u];
+      for (int u = 0; u < kTileRows; ++u) dst[(int64_t)(r + u) * nvec + v] = a[u];
     }
   }
   for (; r < rows; ++r)

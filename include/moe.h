@@ -220,7 +220,8 @@ moe_status moe_stash_load(const void* pool, const float* pool_scale, int64_t liv
  * first chunk's routing and dispatch, the last chunk's combine and the first chunk's combine
  * backward run on `compute`, which waits on `aux` only where it consumes aux work. On return
  * all work is ordered before later work on `compute`. Both streams at the default priority;
- * with compute == aux everything runs in issue order on that one stream.
+ * with compute == aux everything runs in issue order on that one stream. With `logits` NULL the
+ * forward routes from x and `w_r` (moe_route_x; BF16 or FP8 descriptor, E % 32 == 0, E <= 512).
  * ------------------------------------------------------------------------------------- */
 typedef struct moe_tensors {
   /* inputs */

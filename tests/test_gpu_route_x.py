@@ -96,3 +96,35 @@ def test_route_x_rejects_unsupported_shapes():
     d = mh.make_desc(T=64, H=128, I=64, E=48, E_local=4, k=2, n_chunks=1, dtype="bf16")
     with pytest.raises(mh.MoeError):
         mh.moe_route_x(d, -1, 1 << 20, 1 << 20, None, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20)
+
+
+def test_layer_routes_from_x_when_logits_are_null():
+    """The fused layer primitive with logits NULL (routing from x and W_r) gives bitwise the
+    results of the same primitive fed the logits that moe_route_x returns."""
+    torch, mh = _require_gpu()
+    cfg = MoeConfig("rx_layer", T=2048, H=512, I=256, E=64, E_local=8, e0=8, k=4, n_chunks=2, dtype="bf16",
+                    seed_base=740, backward=True)
+    inp = moe_inputs.make_inputs(cfg, with_backward=True)
+    d = mh.make_desc(T=cfg.T, H=cfg.H, I=cfg.I, E=cfg.E, E_local=cfg.E_local, k=cfg.k, n_chunks=cfg.n_chunks,
+                     dtype="bf16", e0=cfg.e0)
+    dev = {n: torch.from_numpy(inp[n + "_bits"].view(np.int16)).cuda().view(torch.bfloat16)
+           for n in ("x", "w1", "w2", "w_r", "dy")}
+    r = _route_bufs(torch, mh, d, cfg)
+    mh.moe_route_x(d, -1, dev["x"], dev["w_r"], r["logits"], r["topk_idx"], r["gates"], r["counts"], r["offsets"],
+                   r["row_of"], r["src_token"], r["workspace"])
+
+    def run(logits):
+        b = mh.allocate(d, backward=True)
+        b.update(dev)
+        b["logits"] = logits
+        cs, aux = torch.cuda.Stream(), torch.cuda.Stream()
+        mh.moe_layer_forward_backward(d, b, cs, aux)
+        torch.cuda.synchronize()
+        res = {k: b[k].cpu() for k in ("topk_idx", "gates", "row_of", "dx", "dw1", "dw2", "dwr", "dlogits")}
+        res["out"] = b["out"][:cfg.T].cpu()
+        return res
+
+    a, c = run(r["logits"]), run(None)
+    for k in a:
+        assert torch.equal(a[k].view(torch.int16) if a[k].dtype == torch.bfloat16 else a[k],
+                           c[k].view(torch.int16) if c[k].dtype == torch.bfloat16 else c[k]), k
