@@ -44,8 +44,7 @@ KERNEL_SYMBOLS = {
     "gemm_down": ("grouped_gemm.hip", "rows_kernel<256, 256, 1, false>"),
     "gemm_down_dgrad_swiglu": ("grouped_gemm.hip", "rows_kernel<256, 128, 2, false>"),
     "gemm_gateup_dgrad": ("grouped_gemm.hip", "rows_kernel<256, 256, 3, false>"),
-    "gemm_wgrad_down": ("grouped_gemm.hip", "wgrad_kernel<256, 128>"),
-    "gemm_wgrad_gateup": ("grouped_gemm.hip", "wgrad_kernel<256, 256>"),
+    "gemm_wgrad": ("grouped_gemm.hip", "wgrad_kernel<256, 256>"),
     "gemm_router_wgrad": ("gemm.hip", "router_wgrad_kernel"),
     "router_reduce": ("gemm.hip", "reduce_partials_kernel"),
 }
@@ -132,7 +131,7 @@ def committed_traffic(name: str):
 
 
 GEMM_KERNELS = {"gemm_gateup_swiglu", "gemm_down", "gemm_down_dgrad_swiglu", "gemm_gateup_dgrad",
-                "gemm_wgrad_down", "gemm_wgrad_gateup", "gemm_router_wgrad"}
+                "gemm_wgrad", "gemm_router_wgrad"}
 
 
 def algorithmic_work(cfg, counts, offsets, k_sel_local_tokens):
@@ -148,8 +147,7 @@ def algorithmic_work(cfg, counts, offsets, k_sel_local_tokens):
         "gemm_down": (2.0 * N * I * H, "flop"),
         "gemm_down_dgrad_swiglu": (2.0 * N * H * I, "flop"),
         "gemm_gateup_dgrad": (2.0 * N * 2 * I * H, "flop"),
-        "gemm_wgrad_down": (2.0 * N * H * I, "flop"),
-        "gemm_wgrad_gateup": (2.0 * N * 2 * I * H, "flop"),
+        "gemm_wgrad": (2.0 * N * H * I + 2.0 * N * 2 * I * H, "flop"),  # dW2 and dW1, one launch
         "gemm_router_wgrad": (2.0 * T * E * H, "flop"),
         "route_topk": (T * E * 4 + T * k * 8, "byte"),
         "route_layout": (T * k * 8 + cfg.n_chunks * 0 + N * 4, "byte"),
@@ -175,8 +173,7 @@ def gemm_bytes(cfg, N):
         "gemm_down": N * I * s + n * w2 + N * H * s,
         "gemm_down_dgrad_swiglu": N * H * s + n * w2 + 2 * N * 2 * I * s,
         "gemm_gateup_dgrad": N * 2 * I * s + n * w1 + N * H * s,
-        "gemm_wgrad_down": N * H * s + N * I * s + w2,
-        "gemm_wgrad_gateup": N * 2 * I * s + N * H * s + w1,
+        "gemm_wgrad": (N * H * s + N * I * s + w2) + (N * 2 * I * s + N * H * s + w1),
     }
 
 

@@ -448,7 +448,7 @@ static moe_status check_bwd_tensors(const moe_desc* d, const moe_tensors* t) {
 // Routing of one chunk in a layer primitive: from the given logits, or (logits NULL) from x and
 // the router weight with the projection fused into the top-k.
 static moe_status route_any(const moe_desc* d, int c, const moe_tensors* t, hipStream_t s) {
-  if (t->logits)
+  if (t->logits || d->T == 0)
     return moe_route(d, c, t->logits, t->topk_idx, t->gates, t->counts, t->offsets, t->row_of, t->src_token,
                      t->workspace, s);
   return moe_route_x(d, c, t->x, t->w_r, nullptr, t->topk_idx, t->gates, t->counts, t->offsets, t->row_of,

@@ -588,61 +588,78 @@ constexpr size_t wgrad_lds_bytes() {
   return ring > ep ? ring : ep;
 }
 
+// One weight-gradient tile: C[grp][m0.., n0..] = sum over the rows of every chunk of expert grp
+// of A_rows^T B_rows (both operands K-slow), one FP32 K loop, one BF16 store.
 template <int BM, int BN>
-__global__ __launch_bounds__(kThreads) void wgrad_kernel(WgradArgs a) {
+MOE_DEV void wgrad_tile(const WgradArgs& a, int tile, char* ring, int tid, int lane, int wave) {
   constexpr int WTM = BM / kWM, WTN = BN / kWN, TM = WTM / 32, TN = WTN / 32;
+  const int wm = wave / kWN, wn = wave % kWN;
+  const int mtiles = (a.M + BM - 1) / BM, ntiles = (a.N + BN - 1) / BN;
+  const int grp = tile / (mtiles * ntiles);
+  const int t_in = tile % (mtiles * ntiles);
+  const int m0 = (t_in / ntiles) * BM, n0 = (t_in % ntiles) * BN;
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[tm][tn][q] = 0.f;
+
+  for (int c = 0; c < a.n_chunks; ++c) {
+    const int32_t* off = a.offsets + (int64_t)c * (a.El + 1);
+    const int64_t row0 = (int64_t)c * a.P_c + off[grp];
+    const int len = __builtin_amdgcn_readfirstlane(off[grp + 1] - off[grp]);
+    if (len <= 0) continue;
+    Loader<BM, true> la;
+    la.init_kslow(a.A + row0 * a.lda + m0, a.lda * 2, ((int64_t)len * a.lda - m0) * 2, wave, lane);
+    Loader<BN, true> lb;
+    lb.init_kslow(a.B + row0 * a.ldb + n0, a.ldb * 2, ((int64_t)len * a.ldb - n0) * 2, wave, lane);
+    const int nks = (len + kKRows - 1) / kKRows;
+    kloop<false, true, true, BM, BN, TM, TN, TM>(la, lb, ring, nks, wm * WTM, wn * WTN, lane, acc);
+  }
+
+  const int mrow = wm * WTM + out_row(lane);
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int nl = wn * WTN + tn * 32 + out_col(gq, lane);
+        const f32x16_t& v = acc[tm][tn];
+        *(uint2*)(ring + (mrow + tm * 32) * pitch<BN>() + 2 * nl) =
+            pack4(v[4 * gq], v[4 * gq + 1], v[4 * gq + 2], v[4 * gq + 3]);
+      }
+  lds_barrier();
+  store_staged<BM, BN>(ring, a.C + (int64_t)grp * a.strideC + (int64_t)m0 * a.N + n0, a.N,
+                       min(BM, a.M - m0), min(BN, a.N - n0), tid);
+  lds_barrier();
+}
+
+template <int BM, int BN>
+MOE_DEV int wgrad_tiles(const WgradArgs& a) { return a.El * ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN); }
+
+// Persistent over the tiles of up to two independent weight gradients in one launch (b.El = 0:
+// none), so the second fills the first one's last round. Each XCD owns a contiguous range of
+// a's tiles and one of b's, and walks them in that order.
+template <int BM, int BN>
+__global__ __launch_bounds__(kThreads) void wgrad_kernel(WgradArgs a, WgradArgs b) {
   extern __shared__ __attribute__((aligned(1024))) char ring[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / kWN, wn = wave % kWN;
-  const int mtiles = (a.M + BM - 1) / BM, ntiles = (a.N + BN - 1) / BN;
-  const int total = a.El * mtiles * ntiles;
-  const int per_xcd = (total + 7) / 8;
+  const int ta = wgrad_tiles<BM, BN>(a), tb = b.El > 0 ? wgrad_tiles<BM, BN>(b) : 0;
+  const int pxa = (ta + 7) / 8, pxb = (tb + 7) / 8;
   const int xcd = blockIdx.x % 8, wg_per_xcd = gridDim.x / 8;
-  for (int slot = blockIdx.x / 8; slot < per_xcd; slot += wg_per_xcd) {
-    const int tile = xcd * per_xcd + slot;
-    if (tile >= total) break;
-    const int grp = tile / (mtiles * ntiles);
-    const int t_in = tile % (mtiles * ntiles);
-    const int m0 = (t_in / ntiles) * BM, n0 = (t_in % ntiles) * BN;
-
-    f32x16_t acc[TM][TN];
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) acc[tm][tn][q] = 0.f;
-
-    for (int c = 0; c < a.n_chunks; ++c) {
-      const int32_t* off = a.offsets + (int64_t)c * (a.El + 1);
-      const int64_t row0 = (int64_t)c * a.P_c + off[grp];
-      const int len = __builtin_amdgcn_readfirstlane(off[grp + 1] - off[grp]);
-      if (len <= 0) continue;
-      Loader<BM, true> la;
-      la.init_kslow(a.A + row0 * a.lda + m0, a.lda * 2, ((int64_t)len * a.lda - m0) * 2, wave, lane);
-      Loader<BN, true> lb;
-      lb.init_kslow(a.B + row0 * a.ldb + n0, a.ldb * 2, ((int64_t)len * a.ldb - n0) * 2, wave, lane);
-      const int nks = (len + kKRows - 1) / kKRows;
-      kloop<false, true, true, BM, BN, TM, TN, TM>(la, lb, ring, nks, wm * WTM, wn * WTN, lane, acc);
+  for (int slot = blockIdx.x / 8; slot < pxa + pxb; slot += wg_per_xcd) {
+    if (slot < pxa) {
+      const int tile = xcd * pxa + slot;
+      if (tile < ta) wgrad_tile<BM, BN>(a, tile, ring, tid, lane, wave);
+    } else {
+      const int tile = xcd * pxb + (slot - pxa);
+      if (tile < tb) wgrad_tile<BM, BN>(b, tile, ring, tid, lane, wave);
     }
-
-    const int mrow = wm * WTM + out_row(lane);
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int nl = wn * WTN + tn * 32 + out_col(gq, lane);
-          const f32x16_t& v = acc[tm][tn];
-          *(uint2*)(ring + (mrow + tm * 32) * pitch<BN>() + 2 * nl) =
-              pack4(v[4 * gq], v[4 * gq + 1], v[4 * gq + 2], v[4 * gq + 3]);
-        }
-    lds_barrier();
-    store_staged<BM, BN>(ring, a.C + (int64_t)grp * a.strideC + (int64_t)m0 * a.N + n0, a.N,
-                         min(BM, a.M - m0), min(BN, a.N - n0), tid);
-    lds_barrier();
   }
 }
 
@@ -690,17 +707,19 @@ hipError_t run_rows(const char* name, const RowsArgs& a, hipStream_t s) {
 }
 
 template <int BM, int BN>
-hipError_t run_wgrad(const char* name, const WgradArgs& a, hipStream_t s) {
+hipError_t run_wgrad(const char* name, const WgradArgs& a, const WgradArgs& b, hipStream_t s) {
   const size_t lds = wgrad_lds_bytes<BM, BN>();
   auto k = wgrad_kernel<BM, BN>;
   hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  const int64_t total = (int64_t)a.El * ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  const int64_t grid = persistent_grid(total);
+  auto tiles = [](const WgradArgs& w) {
+    return w.El > 0 ? (int64_t)w.El * ((w.M + BM - 1) / BM) * ((w.N + BN - 1) / BN) : 0;
+  };
+  const int64_t grid = persistent_grid(tiles(a) + tiles(b));
   if (grid <= 0) return hipSuccess;
   {
     MOE_TRACE(name, s);
-    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kThreads), lds, s, a);
+    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kThreads), lds, s, a, b);
   }
   return hipGetLastError();
 }
@@ -748,13 +767,12 @@ hipError_t gg_expert_wgrad_bf16(const void* dyd, const void* dgu, const void* xd
   WgradArgs a{};
   a.A = (const uint16_t*)dyd; a.B = (const uint16_t*)h; a.C = (uint16_t*)dw2; a.lda = H; a.ldb = I;
   a.strideC = (int64_t)H * I; a.M = H; a.N = I; a.offsets = offsets; a.El = El; a.n_chunks = n; a.P_c = P_c;
-  hipError_t e = run_wgrad<256, 128>("gemm_wgrad_down", a, s);
-  if (e != hipSuccess) return e;
   // dW1[e] [2I, H] = sum dgu^T xd
   WgradArgs b{};
   b.A = (const uint16_t*)dgu; b.B = (const uint16_t*)xd; b.C = (uint16_t*)dw1; b.lda = 2 * I; b.ldb = H;
   b.strideC = (int64_t)2 * I * H; b.M = 2 * I; b.N = H; b.offsets = offsets; b.El = El; b.n_chunks = n; b.P_c = P_c;
-  return run_wgrad<256, 256>("gemm_wgrad_gateup", b, s);
+  // both in one launch: dW1's tiles (the longer list) first, dW2's fill the last round
+  return run_wgrad<256, 256>("gemm_wgrad", b, a, s);
 }
 
 // FP8 forward: gate/up on FP8 MFMA with s_row * s_col dequantisation and SwiGLU -> h (BF16);

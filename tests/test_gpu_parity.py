@@ -173,7 +173,7 @@ def test_backward_launch_order_input_grad_before_wgrad():
     def streams_of(kind):
         return [s for n, s, _ in log if n == kind]
     compute = streams_of("gemm_gateup_swiglu")[0]
-    assert set(streams_of("gemm_gateup_swiglu") + streams_of("gemm_wgrad_gateup")) == {compute}
+    assert set(streams_of("gemm_gateup_swiglu") + streams_of("gemm_wgrad")) == {compute}
     disp, comb = streams_of("dispatch"), streams_of("combine")
     assert disp[0] == compute and comb[-1] == compute
     aux = disp[1]
