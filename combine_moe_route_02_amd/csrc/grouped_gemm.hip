@@ -751,7 +751,7 @@ hipError_t gg_expert_dgrad_bf16(const void* dyd, const void* gu, const void* w1,
   a.A = dyd; a.B = w2; a.C = (uint16_t*)dgu; a.aux = (const uint16_t*)gu;
   a.lda = H; a.ldc = 2 * I; a.strideB = (int64_t)H * I; a.K = H; a.N = I; a.I = I;
   a.offsets = offsets; a.El = El; a.c0 = c0; a.nc = nc; a.P_c = P_c;
-  hipError_t e = run_rows<256, 128, kDownBwd, false>("gemm_down_dgrad_swiglu", a, s);
+  hipError_t e = run_rows<128, 256, kDownBwd, false>("gemm_down_dgrad_swiglu", a, s);
   if (e != hipSuccess) return e;
   RowsArgs b{};
   b.A = dgu; b.B = w1; b.C = (uint16_t*)dxd;
