@@ -209,8 +209,8 @@ moe_status moe_route_x(const moe_desc* d, int chunk, const void* x, const void* 
   MOE_TRY(validate(d));
   MOE_TRY(check_chunk(d, chunk));
   if (d->dtype == MOE_F32) return fail(MOE_ERR_UNSUPPORTED, "moe_route_x: x and W_r must be BF16 (dtype BF16 or FP8)");
-  if (d->E % 32 || d->E > 512)
-    return fail(MOE_ERR_UNSUPPORTED, "moe_route_x: E = %d must be a multiple of 32, at most 512", d->E);
+  if (d->E % 32 || d->E > 256)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_route_x: E = %d must be a multiple of 32, at most 256", d->E);
   if (d->T > 0) { MOE_NEED(x); MOE_NEED(w_r); MOE_NEED(topk_idx); MOE_NEED(gates); MOE_NEED(row_of); }
   if (rows_of(d) > 0) MOE_NEED(src_token);
   MOE_NEED(counts); MOE_NEED(offsets); MOE_NEED(workspace);

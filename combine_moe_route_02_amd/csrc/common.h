@@ -59,6 +59,23 @@ MOE_DEV float wave_max(float v) {
   return v;
 }
 
+// Raw buffer descriptor over [base, base + bytes): loads at offsets past `bytes` return zero
+// without touching memory (the extent masks rows past a segment or a matrix edge).
+typedef __attribute__((address_space(3))) void lds_void_t;
+MOE_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int64_t lim = 0x7fffffff;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0,
+                                           (int)(bytes < 0 ? 0 : (bytes > lim ? lim : bytes)),
+                                           0x00020000);  // gfx9 raw buffer descriptor word 3
+}
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+MOE_DEV void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Token range of chunk c (chunks of ceil(T/n) tokens, the last takes the remainder).
 struct ChunkRange { int64_t t0, t1; };
 MOE_DEV ChunkRange chunk_range(int64_t T, int n, int c) {

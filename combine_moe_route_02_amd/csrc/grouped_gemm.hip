@@ -47,24 +47,8 @@ constexpr int kRowB = 64;           // K bytes per MN row per stage
 constexpr int kKRows = 32;          // K rows per stage for 16-bit K-slow operands
 constexpr int kMaxGroups = 1024;
 
-typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((ext_vector_type(8))) int i32x8_t;
-
-MOE_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int64_t lim = 0x7fffffff;
-  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0,
-                                           (int)(bytes < 0 ? 0 : (bytes > lim ? lim : bytes)),
-                                           0x00020000);  // gfx9 raw buffer descriptor word 3
-}
-
-// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt in bits 3:0 and
-// 15:14, expcnt 6:4, lgkmcnt 11:8).
-template <int N>
-MOE_DEV void wait_vm() {
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 // LDS byte offset of 16-byte chunk c of row r in a K-major stage.
 MOE_DEV int km_off(int r, int c) { return r * kRowB + ((c ^ ((r >> 2) & 3)) << 4); }

@@ -11,7 +11,7 @@ namespace moe {
 int route_blocks_per_chunk(int64_t T, int n);
 int64_t route_scratch_bytes(int64_t T, int n, int E);
 // routing from x: logits = x . W_r^T (BF16 MFMA, FP32 accumulation) fused with the top-k, then
-// the layout kernel; logits may be NULL. Needs E % 32 == 0, E <= 512.
+// the layout kernel; logits may be NULL. Needs E % 32 == 0, E <= 256.
 hipError_t launch_route_x(const void* x, const void* w_r, float* logits, int32_t* topk_idx, float* gates,
                           int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* src_token,
                           int32_t* scratch, int64_t T, int E, int H, int e0, int El, int K, int n, int chunk0,

@@ -152,83 +152,96 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
   for (int e = tid; e < E; e += kTopkThreads) out[(int64_t)e * nbpc] = hist[e];
 }
 
-// Router projection fused with the top-K: logits = x . W_r^T for 32 tokens and all E experts on
-// BF16 MFMA with FP32 accumulation, then the same selection as route_topk from LDS. 4 * KS waves:
-// wave w takes the 32-expert blocks w % 4, w % 4 + 4, ... (NB of them) over K part w / 4 of KS;
-// the KS partial tiles are added in LDS in a fixed order (part KS-1 first, part 0 last). Operands
-// come straight from global memory (x rows once per block, W_r from L2) in batches of four
-// 16-wide K steps, double-buffered: the next batch's loads are in flight while this one's MFMAs
-// run.
+// Router projection fused with the top-K: logits = x . W_r^T for 32 tokens and all E experts
+// (E <= 256) on BF16 MFMA with FP32 accumulation, then the same selection as route_topk from LDS.
+// The K loop streams 64-wide K stages of the 32 x rows and the E W_r rows through a 4-stage LDS
+// ring with direct-to-LDS 16-byte loads: one wave instruction moves 8 whole 128-byte row
+// segments, and each stage holds (32 + E) rows of 128 bytes whose 16-byte chunks are
+// XOR-swizzled by (row & 7), so the 32-row fragment reads hit every bank once. Loads run three
+// stages ahead with one barrier per stage, spread over all eight waves (a wave issues these
+// loads at only a few bytes per clock). Wave w multiplies the 32-expert blocks w % 4,
+// w % 4 + 4, ... over the K steps 2 (w / 4), 2 (w / 4) + 1 of each stage; the two partial tiles
+// are added in LDS in a fixed order.
 constexpr int kProjTok = 32;
+constexpr int kRxThreads = 512;
+constexpr int kRxNst = 4;        // LDS ring stages
+constexpr int kRxRowB = 128;     // bytes of K per row per stage (64 BF16)
 
-template <int K, int NB, int KS>
-__global__ __launch_bounds__(256 * KS) void route_proj_topk_kernel(
+MOE_DEV int rx_off(int row, int chunk) { return row * kRxRowB + ((chunk ^ (row & 7)) << 4); }
+
+template <int N>
+MOE_DEV void rx_wait(int loads_per_stage) {  // vmcnt(2 * loads_per_stage), 1 <= loads_per_stage <= N
+  if (loads_per_stage >= N) { wait_vm<2 * N>(); return; }
+  if constexpr (N > 1) rx_wait<N - 1>(loads_per_stage);
+}
+
+template <int K, int NB>
+__global__ __launch_bounds__(kRxThreads) void route_proj_topk_kernel(
     const __bf16* __restrict__ x, const __bf16* __restrict__ w_r, float* __restrict__ logits,
     int32_t* __restrict__ topk_idx, float* __restrict__ gates, int32_t* __restrict__ block_hist, int64_t T,
     int E, int H, int n, int chunk0, int nb32) {
-  constexpr int kThreads = 256 * KS, NS = 4;
-  extern __shared__ __attribute__((aligned(16))) float lg[];  // [kProjTok][E + 4], then int [2][E]
+  extern __shared__ __attribute__((aligned(1024))) char rx_smem[];
+  char* smem = rx_smem;
+  const int SS = (kProjTok + E) * kRxRowB;        // stage bytes
+  int* hist = (int*)(smem + kRxNst * SS);          // [2][E], outside the ring
+  float* lg = (float*)smem;                        // [kProjTok][E + 4] logits, on the ring after the K loop
   const int ldl = E + 4;
-  int* hist = (int*)(lg + kProjTok * ldl);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = chunk0 + blockIdx.x / nb32, bl = blockIdx.x % nb32;
   const ChunkRange cr = chunk_range(T, n, c);
   const int64_t tb = cr.t0 + (int64_t)bl * kProjTok;  // first token of the block
   const int ntok = (int)max((int64_t)0, min((int64_t)kProjTok, cr.t1 - tb));
-  for (int e = tid; e < 2 * E; e += kThreads) hist[e] = 0;
-  const int neb = E / 32, kp = wave / 4, Hq = H / KS;
+  for (int e = tid; e < 2 * E; e += kRxThreads) hist[e] = 0;
+  const int neb = E / 32, kp = wave / 4;
+  const int r = lane & 31, h = lane >> 5;
   if (ntok > 0) {
-    // MFMA fragments: lane l holds rows l & 31 and K values 8 (l >> 5) .. +7 of each 16-wide step
-    const int r = lane & 31, h8 = 8 * (lane >> 5);
-    const __bf16* xa = x + (tb + min(r, ntok - 1)) * (int64_t)H + kp * Hq + h8;  // tail rows repeat
-    const __bf16* wb[NB];
-#pragma unroll
-    for (int i = 0; i < NB; ++i)
-      wb[i] = w_r + (int64_t)(min(wave % 4 + 4 * i, neb - 1) * 32 + r) * H + kp * Hq + h8;
+    // loads: the stage's M = (32 + E) / 8 wave instructions (8 rows each) are dealt round-robin
+    // to the 8 waves; rows 0..31 are x (masked past ntok), rows 32.. are W_r
+    const int M = (kProjTok + E) / 8;
+    const int mine = (M - wave + 7) / 8;           // this wave's instructions per stage (>= 1)
+    const __amdgpu_buffer_rsrc_t rsx = make_rsrc(x + tb * (int64_t)H, (int64_t)ntok * H * 2);
+    const __amdgpu_buffer_rsrc_t rsw = make_rsrc(w_r, (int64_t)E * H * 2);
+    auto issue = [&](int stage) {
+      char* slot = smem + (stage % kRxNst) * SS;
+      for (int q = wave; q < M; q += 8) {
+        const int row = 8 * q + (lane >> 3);
+        const int g = (lane & 7) ^ (row & 7);                 // global chunk this lane fetches
+        const bool isx = row < kProjTok;
+        const int grow = isx ? row : row - kProjTok;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(isx ? rsx : rsw, (lds_void_t*)(slot + q * 1024), 16,
+                                                 grow * H * 2 + g * 16, stage * kRxRowB, 0, 0);
+      }
+    };
     f32x16_t acc[NB];
 #pragma unroll
     for (int i = 0; i < NB; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
-    auto load = [&](int k0, bf16x8_t (&fa)[NS], bf16x8_t (&fb)[NB][NS]) {
+    const int nks = H / 64;
+    for (int s0 = 0; s0 < kRxNst - 1; ++s0) issue(s0);
+    for (int st = 0; st < nks; ++st) {
+      rx_wait<5>(mine);              // this wave's loads of stage st have landed (two younger in flight)
+      __builtin_amdgcn_s_barrier();  // stage st is in LDS for every wave; stage st-1 is consumed
+      issue(st + kRxNst - 1);        // into the slot of stage st-1 (past the end: masked or unused)
+      const char* slot = smem + (st % kRxNst) * SS;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) fa[s] = *(const bf16x8_t*)(xa + k0 + 16 * s);
+      for (int s = 2 * kp; s < 2 * kp + 2; ++s) {
+        const bf16x8_t fa = *(const bf16x8_t*)(slot + rx_off(r, 2 * s + h));
 #pragma unroll
-      for (int i = 0; i < NB; ++i)
-#pragma unroll
-        for (int s = 0; s < NS; ++s) fb[i][s] = *(const bf16x8_t*)(wb[i] + k0 + 16 * s);
-    };
-    auto mma = [&](const bf16x8_t (&fa)[NS], const bf16x8_t (&fb)[NB][NS]) {
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int i = 0; i < NB; ++i)
-          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[i][s], fa[s], acc[i], 0, 0, 0);
-    };
-    constexpr int kStep = 16 * NS;
-    if (Hq % (2 * kStep) == 0) {
-      bf16x8_t fa0[NS], fb0[NB][NS], fa1[NS], fb1[NB][NS];
-      load(0, fa0, fb0);
-      for (int k0 = 0; k0 < Hq; k0 += 2 * kStep) {
-        load(k0 + kStep, fa1, fb1);
-        mma(fa0, fb0);
-        if (k0 + 2 * kStep < Hq) load(k0 + 2 * kStep, fa0, fb0);
-        mma(fa1, fb1);
-      }
-    } else {
-      for (int k0 = 0; k0 < Hq; k0 += 16) {  // H / KS is a multiple of 16
-        bf16x8_t fa[1], fb[NB][1];
-#pragma unroll
-        for (int i = 0; i < NB; ++i) fb[i][0] = *(const bf16x8_t*)(wb[i] + k0);
-        fa[0] = *(const bf16x8_t*)(xa + k0);
-#pragma unroll
-        for (int i = 0; i < NB; ++i)
-          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[i][0], fa[0], acc[i], 0, 0, 0);
+        for (int i = 0; i < NB; ++i) {
+          const int eb = wave % 4 + 4 * i;
+          if (eb < neb) {
+            const bf16x8_t fb = *(const bf16x8_t*)(slot + rx_off(kProjTok + 32 * eb + r, 2 * s + h));
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb, fa, acc[i], 0, 0, 0);
+          }
+        }
       }
     }
-    // acc[i][4g + q] is (token r, expert 32 eb + 8g + 4 (lane >> 5) + q): part KS-1 stores, the
-    // others add in descending part order
-    for (int pass = KS - 1; pass >= 0; --pass) {
+    wait_vm<0>();
+    __syncthreads();  // ring free
+    // acc[i][4g + q] is (token r, expert 32 eb + 8g + 4 h + q): K part 1 stores, part 0 adds
+    for (int pass = 1; pass >= 0; --pass) {
       if (kp == pass) {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
@@ -238,8 +251,8 @@ __global__ __launch_bounds__(256 * KS) void route_proj_topk_kernel(
           for (int g = 0; g < 4; ++g)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              float* d = lg + r * ldl + eb * 32 + 8 * g + 4 * (lane >> 5) + q;
-              *d = pass == KS - 1 ? acc[i][4 * g + q] : acc[i][4 * g + q] + *d;
+              float* d = lg + r * ldl + eb * 32 + 8 * g + 4 * h + q;
+              *d = pass ? acc[i][4 * g + q] : acc[i][4 * g + q] + *d;
             }
         }
       }
@@ -248,22 +261,20 @@ __global__ __launch_bounds__(256 * KS) void route_proj_topk_kernel(
   } else {
     __syncthreads();
   }
-  // top-K: 16 lanes per token, kThreads / 16 tokens per round
+  // top-K: 16 lanes per token, all 32 tokens at once
   const int q = tid & (kGroup - 1);
-  for (int tl0 = 0; tl0 < kProjTok; tl0 += kThreads / kGroup) {
-    const int tl = tl0 + tid / kGroup;
-    const bool valid = tl < ntok;
-    uint64_t sel[K];
-    select_topk<K>(valid ? lg + tl * ldl : nullptr, E, q, sel);
-    if (valid && q < K) emit_topk<K>(sel, q, tb + tl, topk_idx, gates, hist + (tl / kHistTok) * E);
-  }
+  const int tl = tid / kGroup;
+  const bool valid = tl < ntok;
+  uint64_t sel[K];
+  select_topk<K>(valid ? lg + tl * ldl : nullptr, E, q, sel);
+  if (valid && q < K) emit_topk<K>(sel, q, tb + tl, topk_idx, gates, hist + (tl / kHistTok) * E);
   if (logits)
-    for (int i = tid; i < ntok * E; i += kThreads)
+    for (int i = tid; i < ntok * E; i += kRxThreads)
       logits[(tb + i / E) * (int64_t)E + i % E] = lg[(i / E) * ldl + i % E];
   __syncthreads();
   // this block's two 16-token histograms, expert-major
   const int nh = 2 * nb32;
-  for (int i = tid; i < 2 * E; i += kThreads)
+  for (int i = tid; i < 2 * E; i += kRxThreads)
     block_hist[((int64_t)c * E + i % E) * nh + 2 * bl + i / E] = hist[i];
 }
 
@@ -380,29 +391,29 @@ static hipError_t launch_layout(const int32_t* topk_idx, const int32_t* scratch,
   return hipGetLastError();
 }
 
-size_t route_x_lds_bytes(int E) { return (size_t)kProjTok * (E + 4) * 4 + (size_t)2 * E * 4; }
+size_t route_x_lds_bytes(int E) { return (size_t)kRxNst * (kProjTok + E) * kRxRowB + (size_t)2 * E * 4; }
 
 hipError_t launch_route_x(const void* x, const void* w_r, float* logits, int32_t* topk_idx, float* gates,
                           int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* src_token,
                           int32_t* scratch, int64_t T, int E, int H, int e0, int El, int K, int n, int chunk0,
                           int nchunks, int64_t P_c, hipStream_t s) {
   const int nb32 = route_blocks_per_chunk(T, n) * (kRouteBlock / kProjTok);
-  const int NB = (E + 127) / 128;
+  const int NB = (E + 127) / 128;  // 32-expert blocks per wave (E <= 256)
   const size_t lds = route_x_lds_bytes(E);
   dim3 grid(nb32 * nchunks);
   {
     MOE_TRACE("route_proj_topk", s);
     switch (K * 8 + NB) {
-#define MOE_RX(KK, NN, KS)                                                                             \
+#define MOE_RX(KK, NN)                                                                                 \
   case KK * 8 + NN: {                                                                                 \
-    auto k = route_proj_topk_kernel<KK, NN, KS>;                                                      \
+    auto k = route_proj_topk_kernel<KK, NN>;                                                          \
     hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
     if (e != hipSuccess) return e;                                                                    \
-    hipLaunchKernelGGL(k, grid, dim3(256 * KS), lds, s, (const __bf16*)x, (const __bf16*)w_r, logits,  \
+    hipLaunchKernelGGL(k, grid, dim3(kRxThreads), lds, s, (const __bf16*)x, (const __bf16*)w_r, logits, \
                        topk_idx, gates, scratch, T, E, H, n, chunk0, nb32);                            \
     break;                                                                                            \
   }
-#define MOE_RX_K(KK) MOE_RX(KK, 1, 4) MOE_RX(KK, 2, 2) MOE_RX(KK, 3, 1) MOE_RX(KK, 4, 1)
+#define MOE_RX_K(KK) MOE_RX(KK, 1) MOE_RX(KK, 2)
       MOE_RX_K(1) MOE_RX_K(2) MOE_RX_K(3) MOE_RX_K(4) MOE_RX_K(5) MOE_RX_K(6) MOE_RX_K(7) MOE_RX_K(8)
 #undef MOE_RX_K
 #undef MOE_RX

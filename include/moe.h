@@ -106,7 +106,7 @@ moe_status moe_route(const moe_desc* d, int chunk, const float* logits, int32_t*
  * x . W_r^T with BF16 x [T,H] and W_r [E,H], FP32 accumulation on MFMA, then the top-k of
  * moe_route on those logits, which stay in registers and LDS; `logits` (nullable, FP32 [T,E])
  * receives them. Every other argument and output is moe_route's. Needs a BF16 or FP8 descriptor
- * (x is BF16 in both) and E a multiple of 32, at most 512 (MOE_ERR_UNSUPPORTED otherwise). */
+ * (x is BF16 in both) and E a multiple of 32, at most 256 (MOE_ERR_UNSUPPORTED otherwise). */
 moe_status moe_route_x(const moe_desc* d, int chunk, const void* x, const void* w_r, float* logits,
                        int32_t* topk_idx, float* gates, int32_t* counts, int32_t* offsets, int32_t* row_of,
                        int32_t* src_token, void* workspace, void* stream);
@@ -221,7 +221,7 @@ moe_status moe_stash_load(const void* pool, const float* pool_scale, int64_t liv
  * backward run on `compute`, which waits on `aux` only where it consumes aux work. On return
  * all work is ordered before later work on `compute`. Both streams at the default priority;
  * with compute == aux everything runs in issue order on that one stream. With `logits` NULL the
- * forward routes from x and `w_r` (moe_route_x; BF16 or FP8 descriptor, E % 32 == 0, E <= 512).
+ * forward routes from x and `w_r` (moe_route_x; BF16 or FP8 descriptor, E % 32 == 0, E <= 256).
  * ------------------------------------------------------------------------------------- */
 typedef struct moe_tensors {
   /* inputs */
