@@ -261,15 +261,21 @@ template <int W> constexpr int pitch() { return W * 2 + 16; }
 template <int BM, int W> constexpr size_t stage_bytes() { return (size_t)BM * pitch<W>(); }
 
 // Store rows < mvalid and columns < nvalid (a multiple of 8) of a staged tile to dst (row stride
-// ld elements) with 16-byte writes: each wave instruction writes whole rows.
-template <int BM, int W>
+// ld elements) with 16-byte writes: each wave instruction writes whole rows. NT: non-temporal
+// stores, for outputs no kernel reads soon (saved G/U, weight gradients); measured faster there,
+// and slower for outputs the next kernel reads (h, yd, dG/dU, dxd), which stay normal.
+template <int BM, int W, bool NT = false>
 MOE_DEV void store_staged(const char* lds, uint16_t* dst, int64_t ld, int mvalid, int nvalid, int tid) {
   constexpr int CPR = W / 8, RPP = kThreads / CPR;
   const int c = tid % CPR;
 #pragma unroll 4
   for (int r = tid / CPR; r < BM; r += RPP)
-    if (r < mvalid && 8 * c < nvalid)
-      *(uint4*)(dst + (int64_t)r * ld + 8 * c) = *(const uint4*)(lds + r * pitch<W>() + 16 * c);
+    if (r < mvalid && 8 * c < nvalid) {
+      const i32x4_t v = *(const i32x4_t*)(lds + r * pitch<W>() + 16 * c);
+      i32x4_t* p = (i32x4_t*)(dst + (int64_t)r * ld + 8 * c);
+      if constexpr (NT) __builtin_nontemporal_store(v, p);
+      else *p = v;
+    }
 }
 
 // Load rows < mvalid, columns < nvalid of a [BM, W] BF16 tile from src into LDS staging.
@@ -459,8 +465,8 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(RowsArgs a) {
           }
       lds_barrier();
       if (a.C2) {
-        store_staged<BM, W>(sg, a.C2 + r0 * 2 * (int64_t)a.I + n0, 2 * (int64_t)a.I, mvalid, nvalid, tid);
-        store_staged<BM, W>(su, a.C2 + r0 * 2 * (int64_t)a.I + a.I + n0, 2 * (int64_t)a.I, mvalid, nvalid, tid);
+        store_staged<BM, W, true>(sg, a.C2 + r0 * 2 * (int64_t)a.I + n0, 2 * (int64_t)a.I, mvalid, nvalid, tid);
+        store_staged<BM, W, true>(su, a.C2 + r0 * 2 * (int64_t)a.I + a.I + n0, 2 * (int64_t)a.I, mvalid, nvalid, tid);
       }
       lds_barrier();
       // h = silu(G) * U from the FP32 accumulators
@@ -617,7 +623,7 @@ MOE_DEV void wgrad_tile(const WgradArgs& a, int tile, char* ring, int tid, int l
             pack4(v[4 * gq], v[4 * gq + 1], v[4 * gq + 2], v[4 * gq + 3]);
       }
   lds_barrier();
-  store_staged<BM, BN>(ring, a.C + (int64_t)grp * a.strideC + (int64_t)m0 * a.N + n0, a.N,
+  store_staged<BM, BN, true>(ring, a.C + (int64_t)grp * a.strideC + (int64_t)m0 * a.N + n0, a.N,
                        min(BM, a.M - m0), min(BN, a.N - n0), tid);
   lds_barrier();
 }
