@@ -466,7 +466,8 @@ static moe_status route_any(const moe_desc* d, int c, const moe_tensors* t, hipS
 //   compute: R0 D0 F0 | wait(disp1) F1 | ... | wait(disp n-1) F n-1, C n-1
 //   aux:     wait(disp0) R1 D1 | wait(ffn0) C0, R2 D2 | wait(ffn1) C1, R3 D3 | ...
 // Routing/dispatch of chunk c+1 overlaps the expert GEMMs of chunk c; combine c-1 overlaps F c.
-// With `join` the compute stream finally waits for the auxiliary stream.
+// With `join` the compute stream finally waits for the auxiliary stream. Without it (the fused
+// forward+backward) the last combine also runs on aux, beside the backward's first kernels.
 static moe_status forward_sched(const moe_desc* d, const moe_tensors* t, hipStream_t cs, hipStream_t as,
                                 bool join) {
   const int n = d->n_chunks;
@@ -492,7 +493,9 @@ static moe_status forward_sched(const moe_desc* d, const moe_tensors* t, hipStre
     if (two && c >= 1) MOE_HIP(hipStreamWaitEvent(cs, disp[c], 0), "hipStreamWaitEvent");
     MOE_TRY(moe_expert_ffn(d, c, t->xd, t->xd_scale, t->w1, t->w1_scale, t->w2, t->w2_scale, t->offsets,
                            t->gu, t->h, t->h_scale, t->yd, cs));
-    if (c + 1 < n) {
+    // combine on aux after this chunk's GEMMs; the last chunk's on compute when the forward
+    // ends here (join), on aux when the backward follows (nothing there reads `out`)
+    if (c + 1 < n || (two && !join)) {
       if (two) {
         MOE_HIP(hipEventRecord(ffn[c], cs), "hipEventRecord");
         MOE_HIP(hipStreamWaitEvent(as, ffn[c], 0), "hipStreamWaitEvent");

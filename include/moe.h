@@ -217,8 +217,9 @@ moe_status moe_stash_load(const void* pool, const float* pool_scale, int64_t liv
  * Layer primitives (ChunkedEP "Summary": forward, backward, fused forward/backward). They
  * own the two-stream chunk schedule: routing and dispatch of chunk c+1 on `aux` overlap the
  * expert GEMMs of chunk c on `compute`, and combine of chunk c runs on `aux` after them. The
- * first chunk's routing and dispatch, the last chunk's combine and the first chunk's combine
- * backward run on `compute`, which waits on `aux` only where it consumes aux work. On return
+ * first chunk's routing and dispatch, the last chunk's combine (on `aux` in the fused
+ * forward+backward, where nothing after it reads `out`) and the first chunk's combine backward
+ * run on `compute`, which waits on `aux` only where it consumes aux work. On return
  * all work is ordered before later work on `compute`. Both streams at the default priority;
  * with compute == aux everything runs in issue order on that one stream. With `logits` NULL the
  * forward routes from x and `w_r` (moe_route_x; BF16 or FP8 descriptor, E % 32 == 0, E <= 256).

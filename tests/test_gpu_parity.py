@@ -167,17 +167,18 @@ def test_backward_launch_order_input_grad_before_wgrad():
         assert max(idx) < first_wgrad, kind
     # forward overlap order: route of chunk 1 precedes combine of chunk 0
     assert names.index("route_topk", names.index("route_topk") + 1) < names.index("combine")
-    # stream placement: the first chunk's routing/dispatch and the last chunk's combine (nothing
-    # to overlap them with) run on the compute stream; later chunks' routing/dispatch and the
-    # earlier chunks' combines run on the auxiliary stream
+    # stream placement: the first chunk's routing/dispatch (nothing to overlap it with) runs on
+    # the compute stream; later chunks' routing/dispatch and the combines run on the auxiliary
+    # stream
     def streams_of(kind):
         return [s for n, s, _ in log if n == kind]
     compute = streams_of("gemm_gateup_swiglu")[0]
     assert set(streams_of("gemm_gateup_swiglu") + streams_of("gemm_wgrad")) == {compute}
     disp, comb = streams_of("dispatch"), streams_of("combine")
-    assert disp[0] == compute and comb[-1] == compute
+    assert disp[0] == compute
     aux = disp[1]
-    assert aux != compute and set(disp[1:]) == {aux} and set(comb[:-1]) == {aux}
+    # the fused primitive runs every combine on aux (the last one beside the backward's start)
+    assert aux != compute and set(disp[1:]) == {aux} and set(comb) == {aux}
     cbw, dbw = streams_of("combine_bwd"), streams_of("dispatch_bwd")
     assert cbw[0] == compute and set(cbw[1:]) == {aux} and set(dbw) == {aux}
     assert set(streams_of("route_bwd_dlogits")) == {aux}
