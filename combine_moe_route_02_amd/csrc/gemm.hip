@@ -504,7 +504,7 @@ hipError_t launch_expert_fwd(bool bf16, const void* xd, const void* w1, const vo
   a.offsets = offsets; a.El = El; a.c0 = c0; a.nc = nc; a.P_c = P_c; a.one = 1; a.zero = 0;
   {
     MOE_TRACE("gemm_gateup_swiglu_f32", s);
-    hipLaunchKernelGGL(simt_rows_kernel<kGateUp>, dim3(kSimtGrid), dim3(256), 0, s, a);
+    MOE_LAUNCH(simt_rows_kernel<kGateUp>, dim3(kSimtGrid), dim3(256), 0, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -514,7 +514,7 @@ hipError_t launch_expert_fwd(bool bf16, const void* xd, const void* w1, const vo
   b.offsets = offsets; b.El = El; b.c0 = c0; b.nc = nc; b.P_c = P_c; b.one = 1; b.zero = 0;
   {
     MOE_TRACE("gemm_down_f32", s);
-    hipLaunchKernelGGL(simt_rows_kernel<kDown>, dim3(kSimtGrid), dim3(256), 0, s, b);
+    MOE_LAUNCH(simt_rows_kernel<kDown>, dim3(kSimtGrid), dim3(256), 0, s, b);
   }
   return hipGetLastError();
 }
@@ -530,7 +530,7 @@ hipError_t launch_expert_dgrad(bool bf16, const void* dyd, const void* gu, const
   a.offsets = offsets; a.El = El; a.c0 = c0; a.nc = nc; a.P_c = P_c; a.one = 1; a.zero = 0;
   {
     MOE_TRACE("gemm_down_dgrad_swiglu_f32", s);
-    hipLaunchKernelGGL(simt_rows_kernel<kDownBwd>, dim3(kSimtGrid), dim3(256), 0, s, a);
+    MOE_LAUNCH(simt_rows_kernel<kDownBwd>, dim3(kSimtGrid), dim3(256), 0, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -540,7 +540,7 @@ hipError_t launch_expert_dgrad(bool bf16, const void* dyd, const void* gu, const
   b.offsets = offsets; b.El = El; b.c0 = c0; b.nc = nc; b.P_c = P_c; b.one = 1; b.zero = 0;
   {
     MOE_TRACE("gemm_gateup_dgrad_f32", s);
-    hipLaunchKernelGGL(simt_rows_kernel<kGateUpBwd>, dim3(kSimtGrid), dim3(256), 0, s, b);
+    MOE_LAUNCH(simt_rows_kernel<kGateUpBwd>, dim3(kSimtGrid), dim3(256), 0, s, b);
   }
   return hipGetLastError();
 }
@@ -555,7 +555,7 @@ hipError_t launch_expert_wgrad(bool bf16, const void* dyd, const void* dgu, cons
   a.strideC = (int64_t)H * I; a.M = H; a.N = I; a.offsets = offsets; a.El = El; a.n_chunks = n; a.P_c = P_c;
   {
     MOE_TRACE("gemm_wgrad_down_f32", s);
-    hipLaunchKernelGGL(simt_kgroup_kernel, dim3(El * ((H + 63) / 64) * ((I + 63) / 64)), dim3(256), 0, s, a);
+    MOE_LAUNCH(simt_kgroup_kernel, dim3(El * ((H + 63) / 64) * ((I + 63) / 64)), dim3(256), 0, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -564,7 +564,7 @@ hipError_t launch_expert_wgrad(bool bf16, const void* dyd, const void* dgu, cons
   b.strideC = (int64_t)2 * I * H; b.M = 2 * I; b.N = H; b.offsets = offsets; b.El = El; b.n_chunks = n; b.P_c = P_c;
   {
     MOE_TRACE("gemm_wgrad_gateup_f32", s);
-    hipLaunchKernelGGL(simt_kgroup_kernel, dim3(El * ((2 * I + 63) / 64) * ((H + 63) / 64)), dim3(256), 0, s, b);
+    MOE_LAUNCH(simt_kgroup_kernel, dim3(El * ((2 * I + 63) / 64) * ((H + 63) / 64)), dim3(256), 0, s, b);
   }
   return hipGetLastError();
 }
@@ -604,7 +604,7 @@ hipError_t launch_router_wgrad(bool bf16, const float* dlogits, const void* x, f
       a.strideC = (int64_t)E * H; a.M = E; a.N = H; a.k0 = t0; a.klen = len; a.ksplit = ks;
       {
         MOE_TRACE("gemm_router_wgrad", s);
-        hipLaunchKernelGGL(k, dim3(S * ((E + BM - 1) / BM) * ((H + BN - 1) / BN)), dim3(kThreads), lds, s, a);
+        MOE_LAUNCH(k, dim3(S * ((E + BM - 1) / BM) * ((H + BN - 1) / BN)), dim3(kThreads), lds, s, a);
       }
     } else {
       SimtKArgs a{};
@@ -612,7 +612,7 @@ hipError_t launch_router_wgrad(bool bf16, const float* dlogits, const void* x, f
       a.strideC = (int64_t)E * H; a.M = E; a.N = H; a.k0 = t0; a.klen = len; a.ksplit = ks; a.router = true;
       {
         MOE_TRACE("gemm_router_wgrad_f32", s);
-        hipLaunchKernelGGL(simt_kgroup_kernel, dim3(S * ((E + 63) / 64) * ((H + 63) / 64)), dim3(256), 0, s, a);
+        MOE_LAUNCH(simt_kgroup_kernel, dim3(S * ((E + 63) / 64) * ((H + 63) / 64)), dim3(256), 0, s, a);
       }
     }
     hipError_t e = hipGetLastError();
@@ -625,13 +625,13 @@ hipError_t launch_router_wgrad(bool bf16, const float* dlogits, const void* x, f
   if (bf16)
     {
       MOE_TRACE("router_reduce", s);
-      hipLaunchKernelGGL(reduce_partials_kernel<uint16_t>, g, dim3(256), 0, s, partials, S, MN, dwr_acc,
+      MOE_LAUNCH(reduce_partials_kernel<uint16_t>, g, dim3(256), 0, s, partials, S, MN, dwr_acc,
                          first, (uint16_t*)dwr);
     }
   else
     {
       MOE_TRACE("router_reduce", s);
-      hipLaunchKernelGGL(reduce_partials_kernel<float>, g, dim3(256), 0, s, partials, S, MN, dwr_acc,
+      MOE_LAUNCH(reduce_partials_kernel<float>, g, dim3(256), 0, s, partials, S, MN, dwr_acc,
                          first, (float*)dwr);
     }
   return hipGetLastError();

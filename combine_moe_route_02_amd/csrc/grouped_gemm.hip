@@ -691,7 +691,7 @@ hipError_t run_rows(const char* name, const RowsArgs& a, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
   {
     MOE_TRACE(name, s);
-    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kThreads), lds, s, a);
+    MOE_LAUNCH(k, dim3((unsigned)grid), dim3(kThreads), lds, s, a);
   }
   return hipGetLastError();
 }
@@ -709,7 +709,7 @@ hipError_t run_wgrad(const char* name, const WgradArgs& a, const WgradArgs& b, h
   if (grid <= 0) return hipSuccess;
   {
     MOE_TRACE(name, s);
-    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kThreads), lds, s, a, b);
+    MOE_LAUNCH(k, dim3((unsigned)grid), dim3(kThreads), lds, s, a, b);
   }
   return hipGetLastError();
 }

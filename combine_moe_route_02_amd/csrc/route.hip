@@ -386,7 +386,7 @@ static hipError_t launch_layout(const int32_t* topk_idx, const int32_t* scratch,
   const int nbpc = route_blocks_per_chunk(T, n);
   size_t sm2 = (size_t)El * 4 + (size_t)(El + 1) * 4 + 8 + (size_t)El * 8;
   MOE_TRACE("route_layout", s);
-  hipLaunchKernelGGL(route_layout_kernel, dim3(nbpc * nchunks), dim3(kRouteThreads), sm2, s, topk_idx, scratch,
+  MOE_LAUNCH(route_layout_kernel, dim3(nbpc * nchunks), dim3(kRouteThreads), sm2, s, topk_idx, scratch,
                      counts, offsets, row_of, src_token, T, E, e0, El, K, n, chunk0, nbpc, P_c);
   return hipGetLastError();
 }
@@ -409,7 +409,7 @@ hipError_t launch_route_x(const void* x, const void* w_r, float* logits, int32_t
     auto k = route_proj_topk_kernel<KK, NN>;                                                          \
     hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
     if (e != hipSuccess) return e;                                                                    \
-    hipLaunchKernelGGL(k, grid, dim3(kRxThreads), lds, s, (const __bf16*)x, (const __bf16*)w_r, logits, \
+    MOE_LAUNCH(k, grid, dim3(kRxThreads), lds, s, (const __bf16*)x, (const __bf16*)w_r, logits, \
                        topk_idx, gates, scratch, T, E, H, n, chunk0, nb32);                            \
     break;                                                                                            \
   }
@@ -437,7 +437,7 @@ hipError_t launch_route(const float* logits, int32_t* topk_idx, float* gates, in
 #define MOE_ROUTE_K(KK)                                                                      \
   case KK: {                                                                                 \
     MOE_TRACE("route_topk", s);                                                              \
-    hipLaunchKernelGGL(route_topk_kernel<KK>, grid1, block1, sm1, s, logits, topk_idx, gates, \
+    MOE_LAUNCH(route_topk_kernel<KK>, grid1, block1, sm1, s, logits, topk_idx, gates, \
                        scratch, T, E, n, chunk0, nbpc * kSub);                               \
     break;                                                                                   \
   }

@@ -382,7 +382,7 @@ hipError_t launch_dispatch(const void* x, const int32_t* row_of, void* xd, int64
   if (t1 <= t0) return hipSuccess;
   {
     MOE_TRACE("dispatch", s);
-    MOE_SWITCH_K(K, hipLaunchKernelGGL(dispatch_copy_kernel<KK>, dim3((unsigned)(t1 - t0)), dim3(kBlockThreads), 0, s,
+    MOE_SWITCH_K(K, MOE_LAUNCH(dispatch_copy_kernel<KK>, dim3((unsigned)(t1 - t0)), dim3(kBlockThreads), 0, s,
                                        (const u32x4*)x, row_of, (u32x4*)xd, t0, t1, row_bytes / 16));
   }
   return hipGetLastError();
@@ -393,7 +393,7 @@ hipError_t launch_dispatch_fp8(const void* x, const int32_t* row_of, void* xd, f
   if (t1 <= t0) return hipSuccess;
   {
     MOE_TRACE("dispatch_fp8", s);
-    hipLaunchKernelGGL(dispatch_fp8_kernel, tok_grid(t1 - t0), dim3(256), 0, s, (const u32x4*)x,
+    MOE_LAUNCH(dispatch_fp8_kernel, tok_grid(t1 - t0), dim3(256), 0, s, (const u32x4*)x,
                        row_of, (uint2*)xd, xd_scale, h_scale, t0, t1, K, (int64_t)H / 8);
   }
   return hipGetLastError();
@@ -404,7 +404,7 @@ hipError_t launch_quantize_rows_fp8(const void* src, void* codes, float* scale, 
   if (rows <= 0) return hipSuccess;
   {
     MOE_TRACE("quantize_rows_fp8", s);
-    hipLaunchKernelGGL(quantize_rows_fp8_kernel, tok_grid(rows), dim3(256), 0, s, (const u32x4*)src,
+    MOE_LAUNCH(quantize_rows_fp8_kernel, tok_grid(rows), dim3(256), 0, s, (const u32x4*)src,
                        (uint2*)codes, scale, rows, (int64_t)cols / 8);
   }
   return hipGetLastError();
@@ -416,7 +416,7 @@ hipError_t launch_quantize_segments_fp8(const void* src, void* codes, float* sca
   if (nc <= 0 || El <= 0) return hipSuccess;
   {
     MOE_TRACE("quantize_h_fp8", s);
-    hipLaunchKernelGGL(quantize_segments_fp8_kernel, dim3(256, (unsigned)nc), dim3(256), 0, s,
+    MOE_LAUNCH(quantize_segments_fp8_kernel, dim3(256, (unsigned)nc), dim3(256), 0, s,
                        (const u32x4*)src, (uint2*)codes, scale, offsets, El, c0, P_c, (int64_t)cols / 8);
   }
   return hipGetLastError();
@@ -428,13 +428,13 @@ hipError_t launch_combine(bool bf16, const void* yd, const float* gates, const i
   if (bf16)
     {
       MOE_TRACE("combine", s);
-      MOE_SWITCH_K(K, hipLaunchKernelGGL((combine_kernel<uint16_t, KK>), dim3((unsigned)(t1 - t0)), dim3(kBlockThreads), 0, s,
+      MOE_SWITCH_K(K, MOE_LAUNCH((combine_kernel<uint16_t, KK>), dim3((unsigned)(t1 - t0)), dim3(kBlockThreads), 0, s,
                          (const u32x4*)yd, gates, row_of, (u32x4*)out, t0, t1, row_bytes / 16));
     }
   else
     {
       MOE_TRACE("combine", s);
-      MOE_SWITCH_K(K, hipLaunchKernelGGL((combine_kernel<float, KK>), dim3((unsigned)(t1 - t0)), dim3(kBlockThreads), 0, s,
+      MOE_SWITCH_K(K, MOE_LAUNCH((combine_kernel<float, KK>), dim3((unsigned)(t1 - t0)), dim3(kBlockThreads), 0, s,
                          (const u32x4*)yd, gates, row_of, (u32x4*)out, t0, t1, row_bytes / 16));
     }
   return hipGetLastError();
@@ -447,14 +447,14 @@ hipError_t launch_combine_bwd(bool bf16, const void* dy, const void* yd, const f
   if (bf16)
     {
       MOE_TRACE("combine_bwd", s);
-      MOE_SWITCH_K(K, hipLaunchKernelGGL((combine_bwd_kernel<uint16_t, KK>), dim3((unsigned)(t1 - t0)), dim3(kBlockThreads), 0, s,
+      MOE_SWITCH_K(K, MOE_LAUNCH((combine_bwd_kernel<uint16_t, KK>), dim3((unsigned)(t1 - t0)), dim3(kBlockThreads), 0, s,
                          (const u32x4*)dy, (const u32x4*)yd, gates, row_of, (u32x4*)dyd, dgates,
                          t0, t1, row_bytes / 16));
     }
   else
     {
       MOE_TRACE("combine_bwd", s);
-      MOE_SWITCH_K(K, hipLaunchKernelGGL((combine_bwd_kernel<float, KK>), dim3((unsigned)(t1 - t0)), dim3(kBlockThreads), 0, s,
+      MOE_SWITCH_K(K, MOE_LAUNCH((combine_bwd_kernel<float, KK>), dim3((unsigned)(t1 - t0)), dim3(kBlockThreads), 0, s,
                          (const u32x4*)dy, (const u32x4*)yd, gates, row_of, (u32x4*)dyd, dgates,
                          t0, t1, row_bytes / 16));
     }
@@ -467,7 +467,7 @@ hipError_t launch_route_bwd_dlogits(const float* dgates, const float* gates, con
   if (t1 <= t0) return hipSuccess;
   {
     MOE_TRACE("route_bwd_dlogits", s);
-    hipLaunchKernelGGL(route_bwd_dlogits_kernel, tok_grid(t1 - t0), dim3(256), 0, s, dgates, gates,
+    MOE_LAUNCH(route_bwd_dlogits_kernel, tok_grid(t1 - t0), dim3(256), 0, s, dgates, gates,
                        idx, dlogits, t0, t1, K, E);
   }
   return hipGetLastError();
@@ -480,14 +480,14 @@ hipError_t launch_dispatch_bwd(bool bf16, const void* dxd, const int32_t* row_of
   if (bf16)
     {
       MOE_TRACE("dispatch_bwd", s);
-      MOE_SWITCH_K(K, hipLaunchKernelGGL((dispatch_bwd_kernel<uint16_t, KK>), tok_grid(t1 - t0), dim3(256), 0, s,
+      MOE_SWITCH_K(K, MOE_LAUNCH((dispatch_bwd_kernel<uint16_t, KK>), tok_grid(t1 - t0), dim3(256), 0, s,
                          (const u32x4*)dxd, row_of, idx, dlogits, (const u32x4*)w_r, (u32x4*)dx,
                          t0, t1, E, row_bytes / 16));
     }
   else
     {
       MOE_TRACE("dispatch_bwd", s);
-      MOE_SWITCH_K(K, hipLaunchKernelGGL((dispatch_bwd_kernel<float, KK>), tok_grid(t1 - t0), dim3(256), 0, s,
+      MOE_SWITCH_K(K, MOE_LAUNCH((dispatch_bwd_kernel<float, KK>), tok_grid(t1 - t0), dim3(256), 0, s,
                          (const u32x4*)dxd, row_of, idx, dlogits, (const u32x4*)w_r, (u32x4*)dx,
                          t0, t1, E, row_bytes / 16));
     }

@@ -81,12 +81,12 @@ hipError_t launch_stash_copy(bool store, const void* from, const float* from_sca
   const int64_t nvec = row_bytes / 16;
   if (store) {
     MOE_TRACE("stash_store", s);
-    hipLaunchKernelGGL(stash_copy_kernel<true>, dim3((unsigned)grid), dim3(kStashThreads), 0, s,
+    MOE_LAUNCH(stash_copy_kernel<true>, dim3((unsigned)grid), dim3(kStashThreads), 0, s,
                        (const u32x4*)from, from_scale, (u32x4*)to, to_scale, live_rows, nvec, num_pages,
                        page_rows, pages, record, owner, tpp, ntiles);
   } else {
     MOE_TRACE("stash_load", s);
-    hipLaunchKernelGGL(stash_copy_kernel<false>, dim3((unsigned)grid), dim3(kStashThreads), 0, s,
+    MOE_LAUNCH(stash_copy_kernel<false>, dim3((unsigned)grid), dim3(kStashThreads), 0, s,
                        (const u32x4*)from, from_scale, (u32x4*)to, to_scale, live_rows, nvec, num_pages,
                        page_rows, pages, record, owner, tpp, ntiles);
   }

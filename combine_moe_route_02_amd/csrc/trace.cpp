@@ -14,6 +14,7 @@ struct Rec {
   const char* name;
   hipStream_t stream;
   int ev0, ev1;  // indices into the event pool, -1 without timing
+  bool launched; // the kernel dispatch recorded ev0/ev1
 };
 
 struct State {
@@ -43,25 +44,32 @@ int take_event() {
 bool active() { return g.on; }
 
 void begin(const char* name, hipStream_t s) {
-  Rec r{name, s, -1, -1};
+  Rec r{name, s, -1, -1, false};
   if (g.timing) {
     r.ev0 = take_event();
-    if (r.ev0 >= 0) {
-      hipError_t e = hipEventRecord(g.pool[r.ev0], s);
-      if (e != hipSuccess) g.err = e;
-    }
+    r.ev1 = take_event();
   }
   g.recs.push_back(r);
   g.open = (int)g.recs.size() - 1;
 }
 
+void launch_events(hipEvent_t* start, hipEvent_t* stop) {
+  *start = *stop = nullptr;
+  if (g.open < 0 || !g.timing) return;
+  Rec& r = g.recs[g.open];
+  if (r.ev0 < 0 || r.ev1 < 0 || r.launched) return;
+  *start = g.pool[r.ev0];
+  *stop = g.pool[r.ev1];
+  r.launched = true;
+}
+
 void end(hipStream_t s) {
   if (g.open < 0) return;
   Rec& r = g.recs[g.open];
-  if (g.timing) {
-    r.ev1 = take_event();
-    if (r.ev1 >= 0) {
-      hipError_t e = hipEventRecord(g.pool[r.ev1], s);
+  if (g.timing && !r.launched) {  // no launch took the events: record them here so they are valid
+    for (int ev : {r.ev0, r.ev1}) {
+      if (ev < 0) continue;
+      hipError_t e = hipEventRecord(g.pool[ev], s);
       if (e != hipSuccess) g.err = e;
     }
   }
