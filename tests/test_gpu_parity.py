@@ -322,3 +322,40 @@ def test_zero_tokens_launches_nothing():
     assert torch.all(b["counts"] == 0) and torch.all(b["offsets"] == 0)
     # weight gradients of an empty batch are zero
     assert torch.all(b["dw1"] == 0) and torch.all(b["dw2"] == 0) and torch.all(b["dwr"] == 0)
+
+
+def test_layer_step_under_hip_graph_capture():
+    """The fused layer primitive captured into a HIP graph (both streams; no memset nodes, no
+    allocation) replays to bitwise the eager results, three times, with eager work and
+    synchronisations between the replays."""
+    _require_gpu()
+    import torch
+    import combine_moe_route_02_amd as mh
+    cfg = SMALL[3]
+    inp = moe_inputs.make_inputs(cfg, with_backward=True)
+    d = mh.make_desc(T=cfg.T, H=cfg.H, I=cfg.I, E=cfg.E, E_local=cfg.E_local, k=cfg.k, n_chunks=cfg.n_chunks,
+                     dtype=cfg.dtype, e0=cfg.e0)
+    b = mh.allocate(d, backward=True)
+    for name in ("x", "w1", "w2", "w_r", "dy"):
+        b[name] = torch.from_numpy(inp[name + "_bits"].view(np.int16)).cuda().view(torch.bfloat16)
+    b["logits"] = torch.from_numpy(inp["logits"]).cuda()
+    cs, aux = torch.cuda.Stream(), torch.cuda.Stream()
+    mh.moe_layer_forward_backward(d, b, cs, aux)
+    torch.cuda.synchronize()
+    keys = ("topk_idx", "gates", "row_of", "dx", "dw1", "dw2", "dwr", "dlogits")
+    ref = {k: b[k].clone() for k in keys}
+    ref_out = b["out"][:cfg.T].clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cs):
+        mh.moe_layer_forward_backward(d, b, cs, aux)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for k in keys:
+            b[k].fill_(-3)          # eager work between replays
+        b["out"].fill_(-3)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in keys:
+            assert torch.equal(b[k], ref[k]), (rep, k)
+        assert torch.equal(b["out"][:cfg.T], ref_out), rep
