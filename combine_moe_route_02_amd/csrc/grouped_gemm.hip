@@ -11,8 +11,8 @@
 // "Numerical status -- unresolved" states for the router weights).
 //
 // Engine (one 512-thread workgroup = 8 waves in a 2 x 4 grid over a BM x BN output tile, two
-// waves per SIMD: on gfx950 one wave issues global -> LDS loads at only ~5 B/clk, so eight waves
-// share the ~32 B/clk per CU that a 256 x 256 tile needs; LDS reads stay below the port's rate):
+// waves per SIMD, so the second wave on a SIMD issues MFMAs while the first waits; four waves
+// with 128 x 128 wave tiles read a third fewer LDS bytes but measured slower on every GEMM here):
 //   * Operands reach LDS by direct-to-LDS 16-byte buffer loads (buffer_load_dwordx4 ... lds):
 //     no staging registers, no VALU on the load path. The scalar buffer descriptor's extent
 //     masks rows past an expert's segment or a matrix edge (such loads return zero).

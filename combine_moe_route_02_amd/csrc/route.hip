@@ -158,8 +158,8 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
 // ring with direct-to-LDS 16-byte loads: one wave instruction moves 8 whole 128-byte row
 // segments, and each stage holds (32 + E) rows of 128 bytes whose 16-byte chunks are
 // XOR-swizzled by (row & 7), so the 32-row fragment reads hit every bank once. Loads run three
-// stages ahead with one barrier per stage, spread over all eight waves (a wave issues these
-// loads at only a few bytes per clock). Wave w multiplies the 32-expert blocks w % 4,
+// stages ahead with one barrier per stage, spread over all eight waves (measured faster than
+// four waves issuing them). Wave w multiplies the 32-expert blocks w % 4,
 // w % 4 + 4, ... over the K steps 2 (w / 4), 2 (w / 4) + 1 of each stage; the two partial tiles
 // are added in LDS in a fixed order.
 constexpr int kProjTok = 32;
