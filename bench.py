@@ -52,15 +52,24 @@ CALIBRATION_BYTES = 64 << 20   # a plain elementwise copy of this many bytes (re
 CALIBRATION_SYMBOL = "MulFunctor"  # one dispatch: y = 2 * x in FP32) runs before the timed region
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and whitespace (string literals in these files hold no
+    comment markers), so that an edit to comments alone keeps a kernel's counters valid."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return re.sub(r"\s+", "", text)
+
+
 def source_sha(name: str) -> str:
-    """Short hash of a kernel's source file (and the shared headers): counters taken on other
-    source are not reported for this build."""
+    """Short hash of a kernel's source code (and the shared header), comments and whitespace
+    removed: counters taken on other code are not reported for this build."""
     import hashlib
     csrc = os.path.join(ROOT, "combine_moe_route_02_amd", "csrc")
     h = hashlib.sha256()
     for f in (KERNEL_SYMBOLS[name][0], "common.h"):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
