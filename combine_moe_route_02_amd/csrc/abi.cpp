@@ -9,7 +9,6 @@
 #include <cstdarg>
 #include <cstdio>
 #include <map>
-#include <mutex>
 #include <string>
 #include <vector>
 
@@ -103,18 +102,19 @@ bool is_bf16_rows(const moe_desc* d) { return d->dtype != MOE_F32; }
 // dispatch rows of the descriptor (0 when no expert is local)
 int64_t rows_of(const moe_desc* d) { return d->E_local > 0 ? (int64_t)d->n_chunks * d->P_c : 0; }
 
-// Events for the two-stream schedule, created once per device and reused.
+// Events for the two-stream schedule, created once per host thread and device and reused (they
+// live until the process ends). Per thread, so that schedules issued concurrently from several
+// threads never record or wait on each other's events; within one thread the calls are issued
+// one after another, and a wait always refers to the event's latest record.
 struct EventPool {
   std::vector<hipEvent_t> ev;
 };
-std::mutex g_pool_mu;
-std::map<int, EventPool> g_pools;
+thread_local std::map<int, EventPool> t_pools;
 
 moe_status events(int count, hipEvent_t** out) {
   int dev = 0;
   MOE_HIP(hipGetDevice(&dev), "hipGetDevice");
-  std::lock_guard<std::mutex> lk(g_pool_mu);
-  EventPool& p = g_pools[dev];
+  EventPool& p = t_pools[dev];
   while ((int)p.ev.size() < count) {
     hipEvent_t e;
     MOE_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming | hipEventDisableSystemFence), "hipEventCreateWithFlags");

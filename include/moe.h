@@ -223,6 +223,10 @@ moe_status moe_stash_load(const void* pool, const float* pool_scale, int64_t liv
  * all work is ordered before later work on `compute`. Both streams at the default priority;
  * with compute == aux everything runs in issue order on that one stream. With `logits` NULL the
  * forward routes from x and `w_r` (moe_route_x; BF16 or FP8 descriptor, E % 32 == 0, E <= 256).
+ * The schedule's cross-stream dependencies use HIP events from a pool that the library creates
+ * per host thread and device on first use and keeps until the process ends, so layer calls
+ * issued from different threads never share events. Calls that share `workspace` or any saved-
+ * context buffer must still be ordered by the caller.
  * ------------------------------------------------------------------------------------- */
 typedef struct moe_tensors {
   /* inputs */

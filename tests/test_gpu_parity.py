@@ -359,3 +359,57 @@ def test_layer_step_under_hip_graph_capture():
         for k in keys:
             assert torch.equal(b[k], ref[k]), (rep, k)
         assert torch.equal(b["out"][:cfg.T], ref_out), rep
+
+
+def test_layer_calls_from_two_threads():
+    """Two host threads issue fused layer steps at the same time, each on its own buffers and
+    stream pair (the schedule's events are per thread): both match the single-threaded results
+    bitwise, five steps each."""
+    _require_gpu()
+    import threading
+    import torch
+    import combine_moe_route_02_amd as mh
+    cfg = SMALL[3]
+    inp = moe_inputs.make_inputs(cfg, with_backward=True)
+    d = mh.make_desc(T=cfg.T, H=cfg.H, I=cfg.I, E=cfg.E, E_local=cfg.E_local, k=cfg.k, n_chunks=cfg.n_chunks,
+                     dtype=cfg.dtype, e0=cfg.e0)
+    keys = ("topk_idx", "gates", "row_of", "dx", "dw1", "dw2", "dwr", "dlogits")
+
+    def make():
+        b = mh.allocate(d, backward=True)
+        for name in ("x", "w1", "w2", "w_r", "dy"):
+            b[name] = torch.from_numpy(inp[name + "_bits"].view(np.int16)).cuda().view(torch.bfloat16)
+        b["logits"] = torch.from_numpy(inp["logits"]).cuda()
+        return b
+
+    ref_b = make()
+    cs, aux = torch.cuda.Stream(), torch.cuda.Stream()
+    mh.moe_layer_forward_backward(d, ref_b, cs, aux)
+    torch.cuda.synchronize()
+    ref = {k: ref_b[k].clone() for k in keys}
+    ref_out = ref_b["out"][:cfg.T].clone()
+    bufs = [make(), make()]
+    streams = [(torch.cuda.Stream(), torch.cuda.Stream()) for _ in bufs]
+    torch.cuda.synchronize()
+    errors = []
+
+    def work(i):
+        try:
+            torch.cuda.set_device(0)
+            for _ in range(5):
+                mh.moe_layer_forward_backward(d, bufs[i], streams[i][0], streams[i][1])
+        except Exception as exc:  # reported by the main thread
+            errors.append(repr(exc))
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=60)
+    assert not any(th.is_alive() for th in threads), "a layer thread did not return"
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for b in bufs:
+        for k in keys:
+            assert torch.equal(b[k], ref[k]), k
+        assert torch.equal(b["out"][:cfg.T], ref_out)
