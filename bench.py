@@ -42,8 +42,10 @@ KERNEL_SYMBOLS = {
     "dispatch_bwd": ("rows.hip", "dispatch_bwd_kernel"),
     "gemm_gateup_swiglu": ("grouped_gemm.hip", "rows_kernel<256, 256, 0, false>"),
     "gemm_down": ("grouped_gemm.hip", "rows_kernel<256, 256, 1, false>"),
-    "gemm_down_dgrad_swiglu": ("grouped_gemm.hip", "rows_kernel<256, 128, 2, false>"),
+    "gemm_down_dgrad_swiglu": ("grouped_gemm.hip", "rows_kernel<128, 256, 2, false>"),
     "gemm_gateup_dgrad": ("grouped_gemm.hip", "rows_kernel<256, 256, 3, false>"),
+    "gemm_down+gateup_swiglu": ("grouped_gemm.hip", "rows_pair_kernel<256, 256, 1, 256, 256, 0>"),
+    "gemm_gateup_dgrad+down_dgrad_swiglu": ("grouped_gemm.hip", "rows_pair_kernel<256, 256, 3, 128, 256, 2>"),
     "gemm_wgrad": ("grouped_gemm.hip", "wgrad_kernel<256, 256>"),
     "gemm_router_wgrad": ("gemm.hip", "router_wgrad_kernel"),
     "router_reduce": ("gemm.hip", "reduce_partials_kernel"),
@@ -140,7 +142,8 @@ def committed_traffic(name: str):
 
 
 GEMM_KERNELS = {"gemm_gateup_swiglu", "gemm_down", "gemm_down_dgrad_swiglu", "gemm_gateup_dgrad",
-                "gemm_wgrad", "gemm_router_wgrad"}
+                "gemm_wgrad", "gemm_router_wgrad", "gemm_down+gateup_swiglu",
+                "gemm_gateup_dgrad+down_dgrad_swiglu"}
 
 
 def algorithmic_work(cfg, counts, offsets, k_sel_local_tokens):
@@ -168,6 +171,32 @@ def algorithmic_work(cfg, counts, offsets, k_sel_local_tokens):
         "router_reduce": (cfg.n_chunks * (S * E * H * 4 + 2 * E * H * 4) + E * H * s, "byte"),
     }
     return w, N, Tt
+
+
+def fused_gemm_work(cfg, Nc):
+    """The fused step's BF16 GEMM launches (the layer primitive merges independent GEMMs of
+    neighbouring chunks): name -> ((flops, unit), HBM bytes) per step, from the local rows per chunk
+    Nc. Gate/up and down dgrad run alone for chunk 0, down and gate/up dgrad alone for the last
+    chunk; each pair launch does down (gate/up dgrad) of chunk c with gate/up (down dgrad) of c+1."""
+    H, I, El, s, n = cfg.H, cfg.I, cfg.E_local, 2, len(Nc)
+    w1, w2 = El * 2 * I * H * s, El * H * I * s
+    gu_f = lambda m: 2.0 * m * H * 2 * I
+    dn_f = lambda m: 2.0 * m * I * H
+    gu_b = lambda m: m * H * s + w1 + m * I * s + m * 2 * I * s
+    dn_b = lambda m: m * I * s + w2 + m * H * s
+    ddg_b = lambda m: m * H * s + w2 + 2 * m * 2 * I * s
+    gudg_b = lambda m: m * 2 * I * s + w1 + m * H * s
+    pairs = range(n - 1)
+    return {
+        "gemm_gateup_swiglu": ((gu_f(Nc[0]), "flop"), gu_b(Nc[0])),
+        "gemm_down+gateup_swiglu": ((sum(dn_f(Nc[c]) + gu_f(Nc[c + 1]) for c in pairs), "flop"),
+                                    sum(dn_b(Nc[c]) + gu_b(Nc[c + 1]) for c in pairs)),
+        "gemm_down": ((dn_f(Nc[-1]), "flop"), dn_b(Nc[-1])),
+        "gemm_down_dgrad_swiglu": ((dn_f(Nc[0]), "flop"), ddg_b(Nc[0])),
+        "gemm_gateup_dgrad+down_dgrad_swiglu": ((sum(gu_f(Nc[c]) + dn_f(Nc[c + 1]) for c in pairs), "flop"),
+                                                sum(gudg_b(Nc[c]) + ddg_b(Nc[c + 1]) for c in pairs)),
+        "gemm_gateup_dgrad": ((gu_f(Nc[-1]), "flop"), gudg_b(Nc[-1])),
+    }
 
 
 def gemm_bytes(cfg, N):
@@ -479,6 +508,11 @@ def main():
     row_of = bufs["row_of"].cpu().numpy()
     touched = int(np.count_nonzero((row_of >= 0).any(axis=1)))
     work, N, Tt = algorithmic_work(cfg, counts, offsets, touched)
+    # the fused step's GEMM launches: per-step work of the launch kinds the layer primitive issues
+    # (the isolated stage calls keep the per-GEMM kinds of `work`)
+    fused = fused_gemm_work(cfg, [int(v) for v in offsets[:, cfg.E_local]])
+    work_f = dict(work)
+    work_f.update({k: v[0] for k, v in fused.items()})
 
     per = {}
     for name, _stream, ms in entries:
@@ -487,17 +521,22 @@ def main():
         p[1] += ms
     kernels = {}
     gbytes = gemm_bytes(cfg, N)
-    for name, (cnt, tot) in per.items():
-        launches = cnt / args.steps
-        avg_us = tot / cnt * 1e3
-        entry = {"launches_per_step": launches, "avg_us": round(avg_us, 3), "ms_per_step": round(tot / args.steps, 4)}
-        if name in work:
-            wk, unit = work[name]
+    gbytes_f = dict(gbytes)
+    gbytes_f.update({k: v[1] for k, v in fused.items()})
+    names = list(per) + [n for n in iso if n not in per]
+    for name in names:
+        entry = {}
+        if name in per:
+            cnt, tot = per[name]
+            entry = {"launches_per_step": cnt / args.steps, "avg_us": round(tot / cnt * 1e3, 3),
+                     "ms_per_step": round(tot / args.steps, 4)}
+        if name in per and name in work_f:
+            wk, unit = work_f[name]
             rate = wk / (tot / args.steps * 1e-3)
             if unit == "flop":
                 entry.update(achieved_tflops=round(rate / 1e12, 2), frac_mfma=round(rate / 1e12 / PEAK_BF16_TFLOPS, 4))
-                if name in gbytes:
-                    ai = wk / gbytes[name]
+                if name in gbytes_f:
+                    ai = wk / gbytes_f[name]
                     attain = min(PEAK_BF16_TFLOPS, ai * PEAK_HBM_GBS / 1e3)
                     entry.update(intensity_flop_per_byte=round(ai, 1), attainable_tflops=round(attain, 1),
                                  frac_attainable=round(rate / 1e12 / attain, 4))
@@ -516,9 +555,14 @@ def main():
                 r = wk / (it / args.steps * 1e-3)
                 entry["isolated_frac"] = round(r / 1e12 / PEAK_BF16_TFLOPS if unit == "flop" else r / 1e9 / PEAK_HBM_GBS, 4)
         kernels[name] = entry
-    dom = max(per, key=lambda n: per[n][1])
+    # dominant kernel: the largest share of the compute stream, whose work sets the step time
+    # (kernels on the auxiliary stream run beside it, so their in-step durations mostly measure
+    # how much they were slowed by the GEMM next to them, not their own cost)
+    on_compute = {n for n, st, _ in entries if int(st or 0) == int(cs.cuda_stream)}
+    on_compute -= {n for n, st, _ in entries if int(st or 0) != int(cs.cuda_stream)}
+    dom = max((n for n in per if n in on_compute), key=lambda n: per[n][1])
     dcnt, dtot = per[dom]
-    wk, unit = work.get(dom, (None, None))
+    wk, unit = work_f.get(dom, (None, None))
     if unit == "flop":
         ach = wk / (dtot / args.steps * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -531,7 +575,7 @@ def main():
                 "avg_launch_us": round(dtot / dcnt * 1e3, 3), "work_per_launch": wk / (dcnt / args.steps)}
 
     iso_ms = sum(v[1] for v in iso.values()) / args.steps
-    gemm_flops = sum(work[n][0] for n in GEMM_KERNELS)
+    gemm_flops = sum(work_f[n][0] for n in GEMM_KERNELS if n in per)
     gemm_ms = sum(per[n][1] for n in GEMM_KERNELS if n in per) / args.steps
     value = cfg.T / (ms_per_step * 1e-3)
     line = {

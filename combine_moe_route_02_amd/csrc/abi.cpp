@@ -557,9 +557,140 @@ static moe_status backward_sched(const moe_desc* d, const moe_tensors* t, hipStr
   return MOE_OK;
 }
 
+// BF16 schedules with merged GEMM launches. A persistent GEMM launch leaves most CUs idle in
+// its last round (the small last tiles of each expert), and every launch boundary costs a few µs;
+// so the layer issues independent GEMMs of neighbouring steps as one launch: down of chunk c with
+// gate/up of chunk c+1, and gate/up dgrad of chunk c with down dgrad of chunk c+1. Every tile
+// computes exactly what the single launches compute, so the results are bitwise those of the
+// stage calls. The last chunk's gate/up dgrad stays its own launch: its dispatch backward then
+// overlaps the weight gradients instead of waiting for them (input gradients before weight
+// gradients).
+static moe::ExpertGemm expert_gemm(const moe_desc* d, const moe_tensors* t) {
+  moe::ExpertGemm g{};
+  g.xd = t->xd; g.w1 = t->w1; g.w2 = t->w2; g.gu = t->gu; g.h = t->h; g.yd = t->yd;
+  g.dyd = t->dyd; g.dgu = t->dgu; g.dxd = t->dxd; g.dw1 = t->dw1; g.dw2 = t->dw2;
+  g.offsets = t->offsets; g.H = d->H; g.I = d->I; g.El = d->E_local; g.n_chunks = d->n_chunks; g.P_c = d->P_c;
+  return g;
+}
+
+static bool merged_gemms(const moe_desc* d) { return d->dtype == MOE_BF16 && d->T > 0 && rows_of(d) > 0; }
+
+//   compute: R0 D0 GU0 | wait(disp1) [DN0 GU1] | wait(disp2) [DN1 GU2] | ... | DN n-1, C n-1
+//   aux:     wait(disp0) R1 D1 | R2 D2, wait(ffn0) C0 | R3 D3, wait(ffn1) C1 | ...
+static moe_status forward_sched_merged(const moe_desc* d, const moe_tensors* t, hipStream_t cs, hipStream_t as,
+                                       bool join) {
+  const int n = d->n_chunks;
+  const bool two = cs != as && n > 1;
+  const hipStream_t side = two ? as : cs;
+  const moe::ExpertGemm g = expert_gemm(d, t);
+  hipEvent_t* ev = nullptr;
+  MOE_TRY(events(2 * n + 1, &ev));
+  hipEvent_t* disp = ev;
+  hipEvent_t* ffn = ev + n;
+  hipEvent_t done = ev[2 * n];
+  auto route_dispatch = [&](int c, hipStream_t s) -> moe_status {
+    MOE_TRY(route_any(d, c, t, s));
+    MOE_TRY(moe_dispatch(d, c, t->x, t->row_of, t->xd, t->xd_scale, t->h_scale, s));
+    return MOE_OK;
+  };
+  MOE_TRY(route_dispatch(0, cs));
+  if (two) {
+    MOE_HIP(hipEventRecord(disp[0], cs), "hipEventRecord");
+    MOE_HIP(hipStreamWaitEvent(as, disp[0], 0), "hipStreamWaitEvent");
+  }
+  if (n > 1) {
+    MOE_TRY(route_dispatch(1, side));
+    if (two) MOE_HIP(hipEventRecord(disp[1], as), "hipEventRecord");
+  }
+  MOE_HIP(moe::gg_gateup(g, 0, cs), "expert_ffn");
+  for (int c = 0; c < n; ++c) {
+    if (c + 1 < n) {
+      if (two) MOE_HIP(hipStreamWaitEvent(cs, disp[c + 1], 0), "hipStreamWaitEvent");
+      MOE_HIP(moe::gg_down_then_gateup(g, c, c + 1, cs), "expert_ffn");
+      if (c + 2 < n) {
+        MOE_TRY(route_dispatch(c + 2, side));
+        if (two) MOE_HIP(hipEventRecord(disp[c + 2], as), "hipEventRecord");
+      }
+    } else {
+      MOE_HIP(moe::gg_down(g, c, cs), "expert_ffn");
+    }
+    if (c + 1 < n || (two && !join)) {
+      if (two) {
+        MOE_HIP(hipEventRecord(ffn[c], cs), "hipEventRecord");
+        MOE_HIP(hipStreamWaitEvent(as, ffn[c], 0), "hipStreamWaitEvent");
+      }
+      MOE_TRY(moe_combine(d, c, t->yd, t->gates, t->row_of, t->out, side));
+    } else {
+      MOE_TRY(moe_combine(d, c, t->yd, t->gates, t->row_of, t->out, cs));
+    }
+  }
+  if (two && join) {
+    MOE_HIP(hipEventRecord(done, as), "hipEventRecord");
+    MOE_HIP(hipStreamWaitEvent(cs, done, 0), "hipStreamWaitEvent");
+  }
+  return MOE_OK;
+}
+
+//   compute: CB0 DDG0 | wait(cb1) [GUDG0 DDG1] | wait(cb2) [GUDG1 DDG2] | ... | GUDG n-1, W, wait(done)
+//   aux:     wait(cb0) CB1 RB0 | CB2 RB1 wait(dg0) DB0 | CB3 RB2 wait(dg1) DB1 | ... | wait(dg n-1) DB n-1
+static moe_status backward_sched_merged(const moe_desc* d, const moe_tensors* t, hipStream_t cs, hipStream_t as) {
+  const int n = d->n_chunks;
+  const bool two = cs != as;
+  const hipStream_t side = two ? as : cs;
+  const moe::ExpertGemm g = expert_gemm(d, t);
+  hipEvent_t* ev = nullptr;
+  MOE_TRY(events(4 * n + 2, &ev));
+  hipEvent_t* cb = ev + 2 * n + 1;
+  hipEvent_t* dg = ev + 3 * n + 1;
+  hipEvent_t done = ev[4 * n + 1];
+  auto combine_bwd = [&](int c, hipStream_t s) {
+    return moe_combine_bwd(d, c, t->dy, t->yd, t->gates, t->row_of, t->dyd, t->dgates, s);
+  };
+  auto route_bwd = [&](int c) {
+    return moe_route_bwd(d, c, t->dgates, t->gates, t->topk_idx, t->x, t->dlogits, t->dwr_acc, t->dwr,
+                         t->workspace, side);
+  };
+  MOE_TRY(combine_bwd(0, cs));
+  if (two) {
+    MOE_HIP(hipEventRecord(cb[0], cs), "hipEventRecord");
+    MOE_HIP(hipStreamWaitEvent(as, cb[0], 0), "hipStreamWaitEvent");
+  }
+  if (n > 1) {
+    MOE_TRY(combine_bwd(1, side));
+    if (two) MOE_HIP(hipEventRecord(cb[1], as), "hipEventRecord");
+  }
+  MOE_TRY(route_bwd(0));
+  MOE_HIP(moe::gg_down_dgrad(g, 0, cs), "expert_dgrad");
+  for (int c = 0; c < n; ++c) {
+    if (c + 1 < n) {
+      if (two) MOE_HIP(hipStreamWaitEvent(cs, cb[c + 1], 0), "hipStreamWaitEvent");
+      MOE_HIP(moe::gg_gateup_dgrad_then_down_dgrad(g, c, c + 1, cs), "expert_dgrad");
+    } else {
+      MOE_HIP(moe::gg_gateup_dgrad(g, c, cs), "expert_dgrad");
+    }
+    if (two) MOE_HIP(hipEventRecord(dg[c], cs), "hipEventRecord");
+    if (c + 1 < n) {
+      if (c + 2 < n) {
+        MOE_TRY(combine_bwd(c + 2, side));
+        if (two) MOE_HIP(hipEventRecord(cb[c + 2], as), "hipEventRecord");
+      }
+      MOE_TRY(route_bwd(c + 1));
+    }
+    if (two) MOE_HIP(hipStreamWaitEvent(as, dg[c], 0), "hipStreamWaitEvent");
+    MOE_TRY(moe_dispatch_bwd(d, c, t->dxd, t->row_of, t->topk_idx, t->dlogits, t->w_r, t->dx, side));
+  }
+  MOE_TRY(moe_expert_wgrad(d, t->dyd, t->dgu, t->xd, t->h, t->offsets, t->dw1, t->dw2, cs));
+  if (two) {
+    MOE_HIP(hipEventRecord(done, as), "hipEventRecord");
+    MOE_HIP(hipStreamWaitEvent(cs, done, 0), "hipStreamWaitEvent");
+  }
+  return MOE_OK;
+}
+
 moe_status moe_layer_forward(const moe_desc* d, const moe_tensors* t, void* compute_stream, void* aux_stream) {
   MOE_TRY(validate(d));
   MOE_TRY(check_fwd_tensors(d, t));
+  if (merged_gemms(d)) return forward_sched_merged(d, t, (hipStream_t)compute_stream, (hipStream_t)aux_stream, true);
   return forward_sched(d, t, (hipStream_t)compute_stream, (hipStream_t)aux_stream, true);
 }
 
@@ -567,6 +698,7 @@ moe_status moe_layer_backward(const moe_desc* d, const moe_tensors* t, void* com
   MOE_TRY(validate(d));
   MOE_TRY(check_fwd_tensors(d, t));
   MOE_TRY(check_bwd_tensors(d, t));
+  if (merged_gemms(d)) return backward_sched_merged(d, t, (hipStream_t)compute_stream, (hipStream_t)aux_stream);
   return backward_sched(d, t, (hipStream_t)compute_stream, (hipStream_t)aux_stream);
 }
 
@@ -577,6 +709,10 @@ moe_status moe_layer_forward_backward(const moe_desc* d, const moe_tensors* t, v
   MOE_TRY(check_bwd_tensors(d, t));
   // no join between the two: the backward's first wait of the auxiliary stream follows the
   // whole forward on the compute stream, and its final join covers the forward's aux work
+  if (merged_gemms(d)) {
+    MOE_TRY(forward_sched_merged(d, t, (hipStream_t)compute_stream, (hipStream_t)aux_stream, false));
+    return backward_sched_merged(d, t, (hipStream_t)compute_stream, (hipStream_t)aux_stream);
+  }
   MOE_TRY(forward_sched(d, t, (hipStream_t)compute_stream, (hipStream_t)aux_stream, false));
   return backward_sched(d, t, (hipStream_t)compute_stream, (hipStream_t)aux_stream);
 }

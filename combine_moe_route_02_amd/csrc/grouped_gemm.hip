@@ -319,19 +319,38 @@ constexpr size_t rows_lds_bytes() {
   return ring > ep ? ring : ep;
 }
 
+// Group -> tile prefix of one row-grouped GEMM, rebuilt in LDS by every workgroup.
+struct RowsShared {
+  int pre[kMaxGroups + 1];   // large tiles before group g
+  int64_t r0[kMaxGroups];    // first dispatch row of group g
+  int len[kMaxGroups];       // rows of group g
+  int preb[kMaxGroups + 1];  // small tiles before group g
+};
+
+// Persistent work slots. Per XCD the workgroups (block b runs on XCD b % 8; W of them per XCD)
+// share one sequence of slots: slot s goes to the XCD's workgroup s % W, so that a list that
+// starts at slot `first` continues the round robin where the previous list of the same launch
+// ended, and a workgroup that finishes early takes the next list's tiles.
+MOE_DEV int first_slot(int first) {
+  const int w = gridDim.x / 8, j = blockIdx.x / 8;
+  return first + ((j - first) % w + w) % w;
+}
+
+// The tiles of one row-grouped GEMM from per-XCD slot `first` on; returns the slot after its
+// last. Every thread of the workgroup calls it (it contains barriers).
 template <int BM, int BN, int MODE, bool FP8>
-__global__ __launch_bounds__(kThreads) void rows_kernel(RowsArgs a) {
+MOE_DEV int rows_list(const RowsArgs& a, int first, RowsShared& sh, char* ring) {
   constexpr int WTM = BM / kWM, WTN = BN / kWN, TM = WTM / 32, TN = WTN / 32;
   constexpr bool kSwiGLU = (MODE == kGateUp);
   constexpr bool kBKS = (MODE == kDownBwd || MODE == kGateUpBwd);
   constexpr int ES = FP8 ? 1 : 2;      // element bytes
   constexpr int OUTN = kSwiGLU ? BN / 2 : BN;
   static_assert(!(FP8 && kBKS), "FP8 runs the forward GEMMs only");
-  __shared__ int s_pre[kMaxGroups + 1];
-  __shared__ int64_t s_r0[kMaxGroups];
-  __shared__ int s_len[kMaxGroups];
-  __shared__ int s_preb[kMaxGroups + 1];
-  extern __shared__ __attribute__((aligned(1024))) char ring[];
+  int* s_pre = sh.pre;
+  int64_t* s_r0 = sh.r0;
+  int* s_len = sh.len;
+  int* s_preb = sh.preb;
+  __syncthreads();  // a previous list of this launch may still read the prefix
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -366,7 +385,8 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(RowsArgs a) {
   // share that XCD's L2. An XCD's workgroups walk its large range, then its small range.
   const int pxl = (total_l + 7) / 8, pxs = (total_s + 7) / 8;
   const int xcd = blockIdx.x % 8, wg_per_xcd = gridDim.x / 8;
-  for (int slot = blockIdx.x / 8; slot < pxl + pxs; slot += wg_per_xcd) {
+  for (int gs = first_slot(first); gs < first + pxl + pxs; gs += wg_per_xcd) {
+    const int slot = gs - first;
     const bool large = slot < pxl;
     const int tile = large ? xcd * pxl + slot : xcd * pxs + (slot - pxl);
     if (tile >= (large ? total_l : total_s)) continue;
@@ -555,6 +575,24 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(RowsArgs a) {
       lds_barrier();
     }
   }
+  return first + pxl + pxs;
+}
+
+template <int BM, int BN, int MODE, bool FP8>
+__global__ __launch_bounds__(kThreads) void rows_kernel(RowsArgs a) {
+  __shared__ RowsShared sh;
+  extern __shared__ __attribute__((aligned(1024))) char ring[];
+  rows_list<BM, BN, MODE, FP8>(a, 0, sh, ring);
+}
+
+// Two independent row-grouped GEMMs in one persistent launch: the second's tiles fill the
+// workgroups that the first leaves idle in its last round, and one kernel boundary goes away.
+template <int BM1, int BN1, int MODE1, int BM2, int BN2, int MODE2>
+__global__ __launch_bounds__(kThreads) void rows_pair_kernel(RowsArgs a, RowsArgs b) {
+  __shared__ RowsShared sh;
+  extern __shared__ __attribute__((aligned(1024))) char ring[];
+  const int f = rows_list<BM1, BN1, MODE1, false>(a, 0, sh, ring);
+  rows_list<BM2, BN2, MODE2, false>(b, f, sh, ring);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -631,26 +669,30 @@ MOE_DEV void wgrad_tile(const WgradArgs& a, int tile, char* ring, int tid, int l
 template <int BM, int BN>
 MOE_DEV int wgrad_tiles(const WgradArgs& a) { return a.El * ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN); }
 
-// Persistent over the tiles of up to two independent weight gradients in one launch (b.El = 0:
-// none), so the second fills the first one's last round. Each XCD owns a contiguous range of
-// a's tiles and one of b's, and walks them in that order.
+// The tiles of one weight gradient (a.El = 0: none) from per-XCD slot `first` on, in the slot
+// sequence of rows_list; each XCD owns a contiguous range of the tiles. Returns the slot after
+// the last.
+template <int BM, int BN>
+MOE_DEV int wgrad_list(const WgradArgs& a, int first, char* ring) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ta = a.El > 0 ? wgrad_tiles<BM, BN>(a) : 0;
+  const int pxa = (ta + 7) / 8;
+  const int xcd = blockIdx.x % 8, wg_per_xcd = gridDim.x / 8;
+  for (int gs = first_slot(first); gs < first + pxa; gs += wg_per_xcd) {
+    const int tile = xcd * pxa + (gs - first);
+    if (tile < ta) wgrad_tile<BM, BN>(a, tile, ring, tid, lane, wave);
+  }
+  return first + pxa;
+}
+
+// Up to two independent weight gradients in one persistent launch, so the second fills the
+// first one's last round.
 template <int BM, int BN>
 __global__ __launch_bounds__(kThreads) void wgrad_kernel(WgradArgs a, WgradArgs b) {
   extern __shared__ __attribute__((aligned(1024))) char ring[];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int ta = wgrad_tiles<BM, BN>(a), tb = b.El > 0 ? wgrad_tiles<BM, BN>(b) : 0;
-  const int pxa = (ta + 7) / 8, pxb = (tb + 7) / 8;
-  const int xcd = blockIdx.x % 8, wg_per_xcd = gridDim.x / 8;
-  for (int slot = blockIdx.x / 8; slot < pxa + pxb; slot += wg_per_xcd) {
-    if (slot < pxa) {
-      const int tile = xcd * pxa + slot;
-      if (tile < ta) wgrad_tile<BM, BN>(a, tile, ring, tid, lane, wave);
-    } else {
-      const int tile = xcd * pxb + (slot - pxa);
-      if (tile < tb) wgrad_tile<BM, BN>(b, tile, ring, tid, lane, wave);
-    }
-  }
+  const int f = wgrad_list<BM, BN>(a, 0, ring);
+  wgrad_list<BM, BN>(b, f, ring);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -718,52 +760,137 @@ hipError_t run_wgrad(const char* name, const WgradArgs& a, const WgradArgs& b, h
 
 using namespace gg;
 
+// Argument sets of the BF16 expert GEMMs for chunks c0 .. c0 + nc - 1.
+static RowsArgs gateup_args(const ExpertGemm& g, int c0, int nc) {
+  RowsArgs a{};
+  a.A = g.xd; a.B = g.w1; a.C = (uint16_t*)g.h; a.C2 = (uint16_t*)g.gu;
+  a.lda = g.H; a.ldc = g.I; a.strideB = (int64_t)2 * g.I * g.H; a.K = g.H; a.N = g.I; a.I = g.I;
+  a.offsets = g.offsets; a.El = g.El; a.c0 = c0; a.nc = nc; a.P_c = g.P_c;
+  return a;
+}
+static RowsArgs down_args(const ExpertGemm& g, int c0, int nc) {
+  RowsArgs b{};
+  b.A = g.h; b.B = g.w2; b.C = (uint16_t*)g.yd;
+  b.lda = g.I; b.ldc = g.H; b.strideB = (int64_t)g.H * g.I; b.K = g.I; b.N = g.H; b.I = g.I;
+  b.offsets = g.offsets; b.El = g.El; b.c0 = c0; b.nc = nc; b.P_c = g.P_c;
+  return b;
+}
+static RowsArgs down_dgrad_args(const ExpertGemm& g, int c0, int nc) {
+  RowsArgs a{};
+  a.A = g.dyd; a.B = g.w2; a.C = (uint16_t*)g.dgu; a.aux = (const uint16_t*)g.gu;
+  a.lda = g.H; a.ldc = 2 * g.I; a.strideB = (int64_t)g.H * g.I; a.K = g.H; a.N = g.I; a.I = g.I;
+  a.offsets = g.offsets; a.El = g.El; a.c0 = c0; a.nc = nc; a.P_c = g.P_c;
+  return a;
+}
+static RowsArgs gateup_dgrad_args(const ExpertGemm& g, int c0, int nc) {
+  RowsArgs b{};
+  b.A = g.dgu; b.B = g.w1; b.C = (uint16_t*)g.dxd;
+  b.lda = 2 * g.I; b.ldc = g.H; b.strideB = (int64_t)2 * g.I * g.H; b.K = 2 * g.I; b.N = g.H; b.I = g.I;
+  b.offsets = g.offsets; b.El = g.El; b.c0 = c0; b.nc = nc; b.P_c = g.P_c;
+  return b;
+}
+// dW1[e] [2I, H] = sum dgu^T xd (the longer tile list, first) and dW2[e] [H, I] = sum dyd^T h
+static void wgrad_args(const ExpertGemm& g, WgradArgs& w1, WgradArgs& w2) {
+  w1 = WgradArgs{};
+  w1.A = (const uint16_t*)g.dgu; w1.B = (const uint16_t*)g.xd; w1.C = (uint16_t*)g.dw1; w1.lda = 2 * g.I;
+  w1.ldb = g.H; w1.strideC = (int64_t)2 * g.I * g.H; w1.M = 2 * g.I; w1.N = g.H; w1.offsets = g.offsets;
+  w1.El = g.El; w1.n_chunks = g.n_chunks; w1.P_c = g.P_c;
+  w2 = WgradArgs{};
+  w2.A = (const uint16_t*)g.dyd; w2.B = (const uint16_t*)g.h; w2.C = (uint16_t*)g.dw2; w2.lda = g.H;
+  w2.ldb = g.I; w2.strideC = (int64_t)g.H * g.I; w2.M = g.H; w2.N = g.I; w2.offsets = g.offsets;
+  w2.El = g.El; w2.n_chunks = g.n_chunks; w2.P_c = g.P_c;
+}
+
+// Row tiles a launch of this GEMM can hold at most: per chunk floor(P_c / BM) + E_local row tiles
+// (every expert adds at most one partial tile) times the column tiles; the device-side count
+// decides the work.
+template <int BM, int BN, int MODE>
+static int64_t rows_tiles_bound(const RowsArgs& a) {
+  const int outn = (MODE == kGateUp) ? BN / 2 : BN;
+  return (int64_t)a.nc * (a.P_c / BM + a.El) * ((a.N + outn - 1) / outn);
+}
+
+template <int BM1, int BN1, int MODE1, int BM2, int BN2, int MODE2>
+static hipError_t run_pair(const char* name, const RowsArgs& a, const RowsArgs& b, hipStream_t s) {
+  const size_t l1 = rows_lds_bytes<BM1, BN1, MODE1>(), l2 = rows_lds_bytes<BM2, BN2, MODE2>();
+  const size_t lds = l1 > l2 ? l1 : l2;
+  auto k = rows_pair_kernel<BM1, BN1, MODE1, BM2, BN2, MODE2>;
+  hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const int64_t grid = persistent_grid(rows_tiles_bound<BM1, BN1, MODE1>(a) + rows_tiles_bound<BM2, BN2, MODE2>(b));
+  if (grid <= 0) return hipSuccess;
+  {
+    MOE_TRACE(name, s);
+    MOE_LAUNCH(k, dim3((unsigned)grid), dim3(kThreads), lds, s, a, b);
+  }
+  return hipGetLastError();
+}
+
+// Tile shapes: 256 x 256 everywhere except down dgrad (128 x 256: its N = I gives few column
+// tiles, and 128-row tiles keep more CUs busy).
+#define MOE_GATEUP 256, 256, kGateUp
+#define MOE_DOWN 256, 256, kDown
+#define MOE_DDGRAD 128, 256, kDownBwd
+#define MOE_GUDGRAD 256, 256, kGateUpBwd
+
 hipError_t gg_expert_fwd_bf16(const void* xd, const void* w1, const void* w2, const int32_t* offsets,
                               void* gu, void* h, void* yd, int H, int I, int El, int c0, int nc,
                               int64_t P_c, hipStream_t s) {
-  RowsArgs a{};
-  a.A = xd; a.B = w1; a.C = (uint16_t*)h; a.C2 = (uint16_t*)gu;
-  a.lda = H; a.ldc = I; a.strideB = (int64_t)2 * I * H; a.K = H; a.N = I; a.I = I;
-  a.offsets = offsets; a.El = El; a.c0 = c0; a.nc = nc; a.P_c = P_c;
-  hipError_t e = run_rows<256, 256, kGateUp, false>("gemm_gateup_swiglu", a, s);
+  ExpertGemm g{};
+  g.xd = xd; g.w1 = w1; g.w2 = w2; g.offsets = offsets; g.gu = gu; g.h = h; g.yd = yd;
+  g.H = H; g.I = I; g.El = El; g.P_c = P_c;
+  hipError_t e = run_rows<MOE_GATEUP, false>("gemm_gateup_swiglu", gateup_args(g, c0, nc), s);
   if (e != hipSuccess) return e;
-  RowsArgs b{};
-  b.A = h; b.B = w2; b.C = (uint16_t*)yd;
-  b.lda = I; b.ldc = H; b.strideB = (int64_t)H * I; b.K = I; b.N = H; b.I = I;
-  b.offsets = offsets; b.El = El; b.c0 = c0; b.nc = nc; b.P_c = P_c;
-  return run_rows<256, 256, kDown, false>("gemm_down", b, s);
+  return run_rows<MOE_DOWN, false>("gemm_down", down_args(g, c0, nc), s);
 }
 
 hipError_t gg_expert_dgrad_bf16(const void* dyd, const void* gu, const void* w1, const void* w2,
                                 const int32_t* offsets, void* dgu, void* dxd, int H, int I, int El,
                                 int c0, int nc, int64_t P_c, hipStream_t s) {
-  RowsArgs a{};
-  a.A = dyd; a.B = w2; a.C = (uint16_t*)dgu; a.aux = (const uint16_t*)gu;
-  a.lda = H; a.ldc = 2 * I; a.strideB = (int64_t)H * I; a.K = H; a.N = I; a.I = I;
-  a.offsets = offsets; a.El = El; a.c0 = c0; a.nc = nc; a.P_c = P_c;
-  hipError_t e = run_rows<128, 256, kDownBwd, false>("gemm_down_dgrad_swiglu", a, s);
+  ExpertGemm g{};
+  g.dyd = dyd; g.gu = (void*)gu; g.w1 = w1; g.w2 = w2; g.offsets = offsets; g.dgu = dgu; g.dxd = dxd;
+  g.H = H; g.I = I; g.El = El; g.P_c = P_c;
+  hipError_t e = run_rows<MOE_DDGRAD, false>("gemm_down_dgrad_swiglu", down_dgrad_args(g, c0, nc), s);
   if (e != hipSuccess) return e;
-  RowsArgs b{};
-  b.A = dgu; b.B = w1; b.C = (uint16_t*)dxd;
-  b.lda = 2 * I; b.ldc = H; b.strideB = (int64_t)2 * I * H; b.K = 2 * I; b.N = H; b.I = I;
-  b.offsets = offsets; b.El = El; b.c0 = c0; b.nc = nc; b.P_c = P_c;
-  return run_rows<256, 256, kGateUpBwd, false>("gemm_gateup_dgrad", b, s);
+  return run_rows<MOE_GUDGRAD, false>("gemm_gateup_dgrad", gateup_dgrad_args(g, c0, nc), s);
 }
 
 hipError_t gg_expert_wgrad_bf16(const void* dyd, const void* dgu, const void* xd, const void* h,
                                 const int32_t* offsets, void* dw1, void* dw2, int H, int I, int El,
                                 int n, int64_t P_c, hipStream_t s) {
-  // dW2[e] [H, I] = sum dyd^T h
-  WgradArgs a{};
-  a.A = (const uint16_t*)dyd; a.B = (const uint16_t*)h; a.C = (uint16_t*)dw2; a.lda = H; a.ldb = I;
-  a.strideC = (int64_t)H * I; a.M = H; a.N = I; a.offsets = offsets; a.El = El; a.n_chunks = n; a.P_c = P_c;
-  // dW1[e] [2I, H] = sum dgu^T xd
-  WgradArgs b{};
-  b.A = (const uint16_t*)dgu; b.B = (const uint16_t*)xd; b.C = (uint16_t*)dw1; b.lda = 2 * I; b.ldb = H;
-  b.strideC = (int64_t)2 * I * H; b.M = 2 * I; b.N = H; b.offsets = offsets; b.El = El; b.n_chunks = n; b.P_c = P_c;
-  // both in one launch: dW1's tiles (the longer list) first, dW2's fill the last round
-  return run_wgrad<256, 256>("gemm_wgrad", b, a, s);
+  ExpertGemm g{};
+  g.dyd = dyd; g.dgu = (void*)dgu; g.xd = xd; g.h = (void*)h; g.offsets = offsets; g.dw1 = dw1; g.dw2 = dw2;
+  g.H = H; g.I = I; g.El = El; g.n_chunks = n; g.P_c = P_c;
+  WgradArgs a, b;
+  wgrad_args(g, a, b);
+  return run_wgrad<256, 256>("gemm_wgrad", a, b, s);
 }
+
+// Launches of the layer schedule (one chunk each; the pairs take independent work of two steps).
+hipError_t gg_gateup(const ExpertGemm& g, int c, hipStream_t s) {
+  return run_rows<MOE_GATEUP, false>("gemm_gateup_swiglu", gateup_args(g, c, 1), s);
+}
+hipError_t gg_down(const ExpertGemm& g, int c, hipStream_t s) {
+  return run_rows<MOE_DOWN, false>("gemm_down", down_args(g, c, 1), s);
+}
+hipError_t gg_down_then_gateup(const ExpertGemm& g, int c, int c2, hipStream_t s) {
+  return run_pair<MOE_DOWN, MOE_GATEUP>("gemm_down+gateup_swiglu", down_args(g, c, 1), gateup_args(g, c2, 1), s);
+}
+hipError_t gg_down_dgrad(const ExpertGemm& g, int c, hipStream_t s) {
+  return run_rows<MOE_DDGRAD, false>("gemm_down_dgrad_swiglu", down_dgrad_args(g, c, 1), s);
+}
+hipError_t gg_gateup_dgrad_then_down_dgrad(const ExpertGemm& g, int c, int c2, hipStream_t s) {
+  return run_pair<MOE_GUDGRAD, MOE_DDGRAD>("gemm_gateup_dgrad+down_dgrad_swiglu", gateup_dgrad_args(g, c, 1),
+                                           down_dgrad_args(g, c2, 1), s);
+}
+hipError_t gg_gateup_dgrad(const ExpertGemm& g, int c, hipStream_t s) {
+  return run_rows<MOE_GUDGRAD, false>("gemm_gateup_dgrad", gateup_dgrad_args(g, c, 1), s);
+}
+
+#undef MOE_GATEUP
+#undef MOE_DOWN
+#undef MOE_DDGRAD
+#undef MOE_GUDGRAD
 
 // FP8 forward: gate/up on FP8 MFMA with s_row * s_col dequantisation and SwiGLU -> h (BF16);
 // h quantised per row to e4m3 (codes stored after the BF16 values in the h buffer); down on FP8

@@ -69,6 +69,25 @@ hipError_t gg_expert_dgrad_bf16(const void* dyd, const void* gu, const void* w1,
 hipError_t gg_expert_wgrad_bf16(const void* dyd, const void* dgu, const void* xd, const void* h,
                                 const int32_t* offsets, void* dw1, void* dw2, int H, int I, int El,
                                 int n, int64_t P_c, hipStream_t s);
+// Operands of the BF16 expert GEMMs as the layer schedule launches them (device pointers; the
+// ones a launch does not use may be NULL).
+struct ExpertGemm {
+  const void* xd; const void* w1; const void* w2; void* gu; void* h; void* yd;
+  const void* dyd; void* dgu; void* dxd; void* dw1; void* dw2;
+  const int32_t* offsets;
+  int H, I, El, n_chunks;
+  int64_t P_c;
+};
+// One chunk's gate/up (+SwiGLU) or down GEMM; down of chunk c and gate/up of chunk c2 in one
+// persistent launch (independent work: the second fills the first's last round).
+hipError_t gg_gateup(const ExpertGemm& g, int c, hipStream_t s);
+hipError_t gg_down(const ExpertGemm& g, int c, hipStream_t s);
+hipError_t gg_down_then_gateup(const ExpertGemm& g, int c, int c2, hipStream_t s);
+// Input gradients of chunk c: down dgrad (+SwiGLU backward), gate/up dgrad, and gate/up dgrad
+// of chunk c with down dgrad of chunk c2 in one launch.
+hipError_t gg_down_dgrad(const ExpertGemm& g, int c, hipStream_t s);
+hipError_t gg_gateup_dgrad(const ExpertGemm& g, int c, hipStream_t s);
+hipError_t gg_gateup_dgrad_then_down_dgrad(const ExpertGemm& g, int c, int c2, hipStream_t s);
 // paged activation stash (stash.hip): store = rows -> pool pages, else pool pages -> rows
 hipError_t launch_stash_copy(bool store, const void* from, const float* from_scale, void* to,
                              float* to_scale, int64_t live_rows, int64_t row_bytes, int64_t num_pages,

@@ -51,9 +51,10 @@ def test_small_forward_backward(cfg):
     harness.check_backward(run, ref)
 
 
-@pytest.mark.parametrize("cfg", SMALL[1:4], ids=[c.name for c in SMALL[1:4]])
+@pytest.mark.parametrize("cfg", SMALL[1:6], ids=[c.name for c in SMALL[1:6]])
 def test_stage_calls_match_layer_primitive(cfg):
-    """chunk = -1 stage calls on one stream produce bitwise the layer primitive's results."""
+    """chunk = -1 stage calls on one stream produce bitwise the layer primitive's results (which,
+    for BF16, issues independent GEMMs of neighbouring chunks as one launch)."""
     _require_gpu()
     a = harness.run_gpu(cfg, layer=True)
     b = harness.run_gpu(cfg, layer=False, two_streams=False)
@@ -146,34 +147,40 @@ def test_full_fused_16k_forward_backward():
     print("[fb16k bwd]", harness.check_backward(run, ref), flush=True)
 
 
-def test_backward_launch_order_input_grad_before_wgrad():
-    """Every chunk's input-gradient work (combine backward, expert dgrad, dispatch backward) is
-    issued before the expert weight-gradient GEMMs, chunk c+1's routing/dispatch is issued before
-    chunk c's combine, and each kernel runs on the stream the two-stream schedule gives it."""
+@pytest.mark.parametrize("cfg", [SMALL[3], SMALL[4]], ids=[SMALL[3].name, SMALL[4].name])
+def test_layer_launch_order_and_streams(cfg):
+    """The fused BF16 primitive's launches: down of chunk c shares a launch with gate/up of chunk
+    c+1, gate/up dgrad of chunk c with down dgrad of chunk c+1; every chunk's input-gradient work
+    is issued before the expert weight gradients; chunk c+1's routing/dispatch is issued before
+    chunk c's combine; and each kernel runs on the stream the two-stream schedule gives it."""
     _require_gpu()
     import combine_moe_route_02_amd as mh
-    cfg = SMALL[3]
+    n = cfg.n_chunks
     mh.moe_trace_enable(False)
     try:
-        run = harness.run_gpu(cfg)
+        harness.run_gpu(cfg)
     finally:
         mh.moe_trace_disable()
     log = mh.moe_trace_entries()
-    names = [n for n, _, _ in log]
-    first_wgrad = min(i for i, n in enumerate(names) if n.startswith("gemm_wgrad"))
-    for kind in ("combine_bwd", "gemm_down_dgrad_swiglu", "gemm_gateup_dgrad", "dispatch_bwd"):
-        idx = [i for i, n in enumerate(names) if n == kind]
-        assert len(idx) == cfg.n_chunks, (kind, idx)
-        assert max(idx) < first_wgrad, kind
+    names = [nm for nm, _, _ in log]
+    counts = {k: names.count(k) for k in set(names)}
+    expect = {"gemm_gateup_swiglu": 1, "gemm_down+gateup_swiglu": n - 1, "gemm_down": 1, "combine": n,
+              "combine_bwd": n, "gemm_down_dgrad_swiglu": 1, "gemm_gateup_dgrad+down_dgrad_swiglu": n - 1,
+              "gemm_gateup_dgrad": 1, "dispatch_bwd": n, "gemm_wgrad": 1, "dispatch": n}
+    for k, v in expect.items():
+        assert counts.get(k, 0) == v, (k, counts.get(k, 0), v)
+    first_wgrad = names.index("gemm_wgrad")
+    for kind in ("combine_bwd", "gemm_down_dgrad_swiglu", "gemm_gateup_dgrad+down_dgrad_swiglu",
+                 "gemm_gateup_dgrad", "dispatch_bwd"):
+        assert max(i for i, nm in enumerate(names) if nm == kind) < first_wgrad, kind
     # forward overlap order: route of chunk 1 precedes combine of chunk 0
     assert names.index("route_topk", names.index("route_topk") + 1) < names.index("combine")
-    # stream placement: the first chunk's routing/dispatch (nothing to overlap it with) runs on
-    # the compute stream; later chunks' routing/dispatch and the combines run on the auxiliary
-    # stream
+
     def streams_of(kind):
-        return [s for n, s, _ in log if n == kind]
+        return [st for nm, st, _ in log if nm == kind]
     compute = streams_of("gemm_gateup_swiglu")[0]
-    assert set(streams_of("gemm_gateup_swiglu") + streams_of("gemm_wgrad")) == {compute}
+    gemms = [k for k in expect if k.startswith("gemm_")]
+    assert set(sum((streams_of(k) for k in gemms), [])) == {compute}
     disp, comb = streams_of("dispatch"), streams_of("combine")
     assert disp[0] == compute
     aux = disp[1]
