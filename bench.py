@@ -46,6 +46,8 @@ KERNEL_SYMBOLS = {
     "gemm_gateup_dgrad": ("grouped_gemm.hip", "rows_kernel<256, 256, 3, false>"),
     "gemm_down+gateup_swiglu": ("grouped_gemm.hip", "rows_pair_kernel<256, 256, 1, 256, 256, 0>"),
     "gemm_gateup_dgrad+down_dgrad_swiglu": ("grouped_gemm.hip", "rows_pair_kernel<256, 256, 3, 128, 256, 2>"),
+    "gemm_gateup_dgrad+wgrad_w2": ("grouped_gemm.hip", "rows_wgrad_kernel<256, 256, 3, 256, 256>"),
+    "gemm_wgrad_w1": ("grouped_gemm.hip", "wgrad1_kernel<256, 256>"),
     "gemm_wgrad": ("grouped_gemm.hip", "wgrad_kernel<256, 256>"),
     "gemm_router_wgrad": ("gemm.hip", "router_wgrad_kernel"),
     "router_reduce": ("gemm.hip", "reduce_partials_kernel"),
@@ -143,7 +145,7 @@ def committed_traffic(name: str):
 
 GEMM_KERNELS = {"gemm_gateup_swiglu", "gemm_down", "gemm_down_dgrad_swiglu", "gemm_gateup_dgrad",
                 "gemm_wgrad", "gemm_router_wgrad", "gemm_down+gateup_swiglu",
-                "gemm_gateup_dgrad+down_dgrad_swiglu"}
+                "gemm_gateup_dgrad+down_dgrad_swiglu", "gemm_gateup_dgrad+wgrad_w2", "gemm_wgrad_w1"}
 
 
 def algorithmic_work(cfg, counts, offsets, k_sel_local_tokens):
@@ -176,8 +178,9 @@ def algorithmic_work(cfg, counts, offsets, k_sel_local_tokens):
 def fused_gemm_work(cfg, Nc):
     """The fused step's BF16 GEMM launches (the layer primitive merges independent GEMMs of
     neighbouring chunks): name -> ((flops, unit), HBM bytes) per step, from the local rows per chunk
-    Nc. Gate/up and down dgrad run alone for chunk 0, down and gate/up dgrad alone for the last
-    chunk; each pair launch does down (gate/up dgrad) of chunk c with gate/up (down dgrad) of c+1."""
+    Nc. Gate/up and down dgrad run alone for chunk 0 and down alone for the last chunk; each pair
+    launch does down (gate/up dgrad) of chunk c with gate/up (down dgrad) of c+1; the last chunk's
+    gate/up dgrad runs with dW2 over all rows, then dW1 alone."""
     H, I, El, s, n = cfg.H, cfg.I, cfg.E_local, 2, len(Nc)
     w1, w2 = El * 2 * I * H * s, El * H * I * s
     gu_f = lambda m: 2.0 * m * H * 2 * I
@@ -187,6 +190,9 @@ def fused_gemm_work(cfg, Nc):
     ddg_b = lambda m: m * H * s + w2 + 2 * m * 2 * I * s
     gudg_b = lambda m: m * 2 * I * s + w1 + m * H * s
     pairs = range(n - 1)
+    N = sum(Nc)
+    dw2_f, dw2_b = 2.0 * N * H * I, N * H * s + N * I * s + w2
+    dw1_f, dw1_b = 2.0 * N * 2 * I * H, N * 2 * I * s + N * H * s + w1
     return {
         "gemm_gateup_swiglu": ((gu_f(Nc[0]), "flop"), gu_b(Nc[0])),
         "gemm_down+gateup_swiglu": ((sum(dn_f(Nc[c]) + gu_f(Nc[c + 1]) for c in pairs), "flop"),
@@ -195,7 +201,8 @@ def fused_gemm_work(cfg, Nc):
         "gemm_down_dgrad_swiglu": ((dn_f(Nc[0]), "flop"), ddg_b(Nc[0])),
         "gemm_gateup_dgrad+down_dgrad_swiglu": ((sum(gu_f(Nc[c]) + dn_f(Nc[c + 1]) for c in pairs), "flop"),
                                                 sum(gudg_b(Nc[c]) + ddg_b(Nc[c + 1]) for c in pairs)),
-        "gemm_gateup_dgrad": ((gu_f(Nc[-1]), "flop"), gudg_b(Nc[-1])),
+        "gemm_gateup_dgrad+wgrad_w2": ((gu_f(Nc[-1]) + dw2_f, "flop"), gudg_b(Nc[-1]) + dw2_b),
+        "gemm_wgrad_w1": ((dw1_f, "flop"), dw1_b),
     }
 
 

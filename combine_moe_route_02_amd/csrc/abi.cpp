@@ -562,9 +562,10 @@ static moe_status backward_sched(const moe_desc* d, const moe_tensors* t, hipStr
 // so the layer issues independent GEMMs of neighbouring steps as one launch: down of chunk c with
 // gate/up of chunk c+1, and gate/up dgrad of chunk c with down dgrad of chunk c+1. Every tile
 // computes exactly what the single launches compute, so the results are bitwise those of the
-// stage calls. The last chunk's gate/up dgrad stays its own launch: its dispatch backward then
-// overlaps the weight gradients instead of waiting for them (input gradients before weight
-// gradients).
+// stage calls. The weight gradients split by what they need: dW2 (dyd^T h, ready once every
+// combine backward has run) shares a launch with the last chunk's gate/up dgrad, and dW1 (dgu^T
+// xd) runs alone after it, beside the last chunk's dispatch backward (input gradients before the
+// weight gradient that waits for them).
 static moe::ExpertGemm expert_gemm(const moe_desc* d, const moe_tensors* t) {
   moe::ExpertGemm g{};
   g.xd = t->xd; g.w1 = t->w1; g.w2 = t->w2; g.gu = t->gu; g.h = t->h; g.yd = t->yd;
@@ -631,7 +632,7 @@ static moe_status forward_sched_merged(const moe_desc* d, const moe_tensors* t, 
   return MOE_OK;
 }
 
-//   compute: CB0 DDG0 | wait(cb1) [GUDG0 DDG1] | wait(cb2) [GUDG1 DDG2] | ... | GUDG n-1, W, wait(done)
+//   compute: CB0 DDG0 | wait(cb1) [GUDG0 DDG1] | ... | [GUDG n-1, dW2], dW1, wait(done)
 //   aux:     wait(cb0) CB1 RB0 | CB2 RB1 wait(dg0) DB0 | CB3 RB2 wait(dg1) DB1 | ... | wait(dg n-1) DB n-1
 static moe_status backward_sched_merged(const moe_desc* d, const moe_tensors* t, hipStream_t cs, hipStream_t as) {
   const int n = d->n_chunks;
@@ -666,7 +667,7 @@ static moe_status backward_sched_merged(const moe_desc* d, const moe_tensors* t,
       if (two) MOE_HIP(hipStreamWaitEvent(cs, cb[c + 1], 0), "hipStreamWaitEvent");
       MOE_HIP(moe::gg_gateup_dgrad_then_down_dgrad(g, c, c + 1, cs), "expert_dgrad");
     } else {
-      MOE_HIP(moe::gg_gateup_dgrad(g, c, cs), "expert_dgrad");
+      MOE_HIP(moe::gg_gateup_dgrad_then_wgrad2(g, c, cs), "expert_dgrad");
     }
     if (two) MOE_HIP(hipEventRecord(dg[c], cs), "hipEventRecord");
     if (c + 1 < n) {
@@ -679,7 +680,7 @@ static moe_status backward_sched_merged(const moe_desc* d, const moe_tensors* t,
     if (two) MOE_HIP(hipStreamWaitEvent(as, dg[c], 0), "hipStreamWaitEvent");
     MOE_TRY(moe_dispatch_bwd(d, c, t->dxd, t->row_of, t->topk_idx, t->dlogits, t->w_r, t->dx, side));
   }
-  MOE_TRY(moe_expert_wgrad(d, t->dyd, t->dgu, t->xd, t->h, t->offsets, t->dw1, t->dw2, cs));
+  MOE_HIP(moe::gg_wgrad1(g, cs), "expert_wgrad");
   if (two) {
     MOE_HIP(hipEventRecord(done, as), "hipEventRecord");
     MOE_HIP(hipStreamWaitEvent(cs, done, 0), "hipStreamWaitEvent");

@@ -695,6 +695,23 @@ __global__ __launch_bounds__(kThreads) void wgrad_kernel(WgradArgs a, WgradArgs 
   wgrad_list<BM, BN>(b, f, ring);
 }
 
+// One weight gradient alone (dW1 of the layer schedule).
+template <int BM, int BN>
+__global__ __launch_bounds__(kThreads) void wgrad1_kernel(WgradArgs a) {
+  extern __shared__ __attribute__((aligned(1024))) char ring[];
+  wgrad_list<BM, BN>(a, 0, ring);
+}
+
+// A row-grouped GEMM and an independent weight gradient in one launch (the last chunk's gate/up
+// dgrad with dW2, whose tiles fill the dgrad's last round).
+template <int BM1, int BN1, int MODE1, int BM, int BN>
+__global__ __launch_bounds__(kThreads) void rows_wgrad_kernel(RowsArgs r, WgradArgs a) {
+  __shared__ RowsShared sh;
+  extern __shared__ __attribute__((aligned(1024))) char ring[];
+  const int f = rows_list<BM1, BN1, MODE1, false>(r, 0, sh, ring);
+  wgrad_list<BM, BN>(a, f, ring);
+}
+
 // ---------------------------------------------------------------------------------------------
 // Launchers
 
@@ -826,6 +843,23 @@ static hipError_t run_pair(const char* name, const RowsArgs& a, const RowsArgs& 
   return hipGetLastError();
 }
 
+template <int BM1, int BN1, int MODE1, int BM, int BN>
+static hipError_t run_rows_wgrad(const char* name, const RowsArgs& r, const WgradArgs& a, hipStream_t s) {
+  const size_t l1 = rows_lds_bytes<BM1, BN1, MODE1>(), l2 = wgrad_lds_bytes<BM, BN>();
+  const size_t lds = l1 > l2 ? l1 : l2;
+  auto k = rows_wgrad_kernel<BM1, BN1, MODE1, BM, BN>;
+  hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const int64_t tw = a.El > 0 ? (int64_t)a.El * ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) : 0;
+  const int64_t grid = persistent_grid(rows_tiles_bound<BM1, BN1, MODE1>(r) + tw);
+  if (grid <= 0) return hipSuccess;
+  {
+    MOE_TRACE(name, s);
+    MOE_LAUNCH(k, dim3((unsigned)grid), dim3(kThreads), lds, s, r, a);
+  }
+  return hipGetLastError();
+}
+
 // Tile shapes: 256 x 256 everywhere except down dgrad (128 x 256: its N = I gives few column
 // tiles, and 128-row tiles keep more CUs busy).
 #define MOE_GATEUP 256, 256, kGateUp
@@ -885,6 +919,26 @@ hipError_t gg_gateup_dgrad_then_down_dgrad(const ExpertGemm& g, int c, int c2, h
 }
 hipError_t gg_gateup_dgrad(const ExpertGemm& g, int c, hipStream_t s) {
   return run_rows<MOE_GUDGRAD, false>("gemm_gateup_dgrad", gateup_dgrad_args(g, c, 1), s);
+}
+hipError_t gg_gateup_dgrad_then_wgrad2(const ExpertGemm& g, int c, hipStream_t s) {
+  WgradArgs w1, w2;
+  wgrad_args(g, w1, w2);
+  return run_rows_wgrad<MOE_GUDGRAD, 256, 256>("gemm_gateup_dgrad+wgrad_w2", gateup_dgrad_args(g, c, 1), w2, s);
+}
+hipError_t gg_wgrad1(const ExpertGemm& g, hipStream_t s) {
+  WgradArgs w1, w2;
+  wgrad_args(g, w1, w2);
+  const size_t lds = wgrad_lds_bytes<256, 256>();
+  auto k = wgrad1_kernel<256, 256>;
+  hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const int64_t grid = persistent_grid(w1.El > 0 ? (int64_t)w1.El * ((w1.M + 255) / 256) * ((w1.N + 255) / 256) : 0);
+  if (grid <= 0) return hipSuccess;
+  {
+    MOE_TRACE("gemm_wgrad_w1", s);
+    MOE_LAUNCH(k, dim3((unsigned)grid), dim3(kThreads), lds, s, w1);
+  }
+  return hipGetLastError();
 }
 
 #undef MOE_GATEUP

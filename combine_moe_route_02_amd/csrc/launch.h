@@ -88,6 +88,10 @@ hipError_t gg_down_then_gateup(const ExpertGemm& g, int c, int c2, hipStream_t s
 hipError_t gg_down_dgrad(const ExpertGemm& g, int c, hipStream_t s);
 hipError_t gg_gateup_dgrad(const ExpertGemm& g, int c, hipStream_t s);
 hipError_t gg_gateup_dgrad_then_down_dgrad(const ExpertGemm& g, int c, int c2, hipStream_t s);
+// Weight gradients split by what they need: dW2 = sum dyd^T h needs no input-gradient GEMM and
+// shares a launch with the last chunk's gate/up dgrad; dW1 = sum dgu^T xd follows alone.
+hipError_t gg_gateup_dgrad_then_wgrad2(const ExpertGemm& g, int c, hipStream_t s);
+hipError_t gg_wgrad1(const ExpertGemm& g, hipStream_t s);
 // paged activation stash (stash.hip): store = rows -> pool pages, else pool pages -> rows
 hipError_t launch_stash_copy(bool store, const void* from, const float* from_scale, void* to,
                              float* to_scale, int64_t live_rows, int64_t row_bytes, int64_t num_pages,

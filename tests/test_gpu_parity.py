@@ -150,9 +150,10 @@ def test_full_fused_16k_forward_backward():
 @pytest.mark.parametrize("cfg", [SMALL[3], SMALL[4]], ids=[SMALL[3].name, SMALL[4].name])
 def test_layer_launch_order_and_streams(cfg):
     """The fused BF16 primitive's launches: down of chunk c shares a launch with gate/up of chunk
-    c+1, gate/up dgrad of chunk c with down dgrad of chunk c+1; every chunk's input-gradient work
-    is issued before the expert weight gradients; chunk c+1's routing/dispatch is issued before
-    chunk c's combine; and each kernel runs on the stream the two-stream schedule gives it."""
+    c+1, gate/up dgrad of chunk c with down dgrad of chunk c+1, the last gate/up dgrad with dW2;
+    every chunk's input-gradient work is issued before dW1 (the weight gradient that needs it);
+    chunk c+1's routing/dispatch is issued before chunk c's combine; and each kernel runs on the
+    stream the two-stream schedule gives it."""
     _require_gpu()
     import combine_moe_route_02_amd as mh
     n = cfg.n_chunks
@@ -166,12 +167,13 @@ def test_layer_launch_order_and_streams(cfg):
     counts = {k: names.count(k) for k in set(names)}
     expect = {"gemm_gateup_swiglu": 1, "gemm_down+gateup_swiglu": n - 1, "gemm_down": 1, "combine": n,
               "combine_bwd": n, "gemm_down_dgrad_swiglu": 1, "gemm_gateup_dgrad+down_dgrad_swiglu": n - 1,
-              "gemm_gateup_dgrad": 1, "dispatch_bwd": n, "gemm_wgrad": 1, "dispatch": n}
+              "gemm_gateup_dgrad+wgrad_w2": 1, "gemm_wgrad_w1": 1, "dispatch_bwd": n, "dispatch": n,
+              "gemm_gateup_dgrad": 0, "gemm_wgrad": 0}
     for k, v in expect.items():
         assert counts.get(k, 0) == v, (k, counts.get(k, 0), v)
-    first_wgrad = names.index("gemm_wgrad")
+    first_wgrad = names.index("gemm_wgrad_w1")
     for kind in ("combine_bwd", "gemm_down_dgrad_swiglu", "gemm_gateup_dgrad+down_dgrad_swiglu",
-                 "gemm_gateup_dgrad", "dispatch_bwd"):
+                 "gemm_gateup_dgrad+wgrad_w2", "dispatch_bwd"):
         assert max(i for i, nm in enumerate(names) if nm == kind) < first_wgrad, kind
     # forward overlap order: route of chunk 1 precedes combine of chunk 0
     assert names.index("route_topk", names.index("route_topk") + 1) < names.index("combine")
