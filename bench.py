@@ -305,7 +305,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=30)  # the clocks take some tens of ms of load to settle
     ap.add_argument("--workload", default="fb16k")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -365,9 +365,34 @@ def main():
         fb()
     torch.cuda.synchronize()
 
-    # timed region: exactly `steps` fused steps, every kernel launch bracketed by HIP events on
-    # the stream it runs on
+    # per-kernel pass (before the timed region): `steps` fused steps with every kernel launch
+    # bracketed by HIP events on the stream it runs on; it gives each kernel's in-step duration
+    # and picks the dominant kernel, the largest share of the compute stream, whose work sets the
+    # step time (aux-stream kernels run beside a GEMM, so their in-step durations mostly measure
+    # how much that GEMM slowed them)
     mh.moe_trace_enable(True)
+    torch.cuda.synchronize()
+    p0 = time.perf_counter()
+    for _ in range(args.steps):
+        fb()
+    torch.cuda.synchronize()
+    ms_traced = (time.perf_counter() - p0) * 1e3 / args.steps
+    mh.moe_trace_disable()
+    entries = mh.moe_trace_entries()
+    comp = int(cs.cuda_stream)
+    on_compute = {n for n, st, _ in entries if int(st or 0) == comp}
+    on_compute -= {n for n, st, _ in entries if int(st or 0) != comp}
+    step_ms = {}
+    for n, _st, ms in entries:
+        step_ms[n] = step_ms.get(n, 0.0) + ms
+    dom = max((n for n in step_ms if n in on_compute), key=lambda n: step_ms[n])
+
+    # timed region: exactly `steps` fused steps; HIP events bracket the dominant kernel's launches
+    # only, so the rest of the step runs without instrumentation. Reading the log above left the
+    # GPU idle for some ms, so it is warmed up again first (the clocks drop when it idles).
+    for _ in range(args.warmup):
+        fb()
+    mh.moe_trace_enable_only(dom)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -375,10 +400,10 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     mh.moe_trace_disable()
-    entries = mh.moe_trace_entries()
+    dom_ms = [ms for n, _st, ms in mh.moe_trace_entries() if n == dom]
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
-    # the same loop without the launch log, for the tracing overhead
+    # the same loop without any launch log
     torch.cuda.synchronize()
     u0 = time.perf_counter()
     for _ in range(args.steps):
@@ -562,13 +587,8 @@ def main():
                 r = wk / (it / args.steps * 1e-3)
                 entry["isolated_frac"] = round(r / 1e12 / PEAK_BF16_TFLOPS if unit == "flop" else r / 1e9 / PEAK_HBM_GBS, 4)
         kernels[name] = entry
-    # dominant kernel: the largest share of the compute stream, whose work sets the step time
-    # (kernels on the auxiliary stream run beside it, so their in-step durations mostly measure
-    # how much they were slowed by the GEMM next to them, not their own cost)
-    on_compute = {n for n, st, _ in entries if int(st or 0) == int(cs.cuda_stream)}
-    on_compute -= {n for n, st, _ in entries if int(st or 0) != int(cs.cuda_stream)}
-    dom = max((n for n in per if n in on_compute), key=lambda n: per[n][1])
-    dcnt, dtot = per[dom]
+    # the dominant kernel's launches timed inside the timed region
+    dcnt, dtot = len(dom_ms), sum(dom_ms)
     wk, unit = work_f.get(dom, (None, None))
     if unit == "flop":
         ach = wk / (dtot / args.steps * 1e-3) / 1e12
@@ -596,6 +616,7 @@ def main():
                    "local_rows": N, "tokens_with_local_expert": Tt},
         "fwd_tokens_per_s": round(cfg.T / (ms_fwd * 1e-3), 1), "fwd_ms": round(ms_fwd, 4),
         "ms_per_step_untraced": round(ms_untraced, 4),
+        "ms_per_step_traced": round(ms_traced, 4),
         "isolated_kernel_ms_sum": round(iso_ms, 4),
         "gemm_tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 2) if gemm_ms > 0 else None,
         "roofline": roof, "kernels": kernels,

@@ -84,6 +84,7 @@ _SIGS = {
     "moe_extent_release": [c_void_p, c_int64],
     "moe_extent_current": [c_void_p, c_int64],
     "moe_trace_enable": [c_int32],
+    "moe_trace_enable_only": [c_char_p],
     "moe_trace_disable": [],
     "moe_trace_count": [],
     "moe_trace_entry": [c_int64, POINTER(c_char_p), POINTER(c_void_p), POINTER(ctypes.c_float)],
@@ -291,6 +292,11 @@ class ExtentTracker:
 
 def moe_trace_enable(timing: bool = False) -> None:
     _check(lib().moe_trace_enable(1 if timing else 0), "moe_trace_enable")
+
+
+def moe_trace_enable_only(name: str) -> None:
+    """Log every launch, with timing events on the launches called `name` only."""
+    _check(lib().moe_trace_enable_only(name.encode()), "moe_trace_enable_only")
 
 
 def moe_trace_disable() -> None:

@@ -20,6 +20,7 @@ struct Rec {
 struct State {
   bool on = false;
   bool timing = false;
+  std::string only;  // non-empty: timing events for launches of this name only
   std::vector<Rec> recs;
   std::vector<hipEvent_t> pool;  // reused across logs; grows on demand
   size_t used = 0;
@@ -45,7 +46,7 @@ bool active() { return g.on; }
 
 void begin(const char* name, hipStream_t s) {
   Rec r{name, s, -1, -1, false};
-  if (g.timing) {
+  if (g.timing && (g.only.empty() || g.only == name)) {
     r.ev0 = take_event();
     r.ev1 = take_event();
   }
@@ -86,10 +87,18 @@ extern "C" {
 moe_status moe_trace_enable(int32_t timing) {
   g.on = true;
   g.timing = timing != 0;
+  g.only.clear();
   g.recs.clear();
   g.used = 0;
   g.open = -1;
   g.err = hipSuccess;
+  return MOE_OK;
+}
+
+moe_status moe_trace_enable_only(const char* only) {
+  if (!only) return MOE_ERR_ARG;
+  moe_trace_enable(1);
+  g.only = only;
   return MOE_OK;
 }
 

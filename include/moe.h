@@ -286,6 +286,10 @@ int64_t moe_extent_current(const moe_extent_tracker* tr, int64_t required_rows);
  * (name: static string; ms: device duration, -1 without timing; waits for that entry's end
  * event). Tracing adds host work per launch; it is off by default. */
 moe_status moe_trace_enable(int32_t timing);
+/* As moe_trace_enable(1), but only launches whose name equals `only` (a NUL-terminated launch
+ * name, copied) get timing events; the others are logged with ms = -1. Lets a caller time one
+ * kernel kind with almost no instrumentation on the rest. MOE_ERR_ARG if `only` is NULL. */
+moe_status moe_trace_enable_only(const char* only);
 moe_status moe_trace_disable(void);
 int64_t moe_trace_count(void);
 moe_status moe_trace_entry(int64_t i, const char** name, void** stream, float* ms);

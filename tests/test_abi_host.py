@@ -150,3 +150,13 @@ def test_stash_argument_errors_before_any_launch():
     # an empty live prefix is valid and launches nothing (no GPU needed)
     assert L.moe_stash_store(None, None, 0, 16, None, None, 0, 1, None, None, 0, 0, None) == 0
     assert L.moe_stash_load(None, None, 0, 16, 0, 1, None, None, None, None, 0, None) == 0
+
+
+def test_trace_enable_only_host_side():
+    """The name-filtered launch log needs a name; enabling and disabling it touches no GPU."""
+    import combine_moe_route_02_amd as mh
+    L = mh.lib()
+    assert L.moe_trace_enable_only(None) == -1
+    mh.moe_trace_enable_only("gemm_wgrad_w1")
+    assert L.moe_trace_count() == 0
+    mh.moe_trace_disable()
