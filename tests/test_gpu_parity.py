@@ -212,6 +212,25 @@ def _check_fp8_weight_codes(run, ref):
 
 
 @pytest.mark.parametrize("cfg", FP8_SMALL, ids=[c.name for c in FP8_SMALL])
+def test_fp8_layer_matches_stage_calls(cfg):
+    """The FP8 layer forward (down of chunk c with gate/up of chunk c+1 in one launch) gives
+    bitwise the results of the chunk = -1 stage calls on one stream."""
+    _require_gpu()
+    a = harness.run_gpu(cfg, layer=True)
+    b = harness.run_gpu(cfg, layer=False, two_streams=False)
+    for name in ("topk_idx", "row_of", "src_token", "counts", "offsets"):
+        np.testing.assert_array_equal(harness.bits_np(a.bufs[name]), harness.bits_np(b.bufs[name]), err_msg=name)
+    # scales of the dispatched rows (rows past each chunk's N_c are never written)
+    offsets = a.bufs["offsets"].cpu().numpy()
+    for name in ("xd_scale", "h_scale"):
+        ga, gb = harness.bits_np(a.bufs[name]), harness.bits_np(b.bufs[name])
+        for c in range(cfg.n_chunks):
+            r0, n = c * a.desc.P_c, int(offsets[c, cfg.E_local])
+            np.testing.assert_array_equal(ga[r0:r0 + n], gb[r0:r0 + n], err_msg=f"{name} chunk {c}")
+    np.testing.assert_array_equal(harness.bits_np(a.bufs["out"])[:cfg.T], harness.bits_np(b.bufs["out"])[:cfg.T])
+
+
+@pytest.mark.parametrize("cfg", FP8_SMALL, ids=[c.name for c in FP8_SMALL])
 def test_fp8_forward_small(cfg):
     _require_gpu()
     print(f"[parity] {cfg}", flush=True)
