@@ -5,10 +5,13 @@
 // The expert FFN is a grouped GEMM whose groups are the local experts' row segments in the
 // expert-contiguous dispatch buffer (token-wise ChunkedEP, Megatron-LM PR 7342, "Summary": expert
 // compute per token chunk). Group sizes exist only on the device (the offset table written by
-// routing): every workgroup rebuilds the group -> tile prefix in LDS and takes one tile; nothing
-// returns to the host. Weight gradients iterate K over the rows of every chunk of one expert in
-// one FP32 reduction and convert once (the FP32-accumulate-then-convert rule that ChunkedEP's
-// "Numerical status -- unresolved" states for the router weights).
+// routing): every workgroup rebuilds the group -> tile prefix in LDS and walks its share of the
+// tiles (persistent, at most one workgroup per CU); nothing returns to the host. Weight gradients
+// iterate K over the rows of every chunk of one expert in one FP32 reduction and convert once
+// (the FP32-accumulate-then-convert rule that ChunkedEP's "Numerical status -- unresolved" states
+// for the router weights). One launch may carry the tile lists of two independent GEMMs (the
+// layer schedule's merged launches): the second list's tiles continue the first's round robin,
+// so the CUs that the first leaves idle in its last round start the second.
 //
 // Engine (one 512-thread workgroup = 8 waves in a 2 x 4 grid over a BM x BN output tile, two
 // waves per SIMD, so the second wave on a SIMD issues MFMAs while the first waits; four waves
@@ -916,9 +919,6 @@ hipError_t gg_down_dgrad(const ExpertGemm& g, int c, hipStream_t s) {
 hipError_t gg_gateup_dgrad_then_down_dgrad(const ExpertGemm& g, int c, int c2, hipStream_t s) {
   return run_pair<MOE_GUDGRAD, MOE_DDGRAD>("gemm_gateup_dgrad+down_dgrad_swiglu", gateup_dgrad_args(g, c, 1),
                                            down_dgrad_args(g, c2, 1), s);
-}
-hipError_t gg_gateup_dgrad(const ExpertGemm& g, int c, hipStream_t s) {
-  return run_rows<MOE_GUDGRAD, false>("gemm_gateup_dgrad", gateup_dgrad_args(g, c, 1), s);
 }
 hipError_t gg_gateup_dgrad_then_wgrad2(const ExpertGemm& g, int c, hipStream_t s) {
   WgradArgs w1, w2;

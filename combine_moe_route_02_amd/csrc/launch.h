@@ -83,10 +83,9 @@ struct ExpertGemm {
 hipError_t gg_gateup(const ExpertGemm& g, int c, hipStream_t s);
 hipError_t gg_down(const ExpertGemm& g, int c, hipStream_t s);
 hipError_t gg_down_then_gateup(const ExpertGemm& g, int c, int c2, hipStream_t s);
-// Input gradients of chunk c: down dgrad (+SwiGLU backward), gate/up dgrad, and gate/up dgrad
-// of chunk c with down dgrad of chunk c2 in one launch.
+// Input gradients: down dgrad (+SwiGLU backward) of chunk c, and gate/up dgrad of chunk c with
+// down dgrad of chunk c2 in one launch.
 hipError_t gg_down_dgrad(const ExpertGemm& g, int c, hipStream_t s);
-hipError_t gg_gateup_dgrad(const ExpertGemm& g, int c, hipStream_t s);
 hipError_t gg_gateup_dgrad_then_down_dgrad(const ExpertGemm& g, int c, int c2, hipStream_t s);
 // Weight gradients split by what they need: dW2 = sum dyd^T h needs no input-gradient GEMM and
 // shares a launch with the last chunk's gate/up dgrad; dW1 = sum dgu^T xd follows alone.
