@@ -26,8 +26,10 @@
  *   - Pointers named as device buffers are device (HBM) addresses, caller-owned; the library
  *     never allocates device memory and never synchronises the host. `stream` is a hipStream_t
  *     passed as void* (NULL = the null stream).
- *   - Host-side validation happens before any launch; on a non-OK status nothing was launched
- *     and moe_last_error() returns a thread-local message. MOE_ERR_HIP reports a launch error.
+ *   - Host-side validation happens before any launch: on MOE_ERR_ARG, MOE_ERR_CAPACITY or
+ *     MOE_ERR_UNSUPPORTED nothing was launched. MOE_ERR_HIP reports a failing HIP call; a call
+ *     that issues several kernels (chunk = -1, the layer primitives) may have queued the ones
+ *     before it. moe_last_error() returns a thread-local message for every non-OK status.
  *   - `chunk` selects one token chunk c in [0, n_chunks), or -1 for every chunk in order.
  *     Chunk c holds tokens [c*Tc, min(T, (c+1)*Tc)) with Tc = ceil(T / n_chunks), and owns the
  *     dispatch rows [c*P_c, (c+1)*P_c).
