@@ -17,6 +17,7 @@ from __future__ import annotations
 
 import numpy as np
 
+from .ffn import _segments as ffn_segments
 from .ffn import combine, silu
 from .routing import dispatch, layout, route
 
@@ -89,6 +90,60 @@ def quantize_rows(a: np.ndarray):
 
 def dequantize_rows(codes, scale):
     return e4m3_decode(codes) * np.asarray(scale, dtype=np.float64)[..., None]
+
+
+def quantize_cols_t(a: np.ndarray):
+    """Per-column absmax quantisation stored transposed: a [..., R, C] -> codes [..., C, R] and
+    scale [..., C], column j taking the role of a row in :func:`quantize_rows` (same FP32 steps).
+    Reading for the FP8 input gradients: they contract a weight matrix over its rows, so the
+    weight's scale must sit on its columns, and the transposed store makes the contracted
+    dimension contiguous."""
+    return quantize_rows(np.swapaxes(np.asarray(a, dtype=np.float32), -1, -2))
+
+
+def bf16_round(a: np.ndarray) -> np.ndarray:
+    """Round FP32 values to the nearest BF16 value, ties to even (finite inputs); FP32 out."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32)
+
+
+def ffn_bwd_fp8_dgrad(dyd, xd, gu, h, offsets, P_c, w1, w2):
+    """Expert FFN backward with FP8 input gradients (the survey's NEXT-1; the pages fix FP8 only
+    for payloads, so these are readings):
+      * dyd, the combine-backward payload, is stored in BF16 and quantised per row;
+      * W2[e] and W1[e] are quantised per column and transposed (:func:`quantize_cols_t`);
+      * dh = deq(dyd) deq(W2t[e])^T, then dG, dU as in ffn.ffn_bwd from the saved G, U;
+      * dgu = [dG dU] is stored in BF16 and quantised per row; dxd = deq(dgu) deq(W1t[e])^T;
+      * products accumulate exactly (FP64 here) and dequantise by s_row * s_col;
+      * the weight gradients stay BF16: dW2 = dyd^T h and dW1 = dgu^T xd from the unquantised
+        values (an FP8 weight gradient would need activation scales along the token dimension,
+        which per-row payload scales do not give).
+    Returns dgu, dxd, dw1, dw2 (FP64)."""
+    I = w1.shape[1] // 2
+    P, H = xd.shape
+    dyd = np.asarray(dyd, dtype=np.float64)
+    dyd_q = dequantize_rows(*quantize_rows(bf16_round(dyd)))
+    dgu = np.zeros((P, 2 * I))
+    dxd = np.zeros((P, H))
+    dw1 = np.zeros(w1.shape)
+    dw2 = np.zeros(w2.shape)
+    segs = [(e, r0, r1) for e, r0, r1 in ffn_segments(offsets, P_c) if r1 > r0]
+    for e, r0, r1 in segs:
+        w2t = dequantize_rows(*quantize_cols_t(w2[e]))          # [I, H]
+        g = gu[r0:r1, :I]
+        u = gu[r0:r1, I:]
+        sg = 1.0 / (1.0 + np.exp(-g))
+        dh = dyd_q[r0:r1] @ w2t.T
+        dgu[r0:r1, :I] = dh * u * sg * (1.0 + g * (1.0 - sg))
+        dgu[r0:r1, I:] = dh * g * sg
+        dw2[e] += dyd[r0:r1].T @ h[r0:r1]
+        dw1[e] += dgu[r0:r1].T @ xd[r0:r1]
+    dgu_q = dequantize_rows(*quantize_rows(bf16_round(dgu)))
+    for e, r0, r1 in segs:
+        w1t = dequantize_rows(*quantize_cols_t(w1[e]))          # [H, 2I]
+        dxd[r0:r1] = dgu_q[r0:r1] @ w1t.T
+    return dgu, dxd, dw1, dw2
 
 
 def forward(x, logits, w1, w2, *, k, e0, E_local, n_chunks, P_c=None, wq=None):

@@ -151,3 +151,75 @@ def test_fp8_forward_close_to_exact_forward():
     # codes of dispatched rows are the token's codes
     v = f8["src_token"] >= 0
     np.testing.assert_array_equal(f8["xdq"][v], f8["xq"][f8["src_token"][v]])
+
+
+# ----------------------------------------------------------------------------- FP8 input gradients
+
+def test_bf16_round_ties_to_even():
+    from oracle.fp8 import bf16_round
+    one = 1.0
+    vals = np.array([one, one + 2.0 ** -8, one + 3 * 2.0 ** -8, one + 2.0 ** -8 + 2.0 ** -20,
+                     -(one + 2.0 ** -8), 3.0], dtype=np.float32)
+    want = np.array([one, one, one + 2.0 ** -6, one + 2.0 ** -7, -one, 3.0], dtype=np.float32)
+    np.testing.assert_array_equal(bf16_round(vals), want)
+
+
+def test_quantize_cols_transposed_worked_example():
+    """Column j is quantised as a row would be and stored as row j of the transposed codes:
+    column 0 (absmax 448, inverse 1): 448 -> 0x7E, -224 -> 0xF6; column 1 (absmax 1, inverse 448):
+    1 -> 448 -> 0x7E, 0.5 -> 224 -> 0x76, scale 1/448; column 2 (all zero): codes 0, scale 1."""
+    from oracle.fp8 import quantize_cols_t
+    a = np.array([[448.0, 1.0, 0.0], [-224.0, 0.5, 0.0]], dtype=np.float32)
+    codes, scale = quantize_cols_t(a)
+    np.testing.assert_array_equal(codes, np.array([[0x7E, 0xF6], [0x7E, 0x76], [0, 0]], dtype=np.uint8))
+    np.testing.assert_array_equal(scale, np.array([1.0, np.float32(1.0) / np.float32(448.0), 1.0], dtype=np.float32))
+
+
+def _fp8_exact_case(seed=3):
+    """Two experts whose dyd rows hold values in {0, +-1/2, +-1} and a 3.5 (scale 3.5/448 = 2^-7)
+    and whose weight columns hold values in {0, +-1/4, +-1/2} and a +-1.75 (scale 2^-8): every
+    scale is a power of two and every scaled value an e4m3 value, so per-row and per-column
+    quantisation of these is lossless."""
+    rng = np.random.default_rng(seed)
+    H, I, El = 64, 32, 2
+    rows = [5, 7]
+    P_c = 16
+    offsets = np.array([[0, rows[0], rows[0] + rows[1]]])
+    dyd = rng.choice([0.0, 0.5, -0.5, 1.0, -1.0], size=(P_c, H))
+    dyd[:, 0] = 3.5
+    w1 = rng.choice([0.0, 0.25, -0.25, 0.5, -0.5], size=(El, 2 * I, H))
+    w1[:, 0, :] = 1.75
+    w2 = rng.choice([0.0, 0.25, -0.25, 0.5, -0.5], size=(El, H, I))
+    w2[:, 0, :] = -1.75
+    xd = rng.normal(size=(P_c, H))
+    gu = rng.normal(size=(P_c, 2 * I))
+    h = rng.normal(size=(P_c, I))
+    return dyd, xd, gu, h, offsets, P_c, w1, w2
+
+
+def test_fp8_dgrad_oracle_is_exact_on_e4m3_exact_inputs():
+    """With e4m3-exact dyd and W2, the FP8 dh (hence dgu and both weight gradients) equals the
+    exact backward's: a transposed or mis-scaled W2 path fails this."""
+    from oracle import ffn
+    from oracle.fp8 import ffn_bwd_fp8_dgrad
+    dyd, xd, gu, h, offsets, P_c, w1, w2 = _fp8_exact_case()
+    dgu8, dxd8, dw18, dw28 = ffn_bwd_fp8_dgrad(dyd, xd, gu, h, offsets, P_c, w1, w2)
+    dgu, dxd, dw1, dw2 = ffn.ffn_bwd(dyd, xd, gu, h, offsets, P_c, w1, w2)
+    np.testing.assert_allclose(dgu8, dgu, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dw18, dw1, rtol=0, atol=1e-9)
+    np.testing.assert_allclose(dw28, dw2, rtol=0, atol=1e-9)
+
+
+def test_fp8_dgrad_oracle_dxd_within_e4m3_bound():
+    """dgu is not e4m3-exact, so dxd carries its quantisation error: each dequantised value is
+    within 2^-4 relative (plus 2^-9 of the row scale) of the BF16-rounded dgu, which bounds the
+    relative L2 error of dxd by about 2^-4 times the condition of the product; W1 is e4m3-exact,
+    so a wrong transpose or a dropped scale (errors of order 1) fails."""
+    from oracle import ffn
+    from oracle.fp8 import ffn_bwd_fp8_dgrad
+    dyd, xd, gu, h, offsets, P_c, w1, w2 = _fp8_exact_case()
+    _, dxd8, _, _ = ffn_bwd_fp8_dgrad(dyd, xd, gu, h, offsets, P_c, w1, w2)
+    _, dxd, _, _ = ffn.ffn_bwd(dyd, xd, gu, h, offsets, P_c, w1, w2)
+    rows = slice(0, int(offsets[0, -1]))
+    err = np.linalg.norm(dxd8[rows] - dxd[rows]) / np.linalg.norm(dxd[rows])
+    assert 0 < err < 2.0 ** -4, err
