@@ -48,8 +48,19 @@ def e4m3_decode(codes: np.ndarray) -> np.ndarray:
 
 
 def e4m3_encode(v: np.ndarray) -> np.ndarray:
-    """Round FP32 values to e4m3fn codes: nearest, ties to even mantissa, saturating at 448."""
+    """Round FP32 values to e4m3fn codes: nearest, ties to even mantissa, saturating at 448.
+    Elementwise; large arrays go through in blocks of 2^20 values (same result, less memory)."""
     v = np.asarray(v, dtype=np.float32)
+    if v.size > 1 << 20:
+        flat = np.ascontiguousarray(v).reshape(-1)
+        out = np.empty(flat.size, dtype=np.uint8)
+        for i in range(0, flat.size, 1 << 20):
+            out[i:i + (1 << 20)] = _e4m3_encode_block(flat[i:i + (1 << 20)])
+        return out.reshape(v.shape)
+    return _e4m3_encode_block(v)
+
+
+def _e4m3_encode_block(v: np.ndarray) -> np.ndarray:
     a = np.abs(v).astype(np.float64)
     nan = np.isnan(a)
     a = np.where(nan, 0.0, a)
@@ -123,27 +134,47 @@ def ffn_bwd_fp8_dgrad(dyd, xd, gu, h, offsets, P_c, w1, w2):
     I = w1.shape[1] // 2
     P, H = xd.shape
     dyd = np.asarray(dyd, dtype=np.float64)
-    dyd_q = dequantize_rows(*quantize_rows(bf16_round(dyd)))
     dgu = np.zeros((P, 2 * I))
     dxd = np.zeros((P, H))
     dw1 = np.zeros(w1.shape)
     dw2 = np.zeros(w2.shape)
-    segs = [(e, r0, r1) for e, r0, r1 in ffn_segments(offsets, P_c) if r1 > r0]
-    for e, r0, r1 in segs:
-        w2t = dequantize_rows(*quantize_cols_t(w2[e]))          # [I, H]
+    wq = {}   # per expert: the dequantised transposed weights
+
+    def wt(e):
+        if e not in wq:
+            wq[e] = (dequantize_rows(*quantize_cols_t(w2[e])),    # W2t [I, H]
+                     dequantize_rows(*quantize_cols_t(w1[e])))    # W1t [H, 2I]
+        return wq[e]
+
+    # rows are quantised independently, so only the segments' rows are quantised
+    for e, r0, r1 in ffn_segments(offsets, P_c):
+        if r1 == r0:
+            continue
+        dyd_q = dequantize_rows(*quantize_rows(bf16_round(dyd[r0:r1])))
+        w2t, w1t = wt(e)
         g = gu[r0:r1, :I]
         u = gu[r0:r1, I:]
         sg = 1.0 / (1.0 + np.exp(-g))
-        dh = dyd_q[r0:r1] @ w2t.T
+        dh = dyd_q @ w2t.T
         dgu[r0:r1, :I] = dh * u * sg * (1.0 + g * (1.0 - sg))
         dgu[r0:r1, I:] = dh * g * sg
         dw2[e] += dyd[r0:r1].T @ h[r0:r1]
         dw1[e] += dgu[r0:r1].T @ xd[r0:r1]
-    dgu_q = dequantize_rows(*quantize_rows(bf16_round(dgu)))
-    for e, r0, r1 in segs:
-        w1t = dequantize_rows(*quantize_cols_t(w1[e]))          # [H, 2I]
-        dxd[r0:r1] = dgu_q[r0:r1] @ w1t.T
+        dgu_q = dequantize_rows(*quantize_rows(bf16_round(dgu[r0:r1])))
+        dxd[r0:r1] = dgu_q @ w1t.T
     return dgu, dxd, dw1, dw2
+
+
+def backward_fp8_dgrad(fwd: dict, x, dy, w1, w2, w_r):
+    """The layer backward (oracle.ffn.backward) with the expert FFN's input gradients and dW1 from
+    :func:`ffn_bwd_fp8_dgrad`; combine, routing and dispatch backward, dW2 and the router weight
+    gradient are those of the BF16 backward, which does not depend on dgu."""
+    from . import ffn
+    base = ffn.backward(fwd, x, dy, w1, w2, w_r)
+    dgu, dxd, dw1, dw2 = ffn_bwd_fp8_dgrad(base["dyd"], fwd["xd"], fwd["gu"], fwd["h"], fwd["offsets"],
+                                          fwd["P_c"], w1, w2)
+    dx = ffn.dispatch_bwd(dxd, fwd["row_of"], base["dlogits"], w_r)
+    return dict(base, dgu=dgu, dxd=dxd, dx=dx, dw1=dw1, dw2=dw2)
 
 
 def forward(x, logits, w1, w2, *, k, e0, E_local, n_chunks, P_c=None, wq=None):

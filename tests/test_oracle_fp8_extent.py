@@ -223,3 +223,23 @@ def test_fp8_dgrad_oracle_dxd_within_e4m3_bound():
     rows = slice(0, int(offsets[0, -1]))
     err = np.linalg.norm(dxd8[rows] - dxd[rows]) / np.linalg.norm(dxd[rows])
     assert 0 < err < 2.0 ** -4, err
+
+
+def test_fp8_dgrad_layer_backward_changes_only_the_expert_input_gradients():
+    """Gradients that do not pass through dgu (dgates, dlogits, dW2, the router gradient) equal
+    the BF16 backward's exactly; dx and dW1 move by an e4m3-sized relative error, not more."""
+    import oracle
+    from oracle.fp8 import backward_fp8_dgrad
+    from moe_inputs import MoeConfig, make_inputs
+    cfg = MoeConfig("fp8dg", T=96, H=64, I=64, E=8, E_local=4, e0=2, k=2, n_chunks=2, dtype="bf16",
+                    seed_base=70, backward=True)
+    inp = make_inputs(cfg)
+    f = oracle.forward(inp["x"], inp["logits"], inp["w1"], inp["w2"], k=cfg.k, e0=cfg.e0,
+                       E_local=cfg.E_local, n_chunks=cfg.n_chunks)
+    exact = oracle.backward(f, inp["x"], inp["dy"], inp["w1"], inp["w2"], inp["w_r"])
+    q = backward_fp8_dgrad(f, inp["x"], inp["dy"], inp["w1"], inp["w2"], inp["w_r"])
+    for name in ("dyd", "dgates", "dlogits", "dw2", "dwr"):
+        np.testing.assert_array_equal(q[name], exact[name], err_msg=name)
+    for name in ("dx", "dw1"):
+        err = np.linalg.norm(q[name] - exact[name]) / np.linalg.norm(exact[name])
+        assert 1e-4 < err < 2.0 ** -4, (name, err)
