@@ -301,6 +301,50 @@ def fp8_forward(args, cfg, inp, mh, torch, np):
     return out
 
 
+def fp8_dgrad(args, cfg, bufs, mh, torch, np):
+    """The fused forward+backward with FP8 input gradients (MOE_FLAG_FP8_DGRAD; weights quantised
+    per column, transposed, outside the timed region): tokens/s and the FP8 dgrad GEMMs' TFLOP/s."""
+    dq = mh.make_desc(T=cfg.T, H=cfg.H, I=cfg.I, E=cfg.E, E_local=cfg.E_local, k=cfg.k, n_chunks=cfg.n_chunks,
+                      dtype="bf16", e0=cfg.e0, flags=mh.FLAG_FP8_DGRAD)
+    bq = mh.allocate(dq, backward=True)
+    for name in ("x", "logits", "w1", "w2", "w_r", "dy"):
+        bq[name] = bufs[name]
+    mh.moe_quantize_cols_fp8(cfg.E_local, 2 * cfg.I, cfg.H, bq["w1"], bq["w1t"], bq["w1t_scale"])
+    mh.moe_quantize_cols_fp8(cfg.E_local, cfg.H, cfg.I, bq["w2"], bq["w2t"], bq["w2t_scale"])
+    cs, aux = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(args.warmup):
+        mh.moe_layer_forward_backward(dq, bq, cs, aux)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        mh.moe_layer_forward_backward(dq, bq, cs, aux)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    mh.moe_trace_enable(True)
+    for _ in range(args.steps):
+        mh.moe_layer_forward_backward(dq, bq, cs, aux)
+    torch.cuda.synchronize()
+    mh.moe_trace_disable()
+    per = {}
+    for name, _s, t in mh.moe_trace_entries():
+        p = per.setdefault(name, [0, 0.0])
+        p[0] += 1
+        p[1] += t
+    N = int(bq["offsets"].cpu().numpy()[:, cfg.E_local].sum())
+    flops = {"gemm_down_dgrad_swiglu_fp8": 2.0 * N * cfg.H * cfg.I, "gemm_gateup_dgrad_fp8": 2.0 * N * 2 * cfg.I * cfg.H}
+    out = {"tokens_per_s": round(cfg.T / (ms * 1e-3), 1), "ms_per_step_untraced": round(ms, 4),
+           "peak_fp8_tflops": PEAK_FP8_TFLOPS, "kernels": {}}
+    for name, (cnt, tot) in per.items():
+        e = {"avg_us": round(tot / cnt * 1e3, 3), "ms_per_step": round(tot / args.steps, 4)}
+        if name in flops:
+            r = flops[name] / (tot / args.steps * 1e-3) / 1e12
+            e.update(achieved_tflops=round(r, 2), frac_mfma=round(r / PEAK_FP8_TFLOPS, 4))
+        out["kernels"][name] = e
+    del bq
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -534,6 +578,8 @@ def main():
     # FP8 payload path, forward only (the same shapes; weights quantised per output row outside the
     # timed region): expert GEMMs on FP8 MFMA, dispatch quantises per token, combine in BF16
     fp8 = fp8_forward(args, cfg, inp, mh, torch, np)
+    # FP8 input gradients in the fused step (BF16 forward, weight gradients and payload copies)
+    fp8dg = fp8_dgrad(args, cfg, bufs, mh, torch, np)
 
     counts = bufs["counts"].cpu().numpy()
     offsets = bufs["offsets"].cpu().numpy()
@@ -625,6 +671,7 @@ def main():
     line["stash"] = stash_line
     line["route_from_x"] = route_x_line
     line["fp8_fwd"] = fp8
+    line["fp8_dgrad"] = fp8dg
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_budget)
     print(json.dumps(line), flush=True)

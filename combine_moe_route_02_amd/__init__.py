@@ -32,14 +32,18 @@ class MoeError(RuntimeError):
 class MoeDesc(Structure):
     _fields_ = [("T", c_int64), ("H", c_int32), ("I", c_int32), ("E", c_int32), ("e0", c_int32),
                 ("E_local", c_int32), ("k", c_int32), ("n_chunks", c_int32), ("P_c", c_int64),
-                ("P_out", c_int64), ("dtype", c_int32), ("reserved", c_int32)]
+                ("P_out", c_int64), ("dtype", c_int32), ("flags", c_int32)]
+
+
+FLAG_FP8_DGRAD = 1
 
 
 TENSOR_FIELDS = ["x", "logits", "w1", "w1_scale", "w2", "w2_scale", "w_r", "dy",
                  "topk_idx", "gates", "counts", "offsets", "row_of", "src_token", "xd", "xd_scale",
                  "gu", "h", "h_scale", "yd", "out",
                  "dyd", "dgates", "dlogits", "dwr_acc", "dgu", "dxd", "dx", "dw1", "dw2", "dwr",
-                 "workspace"]
+                 "workspace",
+                 "w1t", "w1t_scale", "w2t", "w2t_scale", "dyd_q", "dyd_scale", "dgu_q", "dgu_scale"]
 
 
 class MoeTensors(Structure):
@@ -48,7 +52,8 @@ class MoeTensors(Structure):
 
 SIZE_FIELDS = ["topk_idx", "gates", "counts", "offsets", "row_of", "src_token", "xd", "xd_scale", "gu",
                "h", "h_scale", "yd", "out", "dyd", "dgates", "dlogits", "dwr_acc", "dgu", "dxd", "dx",
-               "dw1", "dw2", "dwr", "route_scratch", "route_bwd_scratch", "workspace"]
+               "dw1", "dw2", "dwr", "route_scratch", "route_bwd_scratch", "workspace",
+               "w1t", "w1t_scale", "w2t", "w2t_scale", "dyd_q", "dyd_scale", "dgu_q", "dgu_scale"]
 
 
 class MoeWorkspaceSizes(Structure):
@@ -69,6 +74,8 @@ _SIGS = {
     "moe_expert_wgrad": [POINTER(MoeDesc)] + [c_void_p] * 8,
     "moe_dispatch_bwd": [POINTER(MoeDesc), c_int] + [c_void_p] * 7,
     "moe_quantize_rows_fp8": [c_int64, c_int32] + [c_void_p] * 4,
+    "moe_quantize_cols_fp8": [c_int64, c_int64, c_int32] + [c_void_p] * 4,
+    "moe_expert_dgrad_fp8": [POINTER(MoeDesc), c_int] + [c_void_p] * 14,
     "moe_stash_store": [c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_int64, c_int64, c_void_p,
                         c_void_p, c_int32, c_int32, c_void_p],
     "moe_stash_load": [c_void_p, c_void_p, c_int64, c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p,
@@ -141,11 +148,11 @@ def last_error() -> str:
     return lib().moe_last_error().decode()
 
 
-def make_desc(T, H, I, E, E_local, k, n_chunks, dtype="bf16", e0=0, P_c=None, P_out=None) -> MoeDesc:
+def make_desc(T, H, I, E, E_local, k, n_chunks, dtype="bf16", e0=0, P_c=None, P_out=None, flags=0) -> MoeDesc:
     pc, po = required_extent(T, k, E_local, n_chunks)
     return MoeDesc(T=T, H=H, I=I, E=E, e0=e0, E_local=E_local, k=k, n_chunks=n_chunks,
                    P_c=pc if P_c is None else P_c, P_out=po if P_out is None else P_out,
-                   dtype=DTYPES[dtype] if isinstance(dtype, str) else dtype, reserved=0)
+                   dtype=DTYPES[dtype] if isinstance(dtype, str) else dtype, flags=flags)
 
 
 # ------------------------------------------------------------------ stage calls (same names)
@@ -204,6 +211,19 @@ def moe_expert_wgrad(d, dyd, dgu, xd, h, offsets, dw1, dw2, stream=None):
 def moe_dispatch_bwd(d, chunk, dxd, row_of, topk_idx, dlogits, w_r, dx, stream=None):
     _check(lib().moe_dispatch_bwd(ctypes.byref(d), chunk, _ptr(dxd), _ptr(row_of), _ptr(topk_idx),
                                   _ptr(dlogits), _ptr(w_r), _ptr(dx), _stream(stream)), "moe_dispatch_bwd")
+
+
+def moe_quantize_cols_fp8(batch, rows, cols, src_bf16, codes_t, scale, stream=None):
+    _check(lib().moe_quantize_cols_fp8(batch, rows, cols, _ptr(src_bf16), _ptr(codes_t), _ptr(scale),
+                                       _stream(stream)), "moe_quantize_cols_fp8")
+
+
+def moe_expert_dgrad_fp8(d, chunk, dyd, gu, w1t, w1t_scale, w2t, w2t_scale, offsets, dyd_q, dyd_scale, dgu,
+                         dgu_q, dgu_scale, dxd, stream=None):
+    _check(lib().moe_expert_dgrad_fp8(ctypes.byref(d), chunk, _ptr(dyd), _ptr(gu), _ptr(w1t), _ptr(w1t_scale),
+                                      _ptr(w2t), _ptr(w2t_scale), _ptr(offsets), _ptr(dyd_q), _ptr(dyd_scale),
+                                      _ptr(dgu), _ptr(dgu_q), _ptr(dgu_scale), _ptr(dxd), _stream(stream)),
+           "moe_expert_dgrad_fp8")
 
 
 def moe_quantize_rows_fp8(rows, cols, src_bf16, codes, scale, stream=None):
@@ -358,6 +378,11 @@ def allocate(d: MoeDesc, device="cuda", backward: bool = True, fill=None):
                      "dwr_acc": ((E, H), f32), "dgu": ((P, 2 * I), pay), "dxd": ((P, H), pay),
                      "dx": ((T, H), pay), "dw1": ((El, 2 * I, H), pay), "dw2": ((El, H, I), pay),
                      "dwr": ((E, H), pay)})
+    if backward and (d.flags & FLAG_FP8_DGRAD):
+        # transposed per-column FP8 weights (moe_quantize_cols_fp8) and the quantised payloads
+        spec.update({"w1t": ((El, H, 2 * I), u8), "w1t_scale": ((El, H), f32), "w2t": ((El, I, H), u8),
+                     "w2t_scale": ((El, I), f32), "dyd_q": ((P, H), u8), "dyd_scale": ((P,), f32),
+                     "dgu_q": ((P, 2 * I), u8), "dgu_scale": ((P,), f32)})
     out = {}
     for name, (shape, dt) in spec.items():
         out[name] = torch.empty(shape, dtype=dt, device=device)

@@ -53,7 +53,7 @@ int elem_size(int dtype) { return dtype == MOE_F32 ? 4 : 2; }  // payload rows (
 
 moe_status validate(const moe_desc* d) {
   if (!d) return fail(MOE_ERR_ARG, "descriptor is NULL");
-  if (d->reserved != 0) return fail(MOE_ERR_ARG, "descriptor field 'reserved' must be 0");
+  if (d->flags & ~MOE_FLAG_FP8_DGRAD) return fail(MOE_ERR_ARG, "descriptor flags 0x%x hold an unknown bit", d->flags);
   if (d->dtype != MOE_F32 && d->dtype != MOE_BF16 && d->dtype != MOE_FP8_E4M3)
     return fail(MOE_ERR_ARG, "unknown dtype %d", d->dtype);
   if (d->T < 0) return fail(MOE_ERR_ARG, "T = %lld is negative", (long long)d->T);
@@ -69,6 +69,8 @@ moe_status validate(const moe_desc* d) {
   if (d->H <= 0 || d->H % 64) return fail(MOE_ERR_UNSUPPORTED, "H = %d must be a positive multiple of 64", d->H);
   if (d->I <= 0 || d->I % 64) return fail(MOE_ERR_UNSUPPORTED, "I = %d must be a positive multiple of 64", d->I);
   if (d->dtype == MOE_BF16 && d->E % 4) return fail(MOE_ERR_UNSUPPORTED, "BF16 path needs E %% 4 == 0 (E = %d)", d->E);
+  if ((d->flags & MOE_FLAG_FP8_DGRAD) && d->dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "MOE_FLAG_FP8_DGRAD needs the BF16 dtype");
   if (d->dtype == MOE_FP8_E4M3 && d->H > 8192)
     return fail(MOE_ERR_UNSUPPORTED, "FP8 dispatch keeps a row in registers: H = %d above 8192", d->H);
   if (d->P_c % 4) return fail(MOE_ERR_CAPACITY, "P_c = %lld is not a multiple of 4", (long long)d->P_c);
@@ -133,7 +135,7 @@ int64_t router_scratch(const moe_desc* d) {
 extern "C" {
 
 const char* moe_last_error(void) { return g_err.c_str(); }
-int32_t moe_abi_version(void) { return 1; }
+int32_t moe_abi_version(void) { return 2; }
 
 moe_status moe_required_extent(int64_t T, int32_t k, int32_t E_local, int32_t n_chunks, int64_t* P_c,
                                int64_t* P_out) {
@@ -178,6 +180,16 @@ moe_status moe_workspace_bytes(const moe_desc* d, moe_workspace_sizes* o) {
     o->dw1 = El * 2 * I * H * es;
     o->dw2 = El * H * I * es;
     o->dwr = E * H * es;
+  }
+  if (d->flags & MOE_FLAG_FP8_DGRAD) {
+    o->w1t = El * H * 2 * I;
+    o->w1t_scale = El * H * 4;
+    o->w2t = El * I * H;
+    o->w2t_scale = El * I * 4;
+    o->dyd_q = P * H;
+    o->dyd_scale = P * 4;
+    o->dgu_q = P * 2 * I;
+    o->dgu_scale = P * 4;
   }
   o->route_scratch = moe::route_scratch_bytes(T, (int)n, (int)E);
   o->route_bwd_scratch = fp8 ? 0 : router_scratch(d);
@@ -281,8 +293,11 @@ static moe_status no_fp8_bwd(const moe_desc* d) {
   return MOE_OK;
 }
 
-moe_status moe_combine_bwd(const moe_desc* d, int chunk, const void* dy, const void* yd, const float* gates,
-                           const int32_t* row_of, void* dyd, float* dgates, void* stream) {
+// Combine backward; with dyd_q (BF16, the FP8 input-gradient layer) it also writes the e4m3 rows
+// of dyd and their scales, as moe_expert_dgrad_fp8 would quantise them.
+static moe_status combine_bwd_impl(const moe_desc* d, int chunk, const void* dy, const void* yd,
+                                   const float* gates, const int32_t* row_of, void* dyd, float* dgates,
+                                   void* dyd_q, float* dyd_scale, void* stream) {
   MOE_TRY(validate(d));
   MOE_TRY(no_fp8_bwd(d));
   MOE_TRY(check_chunk(d, chunk));
@@ -291,8 +306,14 @@ moe_status moe_combine_bwd(const moe_desc* d, int chunk, const void* dy, const v
   MOE_NEED(dy); MOE_NEED(gates); MOE_NEED(row_of); MOE_NEED(dgates);
   if (rows_of(d) > 0) { MOE_NEED(yd); MOE_NEED(dyd); }
   MOE_HIP(moe::launch_combine_bwd(is_bf16_rows(d), dy, yd, gates, row_of, dyd, dgates, r.t0, r.t1, d->k,
-                                  (int64_t)d->H * elem_size(d->dtype), (hipStream_t)stream), "combine_bwd");
+                                  (int64_t)d->H * elem_size(d->dtype), (hipStream_t)stream, dyd_q, dyd_scale),
+          "combine_bwd");
   return MOE_OK;
+}
+
+moe_status moe_combine_bwd(const moe_desc* d, int chunk, const void* dy, const void* yd, const float* gates,
+                           const int32_t* row_of, void* dyd, float* dgates, void* stream) {
+  return combine_bwd_impl(d, chunk, dy, yd, gates, row_of, dyd, dgates, nullptr, nullptr, stream);
 }
 
 moe_status moe_route_bwd(const moe_desc* d, int chunk, const float* dgates, const float* gates,
@@ -344,6 +365,34 @@ moe_status moe_expert_ffn_bwd(const moe_desc* d, int chunk, const void* dyd, con
   return MOE_OK;
 }
 
+static moe_status expert_dgrad_fp8_impl(const moe_desc* d, int chunk, const void* dyd, const void* gu,
+                                        const void* w1t, const float* w1t_scale, const void* w2t,
+                                        const float* w2t_scale, const int32_t* offsets, void* dyd_q,
+                                        float* dyd_scale, void* dgu, void* dgu_q, float* dgu_scale, void* dxd,
+                                        bool quantize_dyd, void* stream) {
+  MOE_TRY(validate(d));
+  if (d->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "FP8 input gradients need the BF16 dtype");
+  MOE_TRY(check_chunk(d, chunk));
+  if (rows_of(d) == 0) return MOE_OK;
+  Range r = range_of(d, chunk);
+  MOE_NEED(dyd); MOE_NEED(gu); MOE_NEED(w1t); MOE_NEED(w1t_scale); MOE_NEED(w2t); MOE_NEED(w2t_scale);
+  MOE_NEED(offsets); MOE_NEED(dyd_q); MOE_NEED(dyd_scale); MOE_NEED(dgu); MOE_NEED(dgu_q); MOE_NEED(dgu_scale);
+  MOE_NEED(dxd);
+  MOE_HIP(moe::launch_expert_dgrad_fp8(dyd, gu, w1t, w1t_scale, w2t, w2t_scale, offsets, dyd_q, dyd_scale, dgu,
+                                       dgu_q, dgu_scale, dxd, d->H, d->I, d->E_local, r.c0, r.nc, d->P_c,
+                                       (hipStream_t)stream, quantize_dyd),
+          "expert_dgrad_fp8");
+  return MOE_OK;
+}
+
+moe_status moe_expert_dgrad_fp8(const moe_desc* d, int chunk, const void* dyd, const void* gu, const void* w1t,
+                                const float* w1t_scale, const void* w2t, const float* w2t_scale,
+                                const int32_t* offsets, void* dyd_q, float* dyd_scale, void* dgu, void* dgu_q,
+                                float* dgu_scale, void* dxd, void* stream) {
+  return expert_dgrad_fp8_impl(d, chunk, dyd, gu, w1t, w1t_scale, w2t, w2t_scale, offsets, dyd_q, dyd_scale, dgu,
+                               dgu_q, dgu_scale, dxd, true, stream);
+}
+
 moe_status moe_dispatch_bwd(const moe_desc* d, int chunk, const void* dxd, const int32_t* row_of,
                             const int32_t* topk_idx, const float* dlogits, const void* w_r, void* dx,
                             void* stream) {
@@ -367,6 +416,18 @@ moe_status moe_quantize_rows_fp8(int64_t rows, int32_t cols, const void* src_bf1
   MOE_NEED(src_bf16); MOE_NEED(codes); MOE_NEED(scale);
   MOE_HIP(moe::launch_quantize_rows_fp8(src_bf16, codes, scale, rows, cols, (hipStream_t)stream),
           "quantize_rows_fp8");
+  return MOE_OK;
+}
+
+moe_status moe_quantize_cols_fp8(int64_t batch, int64_t rows, int32_t cols, const void* src_bf16, void* codes_t,
+                                 float* scale, void* stream) {
+  if (batch < 0 || rows < 0 || rows % 16 || cols <= 0 || cols % 8)
+    return fail(MOE_ERR_ARG, "batch/rows/cols invalid (rows %% 16 == 0 and cols %% 8 == 0 required)");
+  if (batch > 65535) return fail(MOE_ERR_UNSUPPORTED, "batch = %lld above 65535", (long long)batch);
+  if (batch == 0 || rows == 0) return MOE_OK;
+  MOE_NEED(src_bf16); MOE_NEED(codes_t); MOE_NEED(scale);
+  MOE_HIP(moe::launch_quantize_cols_fp8(src_bf16, codes_t, scale, batch, rows, cols, (hipStream_t)stream),
+          "quantize_cols_fp8");
   return MOE_OK;
 }
 
@@ -441,6 +502,10 @@ static moe_status check_bwd_tensors(const moe_desc* d, const moe_tensors* t) {
   if (d->T > 0) { MOE_NEED(t->dy); MOE_NEED(t->dgates); MOE_NEED(t->dlogits); MOE_NEED(t->dx); }
   if (rows_of(d) > 0) {
     MOE_NEED(t->gu); MOE_NEED(t->dyd); MOE_NEED(t->dgu); MOE_NEED(t->dxd); MOE_NEED(t->dw1); MOE_NEED(t->dw2);
+    if (d->flags & MOE_FLAG_FP8_DGRAD) {
+      MOE_NEED(t->w1t); MOE_NEED(t->w1t_scale); MOE_NEED(t->w2t); MOE_NEED(t->w2t_scale);
+      MOE_NEED(t->dyd_q); MOE_NEED(t->dyd_scale); MOE_NEED(t->dgu_q); MOE_NEED(t->dgu_scale);
+    }
   }
   return MOE_OK;
 }
@@ -528,21 +593,33 @@ static moe_status backward_sched(const moe_desc* d, const moe_tensors* t, hipStr
   hipEvent_t* cb = ev + 2 * n + 1;  // n events: combine backward of chunk c done
   hipEvent_t* dg = ev + 3 * n + 1;  // n events: expert dgrad of chunk c done
   hipEvent_t done = ev[4 * n + 1];
-  MOE_TRY(moe_combine_bwd(d, 0, t->dy, t->yd, t->gates, t->row_of, t->dyd, t->dgates, cs));
+  // FP8 input gradients: combine backward also writes the e4m3 rows of dyd (H up to
+  // kCombineQMaxH; above it the expert dgrad quantises the stored rows)
+  const bool q = d->flags & MOE_FLAG_FP8_DGRAD;
+  const bool qcb = q && d->H <= moe::kCombineQMaxH;
+  auto combine_bwd = [&](int c, hipStream_t st) {
+    return combine_bwd_impl(d, c, t->dy, t->yd, t->gates, t->row_of, t->dyd, t->dgates, qcb ? t->dyd_q : nullptr,
+                            qcb ? t->dyd_scale : nullptr, st);
+  };
+  MOE_TRY(combine_bwd(0, cs));
   if (two) {
     MOE_HIP(hipEventRecord(cb[0], cs), "hipEventRecord");
     MOE_HIP(hipStreamWaitEvent(as, cb[0], 0), "hipStreamWaitEvent");
   }
   for (int c = 0; c < n; ++c) {
     if (c + 1 < n) {
-      MOE_TRY(moe_combine_bwd(d, c + 1, t->dy, t->yd, t->gates, t->row_of, t->dyd, t->dgates, side));
+      MOE_TRY(combine_bwd(c + 1, side));
       if (two) MOE_HIP(hipEventRecord(cb[c + 1], as), "hipEventRecord");
     }
     MOE_TRY(moe_route_bwd(d, c, t->dgates, t->gates, t->topk_idx, t->x, t->dlogits, t->dwr_acc, t->dwr,
                           t->workspace, side));
     if (two && c >= 1) MOE_HIP(hipStreamWaitEvent(cs, cb[c], 0), "hipStreamWaitEvent");
-    MOE_TRY(moe_expert_ffn_bwd(d, c, t->dyd, t->xd, t->gu, t->h, t->w1, t->w2, t->offsets, t->dgu, t->dxd,
-                               nullptr, nullptr, cs));
+    if (q)
+      MOE_TRY(expert_dgrad_fp8_impl(d, c, t->dyd, t->gu, t->w1t, t->w1t_scale, t->w2t, t->w2t_scale, t->offsets,
+                                    t->dyd_q, t->dyd_scale, t->dgu, t->dgu_q, t->dgu_scale, t->dxd, !qcb, cs));
+    else
+      MOE_TRY(moe_expert_ffn_bwd(d, c, t->dyd, t->xd, t->gu, t->h, t->w1, t->w2, t->offsets, t->dgu, t->dxd,
+                                 nullptr, nullptr, cs));
     if (two) {
       MOE_HIP(hipEventRecord(dg[c], cs), "hipEventRecord");
       MOE_HIP(hipStreamWaitEvent(as, dg[c], 0), "hipStreamWaitEvent");
@@ -575,6 +652,8 @@ static moe::ExpertGemm expert_gemm(const moe_desc* d, const moe_tensors* t) {
 }
 
 static bool merged_gemms(const moe_desc* d) { return d->dtype == MOE_BF16 && d->T > 0 && rows_of(d) > 0; }
+// the merged backward launches pair BF16 input-gradient GEMMs; FP8 input gradients run per chunk
+static bool merged_bwd(const moe_desc* d) { return merged_gemms(d) && !(d->flags & MOE_FLAG_FP8_DGRAD); }
 
 //   compute: R0 D0 GU0 | wait(disp1) [DN0 GU1] | wait(disp2) [DN1 GU2] | ... | DN n-1, C n-1
 //   aux:     wait(disp0) R1 D1 | R2 D2, wait(ffn0) C0 | R3 D3, wait(ffn1) C1 | ...
@@ -699,7 +778,7 @@ moe_status moe_layer_backward(const moe_desc* d, const moe_tensors* t, void* com
   MOE_TRY(validate(d));
   MOE_TRY(check_fwd_tensors(d, t));
   MOE_TRY(check_bwd_tensors(d, t));
-  if (merged_gemms(d)) return backward_sched_merged(d, t, (hipStream_t)compute_stream, (hipStream_t)aux_stream);
+  if (merged_bwd(d)) return backward_sched_merged(d, t, (hipStream_t)compute_stream, (hipStream_t)aux_stream);
   return backward_sched(d, t, (hipStream_t)compute_stream, (hipStream_t)aux_stream);
 }
 
@@ -710,11 +789,11 @@ moe_status moe_layer_forward_backward(const moe_desc* d, const moe_tensors* t, v
   MOE_TRY(check_bwd_tensors(d, t));
   // no join between the two: the backward's first wait of the auxiliary stream follows the
   // whole forward on the compute stream, and its final join covers the forward's aux work
-  if (merged_gemms(d)) {
+  if (merged_gemms(d))
     MOE_TRY(forward_sched_merged(d, t, (hipStream_t)compute_stream, (hipStream_t)aux_stream, false));
-    return backward_sched_merged(d, t, (hipStream_t)compute_stream, (hipStream_t)aux_stream);
-  }
-  MOE_TRY(forward_sched(d, t, (hipStream_t)compute_stream, (hipStream_t)aux_stream, false));
+  else
+    MOE_TRY(forward_sched(d, t, (hipStream_t)compute_stream, (hipStream_t)aux_stream, false));
+  if (merged_bwd(d)) return backward_sched_merged(d, t, (hipStream_t)compute_stream, (hipStream_t)aux_stream);
   return backward_sched(d, t, (hipStream_t)compute_stream, (hipStream_t)aux_stream);
 }
 

@@ -345,10 +345,11 @@ template <int BM, int BN, int MODE, bool FP8>
 MOE_DEV int rows_list(const RowsArgs& a, int first, RowsShared& sh, char* ring) {
   constexpr int WTM = BM / kWM, WTN = BN / kWN, TM = WTM / 32, TN = WTN / 32;
   constexpr bool kSwiGLU = (MODE == kGateUp);
-  constexpr bool kBKS = (MODE == kDownBwd || MODE == kGateUpBwd);
+  // BF16 input gradients read W_e as stored (K-slow); FP8 ones read a transposed copy (K-major)
+  constexpr bool kBKS = !FP8 && (MODE == kDownBwd || MODE == kGateUpBwd);
   constexpr int ES = FP8 ? 1 : 2;      // element bytes
   constexpr int OUTN = kSwiGLU ? BN / 2 : BN;
-  static_assert(!(FP8 && kBKS), "FP8 runs the forward GEMMs only");
+  static_assert(!(FP8 && MODE == kGateUpBwd), "FP8 gate/up dgrad runs as kDown on the transposed W1");
   int* s_pre = sh.pre;
   int64_t* s_r0 = sh.r0;
   int* s_len = sh.len;
@@ -421,7 +422,7 @@ MOE_DEV int rows_list(const RowsArgs& a, int first, RowsShared& sh, char* ring) 
                        const int q = r % WTN, hw = WTN / 2, j = (r / WTN) * hw + (q < hw ? q : q - hw);
                        return q < hw ? j : I + j;
                      });
-    } else if constexpr (MODE == kDown) {
+    } else if constexpr (MODE == kDown || FP8) {
       lb.init_kmajor(Be + (int64_t)n0 * a.K * ES, (int64_t)a.K * ES, ((int64_t)a.N - n0) * a.K * ES, wave, lane,
                      [](int r) { return r; });
     } else {
@@ -525,6 +526,9 @@ MOE_DEV int rows_list(const RowsArgs& a, int first, RowsShared& sh, char* ring) 
       const int64_t I2 = 2 * (int64_t)a.I;
       load_staged<BM, W>(sg, a.aux + r0 * I2 + n0, I2, mvalid, nvalid, tid);
       load_staged<BM, W>(su, a.aux + r0 * I2 + a.I + n0, I2, mvalid, nvalid, tid);
+      float sr[TM];
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) sr[tm] = (FP8 && mrow + tm * 32 < mvalid) ? a.scale_a[r0 + mrow + tm * 32] : 1.f;
       lds_barrier();
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
@@ -541,7 +545,8 @@ MOE_DEV int rows_list(const RowsArgs& a, int first, RowsShared& sh, char* ring) 
             unpack4(*(const uint2*)pu, uv);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const float dh = acc[tm][tn][4 * gq + q];
+              float dh = acc[tm][tn][4 * gq + q];
+              if constexpr (FP8) dh *= sr[tm] * a.scale_b[(int64_t)e * a.strideSB + min(n0 + jl + q, a.N - 1)];
               const float sgm = sigmoidf_(gv[q]);
               dg[q] = dh * uv[q] * sgm * (1.f + gv[q] * (1.f - sgm));
               du[q] = dh * gv[q] * sgm;
@@ -962,7 +967,7 @@ hipError_t launch_expert_fwd_fp8(const void* xd, const float* xd_scale, const vo
   a.offsets = offsets; a.El = El; a.c0 = c0; a.nc = nc; a.P_c = P_c;
   hipError_t e = run_rows<256, 256, kGateUp, true>("gemm_gateup_swiglu_fp8", a, s);
   if (e != hipSuccess) return e;
-  e = launch_quantize_segments_fp8(h, hq, h_scale, offsets, El, c0, nc, P_c, I, s);
+  e = launch_quantize_segments_fp8("quantize_h_fp8", h, hq, h_scale, offsets, El, c0, nc, P_c, I, s);
   if (e != hipSuccess) return e;
   RowsArgs b{};
   b.A = hq; b.B = w2; b.C = (uint16_t*)yd;
@@ -970,6 +975,39 @@ hipError_t launch_expert_fwd_fp8(const void* xd, const float* xd_scale, const vo
   b.lda = I; b.ldc = H; b.strideB = (int64_t)H * I; b.K = I; b.N = H; b.I = I;
   b.offsets = offsets; b.El = El; b.c0 = c0; b.nc = nc; b.P_c = P_c;
   return run_rows<256, 256, kDown, true>("gemm_down_fp8", b, s);
+}
+
+// FP8 input gradients: dyd quantised per row (FP32 steps of dispatch); dh = deq(dyd) deq(W2t)^T on
+// FP8 MFMA with the SwiGLU gradient in the epilogue -> dgu (BF16); dgu quantised per row; dxd =
+// deq(dgu) deq(W1t)^T on FP8 MFMA -> BF16. W2t [El][I][H] and W1t [El][H][2I] hold the weights'
+// columns as rows (per-column scales), so both products read K-contiguous operands, like the
+// forward ones.
+hipError_t launch_expert_dgrad_fp8(const void* dyd, const void* gu, const void* w1t, const float* w1t_scale,
+                                   const void* w2t, const float* w2t_scale, const int32_t* offsets,
+                                   void* dyd_q, float* dyd_scale, void* dgu, void* dgu_q, float* dgu_scale,
+                                   void* dxd, int H, int I, int El, int c0, int nc, int64_t P_c, hipStream_t s,
+                                   bool quantize_dyd) {
+  if (nc <= 0 || El <= 0) return hipSuccess;
+  hipError_t e = hipSuccess;
+  if (quantize_dyd) {
+    e = launch_quantize_segments_fp8("quantize_dyd_fp8", dyd, dyd_q, dyd_scale, offsets, El, c0, nc, P_c, H, s);
+    if (e != hipSuccess) return e;
+  }
+  RowsArgs a{};
+  a.A = dyd_q; a.B = w2t; a.C = (uint16_t*)dgu; a.aux = (const uint16_t*)gu;
+  a.scale_a = dyd_scale; a.scale_b = w2t_scale; a.strideSB = I;
+  a.lda = H; a.ldc = 2 * (int64_t)I; a.strideB = (int64_t)I * H; a.K = H; a.N = I; a.I = I;
+  a.offsets = offsets; a.El = El; a.c0 = c0; a.nc = nc; a.P_c = P_c;
+  e = run_rows<128, 256, kDownBwd, true>("gemm_down_dgrad_swiglu_fp8", a, s);
+  if (e != hipSuccess) return e;
+  e = launch_quantize_segments_fp8("quantize_dgu_fp8", dgu, dgu_q, dgu_scale, offsets, El, c0, nc, P_c, 2 * I, s);
+  if (e != hipSuccess) return e;
+  RowsArgs b{};
+  b.A = dgu_q; b.B = w1t; b.C = (uint16_t*)dxd;
+  b.scale_a = dgu_scale; b.scale_b = w1t_scale; b.strideSB = H;
+  b.lda = 2 * (int64_t)I; b.ldc = H; b.strideB = (int64_t)H * 2 * I; b.K = 2 * I; b.N = H; b.I = I;
+  b.offsets = offsets; b.El = El; b.c0 = c0; b.nc = nc; b.P_c = P_c;
+  return run_rows<256, 256, kDown, true>("gemm_gateup_dgrad_fp8", b, s);
 }
 
 }  // namespace moe

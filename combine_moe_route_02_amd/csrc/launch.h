@@ -30,9 +30,11 @@ hipError_t launch_quantize_rows_fp8(const void* src, void* codes, float* scale, 
                                     int cols, hipStream_t s);
 hipError_t launch_combine(bool bf16, const void* yd, const float* gates, const int32_t* row_of,
                           void* out, int64_t t0, int64_t t1, int K, int64_t row_bytes, hipStream_t s);
+constexpr int kCombineQMaxH = 8192;  // combine backward quantises dyd rows up to this H
 hipError_t launch_combine_bwd(bool bf16, const void* dy, const void* yd, const float* gates,
                               const int32_t* row_of, void* dyd, float* dgates, int64_t t0,
-                              int64_t t1, int K, int64_t row_bytes, hipStream_t s);
+                              int64_t t1, int K, int64_t row_bytes, hipStream_t s,
+                              void* dyd_q = nullptr, float* dyd_scale = nullptr);  // BF16: also e4m3 rows
 hipError_t launch_route_bwd_dlogits(const float* dgates, const float* gates, const int32_t* idx,
                                     float* dlogits, int64_t t0, int64_t t1, int K, int E,
                                     hipStream_t s);
@@ -50,9 +52,20 @@ hipError_t launch_expert_fwd_fp8(const void* xd, const float* xd_scale, const vo
                                  const int32_t* offsets, void* h, float* h_scale, void* yd, int H,
                                  int I, int El, int c0, int nc, int64_t P_c, int64_t P, hipStream_t s);
 // per-row e4m3 quantisation of the BF16 rows [c*P_c, c*P_c + N_c) of chunks c0..c0+nc-1
-hipError_t launch_quantize_segments_fp8(const void* src, void* codes, float* scale,
+hipError_t launch_quantize_segments_fp8(const char* name, const void* src, void* codes, float* scale,
                                         const int32_t* offsets, int El, int c0, int nc, int64_t P_c,
                                         int cols, hipStream_t s);
+// per-column e4m3 quantisation of batch x [rows, cols] BF16, codes stored transposed [batch, cols, rows]
+hipError_t launch_quantize_cols_fp8(const void* src, void* codes_t, float* scale, int64_t batch, int64_t rows,
+                                    int64_t cols, hipStream_t s);
+// FP8 input gradients of the expert FFN for chunks c0..c0+nc-1: dyd quantised per row, dh on FP8
+// MFMA against the transposed per-column-quantised W2 (w2t [El][I][H]), the SwiGLU gradient -> dgu
+// (BF16), dgu quantised per row, dxd on FP8 MFMA against w1t [El][H][2I]
+hipError_t launch_expert_dgrad_fp8(const void* dyd, const void* gu, const void* w1t, const float* w1t_scale,
+                                   const void* w2t, const float* w2t_scale, const int32_t* offsets,
+                                   void* dyd_q, float* dyd_scale, void* dgu, void* dgu_q, float* dgu_scale,
+                                   void* dxd, int H, int I, int El, int c0, int nc, int64_t P_c, hipStream_t s,
+                                   bool quantize_dyd = true);  // false: dyd_q/dyd_scale already written
 hipError_t launch_expert_dgrad(bool bf16, const void* dyd, const void* gu, const void* w1,
                                const void* w2, const int32_t* offsets, void* dgu, void* dxd, int H,
                                int I, int El, int c0, int nc, int64_t P_c, hipStream_t s);

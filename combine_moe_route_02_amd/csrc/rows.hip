@@ -11,6 +11,7 @@
 // multi-row tiles, tail masks and 64-bit addressing; these kernels keep those properties for the
 // gather/scatter between token order and expert-contiguous order. ART PR 971 (description)
 // gives combine's fresh [P, H] output cropped to the logical rows: only rows t < T are written.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -138,7 +139,9 @@ __global__ __launch_bounds__(256) void quantize_rows_fp8_kernel(
 
 // Per-row quantisation of the dispatch rows [c*P_c, c*P_c + N_c) of chunk c (N_c from the offset
 // table, so the row count stays on the device): one wave per row, grid-stride over the rows, the
-// FP32 steps of dispatch.
+// FP32 steps of dispatch. With kRegs (rows of at most kFp8MaxVec vectors per lane) the row stays in
+// registers between the absmax and the quantisation, so it is read once.
+template <bool kRegs>
 __global__ __launch_bounds__(256) void quantize_segments_fp8_kernel(
     const u32x4* __restrict__ src, uint2* __restrict__ codes, float* __restrict__ scale,
     const int32_t* __restrict__ offsets, int El, int c0, int64_t P_c, int64_t nvec) {
@@ -150,11 +153,100 @@ __global__ __launch_bounds__(256) void quantize_segments_fp8_kernel(
     const int64_t row = (int64_t)c * P_c + r;
     const u32x4* s = src + row * nvec;
     float m = 0.f;
-    for (int64_t i = lane; i < nvec; i += 64) m = fmaxf(m, absmax8(s[i]));
-    const float amax = wave_max(m);
-    const float inv = amax > 0.f ? 448.0f / amax : 0.f;
-    for (int64_t i = lane; i < nvec; i += 64) codes[row * nvec + i] = quant8(s[i], inv);
-    if (lane == 0) scale[row] = amax > 0.f ? amax / 448.0f : 1.0f;
+    if constexpr (kRegs) {
+      u32x4 v[kFp8MaxVec];
+#pragma unroll
+      for (int b = 0; b < kFp8MaxVec; ++b) {
+        const int64_t i = b * 64 + lane;
+        if (i < nvec) { v[b] = s[i]; m = fmaxf(m, absmax8(v[b])); }
+      }
+      const float amax = wave_max(m);
+      const float inv = amax > 0.f ? 448.0f / amax : 0.f;
+#pragma unroll
+      for (int b = 0; b < kFp8MaxVec; ++b) {
+        const int64_t i = b * 64 + lane;
+        if (i < nvec) codes[row * nvec + i] = quant8(v[b], inv);
+      }
+      if (lane == 0) scale[row] = amax > 0.f ? amax / 448.0f : 1.0f;
+    } else {
+      for (int64_t i = lane; i < nvec; i += 64) m = fmaxf(m, absmax8(s[i]));
+      const float amax = wave_max(m);
+      const float inv = amax > 0.f ? 448.0f / amax : 0.f;
+      for (int64_t i = lane; i < nvec; i += 64) codes[row * nvec + i] = quant8(s[i], inv);
+      if (lane == 0) scale[row] = amax > 0.f ? amax / 448.0f : 1.0f;
+    }
+  }
+}
+
+// Per-column quantisation of a batch of [rows, cols] BF16 matrices stored transposed: codes
+// [batch, cols, rows] (the column's values contiguous) and scale [batch, cols], each column with
+// the FP32 steps of dispatch. One block per 64 columns of one matrix: the 256 threads (8 column
+// vectors of 8 values x 32 row groups) first reduce the 64 column maxima through LDS, then walk
+// 64-row tiles, quantise, transpose the bytes in LDS and store 16 code bytes per thread.
+// rows % 16 == 0 and cols % 8 == 0 (checked on the host).
+constexpr int kColTile = 64, kColPitch = kColTile + 16;
+__global__ __launch_bounds__(256) void quantize_cols_fp8_kernel(
+    const u32x4* __restrict__ src, uint8_t* __restrict__ codes, float* __restrict__ scale,
+    int64_t rows, int64_t cols) {
+  __shared__ float red[32][kColTile];
+  __shared__ float s_inv[kColTile];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kColTile * kColPitch];
+  const int t = threadIdx.x, cv = t & 7, rg = t >> 3;
+  const int64_t b = blockIdx.y, c0 = (int64_t)blockIdx.x * kColTile;
+  const int64_t nvec = cols / 8;
+  const bool cin = c0 + cv * 8 < cols;
+  const u32x4* s = src + b * rows * nvec + c0 / 8 + cv;
+  float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (cin)
+    for (int64_t r = rg; r < rows; r += 32) {
+      const u32x4 v = s[r * nvec];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        m[2 * i] = fmaxf(m[2 * i], fabsf(bf2f(w[i] & 0xffff)));
+        m[2 * i + 1] = fmaxf(m[2 * i + 1], fabsf(bf2f(w[i] >> 16)));
+      }
+    }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[rg][cv * 8 + i] = m[i];
+  __syncthreads();
+  if (t < kColTile) {
+    float amax = 0.f;
+    for (int g = 0; g < 32; ++g) amax = fmaxf(amax, red[g][t]);
+    s_inv[t] = amax > 0.f ? 448.0f / amax : 0.f;
+    if (c0 + t < cols) scale[b * cols + c0 + t] = amax > 0.f ? amax / 448.0f : 1.0f;
+  }
+  __syncthreads();
+  float inv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) inv[i] = s_inv[cv * 8 + i];
+  const int oc = t >> 2, orow = (t & 3) * 16;   // output: column oc, 16 rows from orow
+  uint8_t* out = codes + (b * cols + c0 + oc) * rows;
+  for (int64_t r0 = 0; r0 < rows; r0 += kColTile) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int rl = rg + 32 * h;
+      if (cin && r0 + rl < rows) {
+        const u32x4 v = s[(r0 + rl) * nvec];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        float f[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { f[2 * i] = bf2f(w[i] & 0xffff); f[2 * i + 1] = bf2f(w[i] >> 16); }
+        const uint32_t lo = pack_fp8x4(clamp448(f[0] * inv[0]), clamp448(f[1] * inv[1]), clamp448(f[2] * inv[2]),
+                                       clamp448(f[3] * inv[3]));
+        const uint32_t hi = pack_fp8x4(clamp448(f[4] * inv[4]), clamp448(f[5] * inv[5]), clamp448(f[6] * inv[6]),
+                                       clamp448(f[7] * inv[7]));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          tile[(cv * 8 + i) * kColPitch + rl] = (uint8_t)(lo >> (8 * i));
+          tile[(cv * 8 + 4 + i) * kColPitch + rl] = (uint8_t)(hi >> (8 * i));
+        }
+      }
+    }
+    __syncthreads();
+    if (c0 + oc < cols && r0 + orow < rows)
+      *(u32x4*)(out + r0 + orow) = *(const u32x4*)(tile + oc * kColPitch + orow);
+    __syncthreads();
   }
 }
 
@@ -256,6 +348,100 @@ __global__ __launch_bounds__(kBlockThreads) void combine_bwd_kernel(
         for (int q = 0; q < V::N; ++q) { dg[j] = fmaf(d[q], f[q], dg[j]); o[q] = g * d[q]; }
         dyd[(int64_t)r * nvec + i] = V::from_f(o);
       }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    if (!((local >> j) & 1)) continue;
+    const float w = wave_sum(dg[j]);
+    if (lane == 0) part[wave][j] = w;
+  }
+  __syncthreads();
+  if (threadIdx.x < K) {
+    const int j = threadIdx.x;
+    float sum = 0.f;
+    if ((local >> j) & 1) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) sum += part[w][j];
+    }
+    dgates[t * K + j] = sum;
+  }
+}
+
+// Combine backward of BF16 rows that also quantises every written dyd row to e4m3 with the FP32
+// steps of dispatch (the FP8 input gradients take them). The row's absmax is that of the BF16
+// values RNE(g * dy), which equals RNE(|g| * max|dy|) because the FP32 product and the rounding are
+// monotone, so one block reduction of max|dy[t]| gives every slot's scale, and the codes equal those
+// of quantising the stored dyd rows. Each thread holds NV vectors of the token's row (H <= NV * 2048
+// BF16 values): dy and the slots' yd are loaded before the one barrier, then dyd, its codes and the
+// dgates partials follow from registers.
+constexpr int kCombineQMaxVec = kCombineQMaxH / 8 / kBlockThreads;
+template <int K, int NV>
+__global__ __launch_bounds__(kBlockThreads) void combine_bwd_q_kernel(
+    const u32x4* __restrict__ dy, const u32x4* __restrict__ yd, const float* __restrict__ gates,
+    const int32_t* __restrict__ row_of, u32x4* __restrict__ dyd, float* __restrict__ dgates,
+    uint2* __restrict__ dq, float* __restrict__ dq_scale, int64_t t0, int64_t t1, int64_t nvec) {
+  using V = Vec<uint16_t>;
+  constexpr int NW = kBlockThreads / 64;
+  __shared__ float part[NW][K];
+  __shared__ float amx[NW];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t = t0 + blockIdx.x;
+  const int32_t myrow = lane < K ? row_of[t * K + lane] : -1;
+  const float mygate = lane < K ? gates[t * K + lane] : 0.f;
+  const uint64_t local = __ballot(myrow >= 0);   // the same in every wave of the block
+  if (!local) {
+    if (threadIdx.x < K) dgates[t * K + threadIdx.x] = 0.f;
+    return;
+  }
+  u32x4 dv[NV], yv[NV][K];
+  float m = 0.f;
+#pragma unroll
+  for (int b = 0; b < NV; ++b) {
+    const int64_t i = threadIdx.x + (int64_t)b * kBlockThreads;
+    if (i < nvec) {
+      dv[b] = dy[t * nvec + i];
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        const int32_t r = bcast_i(myrow, j);
+        if (r >= 0) yv[b][j] = yd[(int64_t)r * nvec + i];
+      }
+      m = fmaxf(m, absmax8(dv[b]));
+    }
+  }
+  m = wave_max(m);
+  if (lane == 0) amx[wave] = m;
+  __syncthreads();
+  m = amx[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) m = fmaxf(m, amx[w]);
+  float inv[K], dg[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    dg[j] = 0.f;
+    const float a = bf2f(f2bf(fabsf(bcast_f(mygate, j)) * m));
+    inv[j] = a > 0.f ? 448.0f / a : 0.f;
+    const int32_t r = bcast_i(myrow, j);
+    if (threadIdx.x == 0 && r >= 0) dq_scale[r] = a > 0.f ? a / 448.0f : 1.0f;
+  }
+#pragma unroll
+  for (int b = 0; b < NV; ++b) {
+    const int64_t i = threadIdx.x + (int64_t)b * kBlockThreads;
+    if (i >= nvec) continue;
+    float d[V::N];
+    V::to_f(dv[b], d);
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const int32_t r = bcast_i(myrow, j);
+      if (r < 0) continue;
+      const float g = bcast_f(mygate, j);
+      float f[V::N], o[V::N];
+      V::to_f(yv[b][j], f);
+#pragma unroll
+      for (int q = 0; q < V::N; ++q) { dg[j] = fmaf(d[q], f[q], dg[j]); o[q] = g * d[q]; }
+      const u32x4 ov = V::from_f(o);
+      dyd[(int64_t)r * nvec + i] = ov;
+      dq[(int64_t)r * nvec + i] = quant8(ov, inv[j]);
     }
   }
 #pragma unroll
@@ -410,14 +596,32 @@ hipError_t launch_quantize_rows_fp8(const void* src, void* codes, float* scale, 
   return hipGetLastError();
 }
 
-hipError_t launch_quantize_segments_fp8(const void* src, void* codes, float* scale,
+hipError_t launch_quantize_segments_fp8(const char* name, const void* src, void* codes, float* scale,
                                         const int32_t* offsets, int El, int c0, int nc, int64_t P_c,
                                         int cols, hipStream_t s) {
   if (nc <= 0 || El <= 0) return hipSuccess;
+  // enough waves for every row of a chunk up to 16K rows (the row count is on the device)
+  const int64_t nvec = cols / 8;
+  const unsigned gx = (unsigned)std::max<int64_t>(1, std::min<int64_t>((P_c + kTokPerBlock - 1) / kTokPerBlock, 4096));
   {
-    MOE_TRACE("quantize_h_fp8", s);
-    MOE_LAUNCH(quantize_segments_fp8_kernel, dim3(256, (unsigned)nc), dim3(256), 0, s,
-                       (const u32x4*)src, (uint2*)codes, scale, offsets, El, c0, P_c, (int64_t)cols / 8);
+    MOE_TRACE(name, s);
+    if (nvec <= 64 * kFp8MaxVec)
+      MOE_LAUNCH(quantize_segments_fp8_kernel<true>, dim3(gx, (unsigned)nc), dim3(256), 0, s,
+                 (const u32x4*)src, (uint2*)codes, scale, offsets, El, c0, P_c, nvec);
+    else
+      MOE_LAUNCH(quantize_segments_fp8_kernel<false>, dim3(gx, (unsigned)nc), dim3(256), 0, s,
+                 (const u32x4*)src, (uint2*)codes, scale, offsets, El, c0, P_c, nvec);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_cols_fp8(const void* src, void* codes_t, float* scale, int64_t batch, int64_t rows,
+                                    int64_t cols, hipStream_t s) {
+  if (batch <= 0 || rows <= 0 || cols <= 0) return hipSuccess;
+  {
+    MOE_TRACE("quantize_cols_fp8", s);
+    MOE_LAUNCH(quantize_cols_fp8_kernel, dim3((unsigned)((cols + kColTile - 1) / kColTile), (unsigned)batch),
+               dim3(256), 0, s, (const u32x4*)src, (uint8_t*)codes_t, scale, rows, cols);
   }
   return hipGetLastError();
 }
@@ -442,22 +646,36 @@ hipError_t launch_combine(bool bf16, const void* yd, const float* gates, const i
 
 hipError_t launch_combine_bwd(bool bf16, const void* dy, const void* yd, const float* gates,
                               const int32_t* row_of, void* dyd, float* dgates, int64_t t0,
-                              int64_t t1, int K, int64_t row_bytes, hipStream_t s) {
+                              int64_t t1, int K, int64_t row_bytes, hipStream_t s, void* dyd_q,
+                              float* dyd_scale) {
   if (t1 <= t0) return hipSuccess;
-  if (bf16)
-    {
-      MOE_TRACE("combine_bwd", s);
-      MOE_SWITCH_K(K, MOE_LAUNCH((combine_bwd_kernel<uint16_t, KK>), dim3((unsigned)(t1 - t0)), dim3(kBlockThreads), 0, s,
-                         (const u32x4*)dy, (const u32x4*)yd, gates, row_of, (u32x4*)dyd, dgates,
-                         t0, t1, row_bytes / 16));
+  const int64_t nvec = row_bytes / 16;
+  if (bf16 && dyd_q) {
+    if (nvec > kCombineQMaxVec * kBlockThreads) return hipErrorInvalidValue;  // the host checks H first
+    MOE_TRACE("combine_bwd_q", s);
+#define MOE_CBQ(NV_)                                                                                            \
+    MOE_SWITCH_K(K, MOE_LAUNCH((combine_bwd_q_kernel<KK, NV_>), dim3((unsigned)(t1 - t0)), dim3(kBlockThreads), 0, s, \
+                               (const u32x4*)dy, (const u32x4*)yd, gates, row_of, (u32x4*)dyd, dgates,           \
+                               (uint2*)dyd_q, dyd_scale, t0, t1, nvec))
+    if (nvec <= kBlockThreads) {
+      MOE_CBQ(1);
+    } else if (nvec <= 2 * kBlockThreads) {
+      MOE_CBQ(2);
+    } else {
+      MOE_CBQ(4);
     }
-  else
-    {
-      MOE_TRACE("combine_bwd", s);
-      MOE_SWITCH_K(K, MOE_LAUNCH((combine_bwd_kernel<float, KK>), dim3((unsigned)(t1 - t0)), dim3(kBlockThreads), 0, s,
-                         (const u32x4*)dy, (const u32x4*)yd, gates, row_of, (u32x4*)dyd, dgates,
-                         t0, t1, row_bytes / 16));
-    }
+#undef MOE_CBQ
+  } else if (bf16) {
+    MOE_TRACE("combine_bwd", s);
+    MOE_SWITCH_K(K, MOE_LAUNCH((combine_bwd_kernel<uint16_t, KK>), dim3((unsigned)(t1 - t0)), dim3(kBlockThreads),
+                               0, s, (const u32x4*)dy, (const u32x4*)yd, gates, row_of, (u32x4*)dyd, dgates,
+                               t0, t1, nvec));
+  } else {
+    MOE_TRACE("combine_bwd", s);
+    MOE_SWITCH_K(K, MOE_LAUNCH((combine_bwd_kernel<float, KK>), dim3((unsigned)(t1 - t0)), dim3(kBlockThreads),
+                               0, s, (const u32x4*)dy, (const u32x4*)yd, gates, row_of, (u32x4*)dyd, dgates,
+                               t0, t1, nvec));
+  }
   return hipGetLastError();
 }
 

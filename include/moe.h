@@ -77,15 +77,20 @@ typedef enum moe_status {
  *   P_c       dispatch rows per chunk region: multiple of 4, >= ceil(T/n)*min(k, E_local)
  *             (the static worst case, so no count ever returns to the host)
  *   P_out     combine output rows: multiple of 4, >= T (rows T..P_out-1 are never written)
- *   dtype     moe_dtype of the payloads (table above) */
+ *   dtype     moe_dtype of the payloads (table above)
+ *   flags     MOE_FLAG_* bits, 0 for the default path; an unknown bit is MOE_ERR_ARG */
 typedef struct moe_desc {
   int64_t T;
   int32_t H, I, E, e0, E_local, k, n_chunks;
   int64_t P_c;
   int64_t P_out;
   int32_t dtype;
-  int32_t reserved; /* must be 0 */
+  int32_t flags;
 } moe_desc;
+
+/* Input gradients of the expert FFN on FP8 MFMA (moe_expert_dgrad_fp8) in the layer backward;
+ * BF16 dtype only (MOE_ERR_UNSUPPORTED otherwise). Weight gradients stay BF16. */
+#define MOE_FLAG_FP8_DGRAD 1
 
 /* ---------------------------------------------------------------------------------------
  * Stage calls
@@ -172,6 +177,24 @@ moe_status moe_expert_wgrad(const moe_desc* d, const void* dyd, const void* dgu,
                             const void* h, const int32_t* offsets, void* dw1, void* dw2,
                             void* stream);
 
+/* FP8 input gradients (a reading: ChunkedEP "Summary" gives FP8 for the dispatched payloads of
+ * the forward only; the backward applies the same per-row quantisation to its payloads). Needs a
+ * BF16 descriptor. Per chunk:
+ *   dyd rows quantised per row into dyd_q [P,H] e4m3 / dyd_scale [P] (FP32 steps of moe_dispatch);
+ *   dh = deq(dyd_q) deq(W2t)^T on FP8 MFMA (FP32 accumulation, s_row * s_col dequantisation);
+ *   dG, dU as in moe_expert_ffn_bwd from the saved G, U (gu) -> dgu [P,2I] BF16;
+ *   dgu rows quantised per row into dgu_q [P,2I] / dgu_scale [P];
+ *   dxd = deq(dgu_q) deq(W1t)^T on FP8 MFMA -> BF16.
+ * w2t [E_local][I][H] and w1t [E_local][H][2I] are the weights quantised per column and stored
+ * transposed (moe_quantize_cols_fp8 of W2 [E_local][H][I] and W1 [E_local][2I][H]), with scales
+ * w2t_scale [E_local][I] and w1t_scale [E_local][H]. dgu (BF16) is what moe_expert_wgrad then
+ * reads. Rows N_c..P_c-1 of every output are not written. */
+moe_status moe_expert_dgrad_fp8(const moe_desc* d, int chunk, const void* dyd, const void* gu,
+                                const void* w1t, const float* w1t_scale, const void* w2t,
+                                const float* w2t_scale, const int32_t* offsets, void* dyd_q,
+                                float* dyd_scale, void* dgu, void* dgu_q, float* dgu_scale,
+                                void* dxd, void* stream);
+
 /* Dispatch backward: dx[t] = RNE( sum over local slots of dxd[row_of[t][j]]
  * + sum_j dlogits[t][idx[t][j]] * W_r[idx[t][j]] ) with FP32 accumulation (the second sum is
  * the router projection's input gradient; dlogits is zero off the selected experts). */
@@ -183,6 +206,14 @@ moe_status moe_dispatch_bwd(const moe_desc* d, int chunk, const void* dxd, const
  * codes = e4m3(w * (448/amax)) and scale = amax/448 with the FP32 steps of moe_dispatch. */
 moe_status moe_quantize_rows_fp8(int64_t rows, int32_t cols, const void* src_bf16, void* codes,
                                  float* scale, void* stream);
+
+/* Per-column FP8 quantisation, stored transposed (the weights of moe_expert_dgrad_fp8): for each of
+ * `batch` BF16 matrices src [rows, cols] (row-major, contiguous), column j's absmax gives
+ * scale[b][j] = amax/448 (1 for an all-zero column) and codes_t[b][j][i] = e4m3(src[b][i][j] *
+ * (448/amax)) with the FP32 steps of moe_dispatch, so codes_t is [batch, cols, rows]. rows a
+ * multiple of 16, cols a multiple of 8, batch <= 65535 (MOE_ERR_ARG / MOE_ERR_UNSUPPORTED). */
+moe_status moe_quantize_cols_fp8(int64_t batch, int64_t rows, int32_t cols, const void* src_bf16,
+                                 void* codes_t, float* scale, void* stream);
 
 /* ---------------------------------------------------------------------------------------
  * Paged activation stash (torchtitan PR 5541, "AI-Generated Details": page-aligned multi-token
@@ -244,6 +275,10 @@ typedef struct moe_tensors {
   void* dx; void* dw1; void* dw2; void* dwr;
   /* scratch of moe_workspace_bytes().workspace bytes */
   void* workspace;
+  /* MOE_FLAG_FP8_DGRAD only (see moe_expert_dgrad_fp8): transposed FP8 weights and the quantised
+   * backward payloads */
+  const void* w1t; const float* w1t_scale; const void* w2t; const float* w2t_scale;
+  void* dyd_q; float* dyd_scale; void* dgu_q; float* dgu_scale;
 } moe_tensors;
 
 moe_status moe_layer_forward(const moe_desc* d, const moe_tensors* t, void* compute_stream,
@@ -267,6 +302,7 @@ typedef struct moe_workspace_sizes {
   int64_t xd, xd_scale, gu, h, h_scale, yd, out;
   int64_t dyd, dgates, dlogits, dwr_acc, dgu, dxd, dx, dw1, dw2, dwr;
   int64_t route_scratch, route_bwd_scratch, workspace; /* workspace = max of the scratches */
+  int64_t w1t, w1t_scale, w2t, w2t_scale, dyd_q, dyd_scale, dgu_q, dgu_scale; /* MOE_FLAG_FP8_DGRAD */
 } moe_workspace_sizes;
 moe_status moe_workspace_bytes(const moe_desc* d, moe_workspace_sizes* out);
 

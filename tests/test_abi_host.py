@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(mh.exported_symbols())
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
 
 
 @pytest.mark.parametrize("T,k,El,n", [(256, 2, 8, 1), (16384, 8, 16, 2), (32768, 8, 16, 2), (10, 3, 2, 3),
@@ -53,7 +53,7 @@ def _desc(**kw):
         base.setdefault("P_c", pc)
         base.setdefault("P_out", po)
     dt = base.pop("dtype")
-    return mh.MoeDesc(dtype=mh.DTYPES.get(dt, dt) if isinstance(dt, str) else dt, reserved=0, **base)
+    return mh.MoeDesc(dtype=mh.DTYPES.get(dt, dt) if isinstance(dt, str) else dt, flags=0, **base)
 
 
 def _status_of(fn, *a):
@@ -102,6 +102,33 @@ def test_workspace_bytes():
     f8 = mh.make_desc(T=16384, H=2048, I=768, E=128, E_local=16, k=8, n_chunks=2, dtype="fp8")
     ws8 = mh.workspace_bytes(f8)
     assert ws8["xd"] == P * 2048 and ws8["xd_scale"] == P * 4 and ws8["dw1"] == 0
+
+
+def test_fp8_dgrad_flag_validation_and_sizes():
+    _lib_or_skip()
+    d = mh.make_desc(T=16384, H=2048, I=768, E=128, E_local=16, k=8, n_chunks=2, dtype="bf16",
+                     flags=mh.FLAG_FP8_DGRAD)
+    ws = mh.workspace_bytes(d)
+    P = 2 * 65536
+    assert ws["w1t"] == 16 * 2048 * 1536 and ws["w1t_scale"] == 16 * 2048 * 4
+    assert ws["w2t"] == 16 * 768 * 2048 and ws["w2t_scale"] == 16 * 768 * 4
+    assert ws["dyd_q"] == P * 2048 and ws["dgu_q"] == P * 1536 and ws["dyd_scale"] == ws["dgu_scale"] == P * 4
+    assert mh.workspace_bytes(mh.make_desc(T=16384, H=2048, I=768, E=128, E_local=16, k=8, n_chunks=2))["w1t"] == 0
+    bad = mh.make_desc(T=64, H=128, I=64, E=8, E_local=4, k=2, n_chunks=1, flags=2)
+    assert _status_of(mh.workspace_bytes, bad)[0] == -1
+    f8 = mh.make_desc(T=64, H=128, I=64, E=8, E_local=4, k=2, n_chunks=1, dtype="fp8", flags=mh.FLAG_FP8_DGRAD)
+    assert _status_of(mh.workspace_bytes, f8)[0] == -3
+    # the stage call rejects a non-BF16 descriptor before touching any pointer
+    f32 = mh.make_desc(T=64, H=128, I=64, E=8, E_local=4, k=2, n_chunks=1, dtype="f32")
+    assert _status_of(mh.moe_expert_dgrad_fp8, f32, 0, *([1] * 13), 0)[0] == -3
+
+
+def test_quantize_cols_argument_errors():
+    _lib_or_skip()
+    assert _status_of(mh.moe_quantize_cols_fp8, 1, 24, 16, 1, 1, 1, 0)[0] == -1   # rows % 16
+    assert _status_of(mh.moe_quantize_cols_fp8, 1, 32, 12, 1, 1, 1, 0)[0] == -1   # cols % 8
+    assert _status_of(mh.moe_quantize_cols_fp8, 1, 32, 16, None, 1, 1, 0)[0] == -1
+    assert _status_of(mh.moe_quantize_cols_fp8, 0, 32, 16, None, None, None, 0)[0] == 0  # nothing to do
 
 
 def test_extent_tracker_matches_art971_fixture_and_oracle():
