@@ -447,7 +447,9 @@ def main():
     dom_ms = [ms for n, _st, ms in mh.moe_trace_entries() if n == dom]
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
-    # the same loop without any launch log
+    # the same loop without any launch log (warmed up again after reading the log)
+    for _ in range(args.warmup):
+        fb()
     torch.cuda.synchronize()
     u0 = time.perf_counter()
     for _ in range(args.steps):
