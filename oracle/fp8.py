@@ -165,16 +165,56 @@ def ffn_bwd_fp8_dgrad(dyd, xd, gu, h, offsets, P_c, w1, w2):
     return dgu, dxd, dw1, dw2
 
 
-def backward_fp8_dgrad(fwd: dict, x, dy, w1, w2, w_r):
+def expert_rows(offsets, P_c, e):
+    """Dispatch rows of local expert e over every chunk, in chunk order."""
+    offsets = np.asarray(offsets)
+    return np.concatenate([np.arange(c * P_c + offsets[c, e], c * P_c + offsets[c, e + 1])
+                           for c in range(offsets.shape[0])]).astype(np.int64)
+
+
+def ffn_wgrad_fp8(dyd, dgu, xd, h, offsets, P_c, El):
+    """Expert weight gradients on FP8 (the survey's NEXT-1; a reading, the pages give FP8 only for
+    forward payloads). A weight gradient contracts over the expert's token rows, so its operands are
+    scaled per column over those rows (every chunk's rows of the expert together): for each
+    operand, the BF16-rounded rows of expert e are quantised per column (:func:`quantize_cols_t`,
+    the FP32 steps of the row quantiser) and
+      dW2[e] = deq(dyd_e)^T deq(h_e),   dW1[e] = deq(dgu_e)^T deq(xd_e),
+    accumulated exactly (FP64) and dequantised by s_col(A) * s_col(B). An expert without rows
+    gets zeros. Returns dw1 [El, 2I, H], dw2 [El, H, I] (FP64)."""
+    H = np.asarray(xd).shape[1]
+    I = np.asarray(h).shape[1]
+    dw1 = np.zeros((El, 2 * I, H))
+    dw2 = np.zeros((El, H, I))
+
+    def tq(a, rows):   # transposed, per-column dequantised operand [C, R]
+        return dequantize_rows(*quantize_cols_t(bf16_round(np.asarray(a, dtype=np.float64)[rows])))
+
+    for e in range(El):
+        rows = expert_rows(offsets, P_c, e)
+        if rows.size == 0:
+            continue
+        dw2[e] = tq(dyd, rows) @ tq(h, rows).T
+        dw1[e] = tq(dgu, rows) @ tq(xd, rows).T
+    return dw1, dw2
+
+
+def backward_fp8_dgrad(fwd: dict, x, dy, w1, w2, w_r, fp8_dgrad=True, fp8_wgrad=False):
     """The layer backward (oracle.ffn.backward) with the expert FFN's input gradients and dW1 from
-    :func:`ffn_bwd_fp8_dgrad`; combine, routing and dispatch backward, dW2 and the router weight
-    gradient are those of the BF16 backward, which does not depend on dgu."""
+    :func:`ffn_bwd_fp8_dgrad` (fp8_dgrad) and/or the expert weight gradients from
+    :func:`ffn_wgrad_fp8` (fp8_wgrad); combine, routing and dispatch backward and the router
+    weight gradient are those of the BF16 backward, which does not depend on them."""
     from . import ffn
     base = ffn.backward(fwd, x, dy, w1, w2, w_r)
-    dgu, dxd, dw1, dw2 = ffn_bwd_fp8_dgrad(base["dyd"], fwd["xd"], fwd["gu"], fwd["h"], fwd["offsets"],
-                                          fwd["P_c"], w1, w2)
-    dx = ffn.dispatch_bwd(dxd, fwd["row_of"], base["dlogits"], w_r)
-    return dict(base, dgu=dgu, dxd=dxd, dx=dx, dw1=dw1, dw2=dw2)
+    out = dict(base)
+    if fp8_dgrad:
+        dgu, dxd, dw1, dw2 = ffn_bwd_fp8_dgrad(base["dyd"], fwd["xd"], fwd["gu"], fwd["h"], fwd["offsets"],
+                                              fwd["P_c"], w1, w2)
+        dx = ffn.dispatch_bwd(dxd, fwd["row_of"], base["dlogits"], w_r)
+        out.update(dgu=dgu, dxd=dxd, dx=dx, dw1=dw1, dw2=dw2)
+    if fp8_wgrad:
+        out["dw1"], out["dw2"] = ffn_wgrad_fp8(out["dyd"], out["dgu"], fwd["xd"], fwd["h"], fwd["offsets"],
+                                               fwd["P_c"], np.asarray(w1).shape[0])
+    return out
 
 
 def forward(x, logits, w1, w2, *, k, e0, E_local, n_chunks, P_c=None, wq=None):

@@ -243,3 +243,49 @@ def test_fp8_dgrad_layer_backward_changes_only_the_expert_input_gradients():
     for name in ("dx", "dw1"):
         err = np.linalg.norm(q[name] - exact[name]) / np.linalg.norm(exact[name])
         assert 1e-4 < err < 2.0 ** -4, (name, err)
+
+
+def _wgrad_case(exact, seed=5):
+    """Two chunks of 16 rows, two local experts (rows 0-4 and 5-8 of chunk 0, 0-2 and 3-9 of
+    chunk 1). exact: every column of every operand holds values in {0, +-1/2, +-1} over an expert's
+    rows plus a 3.5 in the expert's first row (scale 2^-7), so per-column quantisation is lossless."""
+    rng = np.random.default_rng(seed)
+    P_c, H, I = 16, 32, 16
+    offsets = np.array([[0, 5, 9], [0, 3, 10]])
+    def draw(cols):
+        if not exact:
+            return rng.normal(size=(2 * P_c, cols))
+        a = rng.choice([0.0, 0.5, -0.5, 1.0, -1.0], size=(2 * P_c, cols))
+        a[[0, 5]] = 3.5     # the first row of each expert (chunk 0)
+        return a
+    return dict(dyd=draw(H), dgu=draw(2 * I), xd=draw(H), h=draw(I), offsets=offsets, P_c=P_c, El=2)
+
+
+def test_fp8_wgrad_oracle_is_exact_on_e4m3_exact_columns():
+    """Against a brute-force sum of outer products over the expert's rows of both chunks."""
+    from oracle.fp8 import ffn_wgrad_fp8
+    c = _wgrad_case(exact=True)
+    dw1, dw2 = ffn_wgrad_fp8(c["dyd"], c["dgu"], c["xd"], c["h"], c["offsets"], c["P_c"], c["El"])
+    for e in range(c["El"]):
+        w1 = np.zeros(dw1[e].shape)
+        w2 = np.zeros(dw2[e].shape)
+        for ch in range(2):
+            for r in range(ch * c["P_c"] + c["offsets"][ch, e], ch * c["P_c"] + c["offsets"][ch, e + 1]):
+                w2 += np.outer(c["dyd"][r], c["h"][r])
+                w1 += np.outer(c["dgu"][r], c["xd"][r])
+        np.testing.assert_allclose(dw2[e], w2, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(dw1[e], w1, rtol=0, atol=1e-12)
+
+
+def test_fp8_wgrad_oracle_within_e4m3_bound():
+    from oracle.fp8 import ffn_wgrad_fp8
+    c = _wgrad_case(exact=False)
+    dw1, dw2 = ffn_wgrad_fp8(c["dyd"], c["dgu"], c["xd"], c["h"], c["offsets"], c["P_c"], c["El"])
+    for e in range(c["El"]):
+        rows = np.concatenate([np.arange(ch * 16 + c["offsets"][ch, e], ch * 16 + c["offsets"][ch, e + 1])
+                               for ch in range(2)])
+        w2 = c["dyd"][rows].T @ c["h"][rows]
+        w1 = c["dgu"][rows].T @ c["xd"][rows]
+        for got, want in ((dw2[e], w2), (dw1[e], w1)):
+            err = np.linalg.norm(got - want) / np.linalg.norm(want)
+            assert 1e-4 < err < 2.0 ** -4, err
