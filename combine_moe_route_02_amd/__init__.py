@@ -36,6 +36,7 @@ class MoeDesc(Structure):
 
 
 FLAG_FP8_DGRAD = 1
+FLAG_FP8_WGRAD = 2
 
 
 TENSOR_FIELDS = ["x", "logits", "w1", "w1_scale", "w2", "w2_scale", "w_r", "dy",
@@ -43,7 +44,8 @@ TENSOR_FIELDS = ["x", "logits", "w1", "w1_scale", "w2", "w2_scale", "w_r", "dy",
                  "gu", "h", "h_scale", "yd", "out",
                  "dyd", "dgates", "dlogits", "dwr_acc", "dgu", "dxd", "dx", "dw1", "dw2", "dwr",
                  "workspace",
-                 "w1t", "w1t_scale", "w2t", "w2t_scale", "dyd_q", "dyd_scale", "dgu_q", "dgu_scale"]
+                 "w1t", "w1t_scale", "w2t", "w2t_scale", "dyd_q", "dyd_scale", "dgu_q", "dgu_scale",
+                 "dyd_t", "dyd_cs", "dgu_t", "dgu_cs", "xd_t", "xd_cs", "h_t", "h_cs"]
 
 
 class MoeTensors(Structure):
@@ -53,7 +55,8 @@ class MoeTensors(Structure):
 SIZE_FIELDS = ["topk_idx", "gates", "counts", "offsets", "row_of", "src_token", "xd", "xd_scale", "gu",
                "h", "h_scale", "yd", "out", "dyd", "dgates", "dlogits", "dwr_acc", "dgu", "dxd", "dx",
                "dw1", "dw2", "dwr", "route_scratch", "route_bwd_scratch", "workspace",
-               "w1t", "w1t_scale", "w2t", "w2t_scale", "dyd_q", "dyd_scale", "dgu_q", "dgu_scale"]
+               "w1t", "w1t_scale", "w2t", "w2t_scale", "dyd_q", "dyd_scale", "dgu_q", "dgu_scale",
+               "dyd_t", "dyd_cs", "dgu_t", "dgu_cs", "xd_t", "xd_cs", "h_t", "h_cs"]
 
 
 class MoeWorkspaceSizes(Structure):
@@ -76,6 +79,7 @@ _SIGS = {
     "moe_quantize_rows_fp8": [c_int64, c_int32] + [c_void_p] * 4,
     "moe_quantize_cols_fp8": [c_int64, c_int64, c_int32] + [c_void_p] * 4,
     "moe_expert_dgrad_fp8": [POINTER(MoeDesc), c_int] + [c_void_p] * 14,
+    "moe_expert_wgrad_fp8": [POINTER(MoeDesc)] + [c_void_p] * 16,
     "moe_stash_store": [c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_int64, c_int64, c_void_p,
                         c_void_p, c_int32, c_int32, c_void_p],
     "moe_stash_load": [c_void_p, c_void_p, c_int64, c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p,
@@ -224,6 +228,14 @@ def moe_expert_dgrad_fp8(d, chunk, dyd, gu, w1t, w1t_scale, w2t, w2t_scale, offs
                                       _ptr(w2t), _ptr(w2t_scale), _ptr(offsets), _ptr(dyd_q), _ptr(dyd_scale),
                                       _ptr(dgu), _ptr(dgu_q), _ptr(dgu_scale), _ptr(dxd), _stream(stream)),
            "moe_expert_dgrad_fp8")
+
+
+def moe_expert_wgrad_fp8(d, dyd, dgu, xd, h, offsets, dyd_t, dyd_cs, dgu_t, dgu_cs, xd_t, xd_cs, h_t, h_cs, dw1,
+                         dw2, stream=None):
+    _check(lib().moe_expert_wgrad_fp8(ctypes.byref(d), _ptr(dyd), _ptr(dgu), _ptr(xd), _ptr(h), _ptr(offsets),
+                                      _ptr(dyd_t), _ptr(dyd_cs), _ptr(dgu_t), _ptr(dgu_cs), _ptr(xd_t),
+                                      _ptr(xd_cs), _ptr(h_t), _ptr(h_cs), _ptr(dw1), _ptr(dw2), _stream(stream)),
+           "moe_expert_wgrad_fp8")
 
 
 def moe_quantize_rows_fp8(rows, cols, src_bf16, codes, scale, stream=None):
@@ -383,6 +395,12 @@ def allocate(d: MoeDesc, device="cuda", backward: bool = True, fill=None):
         spec.update({"w1t": ((El, H, 2 * I), u8), "w1t_scale": ((El, H), f32), "w2t": ((El, I, H), u8),
                      "w2t_scale": ((El, I), f32), "dyd_q": ((P, H), u8), "dyd_scale": ((P,), f32),
                      "dgu_q": ((P, 2 * I), u8), "dgu_scale": ((P,), f32)})
+    if backward and (d.flags & FLAG_FP8_WGRAD):
+        # per-expert transposed FP8 operands of the weight gradients (sizes from the library)
+        for name in ("dyd_t", "dgu_t", "xd_t", "h_t"):
+            spec[name] = ((max(1, ws[name]),), u8)
+        for name in ("dyd_cs", "dgu_cs", "xd_cs", "h_cs"):
+            spec[name] = ((max(1, ws[name] // 4),), f32)
     out = {}
     for name, (shape, dt) in spec.items():
         out[name] = torch.empty(shape, dtype=dt, device=device)

@@ -53,7 +53,8 @@ int elem_size(int dtype) { return dtype == MOE_F32 ? 4 : 2; }  // payload rows (
 
 moe_status validate(const moe_desc* d) {
   if (!d) return fail(MOE_ERR_ARG, "descriptor is NULL");
-  if (d->flags & ~MOE_FLAG_FP8_DGRAD) return fail(MOE_ERR_ARG, "descriptor flags 0x%x hold an unknown bit", d->flags);
+  if (d->flags & ~(MOE_FLAG_FP8_DGRAD | MOE_FLAG_FP8_WGRAD))
+    return fail(MOE_ERR_ARG, "descriptor flags 0x%x hold an unknown bit", d->flags);
   if (d->dtype != MOE_F32 && d->dtype != MOE_BF16 && d->dtype != MOE_FP8_E4M3)
     return fail(MOE_ERR_ARG, "unknown dtype %d", d->dtype);
   if (d->T < 0) return fail(MOE_ERR_ARG, "T = %lld is negative", (long long)d->T);
@@ -69,8 +70,8 @@ moe_status validate(const moe_desc* d) {
   if (d->H <= 0 || d->H % 64) return fail(MOE_ERR_UNSUPPORTED, "H = %d must be a positive multiple of 64", d->H);
   if (d->I <= 0 || d->I % 64) return fail(MOE_ERR_UNSUPPORTED, "I = %d must be a positive multiple of 64", d->I);
   if (d->dtype == MOE_BF16 && d->E % 4) return fail(MOE_ERR_UNSUPPORTED, "BF16 path needs E %% 4 == 0 (E = %d)", d->E);
-  if ((d->flags & MOE_FLAG_FP8_DGRAD) && d->dtype != MOE_BF16)
-    return fail(MOE_ERR_UNSUPPORTED, "MOE_FLAG_FP8_DGRAD needs the BF16 dtype");
+  if (d->flags && d->dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "the FP8 backward flags need the BF16 dtype");
   if (d->dtype == MOE_FP8_E4M3 && d->H > 8192)
     return fail(MOE_ERR_UNSUPPORTED, "FP8 dispatch keeps a row in registers: H = %d above 8192", d->H);
   if (d->P_c % 4) return fail(MOE_ERR_CAPACITY, "P_c = %lld is not a multiple of 4", (long long)d->P_c);
@@ -190,6 +191,17 @@ moe_status moe_workspace_bytes(const moe_desc* d, moe_workspace_sizes* o) {
     o->dyd_scale = P * 4;
     o->dgu_q = P * 2 * I;
     o->dgu_scale = P * 4;
+  }
+  if (d->flags & MOE_FLAG_FP8_WGRAD) {
+    const int64_t Kp = P + 64 * El;   // the padded rows of every expert together, at most
+    o->dyd_t = H * Kp;
+    o->dyd_cs = El * H * 4;
+    o->dgu_t = 2 * I * Kp;
+    o->dgu_cs = El * 2 * I * 4;
+    o->xd_t = H * Kp;
+    o->xd_cs = El * H * 4;
+    o->h_t = I * Kp;
+    o->h_cs = El * I * 4;
   }
   o->route_scratch = moe::route_scratch_bytes(T, (int)n, (int)E);
   o->route_bwd_scratch = fp8 ? 0 : router_scratch(d);
@@ -393,6 +405,32 @@ moe_status moe_expert_dgrad_fp8(const moe_desc* d, int chunk, const void* dyd, c
                                dgu_q, dgu_scale, dxd, true, stream);
 }
 
+static moe_status expert_wgrad_fp8_impl(const moe_desc* d, const void* dyd, const void* dgu, const void* xd,
+                                        const void* h, const int32_t* offsets, void* dyd_t, float* dyd_cs,
+                                        void* dgu_t, float* dgu_cs, void* xd_t, float* xd_cs, void* h_t,
+                                        float* h_cs, void* dw1, void* dw2, bool quantize, void* stream) {
+  MOE_TRY(validate(d));
+  if (d->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "FP8 weight gradients need the BF16 dtype");
+  if (d->E_local == 0) return MOE_OK;
+  MOE_NEED(offsets); MOE_NEED(dw1); MOE_NEED(dw2);
+  MOE_NEED(dyd_t); MOE_NEED(dyd_cs); MOE_NEED(dgu_t); MOE_NEED(dgu_cs);
+  MOE_NEED(xd_t); MOE_NEED(xd_cs); MOE_NEED(h_t); MOE_NEED(h_cs);
+  if (rows_of(d) > 0) { MOE_NEED(dyd); MOE_NEED(dgu); MOE_NEED(xd); MOE_NEED(h); }
+  MOE_HIP(moe::launch_expert_wgrad_fp8(dyd, dgu, xd, h, offsets, dyd_t, dyd_cs, dgu_t, dgu_cs, xd_t, xd_cs, h_t,
+                                       h_cs, dw1, dw2, d->H, d->I, d->E_local, d->n_chunks, d->P_c,
+                                       (hipStream_t)stream, quantize),
+          "expert_wgrad_fp8");
+  return MOE_OK;
+}
+
+moe_status moe_expert_wgrad_fp8(const moe_desc* d, const void* dyd, const void* dgu, const void* xd, const void* h,
+                                const int32_t* offsets, void* dyd_t, float* dyd_cs, void* dgu_t, float* dgu_cs,
+                                void* xd_t, float* xd_cs, void* h_t, float* h_cs, void* dw1, void* dw2,
+                                void* stream) {
+  return expert_wgrad_fp8_impl(d, dyd, dgu, xd, h, offsets, dyd_t, dyd_cs, dgu_t, dgu_cs, xd_t, xd_cs, h_t, h_cs,
+                               dw1, dw2, true, stream);
+}
+
 moe_status moe_dispatch_bwd(const moe_desc* d, int chunk, const void* dxd, const int32_t* row_of,
                             const int32_t* topk_idx, const float* dlogits, const void* w_r, void* dx,
                             void* stream) {
@@ -505,6 +543,10 @@ static moe_status check_bwd_tensors(const moe_desc* d, const moe_tensors* t) {
     if (d->flags & MOE_FLAG_FP8_DGRAD) {
       MOE_NEED(t->w1t); MOE_NEED(t->w1t_scale); MOE_NEED(t->w2t); MOE_NEED(t->w2t_scale);
       MOE_NEED(t->dyd_q); MOE_NEED(t->dyd_scale); MOE_NEED(t->dgu_q); MOE_NEED(t->dgu_scale);
+    }
+    if (d->flags & MOE_FLAG_FP8_WGRAD) {
+      MOE_NEED(t->dyd_t); MOE_NEED(t->dyd_cs); MOE_NEED(t->dgu_t); MOE_NEED(t->dgu_cs);
+      MOE_NEED(t->xd_t); MOE_NEED(t->xd_cs); MOE_NEED(t->h_t); MOE_NEED(t->h_cs);
     }
   }
   return MOE_OK;
@@ -626,7 +668,11 @@ static moe_status backward_sched(const moe_desc* d, const moe_tensors* t, hipStr
     }
     MOE_TRY(moe_dispatch_bwd(d, c, t->dxd, t->row_of, t->topk_idx, t->dlogits, t->w_r, t->dx, side));
   }
-  MOE_TRY(moe_expert_wgrad(d, t->dyd, t->dgu, t->xd, t->h, t->offsets, t->dw1, t->dw2, cs));
+  if (d->flags & MOE_FLAG_FP8_WGRAD)
+    MOE_TRY(expert_wgrad_fp8_impl(d, t->dyd, t->dgu, t->xd, t->h, t->offsets, t->dyd_t, t->dyd_cs, t->dgu_t,
+                                  t->dgu_cs, t->xd_t, t->xd_cs, t->h_t, t->h_cs, t->dw1, t->dw2, true, cs));
+  else
+    MOE_TRY(moe_expert_wgrad(d, t->dyd, t->dgu, t->xd, t->h, t->offsets, t->dw1, t->dw2, cs));
   if (two) {
     MOE_HIP(hipEventRecord(done, as), "hipEventRecord");
     MOE_HIP(hipStreamWaitEvent(cs, done, 0), "hipStreamWaitEvent");
@@ -652,8 +698,8 @@ static moe::ExpertGemm expert_gemm(const moe_desc* d, const moe_tensors* t) {
 }
 
 static bool merged_gemms(const moe_desc* d) { return d->dtype == MOE_BF16 && d->T > 0 && rows_of(d) > 0; }
-// the merged backward launches pair BF16 input-gradient GEMMs; FP8 input gradients run per chunk
-static bool merged_bwd(const moe_desc* d) { return merged_gemms(d) && !(d->flags & MOE_FLAG_FP8_DGRAD); }
+// the merged backward launches pair BF16 GEMMs; with an FP8 backward flag the backward runs per chunk
+static bool merged_bwd(const moe_desc* d) { return merged_gemms(d) && d->flags == 0; }
 
 //   compute: R0 D0 GU0 | wait(disp1) [DN0 GU1] | wait(disp2) [DN1 GU2] | ... | DN n-1, C n-1
 //   aux:     wait(disp0) R1 D1 | R2 D2, wait(ffn0) C0 | R3 D3, wait(ffn1) C1 | ...

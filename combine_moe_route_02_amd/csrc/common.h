@@ -43,6 +43,20 @@ template <> MOE_DEV void st_elem<uint16_t>(uint16_t* p, float v) { *p = f2bf(v);
 // epilogues evaluate it for every element of h, where an IEEE division would dominate the VALU time.
 MOE_DEV float sigmoidf_(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
+// Weight-gradient operands in expert-transposed FP8 form: expert e's rows over every chunk (chunk
+// order) are its K_e rows, padded to Kp_e = K_e rounded up to 64; expert e's block starts at
+// koff_e = sum of Kp over the experts before it. offsets: [n_chunks][El + 1] local offsets.
+MOE_DEV void expert_k(const int32_t* offsets, int El, int n_chunks, int e, int64_t& koff, int& K) {
+  koff = 0;
+  K = 0;
+  for (int g = 0; g <= e; ++g) {
+    int kk = 0;
+    for (int c = 0; c < n_chunks; ++c) kk += offsets[c * (El + 1) + g + 1] - offsets[c * (El + 1) + g];
+    if (g < e) koff += (kk + 63) & ~63;
+    else K = kk;
+  }
+}
+
 MOE_DEV float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);

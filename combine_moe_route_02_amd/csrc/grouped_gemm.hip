@@ -710,6 +710,96 @@ __global__ __launch_bounds__(kThreads) void wgrad1_kernel(WgradArgs a) {
   wgrad_list<BM, BN>(a, 0, ring);
 }
 
+// FP8 weight gradients. Both operands hold, per expert, the columns of its rows (every chunk's)
+// quantised per column and stored transposed: A [M][Kp_e] at byte koff_e * M, B [N][Kp_e] at
+// koff_e * N (expert_k; rows past K_e are zero codes), so both are K-major like the forward
+// operands. C[e] = s_a[e][m] * s_b[e][n] * sum_k A[m][k] B[n][k], one FP32 K loop, one BF16 store.
+struct WgradFp8Args {
+  const uint8_t* A;
+  const uint8_t* B;
+  const float* sa;        // [El][M]
+  const float* sb;        // [El][N]
+  uint16_t* C;            // per expert [M, N]
+  int64_t strideC;
+  int M, N;
+  const int32_t* offsets;
+  int El, n_chunks;
+};
+
+template <int BM, int BN>
+MOE_DEV void wgrad_fp8_tile(const WgradFp8Args& a, int tile, char* ring, int tid, int lane, int wave) {
+  constexpr int WTM = BM / kWM, WTN = BN / kWN, TM = WTM / 32, TN = WTN / 32;
+  const int wm = wave / kWN, wn = wave % kWN;
+  const int mtiles = (a.M + BM - 1) / BM, ntiles = (a.N + BN - 1) / BN;
+  const int grp = tile / (mtiles * ntiles);
+  const int t_in = tile % (mtiles * ntiles);
+  const int m0 = (t_in / ntiles) * BM, n0 = (t_in % ntiles) * BN;
+  int64_t koff;
+  int K;
+  expert_k(a.offsets, a.El, a.n_chunks, grp, koff, K);
+  const int Kp = __builtin_amdgcn_readfirstlane((K + 63) & ~63);
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[tm][tn][q] = 0.f;
+  if (Kp > 0) {
+    Loader<BM, false> la;
+    la.init_kmajor(a.A + koff * a.M + (int64_t)m0 * Kp, Kp, (int64_t)(a.M - m0) * Kp, wave, lane,
+                   [](int r) { return r; });
+    Loader<BN, false> lb;
+    lb.init_kmajor(a.B + koff * a.N + (int64_t)n0 * Kp, Kp, (int64_t)(a.N - n0) * Kp, wave, lane,
+                   [](int r) { return r; });
+    kloop<true, false, false, BM, BN, TM, TN, TM>(la, lb, ring, Kp / 64, wm * WTM, wn * WTN, lane, acc);
+  }
+
+  const int mrow = wm * WTM + out_row(lane);
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    const float sr = a.sa[(int64_t)grp * a.M + min(m0 + mrow + tm * 32, a.M - 1)];
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int nl = wn * WTN + tn * 32 + out_col(gq, lane);
+        const f32x16_t& v = acc[tm][tn];
+        float o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = v[4 * gq + q] * sr * a.sb[(int64_t)grp * a.N + min(n0 + nl + q, a.N - 1)];
+        *(uint2*)(ring + (mrow + tm * 32) * pitch<BN>() + 2 * nl) = pack4(o[0], o[1], o[2], o[3]);
+      }
+  }
+  lds_barrier();
+  store_staged<BM, BN, true>(ring, a.C + (int64_t)grp * a.strideC + (int64_t)m0 * a.N + n0, a.N,
+                             min(BM, a.M - m0), min(BN, a.N - n0), tid);
+  lds_barrier();
+}
+
+template <int BM, int BN>
+MOE_DEV int wgrad_fp8_list(const WgradFp8Args& a, int first, char* ring) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ta = a.El > 0 ? a.El * ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) : 0;
+  const int pxa = (ta + 7) / 8;
+  const int xcd = blockIdx.x % 8, wg_per_xcd = gridDim.x / 8;
+  for (int gs = first_slot(first); gs < first + pxa; gs += wg_per_xcd) {
+    const int tile = xcd * pxa + (gs - first);
+    if (tile < ta) wgrad_fp8_tile<BM, BN>(a, tile, ring, tid, lane, wave);
+  }
+  return first + pxa;
+}
+
+// dW1 and dW2 on FP8 in one persistent launch (dW1's longer list first).
+template <int BM, int BN>
+__global__ __launch_bounds__(kThreads) void wgrad_fp8_kernel(WgradFp8Args a, WgradFp8Args b) {
+  extern __shared__ __attribute__((aligned(1024))) char ring[];
+  const int f = wgrad_fp8_list<BM, BN>(a, 0, ring);
+  wgrad_fp8_list<BM, BN>(b, f, ring);
+}
+
 // A row-grouped GEMM and an independent weight gradient in one launch (the last chunk's gate/up
 // dgrad with dW2, whose tiles fill the dgrad's last round).
 template <int BM1, int BN1, int MODE1, int BM, int BN>
@@ -975,6 +1065,43 @@ hipError_t launch_expert_fwd_fp8(const void* xd, const float* xd_scale, const vo
   b.lda = I; b.ldc = H; b.strideB = (int64_t)H * I; b.K = I; b.N = H; b.I = I;
   b.offsets = offsets; b.El = El; b.c0 = c0; b.nc = nc; b.P_c = P_c;
   return run_rows<256, 256, kDown, true>("gemm_down_fp8", b, s);
+}
+
+// FP8 weight gradients: dyd, h, dgu and xd quantised per column over each expert's rows and stored
+// transposed (expert_k layout), then dW1[e] = dgu_e^T xd_e and dW2[e] = dyd_e^T h_e on FP8 MFMA in one
+// launch.
+hipError_t launch_expert_wgrad_fp8(const void* dyd, const void* dgu, const void* xd, const void* h,
+                                   const int32_t* offsets, void* dyd_t, float* dyd_cs, void* dgu_t,
+                                   float* dgu_cs, void* xd_t, float* xd_cs, void* h_t, float* h_cs, void* dw1,
+                                   void* dw2, int H, int I, int El, int n, int64_t P_c, hipStream_t s,
+                                   bool quantize) {
+  if (El <= 0) return hipSuccess;
+  if (quantize) {
+    hipError_t e = launch_quantize_expert_cols_fp8("quantize_dyd_cols_fp8", dyd, dyd_t, dyd_cs, offsets, El, n, P_c, H, s);
+    if (e == hipSuccess) e = launch_quantize_expert_cols_fp8("quantize_h_cols_fp8", h, h_t, h_cs, offsets, El, n, P_c, I, s);
+    if (e == hipSuccess) e = launch_quantize_expert_cols_fp8("quantize_xd_cols_fp8", xd, xd_t, xd_cs, offsets, El, n, P_c, H, s);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = launch_quantize_expert_cols_fp8("quantize_dgu_cols_fp8", dgu, dgu_t, dgu_cs, offsets, El, n, P_c,
+                                                 2 * (int64_t)I, s);
+  if (e != hipSuccess) return e;
+  WgradFp8Args a{}, b{};
+  a.A = (const uint8_t*)dgu_t; a.B = (const uint8_t*)xd_t; a.sa = dgu_cs; a.sb = xd_cs; a.C = (uint16_t*)dw1;
+  a.strideC = (int64_t)2 * I * H; a.M = 2 * I; a.N = H; a.offsets = offsets; a.El = El; a.n_chunks = n;
+  b.A = (const uint8_t*)dyd_t; b.B = (const uint8_t*)h_t; b.sa = dyd_cs; b.sb = h_cs; b.C = (uint16_t*)dw2;
+  b.strideC = (int64_t)H * I; b.M = H; b.N = I; b.offsets = offsets; b.El = El; b.n_chunks = n;
+  const size_t lds = wgrad_lds_bytes<256, 256>();
+  auto k = wgrad_fp8_kernel<256, 256>;
+  e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const int64_t tiles = (int64_t)El * (((2 * I + 255) / 256) * ((H + 255) / 256) + ((H + 255) / 256) * ((I + 255) / 256));
+  const int64_t grid = persistent_grid(tiles);
+  if (grid <= 0) return hipSuccess;
+  {
+    MOE_TRACE("gemm_wgrad_fp8", s);
+    MOE_LAUNCH(k, dim3((unsigned)grid), dim3(kThreads), lds, s, a, b);
+  }
+  return hipGetLastError();
 }
 
 // FP8 input gradients: dyd quantised per row (FP32 steps of dispatch); dh = deq(dyd) deq(W2t)^T on

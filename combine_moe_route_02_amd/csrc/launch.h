@@ -56,6 +56,16 @@ hipError_t launch_quantize_segments_fp8(const char* name, const void* src, void*
                                         const int32_t* offsets, int El, int c0, int nc, int64_t P_c,
                                         int cols, hipStream_t s);
 // per-column e4m3 quantisation of batch x [rows, cols] BF16, codes stored transposed [batch, cols, rows]
+// per-expert, per-column e4m3 quantisation of dispatch rows, stored transposed and zero-padded (expert_k)
+hipError_t launch_quantize_expert_cols_fp8(const char* name, const void* src, void* codes, float* scale,
+                                           const int32_t* offsets, int El, int n_chunks, int64_t P_c, int64_t cols,
+                                           hipStream_t s);
+// FP8 expert weight gradients (dyd, h, xd quantised first unless `quantize` is false; dgu always)
+hipError_t launch_expert_wgrad_fp8(const void* dyd, const void* dgu, const void* xd, const void* h,
+                                   const int32_t* offsets, void* dyd_t, float* dyd_cs, void* dgu_t,
+                                   float* dgu_cs, void* xd_t, float* xd_cs, void* h_t, float* h_cs, void* dw1,
+                                   void* dw2, int H, int I, int El, int n, int64_t P_c, hipStream_t s,
+                                   bool quantize = true);
 hipError_t launch_quantize_cols_fp8(const void* src, void* codes_t, float* scale, int64_t batch, int64_t rows,
                                     int64_t cols, hipStream_t s);
 // FP8 input gradients of the expert FFN for chunks c0..c0+nc-1: dyd quantised per row, dh on FP8

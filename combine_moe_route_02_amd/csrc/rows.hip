@@ -626,6 +626,104 @@ hipError_t launch_quantize_cols_fp8(const void* src, void* codes_t, float* scale
   return hipGetLastError();
 }
 
+// Per-expert, per-column quantisation of dispatch rows for the FP8 weight gradients: expert e's rows
+// of every chunk (chunk order) are quantised per column (absmax over those rows, the FP32 steps of
+// dispatch) and stored transposed and zero-padded: codes[koff_e * C + c * Kp_e + k] (expert_k) and
+// scale[e * C + c]. One block per 64 columns of one expert, the column-quantiser scheme: the column
+// maxima through LDS, then 64-row tiles quantised, transposed in LDS and stored 16 bytes a thread.
+__global__ __launch_bounds__(256) void quantize_expert_cols_fp8_kernel(
+    const u32x4* __restrict__ src, uint8_t* __restrict__ codes, float* __restrict__ scale,
+    const int32_t* __restrict__ offsets, int El, int n_chunks, int64_t P_c, int64_t cols) {
+  __shared__ float red[32][kColTile];
+  __shared__ float s_inv[kColTile];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kColTile * kColPitch];
+  const int t = threadIdx.x, cv = t & 7, rg = t >> 3;
+  const int e = blockIdx.y;
+  const int64_t c0 = (int64_t)blockIdx.x * kColTile;
+  const int64_t nvec = cols / 8;
+  const bool cin = c0 + cv * 8 < cols;
+  int64_t koff;
+  int K;
+  expert_k(offsets, El, n_chunks, e, koff, K);
+  const int Kp = (K + 63) & ~63;
+  // dispatch row of the expert's k-th row
+  auto row_of_k = [&](int k) -> int64_t {
+    for (int c = 0; c < n_chunks; ++c) {
+      const int32_t* off = offsets + (int64_t)c * (El + 1);
+      const int len = off[e + 1] - off[e];
+      if (k < len) return (int64_t)c * P_c + off[e] + k;
+      k -= len;
+    }
+    return -1;
+  };
+  const u32x4* s = src + c0 / 8 + cv;
+  float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (cin)
+    for (int k = rg; k < K; k += 32) {
+      const u32x4 v = s[row_of_k(k) * nvec];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        m[2 * i] = fmaxf(m[2 * i], fabsf(bf2f(w[i] & 0xffff)));
+        m[2 * i + 1] = fmaxf(m[2 * i + 1], fabsf(bf2f(w[i] >> 16)));
+      }
+    }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[rg][cv * 8 + i] = m[i];
+  __syncthreads();
+  if (t < kColTile) {
+    float amax = 0.f;
+    for (int g = 0; g < 32; ++g) amax = fmaxf(amax, red[g][t]);
+    s_inv[t] = amax > 0.f ? 448.0f / amax : 0.f;
+    if (c0 + t < cols) scale[(int64_t)e * cols + c0 + t] = amax > 0.f ? amax / 448.0f : 1.0f;
+  }
+  __syncthreads();
+  float inv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) inv[i] = s_inv[cv * 8 + i];
+  const int oc = t >> 2, orow = (t & 3) * 16;
+  uint8_t* out = codes + koff * cols + (c0 + oc) * Kp;
+  for (int k0 = 0; k0 < Kp; k0 += kColTile) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int rl = rg + 32 * h;
+      if (!cin) continue;
+      uint32_t lo = 0, hi = 0;   // rows past K_e: zero codes
+      if (k0 + rl < K) {
+        const u32x4 v = s[row_of_k(k0 + rl) * nvec];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        float f[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { f[2 * i] = bf2f(w[i] & 0xffff); f[2 * i + 1] = bf2f(w[i] >> 16); }
+        lo = pack_fp8x4(clamp448(f[0] * inv[0]), clamp448(f[1] * inv[1]), clamp448(f[2] * inv[2]),
+                        clamp448(f[3] * inv[3]));
+        hi = pack_fp8x4(clamp448(f[4] * inv[4]), clamp448(f[5] * inv[5]), clamp448(f[6] * inv[6]),
+                        clamp448(f[7] * inv[7]));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        tile[(cv * 8 + i) * kColPitch + rl] = (uint8_t)(lo >> (8 * i));
+        tile[(cv * 8 + 4 + i) * kColPitch + rl] = (uint8_t)(hi >> (8 * i));
+      }
+    }
+    __syncthreads();
+    if (c0 + oc < cols) *(u32x4*)(out + k0 + orow) = *(const u32x4*)(tile + oc * kColPitch + orow);
+    __syncthreads();
+  }
+}
+
+hipError_t launch_quantize_expert_cols_fp8(const char* name, const void* src, void* codes, float* scale,
+                                           const int32_t* offsets, int El, int n_chunks, int64_t P_c, int64_t cols,
+                                           hipStream_t s) {
+  if (El <= 0 || cols <= 0) return hipSuccess;
+  {
+    MOE_TRACE(name, s);
+    MOE_LAUNCH(quantize_expert_cols_fp8_kernel, dim3((unsigned)((cols + kColTile - 1) / kColTile), (unsigned)El),
+               dim3(256), 0, s, (const u32x4*)src, (uint8_t*)codes, scale, offsets, El, n_chunks, P_c, cols);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_combine(bool bf16, const void* yd, const float* gates, const int32_t* row_of,
                           void* out, int64_t t0, int64_t t1, int K, int64_t row_bytes, hipStream_t s) {
   if (t1 <= t0) return hipSuccess;

@@ -89,8 +89,11 @@ typedef struct moe_desc {
 } moe_desc;
 
 /* Input gradients of the expert FFN on FP8 MFMA (moe_expert_dgrad_fp8) in the layer backward;
- * BF16 dtype only (MOE_ERR_UNSUPPORTED otherwise). Weight gradients stay BF16. */
+ * BF16 dtype only (MOE_ERR_UNSUPPORTED otherwise). */
 #define MOE_FLAG_FP8_DGRAD 1
+/* Expert weight gradients on FP8 MFMA (moe_expert_wgrad_fp8) in the layer backward; BF16 dtype
+ * only. Independent of MOE_FLAG_FP8_DGRAD. */
+#define MOE_FLAG_FP8_WGRAD 2
 
 /* ---------------------------------------------------------------------------------------
  * Stage calls
@@ -195,6 +198,21 @@ moe_status moe_expert_dgrad_fp8(const moe_desc* d, int chunk, const void* dyd, c
                                 float* dyd_scale, void* dgu, void* dgu_q, float* dgu_scale,
                                 void* dxd, void* stream);
 
+/* FP8 expert weight gradients (a reading: a weight gradient contracts over the expert's token rows,
+ * so its operands are scaled per column over those rows). For every local expert e, its dispatch
+ * rows of every chunk in chunk order are its K_e rows; dyd [P,H], h [P,I], dgu [P,2I] and xd [P,H]
+ * (BF16) are each quantised per column over those rows (absmax, the FP32 steps of moe_dispatch) and
+ * stored transposed, the rows contiguous and zero-padded to Kp_e = K_e rounded up to 64: with
+ * koff_e the sum of Kp over the experts before e, column j of expert e starts at byte
+ * koff_e * C + j * Kp_e of its *_t buffer (C its columns) and its scale is *_cs[e * C + j]. Then
+ * dW2[e] = s * sum_k dyd_t h_t and dW1[e] = s * sum_k dgu_t xd_t on FP8 MFMA with FP32 accumulation,
+ * dequantised by the two column scales, one BF16 store; an expert without rows gets zeros. Each
+ * *_t buffer holds C * (n_chunks * P_c + 64 * E_local) bytes (moe_workspace_bytes). */
+moe_status moe_expert_wgrad_fp8(const moe_desc* d, const void* dyd, const void* dgu, const void* xd,
+                                const void* h, const int32_t* offsets, void* dyd_t, float* dyd_cs,
+                                void* dgu_t, float* dgu_cs, void* xd_t, float* xd_cs, void* h_t,
+                                float* h_cs, void* dw1, void* dw2, void* stream);
+
 /* Dispatch backward: dx[t] = RNE( sum over local slots of dxd[row_of[t][j]]
  * + sum_j dlogits[t][idx[t][j]] * W_r[idx[t][j]] ) with FP32 accumulation (the second sum is
  * the router projection's input gradient; dlogits is zero off the selected experts). */
@@ -279,6 +297,8 @@ typedef struct moe_tensors {
    * backward payloads */
   const void* w1t; const float* w1t_scale; const void* w2t; const float* w2t_scale;
   void* dyd_q; float* dyd_scale; void* dgu_q; float* dgu_scale;
+  /* MOE_FLAG_FP8_WGRAD only (see moe_expert_wgrad_fp8): the per-expert transposed FP8 operands */
+  void* dyd_t; float* dyd_cs; void* dgu_t; float* dgu_cs; void* xd_t; float* xd_cs; void* h_t; float* h_cs;
 } moe_tensors;
 
 moe_status moe_layer_forward(const moe_desc* d, const moe_tensors* t, void* compute_stream,
@@ -303,6 +323,7 @@ typedef struct moe_workspace_sizes {
   int64_t dyd, dgates, dlogits, dwr_acc, dgu, dxd, dx, dw1, dw2, dwr;
   int64_t route_scratch, route_bwd_scratch, workspace; /* workspace = max of the scratches */
   int64_t w1t, w1t_scale, w2t, w2t_scale, dyd_q, dyd_scale, dgu_q, dgu_scale; /* MOE_FLAG_FP8_DGRAD */
+  int64_t dyd_t, dyd_cs, dgu_t, dgu_cs, xd_t, xd_cs, h_t, h_cs;              /* MOE_FLAG_FP8_WGRAD */
 } moe_workspace_sizes;
 moe_status moe_workspace_bytes(const moe_desc* d, moe_workspace_sizes* out);
 

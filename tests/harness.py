@@ -10,6 +10,8 @@ Runs the HIP library through its C ABI (via the ctypes binding) on seeded inputs
     bounds, with the absolute bound scaled by the tensor's magnitude because a BF16 half-ulp
     alone exceeds 2e-2 once |v| >= 8);
   * FP8 forward output: rel-L2 <= 2e-2 against the FP8 oracle;
+  * FP8 weight gradients (the FP8-wgrad flag): dW1 and dW2 rel-L2 <= 2e-2 against the oracle's
+    FP8 weight gradients;
   * FP8 input gradients (BF16 layer with the FP8-dgrad flag): dx and dW1 rel-L2 <= 2e-2 against
     the oracle's FP8-dgrad backward (the GPU's dgu is BF16 where the oracle keeps FP64, so an
     e4m3 code can fall on the other side of a rounding boundary), every other gradient at the BF16
@@ -149,11 +151,21 @@ def run_stages(mh, d, b, backward, s):
         mh.moe_combine_bwd(d, -1, b["dy"], b["yd"], b["gates"], b["row_of"], b["dyd"], b["dgates"], s)
         mh.moe_route_bwd(d, -1, b["dgates"], b["gates"], b["topk_idx"], b["x"], b["dlogits"], b["dwr_acc"],
                          b["dwr"], b["workspace"], s)
-        if d.flags & mh.FLAG_FP8_DGRAD:
-            mh.moe_expert_dgrad_fp8(d, -1, b["dyd"], b["gu"], b["w1t"], b["w1t_scale"], b["w2t"], b["w2t_scale"],
-                                    b["offsets"], b["dyd_q"], b["dyd_scale"], b["dgu"], b["dgu_q"], b["dgu_scale"],
-                                    b["dxd"], s)
-            mh.moe_expert_wgrad(d, b["dyd"], b["dgu"], b["xd"], b["h"], b["offsets"], b["dw1"], b["dw2"], s)
+        if d.flags:
+            if d.flags & mh.FLAG_FP8_DGRAD:
+                mh.moe_expert_dgrad_fp8(d, -1, b["dyd"], b["gu"], b["w1t"], b["w1t_scale"], b["w2t"],
+                                        b["w2t_scale"], b["offsets"], b["dyd_q"], b["dyd_scale"], b["dgu"],
+                                        b["dgu_q"], b["dgu_scale"], b["dxd"], s)
+            else:
+                for c in range(d.n_chunks):
+                    mh.moe_expert_ffn_bwd(d, c, b["dyd"], b["xd"], b["gu"], b["h"], b["w1"], b["w2"],
+                                          b["offsets"], b["dgu"], b["dxd"], None, None, s)
+            if d.flags & mh.FLAG_FP8_WGRAD:
+                mh.moe_expert_wgrad_fp8(d, b["dyd"], b["dgu"], b["xd"], b["h"], b["offsets"], b["dyd_t"],
+                                        b["dyd_cs"], b["dgu_t"], b["dgu_cs"], b["xd_t"], b["xd_cs"], b["h_t"],
+                                        b["h_cs"], b["dw1"], b["dw2"], s)
+            else:
+                mh.moe_expert_wgrad(d, b["dyd"], b["dgu"], b["xd"], b["h"], b["offsets"], b["dw1"], b["dw2"], s)
         else:
             mh.moe_expert_ffn_bwd(d, -1, b["dyd"], b["xd"], b["gu"], b["h"], b["w1"], b["w2"], b["offsets"],
                                   b["dgu"], b["dxd"], b["dw1"], b["dw2"], s)
@@ -172,8 +184,12 @@ def run_oracle(run: Run, backward: Optional[bool] = None):
     f = oracle.forward(inp["x"], inp["logits"], inp["w1"], inp["w2"], k=cfg.k, e0=cfg.e0,
                        E_local=cfg.E_local, n_chunks=cfg.n_chunks, P_c=run.desc.P_c)
     if backward:
-        bwd = ofp8.backward_fp8_dgrad if run.desc.flags & 1 else oracle.backward
-        f["bwd"] = bwd(f, inp["x"], inp["dy"], inp["w1"], inp["w2"], inp["w_r"])
+        fl = run.desc.flags
+        if fl:
+            f["bwd"] = ofp8.backward_fp8_dgrad(f, inp["x"], inp["dy"], inp["w1"], inp["w2"], inp["w_r"],
+                                               fp8_dgrad=bool(fl & 1), fp8_wgrad=bool(fl & 2))
+        else:
+            f["bwd"] = oracle.backward(f, inp["x"], inp["dy"], inp["w1"], inp["w2"], inp["w_r"])
     return f
 
 
@@ -230,9 +246,11 @@ def check_backward(run: Run, ref) -> Dict[str, float]:
     errs = {}
     errs["dgates"] = assert_close("dgates", to_np(b["dgates"]), bw["dgates"], dt)
     errs["dlogits"] = assert_close("dlogits", to_np(b["dlogits"]), bw["dlogits"], dt)
-    dq = "fp8" if run.desc.flags & 1 else dt    # FP8 input gradients
+    fl = run.desc.flags
+    dq = "fp8" if fl & 1 else dt    # FP8 input gradients
+    wq = "fp8" if fl & 2 else dt    # FP8 weight gradients
     errs["dx"] = assert_close("dx", to_np(b["dx"]), bw["dx"], dq)
-    errs["dw1"] = assert_close("dw1", to_np(b["dw1"]), bw["dw1"], dq)
-    errs["dw2"] = assert_close("dw2", to_np(b["dw2"]), bw["dw2"], dt)
+    errs["dw1"] = assert_close("dw1", to_np(b["dw1"]), bw["dw1"], "fp8" if fl else dt)
+    errs["dw2"] = assert_close("dw2", to_np(b["dw2"]), bw["dw2"], wq)
     errs["dwr"] = assert_close("dwr", to_np(b["dwr"]), bw["dwr"], dt)
     return errs

@@ -114,13 +114,28 @@ def test_fp8_dgrad_flag_validation_and_sizes():
     assert ws["w2t"] == 16 * 768 * 2048 and ws["w2t_scale"] == 16 * 768 * 4
     assert ws["dyd_q"] == P * 2048 and ws["dgu_q"] == P * 1536 and ws["dyd_scale"] == ws["dgu_scale"] == P * 4
     assert mh.workspace_bytes(mh.make_desc(T=16384, H=2048, I=768, E=128, E_local=16, k=8, n_chunks=2))["w1t"] == 0
-    bad = mh.make_desc(T=64, H=128, I=64, E=8, E_local=4, k=2, n_chunks=1, flags=2)
+    bad = mh.make_desc(T=64, H=128, I=64, E=8, E_local=4, k=2, n_chunks=1, flags=8)
     assert _status_of(mh.workspace_bytes, bad)[0] == -1
     f8 = mh.make_desc(T=64, H=128, I=64, E=8, E_local=4, k=2, n_chunks=1, dtype="fp8", flags=mh.FLAG_FP8_DGRAD)
     assert _status_of(mh.workspace_bytes, f8)[0] == -3
     # the stage call rejects a non-BF16 descriptor before touching any pointer
     f32 = mh.make_desc(T=64, H=128, I=64, E=8, E_local=4, k=2, n_chunks=1, dtype="f32")
     assert _status_of(mh.moe_expert_dgrad_fp8, f32, 0, *([1] * 13), 0)[0] == -3
+
+
+def test_fp8_wgrad_sizes():
+    _lib_or_skip()
+    d = mh.make_desc(T=16384, H=2048, I=768, E=128, E_local=16, k=8, n_chunks=2, dtype="bf16",
+                     flags=mh.FLAG_FP8_WGRAD | mh.FLAG_FP8_DGRAD)
+    ws = mh.workspace_bytes(d)
+    Kp = 2 * 65536 + 64 * 16
+    assert ws["dyd_t"] == ws["xd_t"] == 2048 * Kp and ws["h_t"] == 768 * Kp and ws["dgu_t"] == 1536 * Kp
+    assert ws["dyd_cs"] == ws["xd_cs"] == 16 * 2048 * 4 and ws["h_cs"] == 16 * 768 * 4 and ws["dgu_cs"] == 16 * 1536 * 4
+    assert ws["w1t"] > 0   # both flags at once
+    bad = mh.make_desc(T=64, H=128, I=64, E=8, E_local=4, k=2, n_chunks=1, flags=4)
+    assert _status_of(mh.workspace_bytes, bad)[0] == -1
+    f32 = mh.make_desc(T=64, H=128, I=64, E=8, E_local=4, k=2, n_chunks=1, dtype="f32")
+    assert _status_of(mh.moe_expert_wgrad_fp8, f32, *([1] * 15), 0)[0] == -3
 
 
 def test_quantize_cols_argument_errors():

@@ -1,4 +1,5 @@
-"""GPU parity of the FP8 input gradients (BF16 layer with MOE_FLAG_FP8_DGRAD) against the oracle.
+"""GPU parity of the FP8 backward (BF16 layer with MOE_FLAG_FP8_DGRAD and/or MOE_FLAG_FP8_WGRAD)
+against the oracle.
 
 * The transposed per-column weight quantisation: codes and scales bit for bit, on ragged shapes
   (row and column tails of the 64 x 64 transpose tiles), an all-zero column and a saturating one.
@@ -8,6 +9,9 @@
   two-stream configuration.
 * The chunk = -1 stage calls on one stream give the layer primitive's results bit for bit, including
   the e4m3 rows of dyd, which the layer writes inside combine backward.
+* FP8 weight gradients: the per-expert transposed xd operand bit for bit (codes, zero padding,
+  scales), and the layer's dW1, dW2 against the oracle's FP8 weight gradients, alone and with the
+  FP8 input gradients, small and at the one-rank share.
 """
 import numpy as np
 import pytest
@@ -111,3 +115,108 @@ def test_fp8_dgrad_full_16k():
     ref = harness.run_oracle(run)
     harness.check_forward(run, ref)
     print("[fb16k fp8 dgrad]", harness.check_backward(run, ref), flush=True)
+
+
+FP8DG_EDGE = [
+    # H above the combine-backward quantiser's limit: the layer quantises the stored dyd rows, and
+    # the row quantiser walks rows longer than its register tile
+    MoeConfig("fp8dg_h8256", T=200, H=8256, I=64, E=8, E_local=4, e0=1, k=2, n_chunks=2, dtype="bf16",
+              seed_base=540, backward=True),
+    # one local expert takes every routed row of a chunk region (k = 1)
+    MoeConfig("fp8dg_k1", T=333, H=192, I=128, E=4, E_local=1, e0=3, k=1, n_chunks=3, dtype="bf16",
+              seed_base=550, backward=True),
+    # no local expert: no dispatch row, nothing to quantise
+    MoeConfig("fp8dg_none_local", T=200, H=128, I=64, E=8, E_local=0, e0=8, k=2, n_chunks=2, dtype="bf16",
+              seed_base=560, backward=True),
+]
+
+
+@pytest.mark.parametrize("cfg", FP8DG_EDGE, ids=[c.name for c in FP8DG_EDGE])
+def test_fp8_dgrad_edge_shapes(cfg):
+    torch, mh = _require_gpu()
+    print(f"[parity] {cfg} fp8 dgrad", flush=True)
+    run = harness.run_gpu(cfg, sentinel=-3.0, flags=mh.FLAG_FP8_DGRAD)
+    _check_transposed_weights(run)
+    ref = harness.run_oracle(run)
+    harness.check_forward(run, ref, sentinel=-3.0)
+    print("[fp8 dgrad edge]", harness.check_backward(run, ref), flush=True)
+
+
+def test_fp8_dgrad_zero_tokens():
+    """T = 0 with FP8 input gradients: the layer returns OK, writes no output row and gives zero
+    weight gradients."""
+    torch, mh = _require_gpu()
+    d = mh.make_desc(T=0, H=128, I=64, E=8, E_local=4, k=2, n_chunks=2, flags=mh.FLAG_FP8_DGRAD)
+    b = mh.allocate(d, backward=True, fill=7)
+    for name, shape in (("x", (0, 128)), ("dy", (0, 128))):
+        b[name] = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    b["logits"] = torch.empty((0, 8), dtype=torch.float32, device="cuda")
+    b["w1"] = torch.zeros((4, 128, 128), dtype=torch.bfloat16, device="cuda")
+    b["w2"] = torch.zeros((4, 128, 64), dtype=torch.bfloat16, device="cuda")
+    b["w_r"] = torch.zeros((8, 128), dtype=torch.bfloat16, device="cuda")
+    b["out"] = torch.full((max(4, int(d.P_out)), 128), 5.0, dtype=torch.bfloat16, device="cuda")
+    mh.moe_quantize_cols_fp8(4, 128, 128, b["w1"], b["w1t"], b["w1t_scale"])
+    mh.moe_quantize_cols_fp8(4, 128, 64, b["w2"], b["w2t"], b["w2t_scale"])
+    mh.moe_layer_forward_backward(d, b, torch.cuda.current_stream(), torch.cuda.Stream())
+    torch.cuda.synchronize()
+    assert torch.all(b["out"] == 5.0)
+    assert torch.all(b["dw1"] == 0) and torch.all(b["dw2"] == 0) and torch.all(b["dwr"] == 0)
+    # all-zero weight columns: codes 0, scale 1
+    assert torch.all(b["w1t"] == 0) and torch.all(b["w1t_scale"] == 1.0)
+
+
+# ----------------------------------------------------------------------------- FP8 weight gradients
+
+def _check_xd_expert_codes(run, ref):
+    """The weight gradients' transposed xd operand: per expert, every column's codes over the
+    expert's rows of every chunk (then zero padding to a multiple of 64) and its scale, bit for bit."""
+    cfg, d = run.cfg, run.desc
+    offsets = run.bufs["offsets"].cpu().numpy()
+    codes = run.bufs["xd_t"].cpu().numpy()
+    scales = run.bufs["xd_cs"].cpu().numpy()
+    koff = 0
+    for e in range(cfg.E_local):
+        rows = ofp8.expert_rows(offsets, d.P_c, e)
+        K = rows.size
+        Kp = (K + 63) // 64 * 64
+        got = codes[koff * cfg.H: koff * cfg.H + cfg.H * Kp].reshape(cfg.H, Kp)
+        want_c, want_s = ofp8.quantize_cols_t(ofp8.bf16_round(np.asarray(ref["xd"])[rows]))
+        np.testing.assert_array_equal(got[:, :K], want_c, err_msg=f"expert {e}")
+        assert np.all(got[:, K:] == 0), f"expert {e}: padding"
+        np.testing.assert_array_equal(scales[e * cfg.H:(e + 1) * cfg.H].view(np.uint32), want_s.view(np.uint32))
+        koff += Kp
+
+
+@pytest.mark.parametrize("both", [False, True], ids=["wgrad", "dgrad+wgrad"])
+@pytest.mark.parametrize("cfg", FP8DG_SMALL, ids=[c.name for c in FP8DG_SMALL])
+def test_fp8_wgrad_layer_small(cfg, both):
+    torch, mh = _require_gpu()
+    flags = mh.FLAG_FP8_WGRAD | (mh.FLAG_FP8_DGRAD if both else 0)
+    print(f"[parity] {cfg} flags {flags}", flush=True)
+    run = harness.run_gpu(cfg, sentinel=-7.0, flags=flags)
+    ref = harness.run_oracle(run)
+    harness.check_forward(run, ref, sentinel=-7.0)
+    _check_xd_expert_codes(run, ref)
+    print("[fp8 wgrad]", harness.check_backward(run, ref), flush=True)
+
+
+@pytest.mark.parametrize("cfg", FP8DG_SMALL[:3], ids=[c.name for c in FP8DG_SMALL[:3]])
+def test_fp8_wgrad_stage_calls_match_layer(cfg):
+    torch, mh = _require_gpu()
+    flags = mh.FLAG_FP8_WGRAD | mh.FLAG_FP8_DGRAD
+    a = harness.run_gpu(cfg, layer=True, flags=flags)
+    b = harness.run_gpu(cfg, layer=False, two_streams=False, flags=flags)
+    for name in ("dx", "dw1", "dw2", "dwr"):
+        np.testing.assert_array_equal(harness.bits_np(a.bufs[name]), harness.bits_np(b.bufs[name]), err_msg=name)
+
+
+@pytest.mark.timeout(300)
+def test_fp8_dgrad_wgrad_full_16k():
+    """The one-rank share with FP8 input and weight gradients."""
+    torch, mh = _require_gpu()
+    cfg = moe_inputs.CONFIGS["fb16k"]
+    print(f"[parity] {cfg} fp8 dgrad + wgrad", flush=True)
+    run = harness.run_gpu(cfg, flags=mh.FLAG_FP8_DGRAD | mh.FLAG_FP8_WGRAD)
+    ref = harness.run_oracle(run)
+    harness.check_forward(run, ref)
+    print("[fb16k fp8 dgrad+wgrad]", harness.check_backward(run, ref), flush=True)
