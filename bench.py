@@ -340,7 +340,22 @@ def fp8_dgrad(args, cfg, bufs, mh, torch, np):
             r = flops[name] / (tot / args.steps * 1e-3) / 1e12
             e.update(achieved_tflops=round(r, 2), frac_mfma=round(r / PEAK_FP8_TFLOPS, 4))
         out["kernels"][name] = e
-    del bq
+    # FP8 input and weight gradients together (untraced)
+    dw = mh.make_desc(T=cfg.T, H=cfg.H, I=cfg.I, E=cfg.E, E_local=cfg.E_local, k=cfg.k, n_chunks=cfg.n_chunks,
+                      dtype="bf16", e0=cfg.e0, flags=mh.FLAG_FP8_DGRAD | mh.FLAG_FP8_WGRAD)
+    bw = mh.allocate(dw, backward=True)
+    for name in ("x", "logits", "w1", "w2", "w_r", "dy", "w1t", "w1t_scale", "w2t", "w2t_scale"):
+        bw[name] = bq[name]
+    for _ in range(args.warmup):
+        mh.moe_layer_forward_backward(dw, bw, cs, aux)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        mh.moe_layer_forward_backward(dw, bw, cs, aux)
+    torch.cuda.synchronize()
+    ms_w = (time.perf_counter() - t0) * 1e3 / args.steps
+    out["with_fp8_wgrad"] = {"tokens_per_s": round(cfg.T / (ms_w * 1e-3), 1), "ms_per_step_untraced": round(ms_w, 4)}
+    del bq, bw
     torch.cuda.empty_cache()
     return out
 

@@ -630,11 +630,22 @@ static moe_status backward_sched(const moe_desc* d, const moe_tensors* t, hipStr
   const bool two = cs != as;
   const hipStream_t side = two ? as : cs;
   hipEvent_t* ev = nullptr;
-  MOE_TRY(events(4 * n + 2, &ev));
-  // events [2n+1, 4n+2): distinct from the forward schedule's [0, 2n+1)
+  MOE_TRY(events(4 * n + 3, &ev));
+  // events [2n+1, 4n+3): distinct from the forward schedule's [0, 2n+1)
   hipEvent_t* cb = ev + 2 * n + 1;  // n events: combine backward of chunk c done
   hipEvent_t* dg = ev + 3 * n + 1;  // n events: expert dgrad of chunk c done
   hipEvent_t done = ev[4 * n + 1];
+  hipEvent_t wq_done = ev[4 * n + 2];  // FP8 weight gradients: dyd, h, xd operands quantised
+  // FP8 weight gradients: once every combine backward is issued, the auxiliary stream quantises
+  // the operands that do not wait for the input gradients, beside the dgrad GEMMs
+  const bool wq8 = (d->flags & MOE_FLAG_FP8_WGRAD) && rows_of(d) > 0;
+  auto wgrad_operands = [&]() -> moe_status {
+    MOE_HIP(moe::launch_wgrad_fp8_operands(t->dyd, t->xd, t->h, t->offsets, t->dyd_t, t->dyd_cs, t->xd_t, t->xd_cs,
+                                           t->h_t, t->h_cs, d->H, d->I, d->E_local, d->n_chunks, d->P_c, side),
+            "expert_wgrad_fp8");
+    if (two) MOE_HIP(hipEventRecord(wq_done, side), "hipEventRecord");
+    return MOE_OK;
+  };
   // FP8 input gradients: combine backward also writes the e4m3 rows of dyd (H up to
   // kCombineQMaxH; above it the expert dgrad quantises the stored rows)
   const bool q = d->flags & MOE_FLAG_FP8_DGRAD;
@@ -648,10 +659,12 @@ static moe_status backward_sched(const moe_desc* d, const moe_tensors* t, hipStr
     MOE_HIP(hipEventRecord(cb[0], cs), "hipEventRecord");
     MOE_HIP(hipStreamWaitEvent(as, cb[0], 0), "hipStreamWaitEvent");
   }
+  if (wq8 && n == 1) MOE_TRY(wgrad_operands());
   for (int c = 0; c < n; ++c) {
     if (c + 1 < n) {
       MOE_TRY(combine_bwd(c + 1, side));
       if (two) MOE_HIP(hipEventRecord(cb[c + 1], as), "hipEventRecord");
+      if (wq8 && c + 2 == n) MOE_TRY(wgrad_operands());
     }
     MOE_TRY(moe_route_bwd(d, c, t->dgates, t->gates, t->topk_idx, t->x, t->dlogits, t->dwr_acc, t->dwr,
                           t->workspace, side));
@@ -668,9 +681,11 @@ static moe_status backward_sched(const moe_desc* d, const moe_tensors* t, hipStr
     }
     MOE_TRY(moe_dispatch_bwd(d, c, t->dxd, t->row_of, t->topk_idx, t->dlogits, t->w_r, t->dx, side));
   }
-  if (d->flags & MOE_FLAG_FP8_WGRAD)
+  if (d->flags & MOE_FLAG_FP8_WGRAD) {
+    if (wq8 && two) MOE_HIP(hipStreamWaitEvent(cs, wq_done, 0), "hipStreamWaitEvent");
     MOE_TRY(expert_wgrad_fp8_impl(d, t->dyd, t->dgu, t->xd, t->h, t->offsets, t->dyd_t, t->dyd_cs, t->dgu_t,
-                                  t->dgu_cs, t->xd_t, t->xd_cs, t->h_t, t->h_cs, t->dw1, t->dw2, true, cs));
+                                  t->dgu_cs, t->xd_t, t->xd_cs, t->h_t, t->h_cs, t->dw1, t->dw2, !wq8, cs));
+  }
   else
     MOE_TRY(moe_expert_wgrad(d, t->dyd, t->dgu, t->xd, t->h, t->offsets, t->dw1, t->dw2, cs));
   if (two) {

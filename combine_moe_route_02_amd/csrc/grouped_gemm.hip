@@ -1067,6 +1067,16 @@ hipError_t launch_expert_fwd_fp8(const void* xd, const float* xd_scale, const vo
   return run_rows<256, 256, kDown, true>("gemm_down_fp8", b, s);
 }
 
+// The weight gradients' FP8 operands that do not wait for the input gradients: dyd, h and xd.
+hipError_t launch_wgrad_fp8_operands(const void* dyd, const void* xd, const void* h, const int32_t* offsets,
+                                     void* dyd_t, float* dyd_cs, void* xd_t, float* xd_cs, void* h_t, float* h_cs,
+                                     int H, int I, int El, int n, int64_t P_c, hipStream_t s) {
+  hipError_t e = launch_quantize_expert_cols_fp8("quantize_dyd_cols_fp8", dyd, dyd_t, dyd_cs, offsets, El, n, P_c, H, s);
+  if (e == hipSuccess) e = launch_quantize_expert_cols_fp8("quantize_h_cols_fp8", h, h_t, h_cs, offsets, El, n, P_c, I, s);
+  if (e == hipSuccess) e = launch_quantize_expert_cols_fp8("quantize_xd_cols_fp8", xd, xd_t, xd_cs, offsets, El, n, P_c, H, s);
+  return e;
+}
+
 // FP8 weight gradients: dyd, h, dgu and xd quantised per column over each expert's rows and stored
 // transposed (expert_k layout), then dW1[e] = dgu_e^T xd_e and dW2[e] = dyd_e^T h_e on FP8 MFMA in one
 // launch.
@@ -1077,9 +1087,8 @@ hipError_t launch_expert_wgrad_fp8(const void* dyd, const void* dgu, const void*
                                    bool quantize) {
   if (El <= 0) return hipSuccess;
   if (quantize) {
-    hipError_t e = launch_quantize_expert_cols_fp8("quantize_dyd_cols_fp8", dyd, dyd_t, dyd_cs, offsets, El, n, P_c, H, s);
-    if (e == hipSuccess) e = launch_quantize_expert_cols_fp8("quantize_h_cols_fp8", h, h_t, h_cs, offsets, El, n, P_c, I, s);
-    if (e == hipSuccess) e = launch_quantize_expert_cols_fp8("quantize_xd_cols_fp8", xd, xd_t, xd_cs, offsets, El, n, P_c, H, s);
+    hipError_t e = launch_wgrad_fp8_operands(dyd, xd, h, offsets, dyd_t, dyd_cs, xd_t, xd_cs, h_t, h_cs, H, I, El, n,
+                                             P_c, s);
     if (e != hipSuccess) return e;
   }
   hipError_t e = launch_quantize_expert_cols_fp8("quantize_dgu_cols_fp8", dgu, dgu_t, dgu_cs, offsets, El, n, P_c,

@@ -60,6 +60,10 @@ hipError_t launch_quantize_segments_fp8(const char* name, const void* src, void*
 hipError_t launch_quantize_expert_cols_fp8(const char* name, const void* src, void* codes, float* scale,
                                            const int32_t* offsets, int El, int n_chunks, int64_t P_c, int64_t cols,
                                            hipStream_t s);
+// the FP8 weight gradients' operands that do not depend on dgu (dyd, h, xd)
+hipError_t launch_wgrad_fp8_operands(const void* dyd, const void* xd, const void* h, const int32_t* offsets,
+                                     void* dyd_t, float* dyd_cs, void* xd_t, float* xd_cs, void* h_t, float* h_cs,
+                                     int H, int I, int El, int n, int64_t P_c, hipStream_t s);
 // FP8 expert weight gradients (dyd, h, xd quantised first unless `quantize` is false; dgu always)
 hipError_t launch_expert_wgrad_fp8(const void* dyd, const void* dgu, const void* xd, const void* h,
                                    const int32_t* offsets, void* dyd_t, float* dyd_cs, void* dgu_t,

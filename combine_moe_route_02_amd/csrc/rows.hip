@@ -629,14 +629,16 @@ hipError_t launch_quantize_cols_fp8(const void* src, void* codes_t, float* scale
 // Per-expert, per-column quantisation of dispatch rows for the FP8 weight gradients: expert e's rows
 // of every chunk (chunk order) are quantised per column (absmax over those rows, the FP32 steps of
 // dispatch) and stored transposed and zero-padded: codes[koff_e * C + c * Kp_e + k] (expert_k) and
-// scale[e * C + c]. One block per 64 columns of one expert, the column-quantiser scheme: the column
-// maxima through LDS, then 64-row tiles quantised, transposed in LDS and stored 16 bytes a thread.
-__global__ __launch_bounds__(256) void quantize_expert_cols_fp8_kernel(
+// scale[e * C + c]. One 1024-thread block per 64 columns of one expert (8 column vectors x 128 row
+// groups, so that enough rows are in flight): the column maxima through LDS, then 128-row tiles
+// quantised, transposed in LDS and stored 8 bytes a thread.
+constexpr int kEcThreads = 1024, kEcRG = kEcThreads / 8, kEcPitch = kEcRG + 16;
+__global__ __launch_bounds__(kEcThreads) void quantize_expert_cols_fp8_kernel(
     const u32x4* __restrict__ src, uint8_t* __restrict__ codes, float* __restrict__ scale,
     const int32_t* __restrict__ offsets, int El, int n_chunks, int64_t P_c, int64_t cols) {
-  __shared__ float red[32][kColTile];
+  __shared__ float red[kEcRG][kColTile + 1];
   __shared__ float s_inv[kColTile];
-  __shared__ __attribute__((aligned(16))) uint8_t tile[kColTile * kColPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kColTile * kEcPitch];
   const int t = threadIdx.x, cv = t & 7, rg = t >> 3;
   const int e = blockIdx.y;
   const int64_t c0 = (int64_t)blockIdx.x * kColTile;
@@ -658,8 +660,9 @@ __global__ __launch_bounds__(256) void quantize_expert_cols_fp8_kernel(
   };
   const u32x4* s = src + c0 / 8 + cv;
   float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (cin)
-    for (int k = rg; k < K; k += 32) {
+  if (cin) {
+#pragma unroll 4
+    for (int k = rg; k < K; k += kEcRG) {
       const u32x4 v = s[row_of_k(k) * nvec];
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -668,12 +671,13 @@ __global__ __launch_bounds__(256) void quantize_expert_cols_fp8_kernel(
         m[2 * i + 1] = fmaxf(m[2 * i + 1], fabsf(bf2f(w[i] >> 16)));
       }
     }
+  }
 #pragma unroll
   for (int i = 0; i < 8; ++i) red[rg][cv * 8 + i] = m[i];
   __syncthreads();
   if (t < kColTile) {
     float amax = 0.f;
-    for (int g = 0; g < 32; ++g) amax = fmaxf(amax, red[g][t]);
+    for (int g = 0; g < kEcRG; ++g) amax = fmaxf(amax, red[g][t]);
     s_inv[t] = amax > 0.f ? 448.0f / amax : 0.f;
     if (c0 + t < cols) scale[(int64_t)e * cols + c0 + t] = amax > 0.f ? amax / 448.0f : 1.0f;
   }
@@ -681,16 +685,13 @@ __global__ __launch_bounds__(256) void quantize_expert_cols_fp8_kernel(
   float inv[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) inv[i] = s_inv[cv * 8 + i];
-  const int oc = t >> 2, orow = (t & 3) * 16;
+  const int oc = t >> 4, orow = (t & 15) * 8;   // output: column oc, 8 rows from orow
   uint8_t* out = codes + koff * cols + (c0 + oc) * Kp;
-  for (int k0 = 0; k0 < Kp; k0 += kColTile) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int rl = rg + 32 * h;
-      if (!cin) continue;
+  for (int k0 = 0; k0 < Kp; k0 += kEcRG) {
+    if (cin) {
       uint32_t lo = 0, hi = 0;   // rows past K_e: zero codes
-      if (k0 + rl < K) {
-        const u32x4 v = s[row_of_k(k0 + rl) * nvec];
+      if (k0 + rg < K) {
+        const u32x4 v = s[row_of_k(k0 + rg) * nvec];
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
         float f[8];
 #pragma unroll
@@ -702,12 +703,12 @@ __global__ __launch_bounds__(256) void quantize_expert_cols_fp8_kernel(
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        tile[(cv * 8 + i) * kColPitch + rl] = (uint8_t)(lo >> (8 * i));
-        tile[(cv * 8 + 4 + i) * kColPitch + rl] = (uint8_t)(hi >> (8 * i));
+        tile[(cv * 8 + i) * kEcPitch + rg] = (uint8_t)(lo >> (8 * i));
+        tile[(cv * 8 + 4 + i) * kEcPitch + rg] = (uint8_t)(hi >> (8 * i));
       }
     }
     __syncthreads();
-    if (c0 + oc < cols) *(u32x4*)(out + k0 + orow) = *(const u32x4*)(tile + oc * kColPitch + orow);
+    if (c0 + oc < cols && k0 + orow < Kp) *(uint2*)(out + k0 + orow) = *(const uint2*)(tile + oc * kEcPitch + orow);
     __syncthreads();
   }
 }
@@ -719,7 +720,7 @@ hipError_t launch_quantize_expert_cols_fp8(const char* name, const void* src, vo
   {
     MOE_TRACE(name, s);
     MOE_LAUNCH(quantize_expert_cols_fp8_kernel, dim3((unsigned)((cols + kColTile - 1) / kColTile), (unsigned)El),
-               dim3(256), 0, s, (const u32x4*)src, (uint8_t*)codes, scale, offsets, El, n_chunks, P_c, cols);
+               dim3(kEcThreads), 0, s, (const u32x4*)src, (uint8_t*)codes, scale, offsets, El, n_chunks, P_c, cols);
   }
   return hipGetLastError();
 }
