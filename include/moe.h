@@ -278,6 +278,11 @@ moe_status moe_stash_load(const void* pool, const float* pool_scale, int64_t liv
  * per host thread and device on first use and keeps until the process ends, so layer calls
  * issued from different threads never share events. Calls that share `workspace` or any saved-
  * context buffer must still be ordered by the caller.
+ * With MOE_FLAG_FP8_DGRAD the backward runs moe_expert_dgrad_fp8 per chunk, and combine backward
+ * also writes the e4m3 rows of dyd (H <= 8192; above that the dgrad quantises the stored rows);
+ * t->w1t/w2t and their scales must hold the moe_quantize_cols_fp8 form of the current W1/W2. With
+ * MOE_FLAG_FP8_WGRAD the weight gradients are moe_expert_wgrad_fp8's, whose dyd, h and xd operands
+ * are quantised on `aux` once the last combine backward is issued.
  * ------------------------------------------------------------------------------------- */
 typedef struct moe_tensors {
   /* inputs */

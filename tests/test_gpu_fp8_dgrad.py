@@ -220,3 +220,84 @@ def test_fp8_dgrad_wgrad_full_16k():
     ref = harness.run_oracle(run)
     harness.check_forward(run, ref)
     print("[fb16k fp8 dgrad+wgrad]", harness.check_backward(run, ref), flush=True)
+
+
+@pytest.mark.parametrize("cfg", FP8DG_SMALL[:2], ids=[c.name for c in FP8DG_SMALL[:2]])
+def test_fp8_backward_launch_order_and_streams(cfg):
+    """The fused primitive with FP8 input and weight gradients: per chunk, combine backward with
+    the e4m3 dyd rows, the FP8 down dgrad, the dgu quantisation and the FP8 gate/up dgrad; the
+    weight-gradient operands that do not wait for dgu are quantised on the auxiliary stream after
+    the last combine backward; every chunk's input-gradient work is issued before the weight-
+    gradient GEMM; no BF16 dgrad or wgrad launch remains."""
+    torch, mh = _require_gpu()
+    n = cfg.n_chunks
+    mh.moe_trace_enable(False)
+    try:
+        harness.run_gpu(cfg, flags=mh.FLAG_FP8_DGRAD | mh.FLAG_FP8_WGRAD)
+    finally:
+        mh.moe_trace_disable()
+    log = mh.moe_trace_entries()
+    names = [nm for nm, _, _ in log]
+    counts = {k: names.count(k) for k in set(names)}
+    expect = {"combine_bwd_q": n, "combine_bwd": 0, "gemm_down_dgrad_swiglu_fp8": n, "quantize_dgu_fp8": n,
+              "gemm_gateup_dgrad_fp8": n, "quantize_dyd_fp8": 0, "quantize_dyd_cols_fp8": 1,
+              "quantize_h_cols_fp8": 1, "quantize_xd_cols_fp8": 1, "quantize_dgu_cols_fp8": 1,
+              "gemm_wgrad_fp8": 1, "dispatch_bwd": n, "gemm_down_dgrad_swiglu": 0,
+              "gemm_gateup_dgrad+down_dgrad_swiglu": 0, "gemm_gateup_dgrad+wgrad_w2": 0, "gemm_wgrad_w1": 0,
+              "gemm_wgrad": 0}
+    for k, v in expect.items():
+        assert counts.get(k, 0) == v, (k, counts.get(k, 0), v)
+    wg = names.index("gemm_wgrad_fp8")
+    for kind in ("combine_bwd_q", "gemm_down_dgrad_swiglu_fp8", "quantize_dgu_fp8", "gemm_gateup_dgrad_fp8",
+                 "dispatch_bwd", "quantize_dyd_cols_fp8", "quantize_h_cols_fp8", "quantize_xd_cols_fp8",
+                 "quantize_dgu_cols_fp8"):
+        assert max(i for i, nm in enumerate(names) if nm == kind) < wg, kind
+    last_cb = max(i for i, nm in enumerate(names) if nm == "combine_bwd_q")
+    assert names.index("quantize_dyd_cols_fp8") > last_cb
+
+    def streams_of(kind):
+        return [st for nm, st, _ in log if nm == kind]
+    compute = streams_of("gemm_gateup_swiglu")[0]
+    aux = streams_of("dispatch")[1]
+    assert aux != compute
+    for kind in ("gemm_down_dgrad_swiglu_fp8", "quantize_dgu_fp8", "gemm_gateup_dgrad_fp8",
+                 "quantize_dgu_cols_fp8", "gemm_wgrad_fp8"):
+        assert set(streams_of(kind)) == {compute}, kind
+    for kind in ("quantize_dyd_cols_fp8", "quantize_h_cols_fp8", "quantize_xd_cols_fp8", "dispatch_bwd"):
+        assert set(streams_of(kind)) == {aux}, kind
+    cbq = streams_of("combine_bwd_q")
+    assert cbq[0] == compute and set(cbq[1:]) <= {aux}
+
+
+def test_fp8_backward_under_hip_graph_capture():
+    """The fused primitive with FP8 input and weight gradients captured into a HIP graph (both
+    streams) replays to bitwise the eager results, three times, with eager work between replays."""
+    torch, mh = _require_gpu()
+    cfg = FP8DG_SMALL[0]
+    inp = moe_inputs.make_inputs(cfg, with_backward=True)
+    d = mh.make_desc(T=cfg.T, H=cfg.H, I=cfg.I, E=cfg.E, E_local=cfg.E_local, k=cfg.k, n_chunks=cfg.n_chunks,
+                     dtype=cfg.dtype, e0=cfg.e0, flags=mh.FLAG_FP8_DGRAD | mh.FLAG_FP8_WGRAD)
+    b = mh.allocate(d, backward=True)
+    for name in ("x", "w1", "w2", "w_r", "dy"):
+        b[name] = torch.from_numpy(inp[name + "_bits"].view(np.int16)).cuda().view(torch.bfloat16)
+    b["logits"] = torch.from_numpy(inp["logits"]).cuda()
+    mh.moe_quantize_cols_fp8(cfg.E_local, 2 * cfg.I, cfg.H, b["w1"], b["w1t"], b["w1t_scale"])
+    mh.moe_quantize_cols_fp8(cfg.E_local, cfg.H, cfg.I, b["w2"], b["w2t"], b["w2t_scale"])
+    cs, aux = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    mh.moe_layer_forward_backward(d, b, cs, aux)
+    torch.cuda.synchronize()
+    keys = ("dx", "dw1", "dw2", "dwr", "dlogits")
+    ref = {k: b[k].clone() for k in keys}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cs):
+        mh.moe_layer_forward_backward(d, b, cs, aux)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for k in keys:
+            b[k].fill_(-3)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in keys:
+            assert torch.equal(b[k], ref[k]), (rep, k)
