@@ -67,7 +67,7 @@ def _code_only(text: str) -> str:
 
 def source_sha(name: str) -> str:
     """Short hash of a kernel's source code (and the shared header), comments and whitespace
-    removed: counters taken on other code are not reported for this build."""
+    removed: counters taken on other code are not reported for the current code."""
     import hashlib
     csrc = os.path.join(ROOT, "combine_moe_route_02_amd", "csrc")
     h = hashlib.sha256()
@@ -376,7 +376,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the layer; --gpus {args.gpus} is not supported "
-              f"(this build has no multi-GPU path: run with --gpus 1)", file=sys.stderr)
+              f"(the library runs on one GPU: run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -120,16 +120,16 @@ def bf16_round(a: np.ndarray) -> np.ndarray:
 
 
 def ffn_bwd_fp8_dgrad(dyd, xd, gu, h, offsets, P_c, w1, w2):
-    """Expert FFN backward with FP8 input gradients (the survey's NEXT-1; the pages fix FP8 only
+    """Expert FFN backward with FP8 input gradients (the pages fix FP8 only
     for payloads, so these are readings):
       * dyd, the combine-backward payload, is stored in BF16 and quantised per row;
       * W2[e] and W1[e] are quantised per column and transposed (:func:`quantize_cols_t`);
       * dh = deq(dyd) deq(W2t[e])^T, then dG, dU as in ffn.ffn_bwd from the saved G, U;
       * dgu = [dG dU] is stored in BF16 and quantised per row; dxd = deq(dgu) deq(W1t[e])^T;
       * products accumulate exactly (FP64 here) and dequantise by s_row * s_col;
-      * the weight gradients stay BF16: dW2 = dyd^T h and dW1 = dgu^T xd from the unquantised
-        values (an FP8 weight gradient would need activation scales along the token dimension,
-        which per-row payload scales do not give).
+      * the weight gradients here are the BF16 ones, dW2 = dyd^T h and dW1 = dgu^T xd from the
+        unquantised values (per-row payload scales sit on the dimension they contract over; the
+        FP8 form with per-column scales is :func:`ffn_wgrad_fp8`).
     Returns dgu, dxd, dw1, dw2 (FP64)."""
     I = w1.shape[1] // 2
     P, H = xd.shape
@@ -173,7 +173,7 @@ def expert_rows(offsets, P_c, e):
 
 
 def ffn_wgrad_fp8(dyd, dgu, xd, h, offsets, P_c, El):
-    """Expert weight gradients on FP8 (the survey's NEXT-1; a reading, the pages give FP8 only for
+    """Expert weight gradients on FP8 (a reading: the pages give FP8 only for
     forward payloads). A weight gradient contracts over the expert's token rows, so its operands are
     scaled per column over those rows (every chunk's rows of the expert together): for each
     operand, the BF16-rounded rows of expert e are quantised per column (:func:`quantize_cols_t`,
