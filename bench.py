@@ -127,6 +127,92 @@ def pmc_summary(fetch_dir: str, write_dir: str, cmd: str) -> str:
     return "\n".join(out)
 
 
+# Counter passes for the GEMM engine: each pass stays within one rocprofv3 run's hardware limits
+# (at most 8 SQ, 4 TCC, 4 TCP, 2 TA and 2 GRBM counters).
+COUNTER_PASSES = {
+    "mfma": "GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F8 "
+            "SQ_INSTS_MFMA SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_WAIT_INST_ANY SQ_WAIT_ANY",
+    "lds": "GRBM_GUI_ACTIVE SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_LDS_ADDR_CONFLICT "
+           "SQ_WAIT_INST_LDS SQ_LDS_DATA_FIFO_FULL SQ_ACTIVE_INST_LDS",
+    "l2": "GRBM_GUI_ACTIVE TCC_HIT_sum TCC_MISS_sum TCC_EA0_RDREQ_sum TCC_REQ_sum TCP_TCC_READ_REQ_sum "
+          "TCP_PENDING_STALL_CYCLES_sum TA_TA_BUSY_sum TA_DATA_STALLED_BY_TC_CYCLES_sum SQ_INSTS_VMEM_RD "
+          "SQ_ACTIVE_INST_VMEM",
+}
+SIMDS, CUS = 1024, 256          # MI355X: 256 compute units of 4 SIMDs
+
+
+def counter_summary(dirs, cmd: str) -> str:
+    """Markdown summary of rocprofv3 --pmc runs (the COUNTER_PASSES): per kernel symbol the median
+    per dispatch of every counter, and the derived MFMA, wave-state, LDS and L2 figures.
+    GRBM_GUI_ACTIVE arrives summed over the 8 XCDs, so one XCD's active clocks are a eighth of it."""
+    import statistics
+    per, dur = {}, {}
+    for d in dirs:
+        for r in _counter_rows(d):
+            k = r["Kernel_Name"]
+            per.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                dur.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+    names = {sym: n for n, (_src, sym) in KERNEL_SYMBOLS.items()}
+    out = ["# Engine counters per kernel (rocprofv3 --pmc, medians per dispatch)", "",
+           "Commands (from the repository root, MI355X):", "", "```", cmd, "```", "",
+           "Counter runs serialise the dispatches, so every kernel here ran alone on the GPU. "
+           "`clk` = GRBM_GUI_ACTIVE / 8 XCDs / duration. `mfma busy` = SQ_VALU_MFMA_BUSY_CYCLES / "
+           "(clk cycles x 1024 SIMDs); `bf16 pk` = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 flop / duration / 2.5 "
+           "PFLOP/s (F8 MOPS against 5.0 PFLOP/s for FP8 kernels); `wait` = SQ_WAIT_ANY / SQ_WAVE_CYCLES "
+           "(share of wave time stalled in s_waitcnt); `issue` = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (waiting "
+           "for an instruction to issue); `lds issue` = SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES; `lds act` = "
+           "SQ_LDS_IDX_ACTIVE / (cycles x 256 CUs) (indexed LDS traffic only: direct-to-LDS loads are not "
+           "counted); `bank` = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; `L2 hit` = TCC_HIT / TCC_REQ-side "
+           "(HIT + MISS); `EA rd MB` = TCC_EA0_RDREQ_sum x 128 B; `TA busy` = TA_TA_BUSY_sum / (cycles x "
+           "256).", "",
+           "| kernel | n | us | clk GHz | mfma busy % | bf16 pk % | wait % | issue % | lds issue % | lds act % | "
+           "bank % | L2 hit % | EA rd MB | TA busy % |",
+           "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    raw = ["", "Raw medians per dispatch:", ""]
+
+    def med(c, key):
+        v = c.get(key)
+        return statistics.median(v) if v else None
+
+    def pct(a, b):
+        return f"{100.0 * a / b:.1f}" if a is not None and b else "—"
+    rows = []
+    for k, c in per.items():
+        if not any(s in k for s in ("gg::", "gemm::", "dispatch_bwd", "combine", "route")):
+            continue
+        us = statistics.median(dur[k]) if k in dur else None
+        gui = med(c, "GRBM_GUI_ACTIVE")
+        cyc = gui / 8.0 if gui else None
+        rows.append((k, us, cyc, c))
+    rows.sort(key=lambda r: -(r[1] or 0))
+    for (k, us, cyc, c) in rows:
+        label = next((n for sym, n in names.items() if sym in k), None)
+        name = f"`{label}`" if label else f"`{k.split('(')[0][:70]}`"
+        n = max(len(v) for v in c.values())
+        bf, f8 = med(c, "SQ_INSTS_VALU_MFMA_MOPS_BF16") or 0.0, med(c, "SQ_INSTS_VALU_MFMA_MOPS_F8") or 0.0
+        rate = (bf * 512 / 2.5e15 + f8 * 512 / 5.0e15) / (us * 1e-6) if us else None
+        wc = med(c, "SQ_WAVE_CYCLES")
+        la = med(c, "SQ_LDS_IDX_ACTIVE")
+        hit, miss = med(c, "TCC_HIT_sum"), med(c, "TCC_MISS_sum")
+        ea = med(c, "TCC_EA0_RDREQ_sum")
+        out.append(
+            f"| {name} | {n} | {us:.1f} | {cyc / us / 1e3:.2f} | "
+            f"{pct(med(c, 'SQ_VALU_MFMA_BUSY_CYCLES'), cyc * SIMDS if cyc else None)} | "
+            f"{(100 * rate if rate is not None else float('nan')):.1f} | "
+            f"{pct(med(c, 'SQ_WAIT_ANY'), wc)} | {pct(med(c, 'SQ_WAIT_INST_ANY'), wc)} | "
+            f"{pct(med(c, 'SQ_WAIT_INST_LDS'), wc)} | {pct(la, cyc * CUS if cyc else None)} | "
+            f"{pct(med(c, 'SQ_LDS_BANK_CONFLICT'), la)} | {pct(hit, (hit or 0) + (miss or 0))} | "
+            f"{(ea * 128 / 1e6) if ea is not None else float('nan'):.1f} | "
+            f"{pct(med(c, 'TA_TA_BUSY_sum'), cyc * CUS if cyc else None)} |")
+        if "gg::" in k or "gemm::" in k:
+            raw.append(f"- `{k.split('(')[0][:110]}` ({us:.1f} us): " +
+                       ", ".join(f"{ck}={statistics.median(v):.4g}" for ck, v in sorted(c.items())))
+    src = [f"Source hashes (code without comments): grouped_gemm.hip {source_sha('gemm_gateup_swiglu')}, "
+           f"gemm.hip {source_sha('gemm_router_wgrad')}, rows.hip {source_sha('dispatch')}.", ""]
+    return "\n".join(out[:7] + src + out[7:] + raw) + "\n"
+
+
 def committed_traffic(name: str):
     """Calibrated HBM bytes per launch for a kernel from profiles/*traffic*.md, or None when no
     summary was taken on this kernel's current source."""
@@ -370,9 +456,20 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COMMANDS"),
                     help="write the markdown traffic summary of two rocprofv3 --pmc runs and exit (no GPU)")
+    ap.add_argument("--counter-summary", nargs="+", metavar="DIR_OR_COMMANDS",
+                    help="counter directories of the COUNTER_PASSES runs, then the commands text: write the "
+                         "markdown engine-counter summary and exit (no GPU)")
+    ap.add_argument("--counter-pass", choices=sorted(COUNTER_PASSES),
+                    help="print the counters of one COUNTER_PASSES entry (for rocprofv3 --pmc) and exit")
     args = ap.parse_args()
     if args.pmc_summary:
         print(pmc_summary(*args.pmc_summary))
+        return
+    if args.counter_summary:
+        print(counter_summary(args.counter_summary[:-1], args.counter_summary[-1]))
+        return
+    if args.counter_pass:
+        print(COUNTER_PASSES[args.counter_pass])
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the layer; --gpus {args.gpus} is not supported "

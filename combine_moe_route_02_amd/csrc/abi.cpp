@@ -50,6 +50,7 @@ int64_t min_pc(const moe_desc* d) {
   return tokens_per_chunk(d) * kk;
 }
 int elem_size(int dtype) { return dtype == MOE_F32 ? 4 : 2; }  // payload rows (FP8: BF16 x/yd)
+constexpr int64_t kRsrcMax = 0x7fffffff;  // bytes one raw buffer descriptor addresses
 
 moe_status validate(const moe_desc* d) {
   if (!d) return fail(MOE_ERR_ARG, "descriptor is NULL");
@@ -82,6 +83,33 @@ moe_status validate(const moe_desc* d) {
   if (d->P_out < d->T) return fail(MOE_ERR_CAPACITY, "P_out = %lld below T = %lld", (long long)d->P_out, (long long)d->T);
   if ((int64_t)d->n_chunks * d->P_c > INT32_MAX || d->T * d->k > INT32_MAX)
     return fail(MOE_ERR_UNSUPPORTED, "row indices exceed int32");
+  // the expert GEMMs address one expert's weights through a buffer descriptor
+  const int64_t wes = d->dtype == MOE_F32 ? 4 : 2;
+  if (2 * (int64_t)d->I * d->H * wes > kRsrcMax)
+    return fail(MOE_ERR_UNSUPPORTED, "one expert's W1 (2I x H = %lld elements) exceeds a 2 GiB buffer descriptor",
+                (long long)(2 * (int64_t)d->I * d->H));
+  return MOE_OK;
+}
+
+// Extents that the backward kernels address through one buffer descriptor (at most 2^31 - 1
+// bytes; loads past a descriptor's extent would read zeros): a weight-gradient operand segment
+// (one expert's rows of one chunk, at most P_c rows of max(H, 2I) BF16 values), the router
+// weight gradient's operands of one chunk (ceil(T/n) rows of x and of FP32 dlogits) and, with
+// FP8 weight gradients, one expert's transposed operand (max(H, 2I) rows of its padded rows of
+// every chunk, at most n P_c + 64, FP8 codes).
+moe_status bwd_extent(const moe_desc* d) {
+  const int64_t es = d->dtype == MOE_F32 ? 4 : 2;
+  const int64_t wide = d->H > 2 * (int64_t)d->I ? d->H : 2 * (int64_t)d->I;
+  if (d->E_local > 0 && d->P_c * wide * es > kRsrcMax)
+    return fail(MOE_ERR_UNSUPPORTED, "weight gradients: P_c x max(H, 2I) = %lld elements exceed a 2 GiB buffer descriptor",
+                (long long)(d->P_c * wide));
+  const int64_t tc = tokens_per_chunk(d);
+  if (tc * d->H * es > kRsrcMax || tc * (int64_t)d->E * 4 > kRsrcMax)
+    return fail(MOE_ERR_UNSUPPORTED, "router weight gradient: a chunk's %lld tokens exceed a 2 GiB buffer descriptor",
+                (long long)tc);
+  if ((d->flags & MOE_FLAG_FP8_WGRAD) && d->E_local > 0 && wide * ((int64_t)d->n_chunks * d->P_c + 64) > kRsrcMax)
+    return fail(MOE_ERR_UNSUPPORTED, "FP8 weight gradients: max(H, 2I) x (n_chunks P_c + 64) = %lld bytes exceed a 2 GiB buffer descriptor",
+                (long long)(wide * ((int64_t)d->n_chunks * d->P_c + 64)));
   return MOE_OK;
 }
 
@@ -217,7 +245,7 @@ moe_status moe_route(const moe_desc* d, int chunk, const float* logits, int32_t*
   MOE_TRY(validate(d));
   MOE_TRY(check_chunk(d, chunk));
   if (d->T > 0) { MOE_NEED(logits); MOE_NEED(topk_idx); MOE_NEED(gates); MOE_NEED(row_of); }
-  if (rows_of(d) > 0) MOE_NEED(src_token);
+  if ((int64_t)d->n_chunks * d->P_c > 0) MOE_NEED(src_token);  // rows past N_c are marked -1
   MOE_NEED(counts); MOE_NEED(offsets); MOE_NEED(workspace);
   Range r = range_of(d, chunk);
   MOE_HIP(moe::launch_route(logits, topk_idx, gates, counts, offsets, row_of, src_token,
@@ -236,7 +264,7 @@ moe_status moe_route_x(const moe_desc* d, int chunk, const void* x, const void* 
   if (d->E % 32 || d->E > 256)
     return fail(MOE_ERR_UNSUPPORTED, "moe_route_x: E = %d must be a multiple of 32, at most 256", d->E);
   if (d->T > 0) { MOE_NEED(x); MOE_NEED(w_r); MOE_NEED(topk_idx); MOE_NEED(gates); MOE_NEED(row_of); }
-  if (rows_of(d) > 0) MOE_NEED(src_token);
+  if ((int64_t)d->n_chunks * d->P_c > 0) MOE_NEED(src_token);  // rows past N_c are marked -1
   MOE_NEED(counts); MOE_NEED(offsets); MOE_NEED(workspace);
   Range r = range_of(d, chunk);
   MOE_HIP(moe::launch_route_x(x, w_r, logits, topk_idx, gates, counts, offsets, row_of, src_token,
@@ -333,6 +361,7 @@ moe_status moe_route_bwd(const moe_desc* d, int chunk, const float* dgates, cons
                          void* workspace, void* stream) {
   MOE_TRY(validate(d));
   MOE_TRY(no_fp8_bwd(d));
+  MOE_TRY(bwd_extent(d));
   MOE_TRY(check_chunk(d, chunk));
   MOE_NEED(dwr_acc); MOE_NEED(workspace);
   if (d->T > 0) { MOE_NEED(dgates); MOE_NEED(gates); MOE_NEED(topk_idx); MOE_NEED(x); MOE_NEED(dlogits); }
@@ -353,6 +382,7 @@ moe_status moe_expert_wgrad(const moe_desc* d, const void* dyd, const void* dgu,
                             const int32_t* offsets, void* dw1, void* dw2, void* stream) {
   MOE_TRY(validate(d));
   MOE_TRY(no_fp8_bwd(d));
+  MOE_TRY(bwd_extent(d));
   if (d->E_local == 0) return MOE_OK;
   MOE_NEED(offsets); MOE_NEED(dw1); MOE_NEED(dw2);
   if (rows_of(d) > 0) { MOE_NEED(dyd); MOE_NEED(dgu); MOE_NEED(xd); MOE_NEED(h); }
@@ -367,6 +397,7 @@ moe_status moe_expert_ffn_bwd(const moe_desc* d, int chunk, const void* dyd, con
   MOE_TRY(validate(d));
   MOE_TRY(no_fp8_bwd(d));
   MOE_TRY(check_chunk(d, chunk));
+  if (chunk < 0) MOE_TRY(bwd_extent(d));  // the weight gradients follow the input gradients
   if (d->E_local == 0) return MOE_OK;
   Range r = range_of(d, chunk);
   if (rows_of(d) == 0) return chunk < 0 ? moe_expert_wgrad(d, dyd, dgu, xd, h, offsets, dw1, dw2, stream) : MOE_OK;
@@ -410,6 +441,11 @@ static moe_status expert_wgrad_fp8_impl(const moe_desc* d, const void* dyd, cons
                                         void* dgu_t, float* dgu_cs, void* xd_t, float* xd_cs, void* h_t,
                                         float* h_cs, void* dw1, void* dw2, bool quantize, void* stream) {
   MOE_TRY(validate(d));
+  {
+    moe_desc f = *d;
+    f.flags |= MOE_FLAG_FP8_WGRAD;
+    MOE_TRY(bwd_extent(&f));
+  }
   if (d->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "FP8 weight gradients need the BF16 dtype");
   if (d->E_local == 0) return MOE_OK;
   MOE_NEED(offsets); MOE_NEED(dw1); MOE_NEED(dw2);
@@ -527,8 +563,9 @@ static moe_status check_fwd_tensors(const moe_desc* d, const moe_tensors* t) {
       return fail(MOE_ERR_ARG, "layer: logits and w_r are both NULL (one of them routes the tokens)");
     MOE_NEED(t->out);
   }
+  if ((int64_t)d->n_chunks * d->P_c > 0) MOE_NEED(t->src_token);  // rows past N_c are marked -1
   if (rows_of(d) > 0) {
-    MOE_NEED(t->w1); MOE_NEED(t->w2); MOE_NEED(t->src_token); MOE_NEED(t->xd); MOE_NEED(t->h); MOE_NEED(t->yd);
+    MOE_NEED(t->w1); MOE_NEED(t->w2); MOE_NEED(t->xd); MOE_NEED(t->h); MOE_NEED(t->yd);
     if (d->dtype == MOE_FP8_E4M3) { MOE_NEED(t->xd_scale); MOE_NEED(t->h_scale); MOE_NEED(t->w1_scale); MOE_NEED(t->w2_scale); }
   }
   return MOE_OK;
@@ -536,6 +573,7 @@ static moe_status check_fwd_tensors(const moe_desc* d, const moe_tensors* t) {
 
 static moe_status check_bwd_tensors(const moe_desc* d, const moe_tensors* t) {
   MOE_TRY(no_fp8_bwd(d));
+  MOE_TRY(bwd_extent(d));
   MOE_NEED(t->w_r); MOE_NEED(t->dwr_acc); MOE_NEED(t->dwr);
   if (d->T > 0) { MOE_NEED(t->dy); MOE_NEED(t->dgates); MOE_NEED(t->dlogits); MOE_NEED(t->dx); }
   if (rows_of(d) > 0) {

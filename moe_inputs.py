@@ -10,7 +10,8 @@ Recipe (every tensor):
   * rounded once, round-to-nearest-even, to BF16 when the payload is BF16 or
     FP8 (FP8 quantisation belongs to the method and is done by each side);
   * router logits always stay FP32.
-Tensor ids: x=1, logits=2, W1=3, W2=4, W_r=5, dy=6, Zipf popularity ranks=7.
+Tensor ids: x=1, logits=2, W1=3, W2=4, W_r=5, dy=6, Zipf popularity ranks=7, upstream
+gate gradients for the route-backward stage alone=8, tie-heavy logits=9.
 
 Workloads follow the token-wise ChunkedEP single-layer setting (Megatron-LM
 PR 7342, "Historical single-layer OP measurements": EP8, top-k 8, two token
@@ -23,7 +24,8 @@ from typing import Dict, Optional
 
 import numpy as np
 
-TENSOR_IDS = {"x": 1, "logits": 2, "w1": 3, "w2": 4, "w_r": 5, "dy": 6, "zipf": 7}
+TENSOR_IDS = {"x": 1, "logits": 2, "w1": 3, "w2": 4, "w_r": 5, "dy": 6, "zipf": 7, "dgates": 8,
+              "tie_logits": 9}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -142,3 +144,37 @@ def make_inputs(cfg: MoeConfig, with_backward: Optional[bool] = None,
         if p["bits"] is not None:
             out[name + "_bits"] = p["bits"]
     return out
+
+
+def make_dgates(cfg: MoeConfig) -> np.ndarray:
+    """Upstream gate gradients [T, k] ~ N(0, 1) in FP32, for running the route backward on its own."""
+    return _normal(cfg, "dgates", (cfg.T, cfg.k), 1.0)
+
+
+def make_tie_logits(cfg: MoeConfig, nan_frac: float = 0.02) -> np.ndarray:
+    """Router logits [T, E] in FP32 with many exact ties: N(0, 1) rounded to multiples of 0.5, so
+    that equal values, including the k-th and (k+1)-th largest of a row, are common. Zeros come
+    with both signs (rounding keeps the sign of small negative draws, and half of the remaining
+    zeros are negated), and a fraction ``nan_frac`` of the entries are NaN (at most
+    E - k per row, so every row keeps k non-NaN entries). Row 0 is all zeros of mixed sign, row 1
+    holds k - 1 finite values with -inf and NaN elsewhere (when T > 1)."""
+    rng = np.random.default_rng(cfg.seed_base + TENSOR_IDS["tie_logits"])
+    T, E, k = cfg.T, cfg.E, cfg.k
+    lg = np.round(rng.standard_normal((T, E), dtype=np.float32) * np.float32(2.0)) * np.float32(0.5)
+    zeros = lg == 0
+    flip = rng.random((T, E)) < 0.5
+    lg[zeros & flip] = np.float32(-0.0)
+    if nan_frac > 0 and E > k:
+        cand = rng.random((T, E)) < nan_frac
+        # keep at most E - k NaNs per row
+        over = np.cumsum(cand, axis=1) > (E - k)
+        lg[cand & ~over] = np.float32(np.nan)
+    if T > 0:
+        lg[0] = np.where(rng.random(E) < 0.5, np.float32(0.0), np.float32(-0.0))
+    if T > 1 and k >= 2:
+        row = np.full(E, -np.inf, dtype=np.float32)
+        row[rng.random(E) < 0.5] = np.float32(np.nan)
+        pos = rng.choice(E, size=k - 1, replace=False)
+        row[pos] = np.float32(1.0) + np.arange(k - 1, dtype=np.float32)
+        lg[1] = row
+    return lg.astype(np.float32)

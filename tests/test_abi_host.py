@@ -202,3 +202,84 @@ def test_trace_enable_only_host_side():
     mh.moe_trace_enable_only("gemm_wgrad_w1")
     assert L.moe_trace_count() == 0
     mh.moe_trace_disable()
+
+
+def test_src_token_required_without_local_experts():
+    """With no local expert but a non-empty dispatch region (P_c > 0), routing still marks every
+    row of the region with -1, so a NULL src_token is rejected before any launch."""
+    _lib_or_skip()
+    d = _desc(E_local=0, e0=8, P_c=8, P_out=1000)
+    st, msg = _status_of(mh.moe_route, d, 0, 1, 1, 1, 1, 1, 1, None, 1, 0)
+    assert st == -1 and "src_token" in msg, msg
+    st, msg = _status_of(mh.moe_route_x, _desc(E=32, E_local=0, e0=8, P_c=8, P_out=1000), 0, *([1] * 8), None, 1, 0)
+    assert st == -1 and "src_token" in msg, msg
+    bufs = {f: 1 for f in mh.TENSOR_FIELDS}
+    bufs["src_token"] = None
+    st, msg = _status_of(mh.moe_layer_forward, d, bufs, 0, 0)
+    assert st == -1 and "src_token" in msg, msg
+
+
+def test_extents_past_a_buffer_descriptor_are_rejected():
+    """A kernel operand addressed through one buffer descriptor holds at most 2^31 - 1 bytes: the
+    backward calls reject shapes whose static worst case exceeds it (MOE_ERR_UNSUPPORTED) before
+    any launch, instead of reading zeros past the descriptor's extent."""
+    _lib_or_skip()
+    # weight-gradient segment: P_c x H x 2 = 262144 x 7168 x 2 bytes
+    big = mh.make_desc(T=65536, H=7168, I=768, E=128, E_local=16, k=8, n_chunks=2)
+    assert big.P_c * 7168 * 2 > 2**31 - 1
+    mh.workspace_bytes(big)                       # the descriptor itself is valid
+    st, msg = _status_of(mh.moe_expert_wgrad, big, *([1] * 7), 0)
+    assert st == -3 and "buffer descriptor" in msg, msg
+    st, _ = _status_of(mh.moe_route_bwd, big, -1, *([1] * 8), 0)
+    assert st == -3
+    st, _ = _status_of(mh.moe_expert_ffn_bwd, big, -1, *([1] * 11), 0)
+    assert st == -3
+    bufs = {f: 1 for f in mh.TENSOR_FIELDS}
+    assert _status_of(mh.moe_layer_forward_backward, big, bufs, 0, 0)[0] == -3
+    assert _status_of(mh.moe_layer_backward, big, bufs, 0, 0)[0] == -3
+    # FP8 weight-gradient operand: max(H, 2I) x (n P_c + 64) codes, with the BF16 segment in range
+    f8 = mh.make_desc(T=200000, H=2048, I=768, E=128, E_local=16, k=8, n_chunks=4,
+                      flags=mh.FLAG_FP8_WGRAD | mh.FLAG_FP8_DGRAD)
+    assert f8.P_c * 2048 * 2 <= 2**31 - 1 < 2048 * (4 * f8.P_c + 64)
+    assert _status_of(mh.moe_layer_backward, f8, bufs, 0, 0)[0] == -3
+    plain = mh.make_desc(T=200000, H=2048, I=768, E=128, E_local=16, k=8, n_chunks=4)
+    assert _status_of(mh.moe_expert_wgrad_fp8, plain, *([1] * 15), 0)[0] == -3
+    # an expert's W1 past one descriptor
+    assert _status_of(mh.workspace_bytes, mh.make_desc(T=64, H=65536, I=16384, E=8, E_local=4, k=2,
+                                                       n_chunks=1))[0] == -3
+
+
+def test_host_helpers_do_not_initialise_hip():
+    """The host-only helpers (extents, workspace sizes, the live-extent tracker, argument
+    validation) never initialise the HIP runtime: a fresh process that calls them opens no GPU
+    device file (/dev/kfd, /dev/dri/*) and the runtime reports no initialisation."""
+    import subprocess
+    import sys
+    _lib_or_skip()
+    code = r'''
+import os, sys
+sys.path.insert(0, sys.argv[1])
+import combine_moe_route_02_amd as mh
+d = mh.make_desc(T=16384, H=2048, I=768, E=128, E_local=16, k=8, n_chunks=2)
+mh.workspace_bytes(d)
+mh.required_extent(16384, 8, 16, 2)
+tr = mh.ExtentTracker(); h = tr.acquire(262144); tr.current(131072); tr.release(h)
+try:
+    mh.moe_route(mh.make_desc(T=10, H=100, I=64, E=8, E_local=4, k=2, n_chunks=1), 0, *([None] * 8), 0)
+except mh.MoeError:
+    pass
+mh.moe_trace_enable_only("x"); mh.moe_trace_disable()
+fds = []
+for f in os.listdir("/proc/self/fd"):
+    try:
+        fds.append(os.readlink("/proc/self/fd/" + f))
+    except OSError:
+        pass
+bad = [p for p in fds if p.startswith("/dev/kfd") or p.startswith("/dev/dri")]
+maps = open("/proc/self/maps").read()
+print("OPEN_GPU_FILES", bad, "KFD_MAPPED", "/dev/kfd" in maps)
+'''
+    r = subprocess.run([sys.executable, "-c", code, ROOT], capture_output=True, text=True, timeout=120,
+                       env={k: v for k, v in os.environ.items() if k != "HIP_VISIBLE_DEVICES"})
+    assert r.returncode == 0, r.stderr
+    assert "OPEN_GPU_FILES [] KFD_MAPPED False" in r.stdout, r.stdout
