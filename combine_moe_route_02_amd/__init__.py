@@ -68,6 +68,7 @@ _LIB = None
 _SIGS = {
     "moe_route": [POINTER(MoeDesc), c_int] + [c_void_p] * 9,
     "moe_route_x": [POINTER(MoeDesc), c_int] + [c_void_p] * 11,
+    "moe_route_noalloc": [POINTER(MoeDesc), c_int] + [c_void_p] * 8,
     "moe_dispatch": [POINTER(MoeDesc), c_int] + [c_void_p] * 6,
     "moe_expert_ffn": [POINTER(MoeDesc), c_int] + [c_void_p] * 12,
     "moe_combine": [POINTER(MoeDesc), c_int] + [c_void_p] * 5,
@@ -165,6 +166,12 @@ def moe_route(d, chunk, logits, topk_idx, gates, counts, offsets, row_of, src_to
     _check(lib().moe_route(ctypes.byref(d), chunk, _ptr(logits), _ptr(topk_idx), _ptr(gates), _ptr(counts),
                            _ptr(offsets), _ptr(row_of), _ptr(src_token), _ptr(workspace), _stream(stream)),
            "moe_route")
+
+
+def moe_route_noalloc(d, chunk, logits, topk_idx, gates, counts, offsets, row_of, src_token, stream=None):
+    _check(lib().moe_route_noalloc(ctypes.byref(d), chunk, _ptr(logits), _ptr(topk_idx), _ptr(gates), _ptr(counts),
+                                   _ptr(offsets), _ptr(row_of), _ptr(src_token), _stream(stream)),
+           "moe_route_noalloc")
 
 
 def moe_route_x(d, chunk, x, w_r, logits, topk_idx, gates, counts, offsets, row_of, src_token, workspace,

@@ -255,6 +255,28 @@ moe_status moe_route(const moe_desc* d, int chunk, const float* logits, int32_t*
   return MOE_OK;
 }
 
+moe_status moe_route_noalloc(const moe_desc* d, int chunk, const float* logits, int32_t* topk_idx, float* gates,
+                             int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* src_token, void* stream) {
+  MOE_TRY(validate(d));
+  MOE_TRY(check_chunk(d, chunk));
+  if (d->T > 0) { MOE_NEED(logits); MOE_NEED(topk_idx); MOE_NEED(gates); MOE_NEED(row_of); }
+  if ((int64_t)d->n_chunks * d->P_c > 0) MOE_NEED(src_token);
+  MOE_NEED(counts); MOE_NEED(offsets);
+  const int64_t need = moe::route_scratch_bytes(d->T, d->n_chunks, d->E);
+  if (need > moe::kNoAllocRouteScratchBytes)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "moe_route_noalloc: the routing histograms need %lld bytes, above its fixed %lld-byte device "
+                "scratch (n_chunks * ceil(ceil(T/n_chunks)/64) * 4 * E * 4 bytes); use moe_route with a workspace",
+                (long long)need, (long long)moe::kNoAllocRouteScratchBytes);
+  void* ws = nullptr;
+  MOE_HIP(moe::route_noalloc_scratch(&ws), "moe_route_noalloc: hipGetSymbolAddress");
+  Range r = range_of(d, chunk);
+  MOE_HIP(moe::launch_route(logits, topk_idx, gates, counts, offsets, row_of, src_token, (int32_t*)ws, d->T, d->E,
+                            d->e0, d->E_local, d->k, d->n_chunks, r.c0, r.nc, d->P_c, (hipStream_t)stream),
+          "route");
+  return MOE_OK;
+}
+
 moe_status moe_route_x(const moe_desc* d, int chunk, const void* x, const void* w_r, float* logits,
                        int32_t* topk_idx, float* gates, int32_t* counts, int32_t* offsets, int32_t* row_of,
                        int32_t* src_token, void* workspace, void* stream) {

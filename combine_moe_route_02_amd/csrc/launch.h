@@ -10,6 +10,10 @@ namespace moe {
 // routing
 int route_blocks_per_chunk(int64_t T, int n);
 int64_t route_scratch_bytes(int64_t T, int n, int E);
+// the allocation-free routing variant's scratch: a file-scope device array of this many bytes per
+// GPU; route_noalloc_scratch gives its address on the current device
+constexpr int64_t kNoAllocRouteScratchBytes = 4 << 20;
+hipError_t route_noalloc_scratch(void** out);
 // routing from x: logits = x . W_r^T (BF16 MFMA, FP32 accumulation) fused with the top-k, then
 // the layout kernel; logits may be NULL. Needs E % 32 == 0, E <= 256.
 hipError_t launch_route_x(const void* x, const void* w_r, float* logits, int32_t* topk_idx, float* gates,

@@ -20,6 +20,7 @@
 //                each token's rank among
 //                the block's earlier tokens choosing the same expert from a 64-bit ballot mask
 //                (popcount below the lane); one wave per top-k slot.
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -367,6 +368,33 @@ __global__ __launch_bounds__(kRouteThreads) void route_layout_kernel(
   // rows N_c..P_c-1 of this chunk's region hold no token
   for (int64_t r = N_c + (int64_t)bl * kRouteThreads + tid; r < P_c; r += (int64_t)nbpc * kRouteThreads)
     src_token[(int64_t)c * P_c + r] = -1;
+}
+
+// Routing scratch for callers that cannot allocate (moe_route_noalloc): the per-16-token expert
+// histograms of one call live in this file-scope array instead of a caller workspace. Each GPU
+// holds its own copy until the process ends; every call on that GPU shares it (route_topk
+// overwrites every entry the layout kernel reads, so nothing needs clearing between calls).
+static __device__ __align__(256) int32_t scratch[kNoAllocRouteScratchBytes / sizeof(int32_t)];
+
+// Device address of `scratch` on the current device, looked up once per device with that device
+// current (in host code the array's name is only a host-side stand-in).
+hipError_t route_noalloc_scratch(void** out) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 int route_blocks_per_chunk(int64_t T, int n) {

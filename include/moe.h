@@ -112,6 +112,18 @@ moe_status moe_route(const moe_desc* d, int chunk, const float* logits, int32_t*
                      float* gates, int32_t* counts, int32_t* offsets, int32_t* row_of,
                      int32_t* src_token, void* workspace, void* stream);
 
+/* Routing without a workspace, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): moe_route with the same
+ * arguments and bitwise the same outputs, but its histogram scratch is a fixed 4 MiB device array
+ * inside the library (one per GPU, held until the process ends). It allocates nothing and
+ * returns MOE_ERR_UNSUPPORTED when the call needs more than that scratch:
+ * n_chunks * ceil(ceil(T/n_chunks)/64) * 4 * E * 4 bytes > 4 MiB (at E = 128, more than 131072
+ * tokens). Every call on one GPU shares the array, so calls that overlap on one GPU (different
+ * streams, or other host threads) race: order them on one stream or synchronise between them. */
+moe_status moe_route_noalloc(const moe_desc* d, int chunk, const float* logits, int32_t* topk_idx,
+                             float* gates, int32_t* counts, int32_t* offsets, int32_t* row_of,
+                             int32_t* src_token, void* stream);
+
 /* Routing from the token activations (the router projection fused into routing): logits =
  * x . W_r^T with BF16 x [T,H] and W_r [E,H], FP32 accumulation on MFMA, then the top-k of
  * moe_route on those logits, which stay in registers and LDS; `logits` (nullable, FP32 [T,E])

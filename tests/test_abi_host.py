@@ -283,3 +283,13 @@ print("OPEN_GPU_FILES", bad, "KFD_MAPPED", "/dev/kfd" in maps)
                        env={k: v for k, v in os.environ.items() if k != "HIP_VISIBLE_DEVICES"})
     assert r.returncode == 0, r.stderr
     assert "OPEN_GPU_FILES [] KFD_MAPPED False" in r.stdout, r.stdout
+
+
+def test_noalloc_route_size_limit_is_checked_on_the_host():
+    """moe_route_noalloc rejects a call whose histograms exceed its fixed 4 MiB device scratch
+    before touching the GPU (T = 65536, E = 1024, one chunk: 1024 blocks x 4 x 1024 x 4 = 16 MiB)."""
+    _lib_or_skip()
+    d = mh.make_desc(T=65536, H=128, I=64, E=1024, E_local=8, k=2, n_chunks=1, dtype="bf16")
+    st, msg = _status_of(mh.moe_route_noalloc, d, -1, 1, 1, 1, 1, 1, 1, 1, 0)
+    assert st == -3 and "scratch" in msg, msg
+    assert _status_of(mh.moe_route_noalloc, _desc(), 0, None, None, None, None, None, None, None, 0)[0] == -1
