@@ -309,32 +309,118 @@ def gemm_bytes(cfg, N):
 
 
 def cpu_baseline(cfg, inp, budget_s: float):
-    """Time the CPU oracle (as it stands) on a bounded prefix of the workload's tokens."""
+    """Time the CPU oracle (as it stands) on the workload: the forward and the fused forward +
+    backward, one warmup and three measured runs each, median (and min) scaled to tokens/s. When
+    one fused run would exceed a third of the budget, a prefix of the tokens (same shapes
+    otherwise) is timed instead and scaled."""
     import numpy as np
     import oracle
+    blas = {}
     try:
         import threadpoolctl
-        info = threadpoolctl.threadpool_info()
+        info = [i for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
         threads = max([i.get("num_threads", 1) for i in info] or [1])
+        if info:
+            blas = {"vendor": info[0].get("internal_api"), "version": info[0].get("version"),
+                    "threads": info[0].get("num_threads")}
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    Ts = 1024
-    while True:
-        x = inp["x"][:Ts]
-        lg = inp["logits"][:Ts]
-        dy = inp["dy"][:Ts]
+
+    def run(Ts, backward):
+        x, lg = inp["x"][:Ts], inp["logits"][:Ts]
         t0 = time.perf_counter()
         f = oracle.forward(x, lg, inp["w1"], inp["w2"], k=cfg.k, e0=cfg.e0, E_local=cfg.E_local,
                            n_chunks=cfg.n_chunks)
-        oracle.backward(f, x, dy, inp["w1"], inp["w2"], inp["w_r"])
-        dt = time.perf_counter() - t0
-        if dt * 2 > budget_s or Ts * 2 > cfg.T:
-            break
-        Ts *= 2
-    return {"value": Ts / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"FP64 NumPy oracle, fused forward+backward on the first {Ts} of {cfg.T} tokens "
-                      f"(same H/I/E/k/chunks), {dt:.2f} s, scaled to tokens/s",
+        if backward:
+            oracle.backward(f, x, inp["dy"][:Ts], inp["w1"], inp["w2"], inp["w_r"])
+        return time.perf_counter() - t0
+    Ts = cfg.T
+    first = run(Ts, True)                     # also the warmup of the fused runs
+    while first > budget_s / 4 and Ts > 1024:
+        Ts //= 2
+        first = run(Ts, True)
+    fb = [run(Ts, True) for _ in range(3)]
+    run(Ts, False)
+    fw = [run(Ts, False) for _ in range(3)]
+    med_fb, med_fw = statistics.median(fb), statistics.median(fw)
+    sample = "all" if Ts == cfg.T else f"the first {Ts} of"
+    return {"value": round(Ts / med_fb, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"FP64 NumPy oracle on {sample} {cfg.T} tokens (same H/I/E/k/chunks): fused forward+backward "
+                      f"median of 3 runs after a warmup, {med_fb:.2f} s (min {min(fb):.2f} s); forward median "
+                      f"{med_fw:.2f} s",
+            "fwd_tokens_per_s": round(Ts / med_fw, 1), "fwd_bwd_s": [round(v, 3) for v in fb],
+            "fwd_s": [round(v, 3) for v in fw], "blas": blas,
             "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def step_stats(fn, stream, steps, torch):
+    """Per-step durations (ms) of `steps` calls: HIP events recorded on the compute stream between
+    the calls (each call ends with the auxiliary stream joined into it)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        fn()
+        ev[i + 1].record(stream)
+    ev[-1].synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+
+
+def imbalanced_leg(args, mh, torch, np):
+    """The imbalanced-routing workload (Zipf(1.2) expert popularity, empty local experts) at the same
+    shapes, fused forward+backward, with the combine output at the extent a live 32K-token graph
+    holds (262144 rows): untraced step time, per-step median, per-kernel in-step durations, the
+    local rows, and the time per local row against the balanced step's."""
+    import moe_inputs
+    cfg = moe_inputs.CONFIGS["zipf16k"]
+    big = moe_inputs.CONFIGS["fb32k"]
+    tr = mh.ExtentTracker()
+    own = mh.required_extent(cfg.T, cfg.k, cfg.E_local, cfg.n_chunks)[1]
+    live = tr.acquire(mh.required_extent(big.T, big.k, big.E_local, big.n_chunks)[1])
+    P_out = tr.current(own)
+    inp = moe_inputs.make_inputs(cfg, with_backward=True)
+    d = mh.make_desc(T=cfg.T, H=cfg.H, I=cfg.I, E=cfg.E, E_local=cfg.E_local, k=cfg.k, n_chunks=cfg.n_chunks,
+                     dtype=cfg.dtype, e0=cfg.e0, P_out=P_out)
+    b = mh.allocate(d, backward=True)
+    for name in ("x", "w1", "w2", "w_r", "dy"):
+        b[name] = torch.from_numpy(inp[name + "_bits"].view(np.int16)).cuda().view(torch.bfloat16)
+    b["logits"] = torch.from_numpy(inp["logits"]).cuda()
+    cs, aux = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def fb():
+        mh.moe_layer_forward_backward(d, b, cs, aux)
+    for _ in range(args.warmup):
+        fb()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        fb()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    for _ in range(args.warmup):
+        fb()
+    per_step = step_stats(fb, cs, args.steps, torch)
+    mh.moe_trace_enable(True)
+    for _ in range(args.steps):
+        fb()
+    torch.cuda.synchronize()
+    mh.moe_trace_disable()
+    per = {}
+    for name, _s, t in mh.moe_trace_entries():
+        p = per.setdefault(name, [0, 0.0])
+        p[0] += 1
+        p[1] += t
+    offsets = b["offsets"].cpu().numpy()
+    counts = [int(v) for v in (offsets[:, 1:] - offsets[:, :-1]).sum(axis=0)]
+    N = int(offsets[:, cfg.E_local].sum())
+    tr.release(live)
+    out = {"workload": "Zipf(1.2)-biased routing, 3 empty local experts, same shapes as the main line",
+           "P_out": int(P_out), "ms_per_step_untraced": round(ms, 4), "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
+           "step_ms_median": round(statistics.median(per_step), 4), "local_rows": N,
+           "local_rows_per_expert": counts,
+           "kernels_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in per.items()}}
+    del b
+    torch.cuda.empty_cache()
+    return out
 
 
 def fp8_forward(args, cfg, inp, mh, torch, np):
@@ -449,10 +535,11 @@ def fp8_dgrad(args, cfg, bufs, mh, torch, np):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=30)  # the clocks take some tens of ms of load to settle
     ap.add_argument("--workload", default="fb16k")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-imbalanced", action="store_true", help="skip the imbalanced-routing leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COMMANDS"),
                     help="write the markdown traffic summary of two rocprofv3 --pmc runs and exit (no GPU)")
@@ -568,6 +655,11 @@ def main():
         fb()
     torch.cuda.synchronize()
     ms_untraced = (time.perf_counter() - u0) * 1e3 / args.steps
+
+    # per-step durations: HIP events on the compute stream between steps (after each step's join)
+    for _ in range(args.warmup):
+        fb()
+    per_step = step_stats(fb, cs, args.steps, torch)
 
     # forward only
     for _ in range(args.warmup):
@@ -689,6 +781,8 @@ def main():
         del b1
         torch.cuda.empty_cache()
 
+    imb = None if args.no_imbalanced or args.workload != "fb16k" else imbalanced_leg(args, mh, torch, np)
+
     # FP8 payload path, forward only (the same shapes; weights quantised per output row outside the
     # timed region): expert GEMMs on FP8 MFMA, dispatch quantises per token, combine in BF16
     fp8 = fp8_forward(args, cfg, inp, mh, torch, np)
@@ -776,12 +870,19 @@ def main():
                    "local_rows": N, "tokens_with_local_expert": Tt},
         "fwd_tokens_per_s": round(cfg.T / (ms_fwd * 1e-3), 1), "fwd_ms": round(ms_fwd, 4),
         "ms_per_step_untraced": round(ms_untraced, 4),
+        "step_ms_median": round(statistics.median(per_step), 4), "step_ms_min": round(min(per_step), 4),
+        "step_ms_max": round(max(per_step), 4), "steps_measured": len(per_step),
+        "tokens_per_s_at_median_step": round(cfg.T / (statistics.median(per_step) * 1e-3), 1),
         "ms_per_step_traced": round(ms_traced, 4),
         "isolated_kernel_ms_sum": round(iso_ms, 4),
         "gemm_tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 2) if gemm_ms > 0 else None,
         "roofline": roof, "kernels": kernels,
     }
     line["one_chunk"] = n1
+    if imb:
+        imb["time_per_local_row_vs_balanced"] = round(
+            (imb["ms_per_step_untraced"] / max(1, imb["local_rows"])) / (ms_untraced / max(1, N)), 3)
+    line["imbalanced"] = imb
     line["stash"] = stash_line
     line["route_from_x"] = route_x_line
     line["fp8_fwd"] = fp8
