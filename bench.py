@@ -687,9 +687,10 @@ def main():
             mh.moe_route_bwd(d, c, b["dgates"], b["gates"], b["topk_idx"], b["x"], b["dlogits"], b["dwr_acc"],
                              b["dwr"], b["workspace"], cs)
             mh.moe_expert_ffn_bwd(d, c, b["dyd"], b["xd"], b["gu"], b["h"], b["w1"], b["w2"], b["offsets"],
-                                  b["dgu"], b["dxd"], None, None, cs)
+                                  b["dgu"], b["dxd"], None, None, None, cs)
             mh.moe_dispatch_bwd(d, c, b["dxd"], b["row_of"], b["topk_idx"], b["dlogits"], b["w_r"], b["dx"], cs)
-        mh.moe_expert_wgrad(d, b["dyd"], b["dgu"], b["xd"], b["h"], b["offsets"], b["dw1"], b["dw2"], cs)
+        mh.moe_expert_wgrad(d, b["dyd"], b["dgu"], b["xd"], b["h"], b["offsets"], b["dw1"], b["dw2"], b["workspace"],
+                            cs)
 
     stages()
     torch.cuda.synchronize()

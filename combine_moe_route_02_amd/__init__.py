@@ -56,7 +56,8 @@ SIZE_FIELDS = ["topk_idx", "gates", "counts", "offsets", "row_of", "src_token", 
                "h", "h_scale", "yd", "out", "dyd", "dgates", "dlogits", "dwr_acc", "dgu", "dxd", "dx",
                "dw1", "dw2", "dwr", "route_scratch", "route_bwd_scratch", "workspace",
                "w1t", "w1t_scale", "w2t", "w2t_scale", "dyd_q", "dyd_scale", "dgu_q", "dgu_scale",
-               "dyd_t", "dyd_cs", "dgu_t", "dgu_cs", "xd_t", "xd_cs", "h_t", "h_cs"]
+               "dyd_t", "dyd_cs", "dgu_t", "dgu_cs", "xd_t", "xd_cs", "h_t", "h_cs",
+               "wgrad_scratch", "wgrad_zero_bytes"]
 
 
 class MoeWorkspaceSizes(Structure):
@@ -74,8 +75,8 @@ _SIGS = {
     "moe_combine": [POINTER(MoeDesc), c_int] + [c_void_p] * 5,
     "moe_combine_bwd": [POINTER(MoeDesc), c_int] + [c_void_p] * 7,
     "moe_route_bwd": [POINTER(MoeDesc), c_int] + [c_void_p] * 9,
-    "moe_expert_ffn_bwd": [POINTER(MoeDesc), c_int] + [c_void_p] * 12,
-    "moe_expert_wgrad": [POINTER(MoeDesc)] + [c_void_p] * 8,
+    "moe_expert_ffn_bwd": [POINTER(MoeDesc), c_int] + [c_void_p] * 13,
+    "moe_expert_wgrad": [POINTER(MoeDesc)] + [c_void_p] * 9,
     "moe_dispatch_bwd": [POINTER(MoeDesc), c_int] + [c_void_p] * 7,
     "moe_quantize_rows_fp8": [c_int64, c_int32] + [c_void_p] * 4,
     "moe_quantize_cols_fp8": [c_int64, c_int64, c_int32] + [c_void_p] * 4,
@@ -208,15 +209,16 @@ def moe_route_bwd(d, chunk, dgates, gates, topk_idx, x, dlogits, dwr_acc, dwr, w
            "moe_route_bwd")
 
 
-def moe_expert_ffn_bwd(d, chunk, dyd, xd, gu, h, w1, w2, offsets, dgu, dxd, dw1=None, dw2=None, stream=None):
+def moe_expert_ffn_bwd(d, chunk, dyd, xd, gu, h, w1, w2, offsets, dgu, dxd, dw1=None, dw2=None, workspace=None,
+                       stream=None):
     _check(lib().moe_expert_ffn_bwd(ctypes.byref(d), chunk, _ptr(dyd), _ptr(xd), _ptr(gu), _ptr(h), _ptr(w1),
                                     _ptr(w2), _ptr(offsets), _ptr(dgu), _ptr(dxd), _ptr(dw1), _ptr(dw2),
-                                    _stream(stream)), "moe_expert_ffn_bwd")
+                                    _ptr(workspace), _stream(stream)), "moe_expert_ffn_bwd")
 
 
-def moe_expert_wgrad(d, dyd, dgu, xd, h, offsets, dw1, dw2, stream=None):
+def moe_expert_wgrad(d, dyd, dgu, xd, h, offsets, dw1, dw2, workspace, stream=None):
     _check(lib().moe_expert_wgrad(ctypes.byref(d), _ptr(dyd), _ptr(dgu), _ptr(xd), _ptr(h), _ptr(offsets),
-                                  _ptr(dw1), _ptr(dw2), _stream(stream)), "moe_expert_wgrad")
+                                  _ptr(dw1), _ptr(dw2), _ptr(workspace), _stream(stream)), "moe_expert_wgrad")
 
 
 def moe_dispatch_bwd(d, chunk, dxd, row_of, topk_idx, dlogits, w_r, dx, stream=None):
@@ -410,7 +412,11 @@ def allocate(d: MoeDesc, device="cuda", backward: bool = True, fill=None):
             spec[name] = ((max(1, ws[name] // 4),), f32)
     out = {}
     for name, (shape, dt) in spec.items():
+        if name == "workspace":
+            # zeroed: the weight-gradient counters inside it must be zero when first used
+            out[name] = torch.zeros(shape, dtype=dt, device=device)
+            continue
         out[name] = torch.empty(shape, dtype=dt, device=device)
-        if fill is not None and name not in ("workspace",):
+        if fill is not None:
             out[name].fill_(fill)
     return out

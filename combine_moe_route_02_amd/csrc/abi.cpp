@@ -159,12 +159,27 @@ int64_t router_scratch(const moe_desc* d) {
   return moe::router_partials_bytes(tokens_per_chunk(d), d->E, d->H);
 }
 
+// Workspace layout: the routing histograms and the router weight gradient's partials share its
+// start (they run in order on one stream); the expert weight gradients' scratch (BF16 path)
+// follows at a 256-byte boundary, so the router and expert weight gradients may run concurrently.
+int64_t wgrad_scratch(const moe_desc* d) {
+  return d->dtype == MOE_BF16 ? moe::wgrad_scratch_bytes(d->H, d->I, d->E_local) : 0;
+}
+int64_t wgrad_offset(const moe_desc* d) {
+  const int64_t a = moe::route_scratch_bytes(d->T, d->n_chunks, d->E);
+  const int64_t b = d->dtype == MOE_FP8_E4M3 ? 0 : router_scratch(d);
+  return ((a > b ? a : b) + 255) / 256 * 256;
+}
+void* wgrad_ws(const moe_desc* d, void* workspace) {
+  return wgrad_scratch(d) > 0 && workspace ? (char*)workspace + wgrad_offset(d) : nullptr;
+}
+
 }  // namespace
 
 extern "C" {
 
 const char* moe_last_error(void) { return g_err.c_str(); }
-int32_t moe_abi_version(void) { return 2; }
+int32_t moe_abi_version(void) { return 3; }
 
 moe_status moe_required_extent(int64_t T, int32_t k, int32_t E_local, int32_t n_chunks, int64_t* P_c,
                                int64_t* P_out) {
@@ -233,7 +248,9 @@ moe_status moe_workspace_bytes(const moe_desc* d, moe_workspace_sizes* o) {
   }
   o->route_scratch = moe::route_scratch_bytes(T, (int)n, (int)E);
   o->route_bwd_scratch = fp8 ? 0 : router_scratch(d);
-  o->workspace = o->route_scratch > o->route_bwd_scratch ? o->route_scratch : o->route_bwd_scratch;
+  o->wgrad_scratch = wgrad_scratch(d);
+  o->wgrad_zero_bytes = d->dtype == MOE_BF16 ? moe::wgrad_counter_bytes_of(d->H, d->I, d->E_local) : 0;
+  o->workspace = wgrad_offset(d) + o->wgrad_scratch;
   return MOE_OK;
 }
 
@@ -401,32 +418,36 @@ moe_status moe_route_bwd(const moe_desc* d, int chunk, const float* dgates, cons
 }
 
 moe_status moe_expert_wgrad(const moe_desc* d, const void* dyd, const void* dgu, const void* xd, const void* h,
-                            const int32_t* offsets, void* dw1, void* dw2, void* stream) {
+                            const int32_t* offsets, void* dw1, void* dw2, void* workspace, void* stream) {
   MOE_TRY(validate(d));
   MOE_TRY(no_fp8_bwd(d));
   MOE_TRY(bwd_extent(d));
   if (d->E_local == 0) return MOE_OK;
   MOE_NEED(offsets); MOE_NEED(dw1); MOE_NEED(dw2);
+  if (wgrad_scratch(d) > 0) MOE_NEED(workspace);
   if (rows_of(d) > 0) { MOE_NEED(dyd); MOE_NEED(dgu); MOE_NEED(xd); MOE_NEED(h); }
   MOE_HIP(moe::launch_expert_wgrad(is_bf16_rows(d), dyd, dgu, xd, h, offsets, dw1, dw2, d->H, d->I,
-                                   d->E_local, d->n_chunks, d->P_c, (hipStream_t)stream), "expert_wgrad");
+                                   d->E_local, d->n_chunks, d->P_c, wgrad_ws(d, workspace), (hipStream_t)stream),
+          "expert_wgrad");
   return MOE_OK;
 }
 
 moe_status moe_expert_ffn_bwd(const moe_desc* d, int chunk, const void* dyd, const void* xd, const void* gu,
                               const void* h, const void* w1, const void* w2, const int32_t* offsets,
-                              void* dgu, void* dxd, void* dw1, void* dw2, void* stream) {
+                              void* dgu, void* dxd, void* dw1, void* dw2, void* workspace, void* stream) {
   MOE_TRY(validate(d));
   MOE_TRY(no_fp8_bwd(d));
   MOE_TRY(check_chunk(d, chunk));
   if (chunk < 0) MOE_TRY(bwd_extent(d));  // the weight gradients follow the input gradients
   if (d->E_local == 0) return MOE_OK;
+  if (chunk < 0 && wgrad_scratch(d) > 0) MOE_NEED(workspace);
   Range r = range_of(d, chunk);
-  if (rows_of(d) == 0) return chunk < 0 ? moe_expert_wgrad(d, dyd, dgu, xd, h, offsets, dw1, dw2, stream) : MOE_OK;
+  if (rows_of(d) == 0)
+    return chunk < 0 ? moe_expert_wgrad(d, dyd, dgu, xd, h, offsets, dw1, dw2, workspace, stream) : MOE_OK;
   MOE_NEED(dyd); MOE_NEED(gu); MOE_NEED(w1); MOE_NEED(w2); MOE_NEED(offsets); MOE_NEED(dgu); MOE_NEED(dxd);
   MOE_HIP(moe::launch_expert_dgrad(is_bf16_rows(d), dyd, gu, w1, w2, offsets, dgu, dxd, d->H, d->I,
                                    d->E_local, r.c0, r.nc, d->P_c, (hipStream_t)stream), "expert_dgrad");
-  if (chunk < 0) return moe_expert_wgrad(d, dyd, dgu, xd, h, offsets, dw1, dw2, stream);
+  if (chunk < 0) return moe_expert_wgrad(d, dyd, dgu, xd, h, offsets, dw1, dw2, workspace, stream);
   return MOE_OK;
 }
 
@@ -734,7 +755,7 @@ static moe_status backward_sched(const moe_desc* d, const moe_tensors* t, hipStr
                                     t->dyd_q, t->dyd_scale, t->dgu, t->dgu_q, t->dgu_scale, t->dxd, !qcb, cs));
     else
       MOE_TRY(moe_expert_ffn_bwd(d, c, t->dyd, t->xd, t->gu, t->h, t->w1, t->w2, t->offsets, t->dgu, t->dxd,
-                                 nullptr, nullptr, cs));
+                                 nullptr, nullptr, t->workspace, cs));
     if (two) {
       MOE_HIP(hipEventRecord(dg[c], cs), "hipEventRecord");
       MOE_HIP(hipStreamWaitEvent(as, dg[c], 0), "hipStreamWaitEvent");
@@ -747,7 +768,7 @@ static moe_status backward_sched(const moe_desc* d, const moe_tensors* t, hipStr
                                   t->dgu_cs, t->xd_t, t->xd_cs, t->h_t, t->h_cs, t->dw1, t->dw2, !wq8, cs));
   }
   else
-    MOE_TRY(moe_expert_wgrad(d, t->dyd, t->dgu, t->xd, t->h, t->offsets, t->dw1, t->dw2, cs));
+    MOE_TRY(moe_expert_wgrad(d, t->dyd, t->dgu, t->xd, t->h, t->offsets, t->dw1, t->dw2, t->workspace, cs));
   if (two) {
     MOE_HIP(hipEventRecord(done, as), "hipEventRecord");
     MOE_HIP(hipStreamWaitEvent(cs, done, 0), "hipStreamWaitEvent");
@@ -769,6 +790,7 @@ static moe::ExpertGemm expert_gemm(const moe_desc* d, const moe_tensors* t) {
   g.xd = t->xd; g.w1 = t->w1; g.w2 = t->w2; g.gu = t->gu; g.h = t->h; g.yd = t->yd;
   g.dyd = t->dyd; g.dgu = t->dgu; g.dxd = t->dxd; g.dw1 = t->dw1; g.dw2 = t->dw2;
   g.offsets = t->offsets; g.H = d->H; g.I = d->I; g.El = d->E_local; g.n_chunks = d->n_chunks; g.P_c = d->P_c;
+  g.wgrad_ws = wgrad_ws(d, t->workspace);
   return g;
 }
 

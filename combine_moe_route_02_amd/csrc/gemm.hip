@@ -547,9 +547,9 @@ hipError_t launch_expert_dgrad(bool bf16, const void* dyd, const void* gu, const
 
 hipError_t launch_expert_wgrad(bool bf16, const void* dyd, const void* dgu, const void* xd,
                                const void* h, const int32_t* offsets, void* dw1, void* dw2, int H,
-                               int I, int El, int n, int64_t P_c, hipStream_t s) {
+                               int I, int El, int n, int64_t P_c, void* wgrad_ws, hipStream_t s) {
   if (El <= 0) return hipSuccess;
-  if (bf16) return gg_expert_wgrad_bf16(dyd, dgu, xd, h, offsets, dw1, dw2, H, I, El, n, P_c, s);
+  if (bf16) return gg_expert_wgrad_bf16(dyd, dgu, xd, h, offsets, dw1, dw2, H, I, El, n, P_c, wgrad_ws, s);
   SimtKArgs a{};
   a.A = (const float*)dyd; a.B = (const float*)h; a.C = (float*)dw2; a.lda = H; a.ldb = I;
   a.strideC = (int64_t)H * I; a.M = H; a.N = I; a.offsets = offsets; a.El = El; a.n_chunks = n; a.P_c = P_c;

@@ -13,578 +13,12 @@
 // layer schedule's merged launches): the second list's tiles continue the first's round robin,
 // so the CUs that the first leaves idle in its last round start the second.
 //
-// Engine (one 512-thread workgroup = 8 waves in a 2 x 4 grid over a BM x BN output tile, two
-// waves per SIMD, so the second wave on a SIMD issues MFMAs while the first waits; four waves
-// with 128 x 128 wave tiles read a third fewer LDS bytes but measured slower on every GEMM here):
-//   * Operands reach LDS by direct-to-LDS 16-byte buffer loads (buffer_load_dwordx4 ... lds):
-//     no staging registers, no VALU on the load path. The scalar buffer descriptor's extent
-//     masks rows past an expert's segment or a matrix edge (such loads return zero).
-//   * A ring of kNst LDS stages, each holding 64 bytes of K per MN row (32 BF16 or 64 FP8
-//     values); loads run kNst - 1 stages ahead. One s_barrier per stage, with an explicit
-//     vmcnt wait that leaves the younger stages' loads in flight (a workgroup fence would drain
-//     them).
-//   * Operands with K contiguous in HBM ("K-major") live in LDS as 64-byte rows whose four
-//     16-byte chunks are XOR-swizzled by (row >> 2) & 3: a ds_read_b128 of 16 consecutive rows
-//     at one chunk touches all 64 banks once.
-//   * Operands with K along HBM rows ("K-slow": the weights in the input-gradient GEMMs and
-//     both operands of the weight gradients) live in LDS as K-rows of MN values with chunks
-//     XOR-swizzled by 4 * (k & 3), and reach the MFMA through ds_read_b64_tr_b16, which
-//     transposes 4 x 4 blocks of 16-bit values across each 16-lane group.
-//   * The number of 32-row MFMA blocks a wave holds rows for is a template parameter of the K
-//     loop (chosen once per tile), so the partial last tile of an expert issues no MFMA for empty
-//     row blocks and the loop itself has no branches around MFMAs.
-//   * MFMAs are issued with the B fragment as the first operand: lane l then holds output row
-//     l & 31 and four consecutive columns per accumulator group, stored as one 8-byte BF16 write.
-#include "common.h"
-#include "launch.h"
-#include "trace.h"
+// The shared engine (operand ring, K loop, staging, tile walk) is in gg_engine.h; the BF16 weight
+// gradients are in wgrad.hip.
+#include "gg_engine.h"
 
 namespace moe {
 namespace gg {
-
-constexpr int kWM = 2, kWN = 4;       // waves per workgroup along M and N
-constexpr int kWaves = kWM * kWN;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kNst = 4;             // LDS ring stages
-constexpr int kRowB = 64;           // K bytes per MN row per stage
-constexpr int kKRows = 32;          // K rows per stage for 16-bit K-slow operands
-constexpr int kMaxGroups = 1024;
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-
-// LDS byte offset of 16-byte chunk c of row r in a K-major stage.
-MOE_DEV int km_off(int r, int c) { return r * kRowB + ((c ^ ((r >> 2) & 3)) << 4); }
-// LDS byte offset of 16-byte chunk c of K-row k in a K-slow stage of R MN values (R >= 128).
-template <int R>
-MOE_DEV int ks_off(int k, int c) { return k * (2 * R) + ((c ^ ((k & 3) << 2)) << 4); }
-
-// ---------------------------------------------------------------------------------------------
-// Operand tile loader: R MN rows, one stage = R * 64 bytes = R / 16 wave instructions of 1 KiB,
-// spread over the workgroup's waves.
-template <int R, bool KSLOW>
-struct Loader {
-  static constexpr int NI = R / (16 * kWaves);
-  static_assert(NI >= 1 && R % (16 * kWaves) == 0, "tile rows must cover every wave");
-  __amdgpu_buffer_rsrc_t rs;
-  uint32_t voff[NI];
-  uint32_t step;  // HBM bytes between consecutive stages
-  int wave;
-
-  // K-major: tile row r starts at base + map(r) * ld_bytes; bytes: readable extent from base
-  template <class Map>
-  MOE_DEV void init_kmajor(const void* base, int64_t ld_bytes, int64_t bytes, int wv, int lane, Map map) {
-    wave = wv;
-    rs = make_rsrc(base, bytes);
-    step = kRowB;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int r = 16 * (wave * NI + i) + (lane >> 2);
-      const int c = (lane & 3) ^ ((r >> 2) & 3);
-      voff[i] = (uint32_t)((int64_t)map(r) * ld_bytes) + 16u * (uint32_t)c;
-    }
-  }
-  // K-slow: K-row k of the tile starts at base + k * ld_bytes; its R MN values are contiguous
-  MOE_DEV void init_kslow(const void* base, int64_t ld_bytes, int64_t bytes, int wv, int lane) {
-    static_assert(R >= 128, "K-slow tiles need >= 16 chunks per K-row");
-    constexpr int CPR = 2 * R / 16;      // chunks per K-row
-    constexpr int RPI = 1024 / (2 * R);  // K-rows per wave instruction
-    wave = wv;
-    rs = make_rsrc(base, bytes);
-    step = (uint32_t)(kKRows * ld_bytes);
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int k = RPI * (wave * NI + i) + lane / CPR;
-      const int c = (lane % CPR) ^ ((k & 3) << 2);
-      voff[i] = (uint32_t)(k * ld_bytes) + 16u * (uint32_t)c;
-    }
-  }
-  MOE_DEV void issue(char* stage, int s) const {
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(stage + (wave * NI + i) * 1024), 16,
-                                               (int)voff[i], (int)((uint32_t)s * step), 0, 0);
-  }
-};
-
-// ---------------------------------------------------------------------------------------------
-// Fragments for one MFMA: rows mb + (lane & 31) of the operand.
-
-// K-major BF16: 8 K values, k16 step kk of the stage, K half lane >> 5.
-MOE_DEV bf16x8_t frag_km(const char* st, int mb, int kk, int lane) {
-  return *(const bf16x8_t*)(st + km_off(mb + (lane & 31), 2 * kk + (lane >> 5)));
-}
-
-MOE_DEV s16x4 ds_read_tr(const char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
-}
-
-// K-slow BF16: the same 8 K values assembled by two transposing reads. In each 16-lane group
-// lane q reads the 4 MN-consecutive values (k0 + (q >> 2), m + 4 (q & 3) .. +3); after the
-// transpose lane q holds (k0 .. k0+3, m + q).
-template <int R>
-MOE_DEV bf16x8_t frag_ks(const char* st, int mb, int kk, int lane) {
-  const int g = lane >> 4, q = lane & 15;
-  const int cb = 2 * (mb + 16 * (g & 1) + 4 * (q & 3));  // byte of the first value in its K-row
-  const int k0 = 16 * kk + 8 * (g >> 1) + (q >> 2);
-  const s16x4 lo = ds_read_tr(st + ks_off<R>(k0, cb >> 4) + (cb & 15));
-  const s16x4 hi = ds_read_tr(st + ks_off<R>(k0 + 4, cb >> 4) + (cb & 15));
-  const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8_t, v);
-}
-
-// K-major FP8: 32 K values (bytes 32 * (lane >> 5) .. +32 of the stage row).
-MOE_DEV i32x8_t frag_km8(const char* st, int mb, int lane) {
-  const int r = mb + (lane & 31), hk = lane >> 5;
-  const i32x4_t a = *(const i32x4_t*)(st + km_off(r, 2 * hk));
-  const i32x4_t b = *(const i32x4_t*)(st + km_off(r, 2 * hk + 1));
-  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// One LDS stage of MFMAs: acc[tm][tn] += A[rows of block tm] . B[rows of block tn]^T for
-// tm < TMA (row blocks past the tile's valid rows are skipped at compile time). `loads` issues the
-// global -> LDS loads of a later stage; the schedule spreads them and the fragment reads between
-// the MFMAs (the default scheduler would recycle one fragment register per read and serialise).
-template <bool FP8, bool AKS, bool BKS, int RA, int RB, int TM, int TN, int TMA, int VM, class Loads>
-MOE_DEV void stage_mma(const char* sa, const char* sb, int arow0, int brow0, int lane,
-                       f32x16_t (&acc)[TM][TN], Loads&& loads) {
-  if constexpr (TMA == 0) {
-    loads();
-  } else if constexpr (FP8) {
-    i32x8_t fa[TMA], fb[TN];
-#pragma unroll
-    for (int tm = 0; tm < TMA; ++tm) fa[tm] = frag_km8(sa, arow0 + 32 * tm, lane);
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn) fb[tn] = frag_km8(sb, brow0 + 32 * tn, lane);
-    loads();
-#pragma unroll
-    for (int tm = 0; tm < TMA; ++tm)
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn)
-        acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[tn], fa[tm], acc[tm][tn], 0, 0,
-                                                                       0, 0, 0, 0);
-    constexpr int RD = 2 * (TMA + TN), MF = TMA * TN;
-    __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
-#pragma unroll
-    for (int i = 0; i < VM; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
-  } else {
-    // all fragments of k16 step 0; step 1's reads, then the loads, spread one per MFMA of step 0
-    // onwards; then the remaining MFMAs
-    bf16x8_t fa[2][TMA], fb[2][TN];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-      for (int tm = 0; tm < TMA; ++tm)
-        fa[kk][tm] = AKS ? frag_ks<RA>(sa, arow0 + 32 * tm, kk, lane) : frag_km(sa, arow0 + 32 * tm, kk, lane);
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn)
-        fb[kk][tn] = BKS ? frag_ks<RB>(sb, brow0 + 32 * tn, kk, lane) : frag_km(sb, brow0 + 32 * tn, kk, lane);
-    }
-    loads();
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int tm = 0; tm < TMA; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
-          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk][tn], fa[kk][tm], acc[tm][tn], 0, 0, 0);
-    constexpr int RD = ((AKS ? 2 : 1) * TMA + (BKS ? 2 : 1) * TN);  // LDS reads per k16 step
-    constexpr int MF = TMA * TN;                                     // MFMAs per k16 step
-    // With a K-slow weight operand (input gradients, weight gradients) the loads go out first,
-    // right after the stage barrier (measured faster there); otherwise they follow the first
-    // MFMAs.
-    if constexpr (BKS) __builtin_amdgcn_sched_group_barrier(0x020, VM, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
-#pragma unroll
-    for (int i = 0; i < RD; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    if constexpr (!BKS) {
-#pragma unroll
-      for (int i = 0; i < VM; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      }
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * MF, 0);
-  }
-}
-
-// K loop over nks stages through the LDS ring. Every iteration issues the loads of stage
-// s + kNst - 1; past the last stage they fetch masked (zero) or unused data into a ring slot that
-// is never read again, so every iteration waits with the same count. On return all loads have
-// completed and every wave has passed a barrier after its last LDS read, so the ring is free.
-template <bool FP8, bool AKS, bool BKS, int RA, int RB, int TM, int TN, int TMA, class LA, class LB>
-MOE_DEV void kloop(const LA& la, const LB& lb, char* ring, int nks, int arow0, int brow0, int lane,
-                   f32x16_t (&acc)[TM][TN]) {
-  constexpr int SA = RA * kRowB, SS = (RA + RB) * kRowB;
-  constexpr int NL = LA::NI + LB::NI;  // load instructions per wave per stage
-#pragma unroll
-  for (int s = 0; s < kNst - 1; ++s) {
-    la.issue(ring + s * SS, s);
-    lb.issue(ring + s * SS + SA, s);
-  }
-  for (int s = 0; s < nks; ++s) {
-    wait_vm<(kNst - 2) * NL>();    // stage s has landed (this wave's loads)
-    __builtin_amdgcn_s_barrier();  // every wave's part of stage s is in LDS; stage s-1 is consumed
-    const int ld = s + kNst - 1;
-    char* st = ring + (ld % kNst) * SS;
-    const char* cur = ring + (s % kNst) * SS;
-    stage_mma<FP8, AKS, BKS, RA, RB, TM, TN, TMA, NL>(cur, cur + SA, arow0, brow0, lane, acc, [&] {
-      la.issue(st, ld);
-      lb.issue(st + SA, ld);
-    });
-  }
-  wait_vm<0>();
-  __syncthreads();
-}
-
-MOE_DEV uint2 pack4(float a, float b, float c, float d) { return make_uint2(pack_bf2(a, b), pack_bf2(c, d)); }
-MOE_DEV void unpack4(uint2 v, float* f) {
-  f[0] = bf2f(v.x & 0xffff); f[1] = bf2f(v.x >> 16); f[2] = bf2f(v.y & 0xffff); f[3] = bf2f(v.y >> 16);
-}
-MOE_DEV int out_row(int lane) { return lane & 31; }
-MOE_DEV int out_col(int g, int lane) { return 8 * g + 4 * (lane >> 5); }
-
-// Workgroup barrier for the LDS staging area only: every wave's LDS accesses are complete, but its
-// global stores may still be in flight (a __syncthreads fence would wait for them as well).
-MOE_DEV void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xf | (7 << 4) | (3 << 14));  // lgkmcnt(0), other counters untouched
-  __builtin_amdgcn_s_barrier();
-}
-
-// Output staging: a [BM, W] BF16 tile in LDS with a row pitch of W * 2 + 16 bytes (16-byte aligned
-// rows; the pad spreads the MFMA-layout writes of 32 rows over the banks).
-template <int W> constexpr int pitch() { return W * 2 + 16; }
-template <int BM, int W> constexpr size_t stage_bytes() { return (size_t)BM * pitch<W>(); }
-
-// Store rows < mvalid and columns < nvalid (a multiple of 8) of a staged tile to dst (row stride
-// ld elements) with 16-byte writes: each wave instruction writes whole rows. NT: non-temporal
-// stores, for outputs no kernel reads soon (saved G/U, weight gradients); measured faster there,
-// and slower for outputs the next kernel reads (h, yd, dG/dU, dxd), which stay normal.
-template <int BM, int W, bool NT = false>
-MOE_DEV void store_staged(const char* lds, uint16_t* dst, int64_t ld, int mvalid, int nvalid, int tid) {
-  constexpr int CPR = W / 8, RPP = kThreads / CPR;
-  const int c = tid % CPR;
-#pragma unroll 4
-  for (int r = tid / CPR; r < BM; r += RPP)
-    if (r < mvalid && 8 * c < nvalid) {
-      const i32x4_t v = *(const i32x4_t*)(lds + r * pitch<W>() + 16 * c);
-      i32x4_t* p = (i32x4_t*)(dst + (int64_t)r * ld + 8 * c);
-      if constexpr (NT) __builtin_nontemporal_store(v, p);
-      else *p = v;
-    }
-}
-
-// Load rows < mvalid, columns < nvalid of a [BM, W] BF16 tile from src into LDS staging.
-template <int BM, int W>
-MOE_DEV void load_staged(char* lds, const uint16_t* src, int64_t ld, int mvalid, int nvalid, int tid) {
-  constexpr int CPR = W / 8, RPP = kThreads / CPR;
-  const int c = tid % CPR;
-#pragma unroll 4
-  for (int r = tid / CPR; r < BM; r += RPP)
-    if (r < mvalid && 8 * c < nvalid)
-      *(uint4*)(lds + r * pitch<W>() + 16 * c) = *(const uint4*)(src + (int64_t)r * ld + 8 * c);
-}
-
-// ---------------------------------------------------------------------------------------------
-// Row-grouped GEMMs (forward and input gradients):
-//   C[r0 + m][n] = sum_k A[r0 + m][k] * B_e(n, k) over the rows of local expert e in a chunk.
-// Persistent: the grid holds at most one workgroup per CU; each loops over its XCD's tiles.
-enum Mode { kGateUp = 0, kDown = 1, kDownBwd = 2, kGateUpBwd = 3 };
-
-struct RowsArgs {
-  const void* A;          // [P, K] dispatch-ordered rows (BF16, or e4m3 codes)
-  const void* B;          // expert weights, strideB elements per expert
-  uint16_t* C;            // [P, ldc] BF16 output rows
-  uint16_t* C2;           // kGateUp: G/U save [P, 2I] (nullable)
-  const uint16_t* aux;    // kDownBwd: G/U [P, 2I]
-  const float* scale_a;   // FP8: per dispatch row
-  const float* scale_b;   // FP8: per weight row, strideSB per expert
-  int64_t lda, ldc, strideB, strideSB;
-  int K, N, I;
-  const int32_t* offsets;
-  int El, c0, nc;
-  int64_t P_c;
-};
-
-template <int BM, int BN, int MODE>
-constexpr size_t rows_lds_bytes() {
-  const size_t ring = (size_t)kNst * (BM + BN) * kRowB;
-  // gate/up and down-bwd stage two [BM, W] tiles at once (G and U)
-  const size_t ep = (MODE == kGateUp) ? 2 * stage_bytes<BM, BN / 2>()
-                  : (MODE == kDownBwd) ? 2 * stage_bytes<BM, BN>() : stage_bytes<BM, BN>();
-  return ring > ep ? ring : ep;
-}
-
-// Group -> tile prefix of one row-grouped GEMM, rebuilt in LDS by every workgroup.
-struct RowsShared {
-  int pre[kMaxGroups + 1];   // large tiles before group g
-  int64_t r0[kMaxGroups];    // first dispatch row of group g
-  int len[kMaxGroups];       // rows of group g
-  int preb[kMaxGroups + 1];  // small tiles before group g
-};
-
-// Persistent work slots. Per XCD the workgroups (block b runs on XCD b % 8; W of them per XCD)
-// share one sequence of slots: slot s goes to the XCD's workgroup s % W, so that a list that
-// starts at slot `first` continues the round robin where the previous list of the same launch
-// ended, and a workgroup that finishes early takes the next list's tiles.
-MOE_DEV int first_slot(int first) {
-  const int w = gridDim.x / 8, j = blockIdx.x / 8;
-  return first + ((j - first) % w + w) % w;
-}
-
-// The tiles of one row-grouped GEMM from per-XCD slot `first` on; returns the slot after its
-// last. Every thread of the workgroup calls it (it contains barriers).
-template <int BM, int BN, int MODE, bool FP8>
-MOE_DEV int rows_list(const RowsArgs& a, int first, RowsShared& sh, char* ring) {
-  constexpr int WTM = BM / kWM, WTN = BN / kWN, TM = WTM / 32, TN = WTN / 32;
-  constexpr bool kSwiGLU = (MODE == kGateUp);
-  // BF16 input gradients read W_e as stored (K-slow); FP8 ones read a transposed copy (K-major)
-  constexpr bool kBKS = !FP8 && (MODE == kDownBwd || MODE == kGateUpBwd);
-  constexpr int ES = FP8 ? 1 : 2;      // element bytes
-  constexpr int OUTN = kSwiGLU ? BN / 2 : BN;
-  static_assert(!(FP8 && MODE == kGateUpBwd), "FP8 gate/up dgrad runs as kDown on the transposed W1");
-  int* s_pre = sh.pre;
-  int64_t* s_r0 = sh.r0;
-  int* s_len = sh.len;
-  int* s_preb = sh.preb;
-  __syncthreads();  // a previous list of this launch may still read the prefix
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / kWN, wn = wave % kWN;
-  const int G = a.nc * a.El;
-  const int ntiles = (a.N + OUTN - 1) / OUTN;
-  // Two tile classes, each in group order: "large" row tiles (full, or a last tile of more than
-  // BM / 2 rows) and "small" last tiles (at most BM / 2 rows, cheaper: half the waves issue no
-  // MFMA). Large tiles are dealt first, so the small ones fill a second round where one is needed.
-  for (int g = tid; g < G; g += kThreads) {
-    const int c = a.c0 + g / a.El, e = g % a.El;
-    const int32_t* off = a.offsets + (int64_t)c * (a.El + 1);
-    const int len = off[e + 1] - off[e];
-    const int rem = len % BM;
-    s_r0[g] = (int64_t)c * a.P_c + off[e];
-    s_len[g] = len;
-    s_pre[g + 1] = (len / BM + (rem > BM / 2 ? 1 : 0)) * ntiles;
-    s_preb[g + 1] = (rem > 0 && rem <= BM / 2 ? 1 : 0) * ntiles;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    s_pre[0] = 0;
-    for (int g = 0; g < G; ++g) s_pre[g + 1] += s_pre[g];
-  } else if (tid == 64) {
-    s_preb[0] = 0;
-    for (int g = 0; g < G; ++g) s_preb[g + 1] += s_preb[g];
-  }
-  __syncthreads();
-  const int total_l = s_pre[G], total_s = s_preb[G];
-  // Workgroups are dealt round-robin to the 8 XCDs (block b runs on XCD b % 8); each XCD owns a
-  // contiguous range of the large tiles and one of the small tiles, so the tiles of one expert
-  // share that XCD's L2. An XCD's workgroups walk its large range, then its small range.
-  const int pxl = (total_l + 7) / 8, pxs = (total_s + 7) / 8;
-  const int xcd = blockIdx.x % 8, wg_per_xcd = gridDim.x / 8;
-  for (int gs = first_slot(first); gs < first + pxl + pxs; gs += wg_per_xcd) {
-    const int slot = gs - first;
-    const bool large = slot < pxl;
-    const int tile = large ? xcd * pxl + slot : xcd * pxs + (slot - pxl);
-    if (tile >= (large ? total_l : total_s)) continue;
-    const int* pre = large ? s_pre : s_preb;
-    int lo = 0, hi = G;
-    while (hi - lo > 1) { const int mid = (lo + hi) >> 1; if (pre[mid] <= tile) lo = mid; else hi = mid; }
-    const int g = __builtin_amdgcn_readfirstlane(lo);
-    const int e = g % a.El;
-    const int t_in = tile - __builtin_amdgcn_readfirstlane(pre[g]);
-    const int mt = large ? t_in / ntiles : s_len[g] / BM, nt = t_in % ntiles;
-    const int64_t rg = s_r0[g];
-    const int64_t r0 = (((int64_t)__builtin_amdgcn_readfirstlane((int)(rg >> 32)) << 32) |
-                        (uint32_t)__builtin_amdgcn_readfirstlane((int)(rg & 0xffffffff))) + (int64_t)mt * BM;
-    const int mvalid = min(BM, __builtin_amdgcn_readfirstlane(s_len[g]) - mt * BM);
-    const int n0 = nt * OUTN;
-    const int nvalid = min(OUTN, a.N - n0);
-    const char* Be = (const char*)a.B + (int64_t)e * a.strideB * ES;
-
-    Loader<BM, false> la;
-    la.init_kmajor((const char*)a.A + r0 * a.lda * ES, a.lda * ES, (int64_t)mvalid * a.lda * ES, wave, lane,
-                   [](int r) { return r; });
-    Loader<BN, kBKS> lb;
-    if constexpr (kSwiGLU) {
-      // tile row r -> wave column block r / WTN; its first half are gate rows j, its second half
-      // the matching up rows I + j; readable rows run to the end of this expert's W1
-      const int I = a.I;
-      lb.init_kmajor(Be + (int64_t)n0 * a.K * ES, (int64_t)a.K * ES, (2 * (int64_t)I - n0) * a.K * ES, wave,
-                     lane, [I](int r) {
-                       const int q = r % WTN, hw = WTN / 2, j = (r / WTN) * hw + (q < hw ? q : q - hw);
-                       return q < hw ? j : I + j;
-                     });
-    } else if constexpr (MODE == kDown || FP8) {
-      lb.init_kmajor(Be + (int64_t)n0 * a.K * ES, (int64_t)a.K * ES, ((int64_t)a.N - n0) * a.K * ES, wave, lane,
-                     [](int r) { return r; });
-    } else {
-      // B(n, k) = W_e[k][n]: K-rows of N values, the tile's columns start at n0
-      lb.init_kslow(Be + (int64_t)n0 * 2, (int64_t)a.N * 2, ((int64_t)a.K * a.N - n0) * 2, wave, lane);
-    }
-
-    f32x16_t acc[TM][TN];
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) acc[tm][tn][q] = 0.f;
-
-    const int nks = a.K / (FP8 ? 64 : 32);
-    const int tma = __builtin_amdgcn_readfirstlane(max(0, min(TM, (mvalid - wm * WTM + 31) / 32)));
-    const int arow0 = wm * WTM, brow0 = wn * WTN;
-    static_assert(TM <= 4, "TM > 4");
-    switch (tma) {
-#define MOE_KL(T_) kloop<FP8, false, kBKS, BM, BN, TM, TN, (T_ <= TM ? T_ : TM)>(la, lb, ring, nks, arow0, brow0, lane, acc)
-      case 4: MOE_KL(4); break;
-      case 3: MOE_KL(3); break;
-      case 2: MOE_KL(2); break;
-      case 1: MOE_KL(1); break;
-      default: MOE_KL(0); break;
-#undef MOE_KL
-    }
-
-    // Epilogue through LDS staging (the ring is free): each wave writes its values in the MFMA
-    // layout (row m = lane & 31 of each 32-row block, 4 consecutive columns), then the workgroup
-    // stores whole rows. Rows past the expert's segment and columns past N are not stored.
-    const int mrow = wm * WTM + out_row(lane);
-    if constexpr (kSwiGLU) {
-      constexpr int W = BN / 2;                 // h / G / U columns per tile
-      char* sg = ring;                           // G, then h
-      char* su = ring + stage_bytes<BM, W>();    // U
-      float sr[TM];
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm) sr[tm] = (FP8 && mrow + tm * 32 < mvalid) ? a.scale_a[r0 + mrow + tm * 32] : 1.f;
-      const float* sb = FP8 ? a.scale_b + (int64_t)e * a.strideSB : nullptr;
-      // G and U (dequantised) into the two staging tiles
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < TN / 2; ++tn)
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const int jl = wn * (WTN / 2) + tn * 32 + out_col(gq, lane);   // column within the tile
-            float gv[4], uv[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              gv[q] = acc[tm][tn][4 * gq + q];
-              uv[q] = acc[tm][tn + TN / 2][4 * gq + q];
-              if constexpr (FP8) {
-                const int j = min(n0 + jl + q, a.N - 1);
-                gv[q] *= sr[tm] * sb[j];
-                uv[q] *= sr[tm] * sb[a.I + j];
-              }
-            }
-            const int m = mrow + tm * 32;
-            *(uint2*)(sg + m * pitch<W>() + 2 * jl) = pack4(gv[0], gv[1], gv[2], gv[3]);
-            *(uint2*)(su + m * pitch<W>() + 2 * jl) = pack4(uv[0], uv[1], uv[2], uv[3]);
-          }
-      lds_barrier();
-      if (a.C2) {
-        store_staged<BM, W, true>(sg, a.C2 + r0 * 2 * (int64_t)a.I + n0, 2 * (int64_t)a.I, mvalid, nvalid, tid);
-        store_staged<BM, W, true>(su, a.C2 + r0 * 2 * (int64_t)a.I + a.I + n0, 2 * (int64_t)a.I, mvalid, nvalid, tid);
-      }
-      lds_barrier();
-      // h = silu(G) * U from the FP32 accumulators
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < TN / 2; ++tn)
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const int jl = wn * (WTN / 2) + tn * 32 + out_col(gq, lane);
-            float hv[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              float gv = acc[tm][tn][4 * gq + q], uv = acc[tm][tn + TN / 2][4 * gq + q];
-              if constexpr (FP8) {
-                const int j = min(n0 + jl + q, a.N - 1);
-                gv *= sr[tm] * sb[j];
-                uv *= sr[tm] * sb[a.I + j];
-              }
-              hv[q] = gv * sigmoidf_(gv) * uv;
-            }
-            const int m = mrow + tm * 32;
-            *(uint2*)(sg + m * pitch<W>() + 2 * jl) = pack4(hv[0], hv[1], hv[2], hv[3]);
-          }
-      lds_barrier();
-      store_staged<BM, W>(sg, a.C + r0 * a.ldc + n0, a.ldc, mvalid, nvalid, tid);
-      lds_barrier();
-    } else if constexpr (MODE == kDownBwd) {
-      // G and U of the tile's rows and columns, staged coalesced; dG and dU overwrite them in place
-      constexpr int W = BN;
-      char* sg = ring;
-      char* su = ring + stage_bytes<BM, W>();
-      const int64_t I2 = 2 * (int64_t)a.I;
-      load_staged<BM, W>(sg, a.aux + r0 * I2 + n0, I2, mvalid, nvalid, tid);
-      load_staged<BM, W>(su, a.aux + r0 * I2 + a.I + n0, I2, mvalid, nvalid, tid);
-      float sr[TM];
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm) sr[tm] = (FP8 && mrow + tm * 32 < mvalid) ? a.scale_a[r0 + mrow + tm * 32] : 1.f;
-      lds_barrier();
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const int jl = wn * WTN + tn * 32 + out_col(gq, lane);
-            const int m = mrow + tm * 32;
-            char* pg = sg + m * pitch<W>() + 2 * jl;
-            char* pu = su + m * pitch<W>() + 2 * jl;
-            float gv[4], uv[4], dg[4], du[4];
-            unpack4(*(const uint2*)pg, gv);
-            unpack4(*(const uint2*)pu, uv);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              float dh = acc[tm][tn][4 * gq + q];
-              if constexpr (FP8) dh *= sr[tm] * a.scale_b[(int64_t)e * a.strideSB + min(n0 + jl + q, a.N - 1)];
-              const float sgm = sigmoidf_(gv[q]);
-              dg[q] = dh * uv[q] * sgm * (1.f + gv[q] * (1.f - sgm));
-              du[q] = dh * gv[q] * sgm;
-            }
-            *(uint2*)pg = pack4(dg[0], dg[1], dg[2], dg[3]);
-            *(uint2*)pu = pack4(du[0], du[1], du[2], du[3]);
-          }
-      lds_barrier();
-      store_staged<BM, W>(sg, a.C + r0 * I2 + n0, I2, mvalid, nvalid, tid);
-      store_staged<BM, W>(su, a.C + r0 * I2 + a.I + n0, I2, mvalid, nvalid, tid);
-      lds_barrier();
-    } else {
-      constexpr int W = BN;
-      float sr[TM];
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm) sr[tm] = (FP8 && mrow + tm * 32 < mvalid) ? a.scale_a[r0 + mrow + tm * 32] : 1.f;
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const int nl = wn * WTN + tn * 32 + out_col(gq, lane);
-            float v[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              v[q] = acc[tm][tn][4 * gq + q];
-              if constexpr (FP8) v[q] *= sr[tm] * a.scale_b[(int64_t)e * a.strideSB + min(n0 + nl + q, a.N - 1)];
-            }
-            *(uint2*)(ring + (mrow + tm * 32) * pitch<W>() + 2 * nl) = pack4(v[0], v[1], v[2], v[3]);
-          }
-      lds_barrier();
-      store_staged<BM, W>(ring, a.C + r0 * a.ldc + n0, a.ldc, mvalid, nvalid, tid);
-      lds_barrier();
-    }
-  }
-  return first + pxl + pxs;
-}
 
 template <int BM, int BN, int MODE, bool FP8>
 __global__ __launch_bounds__(kThreads) void rows_kernel(RowsArgs a) {
@@ -601,113 +35,6 @@ __global__ __launch_bounds__(kThreads) void rows_pair_kernel(RowsArgs a, RowsArg
   extern __shared__ __attribute__((aligned(1024))) char ring[];
   const int f = rows_list<BM1, BN1, MODE1, false>(a, 0, sh, ring);
   rows_list<BM2, BN2, MODE2, false>(b, f, sh, ring);
-}
-
-// ---------------------------------------------------------------------------------------------
-// Weight gradients: C_e[m][n] = sum over the rows of every chunk of expert e of A[row][m] B[row][n]
-// (both operands K-slow), accumulated in FP32 across the chunks' segments, converted once.
-// Persistent like rows_kernel.
-struct WgradArgs {
-  const uint16_t* A;      // [P, M]
-  const uint16_t* B;      // [P, N]
-  uint16_t* C;            // per expert [M, N]
-  int64_t lda, ldb, strideC;
-  int M, N;
-  const int32_t* offsets; // per-chunk local offsets
-  int El, n_chunks;
-  int64_t P_c;
-};
-
-template <int BM, int BN>
-constexpr size_t wgrad_lds_bytes() {
-  const size_t ring = (size_t)kNst * (BM + BN) * kRowB, ep = stage_bytes<BM, BN>();
-  return ring > ep ? ring : ep;
-}
-
-// One weight-gradient tile: C[grp][m0.., n0..] = sum over the rows of every chunk of expert grp
-// of A_rows^T B_rows (both operands K-slow), one FP32 K loop, one BF16 store.
-template <int BM, int BN>
-MOE_DEV void wgrad_tile(const WgradArgs& a, int tile, char* ring, int tid, int lane, int wave) {
-  constexpr int WTM = BM / kWM, WTN = BN / kWN, TM = WTM / 32, TN = WTN / 32;
-  const int wm = wave / kWN, wn = wave % kWN;
-  const int mtiles = (a.M + BM - 1) / BM, ntiles = (a.N + BN - 1) / BN;
-  const int grp = tile / (mtiles * ntiles);
-  const int t_in = tile % (mtiles * ntiles);
-  const int m0 = (t_in / ntiles) * BM, n0 = (t_in % ntiles) * BN;
-
-  f32x16_t acc[TM][TN];
-#pragma unroll
-  for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[tm][tn][q] = 0.f;
-
-  for (int c = 0; c < a.n_chunks; ++c) {
-    const int32_t* off = a.offsets + (int64_t)c * (a.El + 1);
-    const int64_t row0 = (int64_t)c * a.P_c + off[grp];
-    const int len = __builtin_amdgcn_readfirstlane(off[grp + 1] - off[grp]);
-    if (len <= 0) continue;
-    Loader<BM, true> la;
-    la.init_kslow(a.A + row0 * a.lda + m0, a.lda * 2, ((int64_t)len * a.lda - m0) * 2, wave, lane);
-    Loader<BN, true> lb;
-    lb.init_kslow(a.B + row0 * a.ldb + n0, a.ldb * 2, ((int64_t)len * a.ldb - n0) * 2, wave, lane);
-    const int nks = (len + kKRows - 1) / kKRows;
-    kloop<false, true, true, BM, BN, TM, TN, TM>(la, lb, ring, nks, wm * WTM, wn * WTN, lane, acc);
-  }
-
-  const int mrow = wm * WTM + out_row(lane);
-#pragma unroll
-  for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int nl = wn * WTN + tn * 32 + out_col(gq, lane);
-        const f32x16_t& v = acc[tm][tn];
-        *(uint2*)(ring + (mrow + tm * 32) * pitch<BN>() + 2 * nl) =
-            pack4(v[4 * gq], v[4 * gq + 1], v[4 * gq + 2], v[4 * gq + 3]);
-      }
-  lds_barrier();
-  store_staged<BM, BN, true>(ring, a.C + (int64_t)grp * a.strideC + (int64_t)m0 * a.N + n0, a.N,
-                       min(BM, a.M - m0), min(BN, a.N - n0), tid);
-  lds_barrier();
-}
-
-template <int BM, int BN>
-MOE_DEV int wgrad_tiles(const WgradArgs& a) { return a.El * ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN); }
-
-// The tiles of one weight gradient (a.El = 0: none) from per-XCD slot `first` on, in the slot
-// sequence of rows_list; each XCD owns a contiguous range of the tiles. Returns the slot after
-// the last.
-template <int BM, int BN>
-MOE_DEV int wgrad_list(const WgradArgs& a, int first, char* ring) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int ta = a.El > 0 ? wgrad_tiles<BM, BN>(a) : 0;
-  const int pxa = (ta + 7) / 8;
-  const int xcd = blockIdx.x % 8, wg_per_xcd = gridDim.x / 8;
-  for (int gs = first_slot(first); gs < first + pxa; gs += wg_per_xcd) {
-    const int tile = xcd * pxa + (gs - first);
-    if (tile < ta) wgrad_tile<BM, BN>(a, tile, ring, tid, lane, wave);
-  }
-  return first + pxa;
-}
-
-// Up to two independent weight gradients in one persistent launch, so the second fills the
-// first one's last round.
-template <int BM, int BN>
-__global__ __launch_bounds__(kThreads) void wgrad_kernel(WgradArgs a, WgradArgs b) {
-  extern __shared__ __attribute__((aligned(1024))) char ring[];
-  const int f = wgrad_list<BM, BN>(a, 0, ring);
-  wgrad_list<BM, BN>(b, f, ring);
-}
-
-// One weight gradient alone (dW1 of the layer schedule).
-template <int BM, int BN>
-__global__ __launch_bounds__(kThreads) void wgrad1_kernel(WgradArgs a) {
-  extern __shared__ __attribute__((aligned(1024))) char ring[];
-  wgrad_list<BM, BN>(a, 0, ring);
 }
 
 // FP8 weight gradients. Both operands hold, per expert, the columns of its rows (every chunk's)
@@ -800,38 +127,8 @@ __global__ __launch_bounds__(kThreads) void wgrad_fp8_kernel(WgradFp8Args a, Wgr
   wgrad_fp8_list<BM, BN>(b, f, ring);
 }
 
-// A row-grouped GEMM and an independent weight gradient in one launch (the last chunk's gate/up
-// dgrad with dW2, whose tiles fill the dgrad's last round).
-template <int BM1, int BN1, int MODE1, int BM, int BN>
-__global__ __launch_bounds__(kThreads) void rows_wgrad_kernel(RowsArgs r, WgradArgs a) {
-  __shared__ RowsShared sh;
-  extern __shared__ __attribute__((aligned(1024))) char ring[];
-  const int f = rows_list<BM1, BN1, MODE1, false>(r, 0, sh, ring);
-  wgrad_list<BM, BN>(a, f, ring);
-}
-
 // ---------------------------------------------------------------------------------------------
 // Launchers
-
-// Compute units of the current device (cached per device; the grids of the persistent kernels
-// hold at most one workgroup per CU).
-static int cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
-static int64_t persistent_grid(int64_t tiles_bound) {
-  const int64_t cap = ((int64_t)cu_count() + 7) / 8 * 8;
-  const int64_t g = (tiles_bound + 7) / 8 * 8;
-  return g < cap ? g : cap;
-}
 
 // Grid bound: per chunk at most floor(P_c / BM) + E_local row tiles (every expert adds at most
 // one partial tile) times the column tiles; the device-side count decides the work.
@@ -853,77 +150,9 @@ hipError_t run_rows(const char* name, const RowsArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BM, int BN>
-hipError_t run_wgrad(const char* name, const WgradArgs& a, const WgradArgs& b, hipStream_t s) {
-  const size_t lds = wgrad_lds_bytes<BM, BN>();
-  auto k = wgrad_kernel<BM, BN>;
-  hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  auto tiles = [](const WgradArgs& w) {
-    return w.El > 0 ? (int64_t)w.El * ((w.M + BM - 1) / BM) * ((w.N + BN - 1) / BN) : 0;
-  };
-  const int64_t grid = persistent_grid(tiles(a) + tiles(b));
-  if (grid <= 0) return hipSuccess;
-  {
-    MOE_TRACE(name, s);
-    MOE_LAUNCH(k, dim3((unsigned)grid), dim3(kThreads), lds, s, a, b);
-  }
-  return hipGetLastError();
-}
-
 }  // namespace gg
 
 using namespace gg;
-
-// Argument sets of the BF16 expert GEMMs for chunks c0 .. c0 + nc - 1.
-static RowsArgs gateup_args(const ExpertGemm& g, int c0, int nc) {
-  RowsArgs a{};
-  a.A = g.xd; a.B = g.w1; a.C = (uint16_t*)g.h; a.C2 = (uint16_t*)g.gu;
-  a.lda = g.H; a.ldc = g.I; a.strideB = (int64_t)2 * g.I * g.H; a.K = g.H; a.N = g.I; a.I = g.I;
-  a.offsets = g.offsets; a.El = g.El; a.c0 = c0; a.nc = nc; a.P_c = g.P_c;
-  return a;
-}
-static RowsArgs down_args(const ExpertGemm& g, int c0, int nc) {
-  RowsArgs b{};
-  b.A = g.h; b.B = g.w2; b.C = (uint16_t*)g.yd;
-  b.lda = g.I; b.ldc = g.H; b.strideB = (int64_t)g.H * g.I; b.K = g.I; b.N = g.H; b.I = g.I;
-  b.offsets = g.offsets; b.El = g.El; b.c0 = c0; b.nc = nc; b.P_c = g.P_c;
-  return b;
-}
-static RowsArgs down_dgrad_args(const ExpertGemm& g, int c0, int nc) {
-  RowsArgs a{};
-  a.A = g.dyd; a.B = g.w2; a.C = (uint16_t*)g.dgu; a.aux = (const uint16_t*)g.gu;
-  a.lda = g.H; a.ldc = 2 * g.I; a.strideB = (int64_t)g.H * g.I; a.K = g.H; a.N = g.I; a.I = g.I;
-  a.offsets = g.offsets; a.El = g.El; a.c0 = c0; a.nc = nc; a.P_c = g.P_c;
-  return a;
-}
-static RowsArgs gateup_dgrad_args(const ExpertGemm& g, int c0, int nc) {
-  RowsArgs b{};
-  b.A = g.dgu; b.B = g.w1; b.C = (uint16_t*)g.dxd;
-  b.lda = 2 * g.I; b.ldc = g.H; b.strideB = (int64_t)2 * g.I * g.H; b.K = 2 * g.I; b.N = g.H; b.I = g.I;
-  b.offsets = g.offsets; b.El = g.El; b.c0 = c0; b.nc = nc; b.P_c = g.P_c;
-  return b;
-}
-// dW1[e] [2I, H] = sum dgu^T xd (the longer tile list, first) and dW2[e] [H, I] = sum dyd^T h
-static void wgrad_args(const ExpertGemm& g, WgradArgs& w1, WgradArgs& w2) {
-  w1 = WgradArgs{};
-  w1.A = (const uint16_t*)g.dgu; w1.B = (const uint16_t*)g.xd; w1.C = (uint16_t*)g.dw1; w1.lda = 2 * g.I;
-  w1.ldb = g.H; w1.strideC = (int64_t)2 * g.I * g.H; w1.M = 2 * g.I; w1.N = g.H; w1.offsets = g.offsets;
-  w1.El = g.El; w1.n_chunks = g.n_chunks; w1.P_c = g.P_c;
-  w2 = WgradArgs{};
-  w2.A = (const uint16_t*)g.dyd; w2.B = (const uint16_t*)g.h; w2.C = (uint16_t*)g.dw2; w2.lda = g.H;
-  w2.ldb = g.I; w2.strideC = (int64_t)g.H * g.I; w2.M = g.H; w2.N = g.I; w2.offsets = g.offsets;
-  w2.El = g.El; w2.n_chunks = g.n_chunks; w2.P_c = g.P_c;
-}
-
-// Row tiles a launch of this GEMM can hold at most: per chunk floor(P_c / BM) + E_local row tiles
-// (every expert adds at most one partial tile) times the column tiles; the device-side count
-// decides the work.
-template <int BM, int BN, int MODE>
-static int64_t rows_tiles_bound(const RowsArgs& a) {
-  const int outn = (MODE == kGateUp) ? BN / 2 : BN;
-  return (int64_t)a.nc * (a.P_c / BM + a.El) * ((a.N + outn - 1) / outn);
-}
 
 template <int BM1, int BN1, int MODE1, int BM2, int BN2, int MODE2>
 static hipError_t run_pair(const char* name, const RowsArgs& a, const RowsArgs& b, hipStream_t s) {
@@ -940,30 +169,6 @@ static hipError_t run_pair(const char* name, const RowsArgs& a, const RowsArgs& 
   }
   return hipGetLastError();
 }
-
-template <int BM1, int BN1, int MODE1, int BM, int BN>
-static hipError_t run_rows_wgrad(const char* name, const RowsArgs& r, const WgradArgs& a, hipStream_t s) {
-  const size_t l1 = rows_lds_bytes<BM1, BN1, MODE1>(), l2 = wgrad_lds_bytes<BM, BN>();
-  const size_t lds = l1 > l2 ? l1 : l2;
-  auto k = rows_wgrad_kernel<BM1, BN1, MODE1, BM, BN>;
-  hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  const int64_t tw = a.El > 0 ? (int64_t)a.El * ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) : 0;
-  const int64_t grid = persistent_grid(rows_tiles_bound<BM1, BN1, MODE1>(r) + tw);
-  if (grid <= 0) return hipSuccess;
-  {
-    MOE_TRACE(name, s);
-    MOE_LAUNCH(k, dim3((unsigned)grid), dim3(kThreads), lds, s, r, a);
-  }
-  return hipGetLastError();
-}
-
-// Tile shapes: 256 x 256 everywhere except down dgrad (128 x 256: its N = I gives few column
-// tiles, and 128-row tiles keep more CUs busy).
-#define MOE_GATEUP 256, 256, kGateUp
-#define MOE_DOWN 256, 256, kDown
-#define MOE_DDGRAD 128, 256, kDownBwd
-#define MOE_GUDGRAD 256, 256, kGateUpBwd
 
 hipError_t gg_expert_fwd_bf16(const void* xd, const void* w1, const void* w2, const int32_t* offsets,
                               void* gu, void* h, void* yd, int H, int I, int El, int c0, int nc,
@@ -987,17 +192,6 @@ hipError_t gg_expert_dgrad_bf16(const void* dyd, const void* gu, const void* w1,
   return run_rows<MOE_GUDGRAD, false>("gemm_gateup_dgrad", gateup_dgrad_args(g, c0, nc), s);
 }
 
-hipError_t gg_expert_wgrad_bf16(const void* dyd, const void* dgu, const void* xd, const void* h,
-                                const int32_t* offsets, void* dw1, void* dw2, int H, int I, int El,
-                                int n, int64_t P_c, hipStream_t s) {
-  ExpertGemm g{};
-  g.dyd = dyd; g.dgu = (void*)dgu; g.xd = xd; g.h = (void*)h; g.offsets = offsets; g.dw1 = dw1; g.dw2 = dw2;
-  g.H = H; g.I = I; g.El = El; g.n_chunks = n; g.P_c = P_c;
-  WgradArgs a, b;
-  wgrad_args(g, a, b);
-  return run_wgrad<256, 256>("gemm_wgrad", a, b, s);
-}
-
 // Launches of the layer schedule (one chunk each; the pairs take independent work of two steps).
 hipError_t gg_gateup(const ExpertGemm& g, int c, hipStream_t s) {
   return run_rows<MOE_GATEUP, false>("gemm_gateup_swiglu", gateup_args(g, c, 1), s);
@@ -1015,31 +209,6 @@ hipError_t gg_gateup_dgrad_then_down_dgrad(const ExpertGemm& g, int c, int c2, h
   return run_pair<MOE_GUDGRAD, MOE_DDGRAD>("gemm_gateup_dgrad+down_dgrad_swiglu", gateup_dgrad_args(g, c, 1),
                                            down_dgrad_args(g, c2, 1), s);
 }
-hipError_t gg_gateup_dgrad_then_wgrad2(const ExpertGemm& g, int c, hipStream_t s) {
-  WgradArgs w1, w2;
-  wgrad_args(g, w1, w2);
-  return run_rows_wgrad<MOE_GUDGRAD, 256, 256>("gemm_gateup_dgrad+wgrad_w2", gateup_dgrad_args(g, c, 1), w2, s);
-}
-hipError_t gg_wgrad1(const ExpertGemm& g, hipStream_t s) {
-  WgradArgs w1, w2;
-  wgrad_args(g, w1, w2);
-  const size_t lds = wgrad_lds_bytes<256, 256>();
-  auto k = wgrad1_kernel<256, 256>;
-  hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  const int64_t grid = persistent_grid(w1.El > 0 ? (int64_t)w1.El * ((w1.M + 255) / 256) * ((w1.N + 255) / 256) : 0);
-  if (grid <= 0) return hipSuccess;
-  {
-    MOE_TRACE("gemm_wgrad_w1", s);
-    MOE_LAUNCH(k, dim3((unsigned)grid), dim3(kThreads), lds, s, w1);
-  }
-  return hipGetLastError();
-}
-
-#undef MOE_GATEUP
-#undef MOE_DOWN
-#undef MOE_DDGRAD
-#undef MOE_GUDGRAD
 
 // FP8 forward: gate/up on FP8 MFMA with s_row * s_col dequantisation and SwiGLU -> h (BF16);
 // h quantised per row to e4m3 (codes stored after the BF16 values in the h buffer); down on FP8

@@ -89,7 +89,7 @@ hipError_t launch_expert_dgrad(bool bf16, const void* dyd, const void* gu, const
                                int I, int El, int c0, int nc, int64_t P_c, hipStream_t s);
 hipError_t launch_expert_wgrad(bool bf16, const void* dyd, const void* dgu, const void* xd,
                                const void* h, const int32_t* offsets, void* dw1, void* dw2, int H,
-                               int I, int El, int n, int64_t P_c, hipStream_t s);
+                               int I, int El, int n, int64_t P_c, void* wgrad_ws, hipStream_t s);
 // BF16 grouped GEMMs on the direct-to-LDS MFMA engine (grouped_gemm.hip)
 hipError_t gg_expert_fwd_bf16(const void* xd, const void* w1, const void* w2, const int32_t* offsets,
                               void* gu, void* h, void* yd, int H, int I, int El, int c0, int nc,
@@ -99,7 +99,7 @@ hipError_t gg_expert_dgrad_bf16(const void* dyd, const void* gu, const void* w1,
                                 int c0, int nc, int64_t P_c, hipStream_t s);
 hipError_t gg_expert_wgrad_bf16(const void* dyd, const void* dgu, const void* xd, const void* h,
                                 const int32_t* offsets, void* dw1, void* dw2, int H, int I, int El,
-                                int n, int64_t P_c, hipStream_t s);
+                                int n, int64_t P_c, void* wgrad_ws, hipStream_t s);
 // Operands of the BF16 expert GEMMs as the layer schedule launches them (device pointers; the
 // ones a launch does not use may be NULL).
 struct ExpertGemm {
@@ -108,7 +108,11 @@ struct ExpertGemm {
   const int32_t* offsets;
   int H, I, El, n_chunks;
   int64_t P_c;
+  void* wgrad_ws;  // weight-gradient scratch (counters zero between launches), wgrad_scratch_bytes
 };
+// weight-gradient scratch: its size, and the bytes of its leading counters (zero when first used)
+int64_t wgrad_scratch_bytes(int H, int I, int El);
+int64_t wgrad_counter_bytes_of(int H, int I, int El);
 // One chunk's gate/up (+SwiGLU) or down GEMM; down of chunk c and gate/up of chunk c2 in one
 // persistent launch (independent work: the second fills the first's last round).
 hipError_t gg_gateup(const ExpertGemm& g, int c, hipStream_t s);

@@ -311,8 +311,10 @@ __global__ __launch_bounds__(kBlockThreads) void combine_kernel(
 
 // Combine backward: dyd[row_of[t][j]] = g_tj * dy[t]; dgates[t][j] = <dy[t], yd[row]> (FP32): each
 // thread's partial over its vectors, a wave sum, then the four waves' sums in order (no atomics).
+// The slots' yd loads are issued four at a time, and the kernel is capped at 64 VGPRs (eight waves
+// per SIMD) so that its waves fit beside the persistent expert GEMMs of the other stream.
 template <typename T, int K>
-__global__ __launch_bounds__(kBlockThreads) void combine_bwd_kernel(
+__global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(8))) void combine_bwd_kernel(
     const u32x4* __restrict__ dy, const u32x4* __restrict__ yd, const float* __restrict__ gates,
     const int32_t* __restrict__ row_of, u32x4* __restrict__ dyd, float* __restrict__ dgates,
     int64_t t0, int64_t t1, int64_t nvec) {
@@ -331,22 +333,27 @@ __global__ __launch_bounds__(kBlockThreads) void combine_bwd_kernel(
     for (int64_t i = threadIdx.x; i < nvec; i += kBlockThreads) {
       float d[V::N];
       V::to_f(dy[t * nvec + i], d);
-      u32x4 v[K];
+      constexpr int G = K < 4 ? K : 4;  // slots whose loads are in flight together
 #pragma unroll
-      for (int j = 0; j < K; ++j) {
-        const int32_t r = bcast_i(myrow, j);
-        if (r >= 0) v[j] = yd[(int64_t)r * nvec + i];
-      }
+      for (int j0 = 0; j0 < K; j0 += G) {
+        u32x4 v[G];
 #pragma unroll
-      for (int j = 0; j < K; ++j) {
-        const int32_t r = bcast_i(myrow, j);
-        if (r < 0) continue;
-        const float g = bcast_f(mygate, j);
-        float f[V::N], o[V::N];
-        V::to_f(v[j], f);
+        for (int jj = 0; jj < G && j0 + jj < K; ++jj) {
+          const int32_t r = bcast_i(myrow, j0 + jj);
+          if (r >= 0) v[jj] = yd[(int64_t)r * nvec + i];
+        }
 #pragma unroll
-        for (int q = 0; q < V::N; ++q) { dg[j] = fmaf(d[q], f[q], dg[j]); o[q] = g * d[q]; }
-        dyd[(int64_t)r * nvec + i] = V::from_f(o);
+        for (int jj = 0; jj < G && j0 + jj < K; ++jj) {
+          const int j = j0 + jj;
+          const int32_t r = bcast_i(myrow, j);
+          if (r < 0) continue;
+          const float g = bcast_f(mygate, j);
+          float f[V::N], o[V::N];
+          V::to_f(v[jj], f);
+#pragma unroll
+          for (int q = 0; q < V::N; ++q) { dg[j] = fmaf(d[q], f[q], dg[j]); o[q] = g * d[q]; }
+          dyd[(int64_t)r * nvec + i] = V::from_f(o);
+        }
       }
     }
   }
@@ -483,8 +490,11 @@ __global__ __launch_bounds__(256) void route_bwd_dlogits_kernel(
 }
 
 // Dispatch backward: dx[t] = RNE(sum_j local dxd[row_of[t][j]] + sum_j dlogits[t][e_j] W_r[e_j]).
+// Capped at 64 VGPRs (eight waves per SIMD): it runs on the aux stream beside the persistent
+// expert GEMMs, whose two waves per SIMD hold up to 448 of a SIMD's 512 VGPRs, so only a wave of at
+// most 64 VGPRs can share a CU with them instead of waiting for a GEMM workgroup to exit.
 template <typename T, int K>
-__global__ __launch_bounds__(256) void dispatch_bwd_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void dispatch_bwd_kernel(
     const u32x4* __restrict__ dxd, const int32_t* __restrict__ row_of, const int32_t* __restrict__ idx,
     const float* __restrict__ dlogits, const u32x4* __restrict__ w_r, u32x4* __restrict__ dx,
     int64_t t0, int64_t t1, int E, int64_t nvec) {

@@ -180,17 +180,24 @@ moe_status moe_route_bwd(const moe_desc* d, int chunk, const float* dgates, cons
 
 /* Expert FFN backward, input-gradient part, per chunk: dh = dyd W2; with s = sigmoid(G):
  * dG = dh * U * s * (1 + G (1 - s)), dU = dh * silu(G) (G, U read from gu);
- * dxd = [dG dU] W1. With chunk = -1 it then runs moe_expert_wgrad over every chunk. */
+ * dxd = [dG dU] W1. With chunk = -1 it then runs moe_expert_wgrad over every chunk (workspace is
+ * moe_expert_wgrad's; unused when chunk >= 0). */
 moe_status moe_expert_ffn_bwd(const moe_desc* d, int chunk, const void* dyd, const void* xd,
                               const void* gu, const void* h, const void* w1, const void* w2,
                               const int32_t* offsets, void* dgu, void* dxd, void* dw1, void* dw2,
-                              void* stream);
+                              void* workspace, void* stream);
 
 /* Expert weight gradients over the rows of every chunk in one FP32 reduction, converted once:
- * dW2[e] = sum_rows dyd^T h, dW1[e] = sum_rows dgu^T xd; an expert with no rows gets zeros. */
+ * dW2[e] = sum_rows dyd^T h, dW1[e] = sum_rows dgu^T xd; an expert with no rows gets zeros
+ * (ChunkedEP "Numerical status": FP32 accumulation across chunks before one conversion, read as
+ * applying to every weight gradient). An expert holding many more rows than the others has its
+ * row range split into parts whose FP32 partial tiles are summed in part order; the split depends
+ * only on the per-expert row counts, so the result is deterministic. workspace: the
+ * moe_workspace_bytes().workspace buffer (BF16 path); its first wgrad_zero_bytes bytes after the
+ * wgrad offset (counters) must be zero when first used, and every call leaves them zero. */
 moe_status moe_expert_wgrad(const moe_desc* d, const void* dyd, const void* dgu, const void* xd,
                             const void* h, const int32_t* offsets, void* dw1, void* dw2,
-                            void* stream);
+                            void* workspace, void* stream);
 
 /* FP8 input gradients (a reading: ChunkedEP "Summary" gives FP8 for the dispatched payloads of
  * the forward only; the backward applies the same per-row quantisation to its payloads). Needs a
@@ -308,7 +315,8 @@ typedef struct moe_tensors {
   /* backward buffers and outputs */
   void* dyd; float* dgates; float* dlogits; float* dwr_acc; void* dgu; void* dxd;
   void* dx; void* dw1; void* dw2; void* dwr;
-  /* scratch of moe_workspace_bytes().workspace bytes */
+  /* scratch of moe_workspace_bytes().workspace bytes (its weight-gradient counters zero when first
+   * used: see moe_workspace_sizes) */
   void* workspace;
   /* MOE_FLAG_FP8_DGRAD only (see moe_expert_dgrad_fp8): transposed FP8 weights and the quantised
    * backward payloads */
@@ -338,9 +346,13 @@ typedef struct moe_workspace_sizes {
   int64_t topk_idx, gates, counts, offsets, row_of, src_token;
   int64_t xd, xd_scale, gu, h, h_scale, yd, out;
   int64_t dyd, dgates, dlogits, dwr_acc, dgu, dxd, dx, dw1, dw2, dwr;
-  int64_t route_scratch, route_bwd_scratch, workspace; /* workspace = max of the scratches */
+  int64_t route_scratch, route_bwd_scratch, workspace; /* workspace: see wgrad_scratch below */
   int64_t w1t, w1t_scale, w2t, w2t_scale, dyd_q, dyd_scale, dgu_q, dgu_scale; /* MOE_FLAG_FP8_DGRAD */
   int64_t dyd_t, dyd_cs, dgu_t, dgu_cs, xd_t, xd_cs, h_t, h_cs;              /* MOE_FLAG_FP8_WGRAD */
+  /* the expert weight gradients' part of the workspace (BF16 path): it starts after the routing
+   * and router scratch at a 256-byte boundary; its first wgrad_zero_bytes bytes are counters that
+   * must be zero when the workspace is first used (every call leaves them zero) */
+  int64_t wgrad_scratch, wgrad_zero_bytes;
 } moe_workspace_sizes;
 moe_status moe_workspace_bytes(const moe_desc* d, moe_workspace_sizes* out);
 

@@ -159,16 +159,17 @@ def run_stages(mh, d, b, backward, s):
             else:
                 for c in range(d.n_chunks):
                     mh.moe_expert_ffn_bwd(d, c, b["dyd"], b["xd"], b["gu"], b["h"], b["w1"], b["w2"],
-                                          b["offsets"], b["dgu"], b["dxd"], None, None, s)
+                                          b["offsets"], b["dgu"], b["dxd"], None, None, None, s)
             if d.flags & mh.FLAG_FP8_WGRAD:
                 mh.moe_expert_wgrad_fp8(d, b["dyd"], b["dgu"], b["xd"], b["h"], b["offsets"], b["dyd_t"],
                                         b["dyd_cs"], b["dgu_t"], b["dgu_cs"], b["xd_t"], b["xd_cs"], b["h_t"],
                                         b["h_cs"], b["dw1"], b["dw2"], s)
             else:
-                mh.moe_expert_wgrad(d, b["dyd"], b["dgu"], b["xd"], b["h"], b["offsets"], b["dw1"], b["dw2"], s)
+                mh.moe_expert_wgrad(d, b["dyd"], b["dgu"], b["xd"], b["h"], b["offsets"], b["dw1"], b["dw2"],
+                                    b["workspace"], s)
         else:
             mh.moe_expert_ffn_bwd(d, -1, b["dyd"], b["xd"], b["gu"], b["h"], b["w1"], b["w2"], b["offsets"],
-                                  b["dgu"], b["dxd"], b["dw1"], b["dw2"], s)
+                                  b["dgu"], b["dxd"], b["dw1"], b["dw2"], b["workspace"], s)
         mh.moe_dispatch_bwd(d, -1, b["dxd"], b["row_of"], b["topk_idx"], b["dlogits"], b["w_r"], b["dx"], s)
 
 

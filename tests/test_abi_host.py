@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(mh.exported_symbols())
-    assert L.moe_abi_version() == 2
+    assert L.moe_abi_version() == 3
 
 
 @pytest.mark.parametrize("T,k,El,n", [(256, 2, 8, 1), (16384, 8, 16, 2), (32768, 8, 16, 2), (10, 3, 2, 3),
@@ -98,10 +98,16 @@ def test_workspace_bytes():
     assert ws["xd"] == P * 2048 * 2 and ws["yd"] == P * 2048 * 2 and ws["gu"] == P * 1536 * 2
     assert ws["out"] == 131072 * 2048 * 2                     # fresh [P_out, H] BF16 output
     assert ws["dw1"] == 16 * 1536 * 2048 * 2 and ws["dwr_acc"] == 128 * 2048 * 4
-    assert ws["workspace"] == max(ws["route_scratch"], ws["route_bwd_scratch"]) > 0
+    # routing / router scratch first, then the expert weight gradients' scratch at a 256-byte boundary:
+    # per-(expert, tile) counters of dW1 (6 x 8 tiles) and dW2 (8 x 3 tiles), then the partial slots
+    base = (max(ws["route_scratch"], ws["route_bwd_scratch"]) + 255) // 256 * 256
+    assert ws["wgrad_zero_bytes"] == (16 * (48 + 24) * 4 + 255) // 256 * 256
+    assert ws["wgrad_scratch"] == ws["wgrad_zero_bytes"] + 2 * 192 * 256 * 256 * 4
+    assert ws["workspace"] == base + ws["wgrad_scratch"] > 0
     f8 = mh.make_desc(T=16384, H=2048, I=768, E=128, E_local=16, k=8, n_chunks=2, dtype="fp8")
     ws8 = mh.workspace_bytes(f8)
     assert ws8["xd"] == P * 2048 and ws8["xd_scale"] == P * 4 and ws8["dw1"] == 0
+    assert ws8["wgrad_scratch"] == ws8["wgrad_zero_bytes"] == 0
 
 
 def test_fp8_dgrad_flag_validation_and_sizes():
@@ -228,11 +234,11 @@ def test_extents_past_a_buffer_descriptor_are_rejected():
     big = mh.make_desc(T=65536, H=7168, I=768, E=128, E_local=16, k=8, n_chunks=2)
     assert big.P_c * 7168 * 2 > 2**31 - 1
     mh.workspace_bytes(big)                       # the descriptor itself is valid
-    st, msg = _status_of(mh.moe_expert_wgrad, big, *([1] * 7), 0)
+    st, msg = _status_of(mh.moe_expert_wgrad, big, *([1] * 8), 0)
     assert st == -3 and "buffer descriptor" in msg, msg
     st, _ = _status_of(mh.moe_route_bwd, big, -1, *([1] * 8), 0)
     assert st == -3
-    st, _ = _status_of(mh.moe_expert_ffn_bwd, big, -1, *([1] * 11), 0)
+    st, _ = _status_of(mh.moe_expert_ffn_bwd, big, -1, *([1] * 12), 0)
     assert st == -3
     bufs = {f: 1 for f in mh.TENSOR_FIELDS}
     assert _status_of(mh.moe_layer_forward_backward, big, bufs, 0, 0)[0] == -3
