@@ -20,7 +20,8 @@ Modules:
             extent rules (rows rounded up to 4).
   ffn       vectorised forward and backward (per-expert matmuls).
   brute     per-token loops for tiny inputs (pins the vectorised forms).
-  fp8       OCP e4m3fn encode/decode and per-row absmax quantisation; FP8 forward.
+  fp8       OCP e4m3fn encode/decode, per-row and per-row-block absmax quantisation; FP8 forward,
+            FP8 input and weight gradients, the FP8 dispatch-backward payload.
   extent    live-extent tracker and combine-output workspace floor.
   stash     paged activation stash: page-aligned store/load of saved rows with live-prefix and
             page-tail masks.

@@ -11,7 +11,13 @@ Details" and "Verification") and say nothing more. Readings:
     these FP32 steps, so the codes are compared bit for bit;
   * activations are scaled per token (row of x), weights per output channel (row of W1[e] over
     H, row of W2[e] over I), h per dispatched row (over I) before the down projection;
-  * products accumulate in FP32 (exactly, here in FP64) and are dequantised by s_row * s_col.
+  * products accumulate in FP32 (exactly, here in FP64) and are dequantised by s_row * s_col;
+  * the dispatch-backward payload dxd (the survey's NEXT-1 asks for FP8 payloads in dispatch
+    backward; the pages give the FP8 payload only as a copy-kernel format) is the BF16 dxd row
+    quantised per block of 256 consecutive columns, each block taking the row quantiser's FP32
+    steps on its own values (a block-scaled row: H / 256 scales per row). The block is the column
+    tile of the GEMM that produces dxd, so the producer can quantise what it stores without a
+    second pass over the row.
 """
 from __future__ import annotations
 
@@ -101,6 +107,32 @@ def quantize_rows(a: np.ndarray):
 
 def dequantize_rows(codes, scale):
     return e4m3_decode(codes) * np.asarray(scale, dtype=np.float64)[..., None]
+
+
+DXD_BLOCK = 256
+
+
+def quantize_row_blocks(a: np.ndarray, block: int = DXD_BLOCK):
+    """Block-scaled rows: every run of `block` consecutive columns of a row (the last run may be
+    shorter) is quantised as one row by :func:`quantize_rows`. Returns codes uint8 [R, C] and
+    scale float32 [R, ceil(C / block)]."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    R, C = a.shape
+    nb = -(-C // block) if C else 0
+    codes = np.zeros((R, C), dtype=np.uint8)
+    scale = np.ones((R, nb), dtype=np.float32)
+    for b in range(nb):
+        c0, c1 = b * block, min(C, (b + 1) * block)
+        codes[:, c0:c1], scale[:, b] = quantize_rows(a[:, c0:c1])
+    return codes, scale
+
+
+def dequantize_row_blocks(codes, scale, block: int = DXD_BLOCK):
+    """Values of block-scaled rows: code value times its block's scale (FP64)."""
+    v = e4m3_decode(codes)
+    C = v.shape[-1]
+    col_scale = np.repeat(np.asarray(scale, dtype=np.float64), block, axis=-1)[..., :C]
+    return v * col_scale
 
 
 def quantize_cols_t(a: np.ndarray):
@@ -198,11 +230,22 @@ def ffn_wgrad_fp8(dyd, dgu, xd, h, offsets, P_c, El):
     return dw1, dw2
 
 
-def backward_fp8_dgrad(fwd: dict, x, dy, w1, w2, w_r, fp8_dgrad=True, fp8_wgrad=False):
+def dispatch_bwd_fp8(dxd, row_of, dlogits, w_r, block: int = DXD_BLOCK):
+    """Dispatch backward on the FP8 payload: dxd (exact values) is rounded to BF16, quantised per
+    row and column block (:func:`quantize_row_blocks`), and the dequantised rows replace dxd in
+    oracle.ffn.dispatch_bwd (router term unchanged)."""
+    from . import ffn
+    pay = dequantize_row_blocks(*quantize_row_blocks(bf16_round(np.asarray(dxd, dtype=np.float64)), block),
+                                block)
+    return ffn.dispatch_bwd(pay, row_of, dlogits, w_r)
+
+
+def backward_fp8_dgrad(fwd: dict, x, dy, w1, w2, w_r, fp8_dgrad=True, fp8_wgrad=False, fp8_dxd=False):
     """The layer backward (oracle.ffn.backward) with the expert FFN's input gradients and dW1 from
     :func:`ffn_bwd_fp8_dgrad` (fp8_dgrad) and/or the expert weight gradients from
-    :func:`ffn_wgrad_fp8` (fp8_wgrad); combine, routing and dispatch backward and the router
-    weight gradient are those of the BF16 backward, which does not depend on them."""
+    :func:`ffn_wgrad_fp8` (fp8_wgrad) and/or dx from the FP8 dispatch-backward payload
+    (:func:`dispatch_bwd_fp8`, fp8_dxd); combine, routing and the router weight gradient are those
+    of the BF16 backward, which does not depend on them."""
     from . import ffn
     base = ffn.backward(fwd, x, dy, w1, w2, w_r)
     out = dict(base)
@@ -211,6 +254,8 @@ def backward_fp8_dgrad(fwd: dict, x, dy, w1, w2, w_r, fp8_dgrad=True, fp8_wgrad=
                                               fwd["P_c"], w1, w2)
         dx = ffn.dispatch_bwd(dxd, fwd["row_of"], base["dlogits"], w_r)
         out.update(dgu=dgu, dxd=dxd, dx=dx, dw1=dw1, dw2=dw2)
+    if fp8_dxd:
+        out["dx"] = dispatch_bwd_fp8(out["dxd"], fwd["row_of"], base["dlogits"], w_r)
     if fp8_wgrad:
         out["dw1"], out["dw2"] = ffn_wgrad_fp8(out["dyd"], out["dgu"], fwd["xd"], fwd["h"], fwd["offsets"],
                                                fwd["P_c"], np.asarray(w1).shape[0])

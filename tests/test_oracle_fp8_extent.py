@@ -335,3 +335,92 @@ def test_fp8_wgrad_oracle_within_e4m3_bound():
         for got, want in ((dw2[e], w2), (dw1[e], w1)):
             err = np.linalg.norm(got - want) / np.linalg.norm(want)
             assert 1e-4 < err < 2.0 ** -4, err
+
+
+def test_quantize_row_blocks_one_block_is_the_row_quantiser():
+    rng = np.random.default_rng(11)
+    a = rng.standard_normal((40, 200)).astype(np.float32) * 3
+    for block in (200, 256, 1024):
+        c1, s1 = fp8.quantize_row_blocks(a, block)
+        c0, s0 = fp8.quantize_rows(a)
+        np.testing.assert_array_equal(c1, c0)
+        np.testing.assert_array_equal(s1[:, 0], s0)
+        assert s1.shape == (40, 1)
+
+
+def test_quantize_row_blocks_independent_bounded_ragged():
+    """600 columns = blocks of 256, 256 and a ragged 88; magnitudes differ by block, one block of
+    one row is all zero. Each block's maximum maps onto +-448, the error stays within the e4m3
+    bound of its own block scale, and changing one block leaves the others' codes and scales."""
+    rng = np.random.default_rng(12)
+    R, C, B = 24, 600, 256
+    mag = np.array([1e-3, 10.0, 0.5], np.float32)
+    a = rng.standard_normal((R, C)).astype(np.float32)
+    for b in range(3):
+        a[:, b * B:(b + 1) * B] *= mag[b]
+    a[7, B:2 * B] = 0
+    codes, scale = fp8.quantize_row_blocks(a)
+    assert codes.shape == (R, C) and scale.shape == (R, 3)
+    assert np.all(codes[7, B:2 * B] == 0) and scale[7, 1] == 1.0
+    deq = fp8.dequantize_row_blocks(codes, scale)
+    col_scale = np.repeat(scale.astype(np.float64), B, axis=1)[:, :C]
+    bound = 2.0 ** -4 * np.abs(a) + 2.0 ** -9 * col_scale * (1 + 1e-6)
+    assert np.all(np.abs(deq - a) <= bound)
+    for b in range(3):
+        top = np.abs(fp8.e4m3_decode(codes[:, b * B:(b + 1) * B])).max(1)
+        live = np.ones(R, bool)
+        if b == 1:
+            live[7] = False
+        assert np.all(top[live] == 448.0), b
+    # scales follow each block's own magnitude
+    assert np.all(scale[:, 0] < scale[np.arange(R) != 7, 1].min())
+    a2 = a.copy()
+    a2[:, B:2 * B] *= 3.0
+    c2, s2 = fp8.quantize_row_blocks(a2)
+    np.testing.assert_array_equal(c2[:, :B], codes[:, :B])
+    np.testing.assert_array_equal(c2[:, 2 * B:], codes[:, 2 * B:])
+    np.testing.assert_array_equal(s2[:, [0, 2]], scale[:, [0, 2]])
+
+
+def test_fp8_dxd_dispatch_bwd_exact_on_block_exact_rows():
+    """Rows whose every 256-column block holds values in {0, +-1/2, +-1} * 2^m plus one 3.5 * 2^m,
+    with m drawn per (row, block): the block scale is 2^m / 128 and every value is an e4m3 code
+    times it, so the FP8 payload is lossless and dispatch backward on it equals the BF16 one
+    exactly; a scale taken from the wrong block or row would break the equality."""
+    from oracle import ffn
+    rng = np.random.default_rng(13)
+    P, H, T, k, E = 40, 768, 12, 3, 8
+    m = rng.integers(-6, 4, size=(P, H // 256))
+    dxd = rng.choice([0.0, 0.5, -0.5, 1.0, -1.0], size=(P, H))
+    dxd[:, ::256] = 3.5
+    dxd *= np.repeat(2.0 ** m, 256, axis=1)
+    row_of = rng.permutation(P)[:T * k].reshape(T, k).astype(np.int32)
+    row_of[rng.random((T, k)) < 0.2] = -1
+    dlogits = rng.standard_normal((T, E))
+    w_r = rng.standard_normal((E, H))
+    np.testing.assert_array_equal(fp8.dispatch_bwd_fp8(dxd, row_of, dlogits, w_r),
+                                  ffn.dispatch_bwd(dxd, row_of, dlogits, w_r))
+    # and not when one block's scale is taken from its neighbour
+    codes, scale = fp8.quantize_row_blocks(dxd.astype(np.float32))
+    wrong = fp8.dequantize_row_blocks(codes, np.roll(scale, 1, axis=1))
+    assert not np.array_equal(wrong, dxd)
+
+
+def test_fp8_dxd_layer_backward_changes_only_dx():
+    """With the FP8 dispatch-backward payload every gradient but dx equals the BF16 backward's
+    exactly; dx moves by an e4m3-sized relative error."""
+    import oracle
+    from oracle.fp8 import backward_fp8_dgrad
+    from moe_inputs import MoeConfig, make_inputs
+    cfg = MoeConfig("fp8dxd", T=96, H=512, I=64, E=8, E_local=4, e0=2, k=2, n_chunks=2, dtype="bf16",
+                    seed_base=71, backward=True)
+    inp = make_inputs(cfg)
+    f = oracle.forward(inp["x"], inp["logits"], inp["w1"], inp["w2"], k=cfg.k, e0=cfg.e0,
+                       E_local=cfg.E_local, n_chunks=cfg.n_chunks)
+    exact = oracle.backward(f, inp["x"], inp["dy"], inp["w1"], inp["w2"], inp["w_r"])
+    q = backward_fp8_dgrad(f, inp["x"], inp["dy"], inp["w1"], inp["w2"], inp["w_r"], fp8_dgrad=False,
+                           fp8_dxd=True)
+    for name in ("dyd", "dgates", "dlogits", "dgu", "dxd", "dw1", "dw2", "dwr"):
+        np.testing.assert_array_equal(q[name], exact[name], err_msg=name)
+    err = np.linalg.norm(q["dx"] - exact["dx"]) / np.linalg.norm(exact["dx"])
+    assert 1e-4 < err < 2.0 ** -4, err
