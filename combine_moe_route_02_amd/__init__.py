@@ -37,6 +37,7 @@ class MoeDesc(Structure):
 
 FLAG_FP8_DGRAD = 1
 FLAG_FP8_WGRAD = 2
+FLAG_FP8_DXD = 4  # dxd as block-scaled e4m3 rows (codes, then per-256-column scales) in the dxd buffer
 
 
 TENSOR_FIELDS = ["x", "logits", "w1", "w1_scale", "w2", "w2_scale", "w_r", "dy",

@@ -54,7 +54,7 @@ constexpr int64_t kRsrcMax = 0x7fffffff;  // bytes one raw buffer descriptor add
 
 moe_status validate(const moe_desc* d) {
   if (!d) return fail(MOE_ERR_ARG, "descriptor is NULL");
-  if (d->flags & ~(MOE_FLAG_FP8_DGRAD | MOE_FLAG_FP8_WGRAD))
+  if (d->flags & ~(MOE_FLAG_FP8_DGRAD | MOE_FLAG_FP8_WGRAD | MOE_FLAG_FP8_DXD))
     return fail(MOE_ERR_ARG, "descriptor flags 0x%x hold an unknown bit", d->flags);
   if (d->dtype != MOE_F32 && d->dtype != MOE_BF16 && d->dtype != MOE_FP8_E4M3)
     return fail(MOE_ERR_ARG, "unknown dtype %d", d->dtype);
@@ -179,7 +179,7 @@ void* wgrad_ws(const moe_desc* d, void* workspace) {
 extern "C" {
 
 const char* moe_last_error(void) { return g_err.c_str(); }
-int32_t moe_abi_version(void) { return 3; }
+int32_t moe_abi_version(void) { return 4; }
 
 moe_status moe_required_extent(int64_t T, int32_t k, int32_t E_local, int32_t n_chunks, int64_t* P_c,
                                int64_t* P_out) {
@@ -367,6 +367,13 @@ moe_status moe_combine(const moe_desc* d, int chunk, const void* yd, const float
   return MOE_OK;
 }
 
+// MOE_FLAG_FP8_DXD: the dxd buffer [n_chunks * P_c, H] (BF16-sized) holds the block-scaled e4m3
+// rows: codes [n_chunks * P_c, H] from its start, then one FP32 scale per row and 256-column block.
+static float* dxd_scales(const moe_desc* d, const void* dxd) {
+  if (!(d->flags & MOE_FLAG_FP8_DXD) || !dxd) return nullptr;
+  return (float*)((char*)dxd + (int64_t)d->n_chunks * d->P_c * d->H);
+}
+
 static moe_status no_fp8_bwd(const moe_desc* d) {
   if (d->dtype == MOE_FP8_E4M3) return fail(MOE_ERR_UNSUPPORTED, "the FP8 payload path is forward only");
   return MOE_OK;
@@ -445,7 +452,7 @@ moe_status moe_expert_ffn_bwd(const moe_desc* d, int chunk, const void* dyd, con
   if (rows_of(d) == 0)
     return chunk < 0 ? moe_expert_wgrad(d, dyd, dgu, xd, h, offsets, dw1, dw2, workspace, stream) : MOE_OK;
   MOE_NEED(dyd); MOE_NEED(gu); MOE_NEED(w1); MOE_NEED(w2); MOE_NEED(offsets); MOE_NEED(dgu); MOE_NEED(dxd);
-  MOE_HIP(moe::launch_expert_dgrad(is_bf16_rows(d), dyd, gu, w1, w2, offsets, dgu, dxd, d->H, d->I,
+  MOE_HIP(moe::launch_expert_dgrad(is_bf16_rows(d), dyd, gu, w1, w2, offsets, dgu, dxd, dxd_scales(d, dxd), d->H, d->I,
                                    d->E_local, r.c0, r.nc, d->P_c, (hipStream_t)stream), "expert_dgrad");
   if (chunk < 0) return moe_expert_wgrad(d, dyd, dgu, xd, h, offsets, dw1, dw2, workspace, stream);
   return MOE_OK;
@@ -465,7 +472,7 @@ static moe_status expert_dgrad_fp8_impl(const moe_desc* d, int chunk, const void
   MOE_NEED(offsets); MOE_NEED(dyd_q); MOE_NEED(dyd_scale); MOE_NEED(dgu); MOE_NEED(dgu_q); MOE_NEED(dgu_scale);
   MOE_NEED(dxd);
   MOE_HIP(moe::launch_expert_dgrad_fp8(dyd, gu, w1t, w1t_scale, w2t, w2t_scale, offsets, dyd_q, dyd_scale, dgu,
-                                       dgu_q, dgu_scale, dxd, d->H, d->I, d->E_local, r.c0, r.nc, d->P_c,
+                                       dgu_q, dgu_scale, dxd, dxd_scales(d, dxd), d->H, d->I, d->E_local, r.c0, r.nc, d->P_c,
                                        (hipStream_t)stream, quantize_dyd),
           "expert_dgrad_fp8");
   return MOE_OK;
@@ -520,8 +527,9 @@ moe_status moe_dispatch_bwd(const moe_desc* d, int chunk, const void* dxd, const
   if (r.t1 <= r.t0) return MOE_OK;
   MOE_NEED(row_of); MOE_NEED(topk_idx); MOE_NEED(dlogits); MOE_NEED(w_r); MOE_NEED(dx);
   if (rows_of(d) > 0) MOE_NEED(dxd);
-  MOE_HIP(moe::launch_dispatch_bwd(is_bf16_rows(d), dxd, row_of, topk_idx, dlogits, w_r, dx, r.t0, r.t1,
-                                   d->k, d->E, (int64_t)d->H * elem_size(d->dtype), (hipStream_t)stream),
+  MOE_HIP(moe::launch_dispatch_bwd(is_bf16_rows(d), dxd, dxd_scales(d, dxd), row_of, topk_idx, dlogits, w_r, dx,
+                                   r.t0, r.t1, d->k, d->E, d->H, (int64_t)d->H * elem_size(d->dtype),
+                                   (hipStream_t)stream),
           "dispatch_bwd");
   return MOE_OK;
 }
@@ -791,12 +799,14 @@ static moe::ExpertGemm expert_gemm(const moe_desc* d, const moe_tensors* t) {
   g.dyd = t->dyd; g.dgu = t->dgu; g.dxd = t->dxd; g.dw1 = t->dw1; g.dw2 = t->dw2;
   g.offsets = t->offsets; g.H = d->H; g.I = d->I; g.El = d->E_local; g.n_chunks = d->n_chunks; g.P_c = d->P_c;
   g.wgrad_ws = wgrad_ws(d, t->workspace);
+  g.dxd_scales = dxd_scales(d, t->dxd);
   return g;
 }
 
 static bool merged_gemms(const moe_desc* d) { return d->dtype == MOE_BF16 && d->T > 0 && rows_of(d) > 0; }
-// the merged backward launches pair BF16 GEMMs; with an FP8 backward flag the backward runs per chunk
-static bool merged_bwd(const moe_desc* d) { return merged_gemms(d) && d->flags == 0; }
+// the merged backward launches pair BF16 GEMMs; with an FP8 GEMM flag the backward runs per chunk (FP8
+// dxd rows only change the gate/up dgrad's epilogue and dispatch backward, both in the merged launches)
+static bool merged_bwd(const moe_desc* d) { return merged_gemms(d) && (d->flags & ~MOE_FLAG_FP8_DXD) == 0; }
 
 //   compute: R0 D0 GU0 | wait(disp1) [DN0 GU1] | wait(disp2) [DN1 GU2] | ... | DN n-1, C n-1
 //   aux:     wait(disp0) R1 D1 | R2 D2, wait(ffn0) C0 | R3 D3, wait(ffn1) C1 | ...

@@ -105,4 +105,42 @@ MOE_DEV ChunkRange chunk_range(int64_t T, int n, int c) {
   return {a, b};
 }
 
+// FP8 conversion: OCP e4m3fn, round to nearest even; inputs are already within +-448.
+MOE_DEV uint32_t pack_fp8x4(float a, float b, float c, float d) {
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+  return (uint32_t)r;
+}
+
+MOE_DEV float clamp448(float v) { return fminf(fmaxf(v, -448.f), 448.f); }
+
+// Quantise one 16-byte BF16 vector (8 values) with multiplier inv -> 8 e4m3 codes.
+MOE_DEV uint2 quant8(const u32x4& v, float inv) {
+  float f[8] = {bf2f(v.x & 0xffff), bf2f(v.x >> 16), bf2f(v.y & 0xffff), bf2f(v.y >> 16),
+                bf2f(v.z & 0xffff), bf2f(v.z >> 16), bf2f(v.w & 0xffff), bf2f(v.w >> 16)};
+  uint2 q;
+  q.x = pack_fp8x4(clamp448(f[0] * inv), clamp448(f[1] * inv), clamp448(f[2] * inv), clamp448(f[3] * inv));
+  q.y = pack_fp8x4(clamp448(f[4] * inv), clamp448(f[5] * inv), clamp448(f[6] * inv), clamp448(f[7] * inv));
+  return q;
+}
+
+MOE_DEV float absmax8(const u32x4& v) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m = fmaxf(m, fabsf(bf2f(w[i] & 0xffff)));
+    m = fmaxf(m, fabsf(bf2f(w[i] >> 16)));
+  }
+  return m;
+}
+
+// Dequantise 8 e4m3 codes (OCP e4m3fn) times scale s.
+MOE_DEV void deq8(uint2 q, float s, float* f) {
+  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.x, false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.x, true);
+  const auto c = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.y, false), d = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.y, true);
+  f[0] = a[0] * s; f[1] = a[1] * s; f[2] = b[0] * s; f[3] = b[1] * s;
+  f[4] = c[0] * s; f[5] = c[1] * s; f[6] = d[0] * s; f[7] = d[1] * s;
+}
+
 }  // namespace moe

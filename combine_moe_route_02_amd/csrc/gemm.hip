@@ -520,10 +520,11 @@ hipError_t launch_expert_fwd(bool bf16, const void* xd, const void* w1, const vo
 }
 
 hipError_t launch_expert_dgrad(bool bf16, const void* dyd, const void* gu, const void* w1,
-                               const void* w2, const int32_t* offsets, void* dgu, void* dxd, int H,
-                               int I, int El, int c0, int nc, int64_t P_c, hipStream_t s) {
+                               const void* w2, const int32_t* offsets, void* dgu, void* dxd, float* dxd_scales,
+                               int H, int I, int El, int c0, int nc, int64_t P_c, hipStream_t s) {
   if (nc <= 0 || El <= 0) return hipSuccess;
-  if (bf16) return gg_expert_dgrad_bf16(dyd, gu, w1, w2, offsets, dgu, dxd, H, I, El, c0, nc, P_c, s);
+  if (bf16) return gg_expert_dgrad_bf16(dyd, gu, w1, w2, offsets, dgu, dxd, dxd_scales, H, I, El, c0, nc, P_c, s);
+  if (dxd_scales) return hipErrorInvalidValue;  // FP8 dxd rows are a BF16-path format
   SimtRowsArgs a{};
   a.A = (const float*)dyd; a.B = (const float*)w2; a.C = (float*)dgu; a.aux = (const float*)gu;
   a.lda = H; a.ldc = 2 * I; a.strideB = (int64_t)H * I; a.K = H; a.N = I; a.I = I;

@@ -282,6 +282,28 @@ MOE_DEV void load_staged(char* lds, const uint16_t* src, int64_t ld, int mvalid,
       *(uint4*)(lds + r * pitch<W>() + 16 * c) = *(const uint4*)(src + (int64_t)r * ld + 8 * c);
 }
 
+// Store rows < mvalid of a staged [BM, 256] BF16 tile as one column block of block-scaled FP8 rows:
+// per row, amax over its nvalid columns, codes RNE(v * (448 / amax)) (FP32 steps, saturated), the
+// scale amax / 448 (an all-zero block: codes 0, scale 1). A half-wave per row, 8 values per lane;
+// every lane of a wave runs the same trip count, so the 32-lane max reduction is never divergent.
+template <int BM, int W>
+MOE_DEV void store_staged_q(const char* lds, uint8_t* dst, int64_t ld, float* sc, int64_t ldcs, int mvalid,
+                            int nvalid, int tid) {
+  static_assert(W == 256, "one 256-column block per staged tile");
+  static_assert(BM % (2 * kWaves) == 0, "whole rows per half-wave");
+  const int lane = tid & 63, l32 = lane & 31;
+  for (int r = 2 * (tid >> 6) + (lane >> 5); r < BM; r += 2 * kWaves) {
+    const bool live = r < mvalid && 8 * l32 < nvalid;
+    u32x4 v{0u, 0u, 0u, 0u};
+    if (live) v = *(const u32x4*)(lds + r * pitch<W>() + 16 * l32);
+    float m = absmax8(v);
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    if (live) *(uint2*)(dst + (int64_t)r * ld + 8 * l32) = m > 0.f ? quant8(v, 448.0f / m) : make_uint2(0u, 0u);
+    if (l32 == 0 && r < mvalid) sc[(int64_t)r * ldcs] = m > 0.f ? m / 448.0f : 1.0f;
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // Row-grouped GEMMs (forward and input gradients):
 //   C[r0 + m][n] = sum_k A[r0 + m][k] * B_e(n, k) over the rows of local expert e in a chunk.
@@ -301,6 +323,11 @@ struct RowsArgs {
   const int32_t* offsets;
   int El, c0, nc;
   int64_t P_c;
+  // QOUT launches (block-scaled FP8 output instead of C): e4m3 codes [P, ldc] and one FP32 scale
+  // per row and 256-column block, [P, ldcs]
+  uint8_t* Cq;
+  float* Cs;
+  int64_t ldcs;
 };
 
 template <int BM, int BN, int MODE>
@@ -338,7 +365,7 @@ MOE_DEV int first_slot(int first) {
 
 // The tiles of one row-grouped GEMM from per-XCD slot `first` on; returns the slot after its
 // last. Every thread of the workgroup calls it (it contains barriers).
-template <int BM, int BN, int MODE, bool FP8>
+template <int BM, int BN, int MODE, bool FP8, bool QOUT = false>
 MOE_DEV int rows_list(const RowsArgs& a, int first, RowsShared& sh, char* ring) {
   constexpr int WTM = BM / kWM, WTN = BN / kWN, TM = WTM / 32, TN = WTN / 32;
   constexpr bool kSwiGLU = (MODE == kGateUp);
@@ -347,6 +374,7 @@ MOE_DEV int rows_list(const RowsArgs& a, int first, RowsShared& sh, char* ring) 
   constexpr int ES = FP8 ? 1 : 2;      // element bytes
   constexpr int OUTN = kSwiGLU ? BN / 2 : BN;
   static_assert(!(FP8 && MODE == kGateUpBwd), "FP8 gate/up dgrad runs as kDown on the transposed W1");
+  static_assert(!QOUT || ((MODE == kDown || MODE == kGateUpBwd) && BN == 256), "FP8 output: plain 256-wide tiles");
   int* s_pre = sh.pre;
   int64_t* s_r0 = sh.r0;
   int* s_len = sh.len;
@@ -576,7 +604,11 @@ MOE_DEV int rows_list(const RowsArgs& a, int first, RowsShared& sh, char* ring) 
             *(uint2*)(ring + (mrow + tm * 32) * pitch<W>() + 2 * nl) = pack4(v[0], v[1], v[2], v[3]);
           }
       lds_barrier();
-      store_staged<BM, W>(ring, a.C + r0 * a.ldc + n0, a.ldc, mvalid, nvalid, tid);
+      if constexpr (QOUT)
+        store_staged_q<BM, W>(ring, a.Cq + r0 * a.ldc + n0, a.ldc, a.Cs + r0 * a.ldcs + n0 / W, a.ldcs, mvalid,
+                              nvalid, tid);
+      else
+        store_staged<BM, W>(ring, a.C + r0 * a.ldc + n0, a.ldc, mvalid, nvalid, tid);
       lds_barrier();
     }
   }
@@ -630,7 +662,12 @@ inline RowsArgs down_dgrad_args(const ExpertGemm& g, int c0, int nc) {
 }
 inline RowsArgs gateup_dgrad_args(const ExpertGemm& g, int c0, int nc) {
   RowsArgs b{};
-  b.A = g.dgu; b.B = g.w1; b.C = (uint16_t*)g.dxd;
+  b.A = g.dgu; b.B = g.w1;
+  if (g.dxd_scales) {  // block-scaled FP8 dxd
+    b.Cq = (uint8_t*)g.dxd; b.Cs = g.dxd_scales; b.ldcs = (g.H + 255) / 256;
+  } else {
+    b.C = (uint16_t*)g.dxd;
+  }
   b.lda = 2 * g.I; b.ldc = g.H; b.strideB = (int64_t)2 * g.I * g.H; b.K = 2 * g.I; b.N = g.H; b.I = g.I;
   b.offsets = g.offsets; b.El = g.El; b.c0 = c0; b.nc = nc; b.P_c = g.P_c;
   return b;

@@ -20,20 +20,20 @@
 namespace moe {
 namespace gg {
 
-template <int BM, int BN, int MODE, bool FP8>
+template <int BM, int BN, int MODE, bool FP8, bool QOUT>
 __global__ __launch_bounds__(kThreads) void rows_kernel(RowsArgs a) {
   __shared__ RowsShared sh;
   extern __shared__ __attribute__((aligned(1024))) char ring[];
-  rows_list<BM, BN, MODE, FP8>(a, 0, sh, ring);
+  rows_list<BM, BN, MODE, FP8, QOUT>(a, 0, sh, ring);
 }
 
 // Two independent row-grouped GEMMs in one persistent launch: the second's tiles fill the
 // workgroups that the first leaves idle in its last round, and one kernel boundary goes away.
-template <int BM1, int BN1, int MODE1, int BM2, int BN2, int MODE2>
+template <int BM1, int BN1, int MODE1, int BM2, int BN2, int MODE2, bool Q1>
 __global__ __launch_bounds__(kThreads) void rows_pair_kernel(RowsArgs a, RowsArgs b) {
   __shared__ RowsShared sh;
   extern __shared__ __attribute__((aligned(1024))) char ring[];
-  const int f = rows_list<BM1, BN1, MODE1, false>(a, 0, sh, ring);
+  const int f = rows_list<BM1, BN1, MODE1, false, Q1>(a, 0, sh, ring);
   rows_list<BM2, BN2, MODE2, false>(b, f, sh, ring);
 }
 
@@ -132,10 +132,12 @@ __global__ __launch_bounds__(kThreads) void wgrad_fp8_kernel(WgradFp8Args a, Wgr
 
 // Grid bound: per chunk at most floor(P_c / BM) + E_local row tiles (every expert adds at most
 // one partial tile) times the column tiles; the device-side count decides the work.
+// QOUT: a.Cq set (block-scaled FP8 output, plain-store modes only).
 template <int BM, int BN, int MODE, bool FP8>
 hipError_t run_rows(const char* name, const RowsArgs& a, hipStream_t s) {
   const size_t lds = rows_lds_bytes<BM, BN, MODE>();
-  auto k = rows_kernel<BM, BN, MODE, FP8>;
+  constexpr bool kQ = (MODE == kDown || MODE == kGateUpBwd) && BN == 256;
+  auto k = (kQ && a.Cq) ? rows_kernel<BM, BN, MODE, FP8, kQ> : rows_kernel<BM, BN, MODE, FP8, false>;
   hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int outn = (MODE == kGateUp) ? BN / 2 : BN;
@@ -158,7 +160,9 @@ template <int BM1, int BN1, int MODE1, int BM2, int BN2, int MODE2>
 static hipError_t run_pair(const char* name, const RowsArgs& a, const RowsArgs& b, hipStream_t s) {
   const size_t l1 = rows_lds_bytes<BM1, BN1, MODE1>(), l2 = rows_lds_bytes<BM2, BN2, MODE2>();
   const size_t lds = l1 > l2 ? l1 : l2;
-  auto k = rows_pair_kernel<BM1, BN1, MODE1, BM2, BN2, MODE2>;
+  constexpr bool kQ = (MODE1 == kDown || MODE1 == kGateUpBwd) && BN1 == 256;
+  auto k = (kQ && a.Cq) ? rows_pair_kernel<BM1, BN1, MODE1, BM2, BN2, MODE2, kQ>
+                        : rows_pair_kernel<BM1, BN1, MODE1, BM2, BN2, MODE2, false>;
   hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int64_t grid = persistent_grid(rows_tiles_bound<BM1, BN1, MODE1>(a) + rows_tiles_bound<BM2, BN2, MODE2>(b));
@@ -182,10 +186,11 @@ hipError_t gg_expert_fwd_bf16(const void* xd, const void* w1, const void* w2, co
 }
 
 hipError_t gg_expert_dgrad_bf16(const void* dyd, const void* gu, const void* w1, const void* w2,
-                                const int32_t* offsets, void* dgu, void* dxd, int H, int I, int El,
-                                int c0, int nc, int64_t P_c, hipStream_t s) {
+                                const int32_t* offsets, void* dgu, void* dxd, float* dxd_scales, int H, int I,
+                                int El, int c0, int nc, int64_t P_c, hipStream_t s) {
   ExpertGemm g{};
   g.dyd = dyd; g.gu = (void*)gu; g.w1 = w1; g.w2 = w2; g.offsets = offsets; g.dgu = dgu; g.dxd = dxd;
+  g.dxd_scales = dxd_scales;
   g.H = H; g.I = I; g.El = El; g.P_c = P_c;
   hipError_t e = run_rows<MOE_DDGRAD, false>("gemm_down_dgrad_swiglu", down_dgrad_args(g, c0, nc), s);
   if (e != hipSuccess) return e;
@@ -290,8 +295,8 @@ hipError_t launch_expert_wgrad_fp8(const void* dyd, const void* dgu, const void*
 hipError_t launch_expert_dgrad_fp8(const void* dyd, const void* gu, const void* w1t, const float* w1t_scale,
                                    const void* w2t, const float* w2t_scale, const int32_t* offsets,
                                    void* dyd_q, float* dyd_scale, void* dgu, void* dgu_q, float* dgu_scale,
-                                   void* dxd, int H, int I, int El, int c0, int nc, int64_t P_c, hipStream_t s,
-                                   bool quantize_dyd) {
+                                   void* dxd, float* dxd_scales, int H, int I, int El, int c0, int nc, int64_t P_c,
+                                   hipStream_t s, bool quantize_dyd) {
   if (nc <= 0 || El <= 0) return hipSuccess;
   hipError_t e = hipSuccess;
   if (quantize_dyd) {
@@ -308,7 +313,12 @@ hipError_t launch_expert_dgrad_fp8(const void* dyd, const void* gu, const void* 
   e = launch_quantize_segments_fp8("quantize_dgu_fp8", dgu, dgu_q, dgu_scale, offsets, El, c0, nc, P_c, 2 * I, s);
   if (e != hipSuccess) return e;
   RowsArgs b{};
-  b.A = dgu_q; b.B = w1t; b.C = (uint16_t*)dxd;
+  b.A = dgu_q; b.B = w1t;
+  if (dxd_scales) {  // block-scaled FP8 dxd
+    b.Cq = (uint8_t*)dxd; b.Cs = dxd_scales; b.ldcs = (H + 255) / 256;
+  } else {
+    b.C = (uint16_t*)dxd;
+  }
   b.scale_a = dgu_scale; b.scale_b = w1t_scale; b.strideSB = H;
   b.lda = 2 * (int64_t)I; b.ldc = H; b.strideB = (int64_t)H * 2 * I; b.K = 2 * I; b.N = H; b.I = I;
   b.offsets = offsets; b.El = El; b.c0 = c0; b.nc = nc; b.P_c = P_c;

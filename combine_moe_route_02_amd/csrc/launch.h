@@ -42,9 +42,11 @@ hipError_t launch_combine_bwd(bool bf16, const void* dy, const void* yd, const f
 hipError_t launch_route_bwd_dlogits(const float* dgates, const float* gates, const int32_t* idx,
                                     float* dlogits, int64_t t0, int64_t t1, int K, int E,
                                     hipStream_t s);
-hipError_t launch_dispatch_bwd(bool bf16, const void* dxd, const int32_t* row_of, const int32_t* idx,
-                               const float* dlogits, const void* w_r, void* dx, int64_t t0,
-                               int64_t t1, int K, int E, int64_t row_bytes, hipStream_t s);
+// dxd_scales non-null: dxd holds block-scaled e4m3 rows (codes [., H], one FP32 scale per row
+// and 256-column block, dxd_scales [., ceil(H/256)]); BF16 payloads only
+hipError_t launch_dispatch_bwd(bool bf16, const void* dxd, const float* dxd_scales, const int32_t* row_of,
+                               const int32_t* idx, const float* dlogits, const void* w_r, void* dx, int64_t t0,
+                               int64_t t1, int K, int E, int H, int64_t row_bytes, hipStream_t s);
 
 // grouped GEMMs
 hipError_t launch_expert_fwd(bool bf16, const void* xd, const void* w1, const void* w2,
@@ -82,11 +84,12 @@ hipError_t launch_quantize_cols_fp8(const void* src, void* codes_t, float* scale
 hipError_t launch_expert_dgrad_fp8(const void* dyd, const void* gu, const void* w1t, const float* w1t_scale,
                                    const void* w2t, const float* w2t_scale, const int32_t* offsets,
                                    void* dyd_q, float* dyd_scale, void* dgu, void* dgu_q, float* dgu_scale,
-                                   void* dxd, int H, int I, int El, int c0, int nc, int64_t P_c, hipStream_t s,
-                                   bool quantize_dyd = true);  // false: dyd_q/dyd_scale already written
+                                   void* dxd, float* dxd_scales, int H, int I, int El, int c0, int nc, int64_t P_c,
+                                   hipStream_t s, bool quantize_dyd = true);  // false: dyd_q/dyd_scale written
+// dxd_scales non-null (BF16 only): dxd is written as block-scaled e4m3 rows (see launch_dispatch_bwd)
 hipError_t launch_expert_dgrad(bool bf16, const void* dyd, const void* gu, const void* w1,
-                               const void* w2, const int32_t* offsets, void* dgu, void* dxd, int H,
-                               int I, int El, int c0, int nc, int64_t P_c, hipStream_t s);
+                               const void* w2, const int32_t* offsets, void* dgu, void* dxd, float* dxd_scales,
+                               int H, int I, int El, int c0, int nc, int64_t P_c, hipStream_t s);
 hipError_t launch_expert_wgrad(bool bf16, const void* dyd, const void* dgu, const void* xd,
                                const void* h, const int32_t* offsets, void* dw1, void* dw2, int H,
                                int I, int El, int n, int64_t P_c, void* wgrad_ws, hipStream_t s);
@@ -95,8 +98,8 @@ hipError_t gg_expert_fwd_bf16(const void* xd, const void* w1, const void* w2, co
                               void* gu, void* h, void* yd, int H, int I, int El, int c0, int nc,
                               int64_t P_c, hipStream_t s);
 hipError_t gg_expert_dgrad_bf16(const void* dyd, const void* gu, const void* w1, const void* w2,
-                                const int32_t* offsets, void* dgu, void* dxd, int H, int I, int El,
-                                int c0, int nc, int64_t P_c, hipStream_t s);
+                                const int32_t* offsets, void* dgu, void* dxd, float* dxd_scales, int H, int I,
+                                int El, int c0, int nc, int64_t P_c, hipStream_t s);
 hipError_t gg_expert_wgrad_bf16(const void* dyd, const void* dgu, const void* xd, const void* h,
                                 const int32_t* offsets, void* dw1, void* dw2, int H, int I, int El,
                                 int n, int64_t P_c, void* wgrad_ws, hipStream_t s);
@@ -109,6 +112,7 @@ struct ExpertGemm {
   int H, I, El, n_chunks;
   int64_t P_c;
   void* wgrad_ws;  // weight-gradient scratch (counters zero between launches), wgrad_scratch_bytes
+  float* dxd_scales;  // non-null: dxd holds block-scaled e4m3 codes [P, H] and these scales [P, ceil(H/256)]
 };
 // weight-gradient scratch: its size, and the bytes of its leading counters (zero when first used)
 int64_t wgrad_scratch_bytes(int H, int I, int El);

@@ -49,35 +49,6 @@ __global__ __launch_bounds__(kBlockThreads) void dispatch_copy_kernel(
   }
 }
 
-// FP8 conversion: OCP e4m3fn, round to nearest even; inputs are already within +-448.
-MOE_DEV uint32_t pack_fp8x4(float a, float b, float c, float d) {
-  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
-  return (uint32_t)r;
-}
-
-MOE_DEV float clamp448(float v) { return fminf(fmaxf(v, -448.f), 448.f); }
-
-// Quantise one 16-byte BF16 vector (8 values) with multiplier inv -> 8 e4m3 codes.
-MOE_DEV uint2 quant8(const u32x4& v, float inv) {
-  float f[8] = {bf2f(v.x & 0xffff), bf2f(v.x >> 16), bf2f(v.y & 0xffff), bf2f(v.y >> 16),
-                bf2f(v.z & 0xffff), bf2f(v.z >> 16), bf2f(v.w & 0xffff), bf2f(v.w >> 16)};
-  uint2 q;
-  q.x = pack_fp8x4(clamp448(f[0] * inv), clamp448(f[1] * inv), clamp448(f[2] * inv), clamp448(f[3] * inv));
-  q.y = pack_fp8x4(clamp448(f[4] * inv), clamp448(f[5] * inv), clamp448(f[6] * inv), clamp448(f[7] * inv));
-  return q;
-}
-
-MOE_DEV float absmax8(const u32x4& v) {
-  uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  float m = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m = fmaxf(m, fabsf(bf2f(w[i] & 0xffff)));
-    m = fmaxf(m, fabsf(bf2f(w[i] >> 16)));
-  }
-  return m;
-}
 
 // Dispatch (FP8): per token absmax over the BF16 row, codes = e4m3(x * (448/amax)),
 // xd_scale[row] = amax/448 (1 for a zero row); h_scale[row] cleared. Row of <= 16 vectors/lane.
@@ -555,6 +526,77 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void d
   for (; i0 < nvec; i0 += 64) pass(i0, std::integral_constant<int, 1>());
 }
 
+// Dispatch backward on block-scaled FP8 dxd rows (e4m3 codes [., H], one FP32 scale per row and
+// 256-column block): dx[t] = RNE(sum_j deq(dxd[row_of[t][j]]) + sum_j dlogits[t][e_j] W_r[e_j]),
+// each code dequantised as code value * its block's scale in FP32, slots in ascending order. Eight
+// columns per lane and vector (8 code bytes, one BF16 vector of W_r and dx). Capped at 64 VGPRs like
+// the BF16 kernel.
+template <int K>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void dispatch_bwd_fp8_kernel(
+    const uint2* __restrict__ dxq, const float* __restrict__ dxs, const int32_t* __restrict__ row_of,
+    const int32_t* __restrict__ idx, const float* __restrict__ dlogits, const u32x4* __restrict__ w_r,
+    u32x4* __restrict__ dx, int64_t t0, int64_t t1, int E, int64_t nvec, int nblk) {
+  using V = Vec<uint16_t>;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = t0 + (int64_t)blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
+  if (t >= t1) return;
+  const int32_t myrow = lane < K ? row_of[t * K + lane] : -1;
+  const int myid = lane < K ? idx[t * K + lane] : 0;
+  const float mydl = lane < K ? dlogits[t * E + myid] : 0.f;
+  const uint64_t local = __ballot(myrow >= 0);
+  u32x4* dst = dx + t * nvec;
+  auto pass = [&](int64_t i0, auto nb) {
+    constexpr int NB = decltype(nb)::value;
+    float acc[NB][8];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[b][q] = 0.f;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      if (!((local >> j) & 1)) continue;
+      const int64_t row = bcast_i(myrow, j);
+      const uint2* src = dxq + row * nvec;
+      const float* sc = dxs + row * nblk;
+      uint2 c[NB];
+      float s[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        c[b] = src[i0 + 64 * b];
+        s[b] = sc[(i0 + 64 * b) >> 5];  // 32 vectors of 8 columns per 256-column block
+      }
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        float f[8];
+        deq8(c[b], s[b], f);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[b][q] += f[q];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const u32x4* wr = w_r + (int64_t)bcast_i(myid, j) * nvec;
+      const float dl = bcast_f(mydl, j);
+      u32x4 w[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) w[b] = wr[i0 + 64 * b];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        float f[8];
+        V::to_f(w[b], f);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[b][q] = fmaf(dl, f[q], acc[b][q]);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) dst[i0 + 64 * b] = V::from_f(acc[b]);
+  };
+  constexpr int NB2 = 2;  // vectors per lane in flight (the 64-VGPR cap spills at 4)
+  int64_t i0 = lane;
+  for (; i0 + 64 * (NB2 - 1) < nvec; i0 += 64 * NB2) pass(i0, std::integral_constant<int, NB2>());
+  for (; i0 < nvec; i0 += 64) pass(i0, std::integral_constant<int, 1>());
+}
+
 // ---------------------------------------------------------------------------------------------
 // Launchers. Token range [t0, t1); nvec = 16-byte vectors per row.
 static inline dim3 tok_grid(int64_t ntok) { return dim3((unsigned)((ntok + kTokPerBlock - 1) / kTokPerBlock)); }
@@ -800,10 +842,18 @@ hipError_t launch_route_bwd_dlogits(const float* dgates, const float* gates, con
   return hipGetLastError();
 }
 
-hipError_t launch_dispatch_bwd(bool bf16, const void* dxd, const int32_t* row_of, const int32_t* idx,
-                               const float* dlogits, const void* w_r, void* dx, int64_t t0,
-                               int64_t t1, int K, int E, int64_t row_bytes, hipStream_t s) {
+hipError_t launch_dispatch_bwd(bool bf16, const void* dxd, const float* dxd_scales, const int32_t* row_of,
+                               const int32_t* idx, const float* dlogits, const void* w_r, void* dx, int64_t t0,
+                               int64_t t1, int K, int E, int H, int64_t row_bytes, hipStream_t s) {
   if (t1 <= t0) return hipSuccess;
+  if (dxd_scales) {
+    if (!bf16 || H % 8) return hipErrorInvalidValue;
+    MOE_TRACE("dispatch_bwd_fp8", s);
+    MOE_SWITCH_K(K, MOE_LAUNCH((dispatch_bwd_fp8_kernel<KK>), tok_grid(t1 - t0), dim3(256), 0, s,
+                               (const uint2*)dxd, dxd_scales, row_of, idx, dlogits, (const u32x4*)w_r, (u32x4*)dx,
+                               t0, t1, E, (int64_t)H / 8, (H + 255) / 256));
+    return hipGetLastError();
+  }
   if (bf16)
     {
       MOE_TRACE("dispatch_bwd", s);

@@ -361,13 +361,13 @@ __global__ __launch_bounds__(kThreads) void wgrad1_kernel(WgradArgs a) {
 
 // A row-grouped GEMM and an independent weight gradient in one launch (the last chunk's gate/up
 // dgrad with dW2, whose tiles fill the dgrad's last round).
-template <int BM1, int BN1, int MODE1, int BM, int BN>
+template <int BM1, int BN1, int MODE1, int BM, int BN, bool Q1>
 __global__ __launch_bounds__(kThreads) void rows_wgrad_kernel(RowsArgs r, WgradArgs a) {
   // the row list's group table and the weight gradient's plan share LDS (the plan is built after
   // a barrier that follows the row list's last read of its table)
   __shared__ union { RowsShared rows; WgradPlan plan; } sh;
   extern __shared__ __attribute__((aligned(1024))) char ring[];
-  const int f = rows_list<BM1, BN1, MODE1, false>(r, 0, sh.rows, ring);
+  const int f = rows_list<BM1, BN1, MODE1, false, Q1>(r, 0, sh.rows, ring);
   wgrad_list<BM, BN>(a, f, ring, sh.plan);
 }
 
@@ -447,7 +447,8 @@ template <int BM1, int BN1, int MODE1, int BM, int BN>
 static hipError_t run_rows_wgrad(const char* name, const RowsArgs& r, const WgradArgs& a, hipStream_t s) {
   const size_t l1 = rows_lds_bytes<BM1, BN1, MODE1>(), l2 = wgrad_lds_bytes<BM, BN>();
   const size_t lds = l1 > l2 ? l1 : l2;
-  auto k = rows_wgrad_kernel<BM1, BN1, MODE1, BM, BN>;
+  constexpr bool kQ = (MODE1 == kDown || MODE1 == kGateUpBwd) && BN1 == 256;
+  auto k = (kQ && r.Cq) ? rows_wgrad_kernel<BM1, BN1, MODE1, BM, BN, kQ> : rows_wgrad_kernel<BM1, BN1, MODE1, BM, BN, false>;
   hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int64_t tw = a.El > 0 ? (int64_t)a.El * ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) + a.slots : 0;

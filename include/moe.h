@@ -94,6 +94,17 @@ typedef struct moe_desc {
 /* Expert weight gradients on FP8 MFMA (moe_expert_wgrad_fp8) in the layer backward; BF16 dtype
  * only. Independent of MOE_FLAG_FP8_DGRAD. */
 #define MOE_FLAG_FP8_WGRAD 2
+/* FP8 payload of dispatch backward (the survey's NEXT-1, FP8 payloads in dispatch backward; the
+ * token-row payload formats of torchtitan PR 5541, "AI-Generated Details"); BF16 dtype only,
+ * independent of the other two flags. The expert input-gradient calls (moe_expert_ffn_bwd,
+ * moe_expert_dgrad_fp8 and the layer primitives) then write dxd as block-scaled e4m3 rows and
+ * moe_dispatch_bwd reads them: the dxd buffer ([n_chunks * P_c, H] BF16-sized, caller-owned) holds
+ * the codes [n_chunks * P_c, H] (one byte each) from its start, then one FP32 scale per row and
+ * block of 256 columns ([n_chunks * P_c, ceil(H / 256)]). Each block is the BF16-rounded dxd values
+ * quantised with the row quantiser's FP32 steps (amax over the block; codes RNE(v * (448 / amax))
+ * saturated; scale amax / 448; an all-zero block stores codes 0 and scale 1). dx is the FP32 sum of
+ * code * scale over the token's local slots plus the router term, rounded once to BF16. */
+#define MOE_FLAG_FP8_DXD 4
 
 /* ---------------------------------------------------------------------------------------
  * Stage calls

@@ -28,7 +28,11 @@ import moe_inputs
 import oracle
 from oracle import fp8 as ofp8
 
-TOL = {"f32": (1e-5, 1e-5), "bf16": (5e-3, 2e-2), "fp8": (2e-2, 1.0)}
+TOL = {"f32": (1e-5, 1e-5), "bf16": (5e-3, 2e-2), "fp8": (2e-2, 1.0),
+       # two e4m3 quantisations in series (FP8 input gradients and the FP8 dxd payload): each
+       # re-quantises values that differ from the oracle's by the BF16 path's rounding, and each
+       # such stage measured 1.3-1.5e-2 on its own, so the bound adds one FP8 bound per stage
+       "fp8x2": (4e-2, 1.0)}
 
 
 def rel_l2(got, want):
@@ -188,7 +192,8 @@ def run_oracle(run: Run, backward: Optional[bool] = None):
         fl = run.desc.flags
         if fl:
             f["bwd"] = ofp8.backward_fp8_dgrad(f, inp["x"], inp["dy"], inp["w1"], inp["w2"], inp["w_r"],
-                                               fp8_dgrad=bool(fl & 1), fp8_wgrad=bool(fl & 2))
+                                               fp8_dgrad=bool(fl & 1), fp8_wgrad=bool(fl & 2),
+                                               fp8_dxd=bool(fl & 4))
         else:
             f["bwd"] = oracle.backward(f, inp["x"], inp["dy"], inp["w1"], inp["w2"], inp["w_r"])
     return f
@@ -248,10 +253,10 @@ def check_backward(run: Run, ref) -> Dict[str, float]:
     errs["dgates"] = assert_close("dgates", to_np(b["dgates"]), bw["dgates"], dt)
     errs["dlogits"] = assert_close("dlogits", to_np(b["dlogits"]), bw["dlogits"], dt)
     fl = run.desc.flags
-    dq = "fp8" if fl & 1 else dt    # FP8 input gradients
+    dq = ("fp8x2" if (fl & 5) == 5 else "fp8") if fl & 5 else dt  # FP8 input gradients, FP8 dxd payload
     wq = "fp8" if fl & 2 else dt    # FP8 weight gradients
     errs["dx"] = assert_close("dx", to_np(b["dx"]), bw["dx"], dq)
-    errs["dw1"] = assert_close("dw1", to_np(b["dw1"]), bw["dw1"], "fp8" if fl else dt)
+    errs["dw1"] = assert_close("dw1", to_np(b["dw1"]), bw["dw1"], "fp8" if fl & 3 else dt)
     errs["dw2"] = assert_close("dw2", to_np(b["dw2"]), bw["dw2"], wq)
     errs["dwr"] = assert_close("dwr", to_np(b["dwr"]), bw["dwr"], dt)
     return errs

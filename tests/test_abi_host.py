@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(mh.exported_symbols())
-    assert L.moe_abi_version() == 3
+    assert L.moe_abi_version() == 4
 
 
 @pytest.mark.parametrize("T,k,El,n", [(256, 2, 8, 1), (16384, 8, 16, 2), (32768, 8, 16, 2), (10, 3, 2, 3),
@@ -138,8 +138,17 @@ def test_fp8_wgrad_sizes():
     assert ws["dyd_t"] == ws["xd_t"] == 2048 * Kp and ws["h_t"] == 768 * Kp and ws["dgu_t"] == 1536 * Kp
     assert ws["dyd_cs"] == ws["xd_cs"] == 16 * 2048 * 4 and ws["h_cs"] == 16 * 768 * 4 and ws["dgu_cs"] == 16 * 1536 * 4
     assert ws["w1t"] > 0   # both flags at once
-    bad = mh.make_desc(T=64, H=128, I=64, E=8, E_local=4, k=2, n_chunks=1, flags=4)
+    bad = mh.make_desc(T=64, H=128, I=64, E=8, E_local=4, k=2, n_chunks=1, flags=8)
     assert _status_of(mh.workspace_bytes, bad)[0] == -1
+    # the FP8 dxd payload flag: accepted with the BF16 dtype, with or without the others, and the
+    # sizes do not change (the payload fits the BF16 dxd buffer)
+    for fl in (mh.FLAG_FP8_DXD, mh.FLAG_FP8_DXD | mh.FLAG_FP8_DGRAD | mh.FLAG_FP8_WGRAD):
+        q = mh.make_desc(T=64, H=320, I=64, E=8, E_local=4, k=2, n_chunks=2, flags=fl)
+        plain = mh.make_desc(T=64, H=320, I=64, E=8, E_local=4, k=2, n_chunks=2, flags=fl & ~mh.FLAG_FP8_DXD)
+        assert mh.workspace_bytes(q) == mh.workspace_bytes(plain)
+    assert 4 * ((320 + 255) // 256) <= 2 * 320 - 320  # scales fit after the codes in a BF16 row
+    f32dxd = mh.make_desc(T=64, H=128, I=64, E=8, E_local=4, k=2, n_chunks=1, dtype="f32", flags=mh.FLAG_FP8_DXD)
+    assert _status_of(mh.workspace_bytes, f32dxd)[0] == -3
     f32 = mh.make_desc(T=64, H=128, I=64, E=8, E_local=4, k=2, n_chunks=1, dtype="f32")
     assert _status_of(mh.moe_expert_wgrad_fp8, f32, *([1] * 15), 0)[0] == -3
 
