@@ -7,19 +7,23 @@
 // the selected logits. The permutation is the stable sort of (token, slot) pairs by expert inside
 // each chunk: within an expert, rows follow ascending token index.
 //
-// Two launches per chunk range, both deterministic (route_topk, or route_proj_topk when routing
-// starts from x and the router weight):
+// Two or three launches per chunk range, all deterministic (route_topk, or route_proj_topk when
+// routing starts from x and the router weight):
 //   route_topk   16 lanes per token (4 tokens per wave, 16 tokens per 256-thread block). Each
 //                lane keeps a sorted top-K list of its share of the experts as 64-bit keys
 //                (order-preserving logit bits above the complemented expert index, so ties go to
 //                the lower index), then K rounds of a 16-lane max merge the lists. A histogram
 //                over all E experts per 16 tokens is summed in LDS with integer atomics (the sum
 //                does not depend on their order).
-//   route_layout per 64-token block: rows that earlier tokens of the chunk give each local expert
-//                (one wave per expert, lanes over the 16-token histograms), local offsets, then
-//                each token's rank among
+//   route_scan   (chunks of more than 128 64-token blocks) one wave per expert and chunk: the
+//                chunk's total per expert (counts) and, per 64-token block, the rows that the
+//                chunk's earlier blocks give the expert (an exclusive scan of the block sums, one
+//                block per lane), so the work is linear in the chunk's tokens.
+//   route_layout per 64-token block: local offsets from the counts, then each token's rank among
 //                the block's earlier tokens choosing the same expert from a 64-bit ballot mask
-//                (popcount below the lane); one wave per top-k slot.
+//                (popcount below the lane) plus the rows of the earlier blocks; one wave per top-k
+//                slot. For shorter chunks the block sums the earlier blocks' histograms itself
+//                (one launch fewer).
 #include <mutex>
 #include <type_traits>
 
@@ -279,11 +283,52 @@ __global__ __launch_bounds__(kRxThreads) void route_proj_topk_kernel(
     block_hist[((int64_t)c * E + i % E) * nh + 2 * bl + i / E] = hist[i];
 }
 
+// Per chunk c and expert e (one wave each): counts[c][e] = the chunk's rows of e, and
+// pre[c][e][b] = rows of e in the chunk's 64-token blocks before b. Lane l of an iteration owns
+// block b0 + l, whose four 16-token histograms it reads as one 16-byte load.
+constexpr int kScanThreads = 1024;
+__global__ __launch_bounds__(kScanThreads) void route_scan_kernel(const int32_t* __restrict__ block_hist,
+                                                                   int32_t* __restrict__ pre,
+                                                                   int32_t* __restrict__ counts, int E,
+                                                                   int chunk0, int nbpc) {
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * (kScanThreads / 64) + (threadIdx.x >> 6);
+  const int c = chunk0 + blockIdx.y;
+  if (e >= E) return;
+  const int nh = nbpc * kSub;
+  const int4* he = (const int4*)(block_hist + ((int64_t)c * E + e) * nh);
+  int32_t* pe = pre + ((int64_t)c * E + e) * nbpc;
+  int carry = 0;
+  for (int b0 = 0; b0 < nbpc; b0 += 64) {
+    const int b = b0 + lane;
+    int v = 0;
+    if (b < nbpc) {
+      const int4 h = he[b];
+      v = h.x + h.y + h.z + h.w;
+    }
+    int incl = v;  // inclusive scan over the wave's lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += u;
+    }
+    if (b < nbpc) pe[b] = carry + incl - v;
+    carry += __shfl(incl, 63, 64);
+  }
+  if (lane == 0) counts[(int64_t)c * E + e] = carry;
+}
+
+// kScanned: the prefixes and counts come from route_scan (long chunks). Otherwise (chunks of at
+// most kLayoutDirectBlocks blocks) each block sums the histograms before it itself, one wave per
+// local expert, and the blocks share the counts of all E experts between them: quadratic in the
+// chunk length but one launch fewer, which is the cheaper form for short chunks.
+constexpr int kLayoutDirectBlocks = 128;
+template <bool kScanned>
 __global__ __launch_bounds__(kRouteThreads) void route_layout_kernel(
-    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ block_hist,
+    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ block_hist, const int32_t* __restrict__ pre,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ row_of,
-    int32_t* __restrict__ src_token, int64_t T, int E, int e0, int El, int K, int n, int chunk0,
-    int nbpc, int64_t P_c) {
+    int32_t* __restrict__ src_token, int64_t T, int E, int e0, int El, int K, int n, int chunk0, int nbpc,
+    int64_t P_c) {
   extern __shared__ unsigned char smem[];
   // layout: base[El] int, off[El+1] int, mask[El] u64
   int* base = (int*)smem;
@@ -295,28 +340,50 @@ __global__ __launch_bounds__(kRouteThreads) void route_layout_kernel(
   const int c = chunk0 + blockIdx.x / nbpc;
   const int bl = blockIdx.x % nbpc;
   const ChunkRange cr = chunk_range(T, n, c);
-  const int nh = nbpc * kSub;  // 16-token histograms of the chunk
-  const int32_t* bh = block_hist + (int64_t)c * E * nh;  // [E][nh]
 
-  // one wave per local expert: rows owned by earlier tokens of this chunk, and the chunk total
-  for (int el = wave; el < El; el += kWaves) {
-    int before = 0, total = 0;
-    const int32_t* he = bh + (int64_t)(e0 + el) * nh;
-    for (int b0 = 0; b0 < nh; b0 += 256) {  // four loads in flight per lane
-      int h[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) h[u] = (b0 + 64 * u + lane < nh) ? he[b0 + 64 * u + lane] : 0;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        before += (b0 + 64 * u + lane < bl * kSub) ? h[u] : 0;
-        total += h[u];
-      }
+  if constexpr (kScanned) {
+    for (int el = tid; el < El; el += kRouteThreads) {
+      base[el] = pre[((int64_t)c * E + e0 + el) * nbpc + bl];
+      off[el + 1] = counts[(int64_t)c * E + e0 + el];
+      mask[el] = 0;
     }
-    before = wave_sum_int(before);
-    total = wave_sum_int(total);
-    if (lane == 0) { base[el] = before; off[el + 1] = total; }
+  } else {
+    const int nh = nbpc * kSub;  // 16-token histograms of the chunk
+    const int32_t* bh = block_hist + (int64_t)c * E * nh;  // [E][nh]
+    // one wave per local expert: rows owned by earlier tokens of this chunk, and the chunk total
+    for (int el = wave; el < El; el += kWaves) {
+      int before = 0, total = 0;
+      const int32_t* he = bh + (int64_t)(e0 + el) * nh;
+      for (int b0 = 0; b0 < nh; b0 += 256) {  // four loads in flight per lane
+        int h[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) h[u] = (b0 + 64 * u + lane < nh) ? he[b0 + 64 * u + lane] : 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          before += (b0 + 64 * u + lane < bl * kSub) ? h[u] : 0;
+          total += h[u];
+        }
+      }
+      before = wave_sum_int(before);
+      total = wave_sum_int(total);
+      if (lane == 0) { base[el] = before; off[el + 1] = total; }
+    }
+    for (int el = tid; el < El; el += kRouteThreads) mask[el] = 0;
+    // per-expert counts over all E experts, spread over the chunk's blocks, one wave per expert
+    for (int e = bl + nbpc * wave; e < E; e += nbpc * kWaves) {
+      const int32_t* he = bh + (int64_t)e * nh;
+      int total = 0;
+      for (int b0 = 0; b0 < nh; b0 += 256) {
+        int h[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) h[u] = (b0 + 64 * u + lane < nh) ? he[b0 + 64 * u + lane] : 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) total += h[u];
+      }
+      total = wave_sum_int(total);
+      if (lane == 0) counts[(int64_t)c * E + e] = total;
+    }
   }
-  for (int el = tid; el < El; el += kRouteThreads) mask[el] = 0;
   __syncthreads();
   if (tid == 0) {  // exclusive scan over the local experts
     int run = 0;
@@ -325,21 +392,6 @@ __global__ __launch_bounds__(kRouteThreads) void route_layout_kernel(
   }
   __syncthreads();
   const int N_c = off[El];
-  // per-expert counts over all E experts, spread over the chunk's blocks, one wave per expert
-  // (integer sums: the order does not matter)
-  for (int e = bl + nbpc * wave; e < E; e += nbpc * kWaves) {
-    const int32_t* he = bh + (int64_t)e * nh;
-    int total = 0;
-    for (int b0 = 0; b0 < nh; b0 += 256) {
-      int h[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) h[u] = (b0 + 64 * u + lane < nh) ? he[b0 + 64 * u + lane] : 0;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) total += h[u];
-    }
-    total = wave_sum_int(total);
-    if (lane == 0) counts[(int64_t)c * E + e] = total;
-  }
   if (bl == 0)
     for (int el = tid; el <= El; el += kRouteThreads) offsets[(int64_t)c * (El + 1) + el] = off[el];
 
@@ -403,19 +455,35 @@ int route_blocks_per_chunk(int64_t T, int n) {
   return (int)(nb < 1 ? 1 : nb);
 }
 
+// Routing scratch: the 16-token histograms [n][E][nbpc * 4], then the per-64-token-block prefixes
+// [n][E][nbpc].
+static int64_t route_hist_ints(int64_t T, int n, int E) { return (int64_t)n * route_blocks_per_chunk(T, n) * kSub * E; }
 int64_t route_scratch_bytes(int64_t T, int n, int E) {
-  return (int64_t)n * route_blocks_per_chunk(T, n) * kSub * E * (int64_t)sizeof(int32_t);
+  return (route_hist_ints(T, n, E) + (int64_t)n * route_blocks_per_chunk(T, n) * E) * (int64_t)sizeof(int32_t);
 }
 
-static hipError_t launch_layout(const int32_t* topk_idx, const int32_t* scratch, int32_t* counts,
+static hipError_t launch_layout(const int32_t* topk_idx, int32_t* scratch, int32_t* counts,
                                int32_t* offsets, int32_t* row_of, int32_t* src_token, int64_t T, int E,
                                int e0, int El, int K, int n, int chunk0, int nchunks, int64_t P_c,
                                hipStream_t s) {
   const int nbpc = route_blocks_per_chunk(T, n);
+  int32_t* pre = scratch + route_hist_ints(T, n, E);
+  const bool scanned = nbpc > kLayoutDirectBlocks;
+  if (scanned) {
+    MOE_TRACE("route_scan", s);
+    MOE_LAUNCH(route_scan_kernel, dim3((unsigned)((E + kScanThreads / 64 - 1) / (kScanThreads / 64)), (unsigned)nchunks),
+               dim3(kScanThreads), 0, s, scratch, pre, counts, E, chunk0, nbpc);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   size_t sm2 = (size_t)El * 4 + (size_t)(El + 1) * 4 + 8 + (size_t)El * 8;
   MOE_TRACE("route_layout", s);
-  MOE_LAUNCH(route_layout_kernel, dim3(nbpc * nchunks), dim3(kRouteThreads), sm2, s, topk_idx, scratch,
-                     counts, offsets, row_of, src_token, T, E, e0, El, K, n, chunk0, nbpc, P_c);
+  if (scanned)
+    MOE_LAUNCH(route_layout_kernel<true>, dim3(nbpc * nchunks), dim3(kRouteThreads), sm2, s, topk_idx, scratch,
+               pre, counts, offsets, row_of, src_token, T, E, e0, El, K, n, chunk0, nbpc, P_c);
+  else
+    MOE_LAUNCH(route_layout_kernel<false>, dim3(nbpc * nchunks), dim3(kRouteThreads), sm2, s, topk_idx, scratch,
+               pre, counts, offsets, row_of, src_token, T, E, e0, El, K, n, chunk0, nbpc, P_c);
   return hipGetLastError();
 }
 

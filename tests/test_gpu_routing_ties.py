@@ -7,8 +7,9 @@ logits rounded to multiples of 0.5, so exact ties are everywhere, including betw
 (k+1)-th largest logit of most rows, with zeros of both signs, NaN entries, an all-zero row and a
 row whose last selected slot falls among -inf and NaN entries. The kernel's top-k indices,
 counts, offsets, row_of and src_token must equal the oracle's bit for bit and the gates must
-agree within 1e-6, through the stage call and through the layer primitive, at small shapes and at
-the 16K-token one-rank share."""
+agree within 1e-6, through the stage call and through the layer primitive, at small shapes, at
+the 16K-token one-rank share, and on chunks long enough for the scanned layout (more than 128
+blocks of 64 tokens)."""
 import numpy as np
 import pytest
 
@@ -146,3 +147,28 @@ def test_full_16k_tied_logits_routing_bitwise():
     # the stage call gives the same integers
     d, b = _route_only(cfg, inp["logits"])
     _check_route(cfg, d, b, inp["logits"])
+
+
+LONG_CHUNKS = [
+    # chunks of more than 128 64-token blocks take the scanned layout (route_scan, then the
+    # layout reads each block's prefix); one just past the switch, one chunk, and a long one
+    MoeConfig("long_n1_8256", T=8256, H=128, I=64, E=64, E_local=16, e0=8, k=8, n_chunks=1, dtype="bf16",
+              seed_base=570),
+    MoeConfig("long_n2_40000", T=40000, H=128, I=64, E=128, E_local=16, e0=112, k=8, n_chunks=2, dtype="bf16",
+              seed_base=580),
+    MoeConfig("long_n3_zipf", T=30001, H=128, I=64, E=32, E_local=8, e0=0, k=6, n_chunks=3, dtype="bf16",
+              seed_base=590, zipf_s=1.2, n_empty=2),
+]
+
+
+@pytest.mark.parametrize("cfg", LONG_CHUNKS, ids=[c.name for c in LONG_CHUNKS])
+def test_route_long_chunks_scanned_layout(cfg):
+    """Routing of long chunks (the scanned layout) on tie-heavy and on Zipf-biased logits:
+    integers bitwise against the oracle."""
+    _require_gpu()
+    for lg in (moe_inputs.make_tie_logits(cfg), moe_inputs.make_inputs(cfg, parts=("logits",))["logits"]):
+        d, b = _route_only(cfg, lg)
+        nbpc = -(-(-(-cfg.T // cfg.n_chunks)) // 64)
+        assert nbpc > 128, nbpc
+        print(f"[long] {cfg.name} blocks per chunk {nbpc}", flush=True)
+        _check_route(cfg, d, b, lg)
