@@ -28,7 +28,6 @@ METRIC = "MoE layer tokens/s (fwd, fwd+bwd) @16K tok top-k8; %HBM BW, %MFMA peak
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense BF16 MFMA, TFLOP/s
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
-PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X vector FP32
 
 # launch-log name -> (source file under the package's csrc/, substring of the kernel symbol that
 # rocprofv3 reports for it)

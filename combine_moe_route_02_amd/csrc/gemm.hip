@@ -26,19 +26,7 @@ constexpr int kMaxGroups = 1024;
 // with the chunk XOR-swizzled by row % 8, so that 8 consecutive rows read at one chunk (MFMA
 // fragments) and the 8 chunks of one row (staging writes) each cover all banks; row % 8 does
 // not change between 32-row MFMA blocks, so their addresses differ by constants.
-#ifndef MOE_SWZ
-#define MOE_SWZ 0
-#endif
-MOE_DEV int swz(int row) {
-#if MOE_SWZ == 0
-  return row & 7;
-#elif MOE_SWZ == 1
-  return (row ^ (row >> 3) ^ (row >> 4)) & 7;
-#else
-  return (row ^ (row >> 3)) & 7;
-#endif
-}
-MOE_DEV int sw(int row, int chunk) { return row * BK + ((chunk ^ swz(row)) << 3); }
+MOE_DEV int sw(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 3); }
 
 MOE_DEV u32x4 zero4() { return {0u, 0u, 0u, 0u}; }
 

@@ -144,7 +144,9 @@ moe_status moe_route_x(const moe_desc* d, int chunk, const void* x, const void* 
                        int32_t* topk_idx, float* gates, int32_t* counts, int32_t* offsets, int32_t* row_of,
                        int32_t* src_token, void* workspace, void* stream);
 
-/* Dispatch: xd[row_of[t][j]] = x[t] for every local slot (a bitwise row copy for F32/BF16;
+/* Dispatch (ChunkedEP "Summary": each token chunk's rows go to the experts before that chunk's
+ * expert compute; torchtitan PR 5541 "AI-Generated Details": BF16/FP8 token-row payloads):
+ * xd[row_of[t][j]] = x[t] for every local slot (a bitwise row copy for F32/BF16;
  * each touched token row is read once). FP8: per token amax over the BF16 row,
  * xd = e4m3(x * (448/amax)) with FP32 steps, RNE, saturating; xd_scale[row] = amax/448 (1 for
  * an all-zero row); h_scale[row] is cleared (moe_expert_ffn writes it). Rows N_c..P_c-1 are not
@@ -152,7 +154,8 @@ moe_status moe_route_x(const moe_desc* d, int chunk, const void* x, const void* 
 moe_status moe_dispatch(const moe_desc* d, int chunk, const void* x, const int32_t* row_of,
                         void* xd, float* xd_scale, float* h_scale, void* stream);
 
-/* Grouped SwiGLU expert FFN over every local expert's rows [c*P_c + offsets[c][e],
+/* Expert compute of a chunk (ChunkedEP "Summary": the expert FFN runs per token chunk, beside the
+ * next chunk's dispatch). Grouped SwiGLU expert FFN over every local expert's rows [c*P_c + offsets[c][e],
  * c*P_c + offsets[c][e+1]): G = xd W1g^T, U = xd W1u^T (FP32 accumulation),
  * h = silu(G) * U with silu(z) = z/(1+exp(-z)), yd = h W2^T. gu (may be NULL) saves G and U
  * for the backward ([P,2I], G in columns 0..I-1). h is required ([P,I]). FP8: both GEMMs run on
@@ -172,8 +175,10 @@ moe_status moe_expert_ffn(const moe_desc* d, int chunk, const void* xd, const fl
 moe_status moe_combine(const moe_desc* d, int chunk, const void* yd, const float* gates,
                        const int32_t* row_of, void* out, void* stream);
 
-/* Combine backward: dyd[row_of[t][j]] = gates[t][j] * dy[t] (rounded once to the payload
- * type); dgates[t][j] = <dy[t], yd[row_of[t][j]]> in FP32, 0 for non-local slots. */
+/* Combine backward (ChunkedEP "Summary": the backward primitive writes the caller's dgrad
+ * buffers; ART PR 971: combine's output rows are the logical tokens, so only they carry dy):
+ * dyd[row_of[t][j]] = gates[t][j] * dy[t] (rounded once to the payload type);
+ * dgates[t][j] = <dy[t], yd[row_of[t][j]]> in FP32, 0 for non-local slots. */
 moe_status moe_combine_bwd(const moe_desc* d, int chunk, const void* dy, const void* yd,
                            const float* gates, const int32_t* row_of, void* dyd, float* dgates,
                            void* stream);
@@ -189,7 +194,9 @@ moe_status moe_route_bwd(const moe_desc* d, int chunk, const float* dgates, cons
                          const int32_t* topk_idx, const void* x, float* dlogits, float* dwr_acc,
                          void* dwr, void* workspace, void* stream);
 
-/* Expert FFN backward, input-gradient part, per chunk: dh = dyd W2; with s = sigmoid(G):
+/* Expert FFN backward, input-gradient part (ChunkedEP "Summary": backward per token chunk;
+ * torchtitan PR 5542 "Verification": input-gradient work is issued before the expert weight
+ * gradients, which chunk = -1 runs last), per chunk: dh = dyd W2; with s = sigmoid(G):
  * dG = dh * U * s * (1 + G (1 - s)), dU = dh * silu(G) (G, U read from gu);
  * dxd = [dG dU] W1. With chunk = -1 it then runs moe_expert_wgrad over every chunk (workspace is
  * moe_expert_wgrad's; unused when chunk >= 0). */
@@ -243,7 +250,9 @@ moe_status moe_expert_wgrad_fp8(const moe_desc* d, const void* dyd, const void* 
                                 void* dgu_t, float* dgu_cs, void* xd_t, float* xd_cs, void* h_t,
                                 float* h_cs, void* dw1, void* dw2, void* stream);
 
-/* Dispatch backward: dx[t] = RNE( sum over local slots of dxd[row_of[t][j]]
+/* Dispatch backward (ChunkedEP "Summary": the backward returns each chunk's token gradients to
+ * token order; the router term is the input gradient of the projection whose weight gradient
+ * "Numerical status -- unresolved" accumulates): dx[t] = RNE( sum over local slots of dxd[row_of[t][j]]
  * + sum_j dlogits[t][idx[t][j]] * W_r[idx[t][j]] ) with FP32 accumulation (the second sum is
  * the router projection's input gradient; dlogits is zero off the selected experts). */
 moe_status moe_dispatch_bwd(const moe_desc* d, int chunk, const void* dxd, const int32_t* row_of,
