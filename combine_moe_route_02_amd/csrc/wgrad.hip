@@ -4,7 +4,7 @@
 // "Numerical status -- unresolved", states for the router weights). Built on the grouped-GEMM
 // engine of gg_engine.h; kept in a translation unit of its own so that its register-heavy split
 // reduction does not change the code generated for the row-grouped kernels.
-#include "gg_engine.h"
+#include "gg_wgrad.h"
 
 namespace moe {
 namespace gg {
@@ -28,23 +28,6 @@ namespace gg {
 // When some expert is split, items (expert, split, tile) are ordered by descending expert rows and
 // dealt to the XCDs in contiguous ranges of equal row cost, so the tiles of one expert share an
 // XCD's L2 where they can.
-struct WgradArgs {
-  const uint16_t* A;      // [P, M]
-  const uint16_t* B;      // [P, N]
-  uint16_t* C;            // per expert [M, N]
-  int64_t lda, ldb, strideC;
-  int M, N;
-  const int32_t* offsets; // per-chunk local offsets
-  int El, n_chunks;
-  int64_t P_c;
-  float* part;            // partial slots (FP32 tiles), may be null when slots = 0
-  int* cnt;               // per (expert, tile) arrival counters, zero between launches
-  int slots;
-};
-
-constexpr int kWgradMinSplitRows = 512;  // never split an expert's K below this many rows
-constexpr int kWgradRefWorkers = 256;    // workers the split size is planned for
-
 // Split plan of one weight gradient, rebuilt in LDS by every workgroup. With no split expert (the
 // usual case) only K and the per-wave partials are written: item i is then tile i % T of expert
 // i / T, and each XCD takes ceil(items / 8) consecutive items (whole rounds of equal-cost tiles).
@@ -58,17 +41,16 @@ struct WgradPlan {
   int red[4];                // reductions and the last-arrival flag
 };
 
-template <int BM, int BN>
-MOE_DEV int wgrad_tiles_per_expert(const WgradArgs& a) { return ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN); }
-
 MOE_DEV int block_sum_to(int v, int* dst) {  // adds v of every thread into *dst (zeroed before)
   v = wave_sum_int(v);
   if ((threadIdx.x & 63) == 0 && v) atomicAdd(dst, v);
   return v;
 }
 
-// Builds the plan; returns Ks (then below the largest K_e, so it fits an int), or 0 when no expert
-// is split (then only p.K is written).
+// Builds the plan; returns Ks (then below the largest K_e, so it fits an int), 0 when no expert
+// is split (then only p.K is written), or -1 for a heavy_only list without a heavy expert (no
+// items). A heavy_only list takes the experts above Ks0 only, split or not; its Ks and splits are
+// those of the full list, so either computes a heavy expert's tiles bitwise alike.
 template <int BM, int BN>
 MOE_DEV int wgrad_plan(const WgradArgs& a, WgradPlan& p) {
   const int tid = threadIdx.x, El = a.El, T = wgrad_tiles_per_expert<BM, BN>(a);
@@ -98,9 +80,9 @@ MOE_DEV int wgrad_plan(const WgradArgs& a, WgradPlan& p) {
     total += p.wsum[w];
     kmax = max(kmax, p.wmax[w]);
   }
-  long long Ks = ((total * T + kWgradRefWorkers - 1) / kWgradRefWorkers);
-  if (Ks < kWgradMinSplitRows) Ks = kWgradMinSplitRows;
-  if (kmax <= Ks) return 0;  // uniform: every thread read the same partials
+  const long long Ks0 = wgrad_ks0(total, T);
+  long long Ks = Ks0;
+  if (kmax <= Ks0) return a.heavy_only ? -1 : 0;  // uniform: every thread read the same partials
   if (tid < 4) p.red[tid] = 0;
   __syncthreads();
   int tot = 0;
@@ -119,7 +101,7 @@ MOE_DEV int wgrad_plan(const WgradArgs& a, WgradPlan& p) {
     if (tot <= a.slots) break;
     Ks *= 2;
   }
-  if (tot == 0) return 0;  // the slots forced a split size above every expert's rows
+  if (tot == 0 && !a.heavy_only) return 0;  // the slots forced a split size above every expert's rows
   // the heaviest experts first
   for (int e = tid; e < El; e += kThreads) {
     const int ke = p.K[e];
@@ -136,7 +118,7 @@ MOE_DEV int wgrad_plan(const WgradArgs& a, WgradPlan& p) {
     for (int o = 0; o < El; ++o) {
       const int e = p.order[o];
       const int se = (int)((p.K[e] + Ks - 1) / Ks);
-      const int s1 = se > 1 ? se : 1;
+      const int s1 = (a.heavy_only && p.K[e] <= Ks0) ? 0 : (se > 1 ? se : 1);
       p.ipre[o] = ip;
       ip += s1 * T;
       p.spre[e] = se > 1 ? sp : -1;
@@ -151,16 +133,16 @@ MOE_DEV int wgrad_plan(const WgradArgs& a, WgradPlan& p) {
     long long C = 0;
     for (int o = 0; o < El; ++o) {
       const int ke = p.K[p.order[o]];
-      const long long se = ke > Ks ? (ke + Ks - 1) / Ks : 1;
-      long long c = (ke + se - 1) / se;
+      const long long se = (a.heavy_only && ke <= Ks0) ? 0 : ke > Ks ? (ke + Ks - 1) / Ks : 1;
+      long long c = se ? (ke + se - 1) / se : 1;
       if (c < 1) c = 1;
       C += se * T * c;
     }
     long long cpre = 0, n = 0;
     for (int o = 0; o < El; ++o) {
       const int ke = p.K[p.order[o]];
-      const long long se = ke > Ks ? (ke + Ks - 1) / Ks : 1;
-      long long c = (ke + se - 1) / se;
+      const long long se = (a.heavy_only && ke <= Ks0) ? 0 : ke > Ks ? (ke + Ks - 1) / Ks : 1;
+      long long c = se ? (ke + se - 1) / se : 1;
       if (c < 1) c = 1;
       const long long items = se * T;
       // item j's midpoint cpre + (j + 1/2) c lies below tid C / 8  <=>  16 c j < 2 tid C - 16 cpre - 8 c
@@ -174,27 +156,6 @@ MOE_DEV int wgrad_plan(const WgradArgs& a, WgradPlan& p) {
   }
   __syncthreads();
   return (int)Ks;
-}
-
-// Accumulator group gq of block (tm, tn) of this lane (four consecutive columns of one row) into the
-// BF16 staging tile in LDS.
-template <int BM, int BN>
-MOE_DEV void wgrad_stage4(char* ring, int tm, int tn, int gq, float a0, float a1, float a2, float a3, int lane,
-                          int wave) {
-  constexpr int WTM = BM / kWM, WTN = BN / kWN;
-  const int wm = wave / kWN, wn = wave % kWN;
-  const int row = wm * WTM + tm * 32 + out_row(lane);
-  const int nl = wn * WTN + tn * 32 + out_col(gq, lane);
-  *(uint2*)(ring + row * pitch<BN>() + 2 * nl) = pack4(a0, a1, a2, a3);
-}
-
-// Store the staged tile as BF16 rows of C[grp] (the ring holds it).
-template <int BM, int BN>
-MOE_DEV void wgrad_store(const WgradArgs& a, int grp, int m0, int n0, char* ring, int tid) {
-  lds_barrier();
-  store_staged<BM, BN, true>(ring, a.C + (int64_t)grp * a.strideC + (int64_t)m0 * a.N + n0, a.N,
-                             min(BM, a.M - m0), min(BN, a.N - n0), tid);
-  lds_barrier();
 }
 
 // One work item: tile t of expert e, split s of se, over rows [k_lo, k_hi) of the expert's chunk
@@ -297,6 +258,7 @@ MOE_DEV int wgrad_list(const WgradArgs& a, int first, char* ring, WgradPlan& p) 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int Ks = wgrad_plan<BM, BN>(a, p);
+  if (Ks < 0) return first;  // the plan depends only on the offsets: the same on every workgroup
   const int T = wgrad_tiles_per_expert<BM, BN>(a);
   const int xcd = blockIdx.x % 8, wg_per_xcd = gridDim.x / 8;
   int maxc, lo_item, hi_item;
@@ -351,26 +313,6 @@ __global__ __launch_bounds__(kThreads) void wgrad_kernel(WgradArgs a, WgradArgs 
   wgrad_list<BM, BN>(b, f, ring, plan);
 }
 
-// One weight gradient alone (dW1 of the layer schedule).
-template <int BM, int BN>
-__global__ __launch_bounds__(kThreads) void wgrad1_kernel(WgradArgs a) {
-  __shared__ WgradPlan plan;
-  extern __shared__ __attribute__((aligned(1024))) char ring[];
-  wgrad_list<BM, BN>(a, 0, ring, plan);
-}
-
-// A row-grouped GEMM and an independent weight gradient in one launch (the last chunk's gate/up
-// dgrad with dW2, whose tiles fill the dgrad's last round).
-template <int BM1, int BN1, int MODE1, int BM, int BN, bool Q1>
-__global__ __launch_bounds__(kThreads) void rows_wgrad_kernel(RowsArgs r, WgradArgs a) {
-  // the row list's group table and the weight gradient's plan share LDS (the plan is built after
-  // a barrier that follows the row list's last read of its table)
-  __shared__ union { RowsShared rows; WgradPlan plan; } sh;
-  extern __shared__ __attribute__((aligned(1024))) char ring[];
-  const int f = rows_list<BM1, BN1, MODE1, false, Q1>(r, 0, sh.rows, ring);
-  wgrad_list<BM, BN>(a, f, ring, sh.plan);
-}
-
 // ---------------------------------------------------------------------------------------------
 // Launchers
 
@@ -396,21 +338,6 @@ hipError_t run_wgrad(const char* name, const WgradArgs& a, const WgradArgs& b, h
 
 using namespace gg;
 
-// Weight-gradient scratch (inside the caller's workspace): the per-(expert, tile) arrival
-// counters of dW1 then dW2, padded to 256 bytes, then the partial slots of dW1 and of dW2
-// (256 x 256 FP32 tiles each). The counters must be zero when the scratch is first used; every
-// launch leaves them zero.
-constexpr int kWgradTile = 256;
-constexpr int kWgradSlots = 192;  // partial tiles per weight gradient at most
-static int64_t wgrad_tiles_1(int H, int I) { return (int64_t)((2 * I + 255) / 256) * ((H + 255) / 256); }
-static int64_t wgrad_tiles_2(int H, int I) { return (int64_t)((H + 255) / 256) * ((I + 255) / 256); }
-static int64_t wgrad_slots(int64_t tiles_per_expert, int El) {
-  const int64_t cap = 4 * tiles_per_expert * El;
-  return cap < kWgradSlots ? cap : kWgradSlots;
-}
-static int64_t wgrad_counter_bytes(int H, int I, int El) {
-  return ((int64_t)El * (wgrad_tiles_1(H, I) + wgrad_tiles_2(H, I)) * 4 + 255) / 256 * 256;
-}
 int64_t wgrad_scratch_bytes(int H, int I, int El) {
   if (El <= 0) return 0;
   const int64_t slot = (int64_t)kWgradTile * kWgradTile * 4;
@@ -418,48 +345,6 @@ int64_t wgrad_scratch_bytes(int H, int I, int El) {
          (wgrad_slots(wgrad_tiles_1(H, I), El) + wgrad_slots(wgrad_tiles_2(H, I), El)) * slot;
 }
 int64_t wgrad_counter_bytes_of(int H, int I, int El) { return El > 0 ? wgrad_counter_bytes(H, I, El) : 0; }
-
-// dW1[e] [2I, H] = sum dgu^T xd (the longer tile list, first) and dW2[e] [H, I] = sum dyd^T h
-static void wgrad_args(const ExpertGemm& g, WgradArgs& w1, WgradArgs& w2) {
-  w1 = WgradArgs{};
-  w1.A = (const uint16_t*)g.dgu; w1.B = (const uint16_t*)g.xd; w1.C = (uint16_t*)g.dw1; w1.lda = 2 * g.I;
-  w1.ldb = g.H; w1.strideC = (int64_t)2 * g.I * g.H; w1.M = 2 * g.I; w1.N = g.H; w1.offsets = g.offsets;
-  w1.El = g.El; w1.n_chunks = g.n_chunks; w1.P_c = g.P_c;
-  w2 = WgradArgs{};
-  w2.A = (const uint16_t*)g.dyd; w2.B = (const uint16_t*)g.h; w2.C = (uint16_t*)g.dw2; w2.lda = g.H;
-  w2.ldb = g.I; w2.strideC = (int64_t)g.H * g.I; w2.M = g.H; w2.N = g.I; w2.offsets = g.offsets;
-  w2.El = g.El; w2.n_chunks = g.n_chunks; w2.P_c = g.P_c;
-  if (g.wgrad_ws && g.El > 0) {
-    char* ws = (char*)g.wgrad_ws;
-    const int64_t t1 = wgrad_tiles_1(g.H, g.I), t2 = wgrad_tiles_2(g.H, g.I);
-    const int64_t slot = (int64_t)kWgradTile * kWgradTile;  // floats
-    w1.cnt = (int*)ws;
-    w2.cnt = (int*)ws + g.El * t1;
-    float* parts = (float*)(ws + wgrad_counter_bytes(g.H, g.I, g.El));
-    w1.slots = (int)wgrad_slots(t1, g.El);
-    w2.slots = (int)wgrad_slots(t2, g.El);
-    w1.part = parts;
-    w2.part = parts + w1.slots * slot;
-  }
-}
-
-template <int BM1, int BN1, int MODE1, int BM, int BN>
-static hipError_t run_rows_wgrad(const char* name, const RowsArgs& r, const WgradArgs& a, hipStream_t s) {
-  const size_t l1 = rows_lds_bytes<BM1, BN1, MODE1>(), l2 = wgrad_lds_bytes<BM, BN>();
-  const size_t lds = l1 > l2 ? l1 : l2;
-  constexpr bool kQ = (MODE1 == kDown || MODE1 == kGateUpBwd) && BN1 == 256;
-  auto k = (kQ && r.Cq) ? rows_wgrad_kernel<BM1, BN1, MODE1, BM, BN, kQ> : rows_wgrad_kernel<BM1, BN1, MODE1, BM, BN, false>;
-  hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  const int64_t tw = a.El > 0 ? (int64_t)a.El * ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) + a.slots : 0;
-  const int64_t grid = persistent_grid(rows_tiles_bound<BM1, BN1, MODE1>(r) + tw);
-  if (grid <= 0) return hipSuccess;
-  {
-    MOE_TRACE(name, s);
-    MOE_LAUNCH(k, dim3((unsigned)grid), dim3(kThreads), lds, s, r, a);
-  }
-  return hipGetLastError();
-}
 
 hipError_t gg_expert_wgrad_bf16(const void* dyd, const void* dgu, const void* xd, const void* h,
                                 const int32_t* offsets, void* dw1, void* dw2, int H, int I, int El,
@@ -472,25 +357,13 @@ hipError_t gg_expert_wgrad_bf16(const void* dyd, const void* dgu, const void* xd
   return run_wgrad<256, 256>("gemm_wgrad", a, b, s);
 }
 
-hipError_t gg_gateup_dgrad_then_wgrad2(const ExpertGemm& g, int c, hipStream_t s) {
-  WgradArgs w1, w2;
-  wgrad_args(g, w1, w2);
-  return run_rows_wgrad<MOE_GUDGRAD, 256, 256>("gemm_gateup_dgrad+wgrad_w2", gateup_dgrad_args(g, c, 1), w2, s);
-}
+// The layer's last weight-gradient launch: every dW1 tile, and the dW2 tiles of the experts above
+// the split threshold (rows_wgrad.hip computed the others beside the last gate/up dgrad).
 hipError_t gg_wgrad1(const ExpertGemm& g, hipStream_t s) {
   WgradArgs w1, w2;
   wgrad_args(g, w1, w2);
-  const size_t lds = wgrad_lds_bytes<256, 256>();
-  auto k = wgrad1_kernel<256, 256>;
-  hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  const int64_t grid = persistent_grid(w1.El > 0 ? (int64_t)w1.El * ((w1.M + 255) / 256) * ((w1.N + 255) / 256) + w1.slots : 0);
-  if (grid <= 0) return hipSuccess;
-  {
-    MOE_TRACE("gemm_wgrad_w1", s);
-    MOE_LAUNCH(k, dim3((unsigned)grid), dim3(kThreads), lds, s, w1);
-  }
-  return hipGetLastError();
+  w2.heavy_only = 1;
+  return run_wgrad<256, 256>("gemm_wgrad_w1", w1, w2, s);
 }
 
 }  // namespace moe
