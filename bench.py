@@ -29,27 +29,30 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense BF16 MFMA, TFLOP/s
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
 
-# launch-log name -> (source file under the package's csrc/, substring of the kernel symbol that
-# rocprofv3 reports for it)
+# launch-log name -> (source files under the package's csrc/ that its code comes from, substring of
+# the kernel symbol that rocprofv3 reports for it)
 KERNEL_SYMBOLS = {
-    "route_topk": ("route.hip", "route_topk_kernel"),
-    "route_layout": ("route.hip", "route_layout_kernel"),
-    "dispatch": ("rows.hip", "dispatch_copy_kernel"),
-    "combine": ("rows.hip", "combine_kernel"),
-    "combine_bwd": ("rows.hip", "combine_bwd_kernel"),
-    "route_bwd_dlogits": ("rows.hip", "route_bwd_dlogits_kernel"),
-    "dispatch_bwd": ("rows.hip", "dispatch_bwd_kernel"),
-    "gemm_gateup_swiglu": ("grouped_gemm.hip", "rows_kernel<256, 256, 0, false>"),
-    "gemm_down": ("grouped_gemm.hip", "rows_kernel<256, 256, 1, false>"),
-    "gemm_down_dgrad_swiglu": ("grouped_gemm.hip", "rows_kernel<128, 256, 2, false>"),
-    "gemm_gateup_dgrad": ("grouped_gemm.hip", "rows_kernel<256, 256, 3, false>"),
-    "gemm_down+gateup_swiglu": ("grouped_gemm.hip", "rows_pair_kernel<256, 256, 1, 256, 256, 0>"),
-    "gemm_gateup_dgrad+down_dgrad_swiglu": ("grouped_gemm.hip", "rows_pair_kernel<256, 256, 3, 128, 256, 2>"),
-    "gemm_gateup_dgrad+wgrad_w2": ("grouped_gemm.hip", "rows_wgrad_kernel<256, 256, 3, 256, 256>"),
-    "gemm_wgrad_w1": ("grouped_gemm.hip", "wgrad1_kernel<256, 256>"),
-    "gemm_wgrad": ("grouped_gemm.hip", "wgrad_kernel<256, 256>"),
-    "gemm_router_wgrad": ("gemm.hip", "router_wgrad_kernel"),
-    "router_reduce": ("gemm.hip", "reduce_partials_kernel"),
+    "route_topk": (("route.hip",), "route_topk_kernel"),
+    "route_layout": (("route.hip",), "route_layout_kernel"),
+    "dispatch": (("rows.hip",), "dispatch_copy_kernel"),
+    "combine": (("rows.hip",), "combine_kernel"),
+    "combine_bwd": (("rows.hip",), "combine_bwd_kernel"),
+    "route_bwd_dlogits": (("rows.hip",), "route_bwd_dlogits_kernel"),
+    "dispatch_bwd": (("rows.hip",), "dispatch_bwd_kernel<"),
+    "gemm_gateup_swiglu": (("grouped_gemm.hip", "gg_engine.h"), "rows_kernel<256, 256, 0, false, false>"),
+    "gemm_down": (("grouped_gemm.hip", "gg_engine.h"), "rows_kernel<256, 256, 1, false, false>"),
+    "gemm_down_dgrad_swiglu": (("grouped_gemm.hip", "gg_engine.h"), "rows_kernel<128, 256, 2, false, false>"),
+    "gemm_gateup_dgrad": (("grouped_gemm.hip", "gg_engine.h"), "rows_kernel<256, 256, 3, false, false>"),
+    "gemm_down+gateup_swiglu": (("grouped_gemm.hip", "gg_engine.h"),
+                                "rows_pair_kernel<256, 256, 1, 256, 256, 0, false>"),
+    "gemm_gateup_dgrad+down_dgrad_swiglu": (("grouped_gemm.hip", "gg_engine.h"),
+                                            "rows_pair_kernel<256, 256, 3, 128, 256, 2, false>"),
+    "gemm_gateup_dgrad+wgrad_w2": (("rows_wgrad.hip", "gg_engine.h", "gg_wgrad.h"),
+                                   "rows_wgrad_kernel<256, 256, 3, 256, 256, false>"),
+    "gemm_wgrad_w1": (("wgrad.hip", "gg_engine.h", "gg_wgrad.h"), "wgrad_kernel<256, 256, 1>"),
+    "gemm_wgrad": (("wgrad.hip", "gg_engine.h", "gg_wgrad.h"), "wgrad_kernel<256, 256, 0>"),
+    "gemm_router_wgrad": (("gemm.hip",), "router_wgrad_kernel"),
+    "router_reduce": (("gemm.hip",), "reduce_partials_kernel"),
 }
 CALIBRATION_BYTES = 64 << 20   # a plain elementwise copy of this many bytes (read and written once,
 CALIBRATION_SYMBOL = "MulFunctor"  # one dispatch: y = 2 * x in FP32) runs before the timed region
@@ -70,7 +73,7 @@ def source_sha(name: str) -> str:
     import hashlib
     csrc = os.path.join(ROOT, "combine_moe_route_02_amd", "csrc")
     h = hashlib.sha256()
-    for f in (KERNEL_SYMBOLS[name][0], "common.h"):
+    for f in KERNEL_SYMBOLS[name][0] + ("common.h",):
         with open(os.path.join(csrc, f), encoding="utf-8") as fh:
             h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
@@ -207,7 +210,9 @@ def counter_summary(dirs, cmd: str) -> str:
         if "gg::" in k or "gemm::" in k:
             raw.append(f"- `{k.split('(')[0][:110]}` ({us:.1f} us): " +
                        ", ".join(f"{ck}={statistics.median(v):.4g}" for ck, v in sorted(c.items())))
-    src = [f"Source hashes (code without comments): grouped_gemm.hip {source_sha('gemm_gateup_swiglu')}, "
+    src = [f"Source hashes (code without comments): grouped_gemm.hip + gg_engine.h "
+           f"{source_sha('gemm_gateup_swiglu')}, wgrad.hip + gg_engine.h + gg_wgrad.h {source_sha('gemm_wgrad')}, "
+           f"rows_wgrad.hip + gg_engine.h + gg_wgrad.h {source_sha('gemm_gateup_dgrad+wgrad_w2')}, "
            f"gemm.hip {source_sha('gemm_router_wgrad')}, rows.hip {source_sha('dispatch')}.", ""]
     return "\n".join(out[:7] + src + out[7:] + raw) + "\n"
 
@@ -526,7 +531,22 @@ def fp8_dgrad(args, cfg, bufs, mh, torch, np):
     torch.cuda.synchronize()
     ms_w = (time.perf_counter() - t0) * 1e3 / args.steps
     out["with_fp8_wgrad"] = {"tokens_per_s": round(cfg.T / (ms_w * 1e-3), 1), "ms_per_step_untraced": round(ms_w, 4)}
-    del bq, bw
+    # the BF16 step with the FP8 dispatch-backward payload alone (untraced)
+    dx8 = mh.make_desc(T=cfg.T, H=cfg.H, I=cfg.I, E=cfg.E, E_local=cfg.E_local, k=cfg.k, n_chunks=cfg.n_chunks,
+                       dtype="bf16", e0=cfg.e0, flags=mh.FLAG_FP8_DXD)
+    bx = mh.allocate(dx8, backward=True)
+    for name in ("x", "logits", "w1", "w2", "w_r", "dy"):
+        bx[name] = bufs[name]
+    for _ in range(args.warmup):
+        mh.moe_layer_forward_backward(dx8, bx, cs, aux)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        mh.moe_layer_forward_backward(dx8, bx, cs, aux)
+    torch.cuda.synchronize()
+    ms_x = (time.perf_counter() - t0) * 1e3 / args.steps
+    out["bf16_with_fp8_dxd"] = {"tokens_per_s": round(cfg.T / (ms_x * 1e-3), 1), "ms_per_step_untraced": round(ms_x, 4)}
+    del bq, bw, bx
     torch.cuda.empty_cache()
     return out
 
