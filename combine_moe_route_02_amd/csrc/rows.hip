@@ -521,8 +521,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void d
 #pragma unroll
     for (int b = 0; b < NB; ++b) dst[i0 + 64 * b] = V::from_f(acc[b]);
   };
+  // vectors per lane in flight: kBatch, or fewer where the 64-VGPR cap would spill at kBatch
+  constexpr int NBV = (sizeof(T) == 2 && K >= 3 && K <= 5) ? 1
+                    : ((sizeof(T) == 2 && K == 2) || (sizeof(T) == 4 && K == 6)) ? 2 : kBatch;
   int64_t i0 = lane;
-  for (; i0 + 64 * (kBatch - 1) < nvec; i0 += 64 * kBatch) pass(i0, std::integral_constant<int, kBatch>());
+  for (; i0 + 64 * (NBV - 1) < nvec; i0 += 64 * NBV) pass(i0, std::integral_constant<int, NBV>());
   for (; i0 < nvec; i0 += 64) pass(i0, std::integral_constant<int, 1>());
 }
 

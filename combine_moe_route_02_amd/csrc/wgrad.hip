@@ -304,8 +304,9 @@ MOE_DEV int wgrad_list(const WgradArgs& a, int first, char* ring, WgradPlan& p) 
 }
 
 // Up to two independent weight gradients in one persistent launch, so the second fills the
-// first one's last round.
-template <int BM, int BN>
+// first one's last round. TAG only names the launch (0: the stage call, 1: the layer's last
+// weight-gradient launch), so that profiles tell the two apart.
+template <int BM, int BN, int TAG>
 __global__ __launch_bounds__(kThreads) void wgrad_kernel(WgradArgs a, WgradArgs b) {
   __shared__ WgradPlan plan;
   extern __shared__ __attribute__((aligned(1024))) char ring[];
@@ -316,10 +317,10 @@ __global__ __launch_bounds__(kThreads) void wgrad_kernel(WgradArgs a, WgradArgs 
 // ---------------------------------------------------------------------------------------------
 // Launchers
 
-template <int BM, int BN>
+template <int BM, int BN, int TAG>
 hipError_t run_wgrad(const char* name, const WgradArgs& a, const WgradArgs& b, hipStream_t s) {
   const size_t lds = wgrad_lds_bytes<BM, BN>();
-  auto k = wgrad_kernel<BM, BN>;
+  auto k = wgrad_kernel<BM, BN, TAG>;
   hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   auto tiles = [](const WgradArgs& w) {  // items at most: every tile once, plus the split partials
@@ -354,7 +355,7 @@ hipError_t gg_expert_wgrad_bf16(const void* dyd, const void* dgu, const void* xd
   g.H = H; g.I = I; g.El = El; g.n_chunks = n; g.P_c = P_c; g.wgrad_ws = wgrad_ws;
   WgradArgs a, b;
   wgrad_args(g, a, b);
-  return run_wgrad<256, 256>("gemm_wgrad", a, b, s);
+  return run_wgrad<256, 256, 0>("gemm_wgrad", a, b, s);
 }
 
 // The layer's last weight-gradient launch: every dW1 tile, and the dW2 tiles of the experts above
@@ -363,7 +364,7 @@ hipError_t gg_wgrad1(const ExpertGemm& g, hipStream_t s) {
   WgradArgs w1, w2;
   wgrad_args(g, w1, w2);
   w2.heavy_only = 1;
-  return run_wgrad<256, 256>("gemm_wgrad_w1", w1, w2, s);
+  return run_wgrad<256, 256, 1>("gemm_wgrad_w1", w1, w2, s);
 }
 
 }  // namespace moe
