@@ -39,10 +39,10 @@ KERNEL_SYMBOLS = {
     "combine_bwd": (("rows.hip",), "combine_bwd_kernel"),
     "route_bwd_dlogits": (("rows.hip",), "route_bwd_dlogits_kernel"),
     "dispatch_bwd": (("rows.hip",), "dispatch_bwd_kernel<"),
-    "gemm_gateup_swiglu": (("grouped_gemm.hip", "gg_engine.h"), "rows_kernel<256, 256, 0, false, false>"),
-    "gemm_down": (("grouped_gemm.hip", "gg_engine.h"), "rows_kernel<256, 256, 1, false, false>"),
-    "gemm_down_dgrad_swiglu": (("grouped_gemm.hip", "gg_engine.h"), "rows_kernel<128, 256, 2, false, false>"),
-    "gemm_gateup_dgrad": (("grouped_gemm.hip", "gg_engine.h"), "rows_kernel<256, 256, 3, false, false>"),
+    "gemm_gateup_swiglu": (("grouped_gemm.hip", "gg_engine.h"), "rows_kernel<256, 256, 0, false, false, "),
+    "gemm_down": (("grouped_gemm.hip", "gg_engine.h"), "rows_kernel<256, 256, 1, false, false, false>"),
+    "gemm_down_dgrad_swiglu": (("grouped_gemm.hip", "gg_engine.h"), "rows_kernel<128, 256, 2, false, false, false>"),
+    "gemm_gateup_dgrad": (("grouped_gemm.hip", "gg_engine.h"), "rows_kernel<256, 256, 3, false, false, false>"),
     "gemm_down+gateup_swiglu": (("grouped_gemm.hip", "gg_engine.h"),
                                 "rows_pair_kernel<256, 256, 1, 256, 256, 0, false>"),
     "gemm_gateup_dgrad+down_dgrad_swiglu": (("grouped_gemm.hip", "gg_engine.h"),

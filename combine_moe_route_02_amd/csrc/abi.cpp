@@ -826,16 +826,33 @@ static moe_status forward_sched_merged(const moe_desc* d, const moe_tensors* t, 
     MOE_TRY(moe_dispatch(d, c, t->x, t->row_of, t->xd, t->xd_scale, t->h_scale, s));
     return MOE_OK;
   };
-  MOE_TRY(route_dispatch(0, cs));
-  if (two) {
+  // With two streams the first chunk's gate/up reads its rows straight from x through src_token,
+  // so only its routing precedes it on the compute stream; its dispatch (xd, which the backward
+  // and the caller read) runs on the auxiliary stream after the next chunk's routing and dispatch.
+  // No forward kernel on the compute stream reads xd of chunk 0 again; the forward's final join
+  // (layer forward) or the backward's first wait on the auxiliary stream (fused step; the kernels
+  // before it read dyd and G/U only) orders every later reader after that dispatch.
+  const bool gather = two && (int64_t)d->T * d->H * 2 <= kRsrcMax;
+  if (gather) {
+    MOE_TRY(route_any(d, 0, t, cs));
     MOE_HIP(hipEventRecord(disp[0], cs), "hipEventRecord");
     MOE_HIP(hipStreamWaitEvent(as, disp[0], 0), "hipStreamWaitEvent");
+    MOE_TRY(route_dispatch(1, as));
+    MOE_HIP(hipEventRecord(disp[1], as), "hipEventRecord");
+    MOE_TRY(moe_dispatch(d, 0, t->x, t->row_of, t->xd, t->xd_scale, t->h_scale, as));
+    MOE_HIP(moe::gg_gateup_gather(g, 0, t->x, t->src_token, d->T, cs), "expert_ffn");
+  } else {
+    MOE_TRY(route_dispatch(0, cs));
+    if (two) {
+      MOE_HIP(hipEventRecord(disp[0], cs), "hipEventRecord");
+      MOE_HIP(hipStreamWaitEvent(as, disp[0], 0), "hipStreamWaitEvent");
+    }
+    if (n > 1) {
+      MOE_TRY(route_dispatch(1, side));
+      if (two) MOE_HIP(hipEventRecord(disp[1], as), "hipEventRecord");
+    }
+    MOE_HIP(moe::gg_gateup(g, 0, cs), "expert_ffn");
   }
-  if (n > 1) {
-    MOE_TRY(route_dispatch(1, side));
-    if (two) MOE_HIP(hipEventRecord(disp[1], as), "hipEventRecord");
-  }
-  MOE_HIP(moe::gg_gateup(g, 0, cs), "expert_ffn");
   for (int c = 0; c < n; ++c) {
     if (c + 1 < n) {
       if (two) MOE_HIP(hipStreamWaitEvent(cs, disp[c + 1], 0), "hipStreamWaitEvent");

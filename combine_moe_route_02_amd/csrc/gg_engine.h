@@ -328,6 +328,10 @@ struct RowsArgs {
   uint8_t* Cq;
   float* Cs;
   int64_t ldcs;
+  // GATHER launches (gate/up): A holds the token rows [gather_rows, K] and dispatch row r reads
+  // token row gather[r] (src_token), so the GEMM needs no dispatched copy of its operand
+  const int32_t* gather;
+  int64_t gather_rows;
 };
 
 template <int BM, int BN, int MODE>
@@ -365,7 +369,7 @@ MOE_DEV int first_slot(int first) {
 
 // The tiles of one row-grouped GEMM from per-XCD slot `first` on; returns the slot after its
 // last. Every thread of the workgroup calls it (it contains barriers).
-template <int BM, int BN, int MODE, bool FP8, bool QOUT = false>
+template <int BM, int BN, int MODE, bool FP8, bool QOUT = false, bool GATHER = false>
 MOE_DEV int rows_list(const RowsArgs& a, int first, RowsShared& sh, char* ring) {
   constexpr int WTM = BM / kWM, WTN = BN / kWN, TM = WTM / 32, TN = WTN / 32;
   constexpr bool kSwiGLU = (MODE == kGateUp);
@@ -375,6 +379,7 @@ MOE_DEV int rows_list(const RowsArgs& a, int first, RowsShared& sh, char* ring) 
   constexpr int OUTN = kSwiGLU ? BN / 2 : BN;
   static_assert(!(FP8 && MODE == kGateUpBwd), "FP8 gate/up dgrad runs as kDown on the transposed W1");
   static_assert(!QOUT || ((MODE == kDown || MODE == kGateUpBwd) && BN == 256), "FP8 output: plain 256-wide tiles");
+  static_assert(!GATHER || (MODE == kGateUp && !FP8), "row gather: the BF16 gate/up GEMM");
   int* s_pre = sh.pre;
   int64_t* s_r0 = sh.r0;
   int* s_len = sh.len;
@@ -435,8 +440,17 @@ MOE_DEV int rows_list(const RowsArgs& a, int first, RowsShared& sh, char* ring) 
     const char* Be = (const char*)a.B + (int64_t)e * a.strideB * ES;
 
     Loader<BM, false> la;
-    la.init_kmajor((const char*)a.A + r0 * a.lda * ES, a.lda * ES, (int64_t)mvalid * a.lda * ES, wave, lane,
-                   [](int r) { return r; });
+    if constexpr (GATHER) {
+      // tile row r reads token row gather[r0 + r]; rows past the segment point one row past the
+      // end of A, which the descriptor's extent turns into zeros
+      const int32_t* gt = a.gather;
+      const int64_t gr = a.gather_rows;
+      la.init_kmajor((const char*)a.A, a.lda * ES, gr * a.lda * ES, wave, lane,
+                     [gt, r0, mvalid, gr](int r) { return r < mvalid ? (int64_t)gt[r0 + r] : gr; });
+    } else {
+      la.init_kmajor((const char*)a.A + r0 * a.lda * ES, a.lda * ES, (int64_t)mvalid * a.lda * ES, wave, lane,
+                     [](int r) { return r; });
+    }
     Loader<BN, kBKS> lb;
     if constexpr (kSwiGLU) {
       // tile row r -> wave column block r / WTN; its first half are gate rows j, its second half

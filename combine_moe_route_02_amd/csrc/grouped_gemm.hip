@@ -20,11 +20,11 @@
 namespace moe {
 namespace gg {
 
-template <int BM, int BN, int MODE, bool FP8, bool QOUT>
+template <int BM, int BN, int MODE, bool FP8, bool QOUT, bool GATHER>
 __global__ __launch_bounds__(kThreads) void rows_kernel(RowsArgs a) {
   __shared__ RowsShared sh;
   extern __shared__ __attribute__((aligned(1024))) char ring[];
-  rows_list<BM, BN, MODE, FP8, QOUT>(a, 0, sh, ring);
+  rows_list<BM, BN, MODE, FP8, QOUT, GATHER>(a, 0, sh, ring);
 }
 
 // Two independent row-grouped GEMMs in one persistent launch: the second's tiles fill the
@@ -137,7 +137,10 @@ template <int BM, int BN, int MODE, bool FP8>
 hipError_t run_rows(const char* name, const RowsArgs& a, hipStream_t s) {
   const size_t lds = rows_lds_bytes<BM, BN, MODE>();
   constexpr bool kQ = (MODE == kDown || MODE == kGateUpBwd) && BN == 256;
-  auto k = (kQ && a.Cq) ? rows_kernel<BM, BN, MODE, FP8, kQ> : rows_kernel<BM, BN, MODE, FP8, false>;
+  constexpr bool kG = MODE == kGateUp && !FP8;
+  auto k = (kQ && a.Cq)       ? rows_kernel<BM, BN, MODE, FP8, kQ, false>
+           : (kG && a.gather) ? rows_kernel<BM, BN, MODE, FP8, false, kG>
+                              : rows_kernel<BM, BN, MODE, FP8, false, false>;
   hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int outn = (MODE == kGateUp) ? BN / 2 : BN;
@@ -200,6 +203,14 @@ hipError_t gg_expert_dgrad_bf16(const void* dyd, const void* gu, const void* w1,
 // Launches of the layer schedule (one chunk each; the pairs take independent work of two steps).
 hipError_t gg_gateup(const ExpertGemm& g, int c, hipStream_t s) {
   return run_rows<MOE_GATEUP, false>("gemm_gateup_swiglu", gateup_args(g, c, 1), s);
+}
+hipError_t gg_gateup_gather(const ExpertGemm& g, int c, const void* x, const int32_t* src_token, int64_t T,
+                            hipStream_t s) {
+  RowsArgs a = gateup_args(g, c, 1);
+  a.A = x;
+  a.gather = src_token;
+  a.gather_rows = T;
+  return run_rows<MOE_GATEUP, false>("gemm_gateup_swiglu", a, s);
 }
 hipError_t gg_down(const ExpertGemm& g, int c, hipStream_t s) {
   return run_rows<MOE_DOWN, false>("gemm_down", down_args(g, c, 1), s);

@@ -120,6 +120,10 @@ int64_t wgrad_counter_bytes_of(int H, int I, int El);
 // One chunk's gate/up (+SwiGLU) or down GEMM; down of chunk c and gate/up of chunk c2 in one
 // persistent launch (independent work: the second fills the first's last round).
 hipError_t gg_gateup(const ExpertGemm& g, int c, hipStream_t s);
+// gate/up of chunk c reading its operand rows straight from the token rows x [T, H] through
+// src_token (no dispatched copy needed; T * H * 2 bytes must fit one buffer descriptor)
+hipError_t gg_gateup_gather(const ExpertGemm& g, int c, const void* x, const int32_t* src_token, int64_t T,
+                            hipStream_t s);
 hipError_t gg_down(const ExpertGemm& g, int c, hipStream_t s);
 hipError_t gg_down_then_gateup(const ExpertGemm& g, int c, int c2, hipStream_t s);
 // Input gradients: down dgrad (+SwiGLU backward) of chunk c, and gate/up dgrad of chunk c with

@@ -152,8 +152,9 @@ def test_layer_launch_order_and_streams(cfg):
     """The fused BF16 primitive's launches: down of chunk c shares a launch with gate/up of chunk
     c+1, gate/up dgrad of chunk c with down dgrad of chunk c+1, the last gate/up dgrad with dW2;
     every chunk's input-gradient work is issued before dW1 (the weight gradient that needs it);
-    chunk c+1's routing/dispatch is issued before chunk c's combine; and each kernel runs on the
-    stream the two-stream schedule gives it."""
+    chunk c+1's routing/dispatch is issued before chunk c's combine; chunk 0's gate/up reads the
+    token rows directly, so its dispatch runs on aux; and each kernel runs on the stream the
+    two-stream schedule gives it."""
     _require_gpu()
     import combine_moe_route_02_amd as mh
     n = cfg.n_chunks
@@ -184,10 +185,14 @@ def test_layer_launch_order_and_streams(cfg):
     gemms = [k for k in expect if k.startswith("gemm_")]
     assert set(sum((streams_of(k) for k in gemms), [])) == {compute}
     disp, comb = streams_of("dispatch"), streams_of("combine")
-    assert disp[0] == compute
-    aux = disp[1]
+    # chunk 0 is routed on the compute stream; its gate/up reads x through src_token, so every
+    # dispatch (chunk 0's included, which the backward reads) runs on aux
+    assert streams_of("route_topk")[0] == compute
+    aux = disp[0]
     # the fused primitive runs every combine on aux (the last one beside the backward's start)
-    assert aux != compute and set(disp[1:]) == {aux} and set(comb) == {aux}
+    assert aux != compute and set(disp) == {aux} and set(comb) == {aux}
+    # chunk 0's dispatch is issued after chunk 1's routing and dispatch
+    assert names.index("dispatch") > names.index("route_topk", names.index("route_topk") + 1)
     cbw, dbw = streams_of("combine_bwd"), streams_of("dispatch_bwd")
     assert cbw[0] == compute and set(cbw[1:]) == {aux} and set(dbw) == {aux}
     assert set(streams_of("route_bwd_dlogits")) == {aux}
