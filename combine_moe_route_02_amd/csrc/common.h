@@ -88,6 +88,21 @@ MOE_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
                                            0x00020000);  // gfx9 raw buffer descriptor word 3
 }
 
+// The same descriptor as four dwords, for instructions written in assembly: base address bits
+// 31:0, bits 47:32 with stride 0, num_records, word 3 (uniform values, made scalar).
+MOE_DEV i32x4_t rsrc_words(const void* base, int64_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  const int64_t lim = 0x7fffffff;
+  return i32x4_t{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                 __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffff)),
+                 __builtin_amdgcn_readfirstlane((int)(bytes < 0 ? 0 : (bytes > lim ? lim : bytes))), 0x00020000};
+}
+
+// LDS byte address of a pointer into LDS.
+MOE_DEV uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt in bits 3:0 and
 // 15:14, expcnt 6:4, lgkmcnt 11:8).
 template <int N>

@@ -56,7 +56,8 @@ template <int R, bool KSLOW>
 struct Loader {
   static constexpr int NI = R / (16 * kWaves);
   static_assert(NI >= 1 && R % (16 * kWaves) == 0, "tile rows must cover every wave");
-  __amdgpu_buffer_rsrc_t rs;
+  __amdgpu_buffer_rsrc_t rb;  // buffer descriptor
+  i32x4_t rs;                 // the same as words, for the loads written in assembly
   uint32_t voff[NI];
   uint32_t step;  // HBM bytes between consecutive stages
   int wave;
@@ -65,7 +66,8 @@ struct Loader {
   template <class Map>
   MOE_DEV void init_kmajor(const void* base, int64_t ld_bytes, int64_t bytes, int wv, int lane, Map map) {
     wave = wv;
-    rs = make_rsrc(base, bytes);
+    rb = make_rsrc(base, bytes);
+    rs = rsrc_words(base, bytes);
     step = kRowB;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -80,7 +82,8 @@ struct Loader {
     constexpr int CPR = 2 * R / 16;      // chunks per K-row
     constexpr int RPI = 1024 / (2 * R);  // K-rows per wave instruction
     wave = wv;
-    rs = make_rsrc(base, bytes);
+    rb = make_rsrc(base, bytes);
+    rs = rsrc_words(base, bytes);
     step = (uint32_t)(kKRows * ld_bytes);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -89,11 +92,44 @@ struct Loader {
       voff[i] = (uint32_t)(k * ld_bytes) + 16u * (uint32_t)c;
     }
   }
-  MOE_DEV void issue(char* stage, int s) const {
+  // Issue the loads of stage s into LDS at byte address `stage` (the operand's part of a ring
+  // slot). ASM: the same loads written in assembly. Before every transposing LDS read
+  // (ds_read_b64_tr_b16) the compiler waits for all outstanding direct-to-LDS loads issued
+  // through its builtin (vmcnt(0)), which drains the ring's prefetch in every stage; GEMMs with a
+  // K-slow operand therefore issue all of their loads in assembly, ordered with the reads of
+  // their stage by the K loop's explicit vmcnt waits. M0 (the LDS destination) is saved and
+  // restored; s_nop 4 covers a VALU write of an SGPR operand.
+  template <bool ASM>
+  MOE_DEV void issue(uint32_t stage, int s) const {
+    static_assert(NI == 1 || NI == 2, "one or two loads per wave and operand stage");
+    const uint32_t l0 = stage + (uint32_t)(wave * NI * 1024);
+    if constexpr (!ASM) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(stage + (wave * NI + i) * 1024), 16,
-                                               (int)voff[i], (int)((uint32_t)s * step), 0, 0);
+      for (int i = 0; i < NI; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(uintptr_t)(l0 + i * 1024), 16, (int)voff[i],
+                                                 (int)((uint32_t)s * step), 0, 0);
+    } else {
+      const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)s * step);
+      const uint32_t lf = __builtin_amdgcn_readfirstlane(l0);
+      uint32_t m0s;
+      if constexpr (NI == 1) {
+        asm volatile(
+            "s_mov_b32 %0, m0\n\ts_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+            "buffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
+            : "=&s"(m0s)
+            : "s"(lf), "v"(voff[0]), "s"(rs), "s"(so)
+            : "memory");
+      } else {
+        const uint32_t l1 = lf + 1024;
+        asm volatile(
+            "s_mov_b32 %0, m0\n\ts_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+            "buffer_load_dwordx4 %3, %5, %6 offen lds\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+            "buffer_load_dwordx4 %4, %5, %6 offen lds\n\ts_mov_b32 m0, %0"
+            : "=&s"(m0s)
+            : "s"(lf), "s"(l1), "v"(voff[0]), "v"(voff[1 % NI]), "s"(rs), "s"(so)
+            : "memory");
+      }
+    }
   }
 };
 
@@ -214,20 +250,22 @@ MOE_DEV void kloop(const LA& la, const LB& lb, char* ring, int nks, int arow0, i
                    f32x16_t (&acc)[TM][TN]) {
   constexpr int SA = RA * kRowB, SS = (RA + RB) * kRowB;
   constexpr int NL = LA::NI + LB::NI;  // load instructions per wave per stage
+  constexpr bool kAsm = AKS || BKS;    // transposing reads follow: loads written in assembly
+  const uint32_t rl = lds_addr(ring);
 #pragma unroll
   for (int s = 0; s < kNst - 1; ++s) {
-    la.issue(ring + s * SS, s);
-    lb.issue(ring + s * SS + SA, s);
+    la.template issue<kAsm>(rl + s * SS, s);
+    lb.template issue<kAsm>(rl + s * SS + SA, s);
   }
   for (int s = 0; s < nks; ++s) {
     wait_vm<(kNst - 2) * NL>();    // stage s has landed (this wave's loads)
     __builtin_amdgcn_s_barrier();  // every wave's part of stage s is in LDS; stage s-1 is consumed
     const int ld = s + kNst - 1;
-    char* st = ring + (ld % kNst) * SS;
+    const uint32_t st = rl + (ld % kNst) * SS;
     const char* cur = ring + (s % kNst) * SS;
     stage_mma<FP8, AKS, BKS, RA, RB, TM, TN, TMA, NL>(cur, cur + SA, arow0, brow0, lane, acc, [&] {
-      la.issue(st, ld);
-      lb.issue(st + SA, ld);
+      la.template issue<kAsm>(st, ld);
+      lb.template issue<kAsm>(st + SA, ld);
     });
   }
   wait_vm<0>();
