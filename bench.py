@@ -39,7 +39,9 @@ KERNEL_SYMBOLS = {
     "combine_bwd": (("rows.hip",), "combine_bwd_kernel"),
     "route_bwd_dlogits": (("rows.hip",), "route_bwd_dlogits_kernel"),
     "dispatch_bwd": (("rows.hip",), "dispatch_bwd_kernel<"),
-    "gemm_gateup_swiglu": (("grouped_gemm.hip", "gg_engine.h"), "rows_kernel<256, 256, 0, false, false, "),
+    "gemm_gateup_swiglu": (("grouped_gemm.hip", "gg_engine.h"), "rows_kernel<256, 256, 0, false, false, false>"),
+    # the same launch name in the fused step, whose chunk-0 gate/up reads token rows through src_token
+    "gemm_gateup_swiglu_gather": (("grouped_gemm.hip", "gg_engine.h"), "rows_kernel<256, 256, 0, false, false, true>"),
     "gemm_down": (("grouped_gemm.hip", "gg_engine.h"), "rows_kernel<256, 256, 1, false, false, false>"),
     "gemm_down_dgrad_swiglu": (("grouped_gemm.hip", "gg_engine.h"), "rows_kernel<128, 256, 2, false, false, false>"),
     "gemm_gateup_dgrad": (("grouped_gemm.hip", "gg_engine.h"), "rows_kernel<256, 256, 3, false, false, false>"),
