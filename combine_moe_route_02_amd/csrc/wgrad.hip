@@ -27,7 +27,13 @@ namespace gg {
 //     used; every launch leaves them zero).
 // When some expert is split, items (expert, split, tile) are ordered by descending expert rows and
 // dealt to the XCDs in contiguous ranges of equal row cost, so the tiles of one expert share an
-// XCD's L2 where they can.
+// XCD's L2 where they can (that static dealing serves the lists without a split). Items of a split
+// list differ in cost by orders of magnitude, so the workgroups take them from one queue (an atomic
+// counter) as they become free: the largest first, each to the first free workgroup, so that no
+// workgroup holds two of the largest items while others idle (measured: with static or per-XCD
+// dealing, the XCDs holding the heaviest expert's splits ran two of them on most of their
+// workgroups and finished last). Which workgroup computes an item does not change its result. The
+// last workgroup to leave the list resets the counters for the next launch.
 // Split plan of one weight gradient, rebuilt in LDS by every workgroup. With no split expert (the
 // usual case) only K and the per-wave partials are written: item i is then tile i % T of expert
 // i / T, and each XCD takes ceil(items / 8) consecutive items (whole rounds of equal-cost tiles).
@@ -261,21 +267,8 @@ MOE_DEV int wgrad_list(const WgradArgs& a, int first, char* ring, WgradPlan& p) 
   if (Ks < 0) return first;  // the plan depends only on the offsets: the same on every workgroup
   const int T = wgrad_tiles_per_expert<BM, BN>(a);
   const int xcd = blockIdx.x % 8, wg_per_xcd = gridDim.x / 8;
-  int maxc, lo_item, hi_item;
-  if (Ks == 0) {  // no split: expert-major tiles, ceil(items / 8) per XCD
-    const int items = a.El * T;
-    maxc = (items + 7) / 8;
-    lo_item = min(items, xcd * maxc);
-    hi_item = min(items, lo_item + maxc);
-  } else {
-    maxc = 0;
-    for (int x = 0; x < 8; ++x) maxc = max(maxc, p.xfirst[x + 1] - p.xfirst[x]);
-    lo_item = p.xfirst[xcd];
-    hi_item = p.xfirst[xcd + 1];
-  }
-  for (int gs = first_slot(first); gs < first + maxc; gs += wg_per_xcd) {
-    const int item = lo_item + (gs - first);
-    if (item >= hi_item) continue;
+  // item -> (expert, split, tile) and its rows
+  auto run_item = [&](int item) {
     int e, j;
     if (Ks == 0) {
       e = item / T;
@@ -299,6 +292,40 @@ MOE_DEV int wgrad_list(const WgradArgs& a, int first, char* ring, WgradPlan& p) 
     const int q = ke / se, r = ke - q * se;
     const int k_lo = sp * q + min(sp, r), k_hi = k_lo + q + (sp < r ? 1 : 0);
     wgrad_item<BM, BN>(a, p, e, sp, se, j - sp * T, k_lo, k_hi, ring, tid, lane, wave);
+  };
+  if (Ks > 0 && a.queue) {
+    const int n_items = p.xfirst[8];
+    for (;;) {  // every thread sees the same index: uniform exit
+      if (tid == 0) p.red[3] = atomicAdd(a.queue, 1);
+      __syncthreads();
+      const int item = p.red[3];
+      __syncthreads();
+      if (item >= n_items) break;
+      run_item(item);
+    }
+    // this workgroup takes no more items of the list; the last one to leave resets the counters
+    if (tid == 0 && atomicAdd(a.queue + 1, 1) == (int)gridDim.x - 1) {
+      a.queue[0] = 0;
+      a.queue[1] = 0;
+    }
+    return first;
+  }
+  int maxc, lo_item, hi_item;
+  if (Ks == 0) {  // no split: expert-major tiles, ceil(items / 8) per XCD
+    const int items = a.El * T;
+    maxc = (items + 7) / 8;
+    lo_item = min(items, xcd * maxc);
+    hi_item = min(items, lo_item + maxc);
+  } else {
+    maxc = 0;
+    for (int x = 0; x < 8; ++x) maxc = max(maxc, p.xfirst[x + 1] - p.xfirst[x]);
+    lo_item = p.xfirst[xcd];
+    hi_item = p.xfirst[xcd + 1];
+  }
+  for (int gs = first_slot(first); gs < first + maxc; gs += wg_per_xcd) {
+    const int item = lo_item + (gs - first);
+    if (item >= hi_item) continue;
+    run_item(item);
   }
   return first + maxc;
 }
@@ -358,13 +385,15 @@ hipError_t gg_expert_wgrad_bf16(const void* dyd, const void* dgu, const void* xd
   return run_wgrad<256, 256, 0>("gemm_wgrad", a, b, s);
 }
 
-// The layer's last weight-gradient launch: every dW1 tile, and the dW2 tiles of the experts above
-// the split threshold (rows_wgrad.hip computed the others beside the last gate/up dgrad).
+// The layer's last weight-gradient launch: the dW2 tiles of the experts above the split threshold
+// (rows_wgrad.hip computed the others beside the last gate/up dgrad), then every dW1 tile. The
+// heavy dW2 list (empty under balanced routing) goes first so that its large items are not left
+// for the end of the launch behind dW1's small ones.
 hipError_t gg_wgrad1(const ExpertGemm& g, hipStream_t s) {
   WgradArgs w1, w2;
   wgrad_args(g, w1, w2);
   w2.heavy_only = 1;
-  return run_wgrad<256, 256, 1>("gemm_wgrad_w1", w1, w2, s);
+  return run_wgrad<256, 256, 1>("gemm_wgrad_w1", w2, w1, s);
 }
 
 }  // namespace moe
