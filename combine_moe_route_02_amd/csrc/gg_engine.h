@@ -370,6 +370,9 @@ struct RowsArgs {
   // token row gather[r] (src_token), so the GEMM needs no dispatched copy of its operand
   const int32_t* gather;
   int64_t gather_rows;
+  // per-XCD next-slot counters then the exit counter (zero between launches), or null: static
+  // round-robin slots
+  int* queue;
 };
 
 template <int BM, int BN, int MODE>
@@ -394,6 +397,7 @@ struct RowsShared {
   int64_t r0[kMaxGroups];    // first dispatch row of group g
   int len[kMaxGroups];       // rows of group g
   int preb[kMaxGroups + 1];  // small tiles before group g
+  int q;                     // the slot this workgroup takes next (queued lists)
 };
 
 // Persistent work slots. Per XCD the workgroups (block b runs on XCD b % 8; W of them per XCD)
@@ -455,214 +459,250 @@ MOE_DEV int rows_list(const RowsArgs& a, int first, RowsShared& sh, char* ring) 
   // Workgroups are dealt round-robin to the 8 XCDs (block b runs on XCD b % 8); each XCD owns a
   // contiguous range of the large tiles and one of the small tiles, so the tiles of one expert
   // share that XCD's L2. An XCD's workgroups walk its large range, then its small range.
+  //
+  // With a queue (a.queue) each workgroup takes its first slot round robin and every later one from
+  // an atomic counter of its XCD as it becomes free, so a workgroup that drew short tiles takes
+  // more. The next slot is fetched after the tile's K loop (and after the epilogue's own loads):
+  // a returning atomic in flight would hold back the wave's later load counts, so fetched during
+  // the K loop it would stall every stage until it returned. Which workgroup computes a tile does
+  // not change its result. The last workgroup to leave the list resets the counters.
   const int pxl = (total_l + 7) / 8, pxs = (total_s + 7) / 8;
   const int xcd = blockIdx.x % 8, wg_per_xcd = gridDim.x / 8;
-  for (int gs = first_slot(first); gs < first + pxl + pxs; gs += wg_per_xcd) {
-    const int slot = gs - first;
+  int* const queue = a.queue;
+  int slot = first_slot(first) - first;
+  for (;;) {
+    if (slot >= pxl + pxs) break;
+    int nxt = 0;
+    auto fetch_next = [&] {
+      if (queue && tid == 0) nxt = wg_per_xcd + atomicAdd(queue + xcd, 1);
+    };
     const bool large = slot < pxl;
     const int tile = large ? xcd * pxl + slot : xcd * pxs + (slot - pxl);
-    if (tile >= (large ? total_l : total_s)) continue;
-    const int* pre = large ? s_pre : s_preb;
-    int lo = 0, hi = G;
-    while (hi - lo > 1) { const int mid = (lo + hi) >> 1; if (pre[mid] <= tile) lo = mid; else hi = mid; }
-    const int g = __builtin_amdgcn_readfirstlane(lo);
-    const int e = g % a.El;
-    const int t_in = tile - __builtin_amdgcn_readfirstlane(pre[g]);
-    const int mt = large ? t_in / ntiles : s_len[g] / BM, nt = t_in % ntiles;
-    const int64_t rg = s_r0[g];
-    const int64_t r0 = (((int64_t)__builtin_amdgcn_readfirstlane((int)(rg >> 32)) << 32) |
-                        (uint32_t)__builtin_amdgcn_readfirstlane((int)(rg & 0xffffffff))) + (int64_t)mt * BM;
-    const int mvalid = min(BM, __builtin_amdgcn_readfirstlane(s_len[g]) - mt * BM);
-    const int n0 = nt * OUTN;
-    const int nvalid = min(OUTN, a.N - n0);
-    const char* Be = (const char*)a.B + (int64_t)e * a.strideB * ES;
+    if (tile < (large ? total_l : total_s)) {
+      const int* pre = large ? s_pre : s_preb;
+      int lo = 0, hi = G;
+      while (hi - lo > 1) { const int mid = (lo + hi) >> 1; if (pre[mid] <= tile) lo = mid; else hi = mid; }
+      const int g = __builtin_amdgcn_readfirstlane(lo);
+      const int e = g % a.El;
+      const int t_in = tile - __builtin_amdgcn_readfirstlane(pre[g]);
+      const int mt = large ? t_in / ntiles : s_len[g] / BM, nt = t_in % ntiles;
+      const int64_t rg = s_r0[g];
+      const int64_t r0 = (((int64_t)__builtin_amdgcn_readfirstlane((int)(rg >> 32)) << 32) |
+                          (uint32_t)__builtin_amdgcn_readfirstlane((int)(rg & 0xffffffff))) + (int64_t)mt * BM;
+      const int mvalid = min(BM, __builtin_amdgcn_readfirstlane(s_len[g]) - mt * BM);
+      const int n0 = nt * OUTN;
+      const int nvalid = min(OUTN, a.N - n0);
+      const char* Be = (const char*)a.B + (int64_t)e * a.strideB * ES;
 
-    Loader<BM, false> la;
-    if constexpr (GATHER) {
-      // tile row r reads token row gather[r0 + r]; rows past the segment point one row past the
-      // end of A, which the descriptor's extent turns into zeros
-      const int32_t* gt = a.gather;
-      const int64_t gr = a.gather_rows;
-      la.init_kmajor((const char*)a.A, a.lda * ES, gr * a.lda * ES, wave, lane,
-                     [gt, r0, mvalid, gr](int r) { return r < mvalid ? (int64_t)gt[r0 + r] : gr; });
-    } else {
-      la.init_kmajor((const char*)a.A + r0 * a.lda * ES, a.lda * ES, (int64_t)mvalid * a.lda * ES, wave, lane,
-                     [](int r) { return r; });
-    }
-    Loader<BN, kBKS> lb;
-    if constexpr (kSwiGLU) {
-      // tile row r -> wave column block r / WTN; its first half are gate rows j, its second half
-      // the matching up rows I + j; readable rows run to the end of this expert's W1
-      const int I = a.I;
-      lb.init_kmajor(Be + (int64_t)n0 * a.K * ES, (int64_t)a.K * ES, (2 * (int64_t)I - n0) * a.K * ES, wave,
-                     lane, [I](int r) {
-                       const int q = r % WTN, hw = WTN / 2, j = (r / WTN) * hw + (q < hw ? q : q - hw);
-                       return q < hw ? j : I + j;
-                     });
-    } else if constexpr (MODE == kDown || FP8) {
-      lb.init_kmajor(Be + (int64_t)n0 * a.K * ES, (int64_t)a.K * ES, ((int64_t)a.N - n0) * a.K * ES, wave, lane,
-                     [](int r) { return r; });
-    } else {
-      // B(n, k) = W_e[k][n]: K-rows of N values, the tile's columns start at n0
-      lb.init_kslow(Be + (int64_t)n0 * 2, (int64_t)a.N * 2, ((int64_t)a.K * a.N - n0) * 2, wave, lane);
-    }
-
-    f32x16_t acc[TM][TN];
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) acc[tm][tn][q] = 0.f;
-
-    const int nks = a.K / (FP8 ? 64 : 32);
-    const int tma = __builtin_amdgcn_readfirstlane(max(0, min(TM, (mvalid - wm * WTM + 31) / 32)));
-    const int arow0 = wm * WTM, brow0 = wn * WTN;
-    static_assert(TM <= 4, "TM > 4");
-    switch (tma) {
-#define MOE_KL(T_) kloop<FP8, false, kBKS, BM, BN, TM, TN, (T_ <= TM ? T_ : TM)>(la, lb, ring, nks, arow0, brow0, lane, acc)
-      case 4: MOE_KL(4); break;
-      case 3: MOE_KL(3); break;
-      case 2: MOE_KL(2); break;
-      case 1: MOE_KL(1); break;
-      default: MOE_KL(0); break;
-#undef MOE_KL
-    }
-
-    // Epilogue through LDS staging (the ring is free): each wave writes its values in the MFMA
-    // layout (row m = lane & 31 of each 32-row block, 4 consecutive columns), then the workgroup
-    // stores whole rows. Rows past the expert's segment and columns past N are not stored.
-    const int mrow = wm * WTM + out_row(lane);
-    if constexpr (kSwiGLU) {
-      constexpr int W = BN / 2;                 // h / G / U columns per tile
-      char* sg = ring;                           // G, then h
-      char* su = ring + stage_bytes<BM, W>();    // U
-      float sr[TM];
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm) sr[tm] = (FP8 && mrow + tm * 32 < mvalid) ? a.scale_a[r0 + mrow + tm * 32] : 1.f;
-      const float* sb = FP8 ? a.scale_b + (int64_t)e * a.strideSB : nullptr;
-      // G and U (dequantised) into the two staging tiles
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < TN / 2; ++tn)
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const int jl = wn * (WTN / 2) + tn * 32 + out_col(gq, lane);   // column within the tile
-            float gv[4], uv[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              gv[q] = acc[tm][tn][4 * gq + q];
-              uv[q] = acc[tm][tn + TN / 2][4 * gq + q];
-              if constexpr (FP8) {
-                const int j = min(n0 + jl + q, a.N - 1);
-                gv[q] *= sr[tm] * sb[j];
-                uv[q] *= sr[tm] * sb[a.I + j];
-              }
-            }
-            const int m = mrow + tm * 32;
-            *(uint2*)(sg + m * pitch<W>() + 2 * jl) = pack4(gv[0], gv[1], gv[2], gv[3]);
-            *(uint2*)(su + m * pitch<W>() + 2 * jl) = pack4(uv[0], uv[1], uv[2], uv[3]);
-          }
-      lds_barrier();
-      if (a.C2) {
-        store_staged<BM, W, true>(sg, a.C2 + r0 * 2 * (int64_t)a.I + n0, 2 * (int64_t)a.I, mvalid, nvalid, tid);
-        store_staged<BM, W, true>(su, a.C2 + r0 * 2 * (int64_t)a.I + a.I + n0, 2 * (int64_t)a.I, mvalid, nvalid, tid);
+      Loader<BM, false> la;
+      if constexpr (GATHER) {
+        // tile row r reads token row gather[r0 + r]; rows past the segment point one row past the
+        // end of A, which the descriptor's extent turns into zeros
+        const int32_t* gt = a.gather;
+        const int64_t gr = a.gather_rows;
+        la.init_kmajor((const char*)a.A, a.lda * ES, gr * a.lda * ES, wave, lane,
+                       [gt, r0, mvalid, gr](int r) { return r < mvalid ? (int64_t)gt[r0 + r] : gr; });
+      } else {
+        la.init_kmajor((const char*)a.A + r0 * a.lda * ES, a.lda * ES, (int64_t)mvalid * a.lda * ES, wave, lane,
+                       [](int r) { return r; });
       }
-      lds_barrier();
-      // h = silu(G) * U from the FP32 accumulators
+      Loader<BN, kBKS> lb;
+      if constexpr (kSwiGLU) {
+        // tile row r -> wave column block r / WTN; its first half are gate rows j, its second half
+        // the matching up rows I + j; readable rows run to the end of this expert's W1
+        const int I = a.I;
+        lb.init_kmajor(Be + (int64_t)n0 * a.K * ES, (int64_t)a.K * ES, (2 * (int64_t)I - n0) * a.K * ES, wave,
+                       lane, [I](int r) {
+                         const int q = r % WTN, hw = WTN / 2, j = (r / WTN) * hw + (q < hw ? q : q - hw);
+                         return q < hw ? j : I + j;
+                       });
+      } else if constexpr (MODE == kDown || FP8) {
+        lb.init_kmajor(Be + (int64_t)n0 * a.K * ES, (int64_t)a.K * ES, ((int64_t)a.N - n0) * a.K * ES, wave, lane,
+                       [](int r) { return r; });
+      } else {
+        // B(n, k) = W_e[k][n]: K-rows of N values, the tile's columns start at n0
+        lb.init_kslow(Be + (int64_t)n0 * 2, (int64_t)a.N * 2, ((int64_t)a.K * a.N - n0) * 2, wave, lane);
+      }
+
+      f32x16_t acc[TM][TN];
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-        for (int tn = 0; tn < TN / 2; ++tn)
+        for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const int jl = wn * (WTN / 2) + tn * 32 + out_col(gq, lane);
-            float hv[4];
+          for (int q = 0; q < 16; ++q) acc[tm][tn][q] = 0.f;
+
+      const int nks = a.K / (FP8 ? 64 : 32);
+      const int tma = __builtin_amdgcn_readfirstlane(max(0, min(TM, (mvalid - wm * WTM + 31) / 32)));
+      const int arow0 = wm * WTM, brow0 = wn * WTN;
+      static_assert(TM <= 4, "TM > 4");
+      switch (tma) {
+#define MOE_KL(T_) kloop<FP8, false, kBKS, BM, BN, TM, TN, (T_ <= TM ? T_ : TM)>(la, lb, ring, nks, arow0, brow0, lane, acc)
+        case 4: MOE_KL(4); break;
+        case 3: MOE_KL(3); break;
+        case 2: MOE_KL(2); break;
+        case 1: MOE_KL(1); break;
+        default: MOE_KL(0); break;
+#undef MOE_KL
+      }
+      if constexpr (MODE != kDownBwd) fetch_next();
+
+      // Epilogue through LDS staging (the ring is free): each wave writes its values in the MFMA
+      // layout (row m = lane & 31 of each 32-row block, 4 consecutive columns), then the workgroup
+      // stores whole rows. Rows past the expert's segment and columns past N are not stored.
+      const int mrow = wm * WTM + out_row(lane);
+      if constexpr (kSwiGLU) {
+        constexpr int W = BN / 2;                 // h / G / U columns per tile
+        char* sg = ring;                           // G, then h
+        char* su = ring + stage_bytes<BM, W>();    // U
+        float sr[TM];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              float gv = acc[tm][tn][4 * gq + q], uv = acc[tm][tn + TN / 2][4 * gq + q];
-              if constexpr (FP8) {
-                const int j = min(n0 + jl + q, a.N - 1);
-                gv *= sr[tm] * sb[j];
-                uv *= sr[tm] * sb[a.I + j];
+        for (int tm = 0; tm < TM; ++tm)
+          sr[tm] = (FP8 && mrow + tm * 32 < mvalid) ? a.scale_a[r0 + mrow + tm * 32] : 1.f;
+        const float* sb = FP8 ? a.scale_b + (int64_t)e * a.strideSB : nullptr;
+        // G and U (dequantised) into the two staging tiles
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+          for (int tn = 0; tn < TN / 2; ++tn)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const int jl = wn * (WTN / 2) + tn * 32 + out_col(gq, lane);   // column within the tile
+              float gv[4], uv[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                gv[q] = acc[tm][tn][4 * gq + q];
+                uv[q] = acc[tm][tn + TN / 2][4 * gq + q];
+                if constexpr (FP8) {
+                  const int j = min(n0 + jl + q, a.N - 1);
+                  gv[q] *= sr[tm] * sb[j];
+                  uv[q] *= sr[tm] * sb[a.I + j];
+                }
               }
-              hv[q] = gv * sigmoidf_(gv) * uv;
+              const int m = mrow + tm * 32;
+              *(uint2*)(sg + m * pitch<W>() + 2 * jl) = pack4(gv[0], gv[1], gv[2], gv[3]);
+              *(uint2*)(su + m * pitch<W>() + 2 * jl) = pack4(uv[0], uv[1], uv[2], uv[3]);
             }
-            const int m = mrow + tm * 32;
-            *(uint2*)(sg + m * pitch<W>() + 2 * jl) = pack4(hv[0], hv[1], hv[2], hv[3]);
-          }
-      lds_barrier();
-      store_staged<BM, W>(sg, a.C + r0 * a.ldc + n0, a.ldc, mvalid, nvalid, tid);
-      lds_barrier();
-    } else if constexpr (MODE == kDownBwd) {
-      // G and U of the tile's rows and columns, staged coalesced; dG and dU overwrite them in place
-      constexpr int W = BN;
-      char* sg = ring;
-      char* su = ring + stage_bytes<BM, W>();
-      const int64_t I2 = 2 * (int64_t)a.I;
-      load_staged<BM, W>(sg, a.aux + r0 * I2 + n0, I2, mvalid, nvalid, tid);
-      load_staged<BM, W>(su, a.aux + r0 * I2 + a.I + n0, I2, mvalid, nvalid, tid);
-      float sr[TM];
+        lds_barrier();
+        if (a.C2) {
+          store_staged<BM, W, true>(sg, a.C2 + r0 * 2 * (int64_t)a.I + n0, 2 * (int64_t)a.I, mvalid, nvalid, tid);
+          store_staged<BM, W, true>(su, a.C2 + r0 * 2 * (int64_t)a.I + a.I + n0, 2 * (int64_t)a.I, mvalid, nvalid, tid);
+        }
+        lds_barrier();
+        // h = silu(G) * U from the FP32 accumulators
 #pragma unroll
-      for (int tm = 0; tm < TM; ++tm) sr[tm] = (FP8 && mrow + tm * 32 < mvalid) ? a.scale_a[r0 + mrow + tm * 32] : 1.f;
-      lds_barrier();
+        for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
+          for (int tn = 0; tn < TN / 2; ++tn)
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
+            for (int gq = 0; gq < 4; ++gq) {
+              const int jl = wn * (WTN / 2) + tn * 32 + out_col(gq, lane);
+              float hv[4];
 #pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const int jl = wn * WTN + tn * 32 + out_col(gq, lane);
-            const int m = mrow + tm * 32;
-            char* pg = sg + m * pitch<W>() + 2 * jl;
-            char* pu = su + m * pitch<W>() + 2 * jl;
-            float gv[4], uv[4], dg[4], du[4];
-            unpack4(*(const uint2*)pg, gv);
-            unpack4(*(const uint2*)pu, uv);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              float dh = acc[tm][tn][4 * gq + q];
-              if constexpr (FP8) dh *= sr[tm] * a.scale_b[(int64_t)e * a.strideSB + min(n0 + jl + q, a.N - 1)];
-              const float sgm = sigmoidf_(gv[q]);
-              dg[q] = dh * uv[q] * sgm * (1.f + gv[q] * (1.f - sgm));
-              du[q] = dh * gv[q] * sgm;
+              for (int q = 0; q < 4; ++q) {
+                float gv = acc[tm][tn][4 * gq + q], uv = acc[tm][tn + TN / 2][4 * gq + q];
+                if constexpr (FP8) {
+                  const int j = min(n0 + jl + q, a.N - 1);
+                  gv *= sr[tm] * sb[j];
+                  uv *= sr[tm] * sb[a.I + j];
+                }
+                hv[q] = gv * sigmoidf_(gv) * uv;
+              }
+              const int m = mrow + tm * 32;
+              *(uint2*)(sg + m * pitch<W>() + 2 * jl) = pack4(hv[0], hv[1], hv[2], hv[3]);
             }
-            *(uint2*)pg = pack4(dg[0], dg[1], dg[2], dg[3]);
-            *(uint2*)pu = pack4(du[0], du[1], du[2], du[3]);
-          }
-      lds_barrier();
-      store_staged<BM, W>(sg, a.C + r0 * I2 + n0, I2, mvalid, nvalid, tid);
-      store_staged<BM, W>(su, a.C + r0 * I2 + a.I + n0, I2, mvalid, nvalid, tid);
-      lds_barrier();
+        lds_barrier();
+        store_staged<BM, W>(sg, a.C + r0 * a.ldc + n0, a.ldc, mvalid, nvalid, tid);
+        lds_barrier();
+      } else if constexpr (MODE == kDownBwd) {
+        // G and U of the tile's rows and columns, staged coalesced; dG and dU overwrite them in place
+        constexpr int W = BN;
+        char* sg = ring;
+        char* su = ring + stage_bytes<BM, W>();
+        const int64_t I2 = 2 * (int64_t)a.I;
+        load_staged<BM, W>(sg, a.aux + r0 * I2 + n0, I2, mvalid, nvalid, tid);
+        load_staged<BM, W>(su, a.aux + r0 * I2 + a.I + n0, I2, mvalid, nvalid, tid);
+        fetch_next();
+        float sr[TM];
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+          sr[tm] = (FP8 && mrow + tm * 32 < mvalid) ? a.scale_a[r0 + mrow + tm * 32] : 1.f;
+        lds_barrier();
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const int jl = wn * WTN + tn * 32 + out_col(gq, lane);
+              const int m = mrow + tm * 32;
+              char* pg = sg + m * pitch<W>() + 2 * jl;
+              char* pu = su + m * pitch<W>() + 2 * jl;
+              float gv[4], uv[4], dg[4], du[4];
+              unpack4(*(const uint2*)pg, gv);
+              unpack4(*(const uint2*)pu, uv);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                float dh = acc[tm][tn][4 * gq + q];
+                if constexpr (FP8) dh *= sr[tm] * a.scale_b[(int64_t)e * a.strideSB + min(n0 + jl + q, a.N - 1)];
+                const float sgm = sigmoidf_(gv[q]);
+                dg[q] = dh * uv[q] * sgm * (1.f + gv[q] * (1.f - sgm));
+                du[q] = dh * gv[q] * sgm;
+              }
+              *(uint2*)pg = pack4(dg[0], dg[1], dg[2], dg[3]);
+              *(uint2*)pu = pack4(du[0], du[1], du[2], du[3]);
+            }
+        lds_barrier();
+        store_staged<BM, W>(sg, a.C + r0 * I2 + n0, I2, mvalid, nvalid, tid);
+        store_staged<BM, W>(su, a.C + r0 * I2 + a.I + n0, I2, mvalid, nvalid, tid);
+        lds_barrier();
+      } else {
+        constexpr int W = BN;
+        float sr[TM];
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+          sr[tm] = (FP8 && mrow + tm * 32 < mvalid) ? a.scale_a[r0 + mrow + tm * 32] : 1.f;
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const int nl = wn * WTN + tn * 32 + out_col(gq, lane);
+              float v[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                v[q] = acc[tm][tn][4 * gq + q];
+                if constexpr (FP8) v[q] *= sr[tm] * a.scale_b[(int64_t)e * a.strideSB + min(n0 + nl + q, a.N - 1)];
+              }
+              *(uint2*)(ring + (mrow + tm * 32) * pitch<W>() + 2 * nl) = pack4(v[0], v[1], v[2], v[3]);
+            }
+        lds_barrier();
+        if constexpr (QOUT)
+          store_staged_q<BM, W>(ring, a.Cq + r0 * a.ldc + n0, a.ldc, a.Cs + r0 * a.ldcs + n0 / W, a.ldcs, mvalid,
+                                nvalid, tid);
+        else
+          store_staged<BM, W>(ring, a.C + r0 * a.ldc + n0, a.ldc, mvalid, nvalid, tid);
+        lds_barrier();
+      }
     } else {
-      constexpr int W = BN;
-      float sr[TM];
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm) sr[tm] = (FP8 && mrow + tm * 32 < mvalid) ? a.scale_a[r0 + mrow + tm * 32] : 1.f;
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const int nl = wn * WTN + tn * 32 + out_col(gq, lane);
-            float v[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              v[q] = acc[tm][tn][4 * gq + q];
-              if constexpr (FP8) v[q] *= sr[tm] * a.scale_b[(int64_t)e * a.strideSB + min(n0 + nl + q, a.N - 1)];
-            }
-            *(uint2*)(ring + (mrow + tm * 32) * pitch<W>() + 2 * nl) = pack4(v[0], v[1], v[2], v[3]);
-          }
-      lds_barrier();
-      if constexpr (QOUT)
-        store_staged_q<BM, W>(ring, a.Cq + r0 * a.ldc + n0, a.ldc, a.Cs + r0 * a.ldcs + n0 / W, a.ldcs, mvalid,
-                              nvalid, tid);
-      else
-        store_staged<BM, W>(ring, a.C + r0 * a.ldc + n0, a.ldc, mvalid, nvalid, tid);
-      lds_barrier();
+      fetch_next();  // no such tile in this XCD's range
     }
+    if (queue) {
+      if (tid == 0) sh.q = nxt;
+      __syncthreads();
+      slot = sh.q;
+      __syncthreads();  // every thread has read it before the next write
+    } else {
+      slot += wg_per_xcd;
+    }
+  }
+  if (queue) {
+    if (tid == 0 && atomicAdd(queue + 8, 1) == (int)gridDim.x - 1) {
+#pragma unroll
+      for (int x = 0; x < 9; ++x) queue[x] = 0;
+    }
+    return first;
   }
   return first + pxl + pxs;
 }

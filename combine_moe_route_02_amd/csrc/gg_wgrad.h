@@ -64,21 +64,16 @@ MOE_DEV void wgrad_store(const WgradArgs& a, int grp, int m0, int n0, char* ring
 
 using gg::WgradArgs;
 
-// Weight-gradient scratch (inside the caller's workspace): the per-(expert, tile) arrival
-// counters of dW1 then dW2, the work-queue counters of dW1 and of dW2 (kWgradQueueInts each),
-// padded to 256 bytes, then the partial slots of dW1 and of dW2 (256 x 256 FP32 tiles each). The
-// counters must be zero when the scratch is first used; every launch leaves them zero.
+// Weight-gradient partial slots: 256 x 256 FP32 tiles of dW1 and of dW2 after the counter area
+// (launch.h: gemm_queue).
 constexpr int kWgradTile = 256;
 constexpr int kWgradSlots = 192;  // partial tiles per weight gradient at most
-constexpr int kWgradQueueInts = 16;  // the item counter, the exit counter, padding
-inline int64_t wgrad_tiles_1(int H, int I) { return (int64_t)((2 * I + 255) / 256) * ((H + 255) / 256); }
-inline int64_t wgrad_tiles_2(int H, int I) { return (int64_t)((H + 255) / 256) * ((I + 255) / 256); }
 inline int64_t wgrad_slots(int64_t tiles_per_expert, int El) {
   const int64_t cap = 4 * tiles_per_expert * El;
   return cap < kWgradSlots ? cap : kWgradSlots;
 }
 inline int64_t wgrad_counter_bytes(int H, int I, int El) {
-  return (((int64_t)El * (wgrad_tiles_1(H, I) + wgrad_tiles_2(H, I)) + 2 * kWgradQueueInts) * 4 + 255) / 256 * 256;
+  return (((int64_t)El * (wgrad_tiles_1(H, I) + wgrad_tiles_2(H, I)) + kQueueBlocks * kQueueInts) * 4 + 255) / 256 * 256;
 }
 
 
@@ -98,8 +93,8 @@ inline void wgrad_args(const ExpertGemm& g, WgradArgs& w1, WgradArgs& w2) {
     const int64_t slot = (int64_t)kWgradTile * kWgradTile;  // floats
     w1.cnt = (int*)ws;
     w2.cnt = (int*)ws + g.El * t1;
-    w1.queue = (int*)ws + g.El * (t1 + t2);
-    w2.queue = w1.queue + kWgradQueueInts;
+    w1.queue = gemm_queue(g, kQueueWgrad1);
+    w2.queue = gemm_queue(g, kQueueWgrad2);
     float* parts = (float*)(ws + wgrad_counter_bytes(g.H, g.I, g.El));
     w1.slots = (int)wgrad_slots(t1, g.El);
     w2.slots = (int)wgrad_slots(t2, g.El);

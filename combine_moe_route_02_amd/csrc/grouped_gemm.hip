@@ -29,12 +29,13 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(RowsArgs a) {
 
 // Two independent row-grouped GEMMs in one persistent launch: the second's tiles fill the
 // workgroups that the first leaves idle in its last round, and one kernel boundary goes away.
-template <int BM1, int BN1, int MODE1, int BM2, int BN2, int MODE2, bool Q1>
+// Q1 / Q2: that list writes block-scaled FP8 rows.
+template <int BM1, int BN1, int MODE1, int BM2, int BN2, int MODE2, bool Q1, bool Q2>
 __global__ __launch_bounds__(kThreads) void rows_pair_kernel(RowsArgs a, RowsArgs b) {
   __shared__ RowsShared sh;
   extern __shared__ __attribute__((aligned(1024))) char ring[];
   const int f = rows_list<BM1, BN1, MODE1, false, Q1>(a, 0, sh, ring);
-  rows_list<BM2, BN2, MODE2, false>(b, f, sh, ring);
+  rows_list<BM2, BN2, MODE2, false, Q2>(b, f, sh, ring);
 }
 
 // FP8 weight gradients. Both operands hold, per expert, the columns of its rows (every chunk's)
@@ -163,9 +164,11 @@ template <int BM1, int BN1, int MODE1, int BM2, int BN2, int MODE2>
 static hipError_t run_pair(const char* name, const RowsArgs& a, const RowsArgs& b, hipStream_t s) {
   const size_t l1 = rows_lds_bytes<BM1, BN1, MODE1>(), l2 = rows_lds_bytes<BM2, BN2, MODE2>();
   const size_t lds = l1 > l2 ? l1 : l2;
-  constexpr bool kQ = (MODE1 == kDown || MODE1 == kGateUpBwd) && BN1 == 256;
-  auto k = (kQ && a.Cq) ? rows_pair_kernel<BM1, BN1, MODE1, BM2, BN2, MODE2, kQ>
-                        : rows_pair_kernel<BM1, BN1, MODE1, BM2, BN2, MODE2, false>;
+  // FP8 output rows: only the second list of a pair has them (the gate/up dgrad's dxd)
+  constexpr bool kQ2 = (MODE2 == kDown || MODE2 == kGateUpBwd) && BN2 == 256;
+  if (a.Cq) return hipErrorInvalidValue;
+  auto k = (kQ2 && b.Cq) ? rows_pair_kernel<BM1, BN1, MODE1, BM2, BN2, MODE2, false, kQ2>
+                         : rows_pair_kernel<BM1, BN1, MODE1, BM2, BN2, MODE2, false, false>;
   hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int64_t grid = persistent_grid(rows_tiles_bound<BM1, BN1, MODE1>(a) + rows_tiles_bound<BM2, BN2, MODE2>(b));
@@ -201,29 +204,40 @@ hipError_t gg_expert_dgrad_bf16(const void* dyd, const void* gu, const void* w1,
 }
 
 // Launches of the layer schedule (one chunk each; the pairs take independent work of two steps).
+// Their lists take tiles from the work queues in the expert-GEMM scratch: a workgroup that drew
+// short tiles takes more, so a launch ends closer to its mean workgroup time. A pair runs the list
+// with the longer tiles first and the shorter tiles fill the end (measured with per-tile timing:
+// with round-robin slots the pairs ended 11-21 us after their mean workgroup).
+static RowsArgs queued(RowsArgs a, const ExpertGemm& g, int which) {
+  a.queue = gemm_queue(g, which);
+  return a;
+}
 hipError_t gg_gateup(const ExpertGemm& g, int c, hipStream_t s) {
-  return run_rows<MOE_GATEUP, false>("gemm_gateup_swiglu", gateup_args(g, c, 1), s);
+  return run_rows<MOE_GATEUP, false>("gemm_gateup_swiglu", queued(gateup_args(g, c, 1), g, kQueueRows1), s);
 }
 hipError_t gg_gateup_gather(const ExpertGemm& g, int c, const void* x, const int32_t* src_token, int64_t T,
                             hipStream_t s) {
-  RowsArgs a = gateup_args(g, c, 1);
+  RowsArgs a = queued(gateup_args(g, c, 1), g, kQueueRows1);
   a.A = x;
   a.gather = src_token;
   a.gather_rows = T;
   return run_rows<MOE_GATEUP, false>("gemm_gateup_swiglu", a, s);
 }
 hipError_t gg_down(const ExpertGemm& g, int c, hipStream_t s) {
-  return run_rows<MOE_DOWN, false>("gemm_down", down_args(g, c, 1), s);
+  return run_rows<MOE_DOWN, false>("gemm_down", queued(down_args(g, c, 1), g, kQueueRows1), s);
 }
 hipError_t gg_down_then_gateup(const ExpertGemm& g, int c, int c2, hipStream_t s) {
-  return run_pair<MOE_DOWN, MOE_GATEUP>("gemm_down+gateup_swiglu", down_args(g, c, 1), gateup_args(g, c2, 1), s);
+  return run_pair<MOE_GATEUP, MOE_DOWN>("gemm_down+gateup_swiglu",
+                                        queued(gateup_args(g, c2, 1), g, kQueueRows1),
+                                        queued(down_args(g, c, 1), g, kQueueRows2), s);
 }
 hipError_t gg_down_dgrad(const ExpertGemm& g, int c, hipStream_t s) {
-  return run_rows<MOE_DDGRAD, false>("gemm_down_dgrad_swiglu", down_dgrad_args(g, c, 1), s);
+  return run_rows<MOE_DDGRAD, false>("gemm_down_dgrad_swiglu", queued(down_dgrad_args(g, c, 1), g, kQueueRows1), s);
 }
 hipError_t gg_gateup_dgrad_then_down_dgrad(const ExpertGemm& g, int c, int c2, hipStream_t s) {
-  return run_pair<MOE_GUDGRAD, MOE_DDGRAD>("gemm_gateup_dgrad+down_dgrad_swiglu", gateup_dgrad_args(g, c, 1),
-                                           down_dgrad_args(g, c2, 1), s);
+  return run_pair<MOE_DDGRAD, MOE_GUDGRAD>("gemm_gateup_dgrad+down_dgrad_swiglu",
+                                           queued(down_dgrad_args(g, c2, 1), g, kQueueRows1),
+                                           queued(gateup_dgrad_args(g, c, 1), g, kQueueRows2), s);
 }
 
 // FP8 forward: gate/up on FP8 MFMA with s_row * s_col dequantisation and SwiGLU -> h (BF16);

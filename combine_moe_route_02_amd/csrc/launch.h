@@ -114,6 +114,19 @@ struct ExpertGemm {
   void* wgrad_ws;  // weight-gradient scratch (counters zero between launches), wgrad_scratch_bytes
   float* dxd_scales;  // non-null: dxd holds block-scaled e4m3 codes [P, H] and these scales [P, ceil(H/256)]
 };
+// Expert-GEMM scratch (ExpertGemm::wgrad_ws): a zeroed counter area, then the weight gradients'
+// partial tiles. The counter area holds the per-(expert, 256 x 256 tile) arrival counters of dW1
+// and of dW2, then four work-queue blocks of kQueueInts counters: the split dW1 and dW2 lists,
+// and the first and second row-grouped list of a layer launch. Every launch leaves them zero.
+inline int64_t wgrad_tiles_1(int H, int I) { return (int64_t)((2 * I + 255) / 256) * ((H + 255) / 256); }
+inline int64_t wgrad_tiles_2(int H, int I) { return (int64_t)((H + 255) / 256) * ((I + 255) / 256); }
+constexpr int kQueueInts = 16;
+constexpr int kQueueBlocks = 4;
+enum { kQueueWgrad1 = 0, kQueueWgrad2 = 1, kQueueRows1 = 2, kQueueRows2 = 3 };
+inline int* gemm_queue(const ExpertGemm& g, int which) {
+  if (!g.wgrad_ws || g.El <= 0) return nullptr;
+  return (int*)g.wgrad_ws + (int64_t)g.El * (wgrad_tiles_1(g.H, g.I) + wgrad_tiles_2(g.H, g.I)) + which * kQueueInts;
+}
 // weight-gradient scratch: its size, and the bytes of its leading counters (zero when first used)
 int64_t wgrad_scratch_bytes(int H, int I, int El);
 int64_t wgrad_counter_bytes_of(int H, int I, int El);

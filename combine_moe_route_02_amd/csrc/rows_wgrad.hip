@@ -118,6 +118,9 @@ using namespace gg;
 hipError_t gg_gateup_dgrad_then_wgrad2(const ExpertGemm& g, int c, hipStream_t s) {
   WgradArgs w1, w2;
   wgrad_args(g, w1, w2);
+  // round-robin slots for both lists: the dW2 tiles continue the row tiles' slot sequence, so the
+  // workgroups with fewer row tiles start on them first (a work queue for the row tiles alone,
+  // with the dW2 tiles then dealt from slot 0, measured 151 against 132 us)
   return run_rows_wgrad<MOE_GUDGRAD, 256, 256>("gemm_gateup_dgrad+wgrad_w2", gateup_dgrad_args(g, c, 1), w2, s);
 }
 

@@ -99,10 +99,11 @@ def test_workspace_bytes():
     assert ws["out"] == 131072 * 2048 * 2                     # fresh [P_out, H] BF16 output
     assert ws["dw1"] == 16 * 1536 * 2048 * 2 and ws["dwr_acc"] == 128 * 2048 * 4
     # routing / router scratch first, then the expert weight gradients' scratch at a 256-byte boundary:
-    # per-(expert, tile) counters of dW1 (6 x 8 tiles) and dW2 (8 x 3 tiles), the two work-queue
-    # counter blocks (16 ints each), then the partial slots
+    # per-(expert, tile) counters of dW1 (6 x 8 tiles) and dW2 (8 x 3 tiles), four work-queue
+    # counter blocks (16 ints each: the split dW1 and dW2 lists, two row-grouped lists), then the
+    # partial slots
     base = (max(ws["route_scratch"], ws["route_bwd_scratch"]) + 255) // 256 * 256
-    assert ws["wgrad_zero_bytes"] == ((16 * (48 + 24) + 2 * 16) * 4 + 255) // 256 * 256
+    assert ws["wgrad_zero_bytes"] == ((16 * (48 + 24) + 4 * 16) * 4 + 255) // 256 * 256
     assert ws["wgrad_scratch"] == ws["wgrad_zero_bytes"] + 2 * 192 * 256 * 256 * 4
     assert ws["workspace"] == base + ws["wgrad_scratch"] > 0
     f8 = mh.make_desc(T=16384, H=2048, I=768, E=128, E_local=16, k=8, n_chunks=2, dtype="fp8")
