@@ -810,8 +810,11 @@ static bool merged_bwd(const moe_desc* d) { return merged_gemms(d) && (d->flags 
 
 //   compute: R0 D0 GU0 | wait(disp1) [DN0 GU1] | wait(disp2) [DN1 GU2] | ... | DN n-1, C n-1
 //   aux:     wait(disp0) R1 D1 | R2 D2, wait(ffn0) C0 | R3 D3, wait(ffn1) C1 | ...
+// defer_last (fused primitive, two streams): the aux stream waits for the last chunk's GEMMs but
+// leaves that chunk's combine to the backward schedule, which issues it after the next combine
+// backward (nothing in the step reads `out`).
 static moe_status forward_sched_merged(const moe_desc* d, const moe_tensors* t, hipStream_t cs, hipStream_t as,
-                                       bool join) {
+                                       bool join, bool defer_last = false) {
   const int n = d->n_chunks;
   const bool two = cs != as && n > 1;
   const hipStream_t side = two ? as : cs;
@@ -869,7 +872,7 @@ static moe_status forward_sched_merged(const moe_desc* d, const moe_tensors* t, 
         MOE_HIP(hipEventRecord(ffn[c], cs), "hipEventRecord");
         MOE_HIP(hipStreamWaitEvent(as, ffn[c], 0), "hipStreamWaitEvent");
       }
-      MOE_TRY(moe_combine(d, c, t->yd, t->gates, t->row_of, t->out, side));
+      if (!(two && defer_last && c + 1 == n)) MOE_TRY(moe_combine(d, c, t->yd, t->gates, t->row_of, t->out, side));
     } else {
       MOE_TRY(moe_combine(d, c, t->yd, t->gates, t->row_of, t->out, cs));
     }
@@ -881,9 +884,13 @@ static moe_status forward_sched_merged(const moe_desc* d, const moe_tensors* t, 
   return MOE_OK;
 }
 
-//   compute: CB0 DDG0 | wait(cb1) [GUDG0 DDG1] | ... | [GUDG n-1, dW2], dW1, wait(done)
-//   aux:     wait(cb0) CB1 RB0 | CB2 RB1 wait(dg0) DB0 | CB3 RB2 wait(dg1) DB1 | ... | wait(dg n-1) DB n-1
-static moe_status backward_sched_merged(const moe_desc* d, const moe_tensors* t, hipStream_t cs, hipStream_t as) {
+//   compute: CB0 DDG0 | wait(cb1) [DDG1 GUDG0] | ... | [GUDG n-1, dW2], dW1, wait(done)
+//   aux:     CB1 (C n-1) wait(cb0) RB0 | CB2 RB1 wait(dg0) DB0 | CB3 RB2 wait(dg1) DB1 | ... | wait(dg n-1) DB n-1
+// (C n-1: the fused primitive's deferred last combine of the forward)
+// deferred_combine: the forward left its last chunk's combine to this schedule (fused primitive);
+// it runs on aux after chunk 1's combine backward.
+static moe_status backward_sched_merged(const moe_desc* d, const moe_tensors* t, hipStream_t cs, hipStream_t as,
+                                        bool deferred_combine = false) {
   const int n = d->n_chunks;
   const bool two = cs != as;
   const hipStream_t side = two ? as : cs;
@@ -901,14 +908,16 @@ static moe_status backward_sched_merged(const moe_desc* d, const moe_tensors* t,
                          t->workspace, side);
   };
   MOE_TRY(combine_bwd(0, cs));
-  if (two) {
-    MOE_HIP(hipEventRecord(cb[0], cs), "hipEventRecord");
-    MOE_HIP(hipStreamWaitEvent(as, cb[0], 0), "hipStreamWaitEvent");
-  }
+  if (two) MOE_HIP(hipEventRecord(cb[0], cs), "hipEventRecord");
+  // chunk 1's combine backward does not need chunk 0's: aux starts it at once (the compute stream
+  // waits for it before the next dgrad launch), then the forward's deferred combine, then waits
+  // for chunk 0's combine backward, whose dgates route backward 0 reads
   if (n > 1) {
     MOE_TRY(combine_bwd(1, side));
     if (two) MOE_HIP(hipEventRecord(cb[1], as), "hipEventRecord");
   }
+  if (deferred_combine) MOE_TRY(moe_combine(d, n - 1, t->yd, t->gates, t->row_of, t->out, side));
+  if (two) MOE_HIP(hipStreamWaitEvent(as, cb[0], 0), "hipStreamWaitEvent");
   MOE_TRY(route_bwd(0));
   MOE_HIP(moe::gg_down_dgrad(g, 0, cs), "expert_dgrad");
   for (int c = 0; c < n; ++c) {
@@ -959,11 +968,16 @@ moe_status moe_layer_forward_backward(const moe_desc* d, const moe_tensors* t, v
   MOE_TRY(check_bwd_tensors(d, t));
   // no join between the two: the backward's first wait of the auxiliary stream follows the
   // whole forward on the compute stream, and its final join covers the forward's aux work
+  // with both schedules merged and two streams (n > 1) the forward's last combine moves behind
+  // chunk 1's combine backward on aux: that combine backward gates the compute stream's next
+  // dgrad launch, the combine gates nothing in the step
+  const bool defer = merged_gemms(d) && merged_bwd(d) && compute_stream != aux_stream && d->n_chunks > 1;
   if (merged_gemms(d))
-    MOE_TRY(forward_sched_merged(d, t, (hipStream_t)compute_stream, (hipStream_t)aux_stream, false));
+    MOE_TRY(forward_sched_merged(d, t, (hipStream_t)compute_stream, (hipStream_t)aux_stream, false, defer));
   else
     MOE_TRY(forward_sched(d, t, (hipStream_t)compute_stream, (hipStream_t)aux_stream, false));
-  if (merged_bwd(d)) return backward_sched_merged(d, t, (hipStream_t)compute_stream, (hipStream_t)aux_stream);
+  if (merged_bwd(d))
+    return backward_sched_merged(d, t, (hipStream_t)compute_stream, (hipStream_t)aux_stream, defer);
   return backward_sched(d, t, (hipStream_t)compute_stream, (hipStream_t)aux_stream);
 }
 

@@ -14,9 +14,11 @@
 namespace moe {
 namespace gg {
 
-// Tile `tile` (expert-major) of a weight gradient over all of its expert's rows.
-template <int BM, int BN>
-MOE_DEV void wgrad_tile_full(const WgradArgs& a, int grp, int t_in, char* ring, int tid, int lane, int wave) {
+// Tile `tile` (expert-major) of a weight gradient over all of its expert's rows; after_k runs once
+// its K loops are done (before the staging of the result).
+template <int BM, int BN, class AfterK>
+MOE_DEV void wgrad_tile_full(const WgradArgs& a, int grp, int t_in, char* ring, int tid, int lane, int wave,
+                             AfterK&& after_k) {
   constexpr int WTM = BM / kWM, WTN = BN / kWN, TM = WTM / 32, TN = WTN / 32;
   const int wm = wave / kWN, wn = wave % kWN;
   const int ntiles = (a.N + BN - 1) / BN;
@@ -43,6 +45,7 @@ MOE_DEV void wgrad_tile_full(const WgradArgs& a, int grp, int t_in, char* ring, 
     const int nks = (len + kKRows - 1) / kKRows;
     kloop<false, true, true, BM, BN, TM, TN, TM>(la, lb, ring, nks, wm * WTM, wn * WTN, lane, acc);
   }
+  after_k();
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
@@ -55,11 +58,14 @@ MOE_DEV void wgrad_tile_full(const WgradArgs& a, int grp, int t_in, char* ring, 
   wgrad_store<BM, BN>(a, grp, m0, n0, ring, tid);
 }
 
-// The light experts' tiles in the slot sequence of rows_list from per-XCD slot `first` on: every
-// expert's tiles are dealt as in the unsplit weight gradient (expert-major, ceil(items / 8) per
-// XCD) and the heavy experts' slots stay empty. Returns the slot after the last.
+// The light experts' tiles (expert-major, ceil(items / 8) per XCD as in the unsplit weight
+// gradient; the heavy experts' slots stay empty). Round robin: in the slot sequence of rows_list
+// from per-XCD slot `first` on; returns the slot after the last. With a queue (a.queue) every
+// workgroup takes its XCD's slots from an atomic counter (fetched after each tile's K loops: a
+// returning atomic in flight would hold back the K loop's load counts), and the last workgroup to
+// leave resets the counters.
 template <int BM, int BN>
-MOE_DEV int wgrad_list_light(const WgradArgs& a, int first, char* ring) {
+MOE_DEV int wgrad_list_light(const WgradArgs& a, int first, char* ring, int* q) {
   if (a.El <= 0) return first;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -69,17 +75,48 @@ MOE_DEV int wgrad_list_light(const WgradArgs& a, int first, char* ring) {
   for (int c = 0; c < a.n_chunks; ++c) total += a.offsets[(int64_t)c * (a.El + 1) + a.El];
   const long long Ks0 = wgrad_ks0(total, T);
   const int xcd = blockIdx.x % 8, wg_per_xcd = gridDim.x / 8;
-  for (int gs = first_slot(first); gs < first + px; gs += wg_per_xcd) {
-    const int item = xcd * px + (gs - first);
-    if (item >= items) continue;
-    const int e = item / T;
-    int ke = 0;
-    for (int c = 0; c < a.n_chunks; ++c) {
-      const int32_t* off = a.offsets + (int64_t)c * (a.El + 1);
-      ke += off[e + 1] - off[e];
+  int* const queue = a.queue;
+  if (queue) {
+    __syncthreads();  // every thread has read *q in the list before
+    if (tid == 0) *q = atomicAdd(queue + xcd, 1);
+  }
+  int slot = first_slot(first) - first;
+  for (;;) {
+    if (queue) {
+      __syncthreads();
+      slot = *q;
+      __syncthreads();  // every thread has read it before the next write
     }
-    if (ke > Ks0) continue;  // heavy: the weight-gradient launch that follows splits it
-    wgrad_tile_full<BM, BN>(a, e, item - e * T, ring, tid, lane, wave);
+    if (slot >= px) break;
+    int nxt = 0;
+    auto fetch_next = [&] {
+      if (queue && tid == 0) nxt = atomicAdd(queue + xcd, 1);
+    };
+    const int item = xcd * px + slot;
+    int e = -1, ke = 0;
+    if (item < items) {
+      e = item / T;
+      for (int c = 0; c < a.n_chunks; ++c) {
+        const int32_t* off = a.offsets + (int64_t)c * (a.El + 1);
+        ke += off[e + 1] - off[e];
+      }
+    }
+    if (e >= 0 && ke <= Ks0)  // heavy experts: the weight-gradient launch that follows splits them
+      wgrad_tile_full<BM, BN>(a, e, item - e * T, ring, tid, lane, wave, fetch_next);
+    else
+      fetch_next();
+    if (queue) {
+      if (tid == 0) *q = nxt;
+    } else {
+      slot += wg_per_xcd;
+    }
+  }
+  if (queue) {
+    if (tid == 0 && atomicAdd(queue + 8, 1) == (int)gridDim.x - 1) {
+#pragma unroll
+      for (int x = 0; x < 9; ++x) queue[x] = 0;
+    }
+    return first;
   }
   return first + px;
 }
@@ -89,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void rows_wgrad_kernel(RowsArgs r, WgradA
   __shared__ RowsShared sh;
   extern __shared__ __attribute__((aligned(1024))) char ring[];
   const int f = rows_list<BM1, BN1, MODE1, false, Q1>(r, 0, sh, ring);
-  wgrad_list_light<BM, BN>(a, f, ring);
+  wgrad_list_light<BM, BN>(a, f, ring, &sh.q);
 }
 
 template <int BM1, int BN1, int MODE1, int BM, int BN>
@@ -118,10 +155,12 @@ using namespace gg;
 hipError_t gg_gateup_dgrad_then_wgrad2(const ExpertGemm& g, int c, hipStream_t s) {
   WgradArgs w1, w2;
   wgrad_args(g, w1, w2);
-  // round-robin slots for both lists: the dW2 tiles continue the row tiles' slot sequence, so the
-  // workgroups with fewer row tiles start on them first (a work queue for the row tiles alone,
-  // with the dW2 tiles then dealt from slot 0, measured 151 against 132 us)
-  return run_rows_wgrad<MOE_GUDGRAD, 256, 256>("gemm_gateup_dgrad+wgrad_w2", gateup_dgrad_args(g, c, 1), w2, s);
+  // both lists from work queues (a queue for the row tiles alone, with the dW2 tiles then dealt
+  // round robin from slot 0, measured 151 against 132 us for round robin throughout)
+  RowsArgs r = gateup_dgrad_args(g, c, 1);
+  r.queue = gemm_queue(g, kQueueRows1);
+  w2.queue = gemm_queue(g, kQueueRows2);
+  return run_rows_wgrad<MOE_GUDGRAD, 256, 256>("gemm_gateup_dgrad+wgrad_w2", r, w2, s);
 }
 
 }  // namespace moe

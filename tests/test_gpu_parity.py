@@ -196,6 +196,9 @@ def test_layer_launch_order_and_streams(cfg):
     cbw, dbw = streams_of("combine_bwd"), streams_of("dispatch_bwd")
     assert cbw[0] == compute and set(cbw[1:]) == {aux} and set(dbw) == {aux}
     assert set(streams_of("route_bwd_dlogits")) == {aux}
+    # the forward's last combine is issued after chunk 1's combine backward (it gates nothing)
+    combines = [i for i, nm in enumerate(names) if nm == "combine"]
+    assert combines[-1] > [i for i, nm in enumerate(names) if nm == "combine_bwd"][1]
 
 
 # ----------------------------------------------------------------------------- FP8 payload path
