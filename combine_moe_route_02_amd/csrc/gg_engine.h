@@ -52,10 +52,12 @@ MOE_DEV int ks_off(int k, int c) { return k * (2 * R) + ((c ^ ((k & 3) << 2)) <<
 // ---------------------------------------------------------------------------------------------
 // Operand tile loader: R MN rows, one stage = R * 64 bytes = R / 16 wave instructions of 1 KiB,
 // spread over the workgroup's waves.
-template <int R, bool KSLOW>
+template <int R, bool KSLOW, int LW = kWaves>
 struct Loader {
-  static constexpr int NI = R / (16 * kWaves);
-  static_assert(NI >= 1 && R % (16 * kWaves) == 0, "tile rows must cover every wave");
+  static constexpr int kLW = LW;  // waves that issue the loads (the first LW of the workgroup)
+  static constexpr int NI = R / (16 * LW);
+  static_assert(LW == kWaves || LW == kWaves / 2, "all waves, or one per SIMD");
+  static_assert(NI >= 1 && R % (16 * LW) == 0, "tile rows must cover every loading wave");
   __amdgpu_buffer_rsrc_t rb;  // buffer descriptor
   i32x4_t rs;                 // the same as words, for the loads written in assembly
   uint32_t voff[NI];
@@ -101,7 +103,7 @@ struct Loader {
   // restored; s_nop 4 covers a VALU write of an SGPR operand.
   template <bool ASM>
   MOE_DEV void issue(uint32_t stage, int s) const {
-    static_assert(NI == 1 || NI == 2, "one or two loads per wave and operand stage");
+    static_assert(NI == 1 || NI % 2 == 0, "one load, or pairs of loads, per wave and operand stage");
     const uint32_t l0 = stage + (uint32_t)(wave * NI * 1024);
     if constexpr (!ASM) {
 #pragma unroll
@@ -120,14 +122,17 @@ struct Loader {
             : "s"(lf), "v"(voff[0]), "s"(rs), "s"(so)
             : "memory");
       } else {
-        const uint32_t l1 = lf + 1024;
-        asm volatile(
-            "s_mov_b32 %0, m0\n\ts_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-            "buffer_load_dwordx4 %3, %5, %6 offen lds\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
-            "buffer_load_dwordx4 %4, %5, %6 offen lds\n\ts_mov_b32 m0, %0"
-            : "=&s"(m0s)
-            : "s"(lf), "s"(l1), "v"(voff[0]), "v"(voff[1 % NI]), "s"(rs), "s"(so)
-            : "memory");
+#pragma unroll
+        for (int i = 0; i < NI; i += 2) {
+          const uint32_t la = lf + i * 1024, lb = la + 1024;
+          asm volatile(
+              "s_mov_b32 %0, m0\n\ts_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+              "buffer_load_dwordx4 %3, %5, %6 offen lds\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+              "buffer_load_dwordx4 %4, %5, %6 offen lds\n\ts_mov_b32 m0, %0"
+              : "=&s"(m0s)
+              : "s"(la), "s"(lb), "v"(voff[i]), "v"(voff[i + 1]), "s"(rs), "s"(so)
+              : "memory");
+        }
       }
     }
   }
@@ -223,7 +228,7 @@ MOE_DEV void stage_mma(const char* sa, const char* sb, int arow0, int brow0, int
     // With a K-slow weight operand (input gradients, weight gradients) the loads go out first,
     // right after the stage barrier (measured faster there); otherwise they follow the first
     // MFMAs.
-    if constexpr (BKS) __builtin_amdgcn_sched_group_barrier(0x020, VM, 0);
+    if constexpr (BKS && VM > 0) __builtin_amdgcn_sched_group_barrier(0x020, VM, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
 #pragma unroll
     for (int i = 0; i < RD; ++i) {
@@ -252,10 +257,15 @@ MOE_DEV void kloop(const LA& la, const LB& lb, char* ring, int nks, int arow0, i
   constexpr int NL = LA::NI + LB::NI;  // load instructions per wave per stage
   constexpr bool kAsm = AKS || BKS;    // transposing reads follow: loads written in assembly
   const uint32_t rl = lds_addr(ring);
+  static_assert(LA::kLW == LB::kLW, "one set of loading waves");
+  constexpr bool kAll = LA::kLW == kWaves;
+  const bool loader = kAll || la.wave < LA::kLW;
+  if (loader) {
 #pragma unroll
-  for (int s = 0; s < kNst - 1; ++s) {
-    la.template issue<kAsm>(rl + s * SS, s);
-    lb.template issue<kAsm>(rl + s * SS + SA, s);
+    for (int s = 0; s < kNst - 1; ++s) {
+      la.template issue<kAsm>(rl + s * SS, s);
+      lb.template issue<kAsm>(rl + s * SS + SA, s);
+    }
   }
   for (int s = 0; s < nks; ++s) {
     wait_vm<(kNst - 2) * NL>();    // stage s has landed (this wave's loads)
@@ -263,10 +273,20 @@ MOE_DEV void kloop(const LA& la, const LB& lb, char* ring, int nks, int arow0, i
     const int ld = s + kNst - 1;
     const uint32_t st = rl + (ld % kNst) * SS;
     const char* cur = ring + (s % kNst) * SS;
-    stage_mma<FP8, AKS, BKS, RA, RB, TM, TN, TMA, NL>(cur, cur + SA, arow0, brow0, lane, acc, [&] {
-      la.template issue<kAsm>(st, ld);
-      lb.template issue<kAsm>(st + SA, ld);
-    });
+    if constexpr (kAll) {
+      stage_mma<FP8, AKS, BKS, RA, RB, TM, TN, TMA, NL>(cur, cur + SA, arow0, brow0, lane, acc, [&] {
+        la.template issue<kAsm>(st, ld);
+        lb.template issue<kAsm>(st + SA, ld);
+      });
+    } else {
+      // the loading waves issue the stage's loads first; the other wave on each SIMD goes
+      // straight to its fragment reads and MFMAs
+      if (loader) {
+        la.template issue<kAsm>(st, ld);
+        lb.template issue<kAsm>(st + SA, ld);
+      }
+      stage_mma<FP8, AKS, BKS, RA, RB, TM, TN, TMA, 0>(cur, cur + SA, arow0, brow0, lane, acc, [] {});
+    }
   }
   wait_vm<0>();
   __syncthreads();

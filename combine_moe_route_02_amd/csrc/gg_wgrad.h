@@ -26,6 +26,10 @@ struct WgradArgs {
   int heavy_only;
 };
 
+// Waves that issue the weight gradients' operand loads: one per SIMD, right after the stage
+// barrier, so that the other wave of each SIMD goes on issuing MFMAs while the loading wave waits
+// to issue its loads (both operands of a weight gradient are K-slow).
+constexpr int kWgradLoadWaves = kWaves / 2;
 constexpr int kWgradMinSplitRows = 512;  // never split an expert's K below this many rows
 constexpr int kWgradRefWorkers = 256;    // workers the split size is planned for
 

@@ -38,9 +38,9 @@ MOE_DEV void wgrad_tile_full(const WgradArgs& a, int grp, int t_in, char* ring, 
     const int len = __builtin_amdgcn_readfirstlane(off[grp + 1]) - o0;
     if (len <= 0) continue;
     const int64_t row0 = (int64_t)c * a.P_c + o0;
-    Loader<BM, true> la;
+    Loader<BM, true, kWgradLoadWaves> la;
     la.init_kslow(a.A + row0 * a.lda + m0, a.lda * 2, ((int64_t)len * a.lda - m0) * 2, wave, lane);
-    Loader<BN, true> lb;
+    Loader<BN, true, kWgradLoadWaves> lb;
     lb.init_kslow(a.B + row0 * a.ldb + n0, a.ldb * 2, ((int64_t)len * a.ldb - n0) * 2, wave, lane);
     const int nks = (len + kKRows - 1) / kKRows;
     kloop<false, true, true, BM, BN, TM, TN, TM>(la, lb, ring, nks, wm * WTM, wn * WTN, lane, acc);
