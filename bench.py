@@ -45,10 +45,12 @@ KERNEL_SYMBOLS = {
     "gemm_down": (("grouped_gemm.hip", "gg_engine.h"), "rows_kernel<256, 256, 1, false, false, false>"),
     "gemm_down_dgrad_swiglu": (("grouped_gemm.hip", "gg_engine.h"), "rows_kernel<128, 256, 2, false, false, false>"),
     "gemm_gateup_dgrad": (("grouped_gemm.hip", "gg_engine.h"), "rows_kernel<256, 256, 3, false, false, false>"),
+    # the fused step's pairs: down of chunk c with gate/up of chunk c+1 (reading token rows through
+    # src_token), and down dgrad of chunk c+1 with gate/up dgrad of chunk c
     "gemm_down+gateup_swiglu": (("grouped_gemm.hip", "gg_engine.h"),
-                                "rows_pair_kernel<256, 256, 0, 256, 256, 1, false, false>"),
+                                "rows_pair_kernel<256, 256, 0, 256, 256, 1, false, false, true>"),
     "gemm_gateup_dgrad+down_dgrad_swiglu": (("grouped_gemm.hip", "gg_engine.h"),
-                                            "rows_pair_kernel<128, 256, 2, 256, 256, 3, false, false>"),
+                                            "rows_pair_kernel<128, 256, 2, 256, 256, 3, false, false, false>"),
     "gemm_gateup_dgrad+wgrad_w2": (("rows_wgrad.hip", "gg_engine.h", "gg_wgrad.h"),
                                    "rows_wgrad_kernel<256, 256, 3, 256, 256, false>"),
     "gemm_wgrad_w1": (("wgrad.hip", "gg_engine.h", "gg_wgrad.h"), "wgrad_kernel<256, 256, 1>"),

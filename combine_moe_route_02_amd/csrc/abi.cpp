@@ -810,6 +810,10 @@ static bool merged_bwd(const moe_desc* d) { return merged_gemms(d) && (d->flags 
 
 //   compute: R0 D0 GU0 | wait(disp1) [DN0 GU1] | wait(disp2) [DN1 GU2] | ... | DN n-1, C n-1
 //   aux:     wait(disp0) R1 D1 | R2 D2, wait(ffn0) C0 | R3 D3, wait(ffn1) C1 | ...
+// and with two streams, when the token rows fit one buffer descriptor (gate/up reading x through
+// src_token):
+//   compute: R(all) GU0 | [DN0 GU1] | [DN1 GU2] | ... | DN n-1
+//   aux:     wait(routed) D(all) | wait(ffn0) C0 | wait(ffn1) C1 | ... | wait(ffn n-1) C n-1
 // defer_last (fused primitive, two streams): the aux stream waits for the last chunk's GEMMs but
 // leaves that chunk's combine to the backward schedule, which issues it after the next combine
 // backward (nothing in the step reads `out`).
@@ -829,20 +833,18 @@ static moe_status forward_sched_merged(const moe_desc* d, const moe_tensors* t, 
     MOE_TRY(moe_dispatch(d, c, t->x, t->row_of, t->xd, t->xd_scale, t->h_scale, s));
     return MOE_OK;
   };
-  // With two streams the first chunk's gate/up reads its rows straight from x through src_token,
-  // so only its routing precedes it on the compute stream; its dispatch (xd, which the backward
-  // and the caller read) runs on the auxiliary stream after the next chunk's routing and dispatch.
-  // No forward kernel on the compute stream reads xd of chunk 0 again; the forward's final join
-  // (layer forward) or the backward's first wait on the auxiliary stream (fused step; the kernels
-  // before it read dyd and G/U only) orders every later reader after that dispatch.
+  // With two streams the gate/up GEMMs read their rows straight from x through src_token: the
+  // compute stream routes every chunk in one launch and then runs the expert GEMMs without waiting
+  // for the auxiliary stream, which dispatches every chunk meanwhile (xd, which the backward and the
+  // caller read). No forward kernel on the compute stream reads xd; the forward's final join (layer
+  // forward) or the backward's first wait on the auxiliary stream (fused step; the kernels before
+  // it read dyd and G/U only) orders every later reader after the dispatch.
   const bool gather = two && (int64_t)d->T * d->H * 2 <= kRsrcMax;
   if (gather) {
-    MOE_TRY(route_any(d, 0, t, cs));
+    MOE_TRY(route_any(d, -1, t, cs));
     MOE_HIP(hipEventRecord(disp[0], cs), "hipEventRecord");
     MOE_HIP(hipStreamWaitEvent(as, disp[0], 0), "hipStreamWaitEvent");
-    MOE_TRY(route_dispatch(1, as));
-    MOE_HIP(hipEventRecord(disp[1], as), "hipEventRecord");
-    MOE_TRY(moe_dispatch(d, 0, t->x, t->row_of, t->xd, t->xd_scale, t->h_scale, as));
+    MOE_TRY(moe_dispatch(d, -1, t->x, t->row_of, t->xd, t->xd_scale, t->h_scale, as));
     MOE_HIP(moe::gg_gateup_gather(g, 0, t->x, t->src_token, d->T, cs), "expert_ffn");
   } else {
     MOE_TRY(route_dispatch(0, cs));
@@ -857,7 +859,9 @@ static moe_status forward_sched_merged(const moe_desc* d, const moe_tensors* t, 
     MOE_HIP(moe::gg_gateup(g, 0, cs), "expert_ffn");
   }
   for (int c = 0; c < n; ++c) {
-    if (c + 1 < n) {
+    if (c + 1 < n && gather) {
+      MOE_HIP(moe::gg_down_then_gateup_gather(g, c, c + 1, t->x, t->src_token, d->T, cs), "expert_ffn");
+    } else if (c + 1 < n) {
       if (two) MOE_HIP(hipStreamWaitEvent(cs, disp[c + 1], 0), "hipStreamWaitEvent");
       MOE_HIP(moe::gg_down_then_gateup(g, c, c + 1, cs), "expert_ffn");
       if (c + 2 < n) {

@@ -29,12 +29,13 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(RowsArgs a) {
 
 // Two independent row-grouped GEMMs in one persistent launch: the second's tiles fill the
 // workgroups that the first leaves idle in its last round, and one kernel boundary goes away.
-// Q1 / Q2: that list writes block-scaled FP8 rows.
-template <int BM1, int BN1, int MODE1, int BM2, int BN2, int MODE2, bool Q1, bool Q2>
+// Q1 / Q2: that list writes block-scaled FP8 rows. G1: the first list (a gate/up GEMM) reads its
+// token rows through src_token.
+template <int BM1, int BN1, int MODE1, int BM2, int BN2, int MODE2, bool Q1, bool Q2, bool G1 = false>
 __global__ __launch_bounds__(kThreads) void rows_pair_kernel(RowsArgs a, RowsArgs b) {
   __shared__ RowsShared sh;
   extern __shared__ __attribute__((aligned(1024))) char ring[];
-  const int f = rows_list<BM1, BN1, MODE1, false, Q1>(a, 0, sh, ring);
+  const int f = rows_list<BM1, BN1, MODE1, false, Q1, G1>(a, 0, sh, ring);
   rows_list<BM2, BN2, MODE2, false, Q2>(b, f, sh, ring);
 }
 
@@ -166,9 +167,11 @@ static hipError_t run_pair(const char* name, const RowsArgs& a, const RowsArgs& 
   const size_t lds = l1 > l2 ? l1 : l2;
   // FP8 output rows: only the second list of a pair has them (the gate/up dgrad's dxd)
   constexpr bool kQ2 = (MODE2 == kDown || MODE2 == kGateUpBwd) && BN2 == 256;
-  if (a.Cq) return hipErrorInvalidValue;
-  auto k = (kQ2 && b.Cq) ? rows_pair_kernel<BM1, BN1, MODE1, BM2, BN2, MODE2, false, kQ2>
-                         : rows_pair_kernel<BM1, BN1, MODE1, BM2, BN2, MODE2, false, false>;
+  constexpr bool kG1 = MODE1 == kGateUp;
+  if (a.Cq || (a.gather && !kG1) || b.gather) return hipErrorInvalidValue;
+  auto k = (kQ2 && b.Cq)    ? rows_pair_kernel<BM1, BN1, MODE1, BM2, BN2, MODE2, false, kQ2>
+           : (kG1 && a.gather) ? rows_pair_kernel<BM1, BN1, MODE1, BM2, BN2, MODE2, false, false, kG1>
+                               : rows_pair_kernel<BM1, BN1, MODE1, BM2, BN2, MODE2, false, false>;
   hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int64_t grid = persistent_grid(rows_tiles_bound<BM1, BN1, MODE1>(a) + rows_tiles_bound<BM2, BN2, MODE2>(b));
@@ -230,6 +233,15 @@ hipError_t gg_down_then_gateup(const ExpertGemm& g, int c, int c2, hipStream_t s
   return run_pair<MOE_GATEUP, MOE_DOWN>("gemm_down+gateup_swiglu",
                                         queued(gateup_args(g, c2, 1), g, kQueueRows1),
                                         queued(down_args(g, c, 1), g, kQueueRows2), s);
+}
+hipError_t gg_down_then_gateup_gather(const ExpertGemm& g, int c, int c2, const void* x, const int32_t* src_token,
+                                      int64_t T, hipStream_t s) {
+  RowsArgs a = queued(gateup_args(g, c2, 1), g, kQueueRows1);
+  a.A = x;
+  a.gather = src_token;
+  a.gather_rows = T;
+  return run_pair<MOE_GATEUP, MOE_DOWN>("gemm_down+gateup_swiglu", a, queued(down_args(g, c, 1), g, kQueueRows2),
+                                        s);
 }
 hipError_t gg_down_dgrad(const ExpertGemm& g, int c, hipStream_t s) {
   return run_rows<MOE_DDGRAD, false>("gemm_down_dgrad_swiglu", queued(down_dgrad_args(g, c, 1), g, kQueueRows1), s);

@@ -139,6 +139,9 @@ hipError_t gg_gateup_gather(const ExpertGemm& g, int c, const void* x, const int
                             hipStream_t s);
 hipError_t gg_down(const ExpertGemm& g, int c, hipStream_t s);
 hipError_t gg_down_then_gateup(const ExpertGemm& g, int c, int c2, hipStream_t s);
+// the same, the gate/up tiles reading chunk c2's token rows from x through src_token
+hipError_t gg_down_then_gateup_gather(const ExpertGemm& g, int c, int c2, const void* x, const int32_t* src_token,
+                                      int64_t T, hipStream_t s);
 // Input gradients: down dgrad (+SwiGLU backward) of chunk c, and gate/up dgrad of chunk c with
 // down dgrad of chunk c2 in one launch.
 hipError_t gg_down_dgrad(const ExpertGemm& g, int c, hipStream_t s);

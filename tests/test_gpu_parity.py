@@ -152,9 +152,9 @@ def test_layer_launch_order_and_streams(cfg):
     """The fused BF16 primitive's launches: down of chunk c shares a launch with gate/up of chunk
     c+1, gate/up dgrad of chunk c with down dgrad of chunk c+1, the last gate/up dgrad with dW2;
     every chunk's input-gradient work is issued before dW1 (the weight gradient that needs it);
-    chunk c+1's routing/dispatch is issued before chunk c's combine; chunk 0's gate/up reads the
-    token rows directly, so its dispatch runs on aux; and each kernel runs on the stream the
-    two-stream schedule gives it."""
+    every chunk is routed in one launch on the compute stream before the first GEMM; the gate/up
+    GEMMs read the token rows directly, so the dispatch (one launch, every chunk) runs on aux; and
+    each kernel runs on the stream the two-stream schedule gives it."""
     _require_gpu()
     import combine_moe_route_02_amd as mh
     n = cfg.n_chunks
@@ -168,16 +168,16 @@ def test_layer_launch_order_and_streams(cfg):
     counts = {k: names.count(k) for k in set(names)}
     expect = {"gemm_gateup_swiglu": 1, "gemm_down+gateup_swiglu": n - 1, "gemm_down": 1, "combine": n,
               "combine_bwd": n, "gemm_down_dgrad_swiglu": 1, "gemm_gateup_dgrad+down_dgrad_swiglu": n - 1,
-              "gemm_gateup_dgrad+wgrad_w2": 1, "gemm_wgrad_w1": 1, "dispatch_bwd": n, "dispatch": n,
-              "gemm_gateup_dgrad": 0, "gemm_wgrad": 0}
+              "gemm_gateup_dgrad+wgrad_w2": 1, "gemm_wgrad_w1": 1, "dispatch_bwd": n, "dispatch": 1,
+              "route_topk": 1, "route_layout": 1, "gemm_gateup_dgrad": 0, "gemm_wgrad": 0}
     for k, v in expect.items():
         assert counts.get(k, 0) == v, (k, counts.get(k, 0), v)
     first_wgrad = names.index("gemm_wgrad_w1")
     for kind in ("combine_bwd", "gemm_down_dgrad_swiglu", "gemm_gateup_dgrad+down_dgrad_swiglu",
                  "gemm_gateup_dgrad+wgrad_w2", "dispatch_bwd"):
         assert max(i for i, nm in enumerate(names) if nm == kind) < first_wgrad, kind
-    # forward overlap order: route of chunk 1 precedes combine of chunk 0
-    assert names.index("route_topk", names.index("route_topk") + 1) < names.index("combine")
+    # every chunk's routing precedes the first GEMM
+    assert names.index("route_layout") < names.index("gemm_gateup_swiglu")
 
     def streams_of(kind):
         return [st for nm, st, _ in log if nm == kind]
@@ -185,14 +185,13 @@ def test_layer_launch_order_and_streams(cfg):
     gemms = [k for k in expect if k.startswith("gemm_")]
     assert set(sum((streams_of(k) for k in gemms), [])) == {compute}
     disp, comb = streams_of("dispatch"), streams_of("combine")
-    # chunk 0 is routed on the compute stream; its gate/up reads x through src_token, so every
-    # dispatch (chunk 0's included, which the backward reads) runs on aux
-    assert streams_of("route_topk")[0] == compute
+    # routing on the compute stream; the gate/up GEMMs read x through src_token, so the dispatch
+    # (xd, which the backward reads) runs on aux, after the routing
+    assert set(streams_of("route_topk")) == {compute} and set(streams_of("route_layout")) == {compute}
     aux = disp[0]
     # the fused primitive runs every combine on aux (the last one beside the backward's start)
     assert aux != compute and set(disp) == {aux} and set(comb) == {aux}
-    # chunk 0's dispatch is issued after chunk 1's routing and dispatch
-    assert names.index("dispatch") > names.index("route_topk", names.index("route_topk") + 1)
+    assert names.index("dispatch") > names.index("route_layout")
     cbw, dbw = streams_of("combine_bwd"), streams_of("dispatch_bwd")
     assert cbw[0] == compute and set(cbw[1:]) == {aux} and set(dbw) == {aux}
     assert set(streams_of("route_bwd_dlogits")) == {aux}
