@@ -94,8 +94,8 @@ typedef struct moe_desc {
 /* Expert weight gradients on FP8 MFMA (moe_expert_wgrad_fp8) in the layer backward; BF16 dtype
  * only. Independent of MOE_FLAG_FP8_DGRAD. */
 #define MOE_FLAG_FP8_WGRAD 2
-/* FP8 payload of dispatch backward (the survey's NEXT-1, FP8 payloads in dispatch backward; the
- * token-row payload formats of torchtitan PR 5541, "AI-Generated Details"); BF16 dtype only,
+/* FP8 payload of dispatch backward (the token-row payload formats of torchtitan PR 5541,
+ * "AI-Generated Details", applied to the backward's token rows); BF16 dtype only,
  * independent of the other two flags. The expert input-gradient calls (moe_expert_ffn_bwd,
  * moe_expert_dgrad_fp8 and the layer primitives) then write dxd as block-scaled e4m3 rows and
  * moe_dispatch_bwd reads them: the dxd buffer ([n_chunks * P_c, H] BF16-sized, caller-owned) holds

@@ -12,8 +12,8 @@ Details" and "Verification") and say nothing more. Readings:
   * activations are scaled per token (row of x), weights per output channel (row of W1[e] over
     H, row of W2[e] over I), h per dispatched row (over I) before the down projection;
   * products accumulate in FP32 (exactly, here in FP64) and are dequantised by s_row * s_col;
-  * the dispatch-backward payload dxd (the survey's NEXT-1 asks for FP8 payloads in dispatch
-    backward; the pages give the FP8 payload only as a copy-kernel format) is the BF16 dxd row
+  * the dispatch-backward payload dxd (FP8 payloads extended to dispatch backward; the pages give
+    the FP8 payload only as a copy-kernel format) is the BF16 dxd row
     quantised per block of 256 consecutive columns, each block taking the row quantiser's FP32
     steps on its own values (a block-scaled row: H / 256 scales per row). The block is the column
     tile of the GEMM that produces dxd, so the producer can quantise what it stores without a
