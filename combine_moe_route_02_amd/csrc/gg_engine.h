@@ -11,7 +11,9 @@
 //   * A ring of kNst LDS stages, each holding 64 bytes of K per MN row (32 BF16 or 64 FP8
 //     values); loads run kNst - 1 stages ahead. One s_barrier per stage, with an explicit
 //     vmcnt wait that leaves the younger stages' loads in flight (a workgroup fence would drain
-//     them).
+//     them). When both operands are K-major BF16 (gate/up and down), the same LDS holds two
+//     slots of two stages each instead (128-byte rows), so that every load request covers a
+//     whole 128-byte line; one barrier per pair of stages.
 //   * Operands with K contiguous in HBM ("K-major") live in LDS as 64-byte rows whose four
 //     16-byte chunks are XOR-swizzled by (row >> 2) & 3: a ds_read_b128 of 16 consecutive rows
 //     at one chunk touches all 64 banks once.
@@ -52,12 +54,15 @@ MOE_DEV int ks_off(int k, int c) { return k * (2 * R) + ((c ^ ((k & 3) << 2)) <<
 // ---------------------------------------------------------------------------------------------
 // Operand tile loader: R MN rows, one stage = R * 64 bytes = R / 16 wave instructions of 1 KiB,
 // spread over the workgroup's waves.
-template <int R, bool KSLOW, int LW = kWaves>
+template <int R, bool KSLOW, int LW = kWaves, bool PAIR = false>
 struct Loader {
   static constexpr int kLW = LW;  // waves that issue the loads (the first LW of the workgroup)
-  static constexpr int NI = R / (16 * LW);
+  // PAIR (K-major): one load covers two stages of 8 rows, 128 bytes (a whole line) per row
+  static constexpr int kRows = PAIR ? 8 : 16;  // rows per wave instruction
+  static_assert(!(PAIR && KSLOW), "pairs of stages: K-major operands");
+  static constexpr int NI = R / (kRows * LW);
   static_assert(LW == kWaves || LW == kWaves / 2, "all waves, or one per SIMD");
-  static_assert(NI >= 1 && R % (16 * LW) == 0, "tile rows must cover every loading wave");
+  static_assert(NI >= 1 && R % (kRows * LW) == 0, "tile rows must cover every loading wave");
   __amdgpu_buffer_rsrc_t rb;  // buffer descriptor
   i32x4_t rs;                 // the same as words, for the loads written in assembly
   uint32_t voff[NI];
@@ -70,12 +75,18 @@ struct Loader {
     wave = wv;
     rb = make_rsrc(base, bytes);
     rs = rsrc_words(base, bytes);
-    step = kRowB;
+    step = PAIR ? 2 * kRowB : kRowB;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int r = 16 * (wave * NI + i) + (lane >> 2);
-      const int c = (lane & 3) ^ ((r >> 2) & 3);
-      voff[i] = (uint32_t)((int64_t)map(r) * ld_bytes) + 16u * (uint32_t)c;
+      if constexpr (PAIR) {
+        const int r = 8 * (wave * NI + i) + (lane >> 3);
+        const int c = (lane & 7) ^ ((r >> 1) & 7);
+        voff[i] = (uint32_t)((int64_t)map(r) * ld_bytes) + 16u * (uint32_t)c;
+      } else {
+        const int r = 16 * (wave * NI + i) + (lane >> 2);
+        const int c = (lane & 3) ^ ((r >> 2) & 3);
+        voff[i] = (uint32_t)((int64_t)map(r) * ld_bytes) + 16u * (uint32_t)c;
+      }
     }
   }
   // K-slow: K-row k of the tile starts at base + k * ld_bytes; its R MN values are contiguous
@@ -146,6 +157,15 @@ MOE_DEV bf16x8_t frag_km(const char* st, int mb, int kk, int lane) {
   return *(const bf16x8_t*)(st + km_off(mb + (lane & 31), 2 * kk + (lane >> 5)));
 }
 
+// K-major BF16 in a pair slot (two stages per 128-byte row, eight 16-byte chunks XOR-swizzled by
+// (row >> 1) & 7: a ds_read_b128 of 16 consecutive rows at one chunk touches all 64 banks once):
+// 8 K values, k16 step kk of stage half H.
+MOE_DEV int km2_off(int r, int c) { return r * (2 * kRowB) + ((c ^ ((r >> 1) & 7)) << 4); }
+template <int H>
+MOE_DEV bf16x8_t frag_km2(const char* st, int mb, int kk, int lane) {
+  return *(const bf16x8_t*)(st + km2_off(mb + (lane & 31), 4 * H + 2 * kk + (lane >> 5)));
+}
+
 MOE_DEV s16x4 ds_read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
 }
@@ -176,9 +196,11 @@ MOE_DEV i32x8_t frag_km8(const char* st, int mb, int lane) {
 // tm < TMA (row blocks past the tile's valid rows are skipped at compile time). `loads` issues the
 // global -> LDS loads of a later stage; the schedule spreads them and the fragment reads between
 // the MFMAs (the default scheduler would recycle one fragment register per read and serialise).
-template <bool FP8, bool AKS, bool BKS, int RA, int RB, int TM, int TN, int TMA, int VM, class Loads>
+template <bool FP8, bool AKS, bool BKS, int RA, int RB, int TM, int TN, int TMA, int VM, int HALF = -1,
+          class Loads>
 MOE_DEV void stage_mma(const char* sa, const char* sb, int arow0, int brow0, int lane,
                        f32x16_t (&acc)[TM][TN], Loads&& loads) {
+  static_assert(HALF < 0 || (!FP8 && !AKS && !BKS), "pair slots: BF16 K-major operands");
   if constexpr (TMA == 0) {
     loads();
   } else if constexpr (FP8) {
@@ -208,12 +230,19 @@ MOE_DEV void stage_mma(const char* sa, const char* sb, int arow0, int brow0, int
     bf16x8_t fa[2][TMA], fb[2][TN];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
+      if constexpr (HALF >= 0) {
 #pragma unroll
-      for (int tm = 0; tm < TMA; ++tm)
-        fa[kk][tm] = AKS ? frag_ks<RA>(sa, arow0 + 32 * tm, kk, lane) : frag_km(sa, arow0 + 32 * tm, kk, lane);
+        for (int tm = 0; tm < TMA; ++tm) fa[kk][tm] = frag_km2<HALF>(sa, arow0 + 32 * tm, kk, lane);
 #pragma unroll
-      for (int tn = 0; tn < TN; ++tn)
-        fb[kk][tn] = BKS ? frag_ks<RB>(sb, brow0 + 32 * tn, kk, lane) : frag_km(sb, brow0 + 32 * tn, kk, lane);
+        for (int tn = 0; tn < TN; ++tn) fb[kk][tn] = frag_km2<HALF>(sb, brow0 + 32 * tn, kk, lane);
+      } else {
+#pragma unroll
+        for (int tm = 0; tm < TMA; ++tm)
+          fa[kk][tm] = AKS ? frag_ks<RA>(sa, arow0 + 32 * tm, kk, lane) : frag_km(sa, arow0 + 32 * tm, kk, lane);
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+          fb[kk][tn] = BKS ? frag_ks<RB>(sb, brow0 + 32 * tn, kk, lane) : frag_km(sb, brow0 + 32 * tn, kk, lane);
+      }
     }
     loads();
 #pragma unroll
@@ -287,6 +316,37 @@ MOE_DEV void kloop(const LA& la, const LB& lb, char* ring, int nks, int arow0, i
       }
       stage_mma<FP8, AKS, BKS, RA, RB, TM, TN, TMA, 0>(cur, cur + SA, arow0, brow0, lane, acc, [] {});
     }
+  }
+  wait_vm<0>();
+  __syncthreads();
+}
+
+// K loop for two K-major BF16 operands over pair slots: the LDS ring holds two slots of two
+// stages each (rows of 128 bytes), and each load brings a whole 128-byte line per row, half the
+// load requests per byte of 64-byte stage rows (the loads' issue limits the 64-byte K loop when
+// every CU runs one). Pair p+1's loads go out during the first half of pair p, into the other
+// slot, which every wave finished reading before pair p's barrier; pair p+1 then waits for all of
+// them. Past the last pair they fetch masked or unused data into the slot no one reads again.
+template <int RA, int RB, int TM, int TN, int TMA, class LA, class LB>
+MOE_DEV void kloop_pairs(const LA& la, const LB& lb, char* ring, int nks, int arow0, int brow0, int lane,
+                         f32x16_t (&acc)[TM][TN]) {
+  constexpr int SA = RA * 2 * kRowB, SS = (RA + RB) * 2 * kRowB;
+  constexpr int NL = LA::NI + LB::NI;  // load instructions per wave per pair
+  const uint32_t rl = lds_addr(ring);
+  const int np = (nks + 1) / 2;
+  la.template issue<false>(rl, 0);
+  lb.template issue<false>(rl + SA, 0);
+  for (int p = 0; p < np; ++p) {
+    wait_vm<0>();                  // pair p has landed (this wave's loads)
+    __builtin_amdgcn_s_barrier();  // every wave's part of pair p is in LDS; pair p-1 is consumed
+    const int ld = p + 1;
+    const uint32_t st = rl + (ld & 1) * SS;
+    const char* cur = ring + (p & 1) * SS;
+    stage_mma<false, false, false, RA, RB, TM, TN, TMA, NL, 0>(cur, cur + SA, arow0, brow0, lane, acc, [&] {
+      la.template issue<false>(st, ld);
+      lb.template issue<false>(st + SA, ld);
+    });
+    if (2 * p + 1 < nks) stage_mma<false, false, false, RA, RB, TM, TN, TMA, 0, 1>(cur, cur + SA, arow0, brow0, lane, acc, [] {});
   }
   wait_vm<0>();
   __syncthreads();
@@ -514,7 +574,9 @@ MOE_DEV int rows_list(const RowsArgs& a, int first, RowsShared& sh, char* ring) 
       const int nvalid = min(OUTN, a.N - n0);
       const char* Be = (const char*)a.B + (int64_t)e * a.strideB * ES;
 
-      Loader<BM, false> la;
+      // both operands K-major (BF16 gate/up and down): pairs of stages, whole lines per row
+      constexpr bool kPair = !FP8 && !kBKS;
+      Loader<BM, false, kWaves, kPair> la;
       if constexpr (GATHER) {
         // tile row r reads token row gather[r0 + r]; rows past the segment point one row past the
         // end of A, which the descriptor's extent turns into zeros
@@ -526,7 +588,7 @@ MOE_DEV int rows_list(const RowsArgs& a, int first, RowsShared& sh, char* ring) 
         la.init_kmajor((const char*)a.A + r0 * a.lda * ES, a.lda * ES, (int64_t)mvalid * a.lda * ES, wave, lane,
                        [](int r) { return r; });
       }
-      Loader<BN, kBKS> lb;
+      Loader<BN, kBKS, kWaves, kPair> lb;
       if constexpr (kSwiGLU) {
         // tile row r -> wave column block r / WTN; its first half are gate rows j, its second half
         // the matching up rows I + j; readable rows run to the end of this expert's W1
@@ -557,7 +619,11 @@ MOE_DEV int rows_list(const RowsArgs& a, int first, RowsShared& sh, char* ring) 
       const int arow0 = wm * WTM, brow0 = wn * WTN;
       static_assert(TM <= 4, "TM > 4");
       switch (tma) {
-#define MOE_KL(T_) kloop<FP8, false, kBKS, BM, BN, TM, TN, (T_ <= TM ? T_ : TM)>(la, lb, ring, nks, arow0, brow0, lane, acc)
+#define MOE_KL(T_)                                                                                        \
+  if constexpr (kPair)                                                                                     \
+    kloop_pairs<BM, BN, TM, TN, (T_ <= TM ? T_ : TM)>(la, lb, ring, nks, arow0, brow0, lane, acc);         \
+  else                                                                                                     \
+    kloop<FP8, false, kBKS, BM, BN, TM, TN, (T_ <= TM ? T_ : TM)>(la, lb, ring, nks, arow0, brow0, lane, acc)
         case 4: MOE_KL(4); break;
         case 3: MOE_KL(3); break;
         case 2: MOE_KL(2); break;
