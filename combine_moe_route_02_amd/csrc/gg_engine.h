@@ -13,7 +13,8 @@
 //     vmcnt wait that leaves the younger stages' loads in flight (a workgroup fence would drain
 //     them). When both operands are K-major BF16 (gate/up and down), the same LDS holds two
 //     slots of two stages each instead (128-byte rows), so that every load request covers a
-//     whole 128-byte line; one barrier per pair of stages.
+//     whole 128-byte line; one barrier per pair of stages. The BF16 input gradients keep their
+//     K-slow weight operand in the stage ring and take the K-major A operand in pair slots.
 //   * Operands with K contiguous in HBM ("K-major") live in LDS as 64-byte rows whose four
 //     16-byte chunks are XOR-swizzled by (row >> 2) & 3: a ds_read_b128 of 16 consecutive rows
 //     at one chunk touches all 64 banks once.
@@ -200,7 +201,7 @@ template <bool FP8, bool AKS, bool BKS, int RA, int RB, int TM, int TN, int TMA,
           class Loads>
 MOE_DEV void stage_mma(const char* sa, const char* sb, int arow0, int brow0, int lane,
                        f32x16_t (&acc)[TM][TN], Loads&& loads) {
-  static_assert(HALF < 0 || (!FP8 && !AKS && !BKS), "pair slots: BF16 K-major operands");
+  static_assert(HALF < 0 || (!FP8 && !AKS), "pair slots: a BF16 K-major A operand");
   if constexpr (TMA == 0) {
     loads();
   } else if constexpr (FP8) {
@@ -231,10 +232,12 @@ MOE_DEV void stage_mma(const char* sa, const char* sb, int arow0, int brow0, int
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       if constexpr (HALF >= 0) {
+        // A in a pair slot; B in a pair slot too, or K-slow in its own stage slot
 #pragma unroll
         for (int tm = 0; tm < TMA; ++tm) fa[kk][tm] = frag_km2<HALF>(sa, arow0 + 32 * tm, kk, lane);
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) fb[kk][tn] = frag_km2<HALF>(sb, brow0 + 32 * tn, kk, lane);
+        for (int tn = 0; tn < TN; ++tn)
+          fb[kk][tn] = BKS ? frag_ks<RB>(sb, brow0 + 32 * tn, kk, lane) : frag_km2<HALF>(sb, brow0 + 32 * tn, kk, lane);
       } else {
 #pragma unroll
         for (int tm = 0; tm < TMA; ++tm)
@@ -347,6 +350,51 @@ MOE_DEV void kloop_pairs(const LA& la, const LB& lb, char* ring, int nks, int ar
       lb.template issue<false>(st + SA, ld);
     });
     if (2 * p + 1 < nks) stage_mma<false, false, false, RA, RB, TM, TN, TMA, 0, 1>(cur, cur + SA, arow0, brow0, lane, acc, [] {});
+  }
+  wait_vm<0>();
+  __syncthreads();
+}
+
+// K loop for a K-major BF16 A operand in pair slots (two slots of two stages, 128-byte rows) and
+// a K-slow B operand in a ring of kNst stage slots (the input gradients): one barrier per stage.
+// Stage 2p issues A's pair p+1 and B's stage 2p+3, stage 2p+1 issues B's stage 2p+4; each slot
+// they fill was last read before that stage's barrier. Load counts complete in issue order: at an
+// even stage the loads younger than its own are B's next two stages, at an odd stage also A's
+// next pair, so the two stages wait with different counts.
+template <int RA, int RB, int TM, int TN, int TMA, class LA, class LB>
+MOE_DEV void kloop_apairs(const LA& la, const LB& lb, char* ring, int nks, int arow0, int brow0, int lane,
+                          f32x16_t (&acc)[TM][TN]) {
+  constexpr int SA = RA * 2 * kRowB;  // A pair slot
+  constexpr int SB = RB * kRowB;      // B stage slot
+  constexpr int NA = LA::NI, NB = LB::NI;
+  const uint32_t rl = lds_addr(ring), rb = rl + 2 * SA;
+  const char* ringb = ring + 2 * SA;
+  const int np = (nks + 1) / 2;
+  la.template issue<true>(rl, 0);
+#pragma unroll
+  for (int s = 0; s < kNst - 1; ++s) lb.template issue<true>(rb + s * SB, s);
+  for (int p = 0; p < np; ++p) {
+    const int s0 = 2 * p;
+    const char* ca = ring + (p & 1) * SA;
+    {
+      wait_vm<(kNst - 2) * NB>();    // A's pair p and B's stage s0 have landed (this wave's loads)
+      __builtin_amdgcn_s_barrier();  // every wave's part is in LDS; stage s0 - 1 is consumed
+      const int lb0 = s0 + kNst - 1;
+      stage_mma<false, false, true, RA, RB, TM, TN, TMA, NA + NB, 0>(
+          ca, ringb + (s0 % kNst) * SB, arow0, brow0, lane, acc, [&] {
+            la.template issue<true>(rl + ((p + 1) & 1) * SA, p + 1);
+            lb.template issue<true>(rb + (lb0 % kNst) * SB, lb0);
+          });
+    }
+    if (s0 + 1 < nks) {
+      wait_vm<(kNst - 2) * NB + NA>();  // B's stage s0 + 1 has landed
+      __builtin_amdgcn_s_barrier();
+      const int lb1 = s0 + kNst;
+      stage_mma<false, false, true, RA, RB, TM, TN, TMA, NB, 1>(
+          ca, ringb + ((s0 + 1) % kNst) * SB, arow0, brow0, lane, acc, [&] {
+            lb.template issue<true>(rb + (lb1 % kNst) * SB, lb1);
+          });
+    }
   }
   wait_vm<0>();
   __syncthreads();
@@ -574,9 +622,11 @@ MOE_DEV int rows_list(const RowsArgs& a, int first, RowsShared& sh, char* ring) 
       const int nvalid = min(OUTN, a.N - n0);
       const char* Be = (const char*)a.B + (int64_t)e * a.strideB * ES;
 
-      // both operands K-major (BF16 gate/up and down): pairs of stages, whole lines per row
+      // both operands K-major (BF16 gate/up and down): pairs of stages, whole lines per row; the
+      // BF16 input gradients take their K-major A operand in pairs as well
       constexpr bool kPair = !FP8 && !kBKS;
-      Loader<BM, false, kWaves, kPair> la;
+      constexpr bool kAPair = !FP8 && kBKS;
+      Loader<BM, false, kWaves, kPair || kAPair> la;
       if constexpr (GATHER) {
         // tile row r reads token row gather[r0 + r]; rows past the segment point one row past the
         // end of A, which the descriptor's extent turns into zeros
@@ -622,6 +672,8 @@ MOE_DEV int rows_list(const RowsArgs& a, int first, RowsShared& sh, char* ring) 
 #define MOE_KL(T_)                                                                                        \
   if constexpr (kPair)                                                                                     \
     kloop_pairs<BM, BN, TM, TN, (T_ <= TM ? T_ : TM)>(la, lb, ring, nks, arow0, brow0, lane, acc);         \
+  else if constexpr (kAPair)                                                                               \
+    kloop_apairs<BM, BN, TM, TN, (T_ <= TM ? T_ : TM)>(la, lb, ring, nks, arow0, brow0, lane, acc);        \
   else                                                                                                     \
     kloop<FP8, false, kBKS, BM, BN, TM, TN, (T_ <= TM ? T_ : TM)>(la, lb, ring, nks, arow0, brow0, lane, acc)
         case 4: MOE_KL(4); break;
