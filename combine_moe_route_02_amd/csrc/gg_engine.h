@@ -13,8 +13,9 @@
 //     vmcnt wait that leaves the younger stages' loads in flight (a workgroup fence would drain
 //     them). When both operands are K-major BF16 (gate/up and down), the same LDS holds two
 //     slots of two stages each instead (128-byte rows), so that every load request covers a
-//     whole 128-byte line; one barrier per pair of stages. The BF16 input gradients keep their
-//     K-slow weight operand in the stage ring and take the K-major A operand in pair slots.
+//     whole 128-byte line; one barrier per pair of stages; the same for the FP8 GEMMs other
+//     than the forward gate/up one, which keeps the stage ring. The BF16 input gradients keep
+//     their K-slow weight operand in the stage ring and take the K-major A operand in pair slots.
 //   * Operands with K contiguous in HBM ("K-major") live in LDS as 64-byte rows whose four
 //     16-byte chunks are XOR-swizzled by (row >> 2) & 3: a ds_read_b128 of 16 consecutive rows
 //     at one chunk touches all 64 banks once.
@@ -193,6 +194,15 @@ MOE_DEV i32x8_t frag_km8(const char* st, int mb, int lane) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// K-major FP8 in a pair slot: 32 K values (bytes 32 * (lane >> 5) .. +32 of stage half H).
+template <int H>
+MOE_DEV i32x8_t frag_km8_2(const char* st, int mb, int lane) {
+  const int r = mb + (lane & 31), c = 4 * H + 2 * (lane >> 5);
+  const i32x4_t a = *(const i32x4_t*)(st + km2_off(r, c));
+  const i32x4_t b = *(const i32x4_t*)(st + km2_off(r, c + 1));
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // One LDS stage of MFMAs: acc[tm][tn] += A[rows of block tm] . B[rows of block tn]^T for
 // tm < TMA (row blocks past the tile's valid rows are skipped at compile time). `loads` issues the
 // global -> LDS loads of a later stage; the schedule spreads them and the fragment reads between
@@ -201,15 +211,17 @@ template <bool FP8, bool AKS, bool BKS, int RA, int RB, int TM, int TN, int TMA,
           class Loads>
 MOE_DEV void stage_mma(const char* sa, const char* sb, int arow0, int brow0, int lane,
                        f32x16_t (&acc)[TM][TN], Loads&& loads) {
-  static_assert(HALF < 0 || (!FP8 && !AKS), "pair slots: a BF16 K-major A operand");
+  static_assert(HALF < 0 || (!AKS && !(FP8 && BKS)), "pair slots: K-major operands");
   if constexpr (TMA == 0) {
     loads();
   } else if constexpr (FP8) {
     i32x8_t fa[TMA], fb[TN];
 #pragma unroll
-    for (int tm = 0; tm < TMA; ++tm) fa[tm] = frag_km8(sa, arow0 + 32 * tm, lane);
+    for (int tm = 0; tm < TMA; ++tm)
+      fa[tm] = HALF < 0 ? frag_km8(sa, arow0 + 32 * tm, lane) : frag_km8_2<(HALF > 0)>(sa, arow0 + 32 * tm, lane);
 #pragma unroll
-    for (int tn = 0; tn < TN; ++tn) fb[tn] = frag_km8(sb, brow0 + 32 * tn, lane);
+    for (int tn = 0; tn < TN; ++tn)
+      fb[tn] = HALF < 0 ? frag_km8(sb, brow0 + 32 * tn, lane) : frag_km8_2<(HALF > 0)>(sb, brow0 + 32 * tn, lane);
     loads();
 #pragma unroll
     for (int tm = 0; tm < TMA; ++tm)
@@ -324,13 +336,13 @@ MOE_DEV void kloop(const LA& la, const LB& lb, char* ring, int nks, int arow0, i
   __syncthreads();
 }
 
-// K loop for two K-major BF16 operands over pair slots: the LDS ring holds two slots of two
-// stages each (rows of 128 bytes), and each load brings a whole 128-byte line per row, half the
+// K loop for two K-major operands (BF16 or FP8) over pair slots: the LDS ring holds two slots of
+// two stages each (rows of 128 bytes), and each load brings a whole 128-byte line per row, half the
 // load requests per byte of 64-byte stage rows (the loads' issue limits the 64-byte K loop when
 // every CU runs one). Pair p+1's loads go out during the first half of pair p, into the other
 // slot, which every wave finished reading before pair p's barrier; pair p+1 then waits for all of
 // them. Past the last pair they fetch masked or unused data into the slot no one reads again.
-template <int RA, int RB, int TM, int TN, int TMA, class LA, class LB>
+template <bool FP8, int RA, int RB, int TM, int TN, int TMA, class LA, class LB>
 MOE_DEV void kloop_pairs(const LA& la, const LB& lb, char* ring, int nks, int arow0, int brow0, int lane,
                          f32x16_t (&acc)[TM][TN]) {
   constexpr int SA = RA * 2 * kRowB, SS = (RA + RB) * 2 * kRowB;
@@ -345,11 +357,11 @@ MOE_DEV void kloop_pairs(const LA& la, const LB& lb, char* ring, int nks, int ar
     const int ld = p + 1;
     const uint32_t st = rl + (ld & 1) * SS;
     const char* cur = ring + (p & 1) * SS;
-    stage_mma<false, false, false, RA, RB, TM, TN, TMA, NL, 0>(cur, cur + SA, arow0, brow0, lane, acc, [&] {
+    stage_mma<FP8, false, false, RA, RB, TM, TN, TMA, NL, 0>(cur, cur + SA, arow0, brow0, lane, acc, [&] {
       la.template issue<false>(st, ld);
       lb.template issue<false>(st + SA, ld);
     });
-    if (2 * p + 1 < nks) stage_mma<false, false, false, RA, RB, TM, TN, TMA, 0, 1>(cur, cur + SA, arow0, brow0, lane, acc, [] {});
+    if (2 * p + 1 < nks) stage_mma<FP8, false, false, RA, RB, TM, TN, TMA, 0, 1>(cur, cur + SA, arow0, brow0, lane, acc, [] {});
   }
   wait_vm<0>();
   __syncthreads();
@@ -622,9 +634,10 @@ MOE_DEV int rows_list(const RowsArgs& a, int first, RowsShared& sh, char* ring) 
       const int nvalid = min(OUTN, a.N - n0);
       const char* Be = (const char*)a.B + (int64_t)e * a.strideB * ES;
 
-      // both operands K-major (BF16 gate/up and down): pairs of stages, whole lines per row; the
-      // BF16 input gradients take their K-major A operand in pairs as well
-      constexpr bool kPair = !FP8 && !kBKS;
+      // both operands K-major: pairs of stages, whole lines per row, except the FP8 gate/up GEMM,
+      // whose short FP8 stages need the ring's three stages of loads ahead (pairs: 8% slower);
+      // the BF16 input gradients take their K-major A operand in pairs as well
+      constexpr bool kPair = !kBKS && !(FP8 && MODE == kGateUp);
       constexpr bool kAPair = !FP8 && kBKS;
       Loader<BM, false, kWaves, kPair || kAPair> la;
       if constexpr (GATHER) {
@@ -671,7 +684,7 @@ MOE_DEV int rows_list(const RowsArgs& a, int first, RowsShared& sh, char* ring) 
       switch (tma) {
 #define MOE_KL(T_)                                                                                        \
   if constexpr (kPair)                                                                                     \
-    kloop_pairs<BM, BN, TM, TN, (T_ <= TM ? T_ : TM)>(la, lb, ring, nks, arow0, brow0, lane, acc);         \
+    kloop_pairs<FP8, BM, BN, TM, TN, (T_ <= TM ? T_ : TM)>(la, lb, ring, nks, arow0, brow0, lane, acc);    \
   else if constexpr (kAPair)                                                                               \
     kloop_apairs<BM, BN, TM, TN, (T_ <= TM ? T_ : TM)>(la, lb, ring, nks, arow0, brow0, lane, acc);        \
   else                                                                                                     \

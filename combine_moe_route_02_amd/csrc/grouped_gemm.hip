@@ -76,13 +76,13 @@ MOE_DEV void wgrad_fp8_tile(const WgradFp8Args& a, int tile, char* ring, int tid
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[tm][tn][q] = 0.f;
   if (Kp > 0) {
-    Loader<BM, false> la;
+    Loader<BM, false, kWaves, true> la;
     la.init_kmajor(a.A + koff * a.M + (int64_t)m0 * Kp, Kp, (int64_t)(a.M - m0) * Kp, wave, lane,
                    [](int r) { return r; });
-    Loader<BN, false> lb;
+    Loader<BN, false, kWaves, true> lb;
     lb.init_kmajor(a.B + koff * a.N + (int64_t)n0 * Kp, Kp, (int64_t)(a.N - n0) * Kp, wave, lane,
                    [](int r) { return r; });
-    kloop<true, false, false, BM, BN, TM, TN, TM>(la, lb, ring, Kp / 64, wm * WTM, wn * WTN, lane, acc);
+    kloop_pairs<true, BM, BN, TM, TN, TM>(la, lb, ring, Kp / 64, wm * WTM, wn * WTN, lane, acc);
   }
 
   const int mrow = wm * WTM + out_row(lane);
