@@ -55,7 +55,7 @@ KERNEL_SYMBOLS = {
                                    "rows_wgrad_kernel<256, 256, 3, 256, 256, false>"),
     "gemm_wgrad_w1": (("wgrad.hip", "gg_engine.h", "gg_wgrad.h"), "wgrad_kernel<256, 256, 1>"),
     "gemm_wgrad": (("wgrad.hip", "gg_engine.h", "gg_wgrad.h"), "wgrad_kernel<256, 256, 0>"),
-    "gemm_router_wgrad": (("gemm.hip",), "router_wgrad_kernel"),
+    "gemm_router_wgrad": (("router_wgrad.hip", "gg_engine.h", "gg_wgrad.h"), "router_wgrad_planes_kernel"),
     "router_reduce": (("gemm.hip",), "reduce_partials_kernel"),
 }
 CALIBRATION_BYTES = 64 << 20   # a plain elementwise copy of this many bytes (read and written once,
@@ -217,7 +217,8 @@ def counter_summary(dirs, cmd: str) -> str:
     src = [f"Source hashes (code without comments): grouped_gemm.hip + gg_engine.h "
            f"{source_sha('gemm_gateup_swiglu')}, wgrad.hip + gg_engine.h + gg_wgrad.h {source_sha('gemm_wgrad')}, "
            f"rows_wgrad.hip + gg_engine.h + gg_wgrad.h {source_sha('gemm_gateup_dgrad+wgrad_w2')}, "
-           f"gemm.hip {source_sha('gemm_router_wgrad')}, rows.hip {source_sha('dispatch')}.", ""]
+           f"router_wgrad.hip + gg_engine.h + gg_wgrad.h {source_sha('gemm_router_wgrad')}, "
+           f"gemm.hip {source_sha('router_reduce')}, rows.hip {source_sha('dispatch')}.", ""]
     return "\n".join(out[:7] + src + out[7:] + raw) + "\n"
 
 

@@ -24,7 +24,8 @@ COMMON = [
     "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
 ]
 
-SOURCES = ["route.hip", "rows.hip", "gemm.hip", "grouped_gemm.hip", "wgrad.hip", "rows_wgrad.hip", "stash.hip", "abi.cpp", "trace.cpp"]
+SOURCES = ["route.hip", "rows.hip", "gemm.hip", "grouped_gemm.hip", "wgrad.hip", "rows_wgrad.hip", "router_wgrad.hip",
+           "stash.hip", "abi.cpp", "trace.cpp"]
 
 
 def _compile(src: str) -> str:

@@ -155,9 +155,15 @@ moe_status events(int count, hipEvent_t** out) {
   return MOE_OK;
 }
 
-int64_t router_scratch(const moe_desc* d) {
-  return moe::router_partials_bytes(tokens_per_chunk(d), d->E, d->H);
+// Router weight-gradient scratch: the split-K partials, then (BF16 rows) the chunk's dlogits as BF16
+// high and low planes [tokens per chunk, router_plane_ld(E)] at a 256-byte boundary.
+int64_t router_partials_span(const moe_desc* d) {
+  return (moe::router_partials_bytes(tokens_per_chunk(d), d->E, d->H) + 255) / 256 * 256;
 }
+int64_t router_plane_bytes(const moe_desc* d) {  // both planes
+  return is_bf16_rows(d) ? 2 * tokens_per_chunk(d) * moe::router_plane_ld(d->E) * 2 : 0;
+}
+int64_t router_scratch(const moe_desc* d) { return router_partials_span(d) + router_plane_bytes(d); }
 
 // Workspace layout: the routing histograms and the router weight gradient's partials share its
 // start (they run in order on one stream); the expert weight gradients' scratch (BF16 path)
@@ -413,11 +419,21 @@ moe_status moe_route_bwd(const moe_desc* d, int chunk, const float* dgates, cons
   if (d->T > 0) { MOE_NEED(dgates); MOE_NEED(gates); MOE_NEED(topk_idx); MOE_NEED(x); MOE_NEED(dlogits); }
   const int cfirst = chunk < 0 ? 0 : chunk, clast = chunk < 0 ? d->n_chunks - 1 : chunk;
   if (clast == d->n_chunks - 1) MOE_NEED(dwr);
+  // BF16 rows: the dlogits planes follow the partials (each chunk's router gradient reads them
+  // before the next chunk's dlogits kernel, on the same stream, rewrites them)
+  uint16_t* hi = nullptr;
+  uint16_t* lo = nullptr;
+  const int ldl = moe::router_plane_ld(d->E);
+  const int64_t pitch = moe::router_plane_pitch(d->E);
+  if (router_plane_bytes(d) > 0) {
+    hi = (uint16_t*)((char*)workspace + router_partials_span(d));
+    lo = hi + moe::router_plane_lo_offset(d->E, tokens_per_chunk(d));
+  }
   for (int c = cfirst; c <= clast; ++c) {
     Range r = range_of(d, c);
     MOE_HIP(moe::launch_route_bwd_dlogits(dgates, gates, topk_idx, dlogits, r.t0, r.t1, d->k, d->E,
-                                          (hipStream_t)stream), "route_bwd_dlogits");
-    MOE_HIP(moe::launch_router_wgrad(is_bf16_rows(d), dlogits, x, (float*)workspace, dwr_acc, c == 0,
+                                          (hipStream_t)stream, hi, lo, ldl, pitch), "route_bwd_dlogits");
+    MOE_HIP(moe::launch_router_wgrad(is_bf16_rows(d), dlogits, hi, lo, ldl, x, (float*)workspace, dwr_acc, c == 0,
                                      c == d->n_chunks - 1 ? dwr : nullptr, r.t0, r.t1, d->E, d->H,
                                      (hipStream_t)stream), "router_wgrad");
   }

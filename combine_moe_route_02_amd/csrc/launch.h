@@ -39,9 +39,12 @@ hipError_t launch_combine_bwd(bool bf16, const void* dy, const void* yd, const f
                               const int32_t* row_of, void* dyd, float* dgates, int64_t t0,
                               int64_t t1, int K, int64_t row_bytes, hipStream_t s,
                               void* dyd_q = nullptr, float* dyd_scale = nullptr);  // BF16: also e4m3 rows
+// dl_hi / dl_lo (nullable): also the rows' BF16 high and low parts, row t - t0 at t * pitch, ldl
+// columns each (zeros past E)
 hipError_t launch_route_bwd_dlogits(const float* dgates, const float* gates, const int32_t* idx,
                                     float* dlogits, int64_t t0, int64_t t1, int K, int E,
-                                    hipStream_t s);
+                                    hipStream_t s, uint16_t* dl_hi = nullptr, uint16_t* dl_lo = nullptr,
+                                    int ldl = 0, int64_t pitch = 0);
 // dxd_scales non-null: dxd holds block-scaled e4m3 rows (codes [., H], one FP32 scale per row
 // and 256-column block, dxd_scales [., ceil(H/256)]); BF16 payloads only
 hipError_t launch_dispatch_bwd(bool bf16, const void* dxd, const float* dxd_scales, const int32_t* row_of,
@@ -157,8 +160,18 @@ hipError_t launch_stash_copy(bool store, const void* from, const float* from_sca
                              int32_t max_ctas, hipStream_t s);
 int router_ksplit(int64_t tokens);
 int64_t router_partials_bytes(int64_t Tc, int E, int H);
-hipError_t launch_router_wgrad(bool bf16, const float* dlogits, const void* x, float* partials,
-                               float* dwr_acc, bool first, void* dwr, int64_t t0, int64_t t1, int E,
-                               int H, hipStream_t s);
+// BF16 rows: the BF16 high/low planes of dlogits ([tokens, ldl], from route_bwd_dlogits) feed the
+// engine kernel (router_wgrad.hip); FP32 rows: the SIMT kernel reads dlogits
+hipError_t launch_router_wgrad(bool bf16, const float* dlogits, const uint16_t* dl_hi, const uint16_t* dl_lo,
+                               int ldl, const void* x, float* partials, float* dwr_acc, bool first, void* dwr,
+                               int64_t t0, int64_t t1, int E, int H, hipStream_t s);
+hipError_t launch_router_wgrad_planes(const uint16_t* hi, const uint16_t* lo, int ldl, const void* x, float* partials,
+                                      int64_t t0, int64_t len, int ks, int S, int E, int H, hipStream_t s);
+// The router gradient's dlogits planes: ld columns per plane (zeros past E). Up to 128 experts the
+// high and low parts sit side by side in one [tokens, 256] matrix (low part at column 128), which
+// one 256 x 256 GEMM tile reads whole; above 128 they are two [tokens, ld] planes.
+inline int router_plane_ld(int E) { return E <= 128 ? 128 : (E + 7) / 8 * 8; }
+inline int64_t router_plane_pitch(int E) { return E <= 128 ? 256 : router_plane_ld(E); }
+inline int64_t router_plane_lo_offset(int E, int64_t tokens) { return E <= 128 ? 128 : tokens * router_plane_ld(E); }
 
 }  // namespace moe

@@ -445,7 +445,8 @@ __global__ __launch_bounds__(kBlockThreads) void combine_bwd_q_kernel(
 // coalesced stores, then lanes 0..K-1 store their slot's value (same wave, program order).
 __global__ __launch_bounds__(256) void route_bwd_dlogits_kernel(
     const float* __restrict__ dgates, const float* __restrict__ gates, const int32_t* __restrict__ idx,
-    float* __restrict__ dlogits, int64_t t0, int64_t t1, int K, int E) {
+    float* __restrict__ dlogits, uint16_t* __restrict__ dl_hi, uint16_t* __restrict__ dl_lo, int ldl, int64_t pitch,
+    int64_t t0, int64_t t1, int K, int E) {
   const int lane = threadIdx.x & 63;
   const int64_t t = t0 + (int64_t)blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
   if (t >= t1) return;
@@ -457,7 +458,33 @@ __global__ __launch_bounds__(256) void route_bwd_dlogits_kernel(
     s = fmaf(bcast_f(g, j), bcast_f(d, j), s);
   float* row = dlogits + t * (int64_t)E;
   for (int e = lane; e < E; e += 64) row[e] = 0.f;
-  if (lane < K) row[id] = g * (d - s);
+  const float v = g * (d - s);
+  if (lane < K) row[id] = v;
+  if (dl_hi) {
+    // BF16 high and low parts of the row for the router weight gradient (row t - t0 of the
+    // planes; zeros past E up to ldl columns)
+    int ids[8];
+    float vs[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      ids[j] = j < K ? bcast_i(id, j) : -1;
+      vs[j] = j < K ? bcast_f(v, j) : 0.f;
+    }
+    // two columns per lane (the pitch is a multiple of 8), one 4-byte store per plane
+    uint32_t* hr = (uint32_t*)(dl_hi + (t - t0) * pitch);
+    uint32_t* lr = (uint32_t*)(dl_lo + (t - t0) * pitch);
+    for (int e = 2 * lane; e < ldl; e += 128) {
+      float x0 = 0.f, x1 = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (ids[j] == e) x0 = vs[j];
+        if (ids[j] == e + 1) x1 = vs[j];
+      }
+      const uint16_t h0 = f2bf(x0), h1 = f2bf(x1);
+      hr[e / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+      lr[e / 2] = (uint32_t)f2bf(x0 - bf2f(h0)) | ((uint32_t)f2bf(x1 - bf2f(h1)) << 16);
+    }
+  }
 }
 
 // Dispatch backward: dx[t] = RNE(sum_j local dxd[row_of[t][j]] + sum_j dlogits[t][e_j] W_r[e_j]).
@@ -835,12 +862,13 @@ hipError_t launch_combine_bwd(bool bf16, const void* dy, const void* yd, const f
 
 hipError_t launch_route_bwd_dlogits(const float* dgates, const float* gates, const int32_t* idx,
                                     float* dlogits, int64_t t0, int64_t t1, int K, int E,
-                                    hipStream_t s) {
+                                    hipStream_t s, uint16_t* dl_hi, uint16_t* dl_lo, int ldl, int64_t pitch) {
+  if (dl_hi && (!dl_lo || ldl < E || ldl % 8 || pitch % 2 || pitch < ldl)) return hipErrorInvalidValue;
   if (t1 <= t0) return hipSuccess;
   {
     MOE_TRACE("route_bwd_dlogits", s);
     MOE_LAUNCH(route_bwd_dlogits_kernel, tok_grid(t1 - t0), dim3(256), 0, s, dgates, gates,
-                       idx, dlogits, t0, t1, K, E);
+                       idx, dlogits, dl_hi, dl_lo, ldl, pitch, t0, t1, K, E);
   }
   return hipGetLastError();
 }

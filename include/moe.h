@@ -189,7 +189,9 @@ moe_status moe_combine_bwd(const moe_desc* d, int chunk, const void* dy, const v
  * caller's projection logits = x W_r^T: the chunk's dlogits^T x is computed in FP32 (dlogits
  * split into a BF16 high and low part, x exact) and stored into dwr_acc for the first chunk,
  * added to it for later chunks; after the last chunk (or chunk = -1) dwr = dwr_acc converted
- * once (RNE) to the payload type. workspace: moe_workspace_bytes().route_bwd_scratch bytes. */
+ * once (RNE) to the payload type. workspace: moe_workspace_bytes().route_bwd_scratch bytes
+ * (the split-K partials and, for BF16 rows, the chunk's dlogits as BF16 high and low planes;
+ * contents undefined between calls). */
 moe_status moe_route_bwd(const moe_desc* d, int chunk, const float* dgates, const float* gates,
                          const int32_t* topk_idx, const void* x, float* dlogits, float* dwr_acc,
                          void* dwr, void* workspace, void* stream);
