@@ -18,11 +18,17 @@ one-rank share (two chunks of 16384 tokens, 128 experts, H 2048, top-8):
     unchunked result and more than ten times further than the FP32-accumulated one.
 
 Inputs are seeded and shared by both sides: x and the logits from the 32K-token workload, the
-routing (indices, gates) from the oracle, and upstream gate gradients N(0, 1)."""
+routing (indices, gates) from the oracle, and upstream gate gradients N(0, 1).
+
+The same stage call at small ragged shapes covers both layouts of the split dlogits that the GPU
+product reads: up to 128 experts the high and low parts side by side in one 256-column operand
+(E = 32 and 128, zero columns past E), above 128 two planes with a pass over each (E = 132 and
+256), with partial output tiles in both directions, one to three chunks."""
 import numpy as np
 import pytest
 
 import moe_inputs
+from moe_inputs import MoeConfig
 
 pytestmark = pytest.mark.gpu
 
@@ -104,3 +110,49 @@ def test_router_grad_fp32_accumulation_across_chunks(name):
     assert chunked <= 1e-4
     assert naive >= 1e-3 and naive >= 10 * chunked
     assert to_ref[0] <= 5e-3 and to_ref[0] < to_ref[1]
+
+
+ROUTER_CASES = [
+    MoeConfig("rb_e32", T=1000, H=256, I=64, E=32, E_local=8, e0=4, k=4, n_chunks=2, dtype="bf16", seed_base=1210),
+    MoeConfig("rb_e128_h320", T=300, H=320, I=64, E=128, E_local=16, e0=0, k=8, n_chunks=1, dtype="bf16",
+              seed_base=1220),
+    MoeConfig("rb_e132", T=500, H=320, I=64, E=132, E_local=12, e0=120, k=6, n_chunks=2, dtype="bf16",
+              seed_base=1230),
+    MoeConfig("rb_e256", T=777, H=192, I=64, E=256, E_local=16, e0=100, k=8, n_chunks=3, dtype="bf16",
+              seed_base=1240),
+]
+
+
+@pytest.mark.parametrize("cfg", ROUTER_CASES, ids=[c.name for c in ROUTER_CASES])
+def test_router_grad_small_shapes(cfg):
+    """dlogits within FP32 rounding of the FP64 VJP (zero off the top-k), the FP32 accumulator over
+    every chunk within rel-L2 1e-5 of dlogits^T x in FP64, and dwr its one BF16 conversion."""
+    _require_gpu()
+    import torch
+    import combine_moe_route_02_amd as mh
+    import oracle
+    from oracle import ffn as offn
+    inp = moe_inputs.make_inputs(cfg, parts=("x", "logits"))
+    idx, gates64 = oracle.route(inp["logits"], cfg.k)
+    gates = gates64.astype(np.float32)
+    dgates = moe_inputs.make_dgates(cfg)
+    dl_ref = offn.route_bwd(dgates.astype(np.float64), gates.astype(np.float64), idx, cfg.E)
+    dwr_ref = dl_ref.T @ inp["x"].astype(np.float64)
+    d = mh.make_desc(T=cfg.T, H=cfg.H, I=cfg.I, E=cfg.E, E_local=cfg.E_local, k=cfg.k, n_chunks=cfg.n_chunks,
+                     dtype="bf16", e0=cfg.e0)
+    ws = torch.full((max(1, mh.workspace_bytes(d)["workspace"]),), 0xFF, dtype=torch.uint8, device="cuda")
+    x = torch.from_numpy(inp["x_bits"].view(np.int16)).cuda().view(torch.bfloat16)
+    dlogits = torch.full((cfg.T, cfg.E), 7.0, dtype=torch.float32, device="cuda")
+    acc = torch.full((cfg.E, cfg.H), 7.0, dtype=torch.float32, device="cuda")
+    dwr = torch.empty((cfg.E, cfg.H), dtype=torch.bfloat16, device="cuda")
+    print(f"[router small] {cfg.name}: T {cfg.T} E {cfg.E} H {cfg.H} k {cfg.k} chunks {cfg.n_chunks}", flush=True)
+    mh.moe_route_bwd(d, -1, torch.from_numpy(dgates).cuda(), torch.from_numpy(gates).cuda(),
+                     torch.from_numpy(idx).cuda(), x, dlogits, acc, dwr, ws)
+    torch.cuda.synchronize()
+    dl = dlogits.cpu().numpy().astype(np.float64)
+    assert harness.rel_l2(dl, dl_ref) <= 1e-6
+    assert np.all(dl[dl_ref == 0] == 0)
+    a64 = acc.cpu().numpy().astype(np.float64)
+    err = harness.rel_l2(a64, dwr_ref)
+    assert err <= 1e-5, err
+    np.testing.assert_array_equal(harness.to_np(dwr), _bf16(a64))
